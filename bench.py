@@ -1,0 +1,287 @@
+#!/usr/bin/env python3
+"""Benchmark of the NVFP4 W4A4 linear-layer hot path on one MI355X.
+
+Workload: the Wan-14B-shaped FFN on one GPU, M = 32760 tokens, hidden 5120, FFN 13824:
+    quantize X[32760,5120] -> mm_fp4 fc_in (W1 13824x5120) -> GELU -> quantize H[32760,13824]
+    -> mm_fp4 fc_out (W2 5120x13824) -> bf16 out[32760,5120]
+Weights are prequantized once at load (timed separately). Inputs are seeded synthetic bf16
+tensors (workloads/, config 4: X ~ N(0,1) with 1% outlier channels x20, W ~ N(0, 0.01^2)),
+resident in HBM before timing. One step = one pass of that FFN. The MXFP8 W8A8 path at the same
+fc_in shape (config 5: online weight conversion, activation quantize, mm_mxfp8) is timed in a
+second loop and reported under "mxfp8".
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP4_TFLOPS = 10100.0   # MI355X dense FP4/FP6 MFMA (published)
+PEAK_FP8_TFLOPS = 5000.0    # dense FP8
+PEAK_F16_TFLOPS = 2500.0    # dense FP16/BF16
+PEAK_HBM_GBS = 8000.0       # HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=1024,
+                    help="tokens of the FFN the CPU oracle runs for cpu_baseline")
+    ap.add_argument("--no-mxfp8", action="store_true")
+    return ap.parse_args()
+
+
+def nvfp4_sf_shape(rows, k):
+    return (-(-rows // 128) * 128, -(-(k // 16) // 4) * 4)
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the FFN shards by tokens or by output features with no exchange; see DESIGN.md). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_scaled_precision_nvfp4_amd as bsp
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = W.config(4)
+    tx, tw1, tw2 = cfg.tensor("X"), cfg.tensor("W"), cfg.tensor("W2")
+    M, K1, N1 = tx.rows, tx.cols, tw1.rows          # 32760, 5120, 13824
+    N2 = tw2.rows                                   # 5120
+
+    def up(bits):
+        return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    t0 = time.perf_counter()
+    x = up(W.generate(tx))
+    w1 = up(W.generate(tw1))
+    w2 = up(W.generate(tw2))
+    log(f"inputs generated and uploaded in {time.perf_counter() - t0:.1f}s")
+
+    stream = torch.cuda.current_stream(dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    # ---- load time: weight global scale + prequantization
+    l0, l1 = ev(), ev()
+    l0.record(stream)
+    pw1, sw1, g1, _, _ = bsp.bsp_nvfp4_prequantize_weight(w1)
+    pw2, sw2, g2, _, _ = bsp.bsp_nvfp4_prequantize_weight(w2)
+    l1.record(stream)
+    one = torch.ones(1, dtype=torch.float32, device=dev)
+    a1 = bsp.bsp_nvfp4_alpha(one, g1)
+    a2 = bsp.bsp_nvfp4_alpha(one, g2)
+    torch.cuda.synchronize()
+    load_ms = l0.elapsed_time(l1)
+    del w1, w2
+
+    # ---- step buffers
+    px = torch.empty((M, K1 // 2), dtype=torch.uint8, device=dev)
+    sx = torch.empty(nvfp4_sf_shape(M, K1), dtype=torch.uint8, device=dev)
+    y = torch.empty((M, N1), dtype=torch.bfloat16, device=dev)
+    h = torch.empty((M, N1), dtype=torch.bfloat16, device=dev)
+    ph = torch.empty((M, N1 // 2), dtype=torch.uint8, device=dev)
+    sh = torch.empty(nvfp4_sf_shape(M, N1), dtype=torch.uint8, device=dev)
+    out = torch.empty((M, N2), dtype=torch.bfloat16, device=dev)
+
+    names = ["quantize_x", "mm_fp4_fc_in", "gelu", "quantize_h", "mm_fp4_fc_out"]
+    acc = {n: 0.0 for n in names}
+
+    def step(events=None):
+        if events:
+            events[0].record(stream)
+        bsp.bsp_nvfp4_quantize(x, one, px, sx)
+        if events:
+            events[1].record(stream)
+        bsp.bsp_mm_fp4(px, sx, pw1, sw1, a1, out=y)
+        if events:
+            events[2].record(stream)
+        bsp.bsp_gelu_tanh_bf16(y, out=h)
+        if events:
+            events[3].record(stream)
+        bsp.bsp_nvfp4_quantize(h, one, ph, sh)
+        if events:
+            events[4].record(stream)
+        bsp.bsp_mm_fp4(ph, sh, pw2, sw2, a2, out=out)
+        if events:
+            events[5].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[ev() for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for e in evs:
+        for j, n in enumerate(names):
+            acc[n] += e[j].elapsed_time(e[j + 1])
+    kms = {n: acc[n] / args.steps for n in names}
+    ms_per_step = wall * 1e3 / args.steps
+
+    gemm_flops = 2.0 * M * N1 * K1 + 2.0 * M * N2 * N1
+    value = gemm_flops / (ms_per_step * 1e-3) / 1e12
+
+    def qbytes(m, k):
+        return 2 * m * k + m * k // 2 + nvfp4_sf_shape(m, k)[0] * k // 16
+
+    kernels = {
+        "quantize_x": {"ms": kms["quantize_x"], "GB/s": qbytes(M, K1) / kms["quantize_x"] / 1e6},
+        "quantize_h": {"ms": kms["quantize_h"], "GB/s": qbytes(M, N1) / kms["quantize_h"] / 1e6},
+        "gelu": {"ms": kms["gelu"], "GB/s": 4.0 * M * N1 / kms["gelu"] / 1e6},
+        "mm_fp4_fc_in": {"ms": kms["mm_fp4_fc_in"],
+                         "TFLOPS": 2.0 * M * N1 * K1 / kms["mm_fp4_fc_in"] / 1e9},
+        "mm_fp4_fc_out": {"ms": kms["mm_fp4_fc_out"],
+                          "TFLOPS": 2.0 * M * N2 * N1 / kms["mm_fp4_fc_out"] / 1e9},
+    }
+    for k_, v in kernels.items():
+        if "GB/s" in v:
+            v["frac_hbm"] = v["GB/s"] / PEAK_HBM_GBS
+        else:
+            v["frac_fp4_peak"] = v["TFLOPS"] / PEAK_FP4_TFLOPS
+            v["frac_f16_mfma_peak"] = v["TFLOPS"] / PEAK_F16_TFLOPS
+    log(json.dumps(kernels))
+
+    dom = "mm_fp4_fc_in" if kms["mm_fp4_fc_in"] >= kms["mm_fp4_fc_out"] else "mm_fp4_fc_out"
+    dom_tf = kernels[dom]["TFLOPS"]
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(dom_tf, 2),
+                "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s", "frac": round(dom_tf / PEAK_FP4_TFLOPS, 4),
+                "traffic": None,
+                "mfma_used": "v_mfma_f32_32x32x16_f16 (exact fp16 dequant of e2m1 x e4m3)",
+                "frac_of_f16_mfma_peak": round(dom_tf / PEAK_F16_TFLOPS, 4)}
+
+    result = {
+        "metric": "mm_fp4 TFLOPS (% FP4 MFMA peak) + quantize GB/s (% HBM) at Wan-14B FFN shape",
+        "value": round(value, 2), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "nvfp4", "data": "synthetic",
+        "config": {"workload": "Wan-14B FFN on one GPU: X[32760,5120] -> fc_in 13824x5120 -> GELU "
+                               "-> fc_out 5120x13824, NVFP4 W4A4, bf16 out",
+                   "tokens": M, "hidden": K1, "ffn": N1, "value_is": "GEMM FLOPs of both "
+                   "projections / whole-step time (quantizes and GELU included)"},
+        "roofline": roofline,
+        "kernels": {k_: {kk: round(vv, 4) for kk, vv in v.items()} for k_, v in kernels.items()},
+        "quantize_GBs": round(kernels["quantize_h"]["GB/s"], 1),
+        "quantize_frac_hbm": round(kernels["quantize_h"]["frac_hbm"], 4),
+        "load_time_ms": {"prequantize_w1_w2": round(load_ms, 3)},
+    }
+
+    # ---- MXFP8 W8A8 at the fc_in shape (config 5)
+    if not args.no_mxfp8:
+        del y, h, ph, sh
+        c5 = W.config(5)
+        x5 = up(W.generate(c5.tensor("X")))
+        w5 = up(W.generate(c5.tensor("W")))
+        m0, m1 = ev(), ev()
+        m0.record(stream)
+        qw, sw = bsp.bsp_mxfp8_quantize(w5)       # online BF16 -> MXFP8 weight conversion
+        m1.record(stream)
+        qx = torch.empty((M, K1), dtype=torch.uint8, device=dev)
+        sxm = torch.empty((M, K1 // 32), dtype=torch.uint8, device=dev)
+        out5 = torch.empty((M, N1), dtype=torch.bfloat16, device=dev)
+        del w5
+
+        def step8(e=None):
+            if e:
+                e[0].record(stream)
+            bsp.bsp_mxfp8_quantize(x5, qx, sxm)
+            if e:
+                e[1].record(stream)
+            bsp.bsp_mm_mxfp8(qx, sxm, qw, sw, out=out5)
+            if e:
+                e[2].record(stream)
+
+        for _ in range(args.warmup):
+            step8()
+        torch.cuda.synchronize()
+        e8 = [[ev() for _ in range(3)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            step8(e8[i])
+        torch.cuda.synchronize()
+        q8 = sum(e[0].elapsed_time(e[1]) for e in e8) / args.steps
+        g8 = sum(e[1].elapsed_time(e[2]) for e in e8) / args.steps
+        tf8 = 2.0 * M * N1 * K1 / g8 / 1e9
+        qb8 = 2 * M * K1 + M * K1 + M * K1 // 32
+        result["mxfp8"] = {
+            "mm_mxfp8_ms": round(g8, 4), "TFLOPS": round(tf8, 2),
+            "frac_fp8_peak": round(tf8 / PEAK_FP8_TFLOPS, 4),
+            "quantize_ms": round(q8, 4), "quantize_GBs": round(qb8 / q8 / 1e6, 1),
+            "quantize_frac_hbm": round(qb8 / q8 / 1e6 / PEAK_HBM_GBS, 4),
+            "weight_conversion_ms": round(m0.elapsed_time(m1), 4)}
+        log(json.dumps(result["mxfp8"]))
+
+    # ---- CPU oracle on a bounded sample of the same workload
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args.cpu_rows)
+        r = result["cpu_baseline"]
+        log(f"cpu baseline: {r['value']:.4f} {r['unit']} on {r['cores']} threads")
+
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(rows: int) -> dict:
+    """The oracle (as it stands) runs the same FFN on the first `rows` tokens of X."""
+    import numpy as np
+
+    import workloads as W
+    from oracle import activations as A
+    from oracle import nvfp4 as N
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = os.cpu_count() or 1
+    cfg = W.config(4)
+    xb = W.generate(cfg.tensor("X"), rows=rows)
+    w1 = W.generate(cfg.tensor("W"))
+    w2 = W.generate(cfg.tensor("W2"))
+    k1, n1, n2 = xb.shape[1], w1.shape[0], w2.shape[0]
+    t0 = time.perf_counter()
+    g1 = N.global_sf(w1)[0]
+    g2 = N.global_sf(w2)[0]
+    pw1, sw1 = N.quantize(w1, g1)
+    pw2, sw2 = N.quantize(w2, g2)
+    t_load = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    px, sx = N.quantize(xb, np.float32(1.0))
+    y = N.mm_fp4(px, sx, pw1, sw1, N.alpha(1.0, g1), rows, n1, k1)
+    yb = A.f64_to_bf16_bits(y)
+    hb = A.gelu_tanh_bf16_bits(yb)
+    ph, sh = N.quantize(hb, np.float32(1.0))
+    _ = N.mm_fp4(ph, sh, pw2, sw2, N.alpha(1.0, g2), rows, n2, n1)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * n1 * k1 + 2.0 * rows * n2 * n1
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOPS", "cores": int(blas_threads),
+            "kind": "oracle", "seconds": round(dt, 2), "weight_prequant_seconds": round(t_load, 2),
+            "host_cpus": os.cpu_count(),
+            "sample": f"first {rows} of 32760 tokens through the same NVFP4 FFN (quantize X, fc_in, "
+                      f"GELU, quantize H, fc_out) with the numpy oracle (fp64 GEMM of dequantized "
+                      f"operands); weight prequantization excluded"}
+
+
+if __name__ == "__main__":
+    main()

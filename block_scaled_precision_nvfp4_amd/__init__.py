@@ -1,0 +1,272 @@
+"""Thin Python binding of libbsp.so: NVFP4 W4A4 and MXFP8 W8A8 linear-layer kernels for MI355X.
+
+Every function has the name of the C entry point it calls (include/bsp.h) and does argument
+marshalling only: it checks dtypes/devices/shapes, allocates outputs with torch when the caller
+does not pass them, and calls the library on torch's current HIP stream. All arithmetic runs in
+the library's HIP kernels; there is no fallback. If libbsp.so is missing or fails to load, every
+call raises ``BspLibraryError`` (build it with ``python -m block_scaled_precision_nvfp4_amd._build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbsp.so")
+
+BSP_OUT_BF16 = 0
+BSP_OUT_F32 = 1
+
+_STATUS = {0: "BSP_OK", -1: "BSP_EINVAL", -2: "BSP_ESHAPE", -3: "BSP_EDTYPE",
+           -4: "BSP_EUNSUPPORTED", -5: "BSP_EHIP"}
+
+# C signatures (argument ctypes), in include/bsp.h order
+_i64, _p, _int = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+SIGNATURES = {
+    "bsp_last_error": ([], ctypes.c_char_p),
+    "bsp_version": ([], _int),
+    "bsp_nvfp4_sf_bytes": ([_i64, _i64, ctypes.POINTER(_i64)], _int),
+    "bsp_nvfp4_global_sf": ([_p, _i64, _i64, _i64, _p, _p, _p, _p], _int),
+    "bsp_nvfp4_quantize": ([_p, _i64, _i64, _i64, _p, _p, _p, _p], _int),
+    "bsp_nvfp4_prequantize_weight": ([_p, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p], _int),
+    "bsp_nvfp4_alpha": ([_p, _p, _p, _p], _int),
+    "bsp_mm_fp4": ([_p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _int, _p], _int),
+    "bsp_mxfp8_quantize": ([_p, _i64, _i64, _i64, _p, _p, _p], _int),
+    "bsp_mm_mxfp8": ([_p, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _int, _p], _int),
+    "bsp_gelu_tanh_bf16": ([_p, _p, _i64, _p], _int),
+}
+
+
+class BspLibraryError(RuntimeError):
+    """libbsp.so could not be loaded."""
+
+
+class BspError(RuntimeError):
+    """A libbsp call returned a non-OK status."""
+
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} -> {_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises BspLibraryError if it is not built or cannot be loaded)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise BspLibraryError(f"{LIB_PATH} not found; build it with "
+                                  "`python -m block_scaled_precision_nvfp4_amd._build`")
+        try:
+            h = ctypes.CDLL(LIB_PATH)
+        except OSError as e:
+            raise BspLibraryError(f"cannot load {LIB_PATH}: {e}") from e
+        for name, (args, res) in SIGNATURES.items():
+            f = getattr(h, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = h
+    return _lib
+
+
+def _call(name: str, *args) -> None:
+    st = getattr(lib(), name)(*args)
+    if st != 0:
+        raise BspError(name, st, lib().bsp_last_error().decode(errors="replace"))
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, dev: Optional[torch.device] = None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device, got {t.device}")
+    if dev is not None and t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, expected {dev}")
+
+
+def _as_bf16_2d(x: torch.Tensor, name: str) -> torch.Tensor:
+    """fp32 activations are cast to bf16 (the pages coerce fp32 to bf16 before the FP4 linear);
+    non-float inputs are rejected; the last dim must be contiguous."""
+    if not x.is_floating_point():
+        raise TypeError(f"{name} must be floating point, got {x.dtype}")
+    if x.dtype == torch.float32:
+        x = x.to(torch.bfloat16)
+    if x.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bf16 (or fp32, cast to bf16), got {x.dtype}")
+    if x.dim() != 2:
+        x = x.reshape(-1, x.shape[-1])
+    if x.stride(-1) != 1:
+        x = x.contiguous()
+    return x
+
+
+# ------------------------------------------------------------------------------------- queries
+def bsp_version() -> int:
+    return lib().bsp_version()
+
+
+def bsp_nvfp4_sf_bytes(rows: int, k: int) -> int:
+    out = ctypes.c_int64(0)
+    _call("bsp_nvfp4_sf_bytes", rows, k, ctypes.byref(out))
+    return out.value
+
+
+# ------------------------------------------------------------------------------------- NVFP4
+def bsp_nvfp4_global_sf(w: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """(gsf, inv_gsf, amax): fp32 device scalars (shape [1]) for bf16 weight w [N, K]."""
+    w = _as_bf16_2d(w, "w")
+    _need(w, "w", torch.bfloat16)
+    sc = torch.empty(3, dtype=torch.float32, device=w.device)
+    gsf, inv, amax = sc[0:1], sc[1:2], sc[2:3]
+    _call("bsp_nvfp4_global_sf", w.data_ptr(), w.shape[0], w.shape[1], w.stride(0),
+          gsf.data_ptr(), inv.data_ptr(), amax.data_ptr(), _stream(w.device))
+    return gsf, inv, amax
+
+
+def bsp_nvfp4_quantize(x: torch.Tensor, gsf: torch.Tensor,
+                       packed: Optional[torch.Tensor] = None,
+                       sf: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """(packed uint8 [M, K/2], sf uint8 [ceil(M/128)*128, ceil(K/64)*4] in the 128x4 layout)."""
+    x = _as_bf16_2d(x, "x")
+    _need(gsf, "gsf", torch.float32, x.device)
+    m, k = x.shape
+    rp = -(-m // 128) * 128
+    kp = -(-(k // 16) // 4) * 4
+    if packed is None:
+        packed = torch.empty((m, k // 2), dtype=torch.uint8, device=x.device)
+    if sf is None:
+        sf = torch.empty((rp, kp), dtype=torch.uint8, device=x.device)
+    _need(packed, "packed", torch.uint8, x.device)
+    _need(sf, "sf", torch.uint8, x.device)
+    if packed.numel() < m * (k // 2) or not packed.is_contiguous():
+        raise ValueError("packed must be contiguous with M*K/2 bytes")
+    if sf.numel() < rp * kp or not sf.is_contiguous():
+        raise ValueError("sf must be contiguous with bsp_nvfp4_sf_bytes(M, K) bytes")
+    _call("bsp_nvfp4_quantize", x.data_ptr(), m, k, x.stride(0), gsf.data_ptr(),
+          packed.data_ptr(), sf.data_ptr(), _stream(x.device))
+    return packed, sf
+
+
+def bsp_nvfp4_prequantize_weight(w: torch.Tensor):
+    """Load-time: (packed, sf, gsf, inv_gsf, amax) for bf16 weight w [N, K]."""
+    w = _as_bf16_2d(w, "w")
+    n, k = w.shape
+    packed = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
+    sf = torch.empty((-(-n // 128) * 128, -(-(k // 16) // 4) * 4), dtype=torch.uint8, device=w.device)
+    sc = torch.empty(3, dtype=torch.float32, device=w.device)
+    gsf, inv, amax = sc[0:1], sc[1:2], sc[2:3]
+    _call("bsp_nvfp4_prequantize_weight", w.data_ptr(), n, k, w.stride(0), packed.data_ptr(),
+          sf.data_ptr(), gsf.data_ptr(), inv.data_ptr(), amax.data_ptr(), _stream(w.device))
+    return packed, sf, gsf, inv, amax
+
+
+def bsp_nvfp4_alpha(x_gsf: torch.Tensor, w_gsf: torch.Tensor) -> torch.Tensor:
+    _need(x_gsf, "x_gsf", torch.float32)
+    _need(w_gsf, "w_gsf", torch.float32, x_gsf.device)
+    out = torch.empty(1, dtype=torch.float32, device=x_gsf.device)
+    _call("bsp_nvfp4_alpha", x_gsf.data_ptr(), w_gsf.data_ptr(), out.data_ptr(), _stream(x_gsf.device))
+    return out
+
+
+def bsp_mm_fp4(a: torch.Tensor, a_sf: torch.Tensor, b: torch.Tensor, b_sf: torch.Tensor,
+               alpha: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16,
+               out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C [M, N] = alpha * A . B^T. a: packed [M, K/2], b: packed weight [N, K/2] (K-major)."""
+    _need(a, "a", torch.uint8)
+    dev = a.device
+    for t, nm in ((a_sf, "a_sf"), (b, "b"), (b_sf, "b_sf")):
+        _need(t, nm, torch.uint8, dev)
+    _need(alpha, "alpha", torch.float32, dev)
+    if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[1]:
+        raise ValueError(f"a {tuple(a.shape)} and b {tuple(b.shape)} must be [M, K/2] and [N, K/2]")
+    if not (a.is_contiguous() and b.is_contiguous() and a_sf.is_contiguous() and b_sf.is_contiguous()):
+        raise ValueError("operands and scales must be contiguous")
+    m, n, k = a.shape[0], b.shape[0], a.shape[1] * 2
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"out_dtype must be bf16 or fp32, got {out_dtype}")
+    code = BSP_OUT_BF16 if out_dtype == torch.bfloat16 else BSP_OUT_F32
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=dev)
+    _need(out, "out", out_dtype, dev)
+    if out.dim() != 2 or out.shape[0] != m or out.shape[1] != n or out.stride(1) != 1:
+        raise ValueError(f"out must be [{m}, {n}] with unit column stride")
+    if a_sf.numel() < bsp_nvfp4_sf_bytes(m, k) or b_sf.numel() < bsp_nvfp4_sf_bytes(n, k):
+        raise ValueError("scale buffers are smaller than bsp_nvfp4_sf_bytes")
+    _call("bsp_mm_fp4", a.data_ptr(), a_sf.data_ptr(), b.data_ptr(), b_sf.data_ptr(),
+          alpha.data_ptr(), m, n, k, out.data_ptr(), out.stride(0), code, _stream(dev))
+    return out
+
+
+# ------------------------------------------------------------------------------------- MXFP8
+def bsp_mxfp8_quantize(x: torch.Tensor, q: Optional[torch.Tensor] = None,
+                       sf: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """(q uint8 e4m3 [M, K], sf uint8 e8m0 [M, K/32])."""
+    x = _as_bf16_2d(x, "x")
+    m, k = x.shape
+    if q is None:
+        q = torch.empty((m, k), dtype=torch.uint8, device=x.device)
+    if sf is None:
+        sf = torch.empty((m, k // 32), dtype=torch.uint8, device=x.device)
+    _need(q, "q", torch.uint8, x.device)
+    _need(sf, "sf", torch.uint8, x.device)
+    if tuple(q.shape) != (m, k) or tuple(sf.shape) != (m, k // 32) or not (q.is_contiguous() and sf.is_contiguous()):
+        raise ValueError("q must be contiguous [M, K] and sf contiguous [M, K/32]")
+    _call("bsp_mxfp8_quantize", x.data_ptr(), m, k, x.stride(0), q.data_ptr(), sf.data_ptr(),
+          _stream(x.device))
+    return q, sf
+
+
+def bsp_mm_mxfp8(a: torch.Tensor, a_sf: torch.Tensor, b: torch.Tensor, b_sf: torch.Tensor,
+                 out_dtype: torch.dtype = torch.bfloat16,
+                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C [M, N] = A . B^T for MXFP8 a [M, K] / a_sf [M, K/32] and b [N, K] / b_sf [N, K/32]."""
+    _need(a, "a", torch.uint8)
+    dev = a.device
+    for t, nm in ((a_sf, "a_sf"), (b, "b"), (b_sf, "b_sf")):
+        _need(t, nm, torch.uint8, dev)
+    if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[1]:
+        raise ValueError(f"a {tuple(a.shape)} and b {tuple(b.shape)} must be [M, K] and [N, K]")
+    m, n, k = a.shape[0], b.shape[0], a.shape[1]
+    if tuple(a_sf.shape) != (m, k // 32) or tuple(b_sf.shape) != (n, k // 32):
+        raise ValueError("scales must be [rows, K/32]")
+    if not (a.is_contiguous() and b.is_contiguous() and a_sf.is_contiguous() and b_sf.is_contiguous()):
+        raise ValueError("operands and scales must be contiguous")
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"out_dtype must be bf16 or fp32, got {out_dtype}")
+    code = BSP_OUT_BF16 if out_dtype == torch.bfloat16 else BSP_OUT_F32
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=dev)
+    _need(out, "out", out_dtype, dev)
+    _call("bsp_mm_mxfp8", a.data_ptr(), a_sf.data_ptr(), b.data_ptr(), b_sf.data_ptr(), m, n, k,
+          out.data_ptr(), out.stride(0), code, _stream(dev))
+    return out
+
+
+def bsp_gelu_tanh_bf16(x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    _need(x, "x", torch.bfloat16)
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    if out is None:
+        out = torch.empty_like(x)
+    _need(out, "out", torch.bfloat16, x.device)
+    _call("bsp_gelu_tanh_bf16", x.data_ptr(), out.data_ptr(), x.numel(), _stream(x.device))
+    return out
+
+
+__all__ = [n for n in SIGNATURES if n not in ("bsp_last_error",)] + [
+    "BspError", "BspLibraryError", "BSP_OUT_BF16", "BSP_OUT_F32", "lib"]

@@ -1,0 +1,406 @@
+// HBM-bound kernels of the NVFP4 / MXFP8 linear layer on gfx950:
+//   a1 weight global scale (amax reduction + scalar finish), a2 NVFP4 quantize, a3 alpha,
+//   a6 MXFP8 quantize, and the bf16 GELU between the FFN projections.
+//
+// Pages (by title, section): FastVideo nvfp4_qat_config.py (convert_model_to_fp4, apply),
+// FastVideo nvfp4_config.py (module docstring, _nvfp4_quantize and its shape kernel,
+// convert_model_to_nvfp4), SGLang nvfp4_online.py (_quantize_weight_nvfp4),
+// vLLM-Omni mxfp8_config.py (DiffusionMXFP8Config, NPUMxfp8LinearMethod).
+#include "common.hpp"
+
+namespace bsp {
+
+// =============================================================================================
+// a1: weight global scale
+// =============================================================================================
+// |bf16| magnitude bits after nan_to_num: NaN -> 0, inf -> largest finite (0x7F7F). Magnitude
+// bit patterns of non-negative bf16 values order like the values, so the max is an integer max.
+__device__ __forceinline__ uint32_t mag_nan_to_num(uint32_t b16) {
+  uint32_t m = b16 & 0x7FFFu;
+  return m > 0x7F80u ? 0u : (m == 0x7F80u ? 0x7F7Fu : m);
+}
+
+__global__ void amax_init_kernel(float* amax) { *reinterpret_cast<uint32_t*>(amax) = 0u; }
+
+template <bool VEC>
+__global__ __launch_bounds__(256) void amax_reduce_kernel(const uint16_t* __restrict__ w, int64_t rows,
+                                                          int64_t K, int64_t ld, float* amax) {
+  uint32_t m = 0;
+  if (VEC) {  // K % 8 == 0, ld % 8 == 0, 16-byte aligned base
+    const int64_t cpr = K / 8;
+    const int64_t total = rows * cpr;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+      int64_t r = i / cpr, c = i - r * cpr;
+      uint4 v = *reinterpret_cast<const uint4*>(w + r * ld + c * 8);
+      uint32_t q[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        m = max(m, mag_nan_to_num(q[j] & 0xFFFFu));
+        m = max(m, mag_nan_to_num(q[j] >> 16));
+      }
+    }
+  } else {
+    const int64_t total = rows * K;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+      int64_t r = i / K, c = i - r * K;
+      m = max(m, mag_nan_to_num(w[r * ld + c]));
+    }
+  }
+  // wave max, then across the 4 waves through LDS, then one atomic per block
+  for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  __shared__ uint32_t part[4];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t b = max(max(part[0], part[1]), max(part[2], part[3]));
+    atomicMax(reinterpret_cast<unsigned int*>(amax), b << 16);  // non-negative fp32 bits order as uint
+  }
+}
+
+__global__ void gsf_finish_kernel(float* amax, float* gsf, float* inv_gsf) {
+  float a = *amax;
+  float g = (a == 0.0f) ? 1.0f : 2688.0f / a;  // 448 * 6 / amax, one IEEE division
+  *gsf = g;
+  *inv_gsf = 1.0f / g;
+}
+
+// =============================================================================================
+// a3: alpha = fl32(1 / fl32(x_gsf * w_gsf))
+// =============================================================================================
+__global__ void alpha_kernel(const float* xg, const float* wg, float* alpha) {
+  float p = (*xg) * (*wg);
+  *alpha = 1.0f / p;
+}
+
+// =============================================================================================
+// a2: NVFP4 quantize
+// =============================================================================================
+// One workgroup quantizes a 128-row x 256-K tile (16 scale columns = 4 column groups of the
+// 128x4 scale layout, i.e. four whole 512-byte scale tiles). 256 threads = 8 rows x 32 lanes;
+// each lane owns 8 consecutive K elements (one 16-byte load), so a 16-element block is a lane
+// pair and its amax is a DPP pair max. The tile is walked in 16 steps of 8 rows; all 16 loads
+// are issued before any arithmetic. Scale bytes are staged in LDS at their 128x4 positions and
+// leave as coalesced 16-byte stores of whole 512-byte tiles. Rows M..Mp-1 and columns past K
+// read as zeros (no copy of the input is made), which yields the 0x00 padding scales.
+constexpr float kSixth = 0.16666667163372040f;  // fl32(1/6) = 0x3E2AAAAB
+
+template <bool HWCVT, bool VEC>
+__global__ __launch_bounds__(256) void nvfp4_quantize_kernel(const uint16_t* __restrict__ x,
+                                                             int64_t M, int64_t K, int64_t ld,
+                                                             const float* __restrict__ gsf,
+                                                             uint8_t* __restrict__ packed,
+                                                             uint8_t* __restrict__ sf, int64_t Kp) {
+  __shared__ uint4 sf_tile[128];  // 2 KB = 4 scale tiles of 512 B
+  uint8_t* sfb = reinterpret_cast<uint8_t*>(sf_tile);
+  const int t = threadIdx.x;
+  const int64_t row0 = (int64_t)blockIdx.y * 128;
+  const int64_t kk = (int64_t)blockIdx.x * 256 + (t & 31) * 8;
+  const int rsub = t >> 5;
+  const bool kin = kk < K;  // K % 16 == 0: a lane's 8 elements are all in range or all out
+  const float g = *gsf;
+
+  uint4 v[16];
+#pragma unroll
+  for (int s = 0; s < 16; ++s) {
+    int64_t r = row0 + s * 8 + rsub;
+    if (kin && r < M) {
+      const uint16_t* p = x + r * ld + kk;
+      if (VEC) {
+        v[s] = *reinterpret_cast<const uint4*>(p);
+      } else {
+        v[s].x = (uint32_t)p[0] | ((uint32_t)p[1] << 16);
+        v[s].y = (uint32_t)p[2] | ((uint32_t)p[3] << 16);
+        v[s].z = (uint32_t)p[4] | ((uint32_t)p[5] << 16);
+        v[s].w = (uint32_t)p[6] | ((uint32_t)p[7] << 16);
+      }
+    } else {
+      v[s] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+
+  const int64_t half_k = K / 2;
+#pragma unroll
+  for (int s = 0; s < 16; ++s) {
+    float f[8];
+    f[0] = bf16_lo(v[s].x); f[1] = bf16_hi(v[s].x);
+    f[2] = bf16_lo(v[s].y); f[3] = bf16_hi(v[s].y);
+    f[4] = bf16_lo(v[s].z); f[5] = bf16_hi(v[s].z);
+    f[6] = bf16_lo(v[s].w); f[7] = bf16_hi(v[s].w);
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a = fmaxf(a, __builtin_fabsf(f[i]));
+    a = pair_max(a);
+    const float sc = g * (a * kSixth);
+    const uint32_t S = e4m3_encode_pos(sc);
+    const float r = (S == 0u) ? 0.0f : g / e4m3_decode_pos(S);
+    uint32_t out = 0;
+    if (HWCVT) {
+      out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, f[0] * r, f[1] * r, 1.0f, 0);
+      out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, f[2] * r, f[3] * r, 1.0f, 1);
+      out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, f[4] * r, f[5] * r, 1.0f, 2);
+      out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, f[6] * r, f[7] * r, 1.0f, 3);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) out |= e2m1_encode(f[i] * r) << (4 * i);
+    }
+    const int rr = s * 8 + rsub;  // row inside the 128-row tile
+    const int64_t row = row0 + rr;
+    if (kin && row < M) *reinterpret_cast<uint32_t*>(packed + row * half_k + kk / 2) = out;
+    if ((t & 1) == 0) {
+      const int cb = (t & 31) >> 1;  // scale column inside the 16-column tile
+      sfb[(cb >> 2) * 512 + (rr & 31) * 16 + (rr >> 5) * 4 + (cb & 3)] = (uint8_t)S;
+    }
+  }
+  __syncthreads();
+  const int64_t groups = Kp / 4;                       // 128x4 column groups in the matrix
+  const int64_t g0 = (int64_t)blockIdx.x * 4;
+  const int64_t ng = groups - g0 < 4 ? groups - g0 : 4;
+  if (t < ng * 32) {
+    const int cg = t >> 5;
+    const int64_t tile = (int64_t)blockIdx.y * groups + g0 + cg;
+    reinterpret_cast<uint4*>(sf + tile * 512)[t & 31] = sf_tile[cg * 32 + (t & 31)];
+  }
+}
+
+// =============================================================================================
+// a6: MXFP8 quantize
+// =============================================================================================
+// One workgroup covers 64 rows x 256 K (8 steps of 8 rows x 32 lanes x 8 elements). A 32-element
+// group is a lane quad; its amax is a DPP quad max. Scale byte = max(biased exponent of amax - 8, 0)
+// (that is Es + 127 with Es = clamp(floor(log2 amax) - 8, -127, 127), and 0x00 for amax == 0).
+template <bool VEC>
+__global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const uint16_t* __restrict__ x,
+                                                             int64_t M, int64_t K, int64_t ld,
+                                                             uint8_t* __restrict__ q,
+                                                             uint8_t* __restrict__ sf) {
+  const int t = threadIdx.x;
+  const int64_t row0 = (int64_t)blockIdx.y * 64;
+  const int64_t kk = (int64_t)blockIdx.x * 256 + (t & 31) * 8;
+  const int rsub = t >> 5;
+  const bool kin = kk < K;  // K % 32 == 0: a quad is entirely in or out
+  uint4 v[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    int64_t r = row0 + s * 8 + rsub;
+    if (kin && r < M) {
+      const uint16_t* p = x + r * ld + kk;
+      if (VEC) {
+        v[s] = *reinterpret_cast<const uint4*>(p);
+      } else {
+        v[s].x = (uint32_t)p[0] | ((uint32_t)p[1] << 16);
+        v[s].y = (uint32_t)p[2] | ((uint32_t)p[3] << 16);
+        v[s].z = (uint32_t)p[4] | ((uint32_t)p[5] << 16);
+        v[s].w = (uint32_t)p[6] | ((uint32_t)p[7] << 16);
+      }
+    } else {
+      v[s] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  const int64_t ng = K / 32;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    float f[8];
+    f[0] = bf16_lo(v[s].x); f[1] = bf16_hi(v[s].x);
+    f[2] = bf16_lo(v[s].y); f[3] = bf16_hi(v[s].y);
+    f[4] = bf16_lo(v[s].z); f[5] = bf16_hi(v[s].z);
+    f[6] = bf16_lo(v[s].w); f[7] = bf16_hi(v[s].w);
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a = fmaxf(a, __builtin_fabsf(f[i]));
+    a = quad_max(a);
+    const uint32_t ef = __float_as_uint(a) >> 23;          // biased exponent (a >= 0, finite)
+    const uint32_t byte = ef > 8u ? ef - 8u : 0u;          // Es + 127
+    const float inv = __uint_as_float((254u - byte) << 23);  // 2^-Es = 2^(127 - byte), exact
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lo |= e4m3_encode(f[i] * inv) << (8 * i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hi |= e4m3_encode(f[4 + i] * inv) << (8 * i);
+    const int64_t row = row0 + s * 8 + rsub;
+    if (kin && row < M) {
+      *reinterpret_cast<uint2*>(q + row * K + kk) = make_uint2(lo, hi);
+      if ((t & 3) == 0) sf[row * ng + kk / 32] = (uint8_t)byte;
+    }
+  }
+}
+
+// =============================================================================================
+// GELU (tanh form), bf16 in/out, fp32 math
+// =============================================================================================
+// gelu(x) = 0.5 x (1 + tanh(z)), z = sqrt(2/pi) (x + 0.044715 x^3). Since 0.5 (1 + tanh z) is the
+// logistic function of 2z, it is evaluated with t = exp(-2|z|) <= 1 as x / (1 + t) for z >= 0 and
+// x t / (1 + t) for z < 0: no cancellation and no overflow anywhere.
+__device__ __forceinline__ float gelu_tanh(float x) {
+  const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
+  const float k1 = 0.044715f;
+  const float z = k0 * (x + k1 * (x * x * x));
+  const float t = expf(-2.0f * __builtin_fabsf(z));
+  const float num = z >= 0.0f ? x : x * t;
+  return num / (1.0f + t);
+}
+
+__global__ __launch_bounds__(256) void gelu_kernel(const uint16_t* __restrict__ x,
+                                                   uint16_t* __restrict__ y, int64_t n) {
+  const int64_t n8 = n / 8;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    uint4 v = reinterpret_cast<const uint4*>(x)[i];
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t lo = f32_to_bf16_rne(gelu_tanh(bf16_lo(w[j])));
+      uint32_t hi = f32_to_bf16_rne(gelu_tanh(bf16_hi(w[j])));
+      w[j] = lo | (hi << 16);
+    }
+    reinterpret_cast<uint4*>(y)[i] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  // tail (n % 8 elements)
+  int64_t i = n8 * 8 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) y[i] = (uint16_t)f32_to_bf16_rne(gelu_tanh(__uint_as_float((uint32_t)x[i] << 16)));
+}
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+static int hw_cvt_enabled() {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = getenv("BSP_QUANT_SW_CVT");
+    v = (e && e[0] == '1') ? 0 : BSP_DEFAULT_HW_CVT;
+  }
+  return v;
+}
+
+int launch_global_sf(const void* w, int64_t rows, int64_t K, int64_t ld, float* gsf, float* inv,
+                     float* amax, hipStream_t s) {
+  hipLaunchKernelGGL(amax_init_kernel, dim3(1), dim3(1), 0, s, amax);
+  if (rows > 0 && K > 0) {
+    const uint16_t* wp = static_cast<const uint16_t*>(w);
+    const bool vec = (K % 8 == 0) && (ld % 8 == 0) && aligned16(w);
+    int64_t work = vec ? rows * (K / 8) : rows * K;
+    int64_t blocks = ceil_div(work, 256);
+    if (blocks > 4096) blocks = 4096;
+    if (vec)
+      hipLaunchKernelGGL(amax_reduce_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, wp, rows,
+                         K, ld, amax);
+    else
+      hipLaunchKernelGGL(amax_reduce_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, wp, rows,
+                         K, ld, amax);
+  }
+  hipLaunchKernelGGL(gsf_finish_kernel, dim3(1), dim3(1), 0, s, amax, gsf, inv);
+  return check_launch("bsp_nvfp4_global_sf");
+}
+
+int launch_nvfp4_quantize(const void* x, int64_t M, int64_t K, int64_t ld, const float* gsf,
+                          uint8_t* packed, uint8_t* sf, hipStream_t s) {
+  const int64_t Mp = ceil_div(M, 128) * 128;
+  const int64_t Kp = ceil_div(K / 16, 4) * 4;
+  dim3 grid((unsigned)ceil_div(Kp, 16), (unsigned)(Mp / 128));
+  const uint16_t* xp = static_cast<const uint16_t*>(x);
+  const bool vec = (ld % 8 == 0) && aligned16(x);
+  const bool hw = hw_cvt_enabled();
+  if (hw && vec)
+    hipLaunchKernelGGL((nvfp4_quantize_kernel<true, true>), grid, dim3(256), 0, s, xp, M, K, ld, gsf,
+                       packed, sf, Kp);
+  else if (hw)
+    hipLaunchKernelGGL((nvfp4_quantize_kernel<true, false>), grid, dim3(256), 0, s, xp, M, K, ld, gsf,
+                       packed, sf, Kp);
+  else if (vec)
+    hipLaunchKernelGGL((nvfp4_quantize_kernel<false, true>), grid, dim3(256), 0, s, xp, M, K, ld, gsf,
+                       packed, sf, Kp);
+  else
+    hipLaunchKernelGGL((nvfp4_quantize_kernel<false, false>), grid, dim3(256), 0, s, xp, M, K, ld,
+                       gsf, packed, sf, Kp);
+  return check_launch("bsp_nvfp4_quantize");
+}
+
+}  // namespace bsp
+
+using namespace bsp;
+
+extern "C" int bsp_nvfp4_global_sf(const void* w, int64_t rows, int64_t K, int64_t ld, float* gsf,
+                                   float* inv_gsf, float* amax, void* stream) {
+  BSP_REQUIRE(gsf && inv_gsf && amax, BSP_EINVAL, "bsp_nvfp4_global_sf: null scalar pointer");
+  BSP_REQUIRE(rows >= 0 && K >= 0, BSP_EINVAL, "bsp_nvfp4_global_sf: negative size");
+  BSP_REQUIRE(rows * K == 0 || w, BSP_EINVAL, "bsp_nvfp4_global_sf: null weight pointer");
+  BSP_REQUIRE(rows <= 1 || ld >= K, BSP_ESHAPE, "bsp_nvfp4_global_sf: ld (%lld) < K (%lld)",
+              (long long)ld, (long long)K);
+  if (int e = check_device()) return e;
+  return launch_global_sf(w, rows, K, ld, gsf, inv_gsf, amax, (hipStream_t)stream);
+}
+
+extern "C" int bsp_nvfp4_quantize(const void* x, int64_t M, int64_t K, int64_t ld, const float* gsf,
+                                  uint8_t* packed, uint8_t* sf, void* stream) {
+  BSP_REQUIRE(M >= 0 && K > 0, BSP_EINVAL, "bsp_nvfp4_quantize: bad size M=%lld K=%lld",
+              (long long)M, (long long)K);
+  BSP_REQUIRE(K % 16 == 0, BSP_ESHAPE, "bsp_nvfp4_quantize: K (%lld) must be a multiple of 16",
+              (long long)K);
+  BSP_REQUIRE(M <= 1 || ld >= K, BSP_ESHAPE, "bsp_nvfp4_quantize: ld (%lld) < K (%lld)",
+              (long long)ld, (long long)K);
+  if (M == 0) return BSP_OK;
+  BSP_REQUIRE(x && gsf && packed && sf, BSP_EINVAL, "bsp_nvfp4_quantize: null pointer");
+  BSP_REQUIRE((reinterpret_cast<uintptr_t>(packed) & 3u) == 0 && (reinterpret_cast<uintptr_t>(sf) & 15u) == 0,
+              BSP_EINVAL, "bsp_nvfp4_quantize: packed must be 4-byte and sf 16-byte aligned");
+  BSP_REQUIRE(ceil_div(M, 128) < 65536, BSP_ESHAPE, "bsp_nvfp4_quantize: M too large");
+  if (int e = check_device()) return e;
+  return launch_nvfp4_quantize(x, M, K, ld, gsf, packed, sf, (hipStream_t)stream);
+}
+
+extern "C" int bsp_nvfp4_prequantize_weight(const void* w, int64_t N, int64_t K, int64_t ld,
+                                            uint8_t* packed, uint8_t* sf, float* gsf,
+                                            float* inv_gsf, float* amax, void* stream) {
+  BSP_REQUIRE(N > 0 && K > 0, BSP_EINVAL, "bsp_nvfp4_prequantize_weight: bad size");
+  BSP_REQUIRE(K % 16 == 0, BSP_ESHAPE, "bsp_nvfp4_prequantize_weight: K (%lld) must be a multiple of 16",
+              (long long)K);
+  BSP_REQUIRE(w && packed && sf && gsf && inv_gsf && amax, BSP_EINVAL,
+              "bsp_nvfp4_prequantize_weight: null pointer");
+  int e = bsp_nvfp4_global_sf(w, N, K, ld, gsf, inv_gsf, amax, stream);
+  if (e) return e;
+  return bsp_nvfp4_quantize(w, N, K, ld, gsf, packed, sf, stream);
+}
+
+extern "C" int bsp_nvfp4_alpha(const float* xg, const float* wg, float* alpha, void* stream) {
+  BSP_REQUIRE(xg && wg && alpha, BSP_EINVAL, "bsp_nvfp4_alpha: null pointer");
+  if (int e = check_device()) return e;
+  hipLaunchKernelGGL(alpha_kernel, dim3(1), dim3(1), 0, (hipStream_t)stream, xg, wg, alpha);
+  return check_launch("bsp_nvfp4_alpha");
+}
+
+extern "C" int bsp_mxfp8_quantize(const void* x, int64_t M, int64_t K, int64_t ld, uint8_t* q,
+                                  uint8_t* sf, void* stream) {
+  BSP_REQUIRE(M >= 0 && K > 0, BSP_EINVAL, "bsp_mxfp8_quantize: bad size M=%lld K=%lld",
+              (long long)M, (long long)K);
+  BSP_REQUIRE(K % 32 == 0, BSP_ESHAPE, "bsp_mxfp8_quantize: K (%lld) must be a multiple of 32",
+              (long long)K);
+  BSP_REQUIRE(M <= 1 || ld >= K, BSP_ESHAPE, "bsp_mxfp8_quantize: ld (%lld) < K (%lld)",
+              (long long)ld, (long long)K);
+  if (M == 0) return BSP_OK;
+  BSP_REQUIRE(x && q && sf, BSP_EINVAL, "bsp_mxfp8_quantize: null pointer");
+  BSP_REQUIRE((reinterpret_cast<uintptr_t>(q) & 7u) == 0, BSP_EINVAL,
+              "bsp_mxfp8_quantize: q must be 8-byte aligned");
+  BSP_REQUIRE(ceil_div(M, 64) < 65536, BSP_ESHAPE, "bsp_mxfp8_quantize: M too large");
+  if (int e = check_device()) return e;
+  dim3 grid((unsigned)ceil_div(K, 256), (unsigned)ceil_div(M, 64));
+  const uint16_t* xp = static_cast<const uint16_t*>(x);
+  if ((ld % 8 == 0) && aligned16(x))
+    hipLaunchKernelGGL(mxfp8_quantize_kernel<true>, grid, dim3(256), 0, (hipStream_t)stream, xp, M, K,
+                       ld, q, sf);
+  else
+    hipLaunchKernelGGL(mxfp8_quantize_kernel<false>, grid, dim3(256), 0, (hipStream_t)stream, xp, M, K,
+                       ld, q, sf);
+  return check_launch("bsp_mxfp8_quantize");
+}
+
+extern "C" int bsp_gelu_tanh_bf16(const void* x, void* y, int64_t n, void* stream) {
+  BSP_REQUIRE(n >= 0, BSP_EINVAL, "bsp_gelu_tanh_bf16: negative size");
+  if (n == 0) return BSP_OK;
+  BSP_REQUIRE(x && y, BSP_EINVAL, "bsp_gelu_tanh_bf16: null pointer");
+  BSP_REQUIRE(aligned16(x) && aligned16(y), BSP_EINVAL, "bsp_gelu_tanh_bf16: pointers must be 16-byte aligned");
+  if (int e = check_device()) return e;
+  int64_t blocks = ceil_div(n / 8 > 0 ? n / 8 : 1, 256);
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(gelu_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+                     static_cast<const uint16_t*>(x), static_cast<uint16_t*>(y), n);
+  return check_launch("bsp_gelu_tanh_bf16");
+}

@@ -1,0 +1,129 @@
+/*
+ * bsp.h -- block-scaled precision linear layers (NVFP4 W4A4, MXFP8 W8A8) for AMD MI355X (gfx950).
+ *
+ * C ABI of libbsp.so. Every entry point:
+ *   - takes plain pointers and sizes; device pointers are HIP device memory owned by the caller
+ *     (the library never allocates, frees or keeps any pointer after the call returns);
+ *   - validates its arguments on the host before launching anything and returns a bsp_status;
+ *     on failure nothing was launched and bsp_last_error() describes the problem;
+ *   - enqueues its kernels on the caller's stream (hipStream_t passed as void*; NULL = the null
+ *     stream) and returns without synchronising or reading anything back;
+ *   - takes scalars that are produced on the device (global scales, alpha) as device pointers, so
+ *     a forward pass needs no device-to-host sync (the FastVideo nvfp4_qat_config.py page keeps
+ *     the activation global scale as a device-resident constant for this reason).
+ *
+ * Pages cited (by title, section = the function or class on the page):
+ *   [FV-QAT]  FastVideo nvfp4_qat_config.py      [FV-NV]  FastVideo nvfp4_config.py
+ *   [SGL]     SGLang nvfp4_online.py             [VLO]    vLLM-Omni mxfp8_config.py
+ *
+ * Formats: e2m1 = 4-bit float (sign, 2 exponent bits bias 1, 1 mantissa bit; max 6);
+ * e4m3 = 8-bit float "fn" (bias 7, max 448, no inf); e8m0 = power-of-two scale 2^(byte-127).
+ * bf16 inputs are row-major with a row stride `ld` given in elements (ld >= K).
+ */
+#ifndef BSP_H
+#define BSP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BSP_OK = 0,
+  BSP_EINVAL = -1,      /* null pointer, negative size, bad enum value                     */
+  BSP_ESHAPE = -2,      /* shape rule violated (K % 16, K % 32, GEMM K/N alignment, ld < K) */
+  BSP_EDTYPE = -3,      /* unsupported output dtype                                        */
+  BSP_EUNSUPPORTED = -4,/* the current device is not gfx950                                */
+  BSP_EHIP = -5         /* a HIP runtime call failed (launch error); see bsp_last_error     */
+} bsp_status;
+
+typedef enum { BSP_OUT_BF16 = 0, BSP_OUT_F32 = 1 } bsp_out_dtype;
+
+/* Message for the last non-OK status returned on this host thread ("" if none). */
+const char* bsp_last_error(void);
+
+/* Library ABI version (major*100 + minor). */
+int bsp_version(void);
+
+/* Bytes of the NVFP4 scale buffer for `rows` x `K`: ceil(rows/128)*128 * ceil(K/64)*4.
+ * [FV-NV] _nvfp4_quantize: swizzled layouts pad the rows to the 128-row tile and the scales keep
+ * the padded rows; the shape kernel gives (rows, (K+15)//16) scale bytes. */
+int bsp_nvfp4_sf_bytes(int64_t rows, int64_t K, int64_t* bytes);
+
+/* a1 -- weight global scale. [FV-QAT] convert_model_to_fp4: gsf = (448*6) / amax(|W|) with NaN/inf
+ * replaced first (NaN -> 0, +-inf -> +-largest finite bf16); [SGL] _quantize_weight_nvfp4: gsf = 1
+ * when amax == 0. Writes three device fp32 scalars: amax, gsf = fl32(2688/amax) and
+ * inv_gsf = fl32(1/gsf) (the fp32 weight alpha of [FV-NV] convert_model_to_nvfp4).
+ * w: device bf16 [rows, K], row stride ld. rows or K may be 0 (then amax = 0, gsf = 1). */
+int bsp_nvfp4_global_sf(const void* w_bf16, int64_t rows, int64_t K, int64_t ld,
+                        float* gsf_dev, float* inv_gsf_dev, float* amax_dev, void* stream);
+
+/* a2 -- NVFP4 quantize. [FV-NV] _nvfp4_quantize / module docstring: e2m1 values, one e4m3 scale
+ * per 16 consecutive K elements under the fp32 global scale *gsf_dev, scales in layout_128x4.
+ * Per block: a = max|x|; s = fl32(g*fl32(a*fl32(1/6))); S = e4m3(s) (nearest-even, saturate 448);
+ * r = S==0 ? 0 : fl32(g/S); q = e2m1(fl32(x*r)) (nearest-even, saturate 6, sign kept).
+ * x: device bf16 [M, K], row stride ld; K % 16 == 0.
+ * packed: device uint8 [M, K/2] (row stride K/2); byte j of a row = q[2j] | q[2j+1] << 4.
+ * sf: device uint8, bsp_nvfp4_sf_bytes(M, K) bytes, 128x4 layout: byte (r, c) at
+ *     ((r/128)*(Kp/4) + c/4)*512 + (r%32)*16 + ((r/32)%4)*4 + c%4 with Kp = ceil(K/64)*4;
+ *     rows M..Mp-1 and columns K/16..Kp-1 are written as 0x00 (zero padding, no copy of x).
+ * M == 0 is a no-op returning BSP_OK. */
+int bsp_nvfp4_quantize(const void* x_bf16, int64_t M, int64_t K, int64_t ld, const float* gsf_dev,
+                       uint8_t* packed, uint8_t* sf, void* stream);
+
+/* Load-time weight prequantization: a1 then a2 on W [N, K] ([FV-QAT] convert_model_to_fp4,
+ * [FV-NV] convert_model_to_nvfp4). Outputs as for the two calls above (gsf_dev, inv_gsf_dev and
+ * amax_dev are all required device fp32 slots; the quantize step reads *gsf_dev on the device, so
+ * nothing is synchronised). The caller may free W once the stream has passed this call. */
+int bsp_nvfp4_prequantize_weight(const void* w_bf16, int64_t N, int64_t K, int64_t ld,
+                                 uint8_t* packed, uint8_t* sf, float* gsf_dev, float* inv_gsf_dev,
+                                 float* amax_dev, void* stream);
+
+/* a3 -- alpha = fl32(1 / fl32(x_gsf * w_gsf)) on the device ([FV-QAT] NVFP4QATQuantizeMethod.apply;
+ * with the static x_gsf = 1.0 this equals [FV-NV]'s stored 1/w_gsf). */
+int bsp_nvfp4_alpha(const float* x_gsf_dev, const float* w_gsf_dev, float* alpha_dev, void* stream);
+
+/* a4 -- mm_fp4: C[m, n] = alpha * sum_k e2m1(A[m,k])*e4m3(SA[m,k/16]) * e2m1(B[n,k])*e4m3(SB[n,k/16]),
+ * fp32 accumulation, fp32 alpha from *alpha_dev, result rounded to bf16 (nearest-even) or stored
+ * as fp32. [FV-NV] _mm_fp4 / [FV-QAT] apply: the weight is passed as the transposed view of its
+ * [N, K/2] packed buffer, i.e. B here is that K-major [N, K/2] buffer.
+ * a_packed: device uint8 [M, K/2]; a_sf: 128x4 scales for M rows (bsp_nvfp4_sf_bytes(M, K));
+ * b_packed: device uint8 [N, K/2]; b_sf: 128x4 scales for N rows; out: device [M, N] with row
+ * stride ldc elements (bf16 or fp32 per out_dtype). Requires K % 64 == 0; M, N arbitrary >= 0. */
+int bsp_mm_fp4(const uint8_t* a_packed, const uint8_t* a_sf, const uint8_t* b_packed,
+               const uint8_t* b_sf, const float* alpha_dev, int64_t M, int64_t N, int64_t K,
+               void* out, int64_t ldc, int out_dtype, void* stream);
+
+/* a6 -- MXFP8 quantize. [VLO] DiffusionMXFP8Config: 32 consecutive K elements share one e8m0
+ * scale (OCP MX). Es = clamp(floor(log2 amax) - 8, -127, 127); scale byte Es+127 (0x00 for an
+ * all-zero group); q = e4m3(fl32(x * 2^-Es)) (nearest-even, saturate 448, sign kept).
+ * x: device bf16 [M, K], row stride ld, K % 32 == 0. q: device uint8 [M, K] row-major.
+ * sf: device uint8 [M, K/32] row-major (the per-row (rows, ceil(K/32)) uint8 scale shape of
+ * [VLO] NPUMxfp8LinearMethod.create_weights). Also used once at load for weights ([VLO]
+ * NPUMxfp8OnlineLinearMethod.process_weights_after_loading). */
+int bsp_mxfp8_quantize(const void* x_bf16, int64_t M, int64_t K, int64_t ld, uint8_t* q,
+                       uint8_t* sf, void* stream);
+
+/* a7 -- mm_mxfp8: C[m, n] = sum_k e4m3(A[m,k])*2^(SA[m,k/32]-127) * e4m3(B[n,k])*2^(SB[n,k/32]-127),
+ * fp32 accumulation, bf16 or fp32 output ([VLO] NPUMxfp8LinearMethod._quant_matmul: per-row e8m0
+ * scales of both operands, group [1, 1, 32], output in the activation dtype).
+ * a: [M, K] e4m3, a_sf [M, K/32]; b: [N, K] e4m3 (K-major weight), b_sf [N, K/32]; out [M, N]
+ * row stride ldc. Requires K % 128 == 0. */
+int bsp_mm_mxfp8(const uint8_t* a, const uint8_t* a_sf, const uint8_t* b, const uint8_t* b_sf,
+                 int64_t M, int64_t N, int64_t K, void* out, int64_t ldc, int out_dtype,
+                 void* stream);
+
+/* GELU (tanh form) on bf16, out of place or in place: y = bf16(gelu(x)) with
+ * gelu(x) = 0.5*x*(1 + tanh(z)), z = sqrt(2/pi)*(x + 0.044715*x^3), evaluated in fp32 through the
+ * logistic form with t = exp(-2|z|) (no cancellation, no overflow); within one bf16 ulp of exact.
+ * It is the activation between fc_in and fc_out of the Wan FFN, both of which are in the NVFP4
+ * layer set of [FV-QAT] (DEFAULT_FP4_LAYERS: ffn.fc_in, ffn.fc_out).
+ * x, y: device bf16 [n], contiguous, 16-byte aligned. */
+int bsp_gelu_tanh_bf16(const void* x, void* y, int64_t n, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSP_H */

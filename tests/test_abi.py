@@ -1,0 +1,84 @@
+"""The C-ABI library loads and exports every entry point include/bsp.h declares; host-side
+argument validation returns the documented status codes before anything touches a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_scaled_precision_nvfp4_amd as bsp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    hdr = open(os.path.join(ROOT, "include", "bsp.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+(bsp_\w+)\s*\(", hdr, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = bsp.lib()
+    names = declared_symbols()
+    assert len(names) >= 11, names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(bsp.SIGNATURES), "binding signatures must cover the header exactly"
+
+
+def test_version_and_sf_bytes():
+    assert bsp.bsp_version() == 100
+    assert bsp.bsp_nvfp4_sf_bytes(32760, 5120) == 32768 * 320
+    assert bsp.bsp_nvfp4_sf_bytes(1, 16) == 128 * 4
+    assert bsp.bsp_nvfp4_sf_bytes(0, 64) == 0
+    assert bsp.bsp_nvfp4_sf_bytes(129, 80) == 256 * 8
+
+
+def _st(fn, *args):
+    st = getattr(bsp.lib(), fn)(*args)
+    return st, bsp.lib().bsp_last_error().decode()
+
+
+P = ctypes.c_void_p(16)  # never dereferenced: validation fails (or returns) before any launch
+
+
+def test_quantize_shape_errors():
+    st, msg = _st("bsp_nvfp4_quantize", P, 4, 24, 24, P, P, P, None)
+    assert st == -2 and "multiple of 16" in msg
+    st, _ = _st("bsp_nvfp4_quantize", P, 4, 32, 16, P, P, P, None)   # ld < K
+    assert st == -2
+    st, _ = _st("bsp_nvfp4_quantize", P, -1, 32, 32, P, P, P, None)
+    assert st == -1
+    st, _ = _st("bsp_nvfp4_quantize", None, 4, 32, 32, P, P, P, None)
+    assert st == -1
+    assert _st("bsp_nvfp4_quantize", None, 0, 32, 32, None, None, None, None)[0] == 0   # M == 0: no-op
+    st, _ = _st("bsp_mxfp8_quantize", P, 4, 48, 48, P, P, None)
+    assert st == -2
+
+
+def test_gemm_shape_and_dtype_errors():
+    st, msg = _st("bsp_mm_fp4", P, P, P, P, P, 8, 8, 96, P, 8, 0, None)
+    assert st == -2 and "multiple of 64" in msg
+    st, _ = _st("bsp_mm_fp4", P, P, P, P, P, 8, 8, 128, P, 8, 7, None)
+    assert st == -3
+    st, _ = _st("bsp_mm_fp4", P, P, P, P, P, 8, 16, 128, P, 8, 0, None)   # ldc < N
+    assert st == -2
+    assert _st("bsp_mm_fp4", None, None, None, None, None, 0, 8, 128, None, 8, 0, None)[0] == 0
+    st, _ = _st("bsp_mm_mxfp8", P, P, P, P, 8, 8, 64, P, 8, 0, None)
+    assert st == -2
+    st, _ = _st("bsp_mm_fp4", None, P, P, P, P, 8, 8, 128, P, 8, 0, None)
+    assert st == -1
+
+
+def test_prequantize_and_alpha_null_checks():
+    assert _st("bsp_nvfp4_prequantize_weight", P, 8, 40, 40, P, P, P, P, P, None)[0] == -2
+    assert _st("bsp_nvfp4_alpha", None, P, P, None)[0] == -1
+    assert _st("bsp_nvfp4_global_sf", P, 2, 8, 8, None, P, P, None)[0] == -1
+    assert _st("bsp_gelu_tanh_bf16", P, P, -1, None)[0] == -1
+
+
+def test_python_binding_rejects_bad_inputs_before_the_library():
+    import torch
+    with pytest.raises(TypeError):
+        bsp.bsp_nvfp4_quantize(torch.zeros(4, 16, dtype=torch.int32), torch.ones(1))
+    with pytest.raises(ValueError):
+        bsp.bsp_nvfp4_quantize(torch.zeros(4, 16, dtype=torch.bfloat16), torch.ones(1))  # CPU tensor

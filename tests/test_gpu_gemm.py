@@ -1,0 +1,176 @@
+"""GPU parity of mm_fp4 and mm_mxfp8 against the oracle's fp64 GEMM of the same operand bytes.
+
+Bar: fp32 output relative Frobenius error <= 1e-3; bf16 output relative Frobenius error against
+the bf16-rounded reference <= 1e-3 and max |C - ref| <= 8e-3 * max |ref|. Small and ragged
+shapes compare every element; the Wan-shaped configurations run at full size in the bench's
+launch configuration and compare sampled entries (plus corners and ragged tails).
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_precision_nvfp4_amd as bsp
+import workloads as W
+from oracle import activations as A
+from oracle import mxfp8 as X
+from oracle import nvfp4 as N
+from tests.gpu_util import (assert_gemm_bf16, assert_gemm_f32, dev_bf16, dev_u8, gather, host_bits,
+                            host_u8, sample_entries, say, scalar, tensor_bits)
+
+pytestmark = pytest.mark.gpu
+f32 = np.float32
+
+
+def _rand_nvfp4_operand(rng, rows, k):
+    packed = rng.integers(0, 256, size=(rows, k // 2)).astype(np.uint8)
+    rp, cp = N.sf_padded_shape(rows, k)
+    lin = np.zeros((rp, cp), dtype=np.uint8)
+    lin[:rows, : k // 16] = rng.integers(0, 0x7F, size=(rows, k // 16))   # incl. subnormal scales
+    return packed, N.swizzle_128x4(lin)
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 64, 64), (77, 200, 192), (256, 256, 512), (300, 384, 128),
+                                   (513, 130, 256), (64, 1000, 64)])
+def test_mm_fp4_random_operands_all_elements(m, n, k):
+    say("mm_fp4 random", m, n, k)
+    rng = np.random.default_rng(m * 7 + n * 3 + k)
+    pa, sa = _rand_nvfp4_operand(rng, m, k)
+    pb, sb = _rand_nvfp4_operand(rng, n, k)
+    al = f32(rng.uniform(0.01, 2.0))
+    ref = N.mm_fp4(pa, sa, pb, sb, al, m, n, k)
+    args = (dev_u8(pa), dev_u8(sa), dev_u8(pb), dev_u8(sb), scalar(al))
+    c32 = bsp.bsp_mm_fp4(*args, out_dtype=torch.float32).cpu().numpy().astype(np.float64)
+    assert_gemm_f32(c32, ref, f"random {m}x{n}x{k}")
+    c16 = bsp.bsp_mm_fp4(*args, out_dtype=torch.bfloat16).float().cpu().numpy().astype(np.float64)
+    assert_gemm_bf16(c16, ref, f"random {m}x{n}x{k}")
+    # the fp32 result should be far inside the budget: the products are exact in fp16
+    assert np.linalg.norm(c32 - ref) <= 1e-5 * np.linalg.norm(ref)
+
+
+def test_mm_fp4_output_stride_and_tiny_config():
+    """Tiny NVFP4 linear (128x256x512): quantize both on the GPU, GEMM into a strided output."""
+    xb, wb = tensor_bits(1, "X"), tensor_bits(1, "W")
+    x, w = dev_bf16(xb), dev_bf16(wb)
+    pw, sw, gw, inv, _ = bsp.bsp_nvfp4_prequantize_weight(w)
+    one = scalar(1.0)
+    px, sx = bsp.bsp_nvfp4_quantize(x, one)
+    alpha = bsp.bsp_nvfp4_alpha(one, gw)
+    rg = N.global_sf(wb)[0]
+    rpx, rsx = N.quantize(xb, f32(1.0))
+    rpw, rsw = N.quantize(wb, rg)
+    assert np.array_equal(host_u8(px), rpx) and np.array_equal(host_u8(pw), rpw)
+    ref = N.mm_fp4(rpx, rsx, rpw, rsw, N.alpha(1.0, rg), 128, 256, 512)
+    big = torch.full((128, 300), float("nan"), dtype=torch.bfloat16, device="cuda")
+    out = big[:, 8:264]
+    bsp.bsp_mm_fp4(px, sx, pw, sw, alpha, out=out)
+    c = out.float().cpu().numpy().astype(np.float64)
+    assert_gemm_bf16(c, ref, "tiny config")
+    b = big.float().cpu().numpy()
+    assert np.all(np.isnan(b[:, :8])) and np.all(np.isnan(b[:, 264:]))   # nothing written outside
+    # and the layer output is close to the bf16 product it stands for (sanity of the whole chain)
+    full = W.bf16_bits_to_f32(xb).astype(np.float64) @ W.bf16_bits_to_f32(wb).astype(np.float64).T
+    assert np.linalg.norm(c - full) / np.linalg.norm(full) < 0.15
+
+
+def _linear_full_size(xb_dev, w_bits, name, seed, gsf_x=1.0):
+    """Quantize X (static gsf) and prequantize W on the GPU, GEMM at full size, check sampled
+    entries against the oracle on the GPU's operand bytes (which are themselves checked on
+    sampled rows against the oracle)."""
+    m, k = xb_dev.shape
+    n = w_bits.shape[0]
+    w = dev_bf16(w_bits)
+    pw, sw, gw, _, _ = bsp.bsp_nvfp4_prequantize_weight(w)
+    del w
+    gx = scalar(gsf_x)
+    px, sx = bsp.bsp_nvfp4_quantize(xb_dev, gx)
+    alpha = bsp.bsp_nvfp4_alpha(gx, gw)
+    c = bsp.bsp_mm_fp4(px, sx, pw, sw, alpha)
+    torch.cuda.synchronize()
+    rows, cols = sample_entries(m, n, 3000, seed)
+    got = gather(c, rows, cols)
+    pxh, sxh, pwh, swh = host_u8(px), host_u8(sx).ravel(), host_u8(pw), host_u8(sw).ravel()
+    rg = N.global_sf(w_bits)[0]
+    assert gw.item() == rg
+    ur = np.unique(rows)
+    xrows = host_bits(xb_dev[torch.from_numpy(ur).cuda()])
+    rp, _ = N.quantize(xrows, f32(gsf_x), layout="linear")
+    assert np.array_equal(pxh[ur], rp), "activation bytes differ from the oracle"
+    ref = N.mm_fp4_entries(pxh, sxh, pwh, swh, N.alpha(gsf_x, rg), m, n, k, rows, cols)
+    assert_gemm_bf16(got, ref, name)
+    return c
+
+
+@pytest.mark.parametrize("cfg", [2, 4])
+def test_mm_fp4_full_size_linear(cfg):
+    xb = tensor_bits(cfg, "X")
+    x = dev_bf16(xb)
+    wname = "W" if cfg == 2 else "W3"       # cfg 4: to_q 5120x5120
+    say("full-size linear cfg", cfg, xb.shape, wname)
+    _linear_full_size(x, tensor_bits(cfg, wname), f"cfg{cfg} {wname}", seed=cfg)
+
+
+@pytest.mark.parametrize("cfg", [3, 4])
+def test_ffn_chain_full_size(cfg):
+    """fc_in -> GELU -> quantize H -> fc_out at full size; each stage checked against the oracle
+    applied to the bytes the previous GPU stage produced."""
+    xb = tensor_bits(cfg, "X")
+    say("ffn chain cfg", cfg)
+    y = _linear_full_size(dev_bf16(xb), tensor_bits(cfg, "W"), f"cfg{cfg} fc_in", seed=10 + cfg)
+    h = bsp.bsp_gelu_tanh_bf16(y)
+    rows = np.unique(np.random.default_rng(cfg).integers(0, y.shape[0], 16))
+    ri = torch.from_numpy(rows).cuda()
+    yh, hh = host_bits(y[ri]), host_bits(h[ri])
+    ref_h = A.gelu_tanh_bf16_bits(yh)
+    gv, rv = W.bf16_bits_to_f32(hh).astype(np.float64), W.bf16_bits_to_f32(ref_h).astype(np.float64)
+    assert np.all(np.abs(gv - rv) <= np.abs(rv) * 2.0 ** -7 + 2.0 ** -126)
+    del y
+    _linear_full_size(h, tensor_bits(cfg, "W2"), f"cfg{cfg} fc_out", seed=20 + cfg)
+
+
+def test_mm_fp4_full_size_fp32_output():
+    xb = tensor_bits(2, "X")
+    wb = tensor_bits(2, "W")
+    px, sx = bsp.bsp_nvfp4_quantize(dev_bf16(xb), scalar(1.0))
+    pw, sw, gw, _, _ = bsp.bsp_nvfp4_prequantize_weight(dev_bf16(wb))
+    alpha = bsp.bsp_nvfp4_alpha(scalar(1.0), gw)
+    c = bsp.bsp_mm_fp4(px, sx, pw, sw, alpha, out_dtype=torch.float32)
+    rows, cols = sample_entries(xb.shape[0], wb.shape[0], 3000, 99)
+    ref = N.mm_fp4_entries(host_u8(px), host_u8(sx).ravel(), host_u8(pw), host_u8(sw).ravel(),
+                           alpha.item(), xb.shape[0], wb.shape[0], xb.shape[1], rows, cols)
+    assert_gemm_f32(gather(c, rows, cols), ref, "cfg2 fp32")
+
+
+# ------------------------------------------------------------------------------------------ MXFP8
+def _rand_mx_operand(rng, rows, k):
+    q = rng.integers(0, 256, size=(rows, k)).astype(np.uint8)
+    q[(q & 0x7F) == 0x7F] = 0x3F                                   # no NaN codes
+    s = rng.integers(110, 140, size=(rows, k // 32)).astype(np.uint8)
+    return q, s
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 64, 128), (77, 200, 256), (256, 256, 512), (300, 130, 384)])
+def test_mm_mxfp8_random_operands_all_elements(m, n, k):
+    say("mm_mxfp8 random", m, n, k)
+    rng = np.random.default_rng(m + n + k)
+    qa, sa = _rand_mx_operand(rng, m, k)
+    qb, sb = _rand_mx_operand(rng, n, k)
+    ref = X.mm_mxfp8(qa, sa, qb, sb, m, n, k)
+    args = (dev_u8(qa), dev_u8(sa), dev_u8(qb), dev_u8(sb))
+    c32 = bsp.bsp_mm_mxfp8(*args, out_dtype=torch.float32).cpu().numpy().astype(np.float64)
+    assert_gemm_f32(c32, ref, f"mx random {m}x{n}x{k}")
+    c16 = bsp.bsp_mm_mxfp8(*args).float().cpu().numpy().astype(np.float64)
+    assert_gemm_bf16(c16, ref, f"mx random {m}x{n}x{k}")
+
+
+def test_mm_mxfp8_full_size():
+    xb, wb = tensor_bits(5, "X"), tensor_bits(5, "W")
+    qx, sx = bsp.bsp_mxfp8_quantize(dev_bf16(xb))
+    qw, sw = bsp.bsp_mxfp8_quantize(dev_bf16(wb))      # online weight conversion
+    c = bsp.bsp_mm_mxfp8(qx, sx, qw, sw)
+    m, n, k = xb.shape[0], wb.shape[0], xb.shape[1]
+    rows, cols = sample_entries(m, n, 3000, 5)
+    ur = np.unique(rows)
+    rq, rs = X.quantize(xb[ur])
+    assert np.array_equal(host_u8(qx[torch.from_numpy(ur).cuda()]), rq)
+    ref = X.mm_mxfp8_entries(host_u8(qx), host_u8(sx), host_u8(qw), host_u8(sw), rows, cols)
+    assert_gemm_bf16(gather(c, rows, cols), ref, "cfg5 mxfp8")
