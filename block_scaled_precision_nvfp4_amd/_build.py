@@ -16,6 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(CSRC, "_build")
 LIB = os.path.join(HERE, "libbsp.so")
 SOURCES = ["api.hip", "quantize.hip", "gemm_fp4.hip", "gemm_mxfp8.hip"]
+HEADERS = ["common.hpp", "gemm_common.hpp"]
 
 # IEEE fp32 everywhere: no contraction into FMA, correctly rounded division, no fast-math; packed
 # fp32 VALU ops disabled (they are not needed and have misbehaved on this hardware).

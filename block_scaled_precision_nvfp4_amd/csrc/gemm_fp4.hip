@@ -7,76 +7,76 @@
 // e4m3 scale needs up to 6 significant bits, so no 4/6/8-bit MFMA operand can hold it exactly.
 // Every such product is exact in fp16, so the packed FP4 bytes and the scale bytes are staged in
 // LDS as they are (0.5 byte per element), and each wave dequantizes its own fragments in
-// registers (v_cvt_scalef32_pk_f16_fp4 then a packed f16 multiply by the decoded scale) right
-// before v_mfma_f32_32x32x16_f16.
+// registers (v_cvt_scalef32_pk_f16_fp4 with unit scale, then a packed f16 multiply by the decoded
+// e4m3 scale; the convert's own scale operand only honours the exponent) right before
+// v_mfma_f32_32x32x16_f16.
 //
 // Tiling: a 256-thread workgroup owns a 256x256 C tile; each of its 4 waves a 128x128 quarter as
-// 4x4 MFMA 32x32 tiles (256 fp32 accumulators per lane). K advances 64 per stage; one stage of
-// LDS holds 256 rows x 32 bytes of packed A and of B plus the two 512-byte 128x4 scale tiles of
-// each operand, double-buffered with register prefetch of the next stage. In the 128x4 layout the
-// four scales of a row for a 64-K step are one dword, so the scale tiles are copied verbatim.
+// 4x4 MFMA 32x32 tiles (256 fp32 accumulators per lane). K advances 128 per stage: one stage of
+// LDS holds 256 rows x 64 bytes of packed A and of B (four 16-byte chunks per row, XOR-swizzled
+// by row for conflict-free 16-byte reads) plus the 128x4 scale tiles (two 128-row tiles x two
+// 4-column groups per operand, copied verbatim: in that layout a row's four scales for 64 K are
+// one dword). Two stages, register prefetch of the next stage's global data. K % 128 == 64 ends
+// with a zero-filled half stage.
+//
+// Lane (i, h) of a wave (i = lane % 32, h = lane / 32) owns, per stage, the 32 bytes of row i at
+// K [64h, 64h + 64): 8 MFMA sub-steps of K 16, sub-step j using its elements 64h + 8j .. + 7
+// (both operands use the same K placement, so the MFMA pairs them correctly) with scale byte j/2
+// of the row's scale dword for column group h. Dequantization of sub-step j+1 is interleaved
+// between the MFMA pairs of sub-step j (explicit scheduling fences), so the VALU work issues while
+// the matrix core is busy instead of in bursts that in-order issue would serialize.
+//
 // The MFMA's A operand is the weight fragment and its B operand the activation fragment, so a
-// lane's accumulators hold four consecutive output columns of one output row per group and the
-// epilogue stores 4 bf16 (8 bytes) per lane per group.
-#include "common.hpp"
+// lane's accumulators hold four consecutive output columns of one output row per group (8-byte
+// bf16 stores).
+#include "gemm_common.hpp"
 
 namespace bsp {
-
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
 namespace fp4 {
 
-constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int BM = 256, BN = 256, BK = 128;
 
 struct Stage {
-  u32x4 a[BM * 2];  // packed A: row r holds its 32 bytes as two 16-byte halves (swizzled)
-  u32x4 b[BN * 2];  // packed B (weights), same
-  u32x4 sa[64];     // 2 scale tiles x 512 B (rows 0-127, 128-255 of the tile) for this K step
-  u32x4 sb[64];
+  u32x4 a[BM * 4];  // packed A: row r, 16-byte chunk c (K [32c, 32c+32) of the stage) at chunk_slot
+  u32x4 b[BN * 4];  // packed B (weights), same
+  u32x4 sa[128];    // scale tiles: (row tile rt, column group cg) at [(rt * 2 + cg) * 32 .. +32)
+  u32x4 sb[128];
 };
 
-__device__ __forceinline__ int half_slot(int row, int h) { return row * 2 + (h ^ ((row >> 2) & 1)); }
+__device__ __forceinline__ int chunk_slot(int row, int c) { return row * 4 + (c ^ ((row >> 1) & 3)); }
 
-// scale word (4 e4m3 bytes for the 64-K step) of tile-local row r from a staged pair of 128x4 tiles
-__device__ __forceinline__ uint32_t scale_word(const u32x4* tiles, int r) {
+// scale dword of tile-local row r for column group cg (K [64cg, 64cg + 64) of the stage)
+__device__ __forceinline__ uint32_t scale_word(const u32x4* tiles, int r, int cg) {
   const uint32_t* w = reinterpret_cast<const uint32_t*>(tiles);
-  return w[(r >> 7) * 128 + (r & 31) * 4 + ((r >> 5) & 3)];
+  return w[((r >> 7) * 2 + cg) * 128 + (r & 31) * 4 + ((r >> 5) & 3)];
 }
 
-// 8 e2m1 values (one dword) times their e4m3 scale -> 8 fp16 (exact)
-__device__ __forceinline__ f16x8 dequant8(uint32_t w, uint32_t sbyte) {
-  const float s = e4m3_decode_pos(sbyte);
-#if BSP_CVT_FULL_SCALE
-  f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, 0);
-  f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, 1);
-  f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, 2);
-  f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, 3);
-  return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-#else
+__device__ __forceinline__ f16x2 scale_pair(uint32_t sbyte) {
+  const _Float16 hs = (_Float16)e4m3_decode_pos(sbyte);  // e4m3 values are exact in fp16
+  return f16x2{hs, hs};
+}
+
+// 8 e2m1 values (one dword) times their e4m3 scale (as an f16 pair) -> 8 fp16 (exact)
+__device__ __forceinline__ f16x8 dequant8(uint32_t w, f16x2 s2) {
   f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
   f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
   f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
   f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
-  const _Float16 hs = (_Float16)s;  // e4m3 values are exact in fp16
-  f16x2 s2 = {hs, hs};
   p0 *= s2; p1 *= s2; p2 *= s2; p3 *= s2;
   return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-#endif
 }
 
 __device__ __forceinline__ uint32_t comp(const u32x4& v, int j) {
   return j == 0 ? v.x : (j == 1 ? v.y : (j == 2 ? v.z : v.w));
 }
 
-// Next stage's global data held in registers while the current stage computes. Named fields
-// (no arrays) so that the whole struct is promoted to registers.
+// Next stage's global data, held in registers while the current stage computes. Named fields
+// (no arrays) so that the struct is promoted to registers.
 struct Prefetch {
-  u32x4 a0, a1, b0, b1, s;  // s: one scale chunk (threads 0-63: A, 64-127: B)
+  u32x4 a0, a1, a2, a3, b0, b1, b2, b3, s;
 };
 
+// Chunk q = t + 256 i of an operand: row q / 4, 16-byte chunk q % 4 (64 contiguous bytes per row).
 __device__ __forceinline__ void load_stage(Prefetch& pf, const uint8_t* __restrict__ A,
                                            const uint8_t* __restrict__ B,
                                            const uint8_t* __restrict__ SA,
@@ -85,54 +85,68 @@ __device__ __forceinline__ void load_stage(Prefetch& pf, const uint8_t* __restri
                                            int64_t mtiles128, int64_t ntiles128, int64_t groups,
                                            int t) {
   const int64_t hk = K / 2;
-  // chunk c = t (+256): row c / 2, 16-byte half c % 2 of the row's 32 bytes for this K step
-  const int row = t >> 1, h = t & 1;
-  int64_t ga0 = m0 + row; ga0 = ga0 < M ? ga0 : M - 1;
-  int64_t ga1 = m0 + row + 128; ga1 = ga1 < M ? ga1 : M - 1;
-  int64_t gb0 = n0 + row; gb0 = gb0 < N ? gb0 : N - 1;
-  int64_t gb1 = n0 + row + 128; gb1 = gb1 < N ? gb1 : N - 1;
-  const int64_t koff = kt * 32 + h * 16;
-  pf.a0 = *reinterpret_cast<const u32x4*>(A + ga0 * hk + koff);
-  pf.a1 = *reinterpret_cast<const u32x4*>(A + ga1 * hk + koff);
-  pf.b0 = *reinterpret_cast<const u32x4*>(B + gb0 * hk + koff);
-  pf.b1 = *reinterpret_cast<const u32x4*>(B + gb1 * hk + koff);
-  // threads 0-63 fetch A's two scale tiles, 64-127 B's; threads 128-255 repeat the same
-  // addresses (an unconditional load keeps the prefetch in registers) and never store them
-  const int which = (t >> 6) & 1, tt = (t >> 5) & 1, q = t & 31;
+  const int row = t >> 2, c = t & 3;
+  const int64_t koff = kt * 64 + c * 16;
+  // K % 128 == 64: the last stage has only its first 64 K; the rest is zero-filled (zero values
+  // and zero scales contribute nothing)
+  const bool tail = kt * 128 + 64 >= K;
+  const bool live = !(tail && c >= 2);
+  int64_t r;
+#define BSP_LD(dst, base, r0, lim, rr)                                  \
+  r = (r0) + (rr); r = r < (lim) ? r : (lim) - 1;                       \
+  dst = live ? *reinterpret_cast<const u32x4*>((base) + r * hk + koff) : u32x4{0u, 0u, 0u, 0u};
+  BSP_LD(pf.a0, A, m0, M, row)
+  BSP_LD(pf.a1, A, m0, M, row + 64)
+  BSP_LD(pf.a2, A, m0, M, row + 128)
+  BSP_LD(pf.a3, A, m0, M, row + 192)
+  BSP_LD(pf.b0, B, n0, N, row)
+  BSP_LD(pf.b1, B, n0, N, row + 64)
+  BSP_LD(pf.b2, B, n0, N, row + 128)
+  BSP_LD(pf.b3, B, n0, N, row + 192)
+#undef BSP_LD
+  // threads 0-127: A's scale tiles, 128-255: B's; (row tile, column group, 16-byte piece)
+  const int which = t >> 7, rt = (t >> 6) & 1, cg = (t >> 5) & 1, q = t & 31;
   const int64_t r0 = which ? n0 / 128 : m0 / 128;
   const int64_t nt = which ? ntiles128 : mtiles128;
-  int64_t rt = r0 + tt; rt = rt < nt ? rt : nt - 1;
-  pf.s = *reinterpret_cast<const u32x4*>((which ? SB : SA) + (rt * groups + kt) * 512 + q * 16);
+  int64_t tr = r0 + rt; tr = tr < nt ? tr : nt - 1;
+  pf.s = (tail && cg == 1)
+             ? u32x4{0u, 0u, 0u, 0u}
+             : *reinterpret_cast<const u32x4*>((which ? SB : SA) + (tr * groups + kt * 2 + cg) * 512 + q * 16);
 }
 
 __device__ __forceinline__ void store_stage(Stage& st, const Prefetch& pf, int t) {
-  const int row = t >> 1, h = t & 1;
-  st.a[half_slot(row, h)] = pf.a0;
-  st.a[half_slot(row + 128, h)] = pf.a1;
-  st.b[half_slot(row, h)] = pf.b0;
-  st.b[half_slot(row + 128, h)] = pf.b1;
-  if (t < 64)
+  const int row = t >> 2, c = t & 3;
+  st.a[chunk_slot(row, c)] = pf.a0;
+  st.a[chunk_slot(row + 64, c)] = pf.a1;
+  st.a[chunk_slot(row + 128, c)] = pf.a2;
+  st.a[chunk_slot(row + 192, c)] = pf.a3;
+  st.b[chunk_slot(row, c)] = pf.b0;
+  st.b[chunk_slot(row + 64, c)] = pf.b1;
+  st.b[chunk_slot(row + 128, c)] = pf.b2;
+  st.b[chunk_slot(row + 192, c)] = pf.b3;
+  if (t < 128)
     st.sa[t] = pf.s;
-  else if (t < 128)
-    st.sb[t - 64] = pf.s;
+  else
+    st.sb[t - 128] = pf.s;
 }
 
 template <bool OUT_F32>
 __global__ __launch_bounds__(256, 1) void mm_fp4_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ SB, const float* __restrict__ alpha_ptr, int64_t M, int64_t N,
-    int64_t K, void* __restrict__ out, int64_t ldc, int ntn, bool vec_store) {
+    int64_t K, void* __restrict__ out, int64_t ldc, int ntm, int ntn, bool vec_store) {
   __shared__ Stage st[2];
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int li = lane & 31, h = lane >> 5;
 
-  const int bid = blockIdx.x;
-  const int64_t m0 = (int64_t)(bid / ntn) * BM;
-  const int64_t n0 = (int64_t)(bid % ntn) * BN;
-  const int64_t nk = K / BK;
-  const int64_t groups = nk;  // 128x4 column groups = K/64
+  int tm, tn;
+  tile_coords(blockIdx.x, ntm, ntn, tm, tn);
+  const int64_t m0 = (int64_t)tm * BM;
+  const int64_t n0 = (int64_t)tn * BN;
+  const int64_t nk = (K + BK - 1) / BK;
+  const int64_t groups = K / 64;  // 128x4 column groups of the scale matrices
   const int64_t mtiles128 = (M + 127) / 128, ntiles128 = (N + 127) / 128;
 
   f32x16 acc[4][4];
@@ -149,80 +163,55 @@ __global__ __launch_bounds__(256, 1) void mm_fp4_kernel(
   for (int64_t kt = 0; kt < nk; ++kt) {
     const int cur = (int)(kt & 1);
     if (kt + 1 < nk) load_stage(pf, A, B, SA, SB, M, N, K, m0, n0, kt + 1, mtiles128, ntiles128, groups, t);
-
     const Stage& s = st[cur];
-    u32x4 pa[4], pb[4];
+
+    u32x4 pa[2][4], pb[2][4];
     uint32_t wa[4], wb[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int ra = wm * 128 + i * 32 + li;
       const int rb = wn * 128 + i * 32 + li;
-      pa[i] = s.a[half_slot(ra, h)];
-      pb[i] = s.b[half_slot(rb, h)];
-      wa[i] = scale_word(s.sa, ra);
-      wb[i] = scale_word(s.sb, rb);
+      pa[0][i] = s.a[chunk_slot(ra, 2 * h)];
+      pa[1][i] = s.a[chunk_slot(ra, 2 * h + 1)];
+      pb[0][i] = s.b[chunk_slot(rb, 2 * h)];
+      pb[1][i] = s.b[chunk_slot(rb, 2 * h + 1)];
+      wa[i] = scale_word(s.sa, ra, h);
+      wb[i] = scale_word(s.sb, rb, h);
+    }
+
+    f16x8 xa[2][4], xb[2][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      xa[0][i] = dequant8(pa[0][i].x, scale_pair(wa[i] & 0xFFu));
+      xb[0][i] = dequant8(pb[0][i].x, scale_pair(wb[i] & 0xFFu));
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      __builtin_amdgcn_sched_barrier(0);  // keep each K sub-step's dequant next to its MFMAs
-      const int sh = 8 * (2 * h + (j >> 1));  // scale byte of this lane's 8 elements
-      f16x8 xa[4], xb[4];
+    for (int j = 0; j < 8; ++j) {
+      const int cb = j & 1, nb = cb ^ 1;
+      const int jn = j + 1;                        // next sub-step
+      const int sh = 8 * (jn >> 1);                // its scale byte
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        xa[i] = dequant8(comp(pa[i], j), (wa[i] >> sh) & 0xFFu);
-        xb[i] = dequant8(comp(pb[i], j), (wb[i] >> sh) & 0xFFu);
+      for (int q = 0; q < 8; ++q) {
+        __builtin_amdgcn_sched_barrier(0);
+        const int n = q >> 1, m = 2 * (q & 1);
+        acc[n][m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xb[cb][n], xa[cb][m], acc[n][m], 0, 0, 0);
+        acc[n][m + 1] =
+            __builtin_amdgcn_mfma_f32_32x32x16_f16(xb[cb][n], xa[cb][m + 1], acc[n][m + 1], 0, 0, 0);
+        if (jn < 8) {                              // dequantize one fragment of sub-step j+1
+          if (q < 4)
+            xa[nb][q] = dequant8(comp(pa[jn >> 2][q], jn & 3), scale_pair((wa[q] >> sh) & 0xFFu));
+          else
+            xb[nb][q - 4] = dequant8(comp(pb[jn >> 2][q - 4], jn & 3), scale_pair((wb[q - 4] >> sh) & 0xFFu));
+        }
       }
-#pragma unroll
-      for (int n = 0; n < 4; ++n)
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-          acc[n][m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xb[n], xa[m], acc[n][m], 0, 0, 0);
     }
+    __builtin_amdgcn_sched_barrier(0);
     if (kt + 1 < nk) store_stage(st[cur ^ 1], pf, t);
     __syncthreads();
   }
 
-  // epilogue: D[n][m] per 32x32 tile; lane holds column m = li and rows n = 8*(r/4) + 4*h + r%4
-  const float alpha = *alpha_ptr;
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int64_t gm = m0 + wm * 128 + m * 32 + li;
-    if (gm >= M) continue;
-#pragma unroll
-    for (int n = 0; n < 4; ++n) {
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int64_t gn = n0 + wn * 128 + n * 32 + 8 * b + 4 * h;
-        float v0 = alpha * acc[n][m][4 * b + 0];
-        float v1 = alpha * acc[n][m][4 * b + 1];
-        float v2 = alpha * acc[n][m][4 * b + 2];
-        float v3 = alpha * acc[n][m][4 * b + 3];
-        if (OUT_F32) {
-          float* o = static_cast<float*>(out) + gm * ldc + gn;
-          if (vec_store && gn + 3 < N) {
-            *reinterpret_cast<float4*>(o) = make_float4(v0, v1, v2, v3);
-          } else {
-            if (gn + 0 < N) o[0] = v0;
-            if (gn + 1 < N) o[1] = v1;
-            if (gn + 2 < N) o[2] = v2;
-            if (gn + 3 < N) o[3] = v3;
-          }
-        } else {
-          uint16_t* o = static_cast<uint16_t*>(out) + gm * ldc + gn;
-          uint32_t b0 = f32_to_bf16_rne(v0), b1 = f32_to_bf16_rne(v1);
-          uint32_t b2 = f32_to_bf16_rne(v2), b3 = f32_to_bf16_rne(v3);
-          if (vec_store && gn + 3 < N) {
-            *reinterpret_cast<uint2*>(o) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
-          } else {
-            if (gn + 0 < N) o[0] = (uint16_t)b0;
-            if (gn + 1 < N) o[1] = (uint16_t)b1;
-            if (gn + 2 < N) o[2] = (uint16_t)b2;
-            if (gn + 3 < N) o[3] = (uint16_t)b3;
-          }
-        }
-      }
-    }
-  }
+  store_wave_tile<OUT_F32>(acc, *alpha_ptr, m0 + wm * 128, n0 + wn * 128, M, N, out, ldc, vec_store,
+                           li, h);
 }
 
 }  // namespace fp4
@@ -236,10 +225,10 @@ int launch_mm_fp4(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const u
   const bool vec = (ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(out) & (4 * esz - 1)) == 0);
   if (out_dtype == BSP_OUT_F32)
     hipLaunchKernelGGL(fp4::mm_fp4_kernel<true>, dim3((unsigned)tiles), dim3(256), 0, s, a, sa, b, sb,
-                       alpha, M, N, K, out, ldc, (int)ntn, vec);
+                       alpha, M, N, K, out, ldc, (int)ntm, (int)ntn, vec);
   else
     hipLaunchKernelGGL(fp4::mm_fp4_kernel<false>, dim3((unsigned)tiles), dim3(256), 0, s, a, sa, b, sb,
-                       alpha, M, N, K, out, ldc, (int)ntn, vec);
+                       alpha, M, N, K, out, ldc, (int)ntm, (int)ntn, vec);
   return check_launch("bsp_mm_fp4");
 }
 

@@ -2,9 +2,12 @@
 // K elements, per row of each operand), fp32 accumulation, bf16 or fp32 output.
 // vLLM-Omni mxfp8_config.py (DiffusionMXFP8Config; NPUMxfp8LinearMethod._quant_matmul).
 //
-// The OCP MX block scale is exactly what gfx950's v_mfma_scale_f32_32x32x64_f8f6f4 consumes: each
-// lane supplies 32 consecutive K elements of one row and that group's e8m0 scale, so the format
-// maps 1:1 onto the instruction (operand format e4m3 for both sides, cbsz = blgp = 0).
+// The OCP MX block scale is exactly what gfx950's v_mfma_scale_f32_32x32x64_f8f6f4 consumes: one
+// e8m0 scale per row and 32-element K block, supplied by the lane half that owns the block (lane
+// i + 32*b for block b of row i), so the format maps 1:1 onto the instruction (operand format
+// e4m3 for both sides, cbsz = blgp = 0). With 8-bit operands each lane holds 16 elements of each
+// of the two blocks (see frag()); this placement was measured on the hardware with one-hot
+// operands and distinct per-lane scales.
 //
 // Tiling: a 256-thread workgroup owns a 256x256 C tile, each wave a 128x128 quarter (4x4 MFMA
 // 32x32 tiles). K advances 64 per stage: LDS holds 256 rows x 64 bytes of A and of B (four
@@ -70,9 +73,14 @@ __device__ __forceinline__ void store_stage(Stage& st, const Prefetch& pf, int t
   st.sb[t] = pf.sb;
 }
 
+// Operand fragment of lane half h for v_mfma_scale_f32_32x32x64_f8f6f4 with 8-bit elements: the
+// instruction takes bytes 0-15 of every lane as K elements of the first 32-element scale block and
+// bytes 16-31 as elements of the second, lane half h supplying the 16-element half h of each block
+// (and lane half h's scale applying to block h). So lane half h carries the 16-byte chunks h and
+// 2 + h of the 64-byte K step.
 __device__ __forceinline__ i32x8 frag(const u32x4* rows, int row, int h) {
-  u32x4 lo = rows[chunk_slot(row, 2 * h)];
-  u32x4 hi = rows[chunk_slot(row, 2 * h + 1)];
+  u32x4 lo = rows[chunk_slot(row, h)];
+  u32x4 hi = rows[chunk_slot(row, 2 + h)];
   return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
