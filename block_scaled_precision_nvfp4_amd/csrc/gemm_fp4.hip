@@ -34,7 +34,8 @@
 namespace bsp {
 namespace fp4 {
 
-constexpr int BM = 256, BN = 256, BK = 128;
+constexpr int BM = 256, BN = 256, BK = 128, NSTAGE = 3;
+constexpr int kLoadsPerStage = 9;  // global_load_lds instructions per wave per stage
 
 struct Stage {
   u32x4 a[BM * 4];  // packed A: row r, 16-byte chunk c (K [32c, 32c+32) of the stage) at chunk_slot
@@ -43,20 +44,22 @@ struct Stage {
   u32x4 sb[128];
 };
 
+typedef __attribute__((address_space(3))) void lds_t;
+
 __device__ __forceinline__ int chunk_slot(int row, int c) { return row * 4 + (c ^ ((row >> 1) & 3)); }
 
-// scale dword of tile-local row r for column group cg (K [64cg, 64cg + 64) of the stage)
-__device__ __forceinline__ uint32_t scale_word(const u32x4* tiles, int r, int cg) {
-  const uint32_t* w = reinterpret_cast<const uint32_t*>(tiles);
-  return w[((r >> 7) * 2 + cg) * 128 + (r & 31) * 4 + ((r >> 5) & 3)];
+// f16 pair holding (e4m3 scale byte) * 2^-8 twice, built from the bits alone: an e4m3 code c
+// (non-negative) shifted left by 7 is an f16 with exponent field e and mantissa m, i.e.
+// 2^(e-15) (1 + m/8) for e >= 1 and the f16 denormal m * 2^-17 for e == 0, which is the e4m3 value
+// times 2^-8 in both cases. The 2^-8 of each operand is undone in the epilogue (alpha * 2^16).
+__device__ __forceinline__ f16x2 scale_pair(uint32_t word, int byte) {
+  const uint32_t c = (word >> (8 * byte)) & 0x7Fu;
+  const uint32_t bits = (c << 7) | (c << 23);
+  return __builtin_bit_cast(f16x2, bits);
 }
 
-__device__ __forceinline__ f16x2 scale_pair(uint32_t sbyte) {
-  const _Float16 hs = (_Float16)e4m3_decode_pos(sbyte);  // e4m3 values are exact in fp16
-  return f16x2{hs, hs};
-}
-
-// 8 e2m1 values (one dword) times their e4m3 scale (as an f16 pair) -> 8 fp16 (exact)
+// 8 e2m1 values (one dword) times their scale pair -> 8 fp16. Exact: every product e2m1 * e4m3 *
+// 2^-8 has at most 6 significant bits and its lowest bit is >= 2^-18, within fp16's reach.
 __device__ __forceinline__ f16x8 dequant8(uint32_t w, f16x2 s2) {
   f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
   f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
@@ -70,64 +73,87 @@ __device__ __forceinline__ uint32_t comp(const u32x4& v, int j) {
   return j == 0 ? v.x : (j == 1 ? v.y : (j == 2 ? v.z : v.w));
 }
 
-// Next stage's global data, held in registers while the current stage computes. Named fields
-// (no arrays) so that the struct is promoted to registers.
-struct Prefetch {
-  u32x4 a0, a1, a2, a3, b0, b1, b2, b3, s;
-};
-
-// Chunk q = t + 256 i of an operand: row q / 4, 16-byte chunk q % 4 (64 contiguous bytes per row).
-__device__ __forceinline__ void load_stage(Prefetch& pf, const uint8_t* __restrict__ A,
-                                           const uint8_t* __restrict__ B,
-                                           const uint8_t* __restrict__ SA,
-                                           const uint8_t* __restrict__ SB, int64_t M, int64_t N,
-                                           int64_t K, int64_t m0, int64_t n0, int64_t kt,
-                                           int64_t mtiles128, int64_t ntiles128, int64_t groups,
-                                           int t) {
+// Stage kt's operand and scale bytes, global -> LDS without passing through registers
+// (global_load_lds_dwordx4: lane l of an instruction lands at the LDS base + 16 l). Each wave
+// issues 4 instructions per operand (64 chunks each) and one for a scale half. The XOR swizzle is
+// applied on the global side: LDS slot s holds row s/4, logical chunk (s%4) ^ ((row/2)%4).
+// K % 128 == 64: the last stage's second half re-reads its first half (in bounds) and the compute
+// zeroes that half's scales.
+__device__ __forceinline__ void issue_stage(Stage& st, const uint8_t* __restrict__ A,
+                                            const uint8_t* __restrict__ B,
+                                            const uint8_t* __restrict__ SA,
+                                            const uint8_t* __restrict__ SB, int64_t M, int64_t N,
+                                            int64_t K, int64_t m0, int64_t n0, int64_t kt,
+                                            int64_t mtiles128, int64_t ntiles128, int64_t groups,
+                                            int wave, int lane) {
   const int64_t hk = K / 2;
-  const int row = t >> 2, c = t & 3;
-  const int64_t koff = kt * 64 + c * 16;
-  // K % 128 == 64: the last stage has only its first 64 K; the rest is zero-filled (zero values
-  // and zero scales contribute nothing)
   const bool tail = kt * 128 + 64 >= K;
-  const bool live = !(tail && c >= 2);
-  int64_t r;
-#define BSP_LD(dst, base, r0, lim, rr)                                  \
-  r = (r0) + (rr); r = r < (lim) ? r : (lim) - 1;                       \
-  dst = live ? *reinterpret_cast<const u32x4*>((base) + r * hk + koff) : u32x4{0u, 0u, 0u, 0u};
-  BSP_LD(pf.a0, A, m0, M, row)
-  BSP_LD(pf.a1, A, m0, M, row + 64)
-  BSP_LD(pf.a2, A, m0, M, row + 128)
-  BSP_LD(pf.a3, A, m0, M, row + 192)
-  BSP_LD(pf.b0, B, n0, N, row)
-  BSP_LD(pf.b1, B, n0, N, row + 64)
-  BSP_LD(pf.b2, B, n0, N, row + 128)
-  BSP_LD(pf.b3, B, n0, N, row + 192)
-#undef BSP_LD
-  // threads 0-127: A's scale tiles, 128-255: B's; (row tile, column group, 16-byte piece)
-  const int which = t >> 7, rt = (t >> 6) & 1, cg = (t >> 5) & 1, q = t & 31;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int slot0 = (wave * 4 + i) * 64;
+    const int s = slot0 + lane;
+    const int row = s >> 2;
+    int c = (s & 3) ^ ((row >> 1) & 3);
+    c = (tail && c >= 2) ? c - 2 : c;
+    const int64_t koff = kt * 64 + c * 16;
+    int64_t ra = m0 + row; ra = ra < M ? ra : M - 1;
+    int64_t rb = n0 + row; rb = rb < N ? rb : N - 1;
+    __builtin_amdgcn_global_load_lds(A + ra * hk + koff, (lds_t*)&st.a[slot0], 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(B + rb * hk + koff, (lds_t*)&st.b[slot0], 16, 0, 0);
+  }
+  // waves 0-1: A's two 128-row scale tiles, waves 2-3: B's; slot = rt*64 + cg*32 + q
+  const int which = wave >> 1, rt = wave & 1;
+  const int cg0 = lane >> 5, q = lane & 31;
+  const int cg = (tail && cg0 == 1) ? 0 : cg0;
   const int64_t r0 = which ? n0 / 128 : m0 / 128;
   const int64_t nt = which ? ntiles128 : mtiles128;
   int64_t tr = r0 + rt; tr = tr < nt ? tr : nt - 1;
-  pf.s = (tail && cg == 1)
-             ? u32x4{0u, 0u, 0u, 0u}
-             : *reinterpret_cast<const u32x4*>((which ? SB : SA) + (tr * groups + kt * 2 + cg) * 512 + q * 16);
+  const uint8_t* src = (which ? SB : SA) + (tr * groups + kt * 2 + cg) * 512 + q * 16;
+  __builtin_amdgcn_global_load_lds(src, (lds_t*)(which ? &st.sb[rt * 64] : &st.sa[rt * 64]), 16, 0, 0);
 }
 
-__device__ __forceinline__ void store_stage(Stage& st, const Prefetch& pf, int t) {
-  const int row = t >> 2, c = t & 3;
-  st.a[chunk_slot(row, c)] = pf.a0;
-  st.a[chunk_slot(row + 64, c)] = pf.a1;
-  st.a[chunk_slot(row + 128, c)] = pf.a2;
-  st.a[chunk_slot(row + 192, c)] = pf.a3;
-  st.b[chunk_slot(row, c)] = pf.b0;
-  st.b[chunk_slot(row + 64, c)] = pf.b1;
-  st.b[chunk_slot(row + 128, c)] = pf.b2;
-  st.b[chunk_slot(row + 192, c)] = pf.b3;
-  if (t < 128)
-    st.sa[t] = pf.s;
-  else
-    st.sb[t - 128] = pf.s;
+// s_waitcnt vmcnt(n) (n < 16), leaving lgkmcnt and expcnt unconstrained
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((n & 0xF) | (0x7 << 4) | (0xF << 8));
+}
+
+// A wave's fragments of one stage: packed bytes for both 16-byte chunks of its K half and the
+// scale dwords of its 4+4 rows (rows r, r+32, r+64, r+96 of a 128x4 tile are one 16-byte run).
+struct Frags {
+  u32x4 pa[2][4], pb[2][4];
+  u32x4 wa, wb;
+};
+
+// Chunk `cc` (0: sub-steps 0-3, 1: sub-steps 4-7) of a wave's packed fragments of one stage.
+__device__ __forceinline__ void read_chunk(Frags& f, const Stage& s, int cc, int wm, int wn, int li,
+                                           int h) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ra = wm * 128 + i * 32 + li;
+    const int rb = wn * 128 + i * 32 + li;
+    f.pa[cc][i] = s.a[chunk_slot(ra, 2 * h + cc)];
+    f.pb[cc][i] = s.b[chunk_slot(rb, 2 * h + cc)];
+  }
+}
+
+// First chunk and the scale dwords (the second chunk is read during sub-steps 1-2, spreading the
+// LDS traffic over the stage).
+__device__ __forceinline__ void read_frags(Frags& f, const Stage& s, int wm, int wn, int li, int h,
+                                           bool zero_half) {
+  read_chunk(f, s, 0, wm, wn, li, h);
+  f.wa = s.sa[(wm * 2 + h) * 32 + li];
+  f.wb = s.sb[(wn * 2 + h) * 32 + li];
+  if (zero_half) {  // K % 128 == 64 tail: this lane half's K range is past the end
+    f.wa = u32x4{0u, 0u, 0u, 0u};
+    f.wb = u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+// dequantize fragment q (0-3: A row tiles, 4-7: B row tiles) of sub-step j from f
+__device__ __forceinline__ f16x8 frag_deq(const Frags& f, int q, int j) {
+  if (q < 4) return dequant8(comp(f.pa[j >> 2][q], j & 3), scale_pair(comp(f.wa, q), j >> 1));
+  return dequant8(comp(f.pb[j >> 2][q - 4], j & 3), scale_pair(comp(f.wb, q - 4), j >> 1));
 }
 
 template <bool OUT_F32>
@@ -135,7 +161,7 @@ __global__ __launch_bounds__(256, 1) void mm_fp4_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ SB, const float* __restrict__ alpha_ptr, int64_t M, int64_t N,
     int64_t K, void* __restrict__ out, int64_t ldc, int ntm, int ntn, bool vec_store) {
-  __shared__ Stage st[2];
+  __shared__ Stage st[NSTAGE];
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -146,7 +172,8 @@ __global__ __launch_bounds__(256, 1) void mm_fp4_kernel(
   const int64_t m0 = (int64_t)tm * BM;
   const int64_t n0 = (int64_t)tn * BN;
   const int64_t nk = (K + BK - 1) / BK;
-  const int64_t groups = K / 64;  // 128x4 column groups of the scale matrices
+  const bool half_tail = (K % BK) != 0;     // K % 128 == 64
+  const int64_t groups = K / 64;            // 128x4 column groups of the scale matrices
   const int64_t mtiles128 = (M + 127) / 128, ntiles128 = (N + 127) / 128;
 
   f32x16 acc[4][4];
@@ -155,63 +182,78 @@ __global__ __launch_bounds__(256, 1) void mm_fp4_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
-  Prefetch pf;
-  load_stage(pf, A, B, SA, SB, M, N, K, m0, n0, 0, mtiles128, ntiles128, groups, t);
-  store_stage(st[0], pf, t);
-  __syncthreads();
+  // Stage kt is loaded into buffer kt % 3 two stages ahead. Past the last stage the loads repeat
+  // stage nk-1 into a buffer nobody reads again, so every iteration issues and waits for the same
+  // number of loads and the loop body has no branches.
+  const int64_t last = nk - 1;
+  issue_stage(st[0], A, B, SA, SB, M, N, K, m0, n0, 0, mtiles128, ntiles128, groups, wave, lane);
+  issue_stage(st[1], A, B, SA, SB, M, N, K, m0, n0, last < 1 ? last : 1, mtiles128, ntiles128, groups,
+              wave, lane);
+  wait_vmcnt<kLoadsPerStage>();
+  __builtin_amdgcn_s_barrier();
+
+  Frags f;
+  read_frags(f, st[0], wm, wn, li, h, half_tail && nk == 1 && h == 1);
+  read_chunk(f, st[0], 1, wm, wn, li, h);
+  f16x8 xa[2][4], xb[2][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    xa[0][i] = frag_deq(f, i, 0);
+    xb[0][i] = frag_deq(f, 4 + i, 0);
+  }
 
   for (int64_t kt = 0; kt < nk; ++kt) {
-    const int cur = (int)(kt & 1);
-    if (kt + 1 < nk) load_stage(pf, A, B, SA, SB, M, N, K, m0, n0, kt + 1, mtiles128, ntiles128, groups, t);
-    const Stage& s = st[cur];
-
-    u32x4 pa[2][4], pb[2][4];
-    uint32_t wa[4], wb[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ra = wm * 128 + i * 32 + li;
-      const int rb = wn * 128 + i * 32 + li;
-      pa[0][i] = s.a[chunk_slot(ra, 2 * h)];
-      pa[1][i] = s.a[chunk_slot(ra, 2 * h + 1)];
-      pb[0][i] = s.b[chunk_slot(rb, 2 * h)];
-      pb[1][i] = s.b[chunk_slot(rb, 2 * h + 1)];
-      wa[i] = scale_word(s.sa, ra, h);
-      wb[i] = scale_word(s.sb, rb, h);
-    }
-
-    f16x8 xa[2][4], xb[2][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      xa[0][i] = dequant8(pa[0][i].x, scale_pair(wa[i] & 0xFFu));
-      xb[0][i] = dequant8(pb[0][i].x, scale_pair(wb[i] & 0xFFu));
-    }
+    const int64_t ahead = kt + 2 < last ? kt + 2 : last;
+    issue_stage(st[(kt + 2) % NSTAGE], A, B, SA, SB, M, N, K, m0, n0, ahead, mtiles128, ntiles128,
+                groups, wave, lane);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int cb = j & 1, nb = cb ^ 1;
-      const int jn = j + 1;                        // next sub-step
-      const int sh = 8 * (jn >> 1);                // its scale byte
+      if (j == 7) {
+        // Stage kt+1 must be in LDS for every wave: wait until only this wave's loads issued in
+        // this iteration are outstanding, then a bare s_barrier (a fence would also wait for the
+        // loads still in flight). Every read of the buffer that the next iteration's loads
+        // overwrite happened in read_frags of stage kt, before this barrier.
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<kLoadsPerStage>();
+        __builtin_amdgcn_s_barrier();
+        read_frags(f, st[(kt + 1) % NSTAGE], wm, wn, li, h, half_tail && kt + 2 == nk && h == 1);
+      }
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         __builtin_amdgcn_sched_barrier(0);
+        // second chunk of this stage: half of it during sub-step 1, half during sub-step 2 (it is
+        // first needed by the dequantization of sub-step 4, issued during sub-step 3)
+        if ((j == 1 && q == 0) || (j == 2 && q == 0)) {
+          const Stage& cs = st[kt % NSTAGE];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (j == 1) {
+              f.pa[1][i] = cs.a[chunk_slot(wm * 128 + i * 32 + li, 2 * h + 1)];
+            } else {
+              f.pb[1][i] = cs.b[chunk_slot(wn * 128 + i * 32 + li, 2 * h + 1)];
+            }
+          }
+        }
         const int n = q >> 1, m = 2 * (q & 1);
         acc[n][m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xb[cb][n], xa[cb][m], acc[n][m], 0, 0, 0);
         acc[n][m + 1] =
             __builtin_amdgcn_mfma_f32_32x32x16_f16(xb[cb][n], xa[cb][m + 1], acc[n][m + 1], 0, 0, 0);
-        if (jn < 8) {                              // dequantize one fragment of sub-step j+1
-          if (q < 4)
-            xa[nb][q] = dequant8(comp(pa[jn >> 2][q], jn & 3), scale_pair((wa[q] >> sh) & 0xFFu));
-          else
-            xb[nb][q - 4] = dequant8(comp(pb[jn >> 2][q - 4], jn & 3), scale_pair((wb[q - 4] >> sh) & 0xFFu));
-        }
+        // dequantize one fragment of the next sub-step (of the next stage after sub-step 7)
+        const f16x8 v = frag_deq(f, q, (j + 1) & 7);
+        if (q < 4)
+          xa[nb][q] = v;
+        else
+          xb[nb][q - 4] = v;
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (kt + 1 < nk) store_stage(st[cur ^ 1], pf, t);
-    __syncthreads();
   }
+  wait_vmcnt<0>();
 
-  store_wave_tile<OUT_F32>(acc, *alpha_ptr, m0 + wm * 128, n0 + wn * 128, M, N, out, ldc, vec_store,
-                           li, h);
+  // operands carried 2^-8 each (scale_pair): the products are 2^-16 of the true ones
+  const float alpha = *alpha_ptr * 65536.0f;
+  store_wave_tile<OUT_F32>(acc, alpha, m0 + wm * 128, n0 + wn * 128, M, N, out, ldc, vec_store, li, h);
 }
 
 }  // namespace fp4

@@ -83,8 +83,41 @@ __global__ void alpha_kernel(const float* xg, const float* wg, float* alpha) {
 // pair and its amax is a DPP pair max. The tile is walked in 16 steps of 8 rows; all 16 loads
 // are issued before any arithmetic. Scale bytes are staged in LDS at their 128x4 positions and
 // leave as coalesced 16-byte stores of whole 512-byte tiles. Rows M..Mp-1 and columns past K
-// read as zeros (no copy of the input is made), which yields the 0x00 padding scales.
+// read as zeros (no copy of the input is made), which yields the 0x00 padding scales. Interior
+// tiles (the common case) take a path without per-row bounds checks.
+//
+// The element scale r = fl32(g / e4m3(S)) depends only on the 7-bit code S, so each workgroup
+// first tabulates it for all 127 codes (the same IEEE division, once per code) and blocks look it
+// up. Elements are encoded with v_cvt_scalef32_pk_fp4_f32 (unit scale): round to nearest even,
+// saturating at +-6, sign of zero kept -- checked against the software encoder on every fp32
+// input class (ties, denormals, huge values) on gfx950; BSP_QUANT_SW_CVT=1 selects that software
+// encoder instead.
 constexpr float kSixth = 0.16666667163372040f;  // fl32(1/6) = 0x3E2AAAAB
+
+template <bool VEC>
+__device__ __forceinline__ uint4 load8(const uint16_t* p) {
+  if (VEC) return *reinterpret_cast<const uint4*>(p);
+  uint4 v;
+  v.x = (uint32_t)p[0] | ((uint32_t)p[1] << 16);
+  v.y = (uint32_t)p[2] | ((uint32_t)p[3] << 16);
+  v.z = (uint32_t)p[4] | ((uint32_t)p[5] << 16);
+  v.w = (uint32_t)p[6] | ((uint32_t)p[7] << 16);
+  return v;
+}
+
+__device__ __forceinline__ void unpack8(const uint4& v, float (&f)[8]) {
+  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+  f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+  f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+  f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+
+__device__ __forceinline__ float absmax8(const float (&f)[8]) {
+  float a = fmaxf(__builtin_fabsf(f[0]), __builtin_fabsf(f[1]));
+#pragma unroll
+  for (int i = 2; i < 8; ++i) a = fmaxf(a, __builtin_fabsf(f[i]));
+  return a;
+}
 
 template <bool HWCVT, bool VEC>
 __global__ __launch_bounds__(256) void nvfp4_quantize_kernel(const uint16_t* __restrict__ x,
@@ -93,48 +126,41 @@ __global__ __launch_bounds__(256) void nvfp4_quantize_kernel(const uint16_t* __r
                                                              uint8_t* __restrict__ packed,
                                                              uint8_t* __restrict__ sf, int64_t Kp) {
   __shared__ uint4 sf_tile[128];  // 2 KB = 4 scale tiles of 512 B
+  __shared__ float rtab[128];     // fl32(g / e4m3(c)) for code c (0 for c == 0)
   uint8_t* sfb = reinterpret_cast<uint8_t*>(sf_tile);
   const int t = threadIdx.x;
   const int64_t row0 = (int64_t)blockIdx.y * 128;
   const int64_t kk = (int64_t)blockIdx.x * 256 + (t & 31) * 8;
   const int rsub = t >> 5;
   const bool kin = kk < K;  // K % 16 == 0: a lane's 8 elements are all in range or all out
+  const bool full = row0 + 128 <= M && (int64_t)blockIdx.x * 256 + 256 <= K;  // uniform
   const float g = *gsf;
+  if (t < 128) rtab[t] = (t == 0 || t > 0x7E) ? 0.0f : g / e4m3_decode_pos((uint32_t)t);
 
+  const uint16_t* xp = x + (row0 + rsub) * ld + kk;
+  const int64_t xstep = 8 * ld;
   uint4 v[16];
+  if (full) {
 #pragma unroll
-  for (int s = 0; s < 16; ++s) {
-    int64_t r = row0 + s * 8 + rsub;
-    if (kin && r < M) {
-      const uint16_t* p = x + r * ld + kk;
-      if (VEC) {
-        v[s] = *reinterpret_cast<const uint4*>(p);
-      } else {
-        v[s].x = (uint32_t)p[0] | ((uint32_t)p[1] << 16);
-        v[s].y = (uint32_t)p[2] | ((uint32_t)p[3] << 16);
-        v[s].z = (uint32_t)p[4] | ((uint32_t)p[5] << 16);
-        v[s].w = (uint32_t)p[6] | ((uint32_t)p[7] << 16);
-      }
-    } else {
-      v[s] = make_uint4(0u, 0u, 0u, 0u);
-    }
+    for (int s = 0; s < 16; ++s) v[s] = load8<VEC>(xp + s * xstep);
+  } else {
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+      v[s] = (kin && row0 + s * 8 + rsub < M) ? load8<VEC>(xp + s * xstep) : make_uint4(0u, 0u, 0u, 0u);
   }
+  __syncthreads();  // rtab
 
   const int64_t half_k = K / 2;
+  uint8_t* pp = packed + (row0 + rsub) * half_k + kk / 2;
+  const int64_t pstep = 8 * half_k;
 #pragma unroll
   for (int s = 0; s < 16; ++s) {
     float f[8];
-    f[0] = bf16_lo(v[s].x); f[1] = bf16_hi(v[s].x);
-    f[2] = bf16_lo(v[s].y); f[3] = bf16_hi(v[s].y);
-    f[4] = bf16_lo(v[s].z); f[5] = bf16_hi(v[s].z);
-    f[6] = bf16_lo(v[s].w); f[7] = bf16_hi(v[s].w);
-    float a = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) a = fmaxf(a, __builtin_fabsf(f[i]));
-    a = pair_max(a);
+    unpack8(v[s], f);
+    const float a = pair_max(absmax8(f));
     const float sc = g * (a * kSixth);
     const uint32_t S = e4m3_encode_pos(sc);
-    const float r = (S == 0u) ? 0.0f : g / e4m3_decode_pos(S);
+    const float r = rtab[S];
     uint32_t out = 0;
     if (HWCVT) {
       out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, f[0] * r, f[1] * r, 1.0f, 0);
@@ -146,8 +172,7 @@ __global__ __launch_bounds__(256) void nvfp4_quantize_kernel(const uint16_t* __r
       for (int i = 0; i < 8; ++i) out |= e2m1_encode(f[i] * r) << (4 * i);
     }
     const int rr = s * 8 + rsub;  // row inside the 128-row tile
-    const int64_t row = row0 + rr;
-    if (kin && row < M) *reinterpret_cast<uint32_t*>(packed + row * half_k + kk / 2) = out;
+    if (full || (kin && row0 + rr < M)) *reinterpret_cast<uint32_t*>(pp + s * pstep) = out;
     if ((t & 1) == 0) {
       const int cb = (t & 31) >> 1;  // scale column inside the 16-column tile
       sfb[(cb >> 2) * 512 + (rr & 31) * 16 + (rr >> 5) * 4 + (cb & 3)] = (uint8_t)S;
@@ -170,7 +195,11 @@ __global__ __launch_bounds__(256) void nvfp4_quantize_kernel(const uint16_t* __r
 // One workgroup covers 64 rows x 256 K (8 steps of 8 rows x 32 lanes x 8 elements). A 32-element
 // group is a lane quad; its amax is a DPP quad max. Scale byte = max(biased exponent of amax - 8, 0)
 // (that is Es + 127 with Es = clamp(floor(log2 amax) - 8, -127, 127), and 0x00 for amax == 0).
-template <bool VEC>
+// Elements: x * 2^-Es (exact), clamped to +-448 (saturation), then v_cvt_pk_fp8_f32, which
+// rounds to nearest even with the sign of zero kept (its only difference from the software
+// encoder on gfx950 is that it does not saturate, hence the clamp); BSP_QUANT_SW_CVT=1 selects
+// the software encoder.
+template <bool HWCVT, bool VEC>
 __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const uint16_t* __restrict__ x,
                                                              int64_t M, int64_t K, int64_t ld,
                                                              uint8_t* __restrict__ q,
@@ -180,48 +209,47 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const uint16_t* __r
   const int64_t kk = (int64_t)blockIdx.x * 256 + (t & 31) * 8;
   const int rsub = t >> 5;
   const bool kin = kk < K;  // K % 32 == 0: a quad is entirely in or out
+  const bool full = row0 + 64 <= M && (int64_t)blockIdx.x * 256 + 256 <= K;
+  const uint16_t* xp = x + (row0 + rsub) * ld + kk;
+  const int64_t xstep = 8 * ld;
   uint4 v[8];
+  if (full) {
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    int64_t r = row0 + s * 8 + rsub;
-    if (kin && r < M) {
-      const uint16_t* p = x + r * ld + kk;
-      if (VEC) {
-        v[s] = *reinterpret_cast<const uint4*>(p);
-      } else {
-        v[s].x = (uint32_t)p[0] | ((uint32_t)p[1] << 16);
-        v[s].y = (uint32_t)p[2] | ((uint32_t)p[3] << 16);
-        v[s].z = (uint32_t)p[4] | ((uint32_t)p[5] << 16);
-        v[s].w = (uint32_t)p[6] | ((uint32_t)p[7] << 16);
-      }
-    } else {
-      v[s] = make_uint4(0u, 0u, 0u, 0u);
-    }
+    for (int s = 0; s < 8; ++s) v[s] = load8<VEC>(xp + s * xstep);
+  } else {
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      v[s] = (kin && row0 + s * 8 + rsub < M) ? load8<VEC>(xp + s * xstep) : make_uint4(0u, 0u, 0u, 0u);
   }
   const int64_t ng = K / 32;
+  uint8_t* qp = q + (row0 + rsub) * K + kk;
+  uint8_t* sp = sf + (row0 + rsub) * ng + kk / 32;
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
     float f[8];
-    f[0] = bf16_lo(v[s].x); f[1] = bf16_hi(v[s].x);
-    f[2] = bf16_lo(v[s].y); f[3] = bf16_hi(v[s].y);
-    f[4] = bf16_lo(v[s].z); f[5] = bf16_hi(v[s].z);
-    f[6] = bf16_lo(v[s].w); f[7] = bf16_hi(v[s].w);
-    float a = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) a = fmaxf(a, __builtin_fabsf(f[i]));
-    a = quad_max(a);
-    const uint32_t ef = __float_as_uint(a) >> 23;          // biased exponent (a >= 0, finite)
-    const uint32_t byte = ef > 8u ? ef - 8u : 0u;          // Es + 127
+    unpack8(v[s], f);
+    const float a = quad_max(absmax8(f));
+    const uint32_t ef = __float_as_uint(a) >> 23;            // biased exponent (a >= 0, finite)
+    const uint32_t byte = ef > 8u ? ef - 8u : 0u;            // Es + 127
     const float inv = __uint_as_float((254u - byte) << 23);  // 2^-Es = 2^(127 - byte), exact
     uint32_t lo = 0, hi = 0;
+    if (HWCVT) {
+      float c[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lo |= e4m3_encode(f[i] * inv) << (8 * i);
+      for (int i = 0; i < 8; ++i) c[i] = __builtin_amdgcn_fmed3f(f[i] * inv, -448.0f, 448.0f);
+      lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], lo, false);
+      lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], lo, true);
+      hi = __builtin_amdgcn_cvt_pk_fp8_f32(c[4], c[5], hi, false);
+      hi = __builtin_amdgcn_cvt_pk_fp8_f32(c[6], c[7], hi, true);
+    } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) hi |= e4m3_encode(f[4 + i] * inv) << (8 * i);
-    const int64_t row = row0 + s * 8 + rsub;
-    if (kin && row < M) {
-      *reinterpret_cast<uint2*>(q + row * K + kk) = make_uint2(lo, hi);
-      if ((t & 3) == 0) sf[row * ng + kk / 32] = (uint8_t)byte;
+      for (int i = 0; i < 4; ++i) lo |= e4m3_encode(f[i] * inv) << (8 * i);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) hi |= e4m3_encode(f[4 + i] * inv) << (8 * i);
+    }
+    if (full || (kin && row0 + s * 8 + rsub < M)) {
+      *reinterpret_cast<uint2*>(qp + s * 8 * K) = make_uint2(lo, hi);
+      if ((t & 3) == 0) sp[s * 8 * ng] = (uint8_t)byte;
     }
   }
 }
@@ -383,12 +411,17 @@ extern "C" int bsp_mxfp8_quantize(const void* x, int64_t M, int64_t K, int64_t l
   if (int e = check_device()) return e;
   dim3 grid((unsigned)ceil_div(K, 256), (unsigned)ceil_div(M, 64));
   const uint16_t* xp = static_cast<const uint16_t*>(x);
-  if ((ld % 8 == 0) && aligned16(x))
-    hipLaunchKernelGGL(mxfp8_quantize_kernel<true>, grid, dim3(256), 0, (hipStream_t)stream, xp, M, K,
-                       ld, q, sf);
+  const bool vec = (ld % 8 == 0) && aligned16(x);
+  const bool hw = hw_cvt_enabled();
+  hipStream_t s = (hipStream_t)stream;
+  if (hw && vec)
+    hipLaunchKernelGGL((mxfp8_quantize_kernel<true, true>), grid, dim3(256), 0, s, xp, M, K, ld, q, sf);
+  else if (hw)
+    hipLaunchKernelGGL((mxfp8_quantize_kernel<true, false>), grid, dim3(256), 0, s, xp, M, K, ld, q, sf);
+  else if (vec)
+    hipLaunchKernelGGL((mxfp8_quantize_kernel<false, true>), grid, dim3(256), 0, s, xp, M, K, ld, q, sf);
   else
-    hipLaunchKernelGGL(mxfp8_quantize_kernel<false>, grid, dim3(256), 0, (hipStream_t)stream, xp, M, K,
-                       ld, q, sf);
+    hipLaunchKernelGGL((mxfp8_quantize_kernel<false, false>), grid, dim3(256), 0, s, xp, M, K, ld, q, sf);
   return check_launch("bsp_mxfp8_quantize");
 }
 

@@ -162,3 +162,34 @@ def test_gelu_within_one_bf16_ulp():
     x = dev_bf16(xb[:1001].copy())
     bsp.bsp_gelu_tanh_bf16(x, out=x)
     assert np.array_equal(host_bits(x), got[:1001])
+
+
+_SW_SCRIPT = r"""
+import sys, numpy as np
+sys.path.insert(0, sys.argv[1])
+import block_scaled_precision_nvfp4_amd as bsp, workloads as W
+from oracle import nvfp4 as N, mxfp8 as X
+from tests.gpu_util import dev_bf16, host_u8, scalar
+for m, k in [(129, 96), (300, 1536)]:
+    xb = W.special_values_block(seed=m, rows=m, cols=k)
+    p, s = bsp.bsp_nvfp4_quantize(dev_bf16(xb), scalar(0.37))
+    rp, rs = N.quantize(xb, np.float32(0.37))
+    assert np.array_equal(host_u8(p), rp) and np.array_equal(host_u8(s).ravel(), rs)
+    q, sq = bsp.bsp_mxfp8_quantize(dev_bf16(xb))
+    rq, rsq = X.quantize(xb)
+    assert np.array_equal(host_u8(q), rq) and np.array_equal(host_u8(sq), rsq)
+print("SW-PATH-OK")
+"""
+
+
+def test_software_encoder_path_bit_exact():
+    """BSP_QUANT_SW_CVT=1 switches both quantizers to the software encoders; they must give the
+    same bytes as the hardware-convert default (both checked against the oracle)."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, BSP_QUANT_SW_CVT="1")
+    r = subprocess.run([sys.executable, "-c", _SW_SCRIPT, root], env=env, capture_output=True,
+                       text=True, timeout=150)
+    assert r.returncode == 0 and "SW-PATH-OK" in r.stdout, r.stdout + r.stderr
