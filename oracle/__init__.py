@@ -29,4 +29,4 @@ values fixed by the format definitions and hand-worked examples
 (``tests/golden/``), closed forms, invariants and brute force; none is
 "parity unpinned" except where a function docstring says so.
 """
-from . import activations, formats, nvfp4, mxfp8  # noqa: F401
+from . import activations, formats, mxfp4, mxfp8, nvfp4  # noqa: F401

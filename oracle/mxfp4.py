@@ -1,0 +1,102 @@
+"""MXFP4 oracle: e2m1 elements with one e8m0 scale per 32 K-elements.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+FastVideo nvfp4_config.py, ``_mm_fp4`` / its custom op: ``mm_fp4`` takes ``use_nvfp4``; with
+``use_nvfp4=False`` the FP4 operands carry OCP MX scales instead of NVFP4's (the module docstring
+contrasts NVFP4 with MX-FP4, "AMD's MX-FP4"). The vLLM-Omni mxfp8_config.py page
+(``DiffusionMXFP8Config``) fixes the MX convention: 32 consecutive K elements share one e8m0
+scale, per the OCP MX specification.
+
+Reading (as for MXFP8, with the e2m1 element):
+  Es   = clamp(floor(log2(amax)) - 2, -127, 127)  (2 = exponent of e2m1's largest power of two, 4),
+  byte = Es + 127, 0x00 when amax == 0;
+  q_i  = e2m1(fl32(x_i * 2^-Es)), nearest even, saturating at +-6.
+Scales use the same 128x4 layout as NVFP4's (one byte per 32 K elements instead of 16), the
+layout ``mm_fp4`` takes for both kinds of operands.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .formats import e2m1_decode, e2m1_encode, e8m0_decode
+from .nvfp4 import pack_nibbles, sf_offset, swizzle_128x4, unpack_nibbles
+
+F32 = np.float32
+GROUP = 32
+E2M1_EMAX = 2
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def sf_padded_shape(rows: int, k: int):
+    cols = (k + GROUP - 1) // GROUP
+    return ((rows + 127) // 128) * 128, ((cols + 3) // 4) * 4
+
+
+def scale_exponent(amax: np.ndarray) -> np.ndarray:
+    a = np.asarray(amax, dtype=np.float64)
+    _, e = np.frexp(a)
+    es = np.clip(e.astype(np.int64) - 1 - E2M1_EMAX, -127, 127)
+    return np.where(a == 0.0, -127, es)
+
+
+def quantize_blocks(xf: np.ndarray):
+    """fp32 [rows, ngroups, 32] -> (e2m1 codes, e8m0 bytes [rows, ngroups])."""
+    xf = np.asarray(xf, dtype=np.float32)
+    es = scale_exponent(np.max(np.abs(xf), axis=-1))
+    inv = np.ldexp(np.float32(1.0), (-es).astype(np.int32)).astype(np.float32)
+    v = (xf * inv[..., None]).astype(np.float32)
+    return e2m1_encode(v), (es + 127).astype(np.uint8)
+
+
+def quantize(x_bits: np.ndarray, layout: str = "128x4"):
+    """bf16 X [M, K] (K % 32 == 0) -> (packed [M, K/2], scales: flat 128x4 bytes or [M, K/32])."""
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    m, k = x_bits.shape
+    if k % GROUP:
+        raise ValueError("K must be a multiple of 32")
+    ng = k // GROUP
+    codes, s = quantize_blocks(bf16_to_f32(x_bits).reshape(m, ng, GROUP))
+    packed = pack_nibbles(codes.reshape(m, k))
+    if layout == "linear":
+        return packed, s
+    rp, cp = sf_padded_shape(m, k)
+    lin = np.zeros((rp, cp), dtype=np.uint8)
+    lin[:m, :ng] = s
+    return packed, swizzle_128x4(lin)
+
+
+def dequant_rows(packed, sf_flat, rows, n_rows_total: int, k: int) -> np.ndarray:
+    rows = np.asarray(rows, dtype=np.int64)
+    _, cp = sf_padded_shape(n_rows_total, k)
+    ng = k // GROUP
+    codes = unpack_nibbles(np.asarray(packed)[rows]).astype(np.int64)
+    r_idx = np.repeat(rows[:, None], ng, axis=1)
+    c_idx = np.repeat(np.arange(ng)[None, :], rows.size, axis=0)
+    sv = e8m0_decode(np.asarray(sf_flat, dtype=np.uint8)[sf_offset(r_idx, c_idx, cp)])
+    vals = e2m1_decode(codes).reshape(rows.size, ng, GROUP) * sv[..., None]
+    return vals.reshape(rows.size, k)
+
+
+def mm_mxfp4(a_packed, a_sf, b_packed, b_sf, alpha_val, m: int, n: int, k: int,
+             row_chunk: int = 2048) -> np.ndarray:
+    """C[m, n] = alpha * sum_k dequant(A)[m, k] * dequant(B)[n, k] in fp64."""
+    B = dequant_rows(b_packed, b_sf, np.arange(n), n, k)
+    out = np.empty((m, n), dtype=np.float64)
+    for r0 in range(0, m, row_chunk):
+        r1 = min(r0 + row_chunk, m)
+        out[r0:r1] = dequant_rows(a_packed, a_sf, np.arange(r0, r1), m, k) @ B.T
+    return np.float64(F32(alpha_val)) * out
+
+
+def mm_mxfp4_entries(a_packed, a_sf, b_packed, b_sf, alpha_val, m: int, n: int, k: int, rows, cols):
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+    ur, ri = np.unique(rows, return_inverse=True)
+    uc, ci = np.unique(cols, return_inverse=True)
+    A = dequant_rows(a_packed, a_sf, ur, m, k)
+    B = dequant_rows(b_packed, b_sf, uc, n, k)
+    return np.float64(F32(alpha_val)) * np.einsum("ik,ik->i", A[ri], B[ci])
