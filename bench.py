@@ -42,7 +42,36 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=1024,
                     help="tokens of the FFN the CPU oracle runs for cpu_baseline")
     ap.add_argument("--no-mxfp8", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a 1 GiB device-to-device copy (reference for HBM byte counters)")
     return ap.parse_args()
+
+
+GEMM_SOURCE = os.path.join(ROOT, "block_scaled_precision_nvfp4_amd", "csrc", "gemm_fp4.hip")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "mm_fp4_wan14b_ffn_pmc.txt")
+
+
+def source_sha256(path: str) -> str:
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None when the summary
+    is missing or was taken on a different version of the GEMM source."""
+    try:
+        kv = {}
+        with open(PMC_SUMMARY) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("gemm_fp4.hip sha256") != source_sha256(GEMM_SOURCE):
+            return None
+        return float(kv[f"{kernel} hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def nvfp4_sf_shape(rows, k):
@@ -66,6 +95,16 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calibrate_copy:
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "copies": 2}), flush=True)
+        return
     cfg = W.config(4)
     tx, tw1, tw2 = cfg.tensor("X"), cfg.tensor("W"), cfg.tensor("W2")
     M, K1, N1 = tx.rows, tx.cols, tw1.rows          # 32760, 5120, 13824
@@ -170,7 +209,7 @@ def main():
     dom_tf = kernels[dom]["TFLOPS"]
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(dom_tf, 2),
                 "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s", "frac": round(dom_tf / PEAK_FP4_TFLOPS, 4),
-                "traffic": None,
+                "traffic": measured_traffic(dom),
                 "mfma_used": "v_mfma_f32_32x32x16_f16 (exact fp16 dequant of e2m1 x e4m3)",
                 "frac_of_f16_mfma_peak": round(dom_tf / PEAK_F16_TFLOPS, 4)}
 
@@ -200,6 +239,7 @@ def main():
         m0.record(stream)
         qw, sw = bsp.bsp_mxfp8_quantize(w5)       # online BF16 -> MXFP8 weight conversion
         m1.record(stream)
+        pw4, sw4 = bsp.bsp_mxfp4_quantize(w5)     # and to MXFP4 for the mm_fp4 MX variant
         qx = torch.empty((M, K1), dtype=torch.uint8, device=dev)
         sxm = torch.empty((M, K1 // 32), dtype=torch.uint8, device=dev)
         out5 = torch.empty((M, N1), dtype=torch.bfloat16, device=dev)
@@ -233,6 +273,39 @@ def main():
             "quantize_frac_hbm": round(qb8 / q8 / 1e6 / PEAK_HBM_GBS, 4),
             "weight_conversion_ms": round(m0.elapsed_time(m1), 4)}
         log(json.dumps(result["mxfp8"]))
+        del qx, sxm
+
+        # ---- MXFP4 (mm_fp4 with MX scales, the format gfx950's FP4 MFMA takes natively)
+        px4 = torch.empty((M, K1 // 2), dtype=torch.uint8, device=dev)
+        sx4 = torch.empty((-(-M // 128) * 128, K1 // 128 * 4), dtype=torch.uint8, device=dev)
+
+        def step4(e=None):
+            if e:
+                e[0].record(stream)
+            bsp.bsp_mxfp4_quantize(x5, px4, sx4)
+            if e:
+                e[1].record(stream)
+            bsp.bsp_mm_mxfp4(px4, sx4, pw4, sw4, out=out5)
+            if e:
+                e[2].record(stream)
+
+        for _ in range(args.warmup):
+            step4()
+        torch.cuda.synchronize()
+        e4 = [[ev() for _ in range(3)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            step4(e4[i])
+        torch.cuda.synchronize()
+        q4 = sum(e[0].elapsed_time(e[1]) for e in e4) / args.steps
+        g4 = sum(e[1].elapsed_time(e[2]) for e in e4) / args.steps
+        tf4 = 2.0 * M * N1 * K1 / g4 / 1e9
+        qb4 = 2 * M * K1 + M * K1 // 2 + (-(-M // 128) * 128) * K1 // 32
+        result["mxfp4"] = {
+            "mm_mxfp4_ms": round(g4, 4), "TFLOPS": round(tf4, 2),
+            "frac_fp4_peak": round(tf4 / PEAK_FP4_TFLOPS, 4),
+            "quantize_ms": round(q4, 4), "quantize_GBs": round(qb4 / q4 / 1e6, 1),
+            "quantize_frac_hbm": round(qb4 / q4 / 1e6 / PEAK_HBM_GBS, 4)}
+        log(json.dumps(result["mxfp4"]))
 
     # ---- CPU oracle on a bounded sample of the same workload
     if not args.no_cpu_baseline:

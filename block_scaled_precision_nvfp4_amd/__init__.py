@@ -36,6 +36,9 @@ SIGNATURES = {
     "bsp_mm_fp4": ([_p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _int, _p], _int),
     "bsp_mxfp8_quantize": ([_p, _i64, _i64, _i64, _p, _p, _p], _int),
     "bsp_mm_mxfp8": ([_p, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _int, _p], _int),
+    "bsp_mxfp4_sf_bytes": ([_i64, _i64, ctypes.POINTER(_i64)], _int),
+    "bsp_mxfp4_quantize": ([_p, _i64, _i64, _i64, _p, _p, _p], _int),
+    "bsp_mm_mxfp4": ([_p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _int, _p], _int),
     "bsp_gelu_tanh_bf16": ([_p, _p, _i64, _p], _int),
 }
 
@@ -254,6 +257,64 @@ def bsp_mm_mxfp8(a: torch.Tensor, a_sf: torch.Tensor, b: torch.Tensor, b_sf: tor
     _need(out, "out", out_dtype, dev)
     _call("bsp_mm_mxfp8", a.data_ptr(), a_sf.data_ptr(), b.data_ptr(), b_sf.data_ptr(), m, n, k,
           out.data_ptr(), out.stride(0), code, _stream(dev))
+    return out
+
+
+# ------------------------------------------------------------------------------------- MXFP4
+def bsp_mxfp4_sf_bytes(rows: int, k: int) -> int:
+    out = ctypes.c_int64(0)
+    _call("bsp_mxfp4_sf_bytes", rows, k, ctypes.byref(out))
+    return out.value
+
+
+def bsp_mxfp4_quantize(x: torch.Tensor, packed: Optional[torch.Tensor] = None,
+                       sf: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """(packed uint8 [M, K/2], sf uint8 [ceil(M/128)*128, ceil(K/128)*4] in the 128x4 layout)."""
+    x = _as_bf16_2d(x, "x")
+    m, k = x.shape
+    rp, kp = -(-m // 128) * 128, -(-k // 128) * 4
+    if packed is None:
+        packed = torch.empty((m, k // 2), dtype=torch.uint8, device=x.device)
+    if sf is None:
+        sf = torch.empty((rp, kp), dtype=torch.uint8, device=x.device)
+    _need(packed, "packed", torch.uint8, x.device)
+    _need(sf, "sf", torch.uint8, x.device)
+    if packed.numel() < m * (k // 2) or not packed.is_contiguous():
+        raise ValueError("packed must be contiguous with M*K/2 bytes")
+    if sf.numel() < rp * kp or not sf.is_contiguous():
+        raise ValueError("sf must be contiguous with bsp_mxfp4_sf_bytes(M, K) bytes")
+    _call("bsp_mxfp4_quantize", x.data_ptr(), m, k, x.stride(0), packed.data_ptr(), sf.data_ptr(),
+          _stream(x.device))
+    return packed, sf
+
+
+def bsp_mm_mxfp4(a: torch.Tensor, a_sf: torch.Tensor, b: torch.Tensor, b_sf: torch.Tensor,
+                 alpha: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.bfloat16,
+                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C [M, N] = alpha * A . B^T for MXFP4 a [M, K/2] and weight b [N, K/2] (128x4 scales)."""
+    _need(a, "a", torch.uint8)
+    dev = a.device
+    for t, nm in ((a_sf, "a_sf"), (b, "b"), (b_sf, "b_sf")):
+        _need(t, nm, torch.uint8, dev)
+    if alpha is not None:
+        _need(alpha, "alpha", torch.float32, dev)
+    if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[1]:
+        raise ValueError(f"a {tuple(a.shape)} and b {tuple(b.shape)} must be [M, K/2] and [N, K/2]")
+    if not (a.is_contiguous() and b.is_contiguous() and a_sf.is_contiguous() and b_sf.is_contiguous()):
+        raise ValueError("operands and scales must be contiguous")
+    m, n, k = a.shape[0], b.shape[0], a.shape[1] * 2
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"out_dtype must be bf16 or fp32, got {out_dtype}")
+    code = BSP_OUT_BF16 if out_dtype == torch.bfloat16 else BSP_OUT_F32
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=dev)
+    _need(out, "out", out_dtype, dev)
+    if out.dim() != 2 or out.shape[0] != m or out.shape[1] != n or out.stride(1) != 1:
+        raise ValueError(f"out must be [{m}, {n}] with unit column stride")
+    if a_sf.numel() < bsp_mxfp4_sf_bytes(m, k) or b_sf.numel() < bsp_mxfp4_sf_bytes(n, k):
+        raise ValueError("scale buffers are smaller than bsp_mxfp4_sf_bytes")
+    _call("bsp_mm_mxfp4", a.data_ptr(), a_sf.data_ptr(), b.data_ptr(), b_sf.data_ptr(),
+          _ptr(alpha), m, n, k, out.data_ptr(), out.stride(0), code, _stream(dev))
     return out
 
 

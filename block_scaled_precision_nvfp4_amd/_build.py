@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(CSRC, "_build")
 LIB = os.path.join(HERE, "libbsp.so")
-SOURCES = ["api.hip", "quantize.hip", "gemm_fp4.hip", "gemm_mxfp8.hip"]
+SOURCES = ["api.hip", "quantize.hip", "gemm_fp4.hip", "gemm_mx.hip"]
 HEADERS = ["common.hpp", "gemm_common.hpp"]
 
 # IEEE fp32 everywhere: no contraction into FMA, correctly rounded division, no fast-math; packed

@@ -46,7 +46,11 @@ struct Stage {
 
 typedef __attribute__((address_space(3))) void lds_t;
 
-__device__ __forceinline__ int chunk_slot(int row, int c) { return row * 4 + (c ^ ((row >> 1) & 3)); }
+// 16-byte chunk c of row r. The XOR pattern makes the 16-byte reads of 8 or 16 consecutive rows
+// (one LDS phase of 32 or 64 banks) hit distinct banks.
+__device__ __forceinline__ int chunk_slot(int row, int c) {
+  return row * 4 + (c ^ (((row >> 1) ^ (row >> 2)) & 3));
+}
 
 // f16 pair holding (e4m3 scale byte) * 2^-8 twice, built from the bits alone: an e4m3 code c
 // (non-negative) shifted left by 7 is an f16 with exponent field e and mantissa m, i.e.
@@ -76,7 +80,7 @@ __device__ __forceinline__ uint32_t comp(const u32x4& v, int j) {
 // Stage kt's operand and scale bytes, global -> LDS without passing through registers
 // (global_load_lds_dwordx4: lane l of an instruction lands at the LDS base + 16 l). Each wave
 // issues 4 instructions per operand (64 chunks each) and one for a scale half. The XOR swizzle is
-// applied on the global side: LDS slot s holds row s/4, logical chunk (s%4) ^ ((row/2)%4).
+// applied on the global side: LDS slot s holds row s/4, logical chunk (s%4) ^ ((row/2 ^ row/4)%4).
 // K % 128 == 64: the last stage's second half re-reads its first half (in bounds) and the compute
 // zeroes that half's scales.
 __device__ __forceinline__ void issue_stage(Stage& st, const uint8_t* __restrict__ A,
@@ -93,7 +97,7 @@ __device__ __forceinline__ void issue_stage(Stage& st, const uint8_t* __restrict
     const int slot0 = (wave * 4 + i) * 64;
     const int s = slot0 + lane;
     const int row = s >> 2;
-    int c = (s & 3) ^ ((row >> 1) & 3);
+    int c = (s & 3) ^ (((row >> 1) ^ (row >> 2)) & 3);
     c = (tail && c >= 2) ? c - 2 : c;
     const int64_t koff = kt * 64 + c * 16;
     int64_t ra = m0 + row; ra = ra < M ? ra : M - 1;
@@ -113,9 +117,12 @@ __device__ __forceinline__ void issue_stage(Stage& st, const uint8_t* __restrict
 }
 
 // s_waitcnt vmcnt(n) (n < 16), leaving lgkmcnt and expcnt unconstrained
+// s_waitcnt vmcnt(n), n < 64 (bits [3:0] and [15:14] of the immediate), leaving lgkmcnt and
+// expcnt unconstrained
 template <int n>
 __device__ __forceinline__ void wait_vmcnt() {
-  __builtin_amdgcn_s_waitcnt((n & 0xF) | (0x7 << 4) | (0xF << 8));
+  static_assert(n >= 0 && n < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
 // A wave's fragments of one stage: packed bytes for both 16-byte chunks of its K half and the

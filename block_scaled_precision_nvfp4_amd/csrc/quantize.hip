@@ -255,6 +255,77 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const uint16_t* __r
 }
 
 // =============================================================================================
+// MXFP4 quantize (mm_fp4's MX operands)
+// =============================================================================================
+// As the NVFP4 kernel (128 rows x 256 K per workgroup, 8 elements per lane), with OCP MX scales:
+// a 32-element group is a lane quad; scale byte = max(biased exponent of amax - 2, 0), i.e.
+// Es + 127 with Es = clamp(floor(log2 amax) - 2, -127, 127) (0x00 for amax == 0); elements
+// e2m1(x * 2^-Es) (exact scaling, nearest even, saturating at 6). The 8 scale columns of a
+// workgroup are two 128x4 column groups, staged in LDS and stored as whole 512-byte tiles.
+template <bool HWCVT, bool VEC>
+__global__ __launch_bounds__(256) void mxfp4_quantize_kernel(const uint16_t* __restrict__ x,
+                                                             int64_t M, int64_t K, int64_t ld,
+                                                             uint8_t* __restrict__ packed,
+                                                             uint8_t* __restrict__ sf, int64_t Kp) {
+  __shared__ uint4 sf_tile[64];  // 1 KB = 2 scale tiles of 512 B
+  uint8_t* sfb = reinterpret_cast<uint8_t*>(sf_tile);
+  const int t = threadIdx.x;
+  const int64_t row0 = (int64_t)blockIdx.y * 128;
+  const int64_t kk = (int64_t)blockIdx.x * 256 + (t & 31) * 8;
+  const int rsub = t >> 5;
+  const bool kin = kk < K;  // K % 32 == 0: a quad is entirely in or out
+  const bool full = row0 + 128 <= M && (int64_t)blockIdx.x * 256 + 256 <= K;
+  const uint16_t* xp = x + (row0 + rsub) * ld + kk;
+  const int64_t xstep = 8 * ld;
+  uint4 v[16];
+  if (full) {
+#pragma unroll
+    for (int s = 0; s < 16; ++s) v[s] = load8<VEC>(xp + s * xstep);
+  } else {
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+      v[s] = (kin && row0 + s * 8 + rsub < M) ? load8<VEC>(xp + s * xstep) : make_uint4(0u, 0u, 0u, 0u);
+  }
+  const int64_t half_k = K / 2;
+  uint8_t* pp = packed + (row0 + rsub) * half_k + kk / 2;
+  const int64_t pstep = 8 * half_k;
+#pragma unroll
+  for (int s = 0; s < 16; ++s) {
+    float f[8];
+    unpack8(v[s], f);
+    const float a = quad_max(absmax8(f));
+    const uint32_t ef = __float_as_uint(a) >> 23;
+    const uint32_t byte = ef > 2u ? ef - 2u : 0u;            // Es + 127
+    const float inv = __uint_as_float((254u - byte) << 23);  // 2^-Es, exact
+    uint32_t out = 0;
+    if (HWCVT) {
+      out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, f[0] * inv, f[1] * inv, 1.0f, 0);
+      out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, f[2] * inv, f[3] * inv, 1.0f, 1);
+      out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, f[4] * inv, f[5] * inv, 1.0f, 2);
+      out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, f[6] * inv, f[7] * inv, 1.0f, 3);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) out |= e2m1_encode(f[i] * inv) << (4 * i);
+    }
+    const int rr = s * 8 + rsub;
+    if (full || (kin && row0 + rr < M)) *reinterpret_cast<uint32_t*>(pp + s * pstep) = out;
+    if ((t & 3) == 0) {
+      const int cb = (t & 31) >> 2;  // scale column inside the 8-column tile
+      sfb[(cb >> 2) * 512 + (rr & 31) * 16 + (rr >> 5) * 4 + (cb & 3)] = (uint8_t)byte;
+    }
+  }
+  __syncthreads();
+  const int64_t groups = Kp / 4;
+  const int64_t g0 = (int64_t)blockIdx.x * 2;
+  const int64_t ng = groups - g0 < 2 ? groups - g0 : 2;
+  if (t < ng * 32) {
+    const int cg = t >> 5;
+    const int64_t tile = (int64_t)blockIdx.y * groups + g0 + cg;
+    reinterpret_cast<uint4*>(sf + tile * 512)[t & 31] = sf_tile[cg * 32 + (t & 31)];
+  }
+}
+
+// =============================================================================================
 // GELU (tanh form), bf16 in/out, fp32 math
 // =============================================================================================
 // gelu(x) = 0.5 x (1 + tanh(z)), z = sqrt(2/pi) (x + 0.044715 x^3). Since 0.5 (1 + tanh z) is the
@@ -436,4 +507,43 @@ extern "C" int bsp_gelu_tanh_bf16(const void* x, void* y, int64_t n, void* strea
   hipLaunchKernelGGL(gelu_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
                      static_cast<const uint16_t*>(x), static_cast<uint16_t*>(y), n);
   return check_launch("bsp_gelu_tanh_bf16");
+}
+
+extern "C" int bsp_mxfp4_sf_bytes(int64_t rows, int64_t K, int64_t* bytes) {
+  BSP_REQUIRE(bytes, BSP_EINVAL, "bsp_mxfp4_sf_bytes: null output pointer");
+  BSP_REQUIRE(rows >= 0 && K >= 0, BSP_EINVAL, "bsp_mxfp4_sf_bytes: negative size");
+  *bytes = ceil_div(rows, 128) * 128 * ceil_div(K, 128) * 4;
+  return BSP_OK;
+}
+
+extern "C" int bsp_mxfp4_quantize(const void* x, int64_t M, int64_t K, int64_t ld, uint8_t* packed,
+                                  uint8_t* sf, void* stream) {
+  BSP_REQUIRE(M >= 0 && K > 0, BSP_EINVAL, "bsp_mxfp4_quantize: bad size M=%lld K=%lld",
+              (long long)M, (long long)K);
+  BSP_REQUIRE(K % 32 == 0, BSP_ESHAPE, "bsp_mxfp4_quantize: K (%lld) must be a multiple of 32",
+              (long long)K);
+  BSP_REQUIRE(M <= 1 || ld >= K, BSP_ESHAPE, "bsp_mxfp4_quantize: ld (%lld) < K (%lld)",
+              (long long)ld, (long long)K);
+  if (M == 0) return BSP_OK;
+  BSP_REQUIRE(x && packed && sf, BSP_EINVAL, "bsp_mxfp4_quantize: null pointer");
+  BSP_REQUIRE((reinterpret_cast<uintptr_t>(packed) & 3u) == 0 && (reinterpret_cast<uintptr_t>(sf) & 15u) == 0,
+              BSP_EINVAL, "bsp_mxfp4_quantize: packed must be 4-byte and sf 16-byte aligned");
+  BSP_REQUIRE(ceil_div(M, 128) < 65536, BSP_ESHAPE, "bsp_mxfp4_quantize: M too large");
+  if (int e = check_device()) return e;
+  const int64_t Mp = ceil_div(M, 128) * 128;
+  const int64_t Kp = ceil_div(K / 32, 4) * 4;
+  dim3 grid((unsigned)ceil_div(Kp, 8), (unsigned)(Mp / 128));
+  const uint16_t* xp = static_cast<const uint16_t*>(x);
+  const bool vec = (ld % 8 == 0) && aligned16(x);
+  const bool hw = hw_cvt_enabled();
+  hipStream_t s = (hipStream_t)stream;
+  if (hw && vec)
+    hipLaunchKernelGGL((mxfp4_quantize_kernel<true, true>), grid, dim3(256), 0, s, xp, M, K, ld, packed, sf, Kp);
+  else if (hw)
+    hipLaunchKernelGGL((mxfp4_quantize_kernel<true, false>), grid, dim3(256), 0, s, xp, M, K, ld, packed, sf, Kp);
+  else if (vec)
+    hipLaunchKernelGGL((mxfp4_quantize_kernel<false, true>), grid, dim3(256), 0, s, xp, M, K, ld, packed, sf, Kp);
+  else
+    hipLaunchKernelGGL((mxfp4_quantize_kernel<false, false>), grid, dim3(256), 0, s, xp, M, K, ld, packed, sf, Kp);
+  return check_launch("bsp_mxfp4_quantize");
 }

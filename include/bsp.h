@@ -114,6 +114,26 @@ int bsp_mm_mxfp8(const uint8_t* a, const uint8_t* a_sf, const uint8_t* b, const 
                  int64_t M, int64_t N, int64_t K, void* out, int64_t ldc, int out_dtype,
                  void* stream);
 
+/* MXFP4 (mm_fp4 with use_nvfp4=False: [FV-NV] _mm_fp4, "MX-FP4" in its module docstring): e2m1
+ * values with one e8m0 scale per 32 K elements (OCP MX rule of [VLO] DiffusionMXFP8Config applied to
+ * e2m1: Es = clamp(floor(log2 amax) - 2, -127, 127), byte Es+127, 0x00 for an all-zero group,
+ * q = e2m1(fl32(x * 2^-Es)) nearest-even saturating at 6). Scales in the 128x4 layout (as NVFP4,
+ * one byte per 32 K): byte (r, c) at ((r/128)*(Kp/4) + c/4)*512 + (r%32)*16 + ((r/32)%4)*4 + c%4,
+ * Kp = ceil(K/128)*4; padded rows/columns 0x00. Size: bsp_mxfp4_sf_bytes = ceil(rows/128)*128 * Kp. */
+int bsp_mxfp4_sf_bytes(int64_t rows, int64_t K, int64_t* bytes);
+
+/* x: device bf16 [M, K] (row stride ld), K % 32 == 0 -> packed uint8 [M, K/2] (even k in the low
+ * nibble), sf (bsp_mxfp4_sf_bytes(M, K) bytes). M == 0 is a no-op. */
+int bsp_mxfp4_quantize(const void* x_bf16, int64_t M, int64_t K, int64_t ld, uint8_t* packed,
+                       uint8_t* sf, void* stream);
+
+/* C[m, n] = alpha * sum_k e2m1(A)*2^(SA-127) * e2m1(B)*2^(SB-127), fp32 accumulation on gfx950's
+ * block-scaled FP4 MFMA; alpha_dev may be NULL (alpha = 1). a: [M, K/2], b: [N, K/2] (K-major
+ * weight), scales as above, out [M, N] row stride ldc (bf16 or fp32). Requires K % 128 == 0. */
+int bsp_mm_mxfp4(const uint8_t* a_packed, const uint8_t* a_sf, const uint8_t* b_packed,
+                 const uint8_t* b_sf, const float* alpha_dev, int64_t M, int64_t N, int64_t K,
+                 void* out, int64_t ldc, int out_dtype, void* stream);
+
 /* GELU (tanh form) on bf16, out of place or in place: y = bf16(gelu(x)) with
  * gelu(x) = 0.5*x*(1 + tanh(z)), z = sqrt(2/pi)*(x + 0.044715*x^3), evaluated in fp32 through the
  * logistic form with t = exp(-2|z|) (no cancellation, no overflow); within one bf16 ulp of exact.

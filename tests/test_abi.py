@@ -31,6 +31,8 @@ def test_version_and_sf_bytes():
     assert bsp.bsp_nvfp4_sf_bytes(1, 16) == 128 * 4
     assert bsp.bsp_nvfp4_sf_bytes(0, 64) == 0
     assert bsp.bsp_nvfp4_sf_bytes(129, 80) == 256 * 8
+    assert bsp.bsp_mxfp4_sf_bytes(32760, 5120) == 32768 * 160
+    assert bsp.bsp_mxfp4_sf_bytes(1, 32) == 128 * 4
 
 
 def _st(fn, *args):
@@ -67,6 +69,10 @@ def test_gemm_shape_and_dtype_errors():
     assert st == -2
     st, _ = _st("bsp_mm_fp4", None, P, P, P, P, 8, 8, 128, P, 8, 0, None)
     assert st == -1
+    st, _ = _st("bsp_mm_mxfp4", P, P, P, P, None, 8, 8, 64, P, 8, 0, None)
+    assert st == -2
+    assert _st("bsp_mm_mxfp4", None, None, None, None, None, 8, 0, 128, None, 8, 0, None)[0] == 0
+    assert _st("bsp_mxfp4_quantize", P, 4, 48, 48, P, P, None)[0] == -2
 
 
 def test_prequantize_and_alpha_null_checks():

@@ -174,3 +174,48 @@ def test_mm_mxfp8_full_size():
     assert np.array_equal(host_u8(qx[torch.from_numpy(ur).cuda()]), rq)
     ref = X.mm_mxfp8_entries(host_u8(qx), host_u8(sx), host_u8(qw), host_u8(sw), rows, cols)
     assert_gemm_bf16(gather(c, rows, cols), ref, "cfg5 mxfp8")
+
+
+# ------------------------------------------------------------------------------------------ MXFP4
+def _rand_mxfp4_operand(rng, rows, k):
+    from oracle import mxfp4 as X4
+    packed = rng.integers(0, 256, size=(rows, k // 2)).astype(np.uint8)
+    rp, cp = X4.sf_padded_shape(rows, k)
+    lin = np.zeros((rp, cp), dtype=np.uint8)
+    lin[:rows, : k // 32] = rng.integers(110, 140, size=(rows, k // 32))
+    return packed, N.swizzle_128x4(lin)
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 64, 128), (77, 200, 256), (256, 256, 512), (300, 130, 384),
+                                   (513, 384, 640)])
+def test_mm_mxfp4_random_operands_all_elements(m, n, k):
+    from oracle import mxfp4 as X4
+    say("mm_mxfp4 random", m, n, k)
+    rng = np.random.default_rng(m * 5 + n + k)
+    pa, sa = _rand_mxfp4_operand(rng, m, k)
+    pb, sb = _rand_mxfp4_operand(rng, n, k)
+    al = f32(0.625)
+    ref = X4.mm_mxfp4(pa, sa, pb, sb, al, m, n, k)
+    args = (dev_u8(pa), dev_u8(sa), dev_u8(pb), dev_u8(sb), scalar(al))
+    c32 = bsp.bsp_mm_mxfp4(*args, out_dtype=torch.float32).cpu().numpy().astype(np.float64)
+    assert_gemm_f32(c32, ref, f"mxfp4 random {m}x{n}x{k}")
+    c16 = bsp.bsp_mm_mxfp4(*args).float().cpu().numpy().astype(np.float64)
+    assert_gemm_bf16(c16, ref, f"mxfp4 random {m}x{n}x{k}")
+    c1 = bsp.bsp_mm_mxfp4(dev_u8(pa), dev_u8(sa), dev_u8(pb), dev_u8(sb), None, torch.float32)
+    assert_gemm_f32(c1.cpu().numpy().astype(np.float64), ref / float(al), "alpha=None")
+
+
+def test_mm_mxfp4_full_size():
+    from oracle import mxfp4 as X4
+    xb, wb = tensor_bits(4, "X"), tensor_bits(4, "W")      # Wan-14B fc_in shape
+    px, sx = bsp.bsp_mxfp4_quantize(dev_bf16(xb))
+    pw, sw = bsp.bsp_mxfp4_quantize(dev_bf16(wb))
+    c = bsp.bsp_mm_mxfp4(px, sx, pw, sw)
+    m, n, k = xb.shape[0], wb.shape[0], xb.shape[1]
+    rows, cols = sample_entries(m, n, 3000, 41)
+    ur = np.unique(rows)
+    rp, _ = X4.quantize(xb[ur], layout="linear")
+    assert np.array_equal(host_u8(px[torch.from_numpy(ur).cuda()]), rp)
+    ref = X4.mm_mxfp4_entries(host_u8(px), host_u8(sx).ravel(), host_u8(pw), host_u8(sw).ravel(), 1.0,
+                              m, n, k, rows, cols)
+    assert_gemm_bf16(gather(c, rows, cols), ref, "cfg4 fc_in mxfp4")

@@ -193,3 +193,16 @@ def test_software_encoder_path_bit_exact():
     r = subprocess.run([sys.executable, "-c", _SW_SCRIPT, root], env=env, capture_output=True,
                        text=True, timeout=150)
     assert r.returncode == 0 and "SW-PATH-OK" in r.stdout, r.stdout + r.stderr
+
+
+@pytest.mark.parametrize("m,k", [(1, 32), (77, 96), (128, 256), (200, 512), (300, 1568)])
+def test_mxfp4_quantize_bit_exact(m, k):
+    from oracle import mxfp4 as X4
+    xb = W.small_case(m, k, seed=3 * m + k, outlier_frac=0.02)
+    p, s = bsp.bsp_mxfp4_quantize(dev_bf16(xb))
+    rp, rs = X4.quantize(xb)
+    assert np.array_equal(host_u8(p), rp) and np.array_equal(host_u8(s).ravel(), rs)
+    xs = W.special_values_block(seed=m, rows=m, cols=k)
+    p, s = bsp.bsp_mxfp4_quantize(dev_bf16(xs))
+    rp, rs = X4.quantize(xs)
+    assert np.array_equal(host_u8(p), rp) and np.array_equal(host_u8(s).ravel(), rs)
