@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=1024,
+    ap.add_argument("--cpu-rows", type=int, default=8192,
                     help="tokens of the FFN the CPU oracle runs for cpu_baseline")
     ap.add_argument("--no-mxfp8", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -47,14 +47,19 @@ def parse():
     return ap.parse_args()
 
 
-GEMM_SOURCE = os.path.join(ROOT, "block_scaled_precision_nvfp4_amd", "csrc", "gemm_fp4.hip")
+CSRC = os.path.join(ROOT, "block_scaled_precision_nvfp4_amd", "csrc")
+GEMM_SOURCES = ("gemm_fp4.hip", "gemm_common.hpp", "common.hpp")
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "mm_fp4_wan14b_ffn_pmc.txt")
 
 
-def source_sha256(path: str) -> str:
+def gemm_sources_sha256() -> str:
+    """Digest of the sources the NVFP4 GEMM kernel is compiled from (identifies the kernel version)."""
     import hashlib
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for name in GEMM_SOURCES:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(kernel: str):
@@ -67,7 +72,7 @@ def measured_traffic(kernel: str):
                 if ":" in line and not line.startswith("#"):
                     k, v = line.split(":", 1)
                     kv[k.strip()] = v.strip()
-        if kv.get("gemm_fp4.hip sha256") != source_sha256(GEMM_SOURCE):
+        if kv.get("kernel sources sha256") != gemm_sources_sha256():
             return None
         return float(kv[f"{kernel} hbm_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
