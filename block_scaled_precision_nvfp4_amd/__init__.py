@@ -40,6 +40,7 @@ SIGNATURES = {
     "bsp_mxfp4_quantize": ([_p, _i64, _i64, _i64, _p, _p, _p], _int),
     "bsp_mm_mxfp4": ([_p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _int, _p], _int),
     "bsp_gelu_tanh_bf16": ([_p, _p, _i64, _p], _int),
+    "bsp_nvfp4_quantize_gelu": ([_p, _i64, _i64, _i64, _p, _p, _p, _p], _int),
 }
 
 
@@ -145,6 +146,18 @@ def bsp_nvfp4_quantize(x: torch.Tensor, gsf: torch.Tensor,
                        packed: Optional[torch.Tensor] = None,
                        sf: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """(packed uint8 [M, K/2], sf uint8 [ceil(M/128)*128, ceil(K/64)*4] in the 128x4 layout)."""
+    return _nvfp4_quantize("bsp_nvfp4_quantize", x, gsf, packed, sf)
+
+
+def bsp_nvfp4_quantize_gelu(y: torch.Tensor, gsf: torch.Tensor,
+                            packed: Optional[torch.Tensor] = None,
+                            sf: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """NVFP4 quantize of bf16(gelu_tanh(y)) in one pass; outputs as bsp_nvfp4_quantize."""
+    return _nvfp4_quantize("bsp_nvfp4_quantize_gelu", y, gsf, packed, sf)
+
+
+def _nvfp4_quantize(fn: str, x: torch.Tensor, gsf: torch.Tensor, packed: Optional[torch.Tensor],
+                    sf: Optional[torch.Tensor]) -> Tuple[torch.Tensor, torch.Tensor]:
     x = _as_bf16_2d(x, "x")
     _need(gsf, "gsf", torch.float32, x.device)
     m, k = x.shape
@@ -160,7 +173,7 @@ def bsp_nvfp4_quantize(x: torch.Tensor, gsf: torch.Tensor,
         raise ValueError("packed must be contiguous with M*K/2 bytes")
     if sf.numel() < rp * kp or not sf.is_contiguous():
         raise ValueError("sf must be contiguous with bsp_nvfp4_sf_bytes(M, K) bytes")
-    _call("bsp_nvfp4_quantize", x.data_ptr(), m, k, x.stride(0), gsf.data_ptr(),
+    _call(fn, x.data_ptr(), m, k, x.stride(0), gsf.data_ptr(),
           packed.data_ptr(), sf.data_ptr(), _stream(x.device))
     return packed, sf
 

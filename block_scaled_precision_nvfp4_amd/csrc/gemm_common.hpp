@@ -65,15 +65,14 @@ __device__ __forceinline__ void store_wave_tile(const f32x16 (&acc)[4][4], float
           }
         } else {
           uint16_t* o = static_cast<uint16_t*>(out) + gm * ldc + gn;
-          const uint32_t b0 = f32_to_bf16_rne(v0), b1 = f32_to_bf16_rne(v1);
-          const uint32_t b2 = f32_to_bf16_rne(v2), b3 = f32_to_bf16_rne(v3);
+          const uint32_t p01 = bf16x2_rne(v0, v1), p23 = bf16x2_rne(v2, v3);
           if (vec_store && gn + 3 < N) {
-            *reinterpret_cast<uint2*>(o) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+            *reinterpret_cast<uint2*>(o) = make_uint2(p01, p23);
           } else {
-            if (gn + 0 < N) o[0] = (uint16_t)b0;
-            if (gn + 1 < N) o[1] = (uint16_t)b1;
-            if (gn + 2 < N) o[2] = (uint16_t)b2;
-            if (gn + 3 < N) o[3] = (uint16_t)b3;
+            if (gn + 0 < N) o[0] = (uint16_t)p01;
+            if (gn + 1 < N) o[1] = (uint16_t)(p01 >> 16);
+            if (gn + 2 < N) o[2] = (uint16_t)p23;
+            if (gn + 3 < N) o[3] = (uint16_t)(p23 >> 16);
           }
         }
       }

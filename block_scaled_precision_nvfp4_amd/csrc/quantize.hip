@@ -94,6 +94,38 @@ __global__ void alpha_kernel(const float* xg, const float* wg, float* alpha) {
 // encoder instead.
 constexpr float kSixth = 0.16666667163372040f;  // fl32(1/6) = 0x3E2AAAAB
 
+// gelu(x) = 0.5 x (1 + tanh(z)), z = sqrt(2/pi) (x + 0.044715 x^3), in fp32, rounded once to bf16
+// by the caller. 0.5 (1 + tanh z) is the logistic function of 2z, evaluated with t = 2^(-2|z| log2 e)
+// <= 1 as x / (1 + t) for z >= 0 and x t / (1 + t) for z < 0: no cancellation and no overflow.
+// v_exp_f32 and v_rcp_f32 (about 1 ulp each) keep the whole function at a dozen instructions; the
+// result is within a few fp32 ulps, far inside one bf16 ulp except next to a rounding boundary.
+// Where t would be an fp32 denormal (2|z| log2 e > 64) it is formed as t * 2^64 and the product
+// scaled back by 2^-64 at the end (a single rounding), so tiny negative outputs keep their bits.
+__device__ __forceinline__ float gelu_tanh(float x) {
+  const float k0 = 0.7978845608028654f;   // sqrt(2/pi)
+  const float k1 = 0.044715f;
+  const float k2 = -2.8853900817779268f;  // -2 log2(e)
+  const float z = k0 * (x + k1 * (x * x * x));
+  const float e = k2 * __builtin_fabsf(z);
+  const bool tiny = e < -64.0f;
+  const float ts = __builtin_amdgcn_exp2f(tiny ? e + 64.0f : e);  // t, or t * 2^64 when tiny
+  const float r = __builtin_amdgcn_rcpf(1.0f + (tiny ? 0.0f : ts));
+  const bool neg = z < 0.0f;                                  // branch-free: selects, no exec masks
+  const float m = neg ? ts : 1.0f;
+  const float sc = (neg && tiny) ? 5.421010862427522e-20f : 1.0f;  // 2^-64
+  return ((x * m) * r) * sc;
+}
+
+// 8 values -> gelu, each rounded to bf16 and widened back to fp32 (what the GELU kernel stores)
+__device__ __forceinline__ void gelu8_bf16(float (&f)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) {
+    const uint32_t p = bf16x2_rne(gelu_tanh(f[i]), gelu_tanh(f[i + 1]));
+    f[i] = bf16_lo(p);
+    f[i + 1] = bf16_hi(p);
+  }
+}
+
 template <bool VEC>
 __device__ __forceinline__ uint4 load8(const uint16_t* p) {
   if (VEC) return *reinterpret_cast<const uint4*>(p);
@@ -119,7 +151,7 @@ __device__ __forceinline__ float absmax8(const float (&f)[8]) {
   return a;
 }
 
-template <bool HWCVT, bool VEC>
+template <bool HWCVT, bool VEC, bool GELU>
 __global__ __launch_bounds__(256) void nvfp4_quantize_kernel(const uint16_t* __restrict__ x,
                                                              int64_t M, int64_t K, int64_t ld,
                                                              const float* __restrict__ gsf,
@@ -157,6 +189,7 @@ __global__ __launch_bounds__(256) void nvfp4_quantize_kernel(const uint16_t* __r
   for (int s = 0; s < 16; ++s) {
     float f[8];
     unpack8(v[s], f);
+    if (GELU) gelu8_bf16(f);  // gelu(0) = 0 keeps the padding zero
     const float a = pair_max(absmax8(f));
     const float sc = g * (a * kSixth);
     const uint32_t S = e4m3_encode_pos(sc);
@@ -326,20 +359,8 @@ __global__ __launch_bounds__(256) void mxfp4_quantize_kernel(const uint16_t* __r
 }
 
 // =============================================================================================
-// GELU (tanh form), bf16 in/out, fp32 math
+// GELU (tanh form), bf16 in/out
 // =============================================================================================
-// gelu(x) = 0.5 x (1 + tanh(z)), z = sqrt(2/pi) (x + 0.044715 x^3). Since 0.5 (1 + tanh z) is the
-// logistic function of 2z, it is evaluated with t = exp(-2|z|) <= 1 as x / (1 + t) for z >= 0 and
-// x t / (1 + t) for z < 0: no cancellation and no overflow anywhere.
-__device__ __forceinline__ float gelu_tanh(float x) {
-  const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
-  const float k1 = 0.044715f;
-  const float z = k0 * (x + k1 * (x * x * x));
-  const float t = expf(-2.0f * __builtin_fabsf(z));
-  const float num = z >= 0.0f ? x : x * t;
-  return num / (1.0f + t);
-}
-
 __global__ __launch_bounds__(256) void gelu_kernel(const uint16_t* __restrict__ x,
                                                    uint16_t* __restrict__ y, int64_t n) {
   const int64_t n8 = n / 8;
@@ -349,9 +370,7 @@ __global__ __launch_bounds__(256) void gelu_kernel(const uint16_t* __restrict__ 
     uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      uint32_t lo = f32_to_bf16_rne(gelu_tanh(bf16_lo(w[j])));
-      uint32_t hi = f32_to_bf16_rne(gelu_tanh(bf16_hi(w[j])));
-      w[j] = lo | (hi << 16);
+      w[j] = bf16x2_rne(gelu_tanh(bf16_lo(w[j])), gelu_tanh(bf16_hi(w[j])));
     }
     reinterpret_cast<uint4*>(y)[i] = make_uint4(w[0], w[1], w[2], w[3]);
   }
@@ -391,27 +410,37 @@ int launch_global_sf(const void* w, int64_t rows, int64_t K, int64_t ld, float* 
   return check_launch("bsp_nvfp4_global_sf");
 }
 
+template <bool GELU>
+static void launch_nvfp4_quantize_t(dim3 grid, const uint16_t* xp, int64_t M, int64_t K, int64_t ld,
+                                    const float* gsf, uint8_t* packed, uint8_t* sf, int64_t Kp,
+                                    bool hw, bool vec, hipStream_t s) {
+  if (hw && vec)
+    hipLaunchKernelGGL((nvfp4_quantize_kernel<true, true, GELU>), grid, dim3(256), 0, s, xp, M, K, ld,
+                       gsf, packed, sf, Kp);
+  else if (hw)
+    hipLaunchKernelGGL((nvfp4_quantize_kernel<true, false, GELU>), grid, dim3(256), 0, s, xp, M, K, ld,
+                       gsf, packed, sf, Kp);
+  else if (vec)
+    hipLaunchKernelGGL((nvfp4_quantize_kernel<false, true, GELU>), grid, dim3(256), 0, s, xp, M, K, ld,
+                       gsf, packed, sf, Kp);
+  else
+    hipLaunchKernelGGL((nvfp4_quantize_kernel<false, false, GELU>), grid, dim3(256), 0, s, xp, M, K,
+                       ld, gsf, packed, sf, Kp);
+}
+
 int launch_nvfp4_quantize(const void* x, int64_t M, int64_t K, int64_t ld, const float* gsf,
-                          uint8_t* packed, uint8_t* sf, hipStream_t s) {
+                          uint8_t* packed, uint8_t* sf, hipStream_t s, bool gelu) {
   const int64_t Mp = ceil_div(M, 128) * 128;
   const int64_t Kp = ceil_div(K / 16, 4) * 4;
   dim3 grid((unsigned)ceil_div(Kp, 16), (unsigned)(Mp / 128));
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   const bool vec = (ld % 8 == 0) && aligned16(x);
   const bool hw = hw_cvt_enabled();
-  if (hw && vec)
-    hipLaunchKernelGGL((nvfp4_quantize_kernel<true, true>), grid, dim3(256), 0, s, xp, M, K, ld, gsf,
-                       packed, sf, Kp);
-  else if (hw)
-    hipLaunchKernelGGL((nvfp4_quantize_kernel<true, false>), grid, dim3(256), 0, s, xp, M, K, ld, gsf,
-                       packed, sf, Kp);
-  else if (vec)
-    hipLaunchKernelGGL((nvfp4_quantize_kernel<false, true>), grid, dim3(256), 0, s, xp, M, K, ld, gsf,
-                       packed, sf, Kp);
+  if (gelu)
+    launch_nvfp4_quantize_t<true>(grid, xp, M, K, ld, gsf, packed, sf, Kp, hw, vec, s);
   else
-    hipLaunchKernelGGL((nvfp4_quantize_kernel<false, false>), grid, dim3(256), 0, s, xp, M, K, ld,
-                       gsf, packed, sf, Kp);
-  return check_launch("bsp_nvfp4_quantize");
+    launch_nvfp4_quantize_t<false>(grid, xp, M, K, ld, gsf, packed, sf, Kp, hw, vec, s);
+  return check_launch(gelu ? "bsp_nvfp4_quantize_gelu" : "bsp_nvfp4_quantize");
 }
 
 }  // namespace bsp
@@ -429,21 +458,28 @@ extern "C" int bsp_nvfp4_global_sf(const void* w, int64_t rows, int64_t K, int64
   return launch_global_sf(w, rows, K, ld, gsf, inv_gsf, amax, (hipStream_t)stream);
 }
 
+static int nvfp4_quantize_entry(const char* fn, const void* x, int64_t M, int64_t K, int64_t ld,
+                                const float* gsf, uint8_t* packed, uint8_t* sf, void* stream, bool gelu) {
+  BSP_REQUIRE(M >= 0 && K > 0, BSP_EINVAL, "%s: bad size M=%lld K=%lld", fn, (long long)M, (long long)K);
+  BSP_REQUIRE(K % 16 == 0, BSP_ESHAPE, "%s: K (%lld) must be a multiple of 16", fn, (long long)K);
+  BSP_REQUIRE(M <= 1 || ld >= K, BSP_ESHAPE, "%s: ld (%lld) < K (%lld)", fn, (long long)ld, (long long)K);
+  if (M == 0) return BSP_OK;
+  BSP_REQUIRE(x && gsf && packed && sf, BSP_EINVAL, "%s: null pointer", fn);
+  BSP_REQUIRE((reinterpret_cast<uintptr_t>(packed) & 3u) == 0 && (reinterpret_cast<uintptr_t>(sf) & 15u) == 0,
+              BSP_EINVAL, "%s: packed must be 4-byte and sf 16-byte aligned", fn);
+  BSP_REQUIRE(ceil_div(M, 128) < 65536, BSP_ESHAPE, "%s: M too large", fn);
+  if (int e = check_device()) return e;
+  return launch_nvfp4_quantize(x, M, K, ld, gsf, packed, sf, (hipStream_t)stream, gelu);
+}
+
 extern "C" int bsp_nvfp4_quantize(const void* x, int64_t M, int64_t K, int64_t ld, const float* gsf,
                                   uint8_t* packed, uint8_t* sf, void* stream) {
-  BSP_REQUIRE(M >= 0 && K > 0, BSP_EINVAL, "bsp_nvfp4_quantize: bad size M=%lld K=%lld",
-              (long long)M, (long long)K);
-  BSP_REQUIRE(K % 16 == 0, BSP_ESHAPE, "bsp_nvfp4_quantize: K (%lld) must be a multiple of 16",
-              (long long)K);
-  BSP_REQUIRE(M <= 1 || ld >= K, BSP_ESHAPE, "bsp_nvfp4_quantize: ld (%lld) < K (%lld)",
-              (long long)ld, (long long)K);
-  if (M == 0) return BSP_OK;
-  BSP_REQUIRE(x && gsf && packed && sf, BSP_EINVAL, "bsp_nvfp4_quantize: null pointer");
-  BSP_REQUIRE((reinterpret_cast<uintptr_t>(packed) & 3u) == 0 && (reinterpret_cast<uintptr_t>(sf) & 15u) == 0,
-              BSP_EINVAL, "bsp_nvfp4_quantize: packed must be 4-byte and sf 16-byte aligned");
-  BSP_REQUIRE(ceil_div(M, 128) < 65536, BSP_ESHAPE, "bsp_nvfp4_quantize: M too large");
-  if (int e = check_device()) return e;
-  return launch_nvfp4_quantize(x, M, K, ld, gsf, packed, sf, (hipStream_t)stream);
+  return nvfp4_quantize_entry("bsp_nvfp4_quantize", x, M, K, ld, gsf, packed, sf, stream, false);
+}
+
+extern "C" int bsp_nvfp4_quantize_gelu(const void* y, int64_t M, int64_t K, int64_t ld,
+                                       const float* gsf, uint8_t* packed, uint8_t* sf, void* stream) {
+  return nvfp4_quantize_entry("bsp_nvfp4_quantize_gelu", y, M, K, ld, gsf, packed, sf, stream, true);
 }
 
 extern "C" int bsp_nvfp4_prequantize_weight(const void* w, int64_t N, int64_t K, int64_t ld,

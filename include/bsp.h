@@ -136,11 +136,21 @@ int bsp_mm_mxfp4(const uint8_t* a_packed, const uint8_t* a_sf, const uint8_t* b_
 
 /* GELU (tanh form) on bf16, out of place or in place: y = bf16(gelu(x)) with
  * gelu(x) = 0.5*x*(1 + tanh(z)), z = sqrt(2/pi)*(x + 0.044715*x^3), evaluated in fp32 through the
- * logistic form with t = exp(-2|z|) (no cancellation, no overflow); within one bf16 ulp of exact.
+ * logistic form with t = exp(-2|z|) (no cancellation, no overflow); within one bf16 ulp of exact
+ * (the fp32 evaluation uses the hardware exp2 and reciprocal, a few fp32 ulps).
  * It is the activation between fc_in and fc_out of the Wan FFN, both of which are in the NVFP4
  * layer set of [FV-QAT] (DEFAULT_FP4_LAYERS: ffn.fc_in, ffn.fc_out).
  * x, y: device bf16 [n], contiguous, 16-byte aligned. */
 int bsp_gelu_tanh_bf16(const void* x, void* y, int64_t n, void* stream);
+
+/* Producer-fused quantize of the FFN activation: exactly bsp_nvfp4_quantize applied to
+ * bsp_gelu_tanh_bf16(y) (GELU evaluated and rounded to bf16 per element as above, then the NVFP4
+ * block quantization of those bf16 values), in one pass over y without writing the bf16 activation.
+ * [FV-NV] apply: a producer may hand mm_fp4 an already quantized (packed, scales, global scale)
+ * triple instead of bf16 activations; here the producer is the GELU between fc_in and fc_out.
+ * Arguments, layouts and errors as bsp_nvfp4_quantize (y: device bf16 [M, K], row stride ld). */
+int bsp_nvfp4_quantize_gelu(const void* y_bf16, int64_t M, int64_t K, int64_t ld, const float* gsf_dev,
+                            uint8_t* packed, uint8_t* sf, void* stream);
 
 #ifdef __cplusplus
 }

@@ -21,6 +21,12 @@ pytestmark = pytest.mark.gpu
 f32 = np.float32
 
 
+def _assert_bf16_is_rne_of_f32(c16, c32):
+    """The bf16 epilogue rounds the same fp32 value the fp32 epilogue stores, to nearest even."""
+    want = W.f32_to_bf16_bits(c32.cpu().numpy())
+    assert np.array_equal(host_bits(c16), want)
+
+
 def _rand_nvfp4_operand(rng, rows, k):
     packed = rng.integers(0, 256, size=(rows, k // 2)).astype(np.uint8)
     rp, cp = N.sf_padded_shape(rows, k)
@@ -39,10 +45,13 @@ def test_mm_fp4_random_operands_all_elements(m, n, k):
     al = f32(rng.uniform(0.01, 2.0))
     ref = N.mm_fp4(pa, sa, pb, sb, al, m, n, k)
     args = (dev_u8(pa), dev_u8(sa), dev_u8(pb), dev_u8(sb), scalar(al))
-    c32 = bsp.bsp_mm_fp4(*args, out_dtype=torch.float32).cpu().numpy().astype(np.float64)
+    t32 = bsp.bsp_mm_fp4(*args, out_dtype=torch.float32)
+    c32 = t32.cpu().numpy().astype(np.float64)
     assert_gemm_f32(c32, ref, f"random {m}x{n}x{k}")
-    c16 = bsp.bsp_mm_fp4(*args, out_dtype=torch.bfloat16).float().cpu().numpy().astype(np.float64)
+    t16 = bsp.bsp_mm_fp4(*args, out_dtype=torch.bfloat16)
+    c16 = t16.float().cpu().numpy().astype(np.float64)
     assert_gemm_bf16(c16, ref, f"random {m}x{n}x{k}")
+    _assert_bf16_is_rne_of_f32(t16, t32)
     # the fp32 result should be far inside the budget: the products are exact in fp16
     assert np.linalg.norm(c32 - ref) <= 1e-5 * np.linalg.norm(ref)
 
@@ -156,10 +165,13 @@ def test_mm_mxfp8_random_operands_all_elements(m, n, k):
     qb, sb = _rand_mx_operand(rng, n, k)
     ref = X.mm_mxfp8(qa, sa, qb, sb, m, n, k)
     args = (dev_u8(qa), dev_u8(sa), dev_u8(qb), dev_u8(sb))
-    c32 = bsp.bsp_mm_mxfp8(*args, out_dtype=torch.float32).cpu().numpy().astype(np.float64)
+    t32 = bsp.bsp_mm_mxfp8(*args, out_dtype=torch.float32)
+    c32 = t32.cpu().numpy().astype(np.float64)
     assert_gemm_f32(c32, ref, f"mx random {m}x{n}x{k}")
-    c16 = bsp.bsp_mm_mxfp8(*args).float().cpu().numpy().astype(np.float64)
+    t16 = bsp.bsp_mm_mxfp8(*args)
+    c16 = t16.float().cpu().numpy().astype(np.float64)
     assert_gemm_bf16(c16, ref, f"mx random {m}x{n}x{k}")
+    _assert_bf16_is_rne_of_f32(t16, t32)
 
 
 def test_mm_mxfp8_full_size():
@@ -197,10 +209,13 @@ def test_mm_mxfp4_random_operands_all_elements(m, n, k):
     al = f32(0.625)
     ref = X4.mm_mxfp4(pa, sa, pb, sb, al, m, n, k)
     args = (dev_u8(pa), dev_u8(sa), dev_u8(pb), dev_u8(sb), scalar(al))
-    c32 = bsp.bsp_mm_mxfp4(*args, out_dtype=torch.float32).cpu().numpy().astype(np.float64)
+    t32 = bsp.bsp_mm_mxfp4(*args, out_dtype=torch.float32)
+    c32 = t32.cpu().numpy().astype(np.float64)
     assert_gemm_f32(c32, ref, f"mxfp4 random {m}x{n}x{k}")
-    c16 = bsp.bsp_mm_mxfp4(*args).float().cpu().numpy().astype(np.float64)
+    t16 = bsp.bsp_mm_mxfp4(*args)
+    c16 = t16.float().cpu().numpy().astype(np.float64)
     assert_gemm_bf16(c16, ref, f"mxfp4 random {m}x{n}x{k}")
+    _assert_bf16_is_rne_of_f32(t16, t32)
     c1 = bsp.bsp_mm_mxfp4(dev_u8(pa), dev_u8(sa), dev_u8(pb), dev_u8(sb), None, torch.float32)
     assert_gemm_f32(c1.cpu().numpy().astype(np.float64), ref / float(al), "alpha=None")
 

@@ -164,6 +164,65 @@ def test_gelu_within_one_bf16_ulp():
     assert np.array_equal(host_bits(x), got[:1001])
 
 
+def _gelu_ref_check(xb, got):
+    """GPU GELU bytes against the oracle: within one bf16 ulp everywhere, equal almost everywhere."""
+    ref = A.gelu_tanh_bf16_bits(xb)
+    gv = W.bf16_bits_to_f32(got).astype(np.float64)
+    rv = W.bf16_bits_to_f32(ref).astype(np.float64)
+    assert np.all(np.abs(gv - rv) <= np.abs(rv) * 2.0 ** -7 + 2.0 ** -126)
+    assert np.mean(got == ref) > 0.99
+
+
+@pytest.mark.parametrize("m,k", [(1, 16), (77, 48), (129, 96), (300, 1536), (256, 1040)])
+@pytest.mark.parametrize("gsf", [1.0, 0.37])
+def test_nvfp4_quantize_gelu_is_quantize_of_gpu_gelu(m, k, gsf):
+    """The fused kernel equals the oracle's NVFP4 quantize of the GPU's own bf16 GELU values (the
+    stage-wise parity of the FFN: the GELU itself is checked against the oracle to one bf16 ulp)."""
+    say("nvfp4_quantize_gelu", m, k, gsf)
+    yb = W.small_case(m, k, seed=3 * m + k, std=2.5, outlier_frac=0.02)
+    y = dev_bf16(yb)
+    hb = host_bits(bsp.bsp_gelu_tanh_bf16(y))
+    _gelu_ref_check(yb, hb)
+    p, sf = bsp.bsp_nvfp4_quantize_gelu(y, scalar(gsf))
+    rp, rs = N.quantize(hb.reshape(m, k), f32(gsf))
+    assert np.array_equal(host_u8(p), rp)
+    assert np.array_equal(host_u8(sf).ravel(), rs)
+
+
+def test_nvfp4_quantize_gelu_strided_and_special():
+    yb = W.special_values_block(seed=13, rows=200, cols=512)
+    big = np.zeros((200, 520), dtype=np.uint16)
+    big[:, :512] = yb
+    y = dev_bf16(big)[:, :512]
+    hb = host_bits(bsp.bsp_gelu_tanh_bf16(dev_bf16(yb)))
+    p, sf = bsp.bsp_nvfp4_quantize_gelu(y, scalar(1.0))
+    rp, rs = N.quantize(hb.reshape(200, 512), f32(1.0))
+    assert np.array_equal(host_u8(p), rp) and np.array_equal(host_u8(sf).ravel(), rs)
+
+
+@pytest.mark.parametrize("m,k", [(32760, 8960), (32760, 13824)])
+def test_nvfp4_quantize_gelu_full_size_sampled_rows(m, k):
+    """The FFN activations at the Wan-1.3B and Wan-14B fc_in output shapes, in the bench's launch
+    configuration; sampled rows against the oracle, every padding scale byte checked."""
+    say("full-size quantize_gelu", m, k)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(k)
+    y = (torch.randn((m, k), device="cuda", generator=g) * 2.0).to(torch.bfloat16)
+    p, sf = bsp.bsp_nvfp4_quantize_gelu(y, scalar(1.0))
+    h = bsp.bsp_gelu_tanh_bf16(y)
+    rows = np.unique(np.concatenate([np.random.default_rng(k).integers(0, m, 40), [0, 127, 128, m - 1]]))
+    ri = torch.from_numpy(rows).cuda()
+    hb = host_bits(h[ri])
+    yb = host_bits(y[ri])
+    _gelu_ref_check(yb.ravel(), hb.ravel())
+    ref_p, ref_s = N.quantize(hb.reshape(len(rows), k), f32(1.0), layout="linear")
+    assert np.array_equal(host_u8(p[ri]), ref_p)
+    rp, cp = N.sf_padded_shape(m, k)
+    lin = N.unswizzle_128x4(host_u8(sf).ravel(), rp, cp)
+    assert np.array_equal(lin[rows, : k // 16], ref_s)
+    assert np.all(lin[m:] == 0)
+
+
 _SW_SCRIPT = r"""
 import sys, numpy as np
 sys.path.insert(0, sys.argv[1])
