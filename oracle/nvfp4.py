@@ -120,7 +120,7 @@ def unswizzle_128x4(sf_flat: np.ndarray, rp: int, cp: int) -> np.ndarray:
 # a2: quantize
 # ----------------------------------------------------------------------------------------
 def quantize_blocks(xf: np.ndarray, gsf) -> tuple:
-    """Quantize fp32 values [rows, nblocks, 16] under global scale gsf.
+    """Quantize fp32 values [rows, nblocks, 16] under global scale gsf (a scalar, or one per row).
 
     Returns (codes [rows, nblocks, 16] uint8, scale bytes [rows, nblocks] uint8).
     Reading U1, per 16-element block:
@@ -130,7 +130,9 @@ def quantize_blocks(xf: np.ndarray, gsf) -> tuple:
       r  = 0 if sd == 0 else fl32(g / sd)  (one correctly rounded division)
       q_i = e2m1(fl32(x_i * r))
     """
-    g = F32(gsf)
+    g = np.asarray(gsf, dtype=np.float32)
+    if g.ndim:                   # one global scale per row (per-token scales): [rows] -> [rows, 1]
+        g = g.reshape(g.shape + (1,) * (np.ndim(xf) - 1 - g.ndim))
     xf = np.asarray(xf, dtype=np.float32)
     a = np.max(np.abs(xf), axis=-1).astype(np.float32)
     s = (g * (a * C_SIXTH).astype(np.float32)).astype(np.float32)
@@ -179,6 +181,37 @@ def quantize(x_bits: np.ndarray, gsf, layout: str = "128x4"):
     return packed, swizzle_128x4(lin)
 
 
+def row_global_sf(x_bits: np.ndarray) -> np.ndarray:
+    """Per-token (per-row) encode scales: gsf_m = fl32(2688 / amax_m), 1.0 for an all-zero row.
+
+    SGLang nvfp4_online.py, ``NVFP4OnlineConfig.__init__``: the weight scale is static while the
+    activation fp32 scales are computed per token at run time. Reading U22: each row's scale
+    follows the same rule as the tensor scale of ``global_sf`` applied to that row alone.
+    """
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    return np.array([global_sf(x_bits[i:i + 1])[0] for i in range(x_bits.shape[0])],
+                    dtype=np.float32)
+
+
+def quantize_per_token(x_bits: np.ndarray, layout: str = "128x4"):
+    """NVFP4 quantize with one encode scale per row; returns (packed, sf, gsf_rows [M] fp32).
+    Row m is quantized exactly as ``quantize`` would with gsf = gsf_rows[m]."""
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    m, k = x_bits.shape
+    if k % BLOCK:
+        raise ValueError("K must be a multiple of 16")
+    g_rows = row_global_sf(x_bits)
+    nb = k // BLOCK
+    codes, S = quantize_blocks(bf16_to_f32(x_bits).reshape(m, nb, BLOCK), g_rows)
+    packed = pack_nibbles(codes.reshape(m, k))
+    if layout == "linear":
+        return packed, S, g_rows
+    rp, cp = sf_padded_shape(m, k)
+    lin = np.zeros((rp, cp), dtype=np.uint8)
+    lin[:m, :nb] = S
+    return packed, swizzle_128x4(lin), g_rows
+
+
 def quantize_rows(x_bits: np.ndarray, gsf):
     """Quantize a subset of rows; returns (packed rows, [rows, K/16] scale bytes)."""
     return quantize(x_bits, gsf, layout="linear")
@@ -219,6 +252,18 @@ def mm_fp4(a_packed, a_sf, b_packed, b_sf, alpha_val, m: int, n: int, k: int,
         A = dequant_rows(a_packed, a_sf, np.arange(r0, r1), m, k)
         out[r0:r1] = A @ B.T
     return np.float64(F32(alpha_val)) * out
+
+
+def alpha_rows(x_gsf_rows, w_gsf) -> np.ndarray:
+    """Per-token alphas fl32(1 / fl32(x_gsf[m] * w_gsf)) (the scalar alpha, row by row)."""
+    xg = np.asarray(x_gsf_rows, dtype=np.float32)
+    return (F32(1.0) / (xg * F32(w_gsf)).astype(np.float32)).astype(np.float32)
+
+
+def mm_fp4_rowscale(a_packed, a_sf, b_packed, b_sf, x_gsf_rows, w_gsf, m: int, n: int, k: int):
+    """mm_fp4 with per-token activation scales: row m of C is scaled by alpha_rows(...)[m]."""
+    c = mm_fp4(a_packed, a_sf, b_packed, b_sf, F32(1.0), m, n, k)
+    return c * alpha_rows(x_gsf_rows, w_gsf).astype(np.float64)[:, None]
 
 
 def mm_fp4_entries(a_packed, a_sf, b_packed, b_sf, alpha_val, m: int, n: int, k: int,

@@ -285,3 +285,81 @@ def test_dequantized_products_fit_bf16():
 def test_k_must_be_multiple_of_16():
     with pytest.raises(ValueError):
         N.quantize(np.zeros((2, 24), dtype=np.uint16), f32(1.0))
+
+
+# ------------------------------------------------------------------- f3 per-token activation scales
+def test_per_token_is_scale_invariant_row_by_row():
+    """Rows that are power-of-two multiples of one row quantize to identical codes and scale bytes,
+    and their per-row encode scales differ by exactly that power of two: the scale is per row (a
+    shared tensor scale would give different bytes) and follows 2688/amax row by row."""
+    base = W.small_case(1, 256, 21, outlier_frac=0.05)
+    exps = np.array([0, 3, -7, 12, -20, 1], dtype=np.int64)
+    xf = W.bf16_bits_to_f32(base)[0][None, :] * (2.0 ** exps[:, None]).astype(np.float32)
+    xb = W.f32_to_bf16_bits(xf)
+    assert np.array_equal(W.bf16_bits_to_f32(xb), xf)        # the scaling is exact in bf16
+    packed, sf, g = N.quantize_per_token(xb, layout="linear")
+    for r in range(1, len(exps)):
+        assert np.array_equal(packed[r], packed[0]) and np.array_equal(sf[r], sf[0])
+        assert g[r] == np.float32(g[0] * np.float32(2.0 ** -int(exps[r])))
+    # a per-tensor scale quantizes the small rows differently
+    gp = N.global_sf(xb)[0]
+    _, sf_t = N.quantize(xb, gp, layout="linear")
+    assert not np.array_equal(sf_t[4], sf[4])
+
+
+def test_per_token_row_max_block_gets_448_and_zero_row():
+    xb = W.small_case(9, 512, 5, outlier_frac=0.02).copy()
+    xb[3] = 0                                                  # an all-zero token
+    packed, sf, g = N.quantize_per_token(xb, layout="linear")
+    assert g[3] == np.float32(1.0) and not sf[3].any() and not packed[3].any()
+    xf = W.bf16_bits_to_f32(xb).reshape(9, 32, 16)
+    for r in range(9):
+        if r == 3:
+            continue
+        amax = np.max(np.abs(xf[r]))
+        assert g[r] == np.float32(np.float32(2688.0) / amax)
+        blk = np.argwhere(np.max(np.abs(xf[r]), axis=-1) == amax)[0][0]
+        assert sf[r, blk] == 0x7E
+
+
+def test_per_token_single_row_reduces_to_tensor_scale():
+    xb = W.small_case(1, 1024, 8)
+    p1, s1, g1 = N.quantize_per_token(xb)
+    g = N.global_sf(xb)[0]
+    p2, s2 = N.quantize(xb, g)
+    assert g1[0] == g and np.array_equal(p1, p2) and np.array_equal(s1, s2)
+
+
+def test_mm_fp4_rowscale_brute_force_and_alpha_rows():
+    rng = np.random.default_rng(31)
+    m, n, k = 4, 6, 32
+    ca, la, pa, sa = _rand_operand(rng, m, k)
+    cb, lb, pb, sb = _rand_operand(rng, n, k)
+    e2 = F.e2m1_decode_table()
+    e4 = F.e4m3_decode_table()
+    xg = np.array([1.0, 0.37, 2688.0 / 3.0, 1e-3], dtype=np.float32)
+    wg = np.float32(512.5)
+    ar = N.alpha_rows(xg, wg)
+    for i in range(m):
+        assert ar[i] == N.alpha(xg[i], wg)
+    ref = np.zeros((m, n))
+    for i in range(m):
+        for j in range(n):
+            acc = 0.0
+            for kk in range(k):
+                acc += e2[ca[i, kk]] * e4[la[i, kk // 16]] * e2[cb[j, kk]] * e4[lb[j, kk // 16]]
+            ref[i, j] = float(ar[i]) * acc
+    got = N.mm_fp4_rowscale(pa, sa, pb, sb, xg, wg, m, n, k)
+    assert np.allclose(got, ref, rtol=1e-12, atol=0)
+
+
+def test_per_token_linear_approximates_the_bf16_product():
+    """Per-token activation scales + a tensor-scaled weight reconstruct X W^T to NVFP4 accuracy."""
+    xb = W.small_case(64, 256, 2, outlier_frac=0.02)
+    wb = W.small_case(32, 256, 3, std=0.02)
+    px, sx, gx = N.quantize_per_token(xb)
+    gw = N.global_sf(wb)[0]
+    pw, sw = N.quantize(wb, gw)
+    c = N.mm_fp4_rowscale(px, sx, pw, sw, gx, gw, 64, 32, 256)
+    full = W.bf16_bits_to_f32(xb).astype(np.float64) @ W.bf16_bits_to_f32(wb).astype(np.float64).T
+    assert np.linalg.norm(c - full) / np.linalg.norm(full) < 0.15
