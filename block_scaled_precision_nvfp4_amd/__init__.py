@@ -41,6 +41,8 @@ SIGNATURES = {
     "bsp_mm_mxfp4": ([_p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _int, _p], _int),
     "bsp_gelu_tanh_bf16": ([_p, _p, _i64, _p], _int),
     "bsp_nvfp4_quantize_gelu": ([_p, _i64, _i64, _i64, _p, _p, _p, _p], _int),
+    "bsp_nvfp4_quantize_per_token": ([_p, _i64, _i64, _i64, _p, _p, _p, _p], _int),
+    "bsp_mm_fp4_per_token": ([_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _int, _p], _int),
 }
 
 
@@ -178,6 +180,34 @@ def _nvfp4_quantize(fn: str, x: torch.Tensor, gsf: torch.Tensor, packed: Optiona
     return packed, sf
 
 
+def bsp_nvfp4_quantize_per_token(x: torch.Tensor, packed: Optional[torch.Tensor] = None,
+                                 sf: Optional[torch.Tensor] = None,
+                                 gsf_rows: Optional[torch.Tensor] = None):
+    """NVFP4 quantize with one encode scale per row: (packed, sf, gsf_rows fp32 [M])."""
+    x = _as_bf16_2d(x, "x")
+    m, k = x.shape
+    rp = -(-m // 128) * 128
+    kp = -(-(k // 16) // 4) * 4
+    if packed is None:
+        packed = torch.empty((m, k // 2), dtype=torch.uint8, device=x.device)
+    if sf is None:
+        sf = torch.empty((rp, kp), dtype=torch.uint8, device=x.device)
+    if gsf_rows is None:
+        gsf_rows = torch.empty((m,), dtype=torch.float32, device=x.device)
+    _need(packed, "packed", torch.uint8, x.device)
+    _need(sf, "sf", torch.uint8, x.device)
+    _need(gsf_rows, "gsf_rows", torch.float32, x.device)
+    if packed.numel() < m * (k // 2) or not packed.is_contiguous():
+        raise ValueError("packed must be contiguous with M*K/2 bytes")
+    if sf.numel() < rp * kp or not sf.is_contiguous():
+        raise ValueError("sf must be contiguous with bsp_nvfp4_sf_bytes(M, K) bytes")
+    if gsf_rows.numel() < m or not gsf_rows.is_contiguous():
+        raise ValueError("gsf_rows must be a contiguous fp32 vector of M scales")
+    _call("bsp_nvfp4_quantize_per_token", x.data_ptr(), m, k, x.stride(0), packed.data_ptr(),
+          sf.data_ptr(), gsf_rows.data_ptr(), _stream(x.device))
+    return packed, sf, gsf_rows
+
+
 def bsp_nvfp4_prequantize_weight(w: torch.Tensor):
     """Load-time: (packed, sf, gsf, inv_gsf, amax) for bf16 weight w [N, K]."""
     w = _as_bf16_2d(w, "w")
@@ -203,11 +233,34 @@ def bsp_mm_fp4(a: torch.Tensor, a_sf: torch.Tensor, b: torch.Tensor, b_sf: torch
                alpha: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16,
                out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """C [M, N] = alpha * A . B^T. a: packed [M, K/2], b: packed weight [N, K/2] (K-major)."""
+    m, n, k, code, out = _mm_fp4_args(a, a_sf, b, b_sf, out_dtype, out)
+    _need(alpha, "alpha", torch.float32, a.device)
+    _call("bsp_mm_fp4", a.data_ptr(), a_sf.data_ptr(), b.data_ptr(), b_sf.data_ptr(),
+          alpha.data_ptr(), m, n, k, out.data_ptr(), out.stride(0), code, _stream(a.device))
+    return out
+
+
+def bsp_mm_fp4_per_token(a: torch.Tensor, a_sf: torch.Tensor, b: torch.Tensor, b_sf: torch.Tensor,
+                         x_gsf_rows: torch.Tensor, w_gsf: torch.Tensor,
+                         out_dtype: torch.dtype = torch.bfloat16,
+                         out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C [M, N] = alpha_m * A . B^T with alpha_m = 1/(x_gsf_rows[m] * w_gsf) (per-token scales)."""
+    m, n, k, code, out = _mm_fp4_args(a, a_sf, b, b_sf, out_dtype, out)
+    _need(x_gsf_rows, "x_gsf_rows", torch.float32, a.device)
+    _need(w_gsf, "w_gsf", torch.float32, a.device)
+    if x_gsf_rows.numel() < m or not x_gsf_rows.is_contiguous():
+        raise ValueError("x_gsf_rows must be a contiguous fp32 vector of M scales")
+    _call("bsp_mm_fp4_per_token", a.data_ptr(), a_sf.data_ptr(), b.data_ptr(), b_sf.data_ptr(),
+          x_gsf_rows.data_ptr(), w_gsf.data_ptr(), m, n, k, out.data_ptr(), out.stride(0), code,
+          _stream(a.device))
+    return out
+
+
+def _mm_fp4_args(a, a_sf, b, b_sf, out_dtype, out):
     _need(a, "a", torch.uint8)
     dev = a.device
     for t, nm in ((a_sf, "a_sf"), (b, "b"), (b_sf, "b_sf")):
         _need(t, nm, torch.uint8, dev)
-    _need(alpha, "alpha", torch.float32, dev)
     if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[1]:
         raise ValueError(f"a {tuple(a.shape)} and b {tuple(b.shape)} must be [M, K/2] and [N, K/2]")
     if not (a.is_contiguous() and b.is_contiguous() and a_sf.is_contiguous() and b_sf.is_contiguous()):
@@ -223,9 +276,7 @@ def bsp_mm_fp4(a: torch.Tensor, a_sf: torch.Tensor, b: torch.Tensor, b_sf: torch
         raise ValueError(f"out must be [{m}, {n}] with unit column stride")
     if a_sf.numel() < bsp_nvfp4_sf_bytes(m, k) or b_sf.numel() < bsp_nvfp4_sf_bytes(n, k):
         raise ValueError("scale buffers are smaller than bsp_nvfp4_sf_bytes")
-    _call("bsp_mm_fp4", a.data_ptr(), a_sf.data_ptr(), b.data_ptr(), b_sf.data_ptr(),
-          alpha.data_ptr(), m, n, k, out.data_ptr(), out.stride(0), code, _stream(dev))
-    return out
+    return m, n, k, code, out
 
 
 # ------------------------------------------------------------------------------------- MXFP8

@@ -36,8 +36,10 @@ __device__ __forceinline__ void tile_coords(int bid, int ntm, int ntn, int& tm, 
 // Epilogue of a 128x128 wave tile made of 4x4 MFMA 32x32 tiles acc[n][m] holding D[n][m] (the
 // MFMA's A operand is the B (weight) fragment): a lane holds output column gm = m0w + 32m + (lane%32)
 // (a row of C) and, per group b, the four consecutive C columns n0w + 32n + 8b + 4*(lane/32) + 0..3.
+// alpha[m] multiplies the lane's row of sub-tile m (the same value four times for a tensor alpha).
 template <bool OUT_F32>
-__device__ __forceinline__ void store_wave_tile(const f32x16 (&acc)[4][4], float alpha, int64_t m0w,
+__device__ __forceinline__ void store_wave_tile(const f32x16 (&acc)[4][4], const float (&alpha)[4],
+                                                int64_t m0w,
                                                 int64_t n0w, int64_t M, int64_t N, void* out,
                                                 int64_t ldc, bool vec_store, int li, int h) {
 #pragma unroll
@@ -49,10 +51,10 @@ __device__ __forceinline__ void store_wave_tile(const f32x16 (&acc)[4][4], float
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const int64_t gn = n0w + n * 32 + 8 * b + 4 * h;
-        const float v0 = alpha * acc[n][m][4 * b + 0];
-        const float v1 = alpha * acc[n][m][4 * b + 1];
-        const float v2 = alpha * acc[n][m][4 * b + 2];
-        const float v3 = alpha * acc[n][m][4 * b + 3];
+        const float v0 = alpha[m] * acc[n][m][4 * b + 0];
+        const float v1 = alpha[m] * acc[n][m][4 * b + 1];
+        const float v2 = alpha[m] * acc[n][m][4 * b + 2];
+        const float v3 = alpha[m] * acc[n][m][4 * b + 3];
         if (OUT_F32) {
           float* o = static_cast<float*>(out) + gm * ldc + gn;
           if (vec_store && gn + 3 < N) {

@@ -163,11 +163,14 @@ __device__ __forceinline__ f16x8 frag_deq(const Frags& f, int q, int j) {
   return dequant8(comp(f.pb[j >> 2][q - 4], j & 3), scale_pair(comp(f.wb, q - 4), j >> 1));
 }
 
-template <bool OUT_F32>
+// ROWSCALE: per-token activation scales; alpha_ptr is then the [M] array of row encode scales
+// and w_gsf_ptr the weight's encode scale, alpha_m = fl32(1 / fl32(x_gsf[m] * w_gsf)).
+template <bool OUT_F32, bool ROWSCALE>
 __global__ __launch_bounds__(256, 1) void mm_fp4_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint8_t* __restrict__ B,
-    const uint8_t* __restrict__ SB, const float* __restrict__ alpha_ptr, int64_t M, int64_t N,
-    int64_t K, void* __restrict__ out, int64_t ldc, int ntm, int ntn, bool vec_store) {
+    const uint8_t* __restrict__ SB, const float* __restrict__ alpha_ptr,
+    const float* __restrict__ w_gsf_ptr, int64_t M, int64_t N, int64_t K, void* __restrict__ out,
+    int64_t ldc, int ntm, int ntn, bool vec_store) {
   __shared__ Stage st[NSTAGE];
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
@@ -259,50 +262,85 @@ __global__ __launch_bounds__(256, 1) void mm_fp4_kernel(
   wait_vmcnt<0>();
 
   // operands carried 2^-8 each (scale_pair): the products are 2^-16 of the true ones
-  const float alpha = *alpha_ptr * 65536.0f;
+  float alpha[4];
+  if (ROWSCALE) {
+    const float wg = *w_gsf_ptr;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int64_t gm = m0 + wm * 128 + m * 32 + li;
+      alpha[m] = gm < M ? (1.0f / (alpha_ptr[gm] * wg)) * 65536.0f : 0.0f;
+    }
+  } else {
+    const float a = *alpha_ptr * 65536.0f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) alpha[m] = a;
+  }
   store_wave_tile<OUT_F32>(acc, alpha, m0 + wm * 128, n0 + wn * 128, M, N, out, ldc, vec_store, li, h);
 }
 
 }  // namespace fp4
 
-int launch_mm_fp4(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
-                  const float* alpha, int64_t M, int64_t N, int64_t K, void* out, int64_t ldc,
-                  int out_dtype, hipStream_t s) {
+template <bool ROWSCALE>
+static void launch_mm_fp4_t(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
+                            const float* alpha, const float* w_gsf, int64_t M, int64_t N, int64_t K,
+                            void* out, int64_t ldc, int out_dtype, hipStream_t s) {
   const int64_t ntm = ceil_div(M, fp4::BM), ntn = ceil_div(N, fp4::BN);
   const int64_t tiles = ntm * ntn;
   const size_t esz = out_dtype == BSP_OUT_F32 ? 4 : 2;
   const bool vec = (ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(out) & (4 * esz - 1)) == 0);
   if (out_dtype == BSP_OUT_F32)
-    hipLaunchKernelGGL(fp4::mm_fp4_kernel<true>, dim3((unsigned)tiles), dim3(256), 0, s, a, sa, b, sb,
-                       alpha, M, N, K, out, ldc, (int)ntm, (int)ntn, vec);
+    hipLaunchKernelGGL((fp4::mm_fp4_kernel<true, ROWSCALE>), dim3((unsigned)tiles), dim3(256), 0, s, a,
+                       sa, b, sb, alpha, w_gsf, M, N, K, out, ldc, (int)ntm, (int)ntn, vec);
   else
-    hipLaunchKernelGGL(fp4::mm_fp4_kernel<false>, dim3((unsigned)tiles), dim3(256), 0, s, a, sa, b, sb,
-                       alpha, M, N, K, out, ldc, (int)ntm, (int)ntn, vec);
-  return check_launch("bsp_mm_fp4");
+    hipLaunchKernelGGL((fp4::mm_fp4_kernel<false, ROWSCALE>), dim3((unsigned)tiles), dim3(256), 0, s, a,
+                       sa, b, sb, alpha, w_gsf, M, N, K, out, ldc, (int)ntm, (int)ntn, vec);
 }
 
 }  // namespace bsp
 
 using namespace bsp;
 
+static int mm_fp4_checks(const char* fn, const uint8_t* a_packed, const uint8_t* a_sf,
+                         const uint8_t* b_packed, const uint8_t* b_sf, const float* alpha_dev,
+                         int64_t M, int64_t N, int64_t K, void* out, int64_t ldc, int out_dtype) {
+  BSP_REQUIRE(M >= 0 && N >= 0 && K > 0, BSP_EINVAL, "%s: bad size M=%lld N=%lld K=%lld", fn,
+              (long long)M, (long long)N, (long long)K);
+  BSP_REQUIRE(out_dtype == BSP_OUT_BF16 || out_dtype == BSP_OUT_F32, BSP_EDTYPE,
+              "%s: out_dtype must be BSP_OUT_BF16 (0) or BSP_OUT_F32 (1), got %d", fn, out_dtype);
+  BSP_REQUIRE(K % 64 == 0, BSP_ESHAPE, "%s: K (%lld) must be a multiple of 64", fn, (long long)K);
+  BSP_REQUIRE(M <= 1 || ldc >= N, BSP_ESHAPE, "%s: ldc (%lld) < N (%lld)", fn, (long long)ldc,
+              (long long)N);
+  if (M == 0 || N == 0) return 1;
+  BSP_REQUIRE(a_packed && a_sf && b_packed && b_sf && alpha_dev && out, BSP_EINVAL, "%s: null pointer", fn);
+  BSP_REQUIRE(((reinterpret_cast<uintptr_t>(a_packed) | reinterpret_cast<uintptr_t>(b_packed) |
+                reinterpret_cast<uintptr_t>(a_sf) | reinterpret_cast<uintptr_t>(b_sf)) & 15u) == 0,
+              BSP_EINVAL, "%s: operand and scale buffers must be 16-byte aligned", fn);
+  BSP_REQUIRE(ceil_div(M, 256) * ceil_div(N, 256) < (1ll << 31), BSP_ESHAPE, "%s: too many tiles", fn);
+  if (int e = check_device()) return e;
+  return 0;
+}
+
 extern "C" int bsp_mm_fp4(const uint8_t* a_packed, const uint8_t* a_sf, const uint8_t* b_packed,
                           const uint8_t* b_sf, const float* alpha_dev, int64_t M, int64_t N,
                           int64_t K, void* out, int64_t ldc, int out_dtype, void* stream) {
-  BSP_REQUIRE(M >= 0 && N >= 0 && K > 0, BSP_EINVAL, "bsp_mm_fp4: bad size M=%lld N=%lld K=%lld",
-              (long long)M, (long long)N, (long long)K);
-  BSP_REQUIRE(out_dtype == BSP_OUT_BF16 || out_dtype == BSP_OUT_F32, BSP_EDTYPE,
-              "bsp_mm_fp4: out_dtype must be BSP_OUT_BF16 (0) or BSP_OUT_F32 (1), got %d", out_dtype);
-  BSP_REQUIRE(K % 64 == 0, BSP_ESHAPE, "bsp_mm_fp4: K (%lld) must be a multiple of 64", (long long)K);
-  BSP_REQUIRE(M <= 1 || ldc >= N, BSP_ESHAPE, "bsp_mm_fp4: ldc (%lld) < N (%lld)", (long long)ldc,
-              (long long)N);
-  if (M == 0 || N == 0) return BSP_OK;
-  BSP_REQUIRE(a_packed && a_sf && b_packed && b_sf && alpha_dev && out, BSP_EINVAL,
-              "bsp_mm_fp4: null pointer");
-  BSP_REQUIRE(((reinterpret_cast<uintptr_t>(a_packed) | reinterpret_cast<uintptr_t>(b_packed) |
-                reinterpret_cast<uintptr_t>(a_sf) | reinterpret_cast<uintptr_t>(b_sf)) & 15u) == 0,
-              BSP_EINVAL, "bsp_mm_fp4: operand and scale buffers must be 16-byte aligned");
-  BSP_REQUIRE(ceil_div(M, 256) * ceil_div(N, 256) < (1ll << 31), BSP_ESHAPE, "bsp_mm_fp4: too many tiles");
-  if (int e = check_device()) return e;
-  return launch_mm_fp4(a_packed, a_sf, b_packed, b_sf, alpha_dev, M, N, K, out, ldc, out_dtype,
-                       (hipStream_t)stream);
+  int e = mm_fp4_checks("bsp_mm_fp4", a_packed, a_sf, b_packed, b_sf, alpha_dev, M, N, K, out, ldc,
+                        out_dtype);
+  if (e) return e > 0 ? BSP_OK : e;
+  launch_mm_fp4_t<false>(a_packed, a_sf, b_packed, b_sf, alpha_dev, nullptr, M, N, K, out, ldc,
+                         out_dtype, (hipStream_t)stream);
+  return check_launch("bsp_mm_fp4");
+}
+
+extern "C" int bsp_mm_fp4_per_token(const uint8_t* a_packed, const uint8_t* a_sf,
+                                    const uint8_t* b_packed, const uint8_t* b_sf,
+                                    const float* x_gsf_rows, const float* w_gsf_dev, int64_t M,
+                                    int64_t N, int64_t K, void* out, int64_t ldc, int out_dtype,
+                                    void* stream) {
+  int e = mm_fp4_checks("bsp_mm_fp4_per_token", a_packed, a_sf, b_packed, b_sf, x_gsf_rows, M, N, K,
+                        out, ldc, out_dtype);
+  if (e) return e > 0 ? BSP_OK : e;
+  BSP_REQUIRE(w_gsf_dev, BSP_EINVAL, "bsp_mm_fp4_per_token: null pointer");
+  launch_mm_fp4_t<true>(a_packed, a_sf, b_packed, b_sf, x_gsf_rows, w_gsf_dev, M, N, K, out, ldc,
+                        out_dtype, (hipStream_t)stream);
+  return check_launch("bsp_mm_fp4_per_token");
 }

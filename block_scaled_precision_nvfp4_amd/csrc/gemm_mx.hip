@@ -256,7 +256,8 @@ __global__ __launch_bounds__(256, 1) void mm_mx_kernel(
     stage_mfma<FMT, 0>(acc, f0, f1, st[(kt + 1) % NSTAGE], wm, wn, li, h);
   }
   wait_vmcnt<0>();
-  const float alpha = alpha_ptr ? *alpha_ptr : 1.0f;
+  const float a = alpha_ptr ? *alpha_ptr : 1.0f;
+  const float alpha[4] = {a, a, a, a};
   store_wave_tile<OUT_F32>(acc, alpha, m0 + wm * 128, n0 + wn * 128, M, N, out, ldc, vec_store, li, h);
 }
 

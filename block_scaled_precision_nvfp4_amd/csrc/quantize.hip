@@ -223,6 +223,92 @@ __global__ __launch_bounds__(256) void nvfp4_quantize_kernel(const uint16_t* __r
 }
 
 // =============================================================================================
+// NVFP4 quantize with per-token (per-row) activation scales
+// =============================================================================================
+// One wave owns one row. The row is read in segments of 64 lanes x C chunks of 8 elements (lane l
+// holds elements (64 j + l) * 8 .. + 7 of chunk j); its amax is a wave max and its encode scale is
+// gsf_m = 2688 / amax (one IEEE division; 1 for an all-zero row), the tensor-scale rule applied to
+// the row. The wave tabulates fl32(gsf_m / e4m3(c)) for the 127 codes in LDS, then quantizes the
+// blocks (lane pairs) exactly as the per-tensor kernel does. When the padded row fits one segment
+// (K <= 64 * 8 * C) it stays in registers between the two phases (one pass over HBM); longer rows
+// are read twice. Rows M..Mp-1 run as zero rows, which writes their 0x00 padding scales. Scale
+// bytes of a row are gathered in LDS and leave as one dword per 128x4 column group.
+constexpr int kTokMaxCols = 1024;  // scale columns per row staged in LDS (K <= 16384 per segment set)
+
+template <int C, bool VEC>
+__global__ __launch_bounds__(256) void nvfp4_quantize_token_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ld, uint8_t* __restrict__ packed,
+    uint8_t* __restrict__ sf, float* __restrict__ gsf_rows, int64_t Kp) {
+  __shared__ float rtab[4][128];
+  __shared__ uint32_t srow[4][kTokMaxCols / 4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  const bool live = row < M;
+  const int64_t seg_elems = 64 * 8 * C;
+  const int64_t kpad = Kp * 16;                     // elements incl. the padding scale columns
+  const int nseg = (int)((kpad + seg_elems - 1) / seg_elems);
+  const uint16_t* xr = x + (live ? row : 0) * ld;
+
+  uint4 v[C];
+  float amax = 0.0f;
+  for (int sg = 0; sg < nseg; ++sg) {
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      const int64_t e = sg * seg_elems + (int64_t)(j * 64 + lane) * 8;
+      v[j] = (live && e < K) ? load8<VEC>(xr + e) : make_uint4(0u, 0u, 0u, 0u);
+      float f[8];
+      unpack8(v[j], f);
+      amax = fmaxf(amax, absmax8(f));
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  const float g = (amax == 0.0f) ? 1.0f : 2688.0f / amax;  // 448 * 6 / amax, one IEEE division
+  if (live && lane == 0) gsf_rows[row] = g;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = lane + 64 * h;
+    rtab[wave][c] = (c == 0 || c > 0x7E) ? 0.0f : g / e4m3_decode_pos((uint32_t)c);
+  }
+  __syncthreads();
+
+  const int64_t half_k = K / 2;
+  uint8_t* prow = packed + (live ? row : 0) * half_k;
+  uint8_t* sb = reinterpret_cast<uint8_t*>(srow[wave]);
+  for (int sg = 0; sg < nseg; ++sg) {
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      const int64_t e = sg * seg_elems + (int64_t)(j * 64 + lane) * 8;
+      if (nseg > 1) v[j] = (live && e < K) ? load8<VEC>(xr + e) : make_uint4(0u, 0u, 0u, 0u);
+      float f[8];
+      unpack8(v[j], f);
+      const float a = pair_max(absmax8(f));
+      const uint32_t S = e4m3_encode_pos(g * (a * kSixth));
+      const float r = rtab[wave][S];
+      uint32_t out = 0;
+      out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, f[0] * r, f[1] * r, 1.0f, 0);
+      out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, f[2] * r, f[3] * r, 1.0f, 1);
+      out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, f[4] * r, f[5] * r, 1.0f, 2);
+      out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, f[6] * r, f[7] * r, 1.0f, 3);
+      if (live && e < K) *reinterpret_cast<uint32_t*>(prow + e / 2) = out;
+      const int64_t col = e / 16;                         // scale column of this lane pair
+      if ((lane & 1) == 0 && col < Kp) sb[col % kTokMaxCols] = (uint8_t)S;
+    }
+    // this segment's scale columns [sg * seg_elems / 16, ...) -> one dword per column group
+    // (LDS operations of one wave complete in order: the reads below see the bytes written above)
+    __builtin_amdgcn_wave_barrier();
+    const int64_t c0 = sg * seg_elems / 16;
+    const int64_t c1 = c0 + seg_elems / 16 < Kp ? c0 + seg_elems / 16 : Kp;
+    const int64_t groups = Kp / 4;
+    for (int64_t cg = c0 / 4 + lane; cg < c1 / 4; cg += 64) {
+      const int64_t off = ((row >> 7) * groups + cg) * 512 + (row & 31) * 16 + ((row >> 5) & 3) * 4;
+      *reinterpret_cast<uint32_t*>(sf + off) = srow[wave][cg % (kTokMaxCols / 4)];
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// =============================================================================================
 // a6: MXFP8 quantize
 // =============================================================================================
 // One workgroup covers 64 rows x 256 K (8 steps of 8 rows x 32 lanes x 8 elements). A 32-element
@@ -458,6 +544,37 @@ extern "C" int bsp_nvfp4_global_sf(const void* w, int64_t rows, int64_t K, int64
   return launch_global_sf(w, rows, K, ld, gsf, inv_gsf, amax, (hipStream_t)stream);
 }
 
+template <int C>
+static void launch_token_c(const uint16_t* xp, int64_t M, int64_t K, int64_t ld, uint8_t* packed,
+                           uint8_t* sf, float* gsf_rows, int64_t Kp, bool vec, hipStream_t s) {
+  const int64_t Mp = ceil_div(M, 128) * 128;
+  dim3 grid((unsigned)(Mp / 4));
+  if (vec)
+    hipLaunchKernelGGL((nvfp4_quantize_token_kernel<C, true>), grid, dim3(256), 0, s, xp, M, K, ld,
+                       packed, sf, gsf_rows, Kp);
+  else
+    hipLaunchKernelGGL((nvfp4_quantize_token_kernel<C, false>), grid, dim3(256), 0, s, xp, M, K, ld,
+                       packed, sf, gsf_rows, Kp);
+}
+
+int launch_nvfp4_quantize_per_token(const void* x, int64_t M, int64_t K, int64_t ld, uint8_t* packed,
+                                    uint8_t* sf, float* gsf_rows, hipStream_t s) {
+  const int64_t Kp = ceil_div(K / 16, 4) * 4;
+  const int64_t kpad = Kp * 16;
+  const uint16_t* xp = static_cast<const uint16_t*>(x);
+  const bool vec = (ld % 8 == 0) && aligned16(x);
+  // smallest register segment that holds the padded row (one HBM pass), else 16384-element segments
+  if (kpad <= 64 * 8 * 4)
+    launch_token_c<4>(xp, M, K, ld, packed, sf, gsf_rows, Kp, vec, s);
+  else if (kpad <= 64 * 8 * 8)
+    launch_token_c<8>(xp, M, K, ld, packed, sf, gsf_rows, Kp, vec, s);
+  else if (kpad <= 64 * 8 * 16)
+    launch_token_c<16>(xp, M, K, ld, packed, sf, gsf_rows, Kp, vec, s);
+  else
+    launch_token_c<32>(xp, M, K, ld, packed, sf, gsf_rows, Kp, vec, s);
+  return check_launch("bsp_nvfp4_quantize_per_token");
+}
+
 static int nvfp4_quantize_entry(const char* fn, const void* x, int64_t M, int64_t K, int64_t ld,
                                 const float* gsf, uint8_t* packed, uint8_t* sf, void* stream, bool gelu) {
   BSP_REQUIRE(M >= 0 && K > 0, BSP_EINVAL, "%s: bad size M=%lld K=%lld", fn, (long long)M, (long long)K);
@@ -475,6 +592,22 @@ static int nvfp4_quantize_entry(const char* fn, const void* x, int64_t M, int64_
 extern "C" int bsp_nvfp4_quantize(const void* x, int64_t M, int64_t K, int64_t ld, const float* gsf,
                                   uint8_t* packed, uint8_t* sf, void* stream) {
   return nvfp4_quantize_entry("bsp_nvfp4_quantize", x, M, K, ld, gsf, packed, sf, stream, false);
+}
+
+extern "C" int bsp_nvfp4_quantize_per_token(const void* x, int64_t M, int64_t K, int64_t ld,
+                                            uint8_t* packed, uint8_t* sf, float* gsf_rows,
+                                            void* stream) {
+  const char* fn = "bsp_nvfp4_quantize_per_token";
+  BSP_REQUIRE(M >= 0 && K > 0, BSP_EINVAL, "%s: bad size M=%lld K=%lld", fn, (long long)M, (long long)K);
+  BSP_REQUIRE(K % 16 == 0, BSP_ESHAPE, "%s: K (%lld) must be a multiple of 16", fn, (long long)K);
+  BSP_REQUIRE(M <= 1 || ld >= K, BSP_ESHAPE, "%s: ld (%lld) < K (%lld)", fn, (long long)ld, (long long)K);
+  if (M == 0) return BSP_OK;
+  BSP_REQUIRE(x && packed && sf && gsf_rows, BSP_EINVAL, "%s: null pointer", fn);
+  BSP_REQUIRE((reinterpret_cast<uintptr_t>(packed) & 3u) == 0 && (reinterpret_cast<uintptr_t>(sf) & 15u) == 0,
+              BSP_EINVAL, "%s: packed must be 4-byte and sf 16-byte aligned", fn);
+  BSP_REQUIRE(ceil_div(M, 128) * 32 < (1ll << 31), BSP_ESHAPE, "%s: M too large", fn);
+  if (int e = check_device()) return e;
+  return launch_nvfp4_quantize_per_token(x, M, K, ld, packed, sf, gsf_rows, (hipStream_t)stream);
 }
 
 extern "C" int bsp_nvfp4_quantize_gelu(const void* y, int64_t M, int64_t K, int64_t ld,

@@ -143,6 +143,25 @@ int bsp_mm_mxfp4(const uint8_t* a_packed, const uint8_t* a_sf, const uint8_t* b_
  * x, y: device bf16 [n], contiguous, 16-byte aligned. */
 int bsp_gelu_tanh_bf16(const void* x, void* y, int64_t n, void* stream);
 
+/* Per-token activation scales (NEXT row f3). [SGL] NVFP4OnlineConfig.__init__ (per-token
+ * activation path): weights keep their static tensor scale while each activation row (token) gets
+ * its own fp32 scale at run time. Row m: amax_m = max|x[m, :]|, gsf_rows[m] = fl32(2688/amax_m)
+ * (1.0 for an all-zero row: the tensor rule of bsp_nvfp4_global_sf applied to the row), and the row
+ * is quantized exactly as bsp_nvfp4_quantize would with gsf = gsf_rows[m]. Outputs as
+ * bsp_nvfp4_quantize plus gsf_rows: device fp32 [M] (written). Inputs must be finite. Rows of up to
+ * 64*8*32 elements (padded to 64) are read once; longer rows are read twice. */
+int bsp_nvfp4_quantize_per_token(const void* x_bf16, int64_t M, int64_t K, int64_t ld,
+                                 uint8_t* packed, uint8_t* sf, float* gsf_rows_dev, void* stream);
+
+/* mm_fp4 with per-token activation scales: C[m, n] = alpha_m * sum_k A*SA * B*SB with
+ * alpha_m = fl32(1 / fl32(x_gsf_rows[m] * w_gsf)) (the scalar alpha of bsp_nvfp4_alpha, row by row),
+ * applied in the epilogue. x_gsf_rows: device fp32 [M] from bsp_nvfp4_quantize_per_token; w_gsf:
+ * device fp32 scalar (the weight's encode scale). Everything else as bsp_mm_fp4. */
+int bsp_mm_fp4_per_token(const uint8_t* a_packed, const uint8_t* a_sf, const uint8_t* b_packed,
+                         const uint8_t* b_sf, const float* x_gsf_rows_dev, const float* w_gsf_dev,
+                         int64_t M, int64_t N, int64_t K, void* out, int64_t ldc, int out_dtype,
+                         void* stream);
+
 /* Producer-fused quantize of the FFN activation: exactly bsp_nvfp4_quantize applied to
  * bsp_gelu_tanh_bf16(y) (GELU evaluated and rounded to bf16 per element as above, then the NVFP4
  * block quantization of those bf16 values), in one pass over y without writing the bf16 activation.

@@ -149,6 +149,49 @@ def test_mm_fp4_full_size_fp32_output():
     assert_gemm_f32(gather(c, rows, cols), ref, "cfg2 fp32")
 
 
+# ------------------------------------------------------------------------------ per-token scales
+@pytest.mark.parametrize("m,n,k", [(1, 64, 64), (77, 200, 192), (300, 384, 512)])
+def test_mm_fp4_per_token_random_all_elements(m, n, k):
+    say("mm_fp4_per_token random", m, n, k)
+    rng = np.random.default_rng(m + 11 * n + k)
+    pa, sa = _rand_nvfp4_operand(rng, m, k)
+    pb, sb = _rand_nvfp4_operand(rng, n, k)
+    xg = (10.0 ** rng.uniform(-2, 3, size=m)).astype(np.float32)
+    wg = f32(777.25)
+    ref = N.mm_fp4_rowscale(pa, sa, pb, sb, xg, wg, m, n, k)
+    args = (dev_u8(pa), dev_u8(sa), dev_u8(pb), dev_u8(sb), torch.from_numpy(xg).cuda(), scalar(wg))
+    t32 = bsp.bsp_mm_fp4_per_token(*args, out_dtype=torch.float32)
+    assert_gemm_f32(t32.cpu().numpy().astype(np.float64), ref, f"per-token {m}x{n}x{k}")
+    t16 = bsp.bsp_mm_fp4_per_token(*args)
+    assert_gemm_bf16(t16.float().cpu().numpy().astype(np.float64), ref, f"per-token {m}x{n}x{k}")
+    _assert_bf16_is_rne_of_f32(t16, t32)
+    # with equal row scales it is the tensor-alpha GEMM, bit for bit
+    same = torch.full((m,), 2.5, dtype=torch.float32, device="cuda")
+    c1 = bsp.bsp_mm_fp4_per_token(*args[:4], same, scalar(wg), out_dtype=torch.float32)
+    c2 = bsp.bsp_mm_fp4(*args[:4], bsp.bsp_nvfp4_alpha(scalar(2.5), scalar(wg)), out_dtype=torch.float32)
+    assert torch.equal(c1, c2)
+
+
+def test_per_token_linear_full_size():
+    """Wan-14B to_q (32760x5120x5120) with per-token activation scales: quantize on the GPU, check
+    sampled rows of the quantization and sampled entries of the GEMM against the oracle."""
+    xb, wb = tensor_bits(4, "X"), tensor_bits(4, "W3")
+    m, n, k = xb.shape[0], wb.shape[0], xb.shape[1]
+    px, sx, gx = bsp.bsp_nvfp4_quantize_per_token(dev_bf16(xb))
+    pw, sw, gw, _, _ = bsp.bsp_nvfp4_prequantize_weight(dev_bf16(wb))
+    c = bsp.bsp_mm_fp4_per_token(px, sx, pw, sw, gx, gw)
+    rows, cols = sample_entries(m, n, 3000, 77)
+    ur = np.unique(rows)
+    rq, _, rg = N.quantize_per_token(xb[ur], layout="linear")
+    assert np.array_equal(host_u8(px[torch.from_numpy(ur).cuda()]), rq)
+    g_rows = gx.cpu().numpy()
+    assert np.array_equal(g_rows[ur], rg)
+    base = N.mm_fp4_entries(host_u8(px), host_u8(sx).ravel(), host_u8(pw), host_u8(sw).ravel(),
+                            f32(1.0), m, n, k, rows, cols)
+    ref = base * N.alpha_rows(g_rows[rows], gw.item()).astype(np.float64)
+    assert_gemm_bf16(gather(c, rows, cols), ref, "cfg4 to_q per-token")
+
+
 # ------------------------------------------------------------------------------------------ MXFP8
 def _rand_mx_operand(rng, rows, k):
     q = rng.integers(0, 256, size=(rows, k)).astype(np.uint8)

@@ -83,6 +83,54 @@ def test_nvfp4_quantize_full_size_sampled_rows(cfg, name):
     assert np.all(lin[m:] == 0) and np.all(lin[:, k // 16:] == 0)
 
 
+@pytest.mark.parametrize("m,k", [(1, 16), (77, 48), (129, 96), (300, 1536), (256, 1040),
+                                 (200, 5120), (130, 13824), (70, 16400)])
+def test_nvfp4_quantize_per_token_bit_exact(m, k):
+    """Per-token scales: packed bytes, 128x4 scale bytes (padding included) and the fp32 row scales
+    equal the oracle's; covers the one-pass register path and the two-pass path (K > 16384)."""
+    say("nvfp4_quantize_per_token", m, k)
+    xb = W.small_case(m, k, seed=m * 17 + k, outlier_frac=0.02).copy()
+    xb[m // 2] = 0                                   # an all-zero token
+    if m > 3:
+        xb[1] = W.small_case(1, k, seed=5, std=1e-30)[0]   # a token of tiny values
+        xb[2] = W.small_case(1, k, seed=6, std=1e4)[0]     # and of large ones
+    p, sf, g = bsp.bsp_nvfp4_quantize_per_token(dev_bf16(xb))
+    rp, rs, rg = N.quantize_per_token(xb)
+    assert np.array_equal(g.cpu().numpy(), rg)
+    assert np.array_equal(host_u8(p), rp)
+    assert np.array_equal(host_u8(sf).ravel(), rs)
+
+
+def test_nvfp4_quantize_per_token_strided_and_special():
+    xb = W.special_values_block(seed=17, rows=140, cols=512)
+    big = np.zeros((140, 520), dtype=np.uint16)
+    big[:, :512] = xb
+    p, sf, g = bsp.bsp_nvfp4_quantize_per_token(dev_bf16(big)[:, :512])
+    rp, rs, rg = N.quantize_per_token(xb)
+    assert np.array_equal(g.cpu().numpy(), rg)
+    assert np.array_equal(host_u8(p), rp) and np.array_equal(host_u8(sf).ravel(), rs)
+    p2, sf2, _ = bsp.bsp_nvfp4_quantize_per_token(dev_bf16(big)[:, 1:513])   # unaligned rows
+    rp2, rs2, _ = N.quantize_per_token(big[:, 1:513])
+    assert np.array_equal(host_u8(p2), rp2) and np.array_equal(host_u8(sf2).ravel(), rs2)
+
+
+@pytest.mark.parametrize("cfg,name", [(4, "X"), (3, "X")])
+def test_nvfp4_quantize_per_token_full_size_sampled_rows(cfg, name):
+    xb = tensor_bits(cfg, name)
+    m, k = xb.shape
+    say("full-size per-token quantize", cfg, name, m, k)
+    p, sf, g = bsp.bsp_nvfp4_quantize_per_token(dev_bf16(xb))
+    rows = np.unique(np.concatenate([np.random.default_rng(cfg + 40).integers(0, m, 48), [0, 127, 128, m - 1]]))
+    ri = torch.from_numpy(rows).cuda()
+    ref_p, ref_s, ref_g = N.quantize_per_token(xb[rows], layout="linear")
+    assert np.array_equal(g[ri].cpu().numpy(), ref_g)
+    assert np.array_equal(host_u8(p[ri]), ref_p)
+    rp, cp = N.sf_padded_shape(m, k)
+    lin = N.unswizzle_128x4(host_u8(sf).ravel(), rp, cp)
+    assert np.array_equal(lin[rows, : k // 16], ref_s)
+    assert np.all(lin[m:] == 0)
+
+
 def test_global_sf_bit_exact():
     cases = [tensor_bits(1, "W"), tensor_bits(2, "W"), W.small_case(3, 100, 4, std=1e-3),
              np.zeros((4, 64), dtype=np.uint16)]
