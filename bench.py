@@ -250,6 +250,30 @@ def main():
         "load_time_ms": {"prequantize_w1_w2": round(load_ms, 3)},
     }
 
+    # ---- per-token activation scales at the fc_in shape: quantize X per row + mm_fp4 with row alphas
+    gx = torch.empty((M,), dtype=torch.float32, device=dev)
+    for _ in range(max(1, args.warmup)):
+        bsp.bsp_nvfp4_quantize_per_token(x, px, sx, gx)
+        bsp.bsp_mm_fp4_per_token(px, sx, pw1, sw1, gx, g1, out=y)
+    torch.cuda.synchronize()
+    ept = [[ev() for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        ept[i][0].record(stream)
+        bsp.bsp_nvfp4_quantize_per_token(x, px, sx, gx)
+        ept[i][1].record(stream)
+        bsp.bsp_mm_fp4_per_token(px, sx, pw1, sw1, gx, g1, out=y)
+        ept[i][2].record(stream)
+    torch.cuda.synchronize()
+    qpt = sum(e[0].elapsed_time(e[1]) for e in ept) / args.steps
+    gpt = sum(e[1].elapsed_time(e[2]) for e in ept) / args.steps
+    result["per_token"] = {
+        "quantize_per_token_x_ms": round(qpt, 4),
+        "quantize_per_token_GBs": round(qbytes(M, K1) / qpt / 1e6, 1),
+        "quantize_per_token_frac_hbm": round(qbytes(M, K1) / qpt / 1e6 / PEAK_HBM_GBS, 4),
+        "mm_fp4_per_token_fc_in_ms": round(gpt, 4),
+        "mm_fp4_per_token_TFLOPS": round(2.0 * M * N1 * K1 / gpt / 1e9, 2)}
+    log(json.dumps(result["per_token"]))
+
     # ---- MXFP8 W8A8 at the fc_in shape (config 5)
     if not args.no_mxfp8:
         del y, ph, sh

@@ -73,6 +73,19 @@ def global_sf(w_bits: np.ndarray):
     return gsf, inv, amax
 
 
+def global_sf_4over6(w_bits: np.ndarray):
+    """Weight scales of the 4over6 variant, returns (gsf, inv_gsf, amax), all fp32.
+
+    SGLang nvfp4_online.py, ``_quantize_weight_nvfp4``: with the 4over6 switches the largest e4m3
+    block scale is taken as 256 instead of 448; the decode scale is fl32(amax / (256 * 6)) (1 when
+    amax is 0) and the encode scale handed to the quantizer is its fl32 reciprocal, in that order.
+    """
+    amax = tensor_amax(w_bits)
+    dec = F32(1.0) if amax == F32(0.0) else F32(amax / F32(256.0 * 6.0))
+    gsf = F32(F32(1.0) / dec)
+    return gsf, F32(F32(1.0) / gsf), amax
+
+
 # ----------------------------------------------------------------------------------------
 # a3: alpha
 # ----------------------------------------------------------------------------------------
@@ -114,6 +127,44 @@ def swizzle_128x4(sf_linear: np.ndarray) -> np.ndarray:
 def unswizzle_128x4(sf_flat: np.ndarray, rp: int, cp: int) -> np.ndarray:
     r, c = np.meshgrid(np.arange(rp), np.arange(cp), indexing="ij")
     return np.asarray(sf_flat, dtype=np.uint8)[sf_offset(r, c, cp)]
+
+
+def sf_padded_shape_8x4(rows: int, k: int):
+    """(Rp, Cp) for layout_8x4: rows padded to the 8-row tile, scale columns padded to 4.
+
+    FastVideo nvfp4_config.py, ``_nvfp4_quantize``: the row tile is 8 for layout_8x4."""
+    cols = (k + BLOCK - 1) // BLOCK
+    return ((rows + 7) // 8) * 8, ((cols + 3) // 4) * 4
+
+
+def sf_offset_8x4(r, c, cp: int):
+    """Byte offset of scale (row r, column c) in the 8x4 layout (reading U23): 32-byte tiles of
+    8 rows x 4 columns ordered row-tile-major, each tile stored row by row (r % 8) * 4 + (c % 4)."""
+    r = np.asarray(r, dtype=np.int64)
+    c = np.asarray(c, dtype=np.int64)
+    tile = (r // 8) * (cp // 4) + (c // 4)
+    return tile * 32 + (r % 8) * 4 + (c % 4)
+
+
+def swizzle_8x4(sf_linear: np.ndarray) -> np.ndarray:
+    rp, cp = sf_linear.shape
+    out = np.zeros(rp * cp, dtype=np.uint8)
+    r, c = np.meshgrid(np.arange(rp), np.arange(cp), indexing="ij")
+    out[sf_offset_8x4(r, c, cp)] = sf_linear
+    return out
+
+
+def unswizzle_8x4(sf_flat: np.ndarray, rp: int, cp: int) -> np.ndarray:
+    r, c = np.meshgrid(np.arange(rp), np.arange(cp), indexing="ij")
+    return np.asarray(sf_flat, dtype=np.uint8)[sf_offset_8x4(r, c, cp)]
+
+
+def _layout_fns(layout: str):
+    if layout == "128x4":
+        return sf_padded_shape, sf_offset, swizzle_128x4
+    if layout == "8x4":
+        return sf_padded_shape_8x4, sf_offset_8x4, swizzle_8x4
+    raise ValueError(layout)
 
 
 # ----------------------------------------------------------------------------------------
@@ -162,7 +213,8 @@ def quantize(x_bits: np.ndarray, gsf, layout: str = "128x4"):
     """NVFP4-quantize bf16 X [M, K] (K % 16 == 0) under fp32 global scale ``gsf``.
 
     Returns (packed [M, K/2] uint8, sf) where sf is the flat 128x4-layout buffer of
-    Rp*Cp bytes (layout "128x4"), or the [M, K/16] row-major bytes (layout "linear").
+    Rp*Cp bytes (layout "128x4"), the flat 8x4-layout buffer (layout "8x4", rows padded to 8),
+    or the [M, K/16] row-major bytes (layout "linear").
     Padded scale rows/columns hold 0x00, the scale of an all-zero padded block.
     """
     x_bits = np.asarray(x_bits, dtype=np.uint16)
@@ -175,10 +227,11 @@ def quantize(x_bits: np.ndarray, gsf, layout: str = "128x4"):
     packed = pack_nibbles(codes.reshape(m, k))
     if layout == "linear":
         return packed, S
-    rp, cp = sf_padded_shape(m, k)
+    shape_fn, _, swz = _layout_fns(layout)
+    rp, cp = shape_fn(m, k)
     lin = np.zeros((rp, cp), dtype=np.uint8)
     lin[:m, :nb] = S
-    return packed, swizzle_128x4(lin)
+    return packed, swz(lin)
 
 
 def row_global_sf(x_bits: np.ndarray) -> np.ndarray:
@@ -221,10 +274,11 @@ def quantize_rows(x_bits: np.ndarray, gsf):
 # dequant and the GEMM
 # ----------------------------------------------------------------------------------------
 def dequant_rows(packed: np.ndarray, sf_flat: np.ndarray, rows, n_rows_total: int, k: int,
-                 gsf=None) -> np.ndarray:
+                 gsf=None, layout: str = "128x4") -> np.ndarray:
     """fp64 values e2m1(q) * e4m3(S) (/ gsf if given) of the selected rows."""
     rows = np.asarray(rows, dtype=np.int64)
-    rp, cp = sf_padded_shape(n_rows_total, k)
+    shape_fn, sf_offset, _ = _layout_fns(layout)
+    rp, cp = shape_fn(n_rows_total, k)
     nb = k // BLOCK
     codes = unpack_nibbles(np.asarray(packed)[rows]).astype(np.int64)       # [r, K]
     r_idx = np.repeat(rows[:, None], nb, axis=1)
@@ -239,17 +293,18 @@ def dequant_rows(packed: np.ndarray, sf_flat: np.ndarray, rows, n_rows_total: in
 
 
 def mm_fp4(a_packed, a_sf, b_packed, b_sf, alpha_val, m: int, n: int, k: int,
-           row_chunk: int = 2048) -> np.ndarray:
+           row_chunk: int = 2048, a_layout: str = "128x4") -> np.ndarray:
     """C[m, n] = alpha * sum_k e2m1(A)*e4m3(SA) * e2m1(B)*e4m3(SB) in fp64 ([M, N]).
 
-    A is packed [M, K/2] with 128x4 scales over M rows; B is packed [N, K/2]
-    (K-major; the pages pass its transposed view) with 128x4 scales over N rows.
+    A is packed [M, K/2] with 128x4 scales over M rows (8x4 with a_layout="8x4", the pages'
+    use_8x4_sf_layout for the activation); B is packed [N, K/2] (K-major; the pages pass its
+    transposed view) with 128x4 scales over N rows.
     """
     B = dequant_rows(b_packed, b_sf, np.arange(n), n, k)
     out = np.empty((m, n), dtype=np.float64)
     for r0 in range(0, m, row_chunk):
         r1 = min(r0 + row_chunk, m)
-        A = dequant_rows(a_packed, a_sf, np.arange(r0, r1), m, k)
+        A = dequant_rows(a_packed, a_sf, np.arange(r0, r1), m, k, layout=a_layout)
         out[r0:r1] = A @ B.T
     return np.float64(F32(alpha_val)) * out
 

@@ -363,3 +363,68 @@ def test_per_token_linear_approximates_the_bf16_product():
     c = N.mm_fp4_rowscale(px, sx, pw, sw, gx, gw, 64, 32, 256)
     full = W.bf16_bits_to_f32(xb).astype(np.float64) @ W.bf16_bits_to_f32(wb).astype(np.float64).T
     assert np.linalg.norm(c - full) / np.linalg.norm(full) < 0.15
+
+
+# ------------------------------------------------------------- f4 layout_8x4 and the 4over6 scale
+def test_sf_offsets_8x4_golden():
+    for line in golden_lines("sf_offsets_8x4.txt"):
+        r, c, off = (int(v) for v in line.split())
+        assert N.sf_offset_8x4(r, c, 8) == off
+
+
+def test_sf_layout_8x4_bijection_and_tiles():
+    rp, cp = N.sf_padded_shape_8x4(37, 16 * 10)
+    assert (rp, cp) == (40, 12)
+    r, c = np.meshgrid(np.arange(rp), np.arange(cp), indexing="ij")
+    off = N.sf_offset_8x4(r, c, cp)
+    assert np.array_equal(np.sort(off.ravel()), np.arange(rp * cp))
+    # each 32-byte tile holds exactly one 8-row x 4-column block
+    for t in range(rp * cp // 32):
+        cells = np.argwhere((off >= 32 * t) & (off < 32 * t + 32))
+        assert len(cells) == 32
+        assert len(np.unique(cells[:, 0] // 8)) == 1 and len(np.unique(cells[:, 1] // 4)) == 1
+    lin = np.random.default_rng(0).integers(0, 256, (rp, cp)).astype(np.uint8)
+    assert np.array_equal(N.unswizzle_8x4(N.swizzle_8x4(lin), rp, cp), lin)
+
+
+def test_quantize_8x4_same_scales_as_128x4_and_padding():
+    xb = W.small_case(13, 80, 4)
+    p1, s1 = N.quantize(xb, f32(2.0), layout="8x4")
+    p2, s2 = N.quantize(xb, f32(2.0), layout="128x4")
+    assert np.array_equal(p1, p2)
+    rp, cp = N.sf_padded_shape_8x4(13, 80)
+    assert s1.size == rp * cp == 16 * 8
+    lin8 = N.unswizzle_8x4(s1, rp, cp)
+    lin128 = N.unswizzle_128x4(s2, *N.sf_padded_shape(13, 80))
+    assert np.array_equal(lin8, lin128[:rp])
+    assert not lin8[13:].any() and not lin8[:, 5:].any()
+
+
+def test_mm_fp4_with_8x4_activation_scales():
+    rng = np.random.default_rng(12)
+    m, n, k = 11, 20, 128
+    ca, la, pa, sa = _rand_operand(rng, m, k)
+    _, _, pb, sb = _rand_operand(rng, n, k)
+    rp8, cp = N.sf_padded_shape_8x4(m, k)
+    lin = N.unswizzle_128x4(sa, *N.sf_padded_shape(m, k))[:rp8]
+    sa8 = N.swizzle_8x4(lin)
+    c128 = N.mm_fp4(pa, sa, pb, sb, f32(0.5), m, n, k)
+    c8 = N.mm_fp4(pa, sa8, pb, sb, f32(0.5), m, n, k, a_layout="8x4")
+    assert np.array_equal(c8, c128)
+
+
+def test_global_sf_4over6_golden_and_256_block():
+    for line in golden_lines("global_sf_4over6.txt"):
+        amax, gsf = (float(v) for v in line.split())
+        w = bits([amax, -amax / 2, 0.0, amax / 4] * 4).reshape(1, 16)
+        g, inv, a = N.global_sf_4over6(w)
+        assert a == f32(amax) and g == f32(gsf) and inv == f32(1.0) / f32(gsf)
+    # the block holding the tensor amax gets the block scale 256 (byte 0x78) instead of 448
+    for seed in range(4):
+        w = W.small_case(32, 256, 40 + seed, std=0.02)
+        g, _, amax = N.global_sf_4over6(w)
+        _, sf = N.quantize(w, g, layout="linear")
+        xf = W.bf16_bits_to_f32(w).reshape(32, 16, 16)
+        blk = np.argwhere(np.max(np.abs(xf), axis=-1) == amax)[0]
+        assert sf[blk[0], blk[1]] == 0x78
+        assert sf.max() <= 0x78
