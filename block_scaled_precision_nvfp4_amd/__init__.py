@@ -42,6 +42,10 @@ SIGNATURES = {
     "bsp_gelu_tanh_bf16": ([_p, _p, _i64, _p], _int),
     "bsp_nvfp4_quantize_gelu": ([_p, _i64, _i64, _i64, _p, _p, _p, _p], _int),
     "bsp_nvfp4_quantize_per_token": ([_p, _i64, _i64, _i64, _p, _p, _p, _p], _int),
+    "bsp_nvfp4_sf_bytes_8x4": ([_i64, _i64, ctypes.POINTER(_i64)], _int),
+    "bsp_nvfp4_quantize_8x4": ([_p, _i64, _i64, _i64, _p, _p, _p, _p], _int),
+    "bsp_mm_fp4_8x4": ([_p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _int, _p], _int),
+    "bsp_nvfp4_global_sf_4over6": ([_p, _i64, _i64, _i64, _p, _p, _p, _p], _int),
     "bsp_mm_fp4_per_token": ([_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _int, _p], _int),
 }
 
@@ -158,12 +162,19 @@ def bsp_nvfp4_quantize_gelu(y: torch.Tensor, gsf: torch.Tensor,
     return _nvfp4_quantize("bsp_nvfp4_quantize_gelu", y, gsf, packed, sf)
 
 
+def bsp_nvfp4_quantize_8x4(x: torch.Tensor, gsf: torch.Tensor,
+                           packed: Optional[torch.Tensor] = None,
+                           sf: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """NVFP4 quantize with layout_8x4 scales: sf uint8 [ceil(M/8)*8, ceil(K/64)*4]."""
+    return _nvfp4_quantize("bsp_nvfp4_quantize_8x4", x, gsf, packed, sf, row_tile=8)
+
+
 def _nvfp4_quantize(fn: str, x: torch.Tensor, gsf: torch.Tensor, packed: Optional[torch.Tensor],
-                    sf: Optional[torch.Tensor]) -> Tuple[torch.Tensor, torch.Tensor]:
+                    sf: Optional[torch.Tensor], row_tile: int = 128) -> Tuple[torch.Tensor, torch.Tensor]:
     x = _as_bf16_2d(x, "x")
     _need(gsf, "gsf", torch.float32, x.device)
     m, k = x.shape
-    rp = -(-m // 128) * 128
+    rp = -(-m // row_tile) * row_tile
     kp = -(-(k // 16) // 4) * 4
     if packed is None:
         packed = torch.empty((m, k // 2), dtype=torch.uint8, device=x.device)
@@ -174,7 +185,7 @@ def _nvfp4_quantize(fn: str, x: torch.Tensor, gsf: torch.Tensor, packed: Optiona
     if packed.numel() < m * (k // 2) or not packed.is_contiguous():
         raise ValueError("packed must be contiguous with M*K/2 bytes")
     if sf.numel() < rp * kp or not sf.is_contiguous():
-        raise ValueError("sf must be contiguous with bsp_nvfp4_sf_bytes(M, K) bytes")
+        raise ValueError("sf must be contiguous with rows padded to the scale tile x ceil(K/64)*4 bytes")
     _call(fn, x.data_ptr(), m, k, x.stride(0), gsf.data_ptr(),
           packed.data_ptr(), sf.data_ptr(), _stream(x.device))
     return packed, sf
@@ -256,7 +267,27 @@ def bsp_mm_fp4_per_token(a: torch.Tensor, a_sf: torch.Tensor, b: torch.Tensor, b
     return out
 
 
-def _mm_fp4_args(a, a_sf, b, b_sf, out_dtype, out):
+def bsp_mm_fp4_8x4(a: torch.Tensor, a_sf: torch.Tensor, b: torch.Tensor, b_sf: torch.Tensor,
+                   alpha: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16,
+                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """bsp_mm_fp4 with A's scales in layout_8x4 (from bsp_nvfp4_quantize_8x4)."""
+    m, n, k, code, out = _mm_fp4_args(a, a_sf, b, b_sf, out_dtype, out, a_row_tile=8)
+    _need(alpha, "alpha", torch.float32, a.device)
+    _call("bsp_mm_fp4_8x4", a.data_ptr(), a_sf.data_ptr(), b.data_ptr(), b_sf.data_ptr(),
+          alpha.data_ptr(), m, n, k, out.data_ptr(), out.stride(0), code, _stream(a.device))
+    return out
+
+
+def bsp_nvfp4_global_sf_4over6(w: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """(gsf, inv_gsf, amax) of the 4over6 variant (block scales capped at 256), device fp32."""
+    w = _as_bf16_2d(w, "w")
+    gsf, inv, amax = (torch.empty(1, dtype=torch.float32, device=w.device) for _ in range(3))
+    _call("bsp_nvfp4_global_sf_4over6", w.data_ptr(), w.shape[0], w.shape[1], w.stride(0),
+          gsf.data_ptr(), inv.data_ptr(), amax.data_ptr(), _stream(w.device))
+    return gsf, inv, amax
+
+
+def _mm_fp4_args(a, a_sf, b, b_sf, out_dtype, out, a_row_tile: int = 128):
     _need(a, "a", torch.uint8)
     dev = a.device
     for t, nm in ((a_sf, "a_sf"), (b, "b"), (b_sf, "b_sf")):
@@ -274,8 +305,9 @@ def _mm_fp4_args(a, a_sf, b, b_sf, out_dtype, out):
     _need(out, "out", out_dtype, dev)
     if out.dim() != 2 or out.shape[0] != m or out.shape[1] != n or out.stride(1) != 1:
         raise ValueError(f"out must be [{m}, {n}] with unit column stride")
-    if a_sf.numel() < bsp_nvfp4_sf_bytes(m, k) or b_sf.numel() < bsp_nvfp4_sf_bytes(n, k):
-        raise ValueError("scale buffers are smaller than bsp_nvfp4_sf_bytes")
+    a_need = bsp_nvfp4_sf_bytes(m, k) if a_row_tile == 128 else -(-m // 8) * 8 * (-(-k // 64) * 4)
+    if a_sf.numel() < a_need or b_sf.numel() < bsp_nvfp4_sf_bytes(n, k):
+        raise ValueError("scale buffers are smaller than the layout needs")
     return m, n, k, code, out
 
 

@@ -44,3 +44,10 @@ extern "C" int bsp_nvfp4_sf_bytes(int64_t rows, int64_t K, int64_t* bytes) {
   *bytes = bsp::ceil_div(rows, 128) * 128 * bsp::ceil_div(K, 64) * 4;
   return BSP_OK;
 }
+
+extern "C" int bsp_nvfp4_sf_bytes_8x4(int64_t rows, int64_t K, int64_t* bytes) {
+  BSP_REQUIRE(bytes, BSP_EINVAL, "bsp_nvfp4_sf_bytes_8x4: null output pointer");
+  BSP_REQUIRE(rows >= 0 && K >= 0, BSP_EINVAL, "bsp_nvfp4_sf_bytes_8x4: negative size");
+  *bytes = bsp::ceil_div(rows, 8) * 8 * bsp::ceil_div(K, 64) * 4;
+  return BSP_OK;
+}

@@ -35,7 +35,9 @@ namespace bsp {
 namespace fp4 {
 
 constexpr int BM = 256, BN = 256, BK = 128, NSTAGE = 3;
-constexpr int kLoadsPerStage = 9;  // global_load_lds instructions per wave per stage
+// global_load_lds instructions per wave per stage: 8 operand chunks + 1 scale half (A scales in
+// the 128x4 layout), or + 2 dword gathers of A's scales + 1 of B's (A scales in layout_8x4)
+template <bool SFA8> constexpr int kLoadsPerStage = SFA8 ? 11 : 9;
 
 struct Stage {
   u32x4 a[BM * 4];  // packed A: row r, 16-byte chunk c (K [32c, 32c+32) of the stage) at chunk_slot
@@ -83,13 +85,14 @@ __device__ __forceinline__ uint32_t comp(const u32x4& v, int j) {
 // applied on the global side: LDS slot s holds row s/4, logical chunk (s%4) ^ ((row/2 ^ row/4)%4).
 // K % 128 == 64: the last stage's second half re-reads its first half (in bounds) and the compute
 // zeroes that half's scales.
+template <bool SFA8>
 __device__ __forceinline__ void issue_stage(Stage& st, const uint8_t* __restrict__ A,
                                             const uint8_t* __restrict__ B,
                                             const uint8_t* __restrict__ SA,
                                             const uint8_t* __restrict__ SB, int64_t M, int64_t N,
                                             int64_t K, int64_t m0, int64_t n0, int64_t kt,
                                             int64_t mtiles128, int64_t ntiles128, int64_t groups,
-                                            int wave, int lane) {
+                                            int64_t rows8, int wave, int lane) {
   const int64_t hk = K / 2;
   const bool tail = kt * 128 + 64 >= K;
 #pragma unroll
@@ -105,15 +108,37 @@ __device__ __forceinline__ void issue_stage(Stage& st, const uint8_t* __restrict
     __builtin_amdgcn_global_load_lds(A + ra * hk + koff, (lds_t*)&st.a[slot0], 16, 0, 0);
     __builtin_amdgcn_global_load_lds(B + rb * hk + koff, (lds_t*)&st.b[slot0], 16, 0, 0);
   }
-  // waves 0-1: A's two 128-row scale tiles, waves 2-3: B's; slot = rt*64 + cg*32 + q
-  const int which = wave >> 1, rt = wave & 1;
   const int cg0 = lane >> 5, q = lane & 31;
   const int cg = (tail && cg0 == 1) ? 0 : cg0;
-  const int64_t r0 = which ? n0 / 128 : m0 / 128;
-  const int64_t nt = which ? ntiles128 : mtiles128;
-  int64_t tr = r0 + rt; tr = tr < nt ? tr : nt - 1;
-  const uint8_t* src = (which ? SB : SA) + (tr * groups + kt * 2 + cg) * 512 + q * 16;
-  __builtin_amdgcn_global_load_lds(src, (lds_t*)(which ? &st.sb[rt * 64] : &st.sa[rt * 64]), 16, 0, 0);
+  if constexpr (!SFA8) {
+    // waves 0-1: A's two 128-row scale tiles, waves 2-3: B's; slot = rt*64 + cg*32 + q
+    const int which = wave >> 1, rt = wave & 1;
+    const int64_t r0 = which ? n0 / 128 : m0 / 128;
+    const int64_t nt = which ? ntiles128 : mtiles128;
+    int64_t tr = r0 + rt; tr = tr < nt ? tr : nt - 1;
+    const uint8_t* src = (which ? SB : SA) + (tr * groups + kt * 2 + cg) * 512 + q * 16;
+    __builtin_amdgcn_global_load_lds(src, (lds_t*)(which ? &st.sb[rt * 64] : &st.sa[rt * 64]), 16, 0, 0);
+  } else {
+    // A's scales in layout_8x4: the same LDS image as the 128x4 tiles (slot rt*64 + cg*32 + q holds
+    // the dwords of rows q, q+32, q+64, q+96 of half rt), gathered one dword (a row's four scales
+    // of a column group) per lane: LDS dword d = 4 * slot + i, two 64-dword loads per wave.
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int d = (wave * 2 + u) * 64 + lane;
+      const int slot = d >> 2, i = d & 3;
+      const int rt = slot >> 6, cgs = (slot >> 5) & 1, qs = slot & 31;
+      const int cgd = (tail && cgs == 1) ? 0 : cgs;
+      int64_t r = m0 + rt * 128 + qs + 32 * i; r = r < rows8 ? r : rows8 - 1;
+      const uint8_t* src = SA + ((r >> 3) * groups + kt * 2 + cgd) * 32 + (r & 7) * 4;
+      __builtin_amdgcn_global_load_lds(src, (lds_t*)(reinterpret_cast<uint32_t*>(st.sa) + (wave * 2 + u) * 64),
+                                       4, 0, 0);
+    }
+    // B's two 128-row tiles: waves w and w+2 load the same bytes to the same place
+    const int rt = wave & 1;
+    int64_t tr = n0 / 128 + rt; tr = tr < ntiles128 ? tr : ntiles128 - 1;
+    const uint8_t* src = SB + (tr * groups + kt * 2 + cg) * 512 + q * 16;
+    __builtin_amdgcn_global_load_lds(src, (lds_t*)&st.sb[rt * 64], 16, 0, 0);
+  }
 }
 
 // s_waitcnt vmcnt(n) (n < 16), leaving lgkmcnt and expcnt unconstrained
@@ -165,12 +190,13 @@ __device__ __forceinline__ f16x8 frag_deq(const Frags& f, int q, int j) {
 
 // ROWSCALE: per-token activation scales; alpha_ptr is then the [M] array of row encode scales
 // and w_gsf_ptr the weight's encode scale, alpha_m = fl32(1 / fl32(x_gsf[m] * w_gsf)).
-template <bool OUT_F32, bool ROWSCALE>
+// SFA8: A's scales are in layout_8x4 with rows8 (= ceil(M/8)*8) rows.
+template <bool OUT_F32, bool ROWSCALE, bool SFA8>
 __global__ __launch_bounds__(256, 1) void mm_fp4_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ SB, const float* __restrict__ alpha_ptr,
     const float* __restrict__ w_gsf_ptr, int64_t M, int64_t N, int64_t K, void* __restrict__ out,
-    int64_t ldc, int ntm, int ntn, bool vec_store) {
+    int64_t ldc, int ntm, int ntn, bool vec_store, int64_t rows8) {
   __shared__ Stage st[NSTAGE];
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
@@ -196,10 +222,11 @@ __global__ __launch_bounds__(256, 1) void mm_fp4_kernel(
   // stage nk-1 into a buffer nobody reads again, so every iteration issues and waits for the same
   // number of loads and the loop body has no branches.
   const int64_t last = nk - 1;
-  issue_stage(st[0], A, B, SA, SB, M, N, K, m0, n0, 0, mtiles128, ntiles128, groups, wave, lane);
-  issue_stage(st[1], A, B, SA, SB, M, N, K, m0, n0, last < 1 ? last : 1, mtiles128, ntiles128, groups,
-              wave, lane);
-  wait_vmcnt<kLoadsPerStage>();
+  issue_stage<SFA8>(st[0], A, B, SA, SB, M, N, K, m0, n0, 0, mtiles128, ntiles128, groups, rows8, wave,
+                    lane);
+  issue_stage<SFA8>(st[1], A, B, SA, SB, M, N, K, m0, n0, last < 1 ? last : 1, mtiles128, ntiles128,
+                    groups, rows8, wave, lane);
+  wait_vmcnt<kLoadsPerStage<SFA8>>();
   __builtin_amdgcn_s_barrier();
 
   Frags f;
@@ -214,8 +241,8 @@ __global__ __launch_bounds__(256, 1) void mm_fp4_kernel(
 
   for (int64_t kt = 0; kt < nk; ++kt) {
     const int64_t ahead = kt + 2 < last ? kt + 2 : last;
-    issue_stage(st[(kt + 2) % NSTAGE], A, B, SA, SB, M, N, K, m0, n0, ahead, mtiles128, ntiles128,
-                groups, wave, lane);
+    issue_stage<SFA8>(st[(kt + 2) % NSTAGE], A, B, SA, SB, M, N, K, m0, n0, ahead, mtiles128,
+                      ntiles128, groups, rows8, wave, lane);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int cb = j & 1, nb = cb ^ 1;
@@ -225,7 +252,7 @@ __global__ __launch_bounds__(256, 1) void mm_fp4_kernel(
         // loads still in flight). Every read of the buffer that the next iteration's loads
         // overwrite happened in read_frags of stage kt, before this barrier.
         __builtin_amdgcn_sched_barrier(0);
-        wait_vmcnt<kLoadsPerStage>();
+        wait_vmcnt<kLoadsPerStage<SFA8>>();
         __builtin_amdgcn_s_barrier();
         read_frags(f, st[(kt + 1) % NSTAGE], wm, wn, li, h, half_tail && kt + 2 == nk && h == 1);
       }
@@ -280,7 +307,7 @@ __global__ __launch_bounds__(256, 1) void mm_fp4_kernel(
 
 }  // namespace fp4
 
-template <bool ROWSCALE>
+template <bool ROWSCALE, bool SFA8>
 static void launch_mm_fp4_t(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
                             const float* alpha, const float* w_gsf, int64_t M, int64_t N, int64_t K,
                             void* out, int64_t ldc, int out_dtype, hipStream_t s) {
@@ -288,12 +315,13 @@ static void launch_mm_fp4_t(const uint8_t* a, const uint8_t* sa, const uint8_t* 
   const int64_t tiles = ntm * ntn;
   const size_t esz = out_dtype == BSP_OUT_F32 ? 4 : 2;
   const bool vec = (ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(out) & (4 * esz - 1)) == 0);
+  const int64_t rows8 = ceil_div(M, 8) * 8;
   if (out_dtype == BSP_OUT_F32)
-    hipLaunchKernelGGL((fp4::mm_fp4_kernel<true, ROWSCALE>), dim3((unsigned)tiles), dim3(256), 0, s, a,
-                       sa, b, sb, alpha, w_gsf, M, N, K, out, ldc, (int)ntm, (int)ntn, vec);
+    hipLaunchKernelGGL((fp4::mm_fp4_kernel<true, ROWSCALE, SFA8>), dim3((unsigned)tiles), dim3(256), 0,
+                       s, a, sa, b, sb, alpha, w_gsf, M, N, K, out, ldc, (int)ntm, (int)ntn, vec, rows8);
   else
-    hipLaunchKernelGGL((fp4::mm_fp4_kernel<false, ROWSCALE>), dim3((unsigned)tiles), dim3(256), 0, s, a,
-                       sa, b, sb, alpha, w_gsf, M, N, K, out, ldc, (int)ntm, (int)ntn, vec);
+    hipLaunchKernelGGL((fp4::mm_fp4_kernel<false, ROWSCALE, SFA8>), dim3((unsigned)tiles), dim3(256), 0,
+                       s, a, sa, b, sb, alpha, w_gsf, M, N, K, out, ldc, (int)ntm, (int)ntn, vec, rows8);
 }
 
 }  // namespace bsp
@@ -326,9 +354,21 @@ extern "C" int bsp_mm_fp4(const uint8_t* a_packed, const uint8_t* a_sf, const ui
   int e = mm_fp4_checks("bsp_mm_fp4", a_packed, a_sf, b_packed, b_sf, alpha_dev, M, N, K, out, ldc,
                         out_dtype);
   if (e) return e > 0 ? BSP_OK : e;
-  launch_mm_fp4_t<false>(a_packed, a_sf, b_packed, b_sf, alpha_dev, nullptr, M, N, K, out, ldc,
-                         out_dtype, (hipStream_t)stream);
+  launch_mm_fp4_t<false, false>(a_packed, a_sf, b_packed, b_sf, alpha_dev, nullptr, M, N, K, out, ldc,
+                                out_dtype, (hipStream_t)stream);
   return check_launch("bsp_mm_fp4");
+}
+
+extern "C" int bsp_mm_fp4_8x4(const uint8_t* a_packed, const uint8_t* a_sf, const uint8_t* b_packed,
+                              const uint8_t* b_sf, const float* alpha_dev, int64_t M, int64_t N,
+                              int64_t K, void* out, int64_t ldc, int out_dtype, void* stream) {
+  int e = mm_fp4_checks("bsp_mm_fp4_8x4", a_packed, a_sf, b_packed, b_sf, alpha_dev, M, N, K, out, ldc,
+                        out_dtype);
+  if (e) return e > 0 ? BSP_OK : e;
+  BSP_REQUIRE((reinterpret_cast<uintptr_t>(a_sf) & 3u) == 0, BSP_EINVAL, "bsp_mm_fp4_8x4: a_sf alignment");
+  launch_mm_fp4_t<false, true>(a_packed, a_sf, b_packed, b_sf, alpha_dev, nullptr, M, N, K, out, ldc,
+                               out_dtype, (hipStream_t)stream);
+  return check_launch("bsp_mm_fp4_8x4");
 }
 
 extern "C" int bsp_mm_fp4_per_token(const uint8_t* a_packed, const uint8_t* a_sf,
@@ -340,7 +380,7 @@ extern "C" int bsp_mm_fp4_per_token(const uint8_t* a_packed, const uint8_t* a_sf
                         out, ldc, out_dtype);
   if (e) return e > 0 ? BSP_OK : e;
   BSP_REQUIRE(w_gsf_dev, BSP_EINVAL, "bsp_mm_fp4_per_token: null pointer");
-  launch_mm_fp4_t<true>(a_packed, a_sf, b_packed, b_sf, x_gsf_rows, w_gsf_dev, M, N, K, out, ldc,
-                        out_dtype, (hipStream_t)stream);
+  launch_mm_fp4_t<true, false>(a_packed, a_sf, b_packed, b_sf, x_gsf_rows, w_gsf_dev, M, N, K, out,
+                               ldc, out_dtype, (hipStream_t)stream);
   return check_launch("bsp_mm_fp4_per_token");
 }

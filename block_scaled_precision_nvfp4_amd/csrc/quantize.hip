@@ -66,6 +66,17 @@ __global__ void gsf_finish_kernel(float* amax, float* gsf, float* inv_gsf) {
   *inv_gsf = 1.0f / g;
 }
 
+// 4over6 variant (SGLang nvfp4_online.py, _quantize_weight_nvfp4): the largest block scale is taken
+// as 256, the decode scale is fl32(amax / 1536) (1 when amax == 0) and the encode scale its fl32
+// reciprocal, computed in that order.
+__global__ void gsf_finish_4over6_kernel(float* amax, float* gsf, float* inv_gsf) {
+  float a = *amax;
+  float dec = (a == 0.0f) ? 1.0f : a / 1536.0f;
+  float g = 1.0f / dec;
+  *gsf = g;
+  *inv_gsf = 1.0f / g;
+}
+
 // =============================================================================================
 // a3: alpha = fl32(1 / fl32(x_gsf * w_gsf))
 // =============================================================================================
@@ -156,7 +167,8 @@ __global__ __launch_bounds__(256) void nvfp4_quantize_kernel(const uint16_t* __r
                                                              int64_t M, int64_t K, int64_t ld,
                                                              const float* __restrict__ gsf,
                                                              uint8_t* __restrict__ packed,
-                                                             uint8_t* __restrict__ sf, int64_t Kp) {
+                                                             uint8_t* __restrict__ sf, int64_t Kp,
+                                                             int64_t rows8) {
   __shared__ uint4 sf_tile[128];  // 2 KB = 4 scale tiles of 512 B
   __shared__ float rtab[128];     // fl32(g / e4m3(c)) for code c (0 for c == 0)
   uint8_t* sfb = reinterpret_cast<uint8_t*>(sf_tile);
@@ -212,13 +224,29 @@ __global__ __launch_bounds__(256) void nvfp4_quantize_kernel(const uint16_t* __r
     }
   }
   __syncthreads();
-  const int64_t groups = Kp / 4;                       // 128x4 column groups in the matrix
+  const int64_t groups = Kp / 4;                       // 4-column groups in the matrix
   const int64_t g0 = (int64_t)blockIdx.x * 4;
   const int64_t ng = groups - g0 < 4 ? groups - g0 : 4;
-  if (t < ng * 32) {
-    const int cg = t >> 5;
-    const int64_t tile = (int64_t)blockIdx.y * groups + g0 + cg;
-    reinterpret_cast<uint4*>(sf + tile * 512)[t & 31] = sf_tile[cg * 32 + (t & 31)];
+  if (rows8 == 0) {                                    // 128x4: four whole 512-byte tiles
+    if (t < ng * 32) {
+      const int cg = t >> 5;
+      const int64_t tile = (int64_t)blockIdx.y * groups + g0 + cg;
+      reinterpret_cast<uint4*>(sf + tile * 512)[t & 31] = sf_tile[cg * 32 + (t & 31)];
+    }
+  } else {
+    // 8x4 (rows padded to rows8, a multiple of 8): 32-byte tiles of 8 rows x 4 columns, row-tile
+    // major. A row's 4 scales of a column group are one dword in both layouts; 8 consecutive
+    // threads write one tile and 32 threads four neighbouring tiles (128 contiguous bytes).
+    const uint32_t* sw = reinterpret_cast<const uint32_t*>(sf_tile);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int idx = t + 256 * i;
+      const int rr = (idx >> 5) * 8 + (idx & 7), cg = (idx >> 3) & 3;
+      const int64_t r = row0 + rr;
+      if (cg < ng && r < rows8)
+        reinterpret_cast<uint32_t*>(sf)[((r >> 3) * groups + g0 + cg) * 8 + (r & 7)] =
+            sw[cg * 128 + (rr & 31) * 4 + (rr >> 5)];
+    }
   }
 }
 
@@ -477,7 +505,7 @@ static int hw_cvt_enabled() {
 }
 
 int launch_global_sf(const void* w, int64_t rows, int64_t K, int64_t ld, float* gsf, float* inv,
-                     float* amax, hipStream_t s) {
+                     float* amax, hipStream_t s, bool four_over_six) {
   hipLaunchKernelGGL(amax_init_kernel, dim3(1), dim3(1), 0, s, amax);
   if (rows > 0 && K > 0) {
     const uint16_t* wp = static_cast<const uint16_t*>(w);
@@ -492,41 +520,47 @@ int launch_global_sf(const void* w, int64_t rows, int64_t K, int64_t ld, float* 
       hipLaunchKernelGGL(amax_reduce_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, wp, rows,
                          K, ld, amax);
   }
-  hipLaunchKernelGGL(gsf_finish_kernel, dim3(1), dim3(1), 0, s, amax, gsf, inv);
-  return check_launch("bsp_nvfp4_global_sf");
+  if (four_over_six)
+    hipLaunchKernelGGL(gsf_finish_4over6_kernel, dim3(1), dim3(1), 0, s, amax, gsf, inv);
+  else
+    hipLaunchKernelGGL(gsf_finish_kernel, dim3(1), dim3(1), 0, s, amax, gsf, inv);
+  return check_launch(four_over_six ? "bsp_nvfp4_global_sf_4over6" : "bsp_nvfp4_global_sf");
 }
 
 template <bool GELU>
 static void launch_nvfp4_quantize_t(dim3 grid, const uint16_t* xp, int64_t M, int64_t K, int64_t ld,
                                     const float* gsf, uint8_t* packed, uint8_t* sf, int64_t Kp,
-                                    bool hw, bool vec, hipStream_t s) {
+                                    int64_t rows8, bool hw, bool vec, hipStream_t s) {
   if (hw && vec)
     hipLaunchKernelGGL((nvfp4_quantize_kernel<true, true, GELU>), grid, dim3(256), 0, s, xp, M, K, ld,
-                       gsf, packed, sf, Kp);
+                       gsf, packed, sf, Kp, rows8);
   else if (hw)
     hipLaunchKernelGGL((nvfp4_quantize_kernel<true, false, GELU>), grid, dim3(256), 0, s, xp, M, K, ld,
-                       gsf, packed, sf, Kp);
+                       gsf, packed, sf, Kp, rows8);
   else if (vec)
     hipLaunchKernelGGL((nvfp4_quantize_kernel<false, true, GELU>), grid, dim3(256), 0, s, xp, M, K, ld,
-                       gsf, packed, sf, Kp);
+                       gsf, packed, sf, Kp, rows8);
   else
     hipLaunchKernelGGL((nvfp4_quantize_kernel<false, false, GELU>), grid, dim3(256), 0, s, xp, M, K,
-                       ld, gsf, packed, sf, Kp);
+                       ld, gsf, packed, sf, Kp, rows8);
 }
 
+// layout8: scales in layout_8x4 (rows padded to 8) instead of 128x4
 int launch_nvfp4_quantize(const void* x, int64_t M, int64_t K, int64_t ld, const float* gsf,
-                          uint8_t* packed, uint8_t* sf, hipStream_t s, bool gelu) {
+                          uint8_t* packed, uint8_t* sf, hipStream_t s, bool gelu, bool layout8) {
   const int64_t Mp = ceil_div(M, 128) * 128;
   const int64_t Kp = ceil_div(K / 16, 4) * 4;
   dim3 grid((unsigned)ceil_div(Kp, 16), (unsigned)(Mp / 128));
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   const bool vec = (ld % 8 == 0) && aligned16(x);
   const bool hw = hw_cvt_enabled();
+  const int64_t rows8 = layout8 ? ceil_div(M, 8) * 8 : 0;
   if (gelu)
-    launch_nvfp4_quantize_t<true>(grid, xp, M, K, ld, gsf, packed, sf, Kp, hw, vec, s);
+    launch_nvfp4_quantize_t<true>(grid, xp, M, K, ld, gsf, packed, sf, Kp, rows8, hw, vec, s);
   else
-    launch_nvfp4_quantize_t<false>(grid, xp, M, K, ld, gsf, packed, sf, Kp, hw, vec, s);
-  return check_launch(gelu ? "bsp_nvfp4_quantize_gelu" : "bsp_nvfp4_quantize");
+    launch_nvfp4_quantize_t<false>(grid, xp, M, K, ld, gsf, packed, sf, Kp, rows8, hw, vec, s);
+  return check_launch(gelu ? "bsp_nvfp4_quantize_gelu"
+                           : (layout8 ? "bsp_nvfp4_quantize_8x4" : "bsp_nvfp4_quantize"));
 }
 
 }  // namespace bsp
@@ -541,7 +575,7 @@ extern "C" int bsp_nvfp4_global_sf(const void* w, int64_t rows, int64_t K, int64
   BSP_REQUIRE(rows <= 1 || ld >= K, BSP_ESHAPE, "bsp_nvfp4_global_sf: ld (%lld) < K (%lld)",
               (long long)ld, (long long)K);
   if (int e = check_device()) return e;
-  return launch_global_sf(w, rows, K, ld, gsf, inv_gsf, amax, (hipStream_t)stream);
+  return launch_global_sf(w, rows, K, ld, gsf, inv_gsf, amax, (hipStream_t)stream, false);
 }
 
 template <int C>
@@ -576,7 +610,8 @@ int launch_nvfp4_quantize_per_token(const void* x, int64_t M, int64_t K, int64_t
 }
 
 static int nvfp4_quantize_entry(const char* fn, const void* x, int64_t M, int64_t K, int64_t ld,
-                                const float* gsf, uint8_t* packed, uint8_t* sf, void* stream, bool gelu) {
+                                const float* gsf, uint8_t* packed, uint8_t* sf, void* stream, bool gelu,
+                                bool layout8 = false) {
   BSP_REQUIRE(M >= 0 && K > 0, BSP_EINVAL, "%s: bad size M=%lld K=%lld", fn, (long long)M, (long long)K);
   BSP_REQUIRE(K % 16 == 0, BSP_ESHAPE, "%s: K (%lld) must be a multiple of 16", fn, (long long)K);
   BSP_REQUIRE(M <= 1 || ld >= K, BSP_ESHAPE, "%s: ld (%lld) < K (%lld)", fn, (long long)ld, (long long)K);
@@ -586,7 +621,7 @@ static int nvfp4_quantize_entry(const char* fn, const void* x, int64_t M, int64_
               BSP_EINVAL, "%s: packed must be 4-byte and sf 16-byte aligned", fn);
   BSP_REQUIRE(ceil_div(M, 128) < 65536, BSP_ESHAPE, "%s: M too large", fn);
   if (int e = check_device()) return e;
-  return launch_nvfp4_quantize(x, M, K, ld, gsf, packed, sf, (hipStream_t)stream, gelu);
+  return launch_nvfp4_quantize(x, M, K, ld, gsf, packed, sf, (hipStream_t)stream, gelu, layout8);
 }
 
 extern "C" int bsp_nvfp4_quantize(const void* x, int64_t M, int64_t K, int64_t ld, const float* gsf,
@@ -608,6 +643,22 @@ extern "C" int bsp_nvfp4_quantize_per_token(const void* x, int64_t M, int64_t K,
   BSP_REQUIRE(ceil_div(M, 128) * 32 < (1ll << 31), BSP_ESHAPE, "%s: M too large", fn);
   if (int e = check_device()) return e;
   return launch_nvfp4_quantize_per_token(x, M, K, ld, packed, sf, gsf_rows, (hipStream_t)stream);
+}
+
+extern "C" int bsp_nvfp4_quantize_8x4(const void* x, int64_t M, int64_t K, int64_t ld, const float* gsf,
+                                      uint8_t* packed, uint8_t* sf, void* stream) {
+  return nvfp4_quantize_entry("bsp_nvfp4_quantize_8x4", x, M, K, ld, gsf, packed, sf, stream, false, true);
+}
+
+extern "C" int bsp_nvfp4_global_sf_4over6(const void* w, int64_t rows, int64_t K, int64_t ld,
+                                          float* gsf, float* inv_gsf, float* amax, void* stream) {
+  BSP_REQUIRE(gsf && inv_gsf && amax, BSP_EINVAL, "bsp_nvfp4_global_sf_4over6: null scalar pointer");
+  BSP_REQUIRE(rows >= 0 && K >= 0, BSP_EINVAL, "bsp_nvfp4_global_sf_4over6: negative size");
+  BSP_REQUIRE(rows * K == 0 || w, BSP_EINVAL, "bsp_nvfp4_global_sf_4over6: null weight pointer");
+  BSP_REQUIRE(rows <= 1 || ld >= K, BSP_ESHAPE, "bsp_nvfp4_global_sf_4over6: ld (%lld) < K (%lld)",
+              (long long)ld, (long long)K);
+  if (int e = check_device()) return e;
+  return launch_global_sf(w, rows, K, ld, gsf, inv_gsf, amax, (hipStream_t)stream, true);
 }
 
 extern "C" int bsp_nvfp4_quantize_gelu(const void* y, int64_t M, int64_t K, int64_t ld,

@@ -143,6 +143,33 @@ int bsp_mm_mxfp4(const uint8_t* a_packed, const uint8_t* a_sf, const uint8_t* b_
  * x, y: device bf16 [n], contiguous, 16-byte aligned. */
 int bsp_gelu_tanh_bf16(const void* x, void* y, int64_t n, void* stream);
 
+/* layout_8x4 for small-M activations and the 4over6 weight scale (NEXT row f4). */
+
+/* Bytes of an NVFP4 scale buffer in layout_8x4: ceil(rows/8)*8 * ceil(K/64)*4. */
+int bsp_nvfp4_sf_bytes_8x4(int64_t rows, int64_t K, int64_t* bytes);
+
+/* bsp_nvfp4_quantize with the scales in layout_8x4. [FV-NV] _nvfp4_quantize: for layout_8x4 the
+ * row tile is 8 (rows padded to a multiple of 8 instead of 128). Layout: 32-byte tiles of 8 rows x
+ * 4 scale columns ordered row-tile-major, byte (r, c) at ((r/8)*(Kp/4) + c/4)*32 + (r%8)*4 + c%4
+ * (Kp = ceil(K/64)*4); padded rows M..ceil(M/8)*8-1 and columns K/16..Kp-1 are 0x00.
+ * sf: bsp_nvfp4_sf_bytes_8x4(M, K) bytes, 4-byte aligned. Everything else as bsp_nvfp4_quantize. */
+int bsp_nvfp4_quantize_8x4(const void* x_bf16, int64_t M, int64_t K, int64_t ld, const float* gsf_dev,
+                           uint8_t* packed, uint8_t* sf, void* stream);
+
+/* bsp_mm_fp4 with the activation (A) scales in layout_8x4 (as written by bsp_nvfp4_quantize_8x4)
+ * and the weight (B) scales in 128x4. [FV-NV] _mm_fp4: use_8x4_sf_layout. */
+int bsp_mm_fp4_8x4(const uint8_t* a_packed, const uint8_t* a_sf, const uint8_t* b_packed,
+                   const uint8_t* b_sf, const float* alpha_dev, int64_t M, int64_t N, int64_t K,
+                   void* out, int64_t ldc, int out_dtype, void* stream);
+
+/* Weight scales of the 4over6 variant. [SGL] _quantize_weight_nvfp4: with the 4over6 switches
+ * the largest e4m3 block scale is taken as 256 instead of 448; the decode scale is
+ * fl32(amax / 1536) (1 when amax == 0) and the encode scale is its fl32 reciprocal, in that order:
+ * gsf = fl32(1 / fl32(amax / 1536)), inv_gsf = fl32(1 / gsf). amax as bsp_nvfp4_global_sf
+ * (nan_to_num first). Quantizing W with this gsf keeps every block scale <= 256. */
+int bsp_nvfp4_global_sf_4over6(const void* w_bf16, int64_t rows, int64_t K, int64_t ld,
+                               float* gsf_dev, float* inv_gsf_dev, float* amax_dev, void* stream);
+
 /* Per-token activation scales (NEXT row f3). [SGL] NVFP4OnlineConfig.__init__ (per-token
  * activation path): weights keep their static tensor scale while each activation row (token) gets
  * its own fp32 scale at run time. Row m: amax_m = max|x[m, :]|, gsf_rows[m] = fl32(2688/amax_m)

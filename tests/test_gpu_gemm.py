@@ -192,6 +192,46 @@ def test_per_token_linear_full_size():
     assert_gemm_bf16(gather(c, rows, cols), ref, "cfg4 to_q per-token")
 
 
+# ------------------------------------------------------------------------- layout_8x4 activations
+@pytest.mark.parametrize("m,n,k", [(1, 64, 64), (3, 256, 192), (13, 200, 512), (77, 384, 256),
+                                   (300, 130, 128)])
+def test_mm_fp4_8x4_random_all_elements(m, n, k):
+    """A's scales in layout_8x4: every element against the oracle, and bit-identical to the same
+    GEMM fed the same scale values in the 128x4 layout."""
+    say("mm_fp4_8x4 random", m, n, k)
+    rng = np.random.default_rng(m * 13 + n + k)
+    pa, sa = _rand_nvfp4_operand(rng, m, k)
+    pb, sb = _rand_nvfp4_operand(rng, n, k)
+    rp8, cp = N.sf_padded_shape_8x4(m, k)
+    sa8 = N.swizzle_8x4(N.unswizzle_128x4(sa, *N.sf_padded_shape(m, k))[:rp8])
+    al = f32(0.75)
+    ref = N.mm_fp4(pa, sa8, pb, sb, al, m, n, k, a_layout="8x4")
+    args8 = (dev_u8(pa), dev_u8(sa8), dev_u8(pb), dev_u8(sb), scalar(al))
+    t32 = bsp.bsp_mm_fp4_8x4(*args8, out_dtype=torch.float32)
+    assert_gemm_f32(t32.cpu().numpy().astype(np.float64), ref, f"8x4 {m}x{n}x{k}")
+    t16 = bsp.bsp_mm_fp4_8x4(*args8)
+    assert_gemm_bf16(t16.float().cpu().numpy().astype(np.float64), ref, f"8x4 {m}x{n}x{k}")
+    c128 = bsp.bsp_mm_fp4(dev_u8(pa), dev_u8(sa), dev_u8(pb), dev_u8(sb), scalar(al), out_dtype=torch.float32)
+    assert torch.equal(t32, c128)
+
+
+@pytest.mark.parametrize("m", [1, 8, 13])
+def test_small_m_linear_8x4_chain(m):
+    """Decode-sized activations: quantize to layout_8x4 and run against a prequantized Wan-14B
+    weight (fc_in 13824x5120), checked element by element against the oracle."""
+    xb = tensor_bits(4, "X")[:m]
+    wb = tensor_bits(4, "W")
+    px, sx = bsp.bsp_nvfp4_quantize_8x4(dev_bf16(xb), scalar(1.0))
+    pw, sw, gw, _, _ = bsp.bsp_nvfp4_prequantize_weight(dev_bf16(wb))
+    alpha = bsp.bsp_nvfp4_alpha(scalar(1.0), gw)
+    c = bsp.bsp_mm_fp4_8x4(px, sx, pw, sw, alpha, out_dtype=torch.float32)
+    rpx, rsx = N.quantize(xb, f32(1.0), layout="8x4")
+    assert np.array_equal(host_u8(px), rpx) and np.array_equal(host_u8(sx).ravel(), rsx)
+    ref = N.mm_fp4(rpx, rsx, host_u8(pw), host_u8(sw).ravel(), alpha.item(), m, wb.shape[0],
+                   wb.shape[1], a_layout="8x4")
+    assert_gemm_f32(c.cpu().numpy().astype(np.float64), ref, f"small-M 8x4 m={m}")
+
+
 # ------------------------------------------------------------------------------------------ MXFP8
 def _rand_mx_operand(rng, rows, k):
     q = rng.integers(0, 256, size=(rows, k)).astype(np.uint8)

@@ -131,6 +131,34 @@ def test_nvfp4_quantize_per_token_full_size_sampled_rows(cfg, name):
     assert np.all(lin[m:] == 0)
 
 
+@pytest.mark.parametrize("m,k", [(1, 16), (5, 64), (13, 80), (77, 1536), (129, 96), (300, 512)])
+@pytest.mark.parametrize("gsf_kind", ["unit", "weight"])
+def test_nvfp4_quantize_8x4_bit_exact(m, k, gsf_kind):
+    say("nvfp4_quantize_8x4", m, k, gsf_kind)
+    xb = W.small_case(m, k, seed=m * 29 + k, outlier_frac=0.02)
+    g = f32(1.0) if gsf_kind == "unit" else N.global_sf(xb)[0]
+    p, sf = bsp.bsp_nvfp4_quantize_8x4(dev_bf16(xb), scalar(g))
+    rp, rs = N.quantize(xb, g, layout="8x4")
+    assert sf.numel() == rs.size
+    assert np.array_equal(host_u8(p), rp)
+    assert np.array_equal(host_u8(sf).ravel(), rs)
+
+
+def test_global_sf_4over6_bit_exact():
+    cases = [tensor_bits(1, "W"), tensor_bits(2, "W"), W.small_case(3, 100, 4, std=1e-3),
+             np.zeros((4, 64), dtype=np.uint16), W.small_case(7, 64, 12, std=30.0)]
+    for wb in cases:
+        gsf, inv, amax = bsp.bsp_nvfp4_global_sf_4over6(dev_bf16(wb))
+        rg, ri, ra = N.global_sf_4over6(wb)
+        assert gsf.item() == rg and inv.item() == ri and amax.item() == ra
+        if wb.shape[1] % 16:
+            continue
+        p, sf = bsp.bsp_nvfp4_quantize(dev_bf16(wb), gsf)
+        rp, rs = N.quantize(wb, rg)
+        assert np.array_equal(host_u8(p), rp) and np.array_equal(host_u8(sf).ravel(), rs)
+        assert rs.max() <= 0x78                        # block scales stay at or below 256
+
+
 def test_global_sf_bit_exact():
     cases = [tensor_bits(1, "W"), tensor_bits(2, "W"), W.small_case(3, 100, 4, std=1e-3),
              np.zeros((4, 64), dtype=np.uint16)]
