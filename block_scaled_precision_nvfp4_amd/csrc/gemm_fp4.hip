@@ -16,8 +16,9 @@
 // LDS holds 256 rows x 64 bytes of packed A and of B (four 16-byte chunks per row, XOR-swizzled
 // by row for conflict-free 16-byte reads) plus the 128x4 scale tiles (two 128-row tiles x two
 // 4-column groups per operand, copied verbatim: in that layout a row's four scales for 64 K are
-// one dword). Two stages, register prefetch of the next stage's global data. K % 128 == 64 ends
-// with a zero-filled half stage.
+// one dword). Three stages in a ring, filled by global_load_lds (global -> LDS with no register
+// staging) two stages ahead. K % 128 == 64 ends with a half stage whose other half's scales are
+// zeroed.
 //
 // Lane (i, h) of a wave (i = lane % 32, h = lane / 32) owns, per stage, the 32 bytes of row i at
 // K [64h, 64h + 64): 8 MFMA sub-steps of K 16, sub-step j using its elements 64h + 8j .. + 7
@@ -85,7 +86,9 @@ __device__ __forceinline__ uint32_t comp(const u32x4& v, int j) {
 // applied on the global side: LDS slot s holds row s/4, logical chunk (s%4) ^ ((row/2 ^ row/4)%4).
 // K % 128 == 64: the last stage's second half re-reads its first half (in bounds) and the compute
 // zeroes that half's scales.
-template <bool SFA8>
+// PART < 0: everything; 0-3: operand chunk pair i = PART; 4: scales. The main loop issues the
+// parts during sub-steps 0-4 instead of in one burst.
+template <bool SFA8, int PART = -1>
 __device__ __forceinline__ void issue_stage(Stage& st, const uint8_t* __restrict__ A,
                                             const uint8_t* __restrict__ B,
                                             const uint8_t* __restrict__ SA,
@@ -97,6 +100,7 @@ __device__ __forceinline__ void issue_stage(Stage& st, const uint8_t* __restrict
   const bool tail = kt * 128 + 64 >= K;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
+    if (PART >= 0 && PART != i) continue;
     const int slot0 = (wave * 4 + i) * 64;
     const int s = slot0 + lane;
     const int row = s >> 2;
@@ -108,6 +112,7 @@ __device__ __forceinline__ void issue_stage(Stage& st, const uint8_t* __restrict
     __builtin_amdgcn_global_load_lds(A + ra * hk + koff, (lds_t*)&st.a[slot0], 16, 0, 0);
     __builtin_amdgcn_global_load_lds(B + rb * hk + koff, (lds_t*)&st.b[slot0], 16, 0, 0);
   }
+  if (PART >= 0 && PART != 4) return;
   const int cg0 = lane >> 5, q = lane & 31;
   const int cg = (tail && cg0 == 1) ? 0 : cg0;
   if constexpr (!SFA8) {
@@ -182,6 +187,24 @@ __device__ __forceinline__ void read_frags(Frags& f, const Stage& s, int wm, int
   }
 }
 
+// Dequantization in two halves: the converts of a fragment in one MFMA group, its scale multiplies
+// in the next (so no multiply waits on a convert issued just before it).
+struct Raw { f16x2 p[4]; f16x2 s; };
+__device__ __forceinline__ Raw frag_cvt(const Frags& f, int q, int j) {
+  const uint32_t w = q < 4 ? comp(f.pa[j >> 2][q], j & 3) : comp(f.pb[j >> 2][q - 4], j & 3);
+  Raw r;
+  r.s = q < 4 ? scale_pair(comp(f.wa, q), j >> 1) : scale_pair(comp(f.wb, q - 4), j >> 1);
+  r.p[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
+  r.p[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
+  r.p[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
+  r.p[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
+  return r;
+}
+__device__ __forceinline__ f16x8 raw_mul(const Raw& r) {
+  f16x2 p0 = r.p[0] * r.s, p1 = r.p[1] * r.s, p2 = r.p[2] * r.s, p3 = r.p[3] * r.s;
+  return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
 // dequantize fragment q (0-3: A row tiles, 4-7: B row tiles) of sub-step j from f
 __device__ __forceinline__ f16x8 frag_deq(const Frags& f, int q, int j) {
   if (q < 4) return dequant8(comp(f.pa[j >> 2][q], j & 3), scale_pair(comp(f.wa, q), j >> 1));
@@ -236,16 +259,21 @@ __global__ __launch_bounds__(256, 1) void mm_fp4_kernel(
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     xa[0][i] = frag_deq(f, i, 0);
-    xb[0][i] = frag_deq(f, 4 + i, 0);
+    if (i < 3) xb[0][i] = frag_deq(f, 4 + i, 0);
   }
+  Raw r7 = frag_cvt(f, 7, 0), rprev;
 
   for (int64_t kt = 0; kt < nk; ++kt) {
     const int64_t ahead = kt + 2 < last ? kt + 2 : last;
-    issue_stage<SFA8>(st[(kt + 2) % NSTAGE], A, B, SA, SB, M, N, K, m0, n0, ahead, mtiles128,
-                      ntiles128, groups, rows8, wave, lane);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int cb = j & 1, nb = cb ^ 1;
+      __builtin_amdgcn_sched_barrier(0);
+      if (j == 0) issue_stage<SFA8, 0>(st[(kt + 2) % NSTAGE], A, B, SA, SB, M, N, K, m0, n0, ahead, mtiles128, ntiles128, groups, rows8, wave, lane);
+      if (j == 1) issue_stage<SFA8, 1>(st[(kt + 2) % NSTAGE], A, B, SA, SB, M, N, K, m0, n0, ahead, mtiles128, ntiles128, groups, rows8, wave, lane);
+      if (j == 2) issue_stage<SFA8, 2>(st[(kt + 2) % NSTAGE], A, B, SA, SB, M, N, K, m0, n0, ahead, mtiles128, ntiles128, groups, rows8, wave, lane);
+      if (j == 3) issue_stage<SFA8, 3>(st[(kt + 2) % NSTAGE], A, B, SA, SB, M, N, K, m0, n0, ahead, mtiles128, ntiles128, groups, rows8, wave, lane);
+      if (j == 4) issue_stage<SFA8, 4>(st[(kt + 2) % NSTAGE], A, B, SA, SB, M, N, K, m0, n0, ahead, mtiles128, ntiles128, groups, rows8, wave, lane);
       if (j == 7) {
         // Stage kt+1 must be in LDS for every wave: wait until only this wave's loads issued in
         // this iteration are outstanding, then a bare s_barrier (a fence would also wait for the
@@ -276,12 +304,16 @@ __global__ __launch_bounds__(256, 1) void mm_fp4_kernel(
         acc[n][m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xb[cb][n], xa[cb][m], acc[n][m], 0, 0, 0);
         acc[n][m + 1] =
             __builtin_amdgcn_mfma_f32_32x32x16_f16(xb[cb][n], xa[cb][m + 1], acc[n][m + 1], 0, 0, 0);
-        // dequantize one fragment of the next sub-step (of the next stage after sub-step 7)
-        const f16x8 v = frag_deq(f, q, (j + 1) & 7);
-        if (q < 4)
-          xa[nb][q] = v;
-        else
-          xb[nb][q - 4] = v;
+        // convert fragment q of the next sub-step now, multiply fragment q-1 (converted in the
+        // previous group; fragment 7 of this sub-step's set was converted in the previous sub-step)
+        const Raw rq = frag_cvt(f, q, (j + 1) & 7);
+        if (q == 0) {
+          xb[cb][3] = raw_mul(r7);     // needed by groups 6-7 of this sub-step
+        } else {
+          const f16x8 v = raw_mul(rprev);
+          if (q - 1 < 4) xa[nb][q - 1] = v; else xb[nb][q - 5] = v;
+        }
+        if (q == 7) r7 = rq; else rprev = rq;
       }
     }
     __builtin_amdgcn_sched_barrier(0);

@@ -17,8 +17,11 @@
 // holds 64 bytes per row of each operand (64 K of e4m3 or 128 K of e2m1) in LDS as four 16-byte
 // chunks XOR-swizzled by row, plus the stage's scale bytes per row, filled by global_load_lds
 // (no register staging), in a 4-stage ring loaded three stages ahead (a stage computes in ~1000
-// cycles, shorter than the memory latency under load). Fragments of the next stage are read into
-// a second register set behind a barrier placed 768 MFMA cycles before the stage ends.
+// cycles, shorter than the memory latency under load). The loads of stage kt+3 are issued one per
+// MFMA pair during stage kt rather than in a burst. Fragments of the next stage are read into a
+// second register set behind a barrier placed 768 MFMA cycles before the stage ends; their scale
+// dwords are shifted for the lane half only when that stage starts, so nothing waits on the LDS
+// reads while the current stage's MFMAs are still to be issued.
 #include "gemm_common.hpp"
 
 namespace bsp {
@@ -63,7 +66,9 @@ __device__ __forceinline__ void wait_vmcnt() {
 //         scale bytes of the 128-K pair of stages the stage belongs to (16-byte reads);
 //  MXFP4: the two 512-byte 128x4 tiles of the stage's column group, copied verbatim (in that
 //         layout the 16 bytes at (r % 32) * 16 are rows r, r+32, r+64, r+96; 16-byte reads).
-template <int FMT>
+// PART < 0: all loads of the stage; else only load PART (0-3 A chunks, 4-7 B chunks, 8 the
+// scales (MXFP8: A's dword), 9 B's scale dword (MXFP8))
+template <int FMT, int PART = -1>
 __device__ __forceinline__ void issue_stage(Stage& st, const uint8_t* __restrict__ A,
                                             const uint8_t* __restrict__ B,
                                             const uint8_t* __restrict__ SA,
@@ -78,11 +83,16 @@ __device__ __forceinline__ void issue_stage(Stage& st, const uint8_t* __restrict
     const int row = s >> 2;
     const int c = (s & 3) ^ (((row >> 1) ^ (row >> 2)) & 3);
     const int64_t off = kt * 64 + c * 16;
-    int64_t ra = m0 + row; ra = ra < M ? ra : M - 1;
-    int64_t rb = n0 + row; rb = rb < N ? rb : N - 1;
-    __builtin_amdgcn_global_load_lds(A + ra * rowbytes + off, (lds_t*)&st.a[slot0], 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(B + rb * rowbytes + off, (lds_t*)&st.b[slot0], 16, 0, 0);
+    if (PART < 0 || PART == i) {
+      int64_t ra = m0 + row; ra = ra < M ? ra : M - 1;
+      __builtin_amdgcn_global_load_lds(A + ra * rowbytes + off, (lds_t*)&st.a[slot0], 16, 0, 0);
+    }
+    if (PART < 0 || PART == 4 + i) {
+      int64_t rb = n0 + row; rb = rb < N ? rb : N - 1;
+      __builtin_amdgcn_global_load_lds(B + rb * rowbytes + off, (lds_t*)&st.b[slot0], 16, 0, 0);
+    }
   }
+  if (PART >= 0 && PART < 8) return;
   if constexpr (FMT == 0) {
     // each wave: 64 dwords of A's and 64 of B's area; the dword of a row holds the scale bytes of
     // this 128-K pair of stages (4-byte aligned: K % 128 == 0), the stage uses 2 of them
@@ -94,8 +104,8 @@ __device__ __forceinline__ void issue_stage(Stage& st, const uint8_t* __restrict
     uint32_t* la = reinterpret_cast<uint32_t*>(st.sa) + wave * 64;
     uint32_t* lb = reinterpret_cast<uint32_t*>(st.sb) + wave * 64;
     const int64_t kb = (kt & ~(int64_t)1) * 2;
-    __builtin_amdgcn_global_load_lds(SA + ra * ng + kb, (lds_t*)la, 4, 0, 0);
-    __builtin_amdgcn_global_load_lds(SB + rb * ng + kb, (lds_t*)lb, 4, 0, 0);
+    if (PART < 0 || PART == 8) __builtin_amdgcn_global_load_lds(SA + ra * ng + kb, (lds_t*)la, 4, 0, 0);
+    if (PART < 0 || PART == 9) __builtin_amdgcn_global_load_lds(SB + rb * ng + kb, (lds_t*)lb, 4, 0, 0);
   } else {
     // 64 lanes x 16 B = the stage's two 512-byte tiles of one operand: waves 0-1 load A's, waves
     // 2-3 B's (each pair loads the same bytes to the same place, which keeps every wave's load
@@ -145,14 +155,14 @@ __device__ __forceinline__ void read_frags(Frags<FMT>& f, const Stage& s, int wm
       }
     }
   }
-  {  // MXFP8: row dwords in the interleaved order; MXFP4: the 128x4 tiles verbatim. Shifted right
-     // by 8h, so that the byte a lane half needs is byte 2*odd (MXFP8) or 2*ks (MXFP4) for both
-     // halves and the MFMA's op_sel immediate can pick it.
+  {  // MXFP8: row dwords in the interleaved order; MXFP4: the 128x4 tiles verbatim. stage_mfma
+     // shifts them right by 8h, so that the byte a lane half needs is byte 2*odd (MXFP8) or 2*ks
+     // (MXFP4) for both halves and the MFMA's op_sel immediate can pick it.
     const u32x4 va = s.sa[wm * 32 + li];
     const u32x4 vb = s.sb[wn * 32 + li];
-    const int sh = 8 * h;
-    f.sa[0] = va.x >> sh; f.sa[1] = va.y >> sh; f.sa[2] = va.z >> sh; f.sa[3] = va.w >> sh;
-    f.sb[0] = vb.x >> sh; f.sb[1] = vb.y >> sh; f.sb[2] = vb.z >> sh; f.sb[3] = vb.w >> sh;
+    (void)h;
+    f.sa[0] = va.x; f.sa[1] = va.y; f.sa[2] = va.z; f.sa[3] = va.w;
+    f.sb[0] = vb.x; f.sb[1] = vb.y; f.sb[2] = vb.z; f.sb[3] = vb.w;
   }
 }
 
@@ -170,16 +180,36 @@ __device__ __forceinline__ i32x8 op_b(const Frags<1>& f, int i, int ks) {
 
 // One stage of MFMAs from `cur`; the barrier and the read of the next stage into `nxt` are placed
 // Cfg::BAR_PAIRS MFMA pairs before the end.
+struct LoadArgs {
+  const uint8_t* A; const uint8_t* B; const uint8_t* SA; const uint8_t* SB;
+  int64_t M, N, K, m0, n0;
+  int wave, lane;
+};
+
+template <int FMT, int P>
+__device__ __forceinline__ void issue_part(Stage& st, int64_t kt, const LoadArgs& l) {
+  issue_stage<FMT, P>(st, l.A, l.B, l.SA, l.SB, l.M, l.N, l.K, l.m0, l.n0, kt, l.wave, l.lane);
+}
+
 template <int FMT, int ODD>
 __device__ __forceinline__ void stage_mfma(f32x16 (&acc)[4][4], const Frags<FMT>& cur, Frags<FMT>& nxt,
-                                           const Stage& next_st, int wm, int wn, int li, int h) {
+                                           const Stage& next_st, int wm, int wn, int li, int h,
+                                           Stage& ld_st, int64_t ld_kt, const LoadArgs& la) {
   using C = Cfg<FMT>;
   constexpr int PAIRS = 8 * C::KSTEPS;
+  constexpr int WP = PAIRS - C::BAR_PAIRS;
+  constexpr int EXTRA = C::LOADS > PAIRS ? C::LOADS - PAIRS : 0;       // loads doubled up on pairs 0..
+  constexpr int ISSUED = WP + (EXTRA < WP ? EXTRA : WP);               // this stage's loads before WP
+  uint32_t ssa[4], ssb[4];
 #pragma unroll
   for (int p = 0; p < PAIRS; ++p) {
+    if (p == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { ssa[i] = cur.sa[i] >> (8 * h); ssb[i] = cur.sb[i] >> (8 * h); }
+    }
     __builtin_amdgcn_sched_barrier(0);
-    if (p == PAIRS - C::BAR_PAIRS) {
-      wait_vmcnt<2 * C::LOADS>();  // stage kt+1 landed; kt+2 and kt+3 may be in flight
+    if (p == WP) {
+      wait_vmcnt<C::LOADS + ISSUED>();  // stage kt+1 landed; kt+2 and part of kt+3 may be in flight
       __builtin_amdgcn_s_barrier();
       read_frags<FMT>(nxt, next_st, wm, wn, li, h);
     }
@@ -191,12 +221,29 @@ __device__ __forceinline__ void stage_mfma(f32x16 (&acc)[4][4], const Frags<FMT>
       const int m = m0 + mm;
       if (ks == 0)
         acc[n][m] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            op_b(cur, n, 0), op_a(cur, m, 0), acc[n][m], C::CODE, C::CODE, SEL0, (int)cur.sb[n], SEL0,
-            (int)cur.sa[m]);
+            op_b(cur, n, 0), op_a(cur, m, 0), acc[n][m], C::CODE, C::CODE, SEL0, (int)ssb[n], SEL0,
+            (int)ssa[m]);
       else
         acc[n][m] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            op_b(cur, n, 1), op_a(cur, m, 1), acc[n][m], C::CODE, C::CODE, 2, (int)cur.sb[n], 2,
-            (int)cur.sa[m]);
+            op_b(cur, n, 1), op_a(cur, m, 1), acc[n][m], C::CODE, C::CODE, 2, (int)ssb[n], 2,
+            (int)ssa[m]);
+    }
+    // one load of stage kt+3 after each MFMA pair (two on the first pairs when there are more
+    // loads than pairs)
+    if (p < C::LOADS) {
+      if (p == 0) issue_part<FMT, 0>(ld_st, ld_kt, la);
+      if (p == 1) issue_part<FMT, 1>(ld_st, ld_kt, la);
+      if (p == 2) issue_part<FMT, 2>(ld_st, ld_kt, la);
+      if (p == 3) issue_part<FMT, 3>(ld_st, ld_kt, la);
+      if (p == 4) issue_part<FMT, 4>(ld_st, ld_kt, la);
+      if (p == 5) issue_part<FMT, 5>(ld_st, ld_kt, la);
+      if (p == 6) issue_part<FMT, 6>(ld_st, ld_kt, la);
+      if (p == 7) issue_part<FMT, 7>(ld_st, ld_kt, la);
+      if (p == 8) issue_part<FMT, 8>(ld_st, ld_kt, la);
+    }
+    if (p < EXTRA) {
+      if (p == 0) issue_part<FMT, 8>(ld_st, ld_kt, la);
+      if (p == 1) issue_part<FMT, 9>(ld_st, ld_kt, la);
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -240,20 +287,18 @@ __global__ __launch_bounds__(256, 1) void mm_mx_kernel(
   // last stage is peeled after the loop (a branch inside the loop makes the compiler spill).
   // Buffer reuse: stage kt+3's loads (issued at stage kt) overwrite the buffer of stage kt-1, whose
   // fragments were read before stage kt-1's barrier, which every wave has passed.
+  const LoadArgs la{A, B, SA, SB, M, N, K, m0, n0, wave, lane};
   const int64_t pairs = nk / 2;
   for (int64_t pi = 0; pi < pairs; ++pi) {
     const int64_t kt = 2 * pi;
-    issue_stage<FMT>(st[(kt + 3) % NSTAGE], A, B, SA, SB, M, N, K, m0, n0, kt + 3 < last ? kt + 3 : last,
-                     wave, lane);
-    stage_mfma<FMT, 0>(acc, f0, f1, st[(kt + 1) % NSTAGE], wm, wn, li, h);
-    issue_stage<FMT>(st[(kt + 4) % NSTAGE], A, B, SA, SB, M, N, K, m0, n0, kt + 4 < last ? kt + 4 : last,
-                     wave, lane);
-    stage_mfma<FMT, 1>(acc, f1, f0, st[(kt + 2) % NSTAGE], wm, wn, li, h);
+    stage_mfma<FMT, 0>(acc, f0, f1, st[(kt + 1) % NSTAGE], wm, wn, li, h, st[(kt + 3) % NSTAGE],
+                       kt + 3 < last ? kt + 3 : last, la);
+    stage_mfma<FMT, 1>(acc, f1, f0, st[(kt + 2) % NSTAGE], wm, wn, li, h, st[(kt + 4) % NSTAGE],
+                       kt + 4 < last ? kt + 4 : last, la);
   }
   if (nk & 1) {
     const int64_t kt = nk - 1;  // even
-    issue_stage<FMT>(st[(kt + 3) % NSTAGE], A, B, SA, SB, M, N, K, m0, n0, last, wave, lane);
-    stage_mfma<FMT, 0>(acc, f0, f1, st[(kt + 1) % NSTAGE], wm, wn, li, h);
+    stage_mfma<FMT, 0>(acc, f0, f1, st[(kt + 1) % NSTAGE], wm, wn, li, h, st[(kt + 3) % NSTAGE], last, la);
   }
   wait_vmcnt<0>();
   const float a = alpha_ptr ? *alpha_ptr : 1.0f;
