@@ -305,7 +305,7 @@ def _mm_fp4_args(a, a_sf, b, b_sf, out_dtype, out, a_row_tile: int = 128):
     _need(out, "out", out_dtype, dev)
     if out.dim() != 2 or out.shape[0] != m or out.shape[1] != n or out.stride(1) != 1:
         raise ValueError(f"out must be [{m}, {n}] with unit column stride")
-    a_need = bsp_nvfp4_sf_bytes(m, k) if a_row_tile == 128 else -(-m // 8) * 8 * (-(-k // 64) * 4)
+    a_need = bsp_nvfp4_sf_bytes(m, k) if a_row_tile == 128 else bsp_nvfp4_sf_bytes_8x4(m, k)
     if a_sf.numel() < a_need or b_sf.numel() < bsp_nvfp4_sf_bytes(n, k):
         raise ValueError("scale buffers are smaller than the layout needs")
     return m, n, k, code, out
@@ -357,6 +357,12 @@ def bsp_mm_mxfp8(a: torch.Tensor, a_sf: torch.Tensor, b: torch.Tensor, b_sf: tor
 
 
 # ------------------------------------------------------------------------------------- MXFP4
+def bsp_nvfp4_sf_bytes_8x4(rows: int, k: int) -> int:
+    out = ctypes.c_int64(0)
+    _call("bsp_nvfp4_sf_bytes_8x4", rows, k, ctypes.byref(out))
+    return out.value
+
+
 def bsp_mxfp4_sf_bytes(rows: int, k: int) -> int:
     out = ctypes.c_int64(0)
     _call("bsp_mxfp4_sf_bytes", rows, k, ctypes.byref(out))

@@ -88,3 +88,28 @@ def test_python_binding_rejects_bad_inputs_before_the_library():
         bsp.bsp_nvfp4_quantize(torch.zeros(4, 16, dtype=torch.int32), torch.ones(1))
     with pytest.raises(ValueError):
         bsp.bsp_nvfp4_quantize(torch.zeros(4, 16, dtype=torch.bfloat16), torch.ones(1))  # CPU tensor
+
+
+def test_producer_fused_per_token_and_8x4_entry_point_errors():
+    # GELU-fused quantize: same rules as the plain quantize
+    assert _st("bsp_nvfp4_quantize_gelu", P, 4, 24, 24, P, P, P, None)[0] == -2
+    assert _st("bsp_nvfp4_quantize_gelu", None, 0, 32, 32, None, None, None, None)[0] == 0
+    # per-token quantize and GEMM
+    assert _st("bsp_nvfp4_quantize_per_token", P, 4, 24, 24, P, P, P, None)[0] == -2
+    assert _st("bsp_nvfp4_quantize_per_token", P, 4, 32, 32, P, P, None, None)[0] == -1   # gsf_rows
+    assert _st("bsp_nvfp4_quantize_per_token", None, 0, 32, 32, None, None, None, None)[0] == 0
+    assert _st("bsp_mm_fp4_per_token", P, P, P, P, P, P, 8, 8, 96, P, 8, 0, None)[0] == -2
+    assert _st("bsp_mm_fp4_per_token", P, P, P, P, None, P, 8, 8, 128, P, 8, 0, None)[0] == -1
+    assert _st("bsp_mm_fp4_per_token", P, P, P, P, P, P, 8, 8, 128, P, 8, 5, None)[0] == -3
+    # layout_8x4 and the 4over6 scale
+    assert _st("bsp_nvfp4_quantize_8x4", P, 4, 40, 40, P, P, P, None)[0] == -2
+    assert _st("bsp_mm_fp4_8x4", P, P, P, P, P, 8, 8, 96, P, 8, 0, None)[0] == -2
+    assert _st("bsp_mm_fp4_8x4", None, None, None, None, None, 0, 8, 128, None, 8, 0, None)[0] == 0
+    assert _st("bsp_nvfp4_global_sf_4over6", P, 2, 8, 8, None, P, P, None)[0] == -1
+    assert _st("bsp_nvfp4_global_sf_4over6", P, 2, 8, 4, P, P, P, None)[0] == -2        # ld < K
+
+
+def test_sf_bytes_8x4():
+    assert bsp.bsp_nvfp4_sf_bytes_8x4(1, 5120) == 8 * 320
+    assert bsp.bsp_nvfp4_sf_bytes_8x4(13, 80) == 16 * 8
+    assert bsp.bsp_nvfp4_sf_bytes_8x4(0, 64) == 0
