@@ -137,9 +137,21 @@ __device__ __forceinline__ void gelu8_bf16(float (&f)[8]) {
   }
 }
 
+// The quantizers read each input byte once and write each output byte once: their global loads and
+// stores are nontemporal (they do not displace other data in the caches; measured 20-30 % faster
+// when the caches hold another kernel's dirty output).
+typedef uint32_t nt_u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load16_nt(const void* p) {
+  const nt_u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4*>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+__device__ __forceinline__ void store4_nt(void* p, uint32_t v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p));
+}
+
 template <bool VEC>
 __device__ __forceinline__ uint4 load8(const uint16_t* p) {
-  if (VEC) return *reinterpret_cast<const uint4*>(p);
+  if (VEC) return load16_nt(p);
   uint4 v;
   v.x = (uint32_t)p[0] | ((uint32_t)p[1] << 16);
   v.y = (uint32_t)p[2] | ((uint32_t)p[3] << 16);
@@ -217,7 +229,7 @@ __global__ __launch_bounds__(256) void nvfp4_quantize_kernel(const uint16_t* __r
       for (int i = 0; i < 8; ++i) out |= e2m1_encode(f[i] * r) << (4 * i);
     }
     const int rr = s * 8 + rsub;  // row inside the 128-row tile
-    if (full || (kin && row0 + rr < M)) *reinterpret_cast<uint32_t*>(pp + s * pstep) = out;
+    if (full || (kin && row0 + rr < M)) store4_nt(pp + s * pstep, out);
     if ((t & 1) == 0) {
       const int cb = (t & 31) >> 1;  // scale column inside the 16-column tile
       sfb[(cb >> 2) * 512 + (rr & 31) * 16 + (rr >> 5) * 4 + (cb & 3)] = (uint8_t)S;
@@ -318,7 +330,7 @@ __global__ __launch_bounds__(256) void nvfp4_quantize_token_kernel(
       out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, f[2] * r, f[3] * r, 1.0f, 1);
       out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, f[4] * r, f[5] * r, 1.0f, 2);
       out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, f[6] * r, f[7] * r, 1.0f, 3);
-      if (live && e < K) *reinterpret_cast<uint32_t*>(prow + e / 2) = out;
+      if (live && e < K) store4_nt(prow + e / 2, out);
       const int64_t col = e / 16;                         // scale column of this lane pair
       if ((lane & 1) == 0 && col < Kp) sb[col % kTokMaxCols] = (uint8_t)S;
     }
@@ -395,7 +407,8 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const uint16_t* __r
       for (int i = 0; i < 4; ++i) hi |= e4m3_encode(f[4 + i] * inv) << (8 * i);
     }
     if (full || (kin && row0 + s * 8 + rsub < M)) {
-      *reinterpret_cast<uint2*>(qp + s * 8 * K) = make_uint2(lo, hi);
+      typedef uint32_t u32x2_nt __attribute__((ext_vector_type(2)));
+      __builtin_nontemporal_store((u32x2_nt){lo, hi}, reinterpret_cast<u32x2_nt*>(qp + s * 8 * K));
       if ((t & 3) == 0) sp[s * 8 * ng] = (uint8_t)byte;
     }
   }
@@ -455,7 +468,7 @@ __global__ __launch_bounds__(256) void mxfp4_quantize_kernel(const uint16_t* __r
       for (int i = 0; i < 8; ++i) out |= e2m1_encode(f[i] * inv) << (4 * i);
     }
     const int rr = s * 8 + rsub;
-    if (full || (kin && row0 + rr < M)) *reinterpret_cast<uint32_t*>(pp + s * pstep) = out;
+    if (full || (kin && row0 + rr < M)) store4_nt(pp + s * pstep, out);
     if ((t & 3) == 0) {
       const int cb = (t & 31) >> 2;  // scale column inside the 8-column tile
       sfb[(cb >> 2) * 512 + (rr & 31) * 16 + (rr >> 5) * 4 + (cb & 3)] = (uint8_t)byte;
@@ -480,13 +493,13 @@ __global__ __launch_bounds__(256) void gelu_kernel(const uint16_t* __restrict__ 
   const int64_t n8 = n / 8;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8;
        i += (int64_t)gridDim.x * blockDim.x) {
-    uint4 v = reinterpret_cast<const uint4*>(x)[i];
+    uint4 v = load16_nt(reinterpret_cast<const uint4*>(x) + i);
     uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       w[j] = bf16x2_rne(gelu_tanh(bf16_lo(w[j])), gelu_tanh(bf16_hi(w[j])));
     }
-    reinterpret_cast<uint4*>(y)[i] = make_uint4(w[0], w[1], w[2], w[3]);
+    __builtin_nontemporal_store((nt_u32x4){w[0], w[1], w[2], w[3]}, reinterpret_cast<nt_u32x4*>(y) + i);
   }
   // tail (n % 8 elements)
   int64_t i = n8 * 8 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
