@@ -271,8 +271,10 @@ __global__ __launch_bounds__(256) void nvfp4_quantize_kernel(const uint16_t* __r
 // the row. The wave tabulates fl32(gsf_m / e4m3(c)) for the 127 codes in LDS, then quantizes the
 // blocks (lane pairs) exactly as the per-tensor kernel does. When the padded row fits one segment
 // (K <= 64 * 8 * C) it stays in registers between the two phases (one pass over HBM); longer rows
-// are read twice. Rows M..Mp-1 run as zero rows, which writes their 0x00 padding scales. Scale
-// bytes of a row are gathered in LDS and leave as one dword per 128x4 column group.
+// are read twice. Rows M..Mp-1 run as zero rows, which writes their 0x00 padding scales. The four
+// waves of a workgroup own rows q, q+32, q+64, q+96 of one 128-row tile, whose scales of a column
+// group form one 16-byte run of the 128x4 layout: they are gathered in LDS and leave as 16-byte
+// stores.
 constexpr int kTokMaxCols = 1024;  // scale columns per row staged in LDS (K <= 16384 per segment set)
 
 template <int C, bool VEC>
@@ -282,7 +284,8 @@ __global__ __launch_bounds__(256) void nvfp4_quantize_token_kernel(
   __shared__ float rtab[4][128];
   __shared__ uint32_t srow[4][kTokMaxCols / 4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  const int64_t tile = blockIdx.x >> 5, q = blockIdx.x & 31;
+  const int64_t row = tile * 128 + q + 32 * wave;
   const bool live = row < M;
   const int64_t seg_elems = 64 * 8 * C;
   const int64_t kpad = Kp * 16;                     // elements incl. the padding scale columns
@@ -334,17 +337,18 @@ __global__ __launch_bounds__(256) void nvfp4_quantize_token_kernel(
       const int64_t col = e / 16;                         // scale column of this lane pair
       if ((lane & 1) == 0 && col < Kp) sb[col % kTokMaxCols] = (uint8_t)S;
     }
-    // this segment's scale columns [sg * seg_elems / 16, ...) -> one dword per column group
-    // (LDS operations of one wave complete in order: the reads below see the bytes written above)
-    __builtin_amdgcn_wave_barrier();
+    // this segment's scale columns [sg * seg_elems / 16, ...): per column group, the dwords of
+    // the four waves' rows are one 16-byte run at (q * 16) of the group's 512-byte tile
+    __syncthreads();
     const int64_t c0 = sg * seg_elems / 16;
     const int64_t c1 = c0 + seg_elems / 16 < Kp ? c0 + seg_elems / 16 : Kp;
     const int64_t groups = Kp / 4;
-    for (int64_t cg = c0 / 4 + lane; cg < c1 / 4; cg += 64) {
-      const int64_t off = ((row >> 7) * groups + cg) * 512 + (row & 31) * 16 + ((row >> 5) & 3) * 4;
-      *reinterpret_cast<uint32_t*>(sf + off) = srow[wave][cg % (kTokMaxCols / 4)];
+    for (int64_t cg = c0 / 4 + threadIdx.x; cg < c1 / 4; cg += 256) {
+      const int i = (int)(cg % (kTokMaxCols / 4));
+      *reinterpret_cast<uint4*>(sf + (tile * groups + cg) * 512 + q * 16) =
+          make_uint4(srow[0][i], srow[1][i], srow[2][i], srow[3][i]);
     }
-    __builtin_amdgcn_wave_barrier();
+    __syncthreads();
   }
 }
 
