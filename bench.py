@@ -236,10 +236,13 @@ def main():
         "metric": "mm_fp4 TFLOPS (% FP4 MFMA peak) + quantize GB/s (% HBM) at Wan-14B FFN shape",
         "value": round(value, 2), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "nvfp4", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
         "config": {"workload": "Wan-14B FFN on one GPU: X[32760,5120] -> fc_in 13824x5120 -> GELU "
                                "(fused into the NVFP4 quantize of H) -> fc_out 5120x13824, NVFP4 W4A4, "
                                "bf16 out",
+                   "format": "nvfp4 (e2m1 + e4m3 per 16, fp32 global scale); the GEMMs multiply "
+                             "exact fp16 dequantized operands with fp32 accumulation, the quantizers "
+                             "compute in fp32",
                    "tokens": M, "hidden": K1, "ffn": N1, "value_is": "GEMM FLOPs of both "
                    "projections / whole-step time (quantizes and GELU included)"},
         "roofline": roofline,

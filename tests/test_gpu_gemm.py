@@ -56,6 +56,24 @@ def test_mm_fp4_random_operands_all_elements(m, n, k):
     assert np.linalg.norm(c32 - ref) <= 1e-5 * np.linalg.norm(ref)
 
 
+def test_empty_inputs_are_no_ops():
+    """M = 0 (no tokens) through every entry point: no launch, empty outputs, no error."""
+    x = torch.empty((0, 512), dtype=torch.bfloat16, device="cuda")
+    p, sf = bsp.bsp_nvfp4_quantize(x, scalar(1.0))
+    assert p.shape == (0, 256) and sf.numel() == 0
+    p2, sf2, g2 = bsp.bsp_nvfp4_quantize_per_token(x)
+    assert p2.shape == (0, 256) and g2.numel() == 0
+    p3, sf3 = bsp.bsp_nvfp4_quantize_gelu(x, scalar(1.0))
+    assert p3.shape == (0, 256)
+    q, s8 = bsp.bsp_mxfp8_quantize(x)
+    assert q.shape == (0, 512) and s8.shape == (0, 16)
+    wb = tensor_bits(1, "W")
+    pw, sw, gw, _, _ = bsp.bsp_nvfp4_prequantize_weight(dev_bf16(wb))
+    c = bsp.bsp_mm_fp4(p, sf, pw, sw, bsp.bsp_nvfp4_alpha(scalar(1.0), gw))
+    assert c.shape == (0, wb.shape[0])
+    torch.cuda.synchronize()
+
+
 def test_mm_fp4_output_stride_and_tiny_config():
     """Tiny NVFP4 linear (128x256x512): quantize both on the GPU, GEMM into a strided output."""
     xb, wb = tensor_bits(1, "X"), tensor_bits(1, "W")
