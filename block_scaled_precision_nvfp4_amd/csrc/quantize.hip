@@ -619,6 +619,8 @@ int launch_nvfp4_quantize_per_token(const void* x, int64_t M, int64_t K, int64_t
     launch_token_c<4>(xp, M, K, ld, packed, sf, gsf_rows, Kp, vec, s);
   else if (kpad <= 64 * 8 * 8)
     launch_token_c<8>(xp, M, K, ld, packed, sf, gsf_rows, Kp, vec, s);
+  else if (kpad <= 64 * 8 * 10)   // K <= 5120 (fewer registers, more rows in flight per CU)
+    launch_token_c<10>(xp, M, K, ld, packed, sf, gsf_rows, Kp, vec, s);
   else if (kpad <= 64 * 8 * 16)
     launch_token_c<16>(xp, M, K, ld, packed, sf, gsf_rows, Kp, vec, s);
   else
