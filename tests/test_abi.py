@@ -113,3 +113,21 @@ def test_sf_bytes_8x4():
     assert bsp.bsp_nvfp4_sf_bytes_8x4(1, 5120) == 8 * 320
     assert bsp.bsp_nvfp4_sf_bytes_8x4(13, 80) == 16 * 8
     assert bsp.bsp_nvfp4_sf_bytes_8x4(0, 64) == 0
+
+
+def test_plain_c_consumer_compiles_links_and_runs(tmp_path):
+    """include/bsp.h is a C header: a C99 program compiles against it, links libbsp.so and gets
+    the documented results from the host-side paths (no GPU needed)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    libdir = os.path.dirname(bsp.lib()._name)
+    exe = str(tmp_path / "c_consumer")
+    r = subprocess.run([cc, "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                        os.path.join(ROOT, "tests", "c_consumer.c"), "-L", libdir, "-lbsp",
+                        f"-Wl,-rpath,{libdir}", "-o", exe], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and "c consumer ok" in r.stdout, (r.stdout, r.stderr)
