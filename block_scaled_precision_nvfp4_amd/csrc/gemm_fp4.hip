@@ -17,8 +17,10 @@
 // by row for conflict-free 16-byte reads) plus the 128x4 scale tiles (two 128-row tiles x two
 // 4-column groups per operand, copied verbatim: in that layout a row's four scales for 64 K are
 // one dword). Three stages in a ring, filled by global_load_lds (global -> LDS with no register
-// staging) two stages ahead. K % 128 == 64 ends with a half stage whose other half's scales are
-// zeroed.
+// staging) two stages ahead, each lane's 32-bit offsets computed once (LoadPlan) and the stage's
+// K offset carried in the wave-uniform base. K % 128 == 64 ends with a half stage whose other
+// half's scales are zeroed. The stage barrier sits at sub-step 5, so the next stage's fragments
+// are read from LDS several MFMA groups before their first use.
 //
 // Lane (i, h) of a wave (i = lane % 32, h = lane / 32) owns, per stage, the 32 bytes of row i at
 // K [64h, 64h + 64): 8 MFMA sub-steps of K 16, sub-step j using its elements 64h + 8j .. + 7
@@ -55,15 +57,22 @@ __device__ __forceinline__ int chunk_slot(int row, int c) {
   return row * 4 + (c ^ (((row >> 1) ^ (row >> 2)) & 3));
 }
 
-// f16 pair holding (e4m3 scale byte) * 2^-8 twice, built from the bits alone: an e4m3 code c
-// (non-negative) shifted left by 7 is an f16 with exponent field e and mantissa m, i.e.
-// 2^(e-15) (1 + m/8) for e >= 1 and the f16 denormal m * 2^-17 for e == 0, which is the e4m3 value
-// times 2^-8 in both cases. The 2^-8 of each operand is undone in the epilogue (alpha * 2^16).
-__device__ __forceinline__ f16x2 scale_pair(uint32_t word, int byte) {
-  const uint32_t c = (word >> (8 * byte)) & 0x7Fu;
-  const uint32_t bits = (c << 7) | (c << 23);
-  return __builtin_bit_cast(f16x2, bits);
+// f16 holding (e4m3 scale byte) * 2^-8, built from the bits alone: an e4m3 code c (non-negative)
+// shifted left by 7 is an f16 with exponent field e and mantissa m, i.e. 2^(e-15) (1 + m/8) for
+// e >= 1 and the f16 denormal m * 2^-17 for e == 0, which is the e4m3 value times 2^-8 in both
+// cases. The 2^-8 of each operand is undone in the epilogue (alpha * 2^16).
+// A row's scale dword holds the bytes of four K blocks; two shifts and masks place bytes 0 and 2
+// (shift left 7) or bytes 1 and 3 (shift right 1) at bit 7 of the low and high f16 halves, and the
+// packed multiply broadcasts the half it needs. `mask` is 0x3F803F80 (sign bits dropped), or 0 to
+// zero every scale of the dword.
+__device__ __forceinline__ uint32_t scale_halves(uint32_t word, int byte, uint32_t mask) {
+  return ((byte & 1) ? (word >> 1) : (word << 7)) & mask;
 }
+__device__ __forceinline__ f16x2 scale_pair(uint32_t word, int byte, uint32_t mask) {
+  const f16x2 t = __builtin_bit_cast(f16x2, scale_halves(word, byte, mask));
+  return (byte & 2) ? __builtin_shufflevector(t, t, 1, 1) : __builtin_shufflevector(t, t, 0, 0);
+}
+constexpr uint32_t kScaleMask = 0x3F803F80u;
 
 // 8 e2m1 values (one dword) times their scale pair -> 8 fp16. Exact: every product e2m1 * e4m3 *
 // 2^-8 has at most 6 significant bits and its lowest bit is >= 2^-18, within fp16's reach.
@@ -80,48 +89,76 @@ __device__ __forceinline__ uint32_t comp(const u32x4& v, int j) {
   return j == 0 ? v.x : (j == 1 ? v.y : (j == 2 ? v.z : v.w));
 }
 
+// Per-lane part of the global -> LDS loads, fixed for the whole K loop. Slot s = slot0 + lane of
+// instruction i holds row s/4 and logical chunk (s%4) ^ ((row/2 ^ row/4) % 4); row/2 and row/4 only
+// see lane bits (slot0 is a multiple of 64), so the chunk is the same for all four instructions.
+// Offsets are 32-bit and relative to the tile's first row; the stage's K offset and the tile's
+// row offset go into the wave-uniform base address.
+struct LoadPlan {
+  uint32_t offa[4], offb[4];  // (clamped local row) * K/2 + chunk * 16
+  uint32_t tail_delta;        // 32 where the chunk is in the stage's second K half, else 0
+  uint32_t soff, stail_delta; // scale tiles: column group * 512 + q * 16; 512 for column group 1
+};
+
+__device__ __forceinline__ LoadPlan make_load_plan(int64_t M, int64_t N, int64_t K, int64_t m0,
+                                                   int64_t n0, int wave, int lane) {
+  LoadPlan lp;
+  const int64_t hk = K / 2;
+  const int row0 = (wave * 16) * 4 + (lane >> 2);  // row of instruction 0; instruction i adds 16 i
+  const int c = (lane & 3) ^ (((row0 >> 1) ^ (row0 >> 2)) & 3);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = row0 + 16 * i;
+    const int64_t ra = m0 + row < M ? row : M - 1 - m0;
+    const int64_t rb = n0 + row < N ? row : N - 1 - n0;
+    lp.offa[i] = (uint32_t)(ra * hk + c * 16);
+    lp.offb[i] = (uint32_t)(rb * hk + c * 16);
+  }
+  lp.tail_delta = c >= 2 ? 32u : 0u;
+  const int cg = lane >> 5, q = lane & 31;
+  lp.soff = (uint32_t)(cg * 512 + q * 16);
+  lp.stail_delta = cg == 1 ? 512u : 0u;
+  return lp;
+}
+
 // Stage kt's operand and scale bytes, global -> LDS without passing through registers
 // (global_load_lds_dwordx4: lane l of an instruction lands at the LDS base + 16 l). Each wave
 // issues 4 instructions per operand (64 chunks each) and one for a scale half. The XOR swizzle is
-// applied on the global side: LDS slot s holds row s/4, logical chunk (s%4) ^ ((row/2 ^ row/4)%4).
+// applied on the global side (LoadPlan).
 // K % 128 == 64: the last stage's second half re-reads its first half (in bounds) and the compute
 // zeroes that half's scales.
 // PART < 0: everything; 0-3: operand chunk pair i = PART; 4: scales. The main loop issues the
 // parts during sub-steps 0-4 instead of in one burst.
 template <bool SFA8, int PART = -1>
-__device__ __forceinline__ void issue_stage(Stage& st, const uint8_t* __restrict__ A,
+__device__ __forceinline__ void issue_stage(Stage& st, const LoadPlan& lp,
+                                            const uint8_t* __restrict__ A,
                                             const uint8_t* __restrict__ B,
                                             const uint8_t* __restrict__ SA,
-                                            const uint8_t* __restrict__ SB, int64_t M, int64_t N,
-                                            int64_t K, int64_t m0, int64_t n0, int64_t kt,
-                                            int64_t mtiles128, int64_t ntiles128, int64_t groups,
-                                            int64_t rows8, int wave, int lane) {
+                                            const uint8_t* __restrict__ SB, int64_t K, int64_t m0,
+                                            int64_t n0, int64_t kt, int64_t mtiles128,
+                                            int64_t ntiles128, int64_t groups, int64_t rows8,
+                                            int wave, int lane) {
   const int64_t hk = K / 2;
   const bool tail = kt * 128 + 64 >= K;
+  const uint32_t td = tail ? lp.tail_delta : 0u;
+  const uint8_t* a_base = A + m0 * hk + kt * 64;
+  const uint8_t* b_base = B + n0 * hk + kt * 64;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if (PART >= 0 && PART != i) continue;
     const int slot0 = (wave * 4 + i) * 64;
-    const int s = slot0 + lane;
-    const int row = s >> 2;
-    int c = (s & 3) ^ (((row >> 1) ^ (row >> 2)) & 3);
-    c = (tail && c >= 2) ? c - 2 : c;
-    const int64_t koff = kt * 64 + c * 16;
-    int64_t ra = m0 + row; ra = ra < M ? ra : M - 1;
-    int64_t rb = n0 + row; rb = rb < N ? rb : N - 1;
-    __builtin_amdgcn_global_load_lds(A + ra * hk + koff, (lds_t*)&st.a[slot0], 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(B + rb * hk + koff, (lds_t*)&st.b[slot0], 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(a_base + (lp.offa[i] - td), (lds_t*)&st.a[slot0], 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(b_base + (lp.offb[i] - td), (lds_t*)&st.b[slot0], 16, 0, 0);
   }
   if (PART >= 0 && PART != 4) return;
-  const int cg0 = lane >> 5, q = lane & 31;
-  const int cg = (tail && cg0 == 1) ? 0 : cg0;
+  const uint32_t soff = lp.soff - (tail ? lp.stail_delta : 0u);
   if constexpr (!SFA8) {
     // waves 0-1: A's two 128-row scale tiles, waves 2-3: B's; slot = rt*64 + cg*32 + q
     const int which = wave >> 1, rt = wave & 1;
     const int64_t r0 = which ? n0 / 128 : m0 / 128;
     const int64_t nt = which ? ntiles128 : mtiles128;
     int64_t tr = r0 + rt; tr = tr < nt ? tr : nt - 1;
-    const uint8_t* src = (which ? SB : SA) + (tr * groups + kt * 2 + cg) * 512 + q * 16;
+    const uint8_t* src = (which ? SB : SA) + (tr * groups + kt * 2) * 512 + soff;
     __builtin_amdgcn_global_load_lds(src, (lds_t*)(which ? &st.sb[rt * 64] : &st.sa[rt * 64]), 16, 0, 0);
   } else {
     // A's scales in layout_8x4: the same LDS image as the 128x4 tiles (slot rt*64 + cg*32 + q holds
@@ -141,7 +178,7 @@ __device__ __forceinline__ void issue_stage(Stage& st, const uint8_t* __restrict
     // B's two 128-row tiles: waves w and w+2 load the same bytes to the same place
     const int rt = wave & 1;
     int64_t tr = n0 / 128 + rt; tr = tr < ntiles128 ? tr : ntiles128 - 1;
-    const uint8_t* src = SB + (tr * groups + kt * 2 + cg) * 512 + q * 16;
+    const uint8_t* src = SB + (tr * groups + kt * 2) * 512 + soff;
     __builtin_amdgcn_global_load_lds(src, (lds_t*)&st.sb[rt * 64], 16, 0, 0);
   }
 }
@@ -160,6 +197,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 struct Frags {
   u32x4 pa[2][4], pb[2][4];
   u32x4 wa, wb;
+  uint32_t ma, mb;  // kScaleMask, or 0 where this lane half's K range is past the end
 };
 
 // Chunk `cc` (0: sub-steps 0-3, 1: sub-steps 4-7) of a wave's packed fragments of one stage.
@@ -174,17 +212,16 @@ __device__ __forceinline__ void read_chunk(Frags& f, const Stage& s, int cc, int
   }
 }
 
-// First chunk and the scale dwords (the second chunk is read during sub-steps 1-2, spreading the
-// LDS traffic over the stage).
+// The scale dwords and the first chunk (the second chunk is read during sub-steps 1-2, spreading
+// the LDS traffic over the stage).
 __device__ __forceinline__ void read_frags(Frags& f, const Stage& s, int wm, int wn, int li, int h,
                                            bool zero_half) {
-  read_chunk(f, s, 0, wm, wn, li, h);
+  // scale dwords first: the first dequantization after the stage barrier needs them and the first
+  // chunk's A fragment, and LDS reads complete in order
   f.wa = s.sa[(wm * 2 + h) * 32 + li];
   f.wb = s.sb[(wn * 2 + h) * 32 + li];
-  if (zero_half) {  // K % 128 == 64 tail: this lane half's K range is past the end
-    f.wa = u32x4{0u, 0u, 0u, 0u};
-    f.wb = u32x4{0u, 0u, 0u, 0u};
-  }
+  read_chunk(f, s, 0, wm, wn, li, h);
+  f.ma = f.mb = zero_half ? 0u : kScaleMask;  // K % 128 == 64 tail: zero this lane half's scales
 }
 
 // Dequantization in two halves: the converts of a fragment in one MFMA group, its scale multiplies
@@ -193,7 +230,7 @@ struct Raw { f16x2 p[4]; f16x2 s; };
 __device__ __forceinline__ Raw frag_cvt(const Frags& f, int q, int j) {
   const uint32_t w = q < 4 ? comp(f.pa[j >> 2][q], j & 3) : comp(f.pb[j >> 2][q - 4], j & 3);
   Raw r;
-  r.s = q < 4 ? scale_pair(comp(f.wa, q), j >> 1) : scale_pair(comp(f.wb, q - 4), j >> 1);
+  r.s = q < 4 ? scale_pair(comp(f.wa, q), j >> 1, f.ma) : scale_pair(comp(f.wb, q - 4), j >> 1, f.mb);
   r.p[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
   r.p[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
   r.p[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
@@ -207,8 +244,8 @@ __device__ __forceinline__ f16x8 raw_mul(const Raw& r) {
 
 // dequantize fragment q (0-3: A row tiles, 4-7: B row tiles) of sub-step j from f
 __device__ __forceinline__ f16x8 frag_deq(const Frags& f, int q, int j) {
-  if (q < 4) return dequant8(comp(f.pa[j >> 2][q], j & 3), scale_pair(comp(f.wa, q), j >> 1));
-  return dequant8(comp(f.pb[j >> 2][q - 4], j & 3), scale_pair(comp(f.wb, q - 4), j >> 1));
+  if (q < 4) return dequant8(comp(f.pa[j >> 2][q], j & 3), scale_pair(comp(f.wa, q), j >> 1, f.ma));
+  return dequant8(comp(f.pb[j >> 2][q - 4], j & 3), scale_pair(comp(f.wb, q - 4), j >> 1, f.mb));
 }
 
 // ROWSCALE: per-token activation scales; alpha_ptr is then the [M] array of row encode scales
@@ -245,9 +282,10 @@ __global__ __launch_bounds__(256, 1) void mm_fp4_kernel(
   // stage nk-1 into a buffer nobody reads again, so every iteration issues and waits for the same
   // number of loads and the loop body has no branches.
   const int64_t last = nk - 1;
-  issue_stage<SFA8>(st[0], A, B, SA, SB, M, N, K, m0, n0, 0, mtiles128, ntiles128, groups, rows8, wave,
+  const LoadPlan lp = make_load_plan(M, N, K, m0, n0, wave, lane);
+  issue_stage<SFA8>(st[0], lp, A, B, SA, SB, K, m0, n0, 0, mtiles128, ntiles128, groups, rows8, wave,
                     lane);
-  issue_stage<SFA8>(st[1], A, B, SA, SB, M, N, K, m0, n0, last < 1 ? last : 1, mtiles128, ntiles128,
+  issue_stage<SFA8>(st[1], lp, A, B, SA, SB, K, m0, n0, last < 1 ? last : 1, mtiles128, ntiles128,
                     groups, rows8, wave, lane);
   wait_vmcnt<kLoadsPerStage<SFA8>>();
   __builtin_amdgcn_s_barrier();
@@ -263,34 +301,50 @@ __global__ __launch_bounds__(256, 1) void mm_fp4_kernel(
   }
   Raw r7 = frag_cvt(f, 7, 0), rprev;
 
+  // ring buffers of stages kt, kt+1 and kt+2 (wave-uniform, rotated each iteration)
+  int b_cur = 0, b_next = 1, b_ahead = 2;
   for (int64_t kt = 0; kt < nk; ++kt) {
     const int64_t ahead = kt + 2 < last ? kt + 2 : last;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int cb = j & 1, nb = cb ^ 1;
       __builtin_amdgcn_sched_barrier(0);
-      if (j == 0) issue_stage<SFA8, 0>(st[(kt + 2) % NSTAGE], A, B, SA, SB, M, N, K, m0, n0, ahead, mtiles128, ntiles128, groups, rows8, wave, lane);
-      if (j == 1) issue_stage<SFA8, 1>(st[(kt + 2) % NSTAGE], A, B, SA, SB, M, N, K, m0, n0, ahead, mtiles128, ntiles128, groups, rows8, wave, lane);
-      if (j == 2) issue_stage<SFA8, 2>(st[(kt + 2) % NSTAGE], A, B, SA, SB, M, N, K, m0, n0, ahead, mtiles128, ntiles128, groups, rows8, wave, lane);
-      if (j == 3) issue_stage<SFA8, 3>(st[(kt + 2) % NSTAGE], A, B, SA, SB, M, N, K, m0, n0, ahead, mtiles128, ntiles128, groups, rows8, wave, lane);
-      if (j == 4) issue_stage<SFA8, 4>(st[(kt + 2) % NSTAGE], A, B, SA, SB, M, N, K, m0, n0, ahead, mtiles128, ntiles128, groups, rows8, wave, lane);
-      if (j == 7) {
+      if (j == 0) issue_stage<SFA8, 0>(st[b_ahead], lp, A, B, SA, SB, K, m0, n0, ahead, mtiles128, ntiles128, groups, rows8, wave, lane);
+      if (j == 1) issue_stage<SFA8, 1>(st[b_ahead], lp, A, B, SA, SB, K, m0, n0, ahead, mtiles128, ntiles128, groups, rows8, wave, lane);
+      if (j == 2) issue_stage<SFA8, 2>(st[b_ahead], lp, A, B, SA, SB, K, m0, n0, ahead, mtiles128, ntiles128, groups, rows8, wave, lane);
+      if (j == 3) issue_stage<SFA8, 3>(st[b_ahead], lp, A, B, SA, SB, K, m0, n0, ahead, mtiles128, ntiles128, groups, rows8, wave, lane);
+      if (j == 4) issue_stage<SFA8, 4>(st[b_ahead], lp, A, B, SA, SB, K, m0, n0, ahead, mtiles128, ntiles128, groups, rows8, wave, lane);
+      if (j == 5) {
         // Stage kt+1 must be in LDS for every wave: wait until only this wave's loads issued in
         // this iteration are outstanding, then a bare s_barrier (a fence would also wait for the
         // loads still in flight). Every read of the buffer that the next iteration's loads
-        // overwrite happened in read_frags of stage kt, before this barrier.
+        // overwrite (stage kt's) happened before this barrier, in sub-steps 1-2 of this iteration
+        // and sub-steps 5-7 of the previous one. The next stage's first chunk goes into
+        // registers that sub-steps 4-7 no longer read, so it lands well before sub-step 7
+        // converts it.
         __builtin_amdgcn_sched_barrier(0);
         wait_vmcnt<kLoadsPerStage<SFA8>>();
         __builtin_amdgcn_s_barrier();
-        read_frags(f, st[(kt + 1) % NSTAGE], wm, wn, li, h, half_tail && kt + 2 == nk && h == 1);
+        read_chunk(f, st[b_next], 0, wm, wn, li, h);
       }
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         __builtin_amdgcn_sched_barrier(0);
+        // the next stage's scale dwords, each as soon as this stage's last dequantization that
+        // reads the old one has issued (A's after fragment 3 of sub-step 7, B's after fragment 7)
+        const bool zero_next = half_tail && kt + 2 == nk && h == 1;
+        if (j == 6 && q == 4) {
+          f.wa = st[b_next].sa[(wm * 2 + h) * 32 + li];
+          f.ma = zero_next ? 0u : kScaleMask;
+        }
+        if (j == 7 && q == 0) {
+          f.wb = st[b_next].sb[(wn * 2 + h) * 32 + li];
+          f.mb = zero_next ? 0u : kScaleMask;
+        }
         // second chunk of this stage: half of it during sub-step 1, half during sub-step 2 (it is
         // first needed by the dequantization of sub-step 4, issued during sub-step 3)
         if ((j == 1 && q == 0) || (j == 2 && q == 0)) {
-          const Stage& cs = st[kt % NSTAGE];
+          const Stage& cs = st[b_cur];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             if (j == 1) {
@@ -317,6 +371,8 @@ __global__ __launch_bounds__(256, 1) void mm_fp4_kernel(
       }
     }
     __builtin_amdgcn_sched_barrier(0);
+    const int b_free = b_cur;
+    b_cur = b_next; b_next = b_ahead; b_ahead = b_free;
   }
   wait_vmcnt<0>();
 
@@ -368,6 +424,8 @@ static int mm_fp4_checks(const char* fn, const uint8_t* a_packed, const uint8_t*
   BSP_REQUIRE(out_dtype == BSP_OUT_BF16 || out_dtype == BSP_OUT_F32, BSP_EDTYPE,
               "%s: out_dtype must be BSP_OUT_BF16 (0) or BSP_OUT_F32 (1), got %d", fn, out_dtype);
   BSP_REQUIRE(K % 64 == 0, BSP_ESHAPE, "%s: K (%lld) must be a multiple of 64", fn, (long long)K);
+  // the loads address a tile's 256 rows with 32-bit offsets
+  BSP_REQUIRE(K <= (1ll << 24), BSP_ESHAPE, "%s: K (%lld) must be at most 16777216", fn, (long long)K);
   BSP_REQUIRE(M <= 1 || ldc >= N, BSP_ESHAPE, "%s: ldc (%lld) < N (%lld)", fn, (long long)ldc,
               (long long)N);
   if (M == 0 || N == 0) return 1;

@@ -90,7 +90,8 @@ int bsp_nvfp4_alpha(const float* x_gsf_dev, const float* w_gsf_dev, float* alpha
  * [N, K/2] packed buffer, i.e. B here is that K-major [N, K/2] buffer.
  * a_packed: device uint8 [M, K/2]; a_sf: 128x4 scales for M rows (bsp_nvfp4_sf_bytes(M, K));
  * b_packed: device uint8 [N, K/2]; b_sf: 128x4 scales for N rows; out: device [M, N] with row
- * stride ldc elements (bf16 or fp32 per out_dtype). Requires K % 64 == 0; M, N arbitrary >= 0. */
+ * stride ldc elements (bf16 or fp32 per out_dtype). Requires K % 64 == 0 and K <= 2^24 (else
+ * BSP_ESHAPE); M, N arbitrary >= 0. */
 int bsp_mm_fp4(const uint8_t* a_packed, const uint8_t* a_sf, const uint8_t* b_packed,
                const uint8_t* b_sf, const float* alpha_dev, int64_t M, int64_t N, int64_t K,
                void* out, int64_t ldc, int out_dtype, void* stream);

@@ -64,6 +64,8 @@ def test_gemm_shape_and_dtype_errors():
     assert st == -3
     st, _ = _st("bsp_mm_fp4", P, P, P, P, P, 8, 16, 128, P, 8, 0, None)   # ldc < N
     assert st == -2
+    st, msg = _st("bsp_mm_fp4", P, P, P, P, P, 8, 8, (1 << 24) + 64, P, 8, 0, None)
+    assert st == -2 and "at most 16777216" in msg
     assert _st("bsp_mm_fp4", None, None, None, None, None, 0, 8, 128, None, 8, 0, None)[0] == 0
     st, _ = _st("bsp_mm_mxfp8", P, P, P, P, 8, 8, 64, P, 8, 0, None)
     assert st == -2
