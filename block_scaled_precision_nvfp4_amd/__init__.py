@@ -47,6 +47,9 @@ SIGNATURES = {
     "bsp_mm_fp4_8x4": ([_p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _int, _p], _int),
     "bsp_nvfp4_global_sf_4over6": ([_p, _i64, _i64, _i64, _p, _p, _p, _p], _int),
     "bsp_mm_fp4_per_token": ([_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _int, _p], _int),
+    "bsp_mm_fp4_bias": ([_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _int, _p], _int),
+    "bsp_mm_mxfp8_bias": ([_p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _int, _p], _int),
+    "bsp_mm_mxfp4_bias": ([_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _int, _p], _int),
 }
 
 
@@ -251,6 +254,25 @@ def bsp_mm_fp4(a: torch.Tensor, a_sf: torch.Tensor, b: torch.Tensor, b_sf: torch
     return out
 
 
+def _bias_vector(bias: torch.Tensor, n: int, dtype: torch.dtype, dev) -> None:
+    _need(bias, "bias", dtype, dev)
+    if bias.dim() != 1 or bias.numel() != n or not bias.is_contiguous():
+        raise ValueError(f"bias must be a contiguous vector of N = {n} elements")
+
+
+def bsp_mm_fp4_bias(a: torch.Tensor, a_sf: torch.Tensor, b: torch.Tensor, b_sf: torch.Tensor,
+                    alpha: torch.Tensor, bias: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16,
+                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """bsp_mm_fp4 with the bf16 bias [N] added to its output in the epilogue (the pages' out + bias)."""
+    m, n, k, code, out = _mm_fp4_args(a, a_sf, b, b_sf, out_dtype, out)
+    _need(alpha, "alpha", torch.float32, a.device)
+    _bias_vector(bias, n, torch.bfloat16, a.device)
+    _call("bsp_mm_fp4_bias", a.data_ptr(), a_sf.data_ptr(), b.data_ptr(), b_sf.data_ptr(),
+          alpha.data_ptr(), bias.data_ptr(), m, n, k, out.data_ptr(), out.stride(0), code,
+          _stream(a.device))
+    return out
+
+
 def bsp_mm_fp4_per_token(a: torch.Tensor, a_sf: torch.Tensor, b: torch.Tensor, b_sf: torch.Tensor,
                          x_gsf_rows: torch.Tensor, w_gsf: torch.Tensor,
                          out_dtype: torch.dtype = torch.bfloat16,
@@ -330,10 +352,7 @@ def bsp_mxfp8_quantize(x: torch.Tensor, q: Optional[torch.Tensor] = None,
     return q, sf
 
 
-def bsp_mm_mxfp8(a: torch.Tensor, a_sf: torch.Tensor, b: torch.Tensor, b_sf: torch.Tensor,
-                 out_dtype: torch.dtype = torch.bfloat16,
-                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """C [M, N] = A . B^T for MXFP8 a [M, K] / a_sf [M, K/32] and b [N, K] / b_sf [N, K/32]."""
+def _mm_mxfp8_args(a, a_sf, b, b_sf, out_dtype, out):
     _need(a, "a", torch.uint8)
     dev = a.device
     for t, nm in ((a_sf, "a_sf"), (b, "b"), (b_sf, "b_sf")):
@@ -351,8 +370,29 @@ def bsp_mm_mxfp8(a: torch.Tensor, a_sf: torch.Tensor, b: torch.Tensor, b_sf: tor
     if out is None:
         out = torch.empty((m, n), dtype=out_dtype, device=dev)
     _need(out, "out", out_dtype, dev)
+    if out.dim() != 2 or out.shape[0] != m or out.shape[1] != n or out.stride(1) != 1:
+        raise ValueError(f"out must be [{m}, {n}] with unit column stride")
+    return m, n, k, code, out
+
+
+def bsp_mm_mxfp8(a: torch.Tensor, a_sf: torch.Tensor, b: torch.Tensor, b_sf: torch.Tensor,
+                 out_dtype: torch.dtype = torch.bfloat16,
+                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C [M, N] = A . B^T for MXFP8 a [M, K] / a_sf [M, K/32] and b [N, K] / b_sf [N, K/32]."""
+    m, n, k, code, out = _mm_mxfp8_args(a, a_sf, b, b_sf, out_dtype, out)
     _call("bsp_mm_mxfp8", a.data_ptr(), a_sf.data_ptr(), b.data_ptr(), b_sf.data_ptr(), m, n, k,
-          out.data_ptr(), out.stride(0), code, _stream(dev))
+          out.data_ptr(), out.stride(0), code, _stream(a.device))
+    return out
+
+
+def bsp_mm_mxfp8_bias(a: torch.Tensor, a_sf: torch.Tensor, b: torch.Tensor, b_sf: torch.Tensor,
+                      bias: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16,
+                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """bsp_mm_mxfp8 with the fp32 bias [N] added to the fp32 product before its rounding."""
+    m, n, k, code, out = _mm_mxfp8_args(a, a_sf, b, b_sf, out_dtype, out)
+    _bias_vector(bias, n, torch.float32, a.device)
+    _call("bsp_mm_mxfp8_bias", a.data_ptr(), a_sf.data_ptr(), b.data_ptr(), b_sf.data_ptr(),
+          bias.data_ptr(), m, n, k, out.data_ptr(), out.stride(0), code, _stream(a.device))
     return out
 
 
@@ -390,10 +430,7 @@ def bsp_mxfp4_quantize(x: torch.Tensor, packed: Optional[torch.Tensor] = None,
     return packed, sf
 
 
-def bsp_mm_mxfp4(a: torch.Tensor, a_sf: torch.Tensor, b: torch.Tensor, b_sf: torch.Tensor,
-                 alpha: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.bfloat16,
-                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """C [M, N] = alpha * A . B^T for MXFP4 a [M, K/2] and weight b [N, K/2] (128x4 scales)."""
+def _mm_mxfp4_args(a, a_sf, b, b_sf, alpha, out_dtype, out):
     _need(a, "a", torch.uint8)
     dev = a.device
     for t, nm in ((a_sf, "a_sf"), (b, "b"), (b_sf, "b_sf")):
@@ -415,8 +452,29 @@ def bsp_mm_mxfp4(a: torch.Tensor, a_sf: torch.Tensor, b: torch.Tensor, b_sf: tor
         raise ValueError(f"out must be [{m}, {n}] with unit column stride")
     if a_sf.numel() < bsp_mxfp4_sf_bytes(m, k) or b_sf.numel() < bsp_mxfp4_sf_bytes(n, k):
         raise ValueError("scale buffers are smaller than bsp_mxfp4_sf_bytes")
+    return m, n, k, code, out
+
+
+def bsp_mm_mxfp4(a: torch.Tensor, a_sf: torch.Tensor, b: torch.Tensor, b_sf: torch.Tensor,
+                 alpha: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.bfloat16,
+                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C [M, N] = alpha * A . B^T for MXFP4 a [M, K/2] and weight b [N, K/2] (128x4 scales)."""
+    m, n, k, code, out = _mm_mxfp4_args(a, a_sf, b, b_sf, alpha, out_dtype, out)
     _call("bsp_mm_mxfp4", a.data_ptr(), a_sf.data_ptr(), b.data_ptr(), b_sf.data_ptr(),
-          _ptr(alpha), m, n, k, out.data_ptr(), out.stride(0), code, _stream(dev))
+          _ptr(alpha), m, n, k, out.data_ptr(), out.stride(0), code, _stream(a.device))
+    return out
+
+
+def bsp_mm_mxfp4_bias(a: torch.Tensor, a_sf: torch.Tensor, b: torch.Tensor, b_sf: torch.Tensor,
+                      bias: torch.Tensor, alpha: Optional[torch.Tensor] = None,
+                      out_dtype: torch.dtype = torch.bfloat16,
+                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """bsp_mm_mxfp4 with the bf16 bias [N] added to its output (as bsp_mm_fp4_bias)."""
+    m, n, k, code, out = _mm_mxfp4_args(a, a_sf, b, b_sf, alpha, out_dtype, out)
+    _bias_vector(bias, n, torch.bfloat16, a.device)
+    _call("bsp_mm_mxfp4_bias", a.data_ptr(), a_sf.data_ptr(), b.data_ptr(), b_sf.data_ptr(),
+          _ptr(alpha), bias.data_ptr(), m, n, k, out.data_ptr(), out.stride(0), code,
+          _stream(a.device))
     return out
 
 

@@ -251,12 +251,12 @@ __device__ __forceinline__ f16x8 frag_deq(const Frags& f, int q, int j) {
 // ROWSCALE: per-token activation scales; alpha_ptr is then the [M] array of row encode scales
 // and w_gsf_ptr the weight's encode scale, alpha_m = fl32(1 / fl32(x_gsf[m] * w_gsf)).
 // SFA8: A's scales are in layout_8x4 with rows8 (= ceil(M/8)*8) rows.
-template <bool OUT_F32, bool ROWSCALE, bool SFA8>
+template <bool OUT_F32, bool ROWSCALE, bool SFA8, int BIAS>
 __global__ __launch_bounds__(256, 1) void mm_fp4_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ SB, const float* __restrict__ alpha_ptr,
     const float* __restrict__ w_gsf_ptr, int64_t M, int64_t N, int64_t K, void* __restrict__ out,
-    int64_t ldc, int ntm, int ntn, bool vec_store, int64_t rows8) {
+    int64_t ldc, int ntm, int ntn, bool vec_store, int64_t rows8, const void* __restrict__ bias) {
   __shared__ Stage st[NSTAGE];
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
@@ -390,35 +390,41 @@ __global__ __launch_bounds__(256, 1) void mm_fp4_kernel(
 #pragma unroll
     for (int m = 0; m < 4; ++m) alpha[m] = a;
   }
-  store_wave_tile<OUT_F32>(acc, alpha, m0 + wm * 128, n0 + wn * 128, M, N, out, ldc, vec_store, li, h);
+  store_wave_tile<OUT_F32, BIAS>(acc, alpha, m0 + wm * 128, n0 + wn * 128, M, N, out, ldc, vec_store,
+                                 li, h, bias);
 }
 
 }  // namespace fp4
 
-template <bool ROWSCALE, bool SFA8>
+template <bool ROWSCALE, bool SFA8, int BIAS = kBiasNone>
 static void launch_mm_fp4_t(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
                             const float* alpha, const float* w_gsf, int64_t M, int64_t N, int64_t K,
-                            void* out, int64_t ldc, int out_dtype, hipStream_t s) {
+                            void* out, int64_t ldc, int out_dtype, hipStream_t s,
+                            const void* bias = nullptr) {
   const int64_t ntm = ceil_div(M, fp4::BM), ntn = ceil_div(N, fp4::BN);
   const int64_t tiles = ntm * ntn;
   const size_t esz = out_dtype == BSP_OUT_F32 ? 4 : 2;
   const bool vec = (ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(out) & (4 * esz - 1)) == 0);
   const int64_t rows8 = ceil_div(M, 8) * 8;
   if (out_dtype == BSP_OUT_F32)
-    hipLaunchKernelGGL((fp4::mm_fp4_kernel<true, ROWSCALE, SFA8>), dim3((unsigned)tiles), dim3(256), 0,
-                       s, a, sa, b, sb, alpha, w_gsf, M, N, K, out, ldc, (int)ntm, (int)ntn, vec, rows8);
+    hipLaunchKernelGGL((fp4::mm_fp4_kernel<true, ROWSCALE, SFA8, BIAS>), dim3((unsigned)tiles), dim3(256),
+                       0, s, a, sa, b, sb, alpha, w_gsf, M, N, K, out, ldc, (int)ntm, (int)ntn, vec,
+                       rows8, bias);
   else
-    hipLaunchKernelGGL((fp4::mm_fp4_kernel<false, ROWSCALE, SFA8>), dim3((unsigned)tiles), dim3(256), 0,
-                       s, a, sa, b, sb, alpha, w_gsf, M, N, K, out, ldc, (int)ntm, (int)ntn, vec, rows8);
+    hipLaunchKernelGGL((fp4::mm_fp4_kernel<false, ROWSCALE, SFA8, BIAS>), dim3((unsigned)tiles), dim3(256),
+                       0, s, a, sa, b, sb, alpha, w_gsf, M, N, K, out, ldc, (int)ntm, (int)ntn, vec,
+                       rows8, bias);
 }
 
 }  // namespace bsp
 
 using namespace bsp;
 
+// bias_align: 0 for the entry points without a bias, else the bias element size (its alignment)
 static int mm_fp4_checks(const char* fn, const uint8_t* a_packed, const uint8_t* a_sf,
                          const uint8_t* b_packed, const uint8_t* b_sf, const float* alpha_dev,
-                         int64_t M, int64_t N, int64_t K, void* out, int64_t ldc, int out_dtype) {
+                         int64_t M, int64_t N, int64_t K, void* out, int64_t ldc, int out_dtype,
+                         const void* bias = nullptr, unsigned bias_align = 0) {
   BSP_REQUIRE(M >= 0 && N >= 0 && K > 0, BSP_EINVAL, "%s: bad size M=%lld N=%lld K=%lld", fn,
               (long long)M, (long long)N, (long long)K);
   BSP_REQUIRE(out_dtype == BSP_OUT_BF16 || out_dtype == BSP_OUT_F32, BSP_EDTYPE,
@@ -434,6 +440,8 @@ static int mm_fp4_checks(const char* fn, const uint8_t* a_packed, const uint8_t*
                 reinterpret_cast<uintptr_t>(a_sf) | reinterpret_cast<uintptr_t>(b_sf)) & 15u) == 0,
               BSP_EINVAL, "%s: operand and scale buffers must be 16-byte aligned", fn);
   BSP_REQUIRE(ceil_div(M, 256) * ceil_div(N, 256) < (1ll << 31), BSP_ESHAPE, "%s: too many tiles", fn);
+  BSP_REQUIRE(bias_align == 0 || (bias && (reinterpret_cast<uintptr_t>(bias) & (bias_align - 1)) == 0),
+              BSP_EINVAL, "%s: bias must be a non-null device pointer aligned to its element size", fn);
   if (int e = check_device()) return e;
   return 0;
 }
@@ -447,6 +455,18 @@ extern "C" int bsp_mm_fp4(const uint8_t* a_packed, const uint8_t* a_sf, const ui
   launch_mm_fp4_t<false, false>(a_packed, a_sf, b_packed, b_sf, alpha_dev, nullptr, M, N, K, out, ldc,
                                 out_dtype, (hipStream_t)stream);
   return check_launch("bsp_mm_fp4");
+}
+
+extern "C" int bsp_mm_fp4_bias(const uint8_t* a_packed, const uint8_t* a_sf, const uint8_t* b_packed,
+                               const uint8_t* b_sf, const float* alpha_dev, const void* bias_bf16,
+                               int64_t M, int64_t N, int64_t K, void* out, int64_t ldc, int out_dtype,
+                               void* stream) {
+  int e = mm_fp4_checks("bsp_mm_fp4_bias", a_packed, a_sf, b_packed, b_sf, alpha_dev, M, N, K, out, ldc,
+                        out_dtype, bias_bf16, 2);
+  if (e) return e > 0 ? BSP_OK : e;
+  launch_mm_fp4_t<false, false, kBiasBf16After>(a_packed, a_sf, b_packed, b_sf, alpha_dev, nullptr, M, N,
+                                                K, out, ldc, out_dtype, (hipStream_t)stream, bias_bf16);
+  return check_launch("bsp_mm_fp4_bias");
 }
 
 extern "C" int bsp_mm_fp4_8x4(const uint8_t* a_packed, const uint8_t* a_sf, const uint8_t* b_packed,

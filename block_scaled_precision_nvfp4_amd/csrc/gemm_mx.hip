@@ -249,11 +249,12 @@ __device__ __forceinline__ void stage_mfma(f32x16 (&acc)[4][4], const Frags<FMT>
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int FMT, bool OUT_F32>
+template <int FMT, bool OUT_F32, int BIAS>
 __global__ __launch_bounds__(256, 1) void mm_mx_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ SB, const float* __restrict__ alpha_ptr, int64_t M, int64_t N,
-    int64_t K, void* __restrict__ out, int64_t ldc, int ntm, int ntn, bool vec_store) {
+    int64_t K, void* __restrict__ out, int64_t ldc, int ntm, int ntn, bool vec_store,
+    const void* __restrict__ bias) {
   using C = Cfg<FMT>;
   __shared__ Stage st[NSTAGE];
   const int t = threadIdx.x;
@@ -303,23 +304,24 @@ __global__ __launch_bounds__(256, 1) void mm_mx_kernel(
   wait_vmcnt<0>();
   const float a = alpha_ptr ? *alpha_ptr : 1.0f;
   const float alpha[4] = {a, a, a, a};
-  store_wave_tile<OUT_F32>(acc, alpha, m0 + wm * 128, n0 + wn * 128, M, N, out, ldc, vec_store, li, h);
+  store_wave_tile<OUT_F32, BIAS>(acc, alpha, m0 + wm * 128, n0 + wn * 128, M, N, out, ldc, vec_store,
+                                 li, h, bias);
 }
 
-template <int FMT>
+template <int FMT, int BIAS = kBiasNone>
 int launch(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
            const float* alpha, int64_t M, int64_t N, int64_t K, void* out, int64_t ldc, int out_dtype,
-           hipStream_t s, const char* name) {
+           hipStream_t s, const char* name, const void* bias = nullptr) {
   const int64_t ntm = ceil_div(M, BM), ntn = ceil_div(N, BN);
   const int64_t tiles = ntm * ntn;
   const size_t esz = out_dtype == BSP_OUT_F32 ? 4 : 2;
   const bool vec = (ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(out) & (4 * esz - 1)) == 0);
   if (out_dtype == BSP_OUT_F32)
-    hipLaunchKernelGGL((mm_mx_kernel<FMT, true>), dim3((unsigned)tiles), dim3(256), 0, s, a, sa, b, sb,
-                       alpha, M, N, K, out, ldc, (int)ntm, (int)ntn, vec);
+    hipLaunchKernelGGL((mm_mx_kernel<FMT, true, BIAS>), dim3((unsigned)tiles), dim3(256), 0, s, a, sa, b,
+                       sb, alpha, M, N, K, out, ldc, (int)ntm, (int)ntn, vec, bias);
   else
-    hipLaunchKernelGGL((mm_mx_kernel<FMT, false>), dim3((unsigned)tiles), dim3(256), 0, s, a, sa, b, sb,
-                       alpha, M, N, K, out, ldc, (int)ntm, (int)ntn, vec);
+    hipLaunchKernelGGL((mm_mx_kernel<FMT, false, BIAS>), dim3((unsigned)tiles), dim3(256), 0, s, a, sa, b,
+                       sb, alpha, M, N, K, out, ldc, (int)ntm, (int)ntn, vec, bias);
   return check_launch(name);
 }
 
@@ -328,9 +330,11 @@ int launch(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t*
 
 using namespace bsp;
 
+// bias_align: 0 for the entry points without a bias, else the bias element size (its alignment)
 static int mx_checks(const char* fn, const uint8_t* a, const uint8_t* a_sf, const uint8_t* b,
                      const uint8_t* b_sf, int64_t M, int64_t N, int64_t K, void* out, int64_t ldc,
-                     int out_dtype, int64_t kmult, int sf_align) {
+                     int out_dtype, int64_t kmult, int sf_align, const void* bias = nullptr,
+                     unsigned bias_align = 0) {
   BSP_REQUIRE(M >= 0 && N >= 0 && K > 0, BSP_EINVAL, "%s: bad size M=%lld N=%lld K=%lld", fn,
               (long long)M, (long long)N, (long long)K);
   BSP_REQUIRE(out_dtype == BSP_OUT_BF16 || out_dtype == BSP_OUT_F32, BSP_EDTYPE,
@@ -344,6 +348,8 @@ static int mx_checks(const char* fn, const uint8_t* a, const uint8_t* a_sf, cons
                   ((reinterpret_cast<uintptr_t>(a_sf) | reinterpret_cast<uintptr_t>(b_sf)) & (sf_align - 1)) == 0,
               BSP_EINVAL, "%s: operands must be 16-byte and scales %d-byte aligned", fn, sf_align);
   BSP_REQUIRE(ceil_div(M, 256) * ceil_div(N, 256) < (1ll << 31), BSP_ESHAPE, "%s: too many tiles", fn);
+  BSP_REQUIRE(bias_align == 0 || (bias && (reinterpret_cast<uintptr_t>(bias) & (bias_align - 1)) == 0),
+              BSP_EINVAL, "%s: bias must be a non-null device pointer aligned to its element size", fn);
   if (int e = check_device()) return e;
   return 0;
 }
@@ -364,4 +370,25 @@ extern "C" int bsp_mm_mxfp4(const uint8_t* a, const uint8_t* a_sf, const uint8_t
   if (e) return e > 0 ? BSP_OK : e;
   return mx::launch<1>(a, a_sf, b, b_sf, alpha_dev, M, N, K, out, ldc, out_dtype, (hipStream_t)stream,
                        "bsp_mm_mxfp4");
+}
+
+extern "C" int bsp_mm_mxfp8_bias(const uint8_t* a, const uint8_t* a_sf, const uint8_t* b,
+                                 const uint8_t* b_sf, const float* bias_f32, int64_t M, int64_t N,
+                                 int64_t K, void* out, int64_t ldc, int out_dtype, void* stream) {
+  int e = mx_checks("bsp_mm_mxfp8_bias", a, a_sf, b, b_sf, M, N, K, out, ldc, out_dtype, 128, 2,
+                    bias_f32, 4);
+  if (e) return e > 0 ? BSP_OK : e;
+  return mx::launch<0, kBiasF32Before>(a, a_sf, b, b_sf, nullptr, M, N, K, out, ldc, out_dtype,
+                                       (hipStream_t)stream, "bsp_mm_mxfp8_bias", bias_f32);
+}
+
+extern "C" int bsp_mm_mxfp4_bias(const uint8_t* a, const uint8_t* a_sf, const uint8_t* b,
+                                 const uint8_t* b_sf, const float* alpha_dev, const void* bias_bf16,
+                                 int64_t M, int64_t N, int64_t K, void* out, int64_t ldc, int out_dtype,
+                                 void* stream) {
+  int e = mx_checks("bsp_mm_mxfp4_bias", a, a_sf, b, b_sf, M, N, K, out, ldc, out_dtype, 128, 16,
+                    bias_bf16, 2);
+  if (e) return e > 0 ? BSP_OK : e;
+  return mx::launch<1, kBiasBf16After>(a, a_sf, b, b_sf, alpha_dev, M, N, K, out, ldc, out_dtype,
+                                       (hipStream_t)stream, "bsp_mm_mxfp4_bias", bias_bf16);
 }

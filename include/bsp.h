@@ -199,6 +199,30 @@ int bsp_mm_fp4_per_token(const uint8_t* a_packed, const uint8_t* a_sf, const uin
 int bsp_nvfp4_quantize_gelu(const void* y_bf16, int64_t M, int64_t K, int64_t ld, const float* gsf_dev,
                             uint8_t* packed, uint8_t* sf, void* stream);
 
+/* a5 fused into the GEMM epilogue -- the linear layer's bias.
+ * bsp_mm_fp4_bias: [FV-NV] NVFP4QuantizeMethod.apply adds the bias to mm_fp4's bf16 output
+ * (out = out + bias, a bf16 add): C[m, n] = bf16(fl32(bf16(alpha * acc)) + fl32(bias[n])), i.e. the
+ * bf16 product of bsp_mm_fp4 plus the bias in fp32, rounded to bf16 again (nearest-even both
+ * times); with out_dtype fp32, C = fl32(alpha * acc) + bias[n]. bias_bf16: device bf16 [N],
+ * 2-byte aligned, not NULL (else BSP_EINVAL). Other arguments, layouts and errors as bsp_mm_fp4. */
+int bsp_mm_fp4_bias(const uint8_t* a_packed, const uint8_t* a_sf, const uint8_t* b_packed,
+                    const uint8_t* b_sf, const float* alpha_dev, const void* bias_bf16, int64_t M,
+                    int64_t N, int64_t K, void* out, int64_t ldc, int out_dtype, void* stream);
+
+/* bsp_mm_mxfp8_bias: [VLO] NPUMxfp8LinearMethod._quant_matmul converts the bias to fp32 and hands it
+ * to the quantized matmul: C[m, n] = round(fl32(acc) + bias[n]) with one rounding to the output
+ * dtype (bf16 nearest-even, or none for fp32). bias_f32: device fp32 [N], 4-byte aligned, not NULL
+ * (else BSP_EINVAL). Other arguments, layouts and errors as bsp_mm_mxfp8. */
+int bsp_mm_mxfp8_bias(const uint8_t* a, const uint8_t* a_sf, const uint8_t* b, const uint8_t* b_sf,
+                      const float* bias_f32, int64_t M, int64_t N, int64_t K, void* out, int64_t ldc,
+                      int out_dtype, void* stream);
+
+/* bsp_mm_mxfp4_bias: the MXFP4 GEMM with the bias added as in bsp_mm_fp4_bias (the same [FV-NV]
+ * apply path, use_nvfp4=False). bias_bf16: device bf16 [N]. Other arguments as bsp_mm_mxfp4. */
+int bsp_mm_mxfp4_bias(const uint8_t* a_packed, const uint8_t* a_sf, const uint8_t* b_packed,
+                      const uint8_t* b_sf, const float* alpha_dev, const void* bias_bf16, int64_t M,
+                      int64_t N, int64_t K, void* out, int64_t ldc, int out_dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

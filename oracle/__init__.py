@@ -17,6 +17,7 @@ from what the pages state the operations compute:
 * vLLM-Omni mxfp8_config.py page: ``DiffusionMXFP8Config`` (32-element groups
   along K sharing one e8m0 scale, per the OCP MX spec) and the online
   BF16 -> MXFP8 weight conversion.
+* The bias each page's linear method adds after the GEMM (``linear``).
 
 Floating-point steps are carried out in IEEE fp32 with numpy float32 arithmetic
 (every operation rounded to nearest even, no fused multiply-add), because the
@@ -29,4 +30,4 @@ values fixed by the format definitions and hand-worked examples
 (``tests/golden/``), closed forms, invariants and brute force; none is
 "parity unpinned" except where a function docstring says so.
 """
-from . import activations, formats, mxfp4, mxfp8, nvfp4  # noqa: F401
+from . import activations, formats, linear, mxfp4, mxfp8, nvfp4  # noqa: F401

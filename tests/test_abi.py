@@ -133,3 +133,17 @@ def test_plain_c_consumer_compiles_links_and_runs(tmp_path):
     assert r.returncode == 0, r.stderr
     r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0 and "c consumer ok" in r.stdout, (r.stdout, r.stderr)
+
+
+def test_bias_entry_point_errors():
+    """Null or misaligned bias pointers are rejected before any launch; M == 0 is a no-op."""
+    st, msg = _st("bsp_mm_fp4_bias", P, P, P, P, P, None, 8, 8, 128, P, 8, 0, None)
+    assert st == -1 and "bias" in msg
+    assert _st("bsp_mm_fp4_bias", P, P, P, P, P, ctypes.c_void_p(17), 8, 8, 128, P, 8, 0, None)[0] == -1
+    assert _st("bsp_mm_fp4_bias", P, P, P, P, P, P, 8, 8, 96, P, 8, 0, None)[0] == -2
+    assert _st("bsp_mm_fp4_bias", None, None, None, None, None, None, 0, 8, 128, None, 8, 0, None)[0] == 0
+    st, msg = _st("bsp_mm_mxfp8_bias", P, P, P, P, ctypes.c_void_p(18), 8, 8, 128, P, 8, 0, None)
+    assert st == -1 and "bias" in msg
+    assert _st("bsp_mm_mxfp8_bias", P, P, P, P, P, 8, 8, 64, P, 8, 0, None)[0] == -2
+    assert _st("bsp_mm_mxfp4_bias", P, P, P, P, P, None, 8, 8, 128, P, 8, 0, None)[0] == -1
+    assert _st("bsp_mm_mxfp4_bias", P, P, P, P, P, P, 8, 8, 128, P, 8, 9, None)[0] == -3

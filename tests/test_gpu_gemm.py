@@ -335,3 +335,104 @@ def test_mm_mxfp4_full_size():
     ref = X4.mm_mxfp4_entries(host_u8(px), host_u8(sx).ravel(), host_u8(pw), host_u8(sw).ravel(), 1.0,
                               m, n, k, rows, cols)
     assert_gemm_bf16(gather(c, rows, cols), ref, "cfg4 fc_in mxfp4")
+
+
+# ------------------------------------------------------------------------------- bias (a5)
+def _ref_plus_bias_bf16(ref, bias_bits):
+    """The pages' result: the oracle's product rounded to bf16, plus the bf16 bias (bf16 add)."""
+    from oracle import linear as L
+    return W.bf16_bits_to_f32(L.add_bias_bf16(A.f64_to_bf16_bits(ref), bias_bits)).astype(np.float64)
+
+
+def _rand_bias(rng, n, scale):
+    """bf16 bits and fp32 values of a bias [N] of about the outputs' size, with some exact zeros."""
+    v = rng.normal(0.0, scale, size=n).astype(np.float32)
+    v[:: 7] = 0.0
+    bits = W.f32_to_bf16_bits(v)
+    return bits, W.bf16_bits_to_f32(bits)
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 64, 64), (77, 200, 192), (256, 256, 512), (300, 130, 128)])
+def test_mm_fp4_bias_random(m, n, k):
+    """bsp_mm_fp4_bias = the bf16 output of bsp_mm_fp4 plus the bf16 bias (bit-exact, the pages'
+    out + bias), and within the GEMM tolerance of the oracle's exact product plus bias."""
+    from oracle import linear as L
+    say("mm_fp4_bias random", m, n, k)
+    rng = np.random.default_rng(m * 11 + n + k)
+    pa, sa = _rand_nvfp4_operand(rng, m, k)
+    pb, sb = _rand_nvfp4_operand(rng, n, k)
+    al = f32(rng.uniform(0.01, 2.0))
+    ref = N.mm_fp4(pa, sa, pb, sb, al, m, n, k)
+    bbits, bf = _rand_bias(rng, n, float(np.std(ref)) + 1e-30)
+    args = (dev_u8(pa), dev_u8(sa), dev_u8(pb), dev_u8(sb), scalar(al))
+    bias = dev_bf16(bbits)
+    t16 = bsp.bsp_mm_fp4(*args)
+    tb16 = bsp.bsp_mm_fp4_bias(*args, bias)
+    assert np.array_equal(host_bits(tb16), L.add_bias_bf16(host_bits(t16), bbits))
+    assert_gemm_bf16(tb16.float().cpu().numpy().astype(np.float64), _ref_plus_bias_bf16(ref, bbits),
+                     f"bias {m}x{n}x{k}")
+    t32 = bsp.bsp_mm_fp4(*args, out_dtype=torch.float32)
+    tb32 = bsp.bsp_mm_fp4_bias(*args, bias, out_dtype=torch.float32)
+    assert np.array_equal(tb32.cpu().numpy(), (t32.cpu().numpy() + bf).astype(np.float32))
+
+
+def test_mm_fp4_bias_full_size_fc_in():
+    """Wan-14B fc_in shape in the bench's launch configuration, with a bias: every element against
+    the no-bias output plus the bias (bf16 add on the device), sampled entries against the oracle."""
+    hb, wb = tensor_bits(4, "X"), tensor_bits(4, "W")
+    pw, sw, gw, _, _ = bsp.bsp_nvfp4_prequantize_weight(dev_bf16(wb))
+    px, sx = bsp.bsp_nvfp4_quantize(dev_bf16(hb), scalar(1.0))
+    alpha = bsp.bsp_nvfp4_alpha(scalar(1.0), gw)
+    m, n, k = hb.shape[0], wb.shape[0], hb.shape[1]
+    rng = np.random.default_rng(404)
+    bbits, bf = _rand_bias(rng, n, 0.5)
+    bias = dev_bf16(bbits)
+    c = bsp.bsp_mm_fp4(px, sx, pw, sw, alpha)
+    cb = bsp.bsp_mm_fp4_bias(px, sx, pw, sw, alpha, bias)
+    assert torch.equal(cb.view(torch.int16), (c.float() + bias.float()).bfloat16().view(torch.int16))
+    rows, cols = sample_entries(m, n, 2000, 404)
+    ref = N.mm_fp4_entries(host_u8(px), host_u8(sx).ravel(), host_u8(pw), host_u8(sw).ravel(),
+                           float(alpha.item()), m, n, k, rows, cols)
+    assert_gemm_bf16(gather(cb, rows, cols), _ref_plus_bias_bf16(ref, bbits[cols]), "cfg4 fc_in + bias")
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 64, 128), (77, 200, 256), (300, 130, 384)])
+def test_mm_mxfp8_bias_random(m, n, k):
+    """bsp_mm_mxfp8_bias: fp32 output = fp32 product + fp32 bias exactly; bf16 output = its one
+    nearest-even rounding; within tolerance of the oracle's exact product plus bias."""
+    from oracle import linear as L
+    say("mm_mxfp8_bias random", m, n, k)
+    rng = np.random.default_rng(m + 3 * n + k)
+    qa, sa = _rand_mx_operand(rng, m, k)
+    qb, sb = _rand_mx_operand(rng, n, k)
+    ref = X.mm_mxfp8(qa, sa, qb, sb, m, n, k)
+    bf = rng.normal(0.0, float(np.std(ref)) + 1e-30, size=n).astype(np.float32)
+    bias = torch.from_numpy(bf).cuda()
+    args = (dev_u8(qa), dev_u8(sa), dev_u8(qb), dev_u8(sb))
+    t32 = bsp.bsp_mm_mxfp8(*args, out_dtype=torch.float32)
+    tb32 = bsp.bsp_mm_mxfp8_bias(*args, bias, out_dtype=torch.float32)
+    assert np.array_equal(tb32.cpu().numpy(), (t32.cpu().numpy() + bf).astype(np.float32))
+    tb16 = bsp.bsp_mm_mxfp8_bias(*args, bias)
+    _assert_bf16_is_rne_of_f32(tb16, tb32)
+    assert_gemm_bf16(tb16.float().cpu().numpy().astype(np.float64), L.gemm_plus_bias(ref, bf),
+                     f"mxfp8 bias {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("m,n,k", [(77, 200, 256), (256, 256, 512)])
+def test_mm_mxfp4_bias_random(m, n, k):
+    from oracle import linear as L
+    from oracle import mxfp4 as X4
+    say("mm_mxfp4_bias random", m, n, k)
+    rng = np.random.default_rng(m * 3 + n + k)
+    pa, sa = _rand_mxfp4_operand(rng, m, k)
+    pb, sb = _rand_mxfp4_operand(rng, n, k)
+    al = f32(0.375)
+    ref = X4.mm_mxfp4(pa, sa, pb, sb, al, m, n, k)
+    bbits, bf = _rand_bias(rng, n, float(np.std(ref)) + 1e-30)
+    args = (dev_u8(pa), dev_u8(sa), dev_u8(pb), dev_u8(sb))
+    bias = dev_bf16(bbits)
+    t16 = bsp.bsp_mm_mxfp4(*args, scalar(al))
+    tb16 = bsp.bsp_mm_mxfp4_bias(*args, bias, scalar(al))
+    assert np.array_equal(host_bits(tb16), L.add_bias_bf16(host_bits(t16), bbits))
+    assert_gemm_bf16(tb16.float().cpu().numpy().astype(np.float64), _ref_plus_bias_bf16(ref, bbits),
+                     f"mxfp4 bias {m}x{n}x{k}")
