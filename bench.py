@@ -355,6 +355,36 @@ def main():
             "quantize_frac_hbm": round(qb4 / q4 / 1e6 / PEAK_HBM_GBS, 4)}
         log(json.dumps(result["mxfp4"]))
 
+    # ---- PyTorch's own memory-bound kernels on the same GPU, for context beside the published
+    # 8 TB/s: a 2 GiB device-to-device copy (read:write 1:1) and a 2 GiB fp32 sum (read only), timed
+    # with events on torch's stream. They are reference rates, not ceilings: the quantizers
+    # (read:write about 3.6:1) run faster than both.
+    nb = 1 << 31
+    src = torch.empty(nb, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    red = src.view(torch.float32)
+
+    def timed(fn, reps=10):
+        for _ in range(2):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    copy_gbs = 2.0 * nb / timed(lambda: dst.copy_(src)) / 1e6
+    read_gbs = 1.0 * nb / timed(lambda: red.sum()) / 1e6
+    del src, dst, red
+    result["torch_hbm_rates"] = {
+        "copy_GBs": round(copy_gbs, 1), "sum_GBs": round(read_gbs, 1),
+        "quantize_x_over_copy": round(kernels["quantize_x"]["GB/s"] / copy_gbs, 4),
+        "quantize_h_over_copy": round(kernels["quantize_h"]["GB/s"] / copy_gbs, 4)}
+    log(json.dumps(result["torch_hbm_rates"]))
+
     # ---- CPU oracle on a bounded sample of the same workload
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_rows)
