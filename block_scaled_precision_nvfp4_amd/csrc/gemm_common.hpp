@@ -45,14 +45,11 @@ enum { kBiasNone = 0, kBiasBf16After = 1, kBiasF32Before = 2 };
 // MFMA's A operand is the B (weight) fragment): a lane holds output column gm = m0w + 32m + (lane%32)
 // (a row of C) and, per group b, the four consecutive C columns n0w + 32n + 8b + 4*(lane/32) + 0..3.
 // alpha[m] multiplies the lane's row of sub-tile m (the same value four times for a tensor alpha).
-template <bool OUT_F32, int BIAS = kBiasNone>
-__device__ __forceinline__ void store_wave_tile(const f32x16 (&acc)[4][4], const float (&alpha)[4],
-                                                int64_t m0w, int64_t n0w, int64_t M, int64_t N,
-                                                void* out, int64_t ldc, bool vec_store, int li, int h,
-                                                const void* bias = nullptr) {
-  constexpr int bias_kind = BIAS;
-  // the lane's 64 bias values (they depend on the column only), zero past N
-  float bq[4][4][4];
+
+// The lane's 64 bias values (they depend on the column only), zero past N.
+template <int BIAS>
+__device__ __forceinline__ void load_bias(float (&bq)[4][4][4], int64_t n0w, int64_t N, int h,
+                                          const void* bias) {
 #pragma unroll
   for (int n = 0; n < 4; ++n)
 #pragma unroll
@@ -61,12 +58,55 @@ __device__ __forceinline__ void store_wave_tile(const f32x16 (&acc)[4][4], const
       for (int i = 0; i < 4; ++i) {
         const int64_t gn = n0w + n * 32 + 8 * b + 4 * h + i;
         float v = 0.0f;
-        if (bias_kind == kBiasBf16After && gn < N)
+        if (BIAS == kBiasBf16After && gn < N)
           v = __builtin_bit_cast(float, (uint32_t)static_cast<const uint16_t*>(bias)[gn] << 16);
-        else if (bias_kind == kBiasF32Before && gn < N)
+        else if (BIAS == kBiasF32Before && gn < N)
           v = static_cast<const float*>(bias)[gn];
         bq[n][b][i] = v;
       }
+}
+
+// The four fp32 results of piece (m, n, b), bias of kind kBiasF32Before (or any kind for fp32
+// output) included.
+template <bool OUT_F32, int BIAS>
+__device__ __forceinline__ void piece_f32(const f32x16 (&acc)[4][4], const float (&alpha)[4],
+                                          const float (&bq)[4][4][4], int m, int n, int b,
+                                          float (&v)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[i] = alpha[m] * acc[n][m][4 * b + i];
+    if (BIAS != kBiasNone && (OUT_F32 || BIAS == kBiasF32Before)) v[i] += bq[n][b][i];
+  }
+}
+
+// The four bf16 results of piece (m, n, b) as two packed pairs (nearest even; a kBiasBf16After
+// bias is added to the rounded product and the sum rounded again).
+template <int BIAS>
+__device__ __forceinline__ void piece_bf16(const f32x16 (&acc)[4][4], const float (&alpha)[4],
+                                           const float (&bq)[4][4][4], int m, int n, int b,
+                                           uint32_t& p01, uint32_t& p23) {
+  float v[4];
+  piece_f32<false, BIAS>(acc, alpha, bq, m, n, b, v);
+  p01 = bf16x2_rne(v[0], v[1]);
+  p23 = bf16x2_rne(v[2], v[3]);
+  if (BIAS == kBiasBf16After) {
+    const float t0 = __builtin_bit_cast(float, p01 << 16) + bq[n][b][0];
+    const float t1 = __builtin_bit_cast(float, p01 & 0xFFFF0000u) + bq[n][b][1];
+    const float t2 = __builtin_bit_cast(float, p23 << 16) + bq[n][b][2];
+    const float t3 = __builtin_bit_cast(float, p23 & 0xFFFF0000u) + bq[n][b][3];
+    p01 = bf16x2_rne(t0, t1);
+    p23 = bf16x2_rne(t2, t3);
+  }
+}
+
+// Direct epilogue: each lane stores its 8-byte (bf16) or 16-byte (fp32) pieces, with bounds checks.
+template <bool OUT_F32, int BIAS = kBiasNone>
+__device__ __forceinline__ void store_wave_tile(const f32x16 (&acc)[4][4], const float (&alpha)[4],
+                                                int64_t m0w, int64_t n0w, int64_t M, int64_t N,
+                                                void* out, int64_t ldc, bool vec_store, int li, int h,
+                                                const void* bias = nullptr) {
+  float bq[4][4][4];
+  load_bias<BIAS>(bq, n0w, N, h, bias);
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     const int64_t gm = m0w + m * 32 + li;
@@ -76,34 +116,22 @@ __device__ __forceinline__ void store_wave_tile(const f32x16 (&acc)[4][4], const
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const int64_t gn = n0w + n * 32 + 8 * b + 4 * h;
-        float v0 = alpha[m] * acc[n][m][4 * b + 0];
-        float v1 = alpha[m] * acc[n][m][4 * b + 1];
-        float v2 = alpha[m] * acc[n][m][4 * b + 2];
-        float v3 = alpha[m] * acc[n][m][4 * b + 3];
-        if (bias_kind != kBiasNone && (OUT_F32 || bias_kind == kBiasF32Before)) {
-          v0 += bq[n][b][0]; v1 += bq[n][b][1]; v2 += bq[n][b][2]; v3 += bq[n][b][3];
-        }
         if (OUT_F32) {
+          float v[4];
+          piece_f32<true, BIAS>(acc, alpha, bq, m, n, b, v);
           float* o = static_cast<float*>(out) + gm * ldc + gn;
           if (vec_store && gn + 3 < N) {
-            *reinterpret_cast<float4*>(o) = make_float4(v0, v1, v2, v3);
+            *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
           } else {
-            if (gn + 0 < N) o[0] = v0;
-            if (gn + 1 < N) o[1] = v1;
-            if (gn + 2 < N) o[2] = v2;
-            if (gn + 3 < N) o[3] = v3;
+            if (gn + 0 < N) o[0] = v[0];
+            if (gn + 1 < N) o[1] = v[1];
+            if (gn + 2 < N) o[2] = v[2];
+            if (gn + 3 < N) o[3] = v[3];
           }
         } else {
+          uint32_t p01, p23;
+          piece_bf16<BIAS>(acc, alpha, bq, m, n, b, p01, p23);
           uint16_t* o = static_cast<uint16_t*>(out) + gm * ldc + gn;
-          uint32_t p01 = bf16x2_rne(v0, v1), p23 = bf16x2_rne(v2, v3);
-          if (bias_kind == kBiasBf16After) {
-            const float t0 = __builtin_bit_cast(float, p01 << 16) + bq[n][b][0];
-            const float t1 = __builtin_bit_cast(float, p01 & 0xFFFF0000u) + bq[n][b][1];
-            const float t2 = __builtin_bit_cast(float, p23 << 16) + bq[n][b][2];
-            const float t3 = __builtin_bit_cast(float, p23 & 0xFFFF0000u) + bq[n][b][3];
-            p01 = bf16x2_rne(t0, t1);
-            p23 = bf16x2_rne(t2, t3);
-          }
           if (vec_store && gn + 3 < N) {
             *reinterpret_cast<uint2*>(o) = make_uint2(p01, p23);
           } else {
@@ -115,6 +143,70 @@ __device__ __forceinline__ void store_wave_tile(const f32x16 (&acc)[4][4], const
         }
       }
     }
+  }
+}
+
+// Staged epilogue for a bf16 wave tile that lies wholly inside C (rows 16-byte aligned): the
+// 8-byte pieces go to a row-major image of 64 rows at a time in this wave's LDS area
+// (kEpiWaveBytes), and come back as 16-byte row segments, so each store instruction writes four
+// whole 256-byte rows instead of 32 rows x 16 bytes; the rows are not read again by this
+// computation, so the stores are nontemporal. Image rows are 272 bytes apart: 16-byte aligned
+// reads, and a 64-bit write of lanes li and li + 16 shares banks at most pairwise.
+constexpr int kEpiRowBytes = 272;
+constexpr int kEpiWaveBytes = 64 * kEpiRowBytes;
+
+template <int BIAS = kBiasNone>
+__device__ __forceinline__ void store_wave_tile_staged(const f32x16 (&acc)[4][4],
+                                                       const float (&alpha)[4], int64_t m0w,
+                                                       int64_t n0w, int64_t N, void* out,
+                                                       int64_t ldc, uint8_t* lds, int lane, int li,
+                                                       int h, const void* bias = nullptr) {
+  float bq[4][4][4];
+  load_bias<BIAS>(bq, n0w, N, h, bias);
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm) {
+#pragma unroll
+      for (int n = 0; n < 4; ++n)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          uint32_t p01, p23;
+          piece_bf16<BIAS>(acc, alpha, bq, 2 * half + mm, n, b, p01, p23);
+          *reinterpret_cast<uint2*>(lds + (mm * 32 + li) * kEpiRowBytes + (n * 32 + 8 * b + 4 * h) * 2) =
+              make_uint2(p01, p23);
+        }
+    }
+    // the same wave reads back what it wrote: LDS executes one wave's operations in order
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int row = it * 4 + (lane >> 4), c16 = lane & 15;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(lds + row * kEpiRowBytes + c16 * 16);
+      uint16_t* o = static_cast<uint16_t*>(out) + (m0w + half * 64 + row) * ldc + n0w + c16 * 8;
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(o));
+    }
+  }
+}
+
+// The workgroup's epilogue (4 waves, 2x2 wave tiles of a 256x256 C tile). `lds` is the
+// workgroup's stage memory, at least 4 * kEpiWaveBytes bytes, which no wave reads or loads into
+// any more (every global -> LDS load has completed). The choice of path is uniform across the
+// workgroup, so the barrier is reached by all waves or none.
+template <bool OUT_F32, int BIAS = kBiasNone>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], const float (&alpha)[4],
+                                           int64_t m0, int64_t n0, int wm, int wn, int64_t M,
+                                           int64_t N, void* out, int64_t ldc, bool vec_store,
+                                           uint8_t* lds, int wave, int lane, int li, int h,
+                                           const void* bias = nullptr) {
+  const bool whole = !OUT_F32 && m0 + 256 <= M && n0 + 256 <= N && ldc % 8 == 0 &&
+                     (reinterpret_cast<uintptr_t>(out) & 15) == 0;
+  if (whole) {
+    __syncthreads();   // every wave is done reading the stage buffers the images overlay
+    store_wave_tile_staged<BIAS>(acc, alpha, m0 + wm * 128, n0 + wn * 128, N, out, ldc,
+                                 lds + wave * kEpiWaveBytes, lane, li, h, bias);
+  } else {
+    store_wave_tile<OUT_F32, BIAS>(acc, alpha, m0 + wm * 128, n0 + wn * 128, M, N, out, ldc,
+                                   vec_store, li, h, bias);
   }
 }
 

@@ -390,8 +390,9 @@ __global__ __launch_bounds__(256, 1) void mm_fp4_kernel(
 #pragma unroll
     for (int m = 0; m < 4; ++m) alpha[m] = a;
   }
-  store_wave_tile<OUT_F32, BIAS>(acc, alpha, m0 + wm * 128, n0 + wn * 128, M, N, out, ldc, vec_store,
-                                 li, h, bias);
+  static_assert(sizeof(st) >= 4 * kEpiWaveBytes, "epilogue images overlay the stage buffers");
+  store_tile<OUT_F32, BIAS>(acc, alpha, m0, n0, wm, wn, M, N, out, ldc, vec_store,
+                            reinterpret_cast<uint8_t*>(st), wave, lane, li, h, bias);
 }
 
 }  // namespace fp4

@@ -436,3 +436,50 @@ def test_mm_mxfp4_bias_random(m, n, k):
     assert np.array_equal(host_bits(tb16), L.add_bias_bf16(host_bits(t16), bbits))
     assert_gemm_bf16(tb16.float().cpu().numpy().astype(np.float64), _ref_plus_bias_bf16(ref, bbits),
                      f"mxfp4 bias {m}x{n}x{k}")
+
+
+# ------------------------------------------------------------------- epilogue paths agree
+def _strided_out(m, n, ldc, dtype):
+    buf = torch.full((m, ldc), float("nan"), dtype=dtype, device="cuda")
+    return buf, buf[:, :n]
+
+
+@pytest.mark.parametrize("kind", ["fp4", "fp4_bias", "mxfp8", "mxfp8_bias", "mxfp4"])
+def test_staged_and_direct_epilogues_agree(kind):
+    """Whole 256x256 tiles with 16-byte aligned output rows leave through the LDS-staged epilogue,
+    others through the direct one: the same product written with row stride N (staged) and with
+    an odd row stride (direct) must be bit-identical, and the padding columns untouched."""
+    say("epilogue paths", kind)
+    m, n, k = 512, 768, 256
+    rng = np.random.default_rng(2024)
+    if kind.startswith("fp4"):
+        pa, sa = _rand_nvfp4_operand(rng, m, k)
+        pb, sb = _rand_nvfp4_operand(rng, n, k)
+        args = (dev_u8(pa), dev_u8(sa), dev_u8(pb), dev_u8(sb), scalar(0.75))
+    elif kind.startswith("mxfp8"):
+        qa, sa = _rand_mx_operand(rng, m, k)
+        qb, sb = _rand_mx_operand(rng, n, k)
+        args = (dev_u8(qa), dev_u8(sa), dev_u8(qb), dev_u8(sb))
+    else:
+        pa, sa = _rand_mxfp4_operand(rng, m, k)
+        pb, sb = _rand_mxfp4_operand(rng, n, k)
+        args = (dev_u8(pa), dev_u8(sa), dev_u8(pb), dev_u8(sb))
+    bias16 = dev_bf16(_rand_bias(rng, n, 4.0)[0])
+    bias32 = torch.from_numpy(rng.normal(0, 4.0, size=n).astype(np.float32)).cuda()
+
+    def run(out):
+        if kind == "fp4":
+            return bsp.bsp_mm_fp4(*args, out=out)
+        if kind == "fp4_bias":
+            return bsp.bsp_mm_fp4_bias(*args, bias16, out=out)
+        if kind == "mxfp8":
+            return bsp.bsp_mm_mxfp8(*args, out=out)
+        if kind == "mxfp8_bias":
+            return bsp.bsp_mm_mxfp8_bias(*args, bias32, out=out)
+        return bsp.bsp_mm_mxfp4(*args, scalar(0.5), out=out)
+
+    staged = run(torch.empty((m, n), dtype=torch.bfloat16, device="cuda"))
+    buf, view = _strided_out(m, n, n + 3, torch.bfloat16)
+    direct = run(view)
+    assert np.array_equal(host_bits(staged), host_bits(direct))
+    assert torch.isnan(buf[:, n:].float()).all()
