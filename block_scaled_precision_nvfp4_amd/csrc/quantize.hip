@@ -107,23 +107,23 @@ constexpr float kSixth = 0.16666667163372040f;  // fl32(1/6) = 0x3E2AAAAB
 
 // gelu(x) = 0.5 x (1 + tanh(z)), z = sqrt(2/pi) (x + 0.044715 x^3), in fp32, rounded once to bf16
 // by the caller. 0.5 (1 + tanh z) is the logistic function of 2z, evaluated with t = 2^(-2|z| log2 e)
-// <= 1 as x / (1 + t) for z >= 0 and x t / (1 + t) for z < 0: no cancellation and no overflow.
-// v_exp_f32 and v_rcp_f32 (about 1 ulp each) keep the whole function at a dozen instructions; the
-// result is within a few fp32 ulps, far inside one bf16 ulp except next to a rounding boundary.
-// Where t would be an fp32 denormal (2|z| log2 e > 64) it is formed as t * 2^64 and the product
-// scaled back by 2^-64 at the end (a single rounding), so tiny negative outputs keep their bits.
+// <= 1 as x / (1 + t) for x >= 0 and x t / (1 + t) for x < 0 (z has the sign of x): no cancellation
+// and no overflow. -2|z| log2 e = |x| (c0 + c2 x^2) with c0 = -2 log2(e) sqrt(2/pi) and
+// c2 = 0.044715 c0, one fused multiply-add. t is always formed as 2^64 t = 2^(that + 64) (the
+// exponent is at most 64, so no overflow) and negative outputs are scaled back by 2^-64 at the end,
+// so tiny negative outputs keep their bits down to where bf16 underflows too. v_exp_f32 and
+// v_rcp_f32 (about 1 ulp each) keep the whole function at a dozen instructions; the result is
+// within a few fp32 ulps, far inside one bf16 ulp except next to a rounding boundary.
 __device__ __forceinline__ float gelu_tanh(float x) {
-  const float k0 = 0.7978845608028654f;   // sqrt(2/pi)
-  const float k1 = 0.044715f;
-  const float k2 = -2.8853900817779268f;  // -2 log2(e)
-  const float z = k0 * (x + k1 * (x * x * x));
-  const float e = k2 * __builtin_fabsf(z);
-  const bool tiny = e < -64.0f;
-  const float ts = __builtin_amdgcn_exp2f(tiny ? e + 64.0f : e);  // t, or t * 2^64 when tiny
-  const float r = __builtin_amdgcn_rcpf(1.0f + (tiny ? 0.0f : ts));
-  const bool neg = z < 0.0f;                                  // branch-free: selects, no exec masks
+  const float c0 = -2.302208198144325f;    // -2 log2(e) sqrt(2/pi)
+  const float c2 = -0.1029432395800235f;   // 0.044715 c0
+  const float x2 = x * x;
+  const float p64 = __builtin_fmaf(__builtin_fmaf(c2, x2, c0), __builtin_fabsf(x), 64.0f);
+  const float ts = __builtin_amdgcn_exp2f(p64);                       // t * 2^64
+  const float r = __builtin_amdgcn_rcpf(__builtin_fmaf(ts, 5.421010862427522e-20f, 1.0f));  // 1/(1+t)
+  const bool neg = x < 0.0f;                                  // branch-free: selects, no exec masks
   const float m = neg ? ts : 1.0f;
-  const float sc = (neg && tiny) ? 5.421010862427522e-20f : 1.0f;  // 2^-64
+  const float sc = neg ? 5.421010862427522e-20f : 1.0f;       // 2^-64
   return ((x * m) * r) * sc;
 }
 
