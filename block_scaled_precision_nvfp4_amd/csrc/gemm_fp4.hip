@@ -368,6 +368,13 @@ __global__ __launch_bounds__(256, 1) void mm_fp4_kernel(
           if (q - 1 < 4) xa[nb][q - 1] = v; else xb[nb][q - 5] = v;
         }
         if (q == 7) r7 = rq; else rprev = rq;
+        // issue order inside the group: one MFMA, six VALU instructions, the other MFMA, the rest,
+        // so each MFMA's 32 cycles cover about half of the group's dequantization (the compiler's
+        // own order front-loads the VALU work after the first MFMA)
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
