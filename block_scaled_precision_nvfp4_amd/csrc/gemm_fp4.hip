@@ -26,12 +26,13 @@
 // K [64h, 64h + 64): 8 MFMA sub-steps of K 16, sub-step j using its elements 64h + 8j .. + 7
 // (both operands use the same K placement, so the MFMA pairs them correctly) with scale byte j/2
 // of the row's scale dword for column group h. Dequantization of sub-step j+1 is interleaved
-// between the MFMA pairs of sub-step j (explicit scheduling fences), so the VALU work issues while
-// the matrix core is busy instead of in bursts that in-order issue would serialize.
+// between the MFMA pairs of sub-step j (explicit scheduling fences, and inside each pair a pinned
+// order: MFMA, six VALU instructions, MFMA, the rest), so the VALU work issues while the matrix
+// core is busy instead of in bursts that in-order issue would serialize.
 //
 // The MFMA's A operand is the weight fragment and its B operand the activation fragment, so a
-// lane's accumulators hold four consecutive output columns of one output row per group (8-byte
-// bf16 stores).
+// lane's accumulators hold four consecutive output columns of one output row per group. A tile
+// wholly inside C leaves through LDS as whole 256-byte rows (store_tile in gemm_common.hpp).
 #include "gemm_common.hpp"
 
 namespace bsp {

@@ -21,7 +21,8 @@
 // MFMA pair during stage kt rather than in a burst. Fragments of the next stage are read into a
 // second register set behind a barrier placed 768 MFMA cycles before the stage ends; their scale
 // dwords are shifted for the lane half only when that stage starts, so nothing waits on the LDS
-// reads while the current stage's MFMAs are still to be issued.
+// reads while the current stage's MFMAs are still to be issued. The epilogue is shared with mm_fp4
+// (store_tile in gemm_common.hpp: whole tiles leave through LDS as whole rows).
 #include "gemm_common.hpp"
 
 namespace bsp {
