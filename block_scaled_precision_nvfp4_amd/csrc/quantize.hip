@@ -693,6 +693,12 @@ extern "C" int bsp_nvfp4_prequantize_weight(const void* w, int64_t N, int64_t K,
               (long long)K);
   BSP_REQUIRE(w && packed && sf && gsf && inv_gsf && amax, BSP_EINVAL,
               "bsp_nvfp4_prequantize_weight: null pointer");
+  // everything the quantize step checks, before the global-scale step launches anything
+  BSP_REQUIRE(N <= 1 || ld >= K, BSP_ESHAPE, "bsp_nvfp4_prequantize_weight: ld (%lld) < K (%lld)",
+              (long long)ld, (long long)K);
+  BSP_REQUIRE((reinterpret_cast<uintptr_t>(packed) & 3u) == 0 && (reinterpret_cast<uintptr_t>(sf) & 15u) == 0,
+              BSP_EINVAL, "bsp_nvfp4_prequantize_weight: packed must be 4-byte and sf 16-byte aligned");
+  BSP_REQUIRE(ceil_div(N, 128) < 65536, BSP_ESHAPE, "bsp_nvfp4_prequantize_weight: N too large");
   int e = bsp_nvfp4_global_sf(w, N, K, ld, gsf, inv_gsf, amax, stream);
   if (e) return e;
   return bsp_nvfp4_quantize(w, N, K, ld, gsf, packed, sf, stream);

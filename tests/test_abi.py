@@ -82,6 +82,11 @@ def test_prequantize_and_alpha_null_checks():
     assert _st("bsp_nvfp4_alpha", None, P, P, None)[0] == -1
     assert _st("bsp_nvfp4_global_sf", P, 2, 8, 8, None, P, P, None)[0] == -1
     assert _st("bsp_gelu_tanh_bf16", P, P, -1, None)[0] == -1
+    # prequantization checks the quantize step's arguments before launching its global-scale step
+    st, msg = _st("bsp_nvfp4_prequantize_weight", P, 8, 64, 64, ctypes.c_void_p(18), P, P, P, P, None)
+    assert st == -1 and "aligned" in msg
+    st, msg = _st("bsp_nvfp4_prequantize_weight", P, 8, 64, 32, P, P, P, P, P, None)
+    assert st == -2 and "ld" in msg
 
 
 def test_python_binding_rejects_bad_inputs_before_the_library():
