@@ -1,4 +1,4 @@
-// a4 -- mm_fp4 on gfx950: C = alpha * A . B^T over NVFP4 operands (e2m1 values, one e4m3 scale
+// mm_fp4 on gfx950: C = alpha * A . B^T over NVFP4 operands (e2m1 values, one e4m3 scale
 // per 16 K elements in the 128x4 layout), fp32 accumulation, bf16 or fp32 output.
 // FastVideo nvfp4_config.py (_mm_fp4, module docstring) and nvfp4_qat_config.py (apply).
 //

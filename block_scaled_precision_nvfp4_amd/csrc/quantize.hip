@@ -11,7 +11,7 @@
 namespace bsp {
 
 // =============================================================================================
-// a1: weight global scale
+// Weight global scale
 // =============================================================================================
 // |bf16| magnitude bits after nan_to_num: NaN -> 0, inf -> largest finite (0x7F7F). Magnitude
 // bit patterns of non-negative bf16 values order like the values, so the max is an integer max.
@@ -78,7 +78,7 @@ __global__ void gsf_finish_4over6_kernel(float* amax, float* gsf, float* inv_gsf
 }
 
 // =============================================================================================
-// a3: alpha = fl32(1 / fl32(x_gsf * w_gsf))
+// alpha = fl32(1 / fl32(x_gsf * w_gsf))
 // =============================================================================================
 __global__ void alpha_kernel(const float* xg, const float* wg, float* alpha) {
   float p = (*xg) * (*wg);
@@ -86,7 +86,7 @@ __global__ void alpha_kernel(const float* xg, const float* wg, float* alpha) {
 }
 
 // =============================================================================================
-// a2: NVFP4 quantize
+// NVFP4 quantize
 // =============================================================================================
 // One workgroup quantizes a 128-row x 256-K tile (16 scale columns = 4 column groups of the
 // 128x4 scale layout, i.e. four whole 512-byte scale tiles). 256 threads = 8 rows x 32 lanes;
@@ -353,7 +353,7 @@ __global__ __launch_bounds__(256) void nvfp4_quantize_token_kernel(
 }
 
 // =============================================================================================
-// a6: MXFP8 quantize
+// MXFP8 quantize
 // =============================================================================================
 // One workgroup covers 64 rows x 256 K (8 steps of 8 rows x 32 lanes x 8 elements). A 32-element
 // group is a lane quad; its amax is a DPP quad max. Scale byte = max(biased exponent of amax - 8, 0)

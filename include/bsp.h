@@ -51,7 +51,7 @@ int bsp_version(void);
  * the padded rows; the shape kernel gives (rows, (K+15)//16) scale bytes. */
 int bsp_nvfp4_sf_bytes(int64_t rows, int64_t K, int64_t* bytes);
 
-/* a1 -- weight global scale. [FV-QAT] convert_model_to_fp4: gsf = (448*6) / amax(|W|) with NaN/inf
+/* Weight global scale. [FV-QAT] convert_model_to_fp4: gsf = (448*6) / amax(|W|) with NaN/inf
  * replaced first (NaN -> 0, +-inf -> +-largest finite bf16); [SGL] _quantize_weight_nvfp4: gsf = 1
  * when amax == 0. Writes three device fp32 scalars: amax, gsf = fl32(2688/amax) and
  * inv_gsf = fl32(1/gsf) (the fp32 weight alpha of [FV-NV] convert_model_to_nvfp4).
@@ -59,7 +59,7 @@ int bsp_nvfp4_sf_bytes(int64_t rows, int64_t K, int64_t* bytes);
 int bsp_nvfp4_global_sf(const void* w_bf16, int64_t rows, int64_t K, int64_t ld,
                         float* gsf_dev, float* inv_gsf_dev, float* amax_dev, void* stream);
 
-/* a2 -- NVFP4 quantize. [FV-NV] _nvfp4_quantize / module docstring: e2m1 values, one e4m3 scale
+/* NVFP4 quantize. [FV-NV] _nvfp4_quantize / module docstring: e2m1 values, one e4m3 scale
  * per 16 consecutive K elements under the fp32 global scale *gsf_dev, scales in layout_128x4.
  * Per block: a = max|x|; s = fl32(g*fl32(a*fl32(1/6))); S = e4m3(s) (nearest-even, saturate 448);
  * r = S==0 ? 0 : fl32(g/S); q = e2m1(fl32(x*r)) (nearest-even, saturate 6, sign kept).
@@ -80,11 +80,11 @@ int bsp_nvfp4_prequantize_weight(const void* w_bf16, int64_t N, int64_t K, int64
                                  uint8_t* packed, uint8_t* sf, float* gsf_dev, float* inv_gsf_dev,
                                  float* amax_dev, void* stream);
 
-/* a3 -- alpha = fl32(1 / fl32(x_gsf * w_gsf)) on the device ([FV-QAT] NVFP4QATQuantizeMethod.apply;
+/* alpha = fl32(1 / fl32(x_gsf * w_gsf)) on the device ([FV-QAT] NVFP4QATQuantizeMethod.apply;
  * with the static x_gsf = 1.0 this equals [FV-NV]'s stored 1/w_gsf). */
 int bsp_nvfp4_alpha(const float* x_gsf_dev, const float* w_gsf_dev, float* alpha_dev, void* stream);
 
-/* a4 -- mm_fp4: C[m, n] = alpha * sum_k e2m1(A[m,k])*e4m3(SA[m,k/16]) * e2m1(B[n,k])*e4m3(SB[n,k/16]),
+/* mm_fp4: C[m, n] = alpha * sum_k e2m1(A[m,k])*e4m3(SA[m,k/16]) * e2m1(B[n,k])*e4m3(SB[n,k/16]),
  * fp32 accumulation, fp32 alpha from *alpha_dev, result rounded to bf16 (nearest-even) or stored
  * as fp32. [FV-NV] _mm_fp4 / [FV-QAT] apply: the weight is passed as the transposed view of its
  * [N, K/2] packed buffer, i.e. B here is that K-major [N, K/2] buffer.
@@ -96,7 +96,7 @@ int bsp_mm_fp4(const uint8_t* a_packed, const uint8_t* a_sf, const uint8_t* b_pa
                const uint8_t* b_sf, const float* alpha_dev, int64_t M, int64_t N, int64_t K,
                void* out, int64_t ldc, int out_dtype, void* stream);
 
-/* a6 -- MXFP8 quantize. [VLO] DiffusionMXFP8Config: 32 consecutive K elements share one e8m0
+/* MXFP8 quantize. [VLO] DiffusionMXFP8Config: 32 consecutive K elements share one e8m0
  * scale (OCP MX). Es = clamp(floor(log2 amax) - 8, -127, 127); scale byte Es+127 (0x00 for an
  * all-zero group); q = e4m3(fl32(x * 2^-Es)) (nearest-even, saturate 448, sign kept).
  * x: device bf16 [M, K], row stride ld, K % 32 == 0. q: device uint8 [M, K] row-major.
@@ -106,7 +106,7 @@ int bsp_mm_fp4(const uint8_t* a_packed, const uint8_t* a_sf, const uint8_t* b_pa
 int bsp_mxfp8_quantize(const void* x_bf16, int64_t M, int64_t K, int64_t ld, uint8_t* q,
                        uint8_t* sf, void* stream);
 
-/* a7 -- mm_mxfp8: C[m, n] = sum_k e4m3(A[m,k])*2^(SA[m,k/32]-127) * e4m3(B[n,k])*2^(SB[n,k/32]-127),
+/* mm_mxfp8: C[m, n] = sum_k e4m3(A[m,k])*2^(SA[m,k/32]-127) * e4m3(B[n,k])*2^(SB[n,k/32]-127),
  * fp32 accumulation, bf16 or fp32 output ([VLO] NPUMxfp8LinearMethod._quant_matmul: per-row e8m0
  * scales of both operands, group [1, 1, 32], output in the activation dtype).
  * a: [M, K] e4m3, a_sf [M, K/32]; b: [N, K] e4m3 (K-major weight), b_sf [N, K/32]; out [M, N]
@@ -144,7 +144,7 @@ int bsp_mm_mxfp4(const uint8_t* a_packed, const uint8_t* a_sf, const uint8_t* b_
  * x, y: device bf16 [n], contiguous, 16-byte aligned. */
 int bsp_gelu_tanh_bf16(const void* x, void* y, int64_t n, void* stream);
 
-/* layout_8x4 for small-M activations and the 4over6 weight scale (NEXT row f4). */
+/* layout_8x4 for small-M activations and the 4over6 weight scale. */
 
 /* Bytes of an NVFP4 scale buffer in layout_8x4: ceil(rows/8)*8 * ceil(K/64)*4. */
 int bsp_nvfp4_sf_bytes_8x4(int64_t rows, int64_t K, int64_t* bytes);
@@ -171,7 +171,7 @@ int bsp_mm_fp4_8x4(const uint8_t* a_packed, const uint8_t* a_sf, const uint8_t* 
 int bsp_nvfp4_global_sf_4over6(const void* w_bf16, int64_t rows, int64_t K, int64_t ld,
                                float* gsf_dev, float* inv_gsf_dev, float* amax_dev, void* stream);
 
-/* Per-token activation scales (NEXT row f3). [SGL] NVFP4OnlineConfig.__init__ (per-token
+/* Per-token activation scales. [SGL] NVFP4OnlineConfig.__init__ (per-token
  * activation path): weights keep their static tensor scale while each activation row (token) gets
  * its own fp32 scale at run time. Row m: amax_m = max|x[m, :]|, gsf_rows[m] = fl32(2688/amax_m)
  * (1.0 for an all-zero row: the tensor rule of bsp_nvfp4_global_sf applied to the row), and the row

@@ -1,4 +1,4 @@
-"""The linear layer's bias (a5), as the pages add it after the quantized GEMM.
+"""The linear layer's bias, as the pages add it after the quantized GEMM.
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 

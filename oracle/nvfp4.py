@@ -48,7 +48,7 @@ def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------------------
-# a1: weight global scale
+# weight global scale
 # ----------------------------------------------------------------------------------------
 def tensor_amax(w_bits: np.ndarray) -> np.float32:
     """max |W| after nan_to_num (NaN -> 0, +-inf -> +-largest finite bf16)."""
@@ -87,7 +87,7 @@ def global_sf_4over6(w_bits: np.ndarray):
 
 
 # ----------------------------------------------------------------------------------------
-# a3: alpha
+# alpha
 # ----------------------------------------------------------------------------------------
 def alpha(x_gsf, w_gsf) -> np.float32:
     """alpha = fl32(1 / fl32(x_gsf * w_gsf)) (fp32 throughout, reading U10)."""
@@ -168,7 +168,7 @@ def _layout_fns(layout: str):
 
 
 # ----------------------------------------------------------------------------------------
-# a2: quantize
+# quantize
 # ----------------------------------------------------------------------------------------
 def quantize_blocks(xf: np.ndarray, gsf) -> tuple:
     """Quantize fp32 values [rows, nblocks, 16] under global scale gsf (a scalar, or one per row).

@@ -258,7 +258,8 @@ def _rand_mx_operand(rng, rows, k):
     return q, s
 
 
-@pytest.mark.parametrize("m,n,k", [(1, 64, 128), (77, 200, 256), (256, 256, 512), (300, 130, 384)])
+@pytest.mark.parametrize("m,n,k", [(1, 64, 128), (77, 200, 256), (256, 256, 512), (300, 130, 384),
+                                   (130, 300, 1536), (257, 129, 2048)])
 def test_mm_mxfp8_random_operands_all_elements(m, n, k):
     say("mm_mxfp8 random", m, n, k)
     rng = np.random.default_rng(m + n + k)
@@ -273,6 +274,36 @@ def test_mm_mxfp8_random_operands_all_elements(m, n, k):
     c16 = t16.float().cpu().numpy().astype(np.float64)
     assert_gemm_bf16(c16, ref, f"mx random {m}x{n}x{k}")
     _assert_bf16_is_rne_of_f32(t16, t32)
+
+
+def _misaligned_copy(t, offset):
+    """A copy of contiguous uint8 tensor t whose data starts `offset` bytes past a 256-byte
+    boundary."""
+    buf = torch.zeros(t.numel() + 256, dtype=torch.uint8, device=t.device)
+    assert buf.data_ptr() % 256 == 0
+    v = buf[offset: offset + t.numel()].view(t.shape)
+    v.copy_(t)
+    return v
+
+
+@pytest.mark.parametrize("m,n,k", [(300, 257, 1536), (64, 96, 512)])
+def test_mm_mxfp8_scale_paths_agree(m, n, k):
+    """With K a multiple of 512 and 16-byte aligned scale matrices the MXFP8 kernel reads the scales
+    in blocks of 512 K per row; with scales at a 4-byte (not 16-byte) aligned address it gathers one
+    dword per row and stage pair. Same inputs: the same fp32 bits either way, and the oracle's
+    values."""
+    say("mm_mxfp8 scale paths", m, n, k)
+    rng = np.random.default_rng(7 * m + n + k)
+    qa, sa = _rand_mx_operand(rng, m, k)
+    qb, sb = _rand_mx_operand(rng, n, k)
+    ref = X.mm_mxfp8(qa, sa, qb, sb, m, n, k)
+    da, dsa, db, dsb = dev_u8(qa), dev_u8(sa), dev_u8(qb), dev_u8(sb)
+    assert dsa.data_ptr() % 16 == 0 and dsb.data_ptr() % 16 == 0
+    c_blk = bsp.bsp_mm_mxfp8(da, dsa, db, dsb, out_dtype=torch.float32)
+    msa, msb = _misaligned_copy(dsa, 4), _misaligned_copy(dsb, 4)
+    c_gat = bsp.bsp_mm_mxfp8(da, msa, db, msb, out_dtype=torch.float32)
+    assert torch.equal(c_blk.view(torch.int32), c_gat.view(torch.int32))
+    assert_gemm_f32(c_blk.cpu().numpy().astype(np.float64), ref, f"mx scale paths {m}x{n}x{k}")
 
 
 def test_mm_mxfp8_full_size():
@@ -337,7 +368,7 @@ def test_mm_mxfp4_full_size():
     assert_gemm_bf16(gather(c, rows, cols), ref, "cfg4 fc_in mxfp4")
 
 
-# ------------------------------------------------------------------------------- bias (a5)
+# ------------------------------------------------------------------------------------ bias
 def _ref_plus_bias_bf16(ref, bias_bits):
     """The pages' result: the oracle's product rounded to bf16, plus the bf16 bias (bf16 add)."""
     from oracle import linear as L
@@ -396,7 +427,7 @@ def test_mm_fp4_bias_full_size_fc_in():
     assert_gemm_bf16(gather(cb, rows, cols), _ref_plus_bias_bf16(ref, bbits[cols]), "cfg4 fc_in + bias")
 
 
-@pytest.mark.parametrize("m,n,k", [(1, 64, 128), (77, 200, 256), (300, 130, 384)])
+@pytest.mark.parametrize("m,n,k", [(1, 64, 128), (77, 200, 256), (300, 130, 384), (129, 260, 1024)])
 def test_mm_mxfp8_bias_random(m, n, k):
     """bsp_mm_mxfp8_bias: fp32 output = fp32 product + fp32 bias exactly; bf16 output = its one
     nearest-even rounding; within tolerance of the oracle's exact product plus bias."""
