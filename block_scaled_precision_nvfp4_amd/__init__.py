@@ -48,6 +48,7 @@ SIGNATURES = {
     "bsp_nvfp4_global_sf_4over6": ([_p, _i64, _i64, _i64, _p, _p, _p, _p], _int),
     "bsp_mm_fp4_per_token": ([_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _int, _p], _int),
     "bsp_mm_fp4_bias": ([_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _int, _p], _int),
+    "bsp_mm_fp4_gelu_nvfp4": ([_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _p, _p], _int),
     "bsp_mm_mxfp8_bias": ([_p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _int, _p], _int),
     "bsp_mm_mxfp4_bias": ([_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _int, _p], _int),
 }
@@ -273,6 +274,33 @@ def bsp_mm_fp4_bias(a: torch.Tensor, a_sf: torch.Tensor, b: torch.Tensor, b_sf: 
     return out
 
 
+def bsp_mm_fp4_gelu_nvfp4(a: torch.Tensor, a_sf: torch.Tensor, b: torch.Tensor, b_sf: torch.Tensor,
+                          alpha: torch.Tensor, out_gsf: torch.Tensor,
+                          packed: Optional[torch.Tensor] = None,
+                          sf: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """NVFP4 of gelu_tanh(alpha * A . B^T) with global scale out_gsf, straight from the GEMM: the
+    same bytes as bsp_nvfp4_quantize_gelu(bsp_mm_fp4(...), out_gsf) without the bf16 product in
+    memory. packed [M, N/2], sf [ceil(M/128)*128, N/16] (128x4); N must be a multiple of 128."""
+    m, n, k = _mm_fp4_shapes(a, a_sf, b, b_sf)
+    _need(alpha, "alpha", torch.float32, a.device)
+    _need(out_gsf, "out_gsf", torch.float32, a.device)
+    rp, kp = -(-m // 128) * 128, n // 16
+    if packed is None:
+        packed = torch.empty((m, n // 2), dtype=torch.uint8, device=a.device)
+    if sf is None:
+        sf = torch.empty((rp, kp), dtype=torch.uint8, device=a.device)
+    _need(packed, "packed", torch.uint8, a.device)
+    _need(sf, "sf", torch.uint8, a.device)
+    if packed.numel() < m * (n // 2) or not packed.is_contiguous():
+        raise ValueError("packed must be contiguous with M*N/2 bytes")
+    if sf.numel() < rp * kp or not sf.is_contiguous():
+        raise ValueError("sf must be contiguous with ceil(M/128)*128 x N/16 bytes")
+    _call("bsp_mm_fp4_gelu_nvfp4", a.data_ptr(), a_sf.data_ptr(), b.data_ptr(), b_sf.data_ptr(),
+          alpha.data_ptr(), out_gsf.data_ptr(), m, n, k, packed.data_ptr(), sf.data_ptr(),
+          _stream(a.device))
+    return packed, sf
+
+
 def bsp_mm_fp4_per_token(a: torch.Tensor, a_sf: torch.Tensor, b: torch.Tensor, b_sf: torch.Tensor,
                          x_gsf_rows: torch.Tensor, w_gsf: torch.Tensor,
                          out_dtype: torch.dtype = torch.bfloat16,
@@ -309,7 +337,8 @@ def bsp_nvfp4_global_sf_4over6(w: torch.Tensor) -> Tuple[torch.Tensor, torch.Ten
     return gsf, inv, amax
 
 
-def _mm_fp4_args(a, a_sf, b, b_sf, out_dtype, out, a_row_tile: int = 128):
+def _mm_fp4_shapes(a, a_sf, b, b_sf, a_row_tile: int = 128):
+    """(M, N, K) of an NVFP4 GEMM after checking the operands and their scale buffers."""
     _need(a, "a", torch.uint8)
     dev = a.device
     for t, nm in ((a_sf, "a_sf"), (b, "b"), (b_sf, "b_sf")):
@@ -319,6 +348,15 @@ def _mm_fp4_args(a, a_sf, b, b_sf, out_dtype, out, a_row_tile: int = 128):
     if not (a.is_contiguous() and b.is_contiguous() and a_sf.is_contiguous() and b_sf.is_contiguous()):
         raise ValueError("operands and scales must be contiguous")
     m, n, k = a.shape[0], b.shape[0], a.shape[1] * 2
+    a_need = bsp_nvfp4_sf_bytes(m, k) if a_row_tile == 128 else bsp_nvfp4_sf_bytes_8x4(m, k)
+    if a_sf.numel() < a_need or b_sf.numel() < bsp_nvfp4_sf_bytes(n, k):
+        raise ValueError("scale buffers are smaller than the layout needs")
+    return m, n, k
+
+
+def _mm_fp4_args(a, a_sf, b, b_sf, out_dtype, out, a_row_tile: int = 128):
+    m, n, k = _mm_fp4_shapes(a, a_sf, b, b_sf, a_row_tile)
+    dev = a.device
     if out_dtype not in (torch.bfloat16, torch.float32):
         raise TypeError(f"out_dtype must be bf16 or fp32, got {out_dtype}")
     code = BSP_OUT_BF16 if out_dtype == torch.bfloat16 else BSP_OUT_F32
@@ -327,9 +365,6 @@ def _mm_fp4_args(a, a_sf, b, b_sf, out_dtype, out, a_row_tile: int = 128):
     _need(out, "out", out_dtype, dev)
     if out.dim() != 2 or out.shape[0] != m or out.shape[1] != n or out.stride(1) != 1:
         raise ValueError(f"out must be [{m}, {n}] with unit column stride")
-    a_need = bsp_nvfp4_sf_bytes(m, k) if a_row_tile == 128 else bsp_nvfp4_sf_bytes_8x4(m, k)
-    if a_sf.numel() < a_need or b_sf.numel() < bsp_nvfp4_sf_bytes(n, k):
-        raise ValueError("scale buffers are smaller than the layout needs")
     return m, n, k, code, out
 
 

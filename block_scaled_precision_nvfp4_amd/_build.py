@@ -24,7 +24,7 @@ HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
     "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-DBSP_DEFAULT_HW_CVT=1", "-DBSP_CVT_FULL_SCALE=0",
+    "-DBSP_DEFAULT_HW_CVT=1",
 ]
 
 

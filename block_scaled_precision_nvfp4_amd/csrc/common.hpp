@@ -116,4 +116,57 @@ __device__ __forceinline__ float quad_max(float x) {
   return fmaxf(x, __int_as_float(y));
 }
 
+// ---------------------------------------------------------------------------------------------
+// device: NVFP4 encoding pieces shared by the quantize kernels and the GEMM epilogue that emits
+// NVFP4
+// ---------------------------------------------------------------------------------------------
+constexpr float kSixth = 0.16666667163372040f;  // fl32(1/6) = 0x3E2AAAAB
+
+// gelu(x) = 0.5 x (1 + tanh(z)), z = sqrt(2/pi) (x + 0.044715 x^3), in fp32, rounded once to bf16
+// by the caller. 0.5 (1 + tanh z) is the logistic function of 2z, evaluated with t = 2^(-2|z| log2 e)
+// <= 1 as x / (1 + t) for x >= 0 and x t / (1 + t) for x < 0 (z has the sign of x): no cancellation
+// and no overflow. -2|z| log2 e = |x| (c0 + c2 x^2) with c0 = -2 log2(e) sqrt(2/pi) and
+// c2 = 0.044715 c0, one fused multiply-add. t is always formed as 2^64 t = 2^(that + 64) (the
+// exponent is at most 64, so no overflow) and negative outputs are scaled back by 2^-64 at the end,
+// so tiny negative outputs keep their bits down to where bf16 underflows too. v_exp_f32 and
+// v_rcp_f32 (about 1 ulp each) keep the whole function at a dozen instructions; the result is
+// within a few fp32 ulps, far inside one bf16 ulp except next to a rounding boundary.
+__device__ __forceinline__ float gelu_tanh(float x) {
+  const float c0 = -2.302208198144325f;    // -2 log2(e) sqrt(2/pi)
+  const float c2 = -0.1029432395800235f;   // 0.044715 c0
+  const float x2 = x * x;
+  const float p64 = __builtin_fmaf(__builtin_fmaf(c2, x2, c0), __builtin_fabsf(x), 64.0f);
+  const float ts = __builtin_amdgcn_exp2f(p64);                       // t * 2^64
+  const float r = __builtin_amdgcn_rcpf(__builtin_fmaf(ts, 5.421010862427522e-20f, 1.0f));  // 1/(1+t)
+  const bool neg = x < 0.0f;                                  // branch-free: selects, no exec masks
+  const float m = neg ? ts : 1.0f;
+  const float sc = neg ? 5.421010862427522e-20f : 1.0f;       // 2^-64
+  return ((x * m) * r) * sc;
+}
+
+// 8 values -> gelu, each rounded to bf16 and widened back to fp32 (what the GELU kernel stores)
+__device__ __forceinline__ void gelu8_bf16(float (&f)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) {
+    const uint32_t p = bf16x2_rne(gelu_tanh(f[i]), gelu_tanh(f[i + 1]));
+    f[i] = bf16_lo(p);
+    f[i + 1] = bf16_hi(p);
+  }
+}
+
+__device__ __forceinline__ void unpack8(const uint4& v, float (&f)[8]) {
+  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+  f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+  f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+  f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+
+__device__ __forceinline__ float absmax8(const float (&f)[8]) {
+  float a = fmaxf(__builtin_fabsf(f[0]), __builtin_fabsf(f[1]));
+#pragma unroll
+  for (int i = 2; i < 8; ++i) a = fmaxf(a, __builtin_fabsf(f[i]));
+  return a;
+}
+
+
 }  // namespace bsp

@@ -39,7 +39,8 @@ __device__ __forceinline__ void tile_coords(int bid, int ntm, int ntn, int& tm, 
 //    again (the pages add the bias to mm_fp4's bf16 output); with fp32 output, product + bias;
 //  kBiasF32Before: an fp32 [N] vector added to the fp32 product before its one rounding (the MXFP8
 //    matmul that takes an fp32 bias).
-enum { kBiasNone = 0, kBiasBf16After = 1, kBiasF32Before = 2 };
+// kGeluNvfp4 is no bias but a different output: NVFP4 of gelu(C) (store_tile_gelu_nvfp4 below).
+enum { kBiasNone = 0, kBiasBf16After = 1, kBiasF32Before = 2, kGeluNvfp4 = 3 };
 
 // Epilogue of a 128x128 wave tile made of 4x4 MFMA 32x32 tiles acc[n][m] holding D[n][m] (the
 // MFMA's A operand is the B (weight) fragment): a lane holds output column gm = m0w + 32m + (lane%32)
@@ -208,6 +209,97 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], const floa
     store_wave_tile<OUT_F32, BIAS>(acc, alpha, m0 + wm * 128, n0 + wn * 128, M, N, out, ldc,
                                    vec_store, li, h, bias);
   }
+}
+
+// GELU + NVFP4 epilogue: instead of C, the NVFP4 encoding of gelu(C) (the input of the next
+// linear layer, quantized with the static global scale *gsf): packed e2m1 [M, N/2] (row stride N/2
+// bytes) and e4m3 scales in the 128x4 layout over [ceil(M/128)*128, N/16], rows M.. of the last
+// 128-row tile zero. Each value is what the separate kernels give: C rounded to bf16, gelu in fp32
+// rounded to bf16, then nvfp4 quantize. Needs N % 128 == 0, so a wave's 128 columns are all inside
+// or all outside C and its scale columns fill two whole 128x4 tiles.
+// The bf16 image of 64 rows is built as in the staged epilogue; each lane then takes one 16-byte
+// segment (8 values, half a 16-value block, the other half in the neighbouring lane), encodes it
+// and writes 4 bytes; the scale bytes gather in a 1 KB image of the wave's two 512-byte scale
+// tiles, stored whole at the end. rtab[c] = fl32(g / e4m3(c)) for the 127 scale codes.
+__device__ __forceinline__ void store_wave_tile_gelu_nvfp4(const f32x16 (&acc)[4][4],
+                                                           const float (&alpha)[4], int64_t m0w,
+                                                           int64_t n0w, int64_t M, int64_t N,
+                                                           uint8_t* packed, uint8_t* sf, float g,
+                                                           const float* rtab, uint8_t* lds,
+                                                           uint8_t* sfimg, int lane, int li, int h) {
+  if (n0w >= N) return;
+  const float bq[4][4][4] = {};
+  const int64_t half_n = N / 2;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm) {
+#pragma unroll
+      for (int n = 0; n < 4; ++n)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          uint32_t p01, p23;
+          piece_bf16<kBiasNone>(acc, alpha, bq, 2 * half + mm, n, b, p01, p23);
+          *reinterpret_cast<uint2*>(lds + (mm * 32 + li) * kEpiRowBytes + (n * 32 + 8 * b + 4 * h) * 2) =
+              make_uint2(p01, p23);
+        }
+    }
+    // the same wave reads back what it wrote: LDS executes one wave's operations in order. All
+    // 16 segments are read first so that the GELU chains of all of them can interleave (one wave
+    // per SIMD has no other wave to hide their latency).
+    const int c16 = lane & 15;
+    u32x4 seg[16];
+#pragma unroll
+    for (int it = 0; it < 16; ++it)
+      seg[it] = *reinterpret_cast<const u32x4*>(lds + (it * 4 + (lane >> 4)) * kEpiRowBytes + c16 * 16);
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int row = it * 4 + (lane >> 4);
+      const u32x4 v = seg[it];
+      float f[8];
+      unpack8(make_uint4(v.x, v.y, v.z, v.w), f);
+      gelu8_bf16(f);
+      const float a = pair_max(absmax8(f));
+      const int rr = half * 64 + row;  // row inside the wave's 128 rows
+      const int64_t gm = m0w + rr;
+      const uint32_t S = gm < M ? e4m3_encode_pos(g * (a * kSixth)) : 0u;
+      const float r = rtab[S];
+      uint32_t o = 0;
+      o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, f[0] * r, f[1] * r, 1.0f, 0);
+      o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, f[2] * r, f[3] * r, 1.0f, 1);
+      o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, f[4] * r, f[5] * r, 1.0f, 2);
+      o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, f[6] * r, f[7] * r, 1.0f, 3);
+      if (gm < M)
+        __builtin_nontemporal_store(o, reinterpret_cast<uint32_t*>(packed + gm * half_n + n0w / 2 + c16 * 4));
+      if ((c16 & 1) == 0) {
+        const int cb = c16 >> 1;  // scale column inside the wave's 8
+        sfimg[(cb >> 2) * 512 + (rr & 31) * 16 + (rr >> 5) * 4 + (cb & 3)] = (uint8_t)S;
+      }
+    }
+  }
+  // the wave's two 512-byte scale tiles: row tile m0w / 128, column groups n0w / 64 and + 1
+  if (m0w < M) {
+    const int64_t groups = N / 64;
+    const int64_t tile = (m0w / 128) * groups + n0w / 64 + (lane >> 5);
+    const u32x4 v = reinterpret_cast<const u32x4*>(sfimg)[lane];
+    *reinterpret_cast<u32x4*>(sf + tile * 512 + (lane & 31) * 16) = v;
+  }
+}
+
+// Workgroup epilogue for the GELU + NVFP4 output. The images overlay the stage memory `lds`
+// (at least 4 * (kEpiWaveBytes + 1024) bytes); rtab is the workgroup's scale-reciprocal table.
+__device__ __forceinline__ void store_tile_gelu_nvfp4(const f32x16 (&acc)[4][4],
+                                                      const float (&alpha)[4], int64_t m0,
+                                                      int64_t n0, int wm, int wn, int64_t M,
+                                                      int64_t N, uint8_t* packed, uint8_t* sf,
+                                                      const float* gsf, float* rtab, uint8_t* lds,
+                                                      int t, int wave, int lane, int li, int h) {
+  const float g = *gsf;
+  if (t < 128) rtab[t] = (t == 0 || t > 0x7E) ? 0.0f : g / e4m3_decode_pos((uint32_t)t);
+  __syncthreads();   // rtab; every wave is done reading the stage buffers the images overlay
+  store_wave_tile_gelu_nvfp4(acc, alpha, m0 + wm * 128, n0 + wn * 128, M, N, packed, sf, g, rtab,
+                             lds + wave * kEpiWaveBytes, lds + 4 * kEpiWaveBytes + wave * 1024, lane,
+                             li, h);
 }
 
 }  // namespace bsp

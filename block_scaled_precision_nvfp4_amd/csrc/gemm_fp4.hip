@@ -252,13 +252,17 @@ __device__ __forceinline__ f16x8 frag_deq(const Frags& f, int q, int j) {
 // ROWSCALE: per-token activation scales; alpha_ptr is then the [M] array of row encode scales
 // and w_gsf_ptr the weight's encode scale, alpha_m = fl32(1 / fl32(x_gsf[m] * w_gsf)).
 // SFA8: A's scales are in layout_8x4 with rows8 (= ceil(M/8)*8) rows.
+// BIAS: the epilogue kind (gemm_common.hpp); with kGeluNvfp4 `out` receives the packed NVFP4 of
+// gelu(C), sf_out its scales and out_gsf is the device global scale it is quantized with.
 template <bool OUT_F32, bool ROWSCALE, bool SFA8, int BIAS>
 __global__ __launch_bounds__(256, 1) void mm_fp4_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ SB, const float* __restrict__ alpha_ptr,
     const float* __restrict__ w_gsf_ptr, int64_t M, int64_t N, int64_t K, void* __restrict__ out,
-    int64_t ldc, int ntm, int ntn, bool vec_store, int64_t rows8, const void* __restrict__ bias) {
+    int64_t ldc, int ntm, int ntn, bool vec_store, int64_t rows8, const void* __restrict__ bias,
+    uint8_t* __restrict__ sf_out, const float* __restrict__ out_gsf) {
   __shared__ Stage st[NSTAGE];
+  __shared__ float rtab[BIAS == kGeluNvfp4 ? 128 : 1];
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -398,9 +402,15 @@ __global__ __launch_bounds__(256, 1) void mm_fp4_kernel(
 #pragma unroll
     for (int m = 0; m < 4; ++m) alpha[m] = a;
   }
-  static_assert(sizeof(st) >= 4 * kEpiWaveBytes, "epilogue images overlay the stage buffers");
-  store_tile<OUT_F32, BIAS>(acc, alpha, m0, n0, wm, wn, M, N, out, ldc, vec_store,
-                            reinterpret_cast<uint8_t*>(st), wave, lane, li, h, bias);
+  static_assert(sizeof(st) >= 4 * (kEpiWaveBytes + 1024), "epilogue images overlay the stage buffers");
+  if constexpr (BIAS == kGeluNvfp4) {
+    store_tile_gelu_nvfp4(acc, alpha, m0, n0, wm, wn, M, N, static_cast<uint8_t*>(out), sf_out,
+                          out_gsf, rtab, reinterpret_cast<uint8_t*>(st), t, wave, lane, li, h);
+  } else {
+    (void)rtab; (void)sf_out; (void)out_gsf;
+    store_tile<OUT_F32, BIAS>(acc, alpha, m0, n0, wm, wn, M, N, out, ldc, vec_store,
+                              reinterpret_cast<uint8_t*>(st), wave, lane, li, h, bias);
+  }
 }
 
 }  // namespace fp4
@@ -409,20 +419,25 @@ template <bool ROWSCALE, bool SFA8, int BIAS = kBiasNone>
 static void launch_mm_fp4_t(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
                             const float* alpha, const float* w_gsf, int64_t M, int64_t N, int64_t K,
                             void* out, int64_t ldc, int out_dtype, hipStream_t s,
-                            const void* bias = nullptr) {
+                            const void* bias = nullptr, uint8_t* sf_out = nullptr,
+                            const float* out_gsf = nullptr) {
   const int64_t ntm = ceil_div(M, fp4::BM), ntn = ceil_div(N, fp4::BN);
   const int64_t tiles = ntm * ntn;
   const size_t esz = out_dtype == BSP_OUT_F32 ? 4 : 2;
   const bool vec = (ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(out) & (4 * esz - 1)) == 0);
   const int64_t rows8 = ceil_div(M, 8) * 8;
-  if (out_dtype == BSP_OUT_F32)
+  if constexpr (BIAS == kGeluNvfp4)
+    hipLaunchKernelGGL((fp4::mm_fp4_kernel<false, ROWSCALE, SFA8, BIAS>), dim3((unsigned)tiles), dim3(256),
+                       0, s, a, sa, b, sb, alpha, w_gsf, M, N, K, out, ldc, (int)ntm, (int)ntn, vec,
+                       rows8, bias, sf_out, out_gsf);
+  else if (out_dtype == BSP_OUT_F32)
     hipLaunchKernelGGL((fp4::mm_fp4_kernel<true, ROWSCALE, SFA8, BIAS>), dim3((unsigned)tiles), dim3(256),
                        0, s, a, sa, b, sb, alpha, w_gsf, M, N, K, out, ldc, (int)ntm, (int)ntn, vec,
-                       rows8, bias);
+                       rows8, bias, sf_out, out_gsf);
   else
     hipLaunchKernelGGL((fp4::mm_fp4_kernel<false, ROWSCALE, SFA8, BIAS>), dim3((unsigned)tiles), dim3(256),
                        0, s, a, sa, b, sb, alpha, w_gsf, M, N, K, out, ldc, (int)ntm, (int)ntn, vec,
-                       rows8, bias);
+                       rows8, bias, sf_out, out_gsf);
 }
 
 }  // namespace bsp
@@ -476,6 +491,28 @@ extern "C" int bsp_mm_fp4_bias(const uint8_t* a_packed, const uint8_t* a_sf, con
   launch_mm_fp4_t<false, false, kBiasBf16After>(a_packed, a_sf, b_packed, b_sf, alpha_dev, nullptr, M, N,
                                                 K, out, ldc, out_dtype, (hipStream_t)stream, bias_bf16);
   return check_launch("bsp_mm_fp4_bias");
+}
+
+extern "C" int bsp_mm_fp4_gelu_nvfp4(const uint8_t* a_packed, const uint8_t* a_sf,
+                                     const uint8_t* b_packed, const uint8_t* b_sf,
+                                     const float* alpha_dev, const float* out_gsf_dev, int64_t M,
+                                     int64_t N, int64_t K, uint8_t* out_packed, uint8_t* out_sf,
+                                     void* stream) {
+  BSP_REQUIRE(N % 128 == 0, BSP_ESHAPE, "bsp_mm_fp4_gelu_nvfp4: N (%lld) must be a multiple of 128",
+              (long long)N);
+  BSP_REQUIRE(M == 0 || N == 0 || (out_sf && out_gsf_dev), BSP_EINVAL,
+              "bsp_mm_fp4_gelu_nvfp4: null pointer");
+  BSP_REQUIRE((reinterpret_cast<uintptr_t>(out_packed) & 3u) == 0 &&
+                  (reinterpret_cast<uintptr_t>(out_sf) & 15u) == 0,
+              BSP_EINVAL, "bsp_mm_fp4_gelu_nvfp4: out_packed must be 4-byte and out_sf 16-byte aligned");
+  // the output is [M, N/2] packed bytes; the ldc and out_dtype given to the checks are nominal
+  int e = mm_fp4_checks("bsp_mm_fp4_gelu_nvfp4", a_packed, a_sf, b_packed, b_sf, alpha_dev, M, N, K,
+                        out_packed, N, BSP_OUT_BF16);
+  if (e) return e > 0 ? BSP_OK : e;
+  launch_mm_fp4_t<false, false, kGeluNvfp4>(a_packed, a_sf, b_packed, b_sf, alpha_dev, nullptr, M, N,
+                                            K, out_packed, N / 2, BSP_OUT_BF16, (hipStream_t)stream,
+                                            nullptr, out_sf, out_gsf_dev);
+  return check_launch("bsp_mm_fp4_gelu_nvfp4");
 }
 
 extern "C" int bsp_mm_fp4_8x4(const uint8_t* a_packed, const uint8_t* a_sf, const uint8_t* b_packed,

@@ -199,7 +199,20 @@ int bsp_mm_fp4_per_token(const uint8_t* a_packed, const uint8_t* a_sf, const uin
 int bsp_nvfp4_quantize_gelu(const void* y_bf16, int64_t M, int64_t K, int64_t ld, const float* gsf_dev,
                             uint8_t* packed, uint8_t* sf, void* stream);
 
-/* a5 fused into the GEMM epilogue -- the linear layer's bias.
+/* The same producer fusion one step earlier, in fc_in's epilogue: the NVFP4 encoding of
+ * gelu_tanh(alpha * A . B^T), byte for byte what bsp_nvfp4_quantize_gelu(bsp_mm_fp4(...), out_gsf)
+ * writes, without the bf16 product ever reaching memory (it exists only as each GEMM tile's LDS
+ * image). [FV-NV] apply (the pre-quantized triple of a producer) with the FFN's fc_in as producer.
+ * A, B, their scales, alpha, M, N, K as bsp_mm_fp4; N must be a multiple of 128 (else BSP_ESHAPE).
+ * out_gsf_dev: device fp32 global scale of the output. out_packed: device u8 [M, N/2], 4-byte
+ * aligned; out_sf: device u8, 128x4 layout over [ceil(M/128)*128, N/16] (bsp_nvfp4_sf_bytes(M, N)
+ * bytes), 16-byte aligned, rows M.. zero. NULL pointers or misalignment: BSP_EINVAL. */
+int bsp_mm_fp4_gelu_nvfp4(const uint8_t* a_packed, const uint8_t* a_sf, const uint8_t* b_packed,
+                          const uint8_t* b_sf, const float* alpha_dev, const float* out_gsf_dev,
+                          int64_t M, int64_t N, int64_t K, uint8_t* out_packed, uint8_t* out_sf,
+                          void* stream);
+
+/* Fused into the GEMM epilogue -- the linear layer's bias.
  * bsp_mm_fp4_bias: [FV-NV] NVFP4QuantizeMethod.apply adds the bias to mm_fp4's bf16 output
  * (out = out + bias, a bf16 add): C[m, n] = bf16(fl32(bf16(alpha * acc)) + fl32(bias[n])), i.e. the
  * bf16 product of bsp_mm_fp4 plus the bias in fp32, rounded to bf16 again (nearest-even both

@@ -152,3 +152,18 @@ def test_bias_entry_point_errors():
     assert _st("bsp_mm_mxfp8_bias", P, P, P, P, P, 8, 8, 64, P, 8, 0, None)[0] == -2
     assert _st("bsp_mm_mxfp4_bias", P, P, P, P, P, None, 8, 8, 128, P, 8, 0, None)[0] == -1
     assert _st("bsp_mm_mxfp4_bias", P, P, P, P, P, P, 8, 8, 128, P, 8, 9, None)[0] == -3
+
+
+def test_gelu_nvfp4_epilogue_entry_point_errors():
+    """bsp_mm_fp4_gelu_nvfp4: N must be a multiple of 128, the scale output and the global scale
+    must be given and the outputs aligned; M == 0 is a no-op."""
+    args = (P, P, P, P, P, P)
+    st, msg = _st("bsp_mm_fp4_gelu_nvfp4", *args, 8, 192, 128, P, P, None)
+    assert st == -2 and "128" in msg
+    assert _st("bsp_mm_fp4_gelu_nvfp4", P, P, P, P, P, None, 8, 256, 128, P, P, None)[0] == -1
+    assert _st("bsp_mm_fp4_gelu_nvfp4", *args, 8, 256, 128, P, None, None)[0] == -1
+    assert _st("bsp_mm_fp4_gelu_nvfp4", *args, 8, 256, 128, ctypes.c_void_p(18), P, None)[0] == -1
+    assert _st("bsp_mm_fp4_gelu_nvfp4", *args, 8, 256, 128, P, ctypes.c_void_p(20), None)[0] == -1
+    assert _st("bsp_mm_fp4_gelu_nvfp4", *args, 8, 256, 96, P, P, None)[0] == -2          # K % 64
+    assert _st("bsp_mm_fp4_gelu_nvfp4", None, None, None, None, None, None, 0, 256, 128, None, None,
+               None)[0] == 0
