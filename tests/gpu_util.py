@@ -1,6 +1,8 @@
-"""Shared helpers of the GPU parity tests (device transfer, seeded inputs, GEMM metrics).
+"""Shared helpers of the GPU parity tests (device transfer, seeded inputs, GEMM metrics, oracle
+references).
 
-Expected values always come from ``oracle/`` applied to the same input bytes the GPU receives.
+Expected values always come from ``oracle/`` applied to the same seeded input the GPU receives
+(the bf16 tensors or the operand bytes a test generates), never to bytes a GPU kernel produced.
 """
 from __future__ import annotations
 
@@ -12,6 +14,8 @@ import torch
 
 import workloads as W
 from oracle import activations as A
+from oracle import formats as F
+from oracle import nvfp4 as N
 
 DEV = "cuda"
 
@@ -93,3 +97,77 @@ def gather(t: torch.Tensor, rows: np.ndarray, cols: np.ndarray) -> np.ndarray:
     ri = torch.from_numpy(rows).to(DEV)
     ci = torch.from_numpy(cols).to(DEV)
     return t[ri, ci].float().cpu().numpy().astype(np.float64)
+
+
+# ------------------------------------------------------------------------------ oracle references
+def oracle_quantize_chunked(x_bits: np.ndarray, gsf, chunk: int = 256):
+    """N.quantize of a large bf16 matrix in row chunks (the quantization is row by row; small
+    chunks keep numpy's temporaries in cache): (packed [M, K/2], flat 128x4 scale buffer)."""
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    m, k = x_bits.shape
+    parts = [N.quantize(x_bits[i: i + chunk], gsf, layout="linear") for i in range(0, m, chunk)]
+    packed = np.concatenate([p for p, _ in parts])
+    rp, cp = N.sf_padded_shape(m, k)
+    lin = np.zeros((rp, cp), dtype=np.uint8)
+    lin[:m, : k // 16] = np.concatenate([s for _, s in parts])
+    return packed, N.swizzle_128x4(lin)
+
+
+def oracle_linear_entries(xb: np.ndarray, wb: np.ndarray, rows: np.ndarray, cols: np.ndarray,
+                          x_gsf: float = 1.0) -> np.ndarray:
+    """The oracle's NVFP4 linear layer y = x w^T at entries (rows[i], cols[i]), from the bf16 bits
+    of x [M, K] and w [N, K]: w's global scale from the whole of w, then only the needed rows of x
+    (static global scale x_gsf) and of w are quantized, and their exact product taken."""
+    ur, ri = np.unique(rows, return_inverse=True)
+    uc, ci = np.unique(cols, return_inverse=True)
+    rg = N.global_sf(wb)[0]
+    px, sx = N.quantize(xb[ur], np.float32(x_gsf))
+    pw, sw = N.quantize(wb[uc], rg)
+    return N.mm_fp4_entries(px, sx, pw, sw, N.alpha(x_gsf, rg), len(ur), len(uc), xb.shape[1], ri, ci)
+
+
+def gelu_rounding_ambiguous(y_bits: np.ndarray, eps: float = 2.0 ** -20) -> np.ndarray:
+    """bf16 inputs whose fp64 GELU lies within eps (relative; about 8 fp32 ulps) of a bf16 rounding
+    boundary, so that a GELU accurate to a few fp32 ulps may round it either way (about one input
+    in 2^11)."""
+    y = (np.asarray(y_bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+    g = A.gelu_tanh(y.astype(np.float64))
+    return A.f64_to_bf16_bits(g * (1 - eps)) != A.f64_to_bf16_bits(g * (1 + eps))
+
+
+def assert_nvfp4_blocks(got_packed, got_sf_lin, ref_packed, ref_sf_lin, exact: np.ndarray,
+                        what: str = "") -> float:
+    """NVFP4 rows (packed [M, K/2], scales [M, >= K/16]) against reference rows: bit-exact in the
+    16-element blocks where `exact` [M, K/16] is set; in the others the scale code within one step
+    and every element within one e2m1 step. Returns the fraction of blocks that differ."""
+    gp, rp = np.asarray(got_packed), np.asarray(ref_packed)
+    m, k = gp.shape[0], gp.shape[1] * 2
+
+    def codes(p):
+        return np.stack([p & 0xF, p >> 4], axis=-1).reshape(m, k // 16, 16)
+
+    gc, rc = codes(gp), codes(rp)
+    gs = np.asarray(got_sf_lin)[:m, : k // 16]
+    rs = np.asarray(ref_sf_lin)[:m, : k // 16]
+    assert np.array_equal(gs[exact], rs[exact]), what
+    assert np.array_equal(gc[exact], rc[exact]), what
+    assert np.all(np.abs(gs.astype(int) - rs) <= 1), what
+    assert np.all(np.abs(F.e2m1_decode(gc) - F.e2m1_decode(rc)) <= 2.0), what
+    return float(np.mean((gs != rs) | np.any(gc != rc, axis=-1)))
+
+
+def assert_nvfp4_of_gelu(got_packed: np.ndarray, got_sf_lin: np.ndarray, y_bits: np.ndarray, gsf,
+                         what: str = "", max_ambiguous: float = 0.03):
+    """The GPU's NVFP4 encoding of gelu(y) (packed [M, K/2], scales unswizzled to [M, K/16])
+    against the oracle's own chain on the same bf16 y: fp64 GELU rounded once to bf16, then the
+    NVFP4 quantize. The GPU's GELU (hardware exp2 and reciprocal) is within a few fp32 ulps, so
+    every 16-element block without a rounding-ambiguous value must be bit-exact (the others within
+    one step, assert_nvfp4_blocks). For smooth data about 16 / 2^11 of the blocks are ambiguous;
+    inputs built from rounding ties and tiny values may set max_ambiguous higher."""
+    y_bits = np.asarray(y_bits, dtype=np.uint16)
+    m, k = y_bits.shape
+    rp, rs = N.quantize(A.gelu_tanh_bf16_bits(y_bits), np.float32(gsf), layout="linear")
+    amb = gelu_rounding_ambiguous(y_bits).reshape(m, k // 16, 16).any(axis=-1)
+    say(what, "gelu-ambiguous blocks:", int(amb.sum()), "of", amb.size)
+    assert amb.mean() < max_ambiguous, (what, amb.mean())
+    assert_nvfp4_blocks(got_packed, got_sf_lin, rp, rs, ~amb, what)

@@ -8,7 +8,8 @@ its own: exact C -> bf16 -> gelu (fp64, one rounding to bf16) -> nvfp4 quantize.
 uses the hardware exp2 and reciprocal (a few fp32 ulps), so a value whose fp64 GELU lies within
 2^-20 (relative) of a bf16 rounding boundary may round the other way; the 16-element blocks holding
 such a value are compared loosely (scale code within one step, element codes within one e2m1
-step), every other block bit for bit, and the padding scale rows must be zero.
+step), every other block bit for bit (gpu_util.assert_nvfp4_of_gelu), and the padding scale rows
+must be zero.
 
 Against the two-kernel path (bsp_mm_fp4 to bf16, then bsp_nvfp4_quantize_gelu), on general
 operands including subnormal scales and at the full Wan-14B fc_in size: the same bytes.
@@ -19,9 +20,8 @@ import torch
 
 import block_scaled_precision_nvfp4_amd as bsp
 from oracle import activations as A
-from oracle import formats as F
 from oracle import nvfp4 as N
-from tests.gpu_util import dev_bf16, dev_u8, host_u8, say, scalar, tensor_bits
+from tests.gpu_util import assert_nvfp4_of_gelu, dev_bf16, dev_u8, host_u8, say, scalar, tensor_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -46,22 +46,6 @@ def _general_operand(rng, rows, k):
     return packed, N.swizzle_128x4(lin)
 
 
-def _ambiguous_gelu(y_bits):
-    """Elements whose bf16 GELU could round either way under a relative error of 2^-20 (about 8
-    fp32 ulps; about one element in 2^11 lies that close to a bf16 rounding boundary)."""
-    y = (y_bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
-    g = A.gelu_tanh(y)
-    eps = 2.0 ** -20
-    lo = A.f64_to_bf16_bits(g * (1 - eps))
-    hi = A.f64_to_bf16_bits(g * (1 + eps))
-    return lo != hi
-
-
-def _codes(packed):
-    """[M, K/2] packed bytes -> [M, K] e2m1 codes (low nibble first)."""
-    return np.stack([packed & 0xF, packed >> 4], axis=-1).reshape(packed.shape[0], -1)
-
-
 @pytest.mark.parametrize("m,n,k,gsf", [(1, 128, 64, 1.0), (77, 384, 256, 1.0), (300, 256, 512, 0.75),
                                        (129, 640, 1024, 3.0), (256, 512, 128, 1.0)])
 def test_gelu_nvfp4_epilogue_matches_oracle_on_exact_products(m, n, k, gsf):
@@ -72,31 +56,16 @@ def test_gelu_nvfp4_epilogue_matches_oracle_on_exact_products(m, n, k, gsf):
     al = np.float32(2.0 ** -9)
     # every product has at most 4 significant bits above 2^-4 and |C| * 2^9 <= 144 k < 2^18: the
     # fp32 sums are exact whatever their order
-    y = N.mm_fp4(pa, sa, pb, sb, al, m, n, k)
-    yb = A.f64_to_bf16_bits(y)
-    hb = A.gelu_tanh_bf16_bits(yb)
-    rp, rs = N.quantize(hb, np.float32(gsf))
+    yb = A.f64_to_bf16_bits(N.mm_fp4(pa, sa, pb, sb, al, m, n, k))
 
     p, s = bsp.bsp_mm_fp4_gelu_nvfp4(dev_u8(pa), dev_u8(sa), dev_u8(pb), dev_u8(sb), scalar(al),
                                      scalar(gsf))
-    gp, gs = host_u8(p), host_u8(s).ravel()
-    assert gp.shape == (m, n // 2) and gs.size == rs.size
-
     rp_, cp_ = N.sf_padded_shape(m, n)
-    g_lin, r_lin = N.unswizzle_128x4(gs, rp_, cp_), N.unswizzle_128x4(rs, rp_, cp_)
-    assert not g_lin[m:].any(), "padding scale rows must be zero"
-    amb = _ambiguous_gelu(yb).reshape(m, n // 16, 16).any(axis=-1)          # [m, n/16] blocks
-    assert amb.mean() < 0.03, amb.mean()     # about 16 / 2^11 of the blocks
-    gc, rc = _codes(gp).reshape(m, n // 16, 16), _codes(rp).reshape(m, n // 16, 16)
-    exact = ~amb
-    assert np.array_equal(g_lin[:m, : n // 16][exact], r_lin[:m, : n // 16][exact])
-    assert np.array_equal(gc[exact], rc[exact])
-    if amb.any():
-        # a one-ulp change of one value moves its block's scale code by at most one and each
-        # element code by at most one e2m1 step
-        assert np.all(np.abs(g_lin[:m, : n // 16][amb].astype(int) - r_lin[:m, : n // 16][amb]) <= 1)
-        gv, rv = F.e2m1_decode(gc[amb]), F.e2m1_decode(rc[amb])
-        assert np.all(np.abs(gv - rv) <= 2.0)
+    gp, gs = host_u8(p), host_u8(s).ravel()
+    assert gp.shape == (m, n // 2) and gs.size == rp_ * cp_
+    lin = N.unswizzle_128x4(gs, rp_, cp_)
+    assert not lin[m:].any(), "padding scale rows must be zero"
+    assert_nvfp4_of_gelu(gp, lin, yb, gsf, f"gelu_nvfp4 epilogue {m}x{n}x{k}")
 
 
 @pytest.mark.parametrize("m,n,k", [(1, 128, 64), (77, 384, 192), (300, 256, 512), (513, 640, 256),

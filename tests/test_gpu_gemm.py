@@ -5,6 +5,8 @@ the bf16-rounded reference <= 1e-3 and max |C - ref| <= 8e-3 * max |ref|. Small 
 shapes compare every element; the Wan-shaped configurations run at full size in the bench's
 launch configuration and compare sampled entries (plus corners and ragged tails).
 """
+import functools
+
 import numpy as np
 import pytest
 import torch
@@ -14,8 +16,9 @@ import workloads as W
 from oracle import activations as A
 from oracle import mxfp8 as X
 from oracle import nvfp4 as N
-from tests.gpu_util import (assert_gemm_bf16, assert_gemm_f32, dev_bf16, dev_u8, gather, host_bits,
-                            host_u8, sample_entries, say, scalar, tensor_bits)
+from tests.gpu_util import (assert_gemm_bf16, assert_gemm_f32, assert_nvfp4_blocks, dev_bf16, dev_u8,
+                            gather, host_bits, host_u8, oracle_linear_entries,
+                            oracle_quantize_chunked, sample_entries, say, scalar, tensor_bits)
 
 pytestmark = pytest.mark.gpu
 f32 = np.float32
@@ -25,6 +28,15 @@ def _assert_bf16_is_rne_of_f32(c16, c32):
     """The bf16 epilogue rounds the same fp32 value the fp32 epilogue stores, to nearest even."""
     want = W.f32_to_bf16_bits(c32.cpu().numpy())
     assert np.array_equal(host_bits(c16), want)
+
+
+@functools.lru_cache(maxsize=2)
+def _oracle_weight(cfg, name):
+    """The oracle's (packed, sf, gsf) of a whole generated weight (prequantization)."""
+    wb = tensor_bits(cfg, name)
+    rg = N.global_sf(wb)[0]
+    p, s = oracle_quantize_chunked(wb, rg)
+    return p, s, rg
 
 
 def _rand_nvfp4_operand(rng, rows, k):
@@ -99,59 +111,83 @@ def test_mm_fp4_output_stride_and_tiny_config():
     assert np.linalg.norm(c - full) / np.linalg.norm(full) < 0.15
 
 
-def _linear_full_size(xb_dev, w_bits, name, seed, gsf_x=1.0):
-    """Quantize X (static gsf) and prequantize W on the GPU, GEMM at full size, check sampled
-    entries against the oracle on the GPU's operand bytes (which are themselves checked on
-    sampled rows against the oracle)."""
-    m, k = xb_dev.shape
+def _linear_full_size(x_bits, w_bits, name, seed, gsf_x=1.0):
+    """Quantize X (static gsf) and prequantize W on the GPU, GEMM at full size; the global scale
+    and sampled rows of the quantized activation against the oracle, sampled entries of the GEMM
+    against the oracle's own linear layer on the same bf16 X and W."""
+    m, k = x_bits.shape
     n = w_bits.shape[0]
     w = dev_bf16(w_bits)
     pw, sw, gw, _, _ = bsp.bsp_nvfp4_prequantize_weight(w)
     del w
     gx = scalar(gsf_x)
-    px, sx = bsp.bsp_nvfp4_quantize(xb_dev, gx)
+    px, sx = bsp.bsp_nvfp4_quantize(dev_bf16(x_bits), gx)
     alpha = bsp.bsp_nvfp4_alpha(gx, gw)
     c = bsp.bsp_mm_fp4(px, sx, pw, sw, alpha)
     torch.cuda.synchronize()
     rows, cols = sample_entries(m, n, 3000, seed)
     got = gather(c, rows, cols)
-    pxh, sxh, pwh, swh = host_u8(px), host_u8(sx).ravel(), host_u8(pw), host_u8(sw).ravel()
-    rg = N.global_sf(w_bits)[0]
-    assert gw.item() == rg
+    assert gw.item() == N.global_sf(w_bits)[0]
     ur = np.unique(rows)
-    xrows = host_bits(xb_dev[torch.from_numpy(ur).cuda()])
-    rp, _ = N.quantize(xrows, f32(gsf_x), layout="linear")
-    assert np.array_equal(pxh[ur], rp), "activation bytes differ from the oracle"
-    ref = N.mm_fp4_entries(pxh, sxh, pwh, swh, N.alpha(gsf_x, rg), m, n, k, rows, cols)
-    assert_gemm_bf16(got, ref, name)
+    rp, _ = N.quantize(x_bits[ur], f32(gsf_x), layout="linear")
+    assert np.array_equal(host_u8(px[torch.from_numpy(ur).cuda()]), rp), "activation bytes differ"
+    assert_gemm_bf16(got, oracle_linear_entries(x_bits, w_bits, rows, cols, gsf_x), name)
     return c
 
 
 @pytest.mark.parametrize("cfg", [2, 4])
 def test_mm_fp4_full_size_linear(cfg):
     xb = tensor_bits(cfg, "X")
-    x = dev_bf16(xb)
     wname = "W" if cfg == 2 else "W3"       # cfg 4: to_q 5120x5120
     say("full-size linear cfg", cfg, xb.shape, wname)
-    _linear_full_size(x, tensor_bits(cfg, wname), f"cfg{cfg} {wname}", seed=cfg)
+    _linear_full_size(xb, tensor_bits(cfg, wname), f"cfg{cfg} {wname}", seed=cfg)
 
 
 @pytest.mark.parametrize("cfg", [3, 4])
 def test_ffn_chain_full_size(cfg):
-    """fc_in -> GELU -> quantize H -> fc_out at full size; each stage checked against the oracle
-    applied to the bytes the previous GPU stage produced."""
-    xb = tensor_bits(cfg, "X")
-    say("ffn chain cfg", cfg)
-    y = _linear_full_size(dev_bf16(xb), tensor_bits(cfg, "W"), f"cfg{cfg} fc_in", seed=10 + cfg)
-    h = bsp.bsp_gelu_tanh_bf16(y)
-    rows = np.unique(np.random.default_rng(cfg).integers(0, y.shape[0], 16))
-    ri = torch.from_numpy(rows).cuda()
-    yh, hh = host_bits(y[ri]), host_bits(h[ri])
-    ref_h = A.gelu_tanh_bf16_bits(yh)
-    gv, rv = W.bf16_bits_to_f32(hh).astype(np.float64), W.bf16_bits_to_f32(ref_h).astype(np.float64)
-    assert np.all(np.abs(gv - rv) <= np.abs(rv) * 2.0 ** -7 + 2.0 ** -126)
+    """The FFN step at full size, X -> quantize -> fc_in -> GELU fused into the quantize of H ->
+    fc_out, against the oracle's own chain from the same bf16 X, W, W2 on sampled token rows
+    (whole rows: fc_out needs all of H's row): H's quantized bytes (GELU-ambiguous blocks aside)
+    and the layer output."""
+    xb, w1b, w2b = tensor_bits(cfg, "X"), tensor_bits(cfg, "W"), tensor_bits(cfg, "W2")
+    m, k1, n1, n2 = xb.shape[0], xb.shape[1], w1b.shape[0], w2b.shape[0]
+    say("ffn chain cfg", cfg, xb.shape, w1b.shape, w2b.shape)
+    one = scalar(1.0)
+    px, sx = bsp.bsp_nvfp4_quantize(dev_bf16(xb), one)
+    pw1, sw1, g1, _, _ = bsp.bsp_nvfp4_prequantize_weight(dev_bf16(w1b))
+    pw2, sw2, g2, _, _ = bsp.bsp_nvfp4_prequantize_weight(dev_bf16(w2b))
+    y = bsp.bsp_mm_fp4(px, sx, pw1, sw1, bsp.bsp_nvfp4_alpha(one, g1))
+    ph, sh = bsp.bsp_nvfp4_quantize_gelu(y, one)
     del y
-    _linear_full_size(h, tensor_bits(cfg, "W2"), f"cfg{cfg} fc_out", seed=20 + cfg)
+    out = bsp.bsp_mm_fp4(ph, sh, pw2, sw2, bsp.bsp_nvfp4_alpha(one, g2))
+    torch.cuda.synchronize()
+
+    rows = np.unique(np.concatenate([np.random.default_rng(cfg).integers(0, m, 12), [0, m - 1]]))
+    r = len(rows)
+    say("oracle chain: quantize W")
+    rpw1, rsw1, rg1 = _oracle_weight(cfg, "W")
+    rg2 = N.global_sf(w2b)[0]
+    assert g1.item() == rg1 and g2.item() == rg2
+    rpx, rsx = N.quantize(xb[rows], f32(1.0))
+    say("oracle chain: fc_in rows")
+    y_ref = N.mm_fp4(rpx, rsx, rpw1, rsw1, N.alpha(1.0, rg1), r, n1, k1)       # [r, n1] exact
+    hb_ref = A.gelu_tanh_bf16_bits(A.f64_to_bf16_bits(y_ref))
+    ri = torch.from_numpy(rows).cuda()
+    # H: the GPU's fc_in sums in fp32, so a value next to a bf16 rounding boundary may round the
+    # other way before the GELU; blocks may differ by one step, and only rarely
+    rp_, cp_ = N.sf_padded_shape(m, n1)
+    sh_lin = N.unswizzle_128x4(host_u8(sh).ravel(), rp_, cp_)
+    rphl, rshl = N.quantize(hb_ref, f32(1.0), layout="linear")
+    nexact = np.zeros((r, n1 // 16), dtype=bool)
+    frac = assert_nvfp4_blocks(host_u8(ph[ri]), sh_lin[rows], rphl, rshl, nexact, f"cfg{cfg} H")
+    say(f"cfg{cfg} H blocks differing from the oracle chain:", frac)
+    assert frac < 0.02
+    cols = np.arange(0, n2, max(1, n2 // 512))
+    rph, rsh = N.quantize(hb_ref, f32(1.0))
+    rpw2, rsw2 = N.quantize(w2b[cols], rg2)
+    ref = N.mm_fp4(rph, rsh, rpw2, rsw2, N.alpha(1.0, rg2), r, len(cols), n1)
+    got = out[ri][:, torch.from_numpy(cols).cuda()].float().cpu().numpy().astype(np.float64)
+    assert_gemm_bf16(got, ref, f"cfg{cfg} fc_out")
 
 
 def test_mm_fp4_full_size_fp32_output():
@@ -162,9 +198,7 @@ def test_mm_fp4_full_size_fp32_output():
     alpha = bsp.bsp_nvfp4_alpha(scalar(1.0), gw)
     c = bsp.bsp_mm_fp4(px, sx, pw, sw, alpha, out_dtype=torch.float32)
     rows, cols = sample_entries(xb.shape[0], wb.shape[0], 3000, 99)
-    ref = N.mm_fp4_entries(host_u8(px), host_u8(sx).ravel(), host_u8(pw), host_u8(sw).ravel(),
-                           alpha.item(), xb.shape[0], wb.shape[0], xb.shape[1], rows, cols)
-    assert_gemm_f32(gather(c, rows, cols), ref, "cfg2 fp32")
+    assert_gemm_f32(gather(c, rows, cols), oracle_linear_entries(xb, wb, rows, cols), "cfg2 fp32")
 
 
 # ------------------------------------------------------------------------------ per-token scales
@@ -199,14 +233,17 @@ def test_per_token_linear_full_size():
     pw, sw, gw, _, _ = bsp.bsp_nvfp4_prequantize_weight(dev_bf16(wb))
     c = bsp.bsp_mm_fp4_per_token(px, sx, pw, sw, gx, gw)
     rows, cols = sample_entries(m, n, 3000, 77)
-    ur = np.unique(rows)
-    rq, _, rg = N.quantize_per_token(xb[ur], layout="linear")
-    assert np.array_equal(host_u8(px[torch.from_numpy(ur).cuda()]), rq)
-    g_rows = gx.cpu().numpy()
-    assert np.array_equal(g_rows[ur], rg)
-    base = N.mm_fp4_entries(host_u8(px), host_u8(sx).ravel(), host_u8(pw), host_u8(sw).ravel(),
-                            f32(1.0), m, n, k, rows, cols)
-    ref = base * N.alpha_rows(g_rows[rows], gw.item()).astype(np.float64)
+    ur, ri = np.unique(rows, return_inverse=True)
+    uc, ci = np.unique(cols, return_inverse=True)
+    rq, rs, rg = N.quantize_per_token(xb[ur])
+    rql, _, _ = N.quantize_per_token(xb[ur], layout="linear")
+    assert np.array_equal(host_u8(px[torch.from_numpy(ur).cuda()]), rql)
+    assert np.array_equal(gx.cpu().numpy()[ur], rg)
+    rgw = N.global_sf(wb)[0]
+    assert gw.item() == rgw
+    rpw, rsw = N.quantize(wb[uc], rgw)
+    base = N.mm_fp4_entries(rq, rs, rpw, rsw, f32(1.0), len(ur), len(uc), k, ri, ci)
+    ref = base * N.alpha_rows(rg[ri], rgw).astype(np.float64)
     assert_gemm_bf16(gather(c, rows, cols), ref, "cfg4 to_q per-token")
 
 
@@ -245,8 +282,9 @@ def test_small_m_linear_8x4_chain(m):
     c = bsp.bsp_mm_fp4_8x4(px, sx, pw, sw, alpha, out_dtype=torch.float32)
     rpx, rsx = N.quantize(xb, f32(1.0), layout="8x4")
     assert np.array_equal(host_u8(px), rpx) and np.array_equal(host_u8(sx).ravel(), rsx)
-    ref = N.mm_fp4(rpx, rsx, host_u8(pw), host_u8(sw).ravel(), alpha.item(), m, wb.shape[0],
-                   wb.shape[1], a_layout="8x4")
+    rpw, rsw, rg = _oracle_weight(4, "W")
+    assert gw.item() == rg
+    ref = N.mm_fp4(rpx, rsx, rpw, rsw, N.alpha(1.0, rg), m, wb.shape[0], wb.shape[1], a_layout="8x4")
     assert_gemm_f32(c.cpu().numpy().astype(np.float64), ref, f"small-M 8x4 m={m}")
 
 
@@ -313,10 +351,12 @@ def test_mm_mxfp8_full_size():
     c = bsp.bsp_mm_mxfp8(qx, sx, qw, sw)
     m, n, k = xb.shape[0], wb.shape[0], xb.shape[1]
     rows, cols = sample_entries(m, n, 3000, 5)
-    ur = np.unique(rows)
+    ur, ri = np.unique(rows, return_inverse=True)
+    uc, ci = np.unique(cols, return_inverse=True)
     rq, rs = X.quantize(xb[ur])
     assert np.array_equal(host_u8(qx[torch.from_numpy(ur).cuda()]), rq)
-    ref = X.mm_mxfp8_entries(host_u8(qx), host_u8(sx), host_u8(qw), host_u8(sw), rows, cols)
+    rqw, rsw = X.quantize(wb[uc])
+    ref = X.mm_mxfp8_entries(rq, rs, rqw, rsw, ri, ci)
     assert_gemm_bf16(gather(c, rows, cols), ref, "cfg5 mxfp8")
 
 
@@ -360,11 +400,13 @@ def test_mm_mxfp4_full_size():
     c = bsp.bsp_mm_mxfp4(px, sx, pw, sw)
     m, n, k = xb.shape[0], wb.shape[0], xb.shape[1]
     rows, cols = sample_entries(m, n, 3000, 41)
-    ur = np.unique(rows)
+    ur, ri = np.unique(rows, return_inverse=True)
+    uc, ci = np.unique(cols, return_inverse=True)
     rp, _ = X4.quantize(xb[ur], layout="linear")
     assert np.array_equal(host_u8(px[torch.from_numpy(ur).cuda()]), rp)
-    ref = X4.mm_mxfp4_entries(host_u8(px), host_u8(sx).ravel(), host_u8(pw), host_u8(sw).ravel(), 1.0,
-                              m, n, k, rows, cols)
+    rpx, rsx = X4.quantize(xb[ur])
+    rpw, rsw = X4.quantize(wb[uc])
+    ref = X4.mm_mxfp4_entries(rpx, rsx, rpw, rsw, 1.0, len(ur), len(uc), k, ri, ci)
     assert_gemm_bf16(gather(c, rows, cols), ref, "cfg4 fc_in mxfp4")
 
 
@@ -385,9 +427,9 @@ def _rand_bias(rng, n, scale):
 
 @pytest.mark.parametrize("m,n,k", [(1, 64, 64), (77, 200, 192), (256, 256, 512), (300, 130, 128)])
 def test_mm_fp4_bias_random(m, n, k):
-    """bsp_mm_fp4_bias = the bf16 output of bsp_mm_fp4 plus the bf16 bias (bit-exact, the pages'
-    out + bias), and within the GEMM tolerance of the oracle's exact product plus bias."""
-    from oracle import linear as L
+    """bsp_mm_fp4_bias = the bf16 output of bsp_mm_fp4 plus the bf16 bias (bit-exact against
+    torch's bf16 add of the two, the pages' out + bias), and within the GEMM tolerance of the
+    oracle's exact product plus bias."""
     say("mm_fp4_bias random", m, n, k)
     rng = np.random.default_rng(m * 11 + n + k)
     pa, sa = _rand_nvfp4_operand(rng, m, k)
@@ -399,7 +441,7 @@ def test_mm_fp4_bias_random(m, n, k):
     bias = dev_bf16(bbits)
     t16 = bsp.bsp_mm_fp4(*args)
     tb16 = bsp.bsp_mm_fp4_bias(*args, bias)
-    assert np.array_equal(host_bits(tb16), L.add_bias_bf16(host_bits(t16), bbits))
+    assert torch.equal(tb16.view(torch.int16), (t16.float() + bias.float()).bfloat16().view(torch.int16))
     assert_gemm_bf16(tb16.float().cpu().numpy().astype(np.float64), _ref_plus_bias_bf16(ref, bbits),
                      f"bias {m}x{n}x{k}")
     t32 = bsp.bsp_mm_fp4(*args, out_dtype=torch.float32)
@@ -422,8 +464,7 @@ def test_mm_fp4_bias_full_size_fc_in():
     cb = bsp.bsp_mm_fp4_bias(px, sx, pw, sw, alpha, bias)
     assert torch.equal(cb.view(torch.int16), (c.float() + bias.float()).bfloat16().view(torch.int16))
     rows, cols = sample_entries(m, n, 2000, 404)
-    ref = N.mm_fp4_entries(host_u8(px), host_u8(sx).ravel(), host_u8(pw), host_u8(sw).ravel(),
-                           float(alpha.item()), m, n, k, rows, cols)
+    ref = oracle_linear_entries(hb, wb, rows, cols)
     assert_gemm_bf16(gather(cb, rows, cols), _ref_plus_bias_bf16(ref, bbits[cols]), "cfg4 fc_in + bias")
 
 
@@ -464,7 +505,7 @@ def test_mm_mxfp4_bias_random(m, n, k):
     bias = dev_bf16(bbits)
     t16 = bsp.bsp_mm_mxfp4(*args, scalar(al))
     tb16 = bsp.bsp_mm_mxfp4_bias(*args, bias, scalar(al))
-    assert np.array_equal(host_bits(tb16), L.add_bias_bf16(host_bits(t16), bbits))
+    assert torch.equal(tb16.view(torch.int16), (t16.float() + bias.float()).bfloat16().view(torch.int16))
     assert_gemm_bf16(tb16.float().cpu().numpy().astype(np.float64), _ref_plus_bias_bf16(ref, bbits),
                      f"mxfp4 bias {m}x{n}x{k}")
 
