@@ -144,13 +144,67 @@ __device__ __forceinline__ float gelu_tanh(float x) {
   return ((x * m) * r) * sc;
 }
 
-// 8 values -> gelu, each rounded to bf16 and widened back to fp32 (what the GELU kernel stores)
-__device__ __forceinline__ void gelu8_bf16(float (&f)[8]) {
+// GELU of bf16 values by table. A bf16 input has 2^16 values, so gelu rounded to bf16 is a
+// function of 16 bits; a workgroup tabulates it in LDS (with gelu_tanh itself, so the table holds
+// exactly what the arithmetic gives) for |x| in [2^-12, 2^6) -- 18 binades x 128 mantissas x 2
+// signs, 9 KB -- which holds nearly all activations of a linear layer. Lookups replace a dozen
+// VALU instructions and two quarter-rate transcendentals per value with about six instructions
+// and an LDS read; values outside the table (zeros, tiny or huge magnitudes, inf, NaN) take
+// gelu_tanh itself.
+constexpr int kGeluTabE0 = 115;                    // bf16 exponent field of 2^-12
+constexpr int kGeluTabHalf = 18 * 128;             // entries per sign
+constexpr int kGeluTabSize = 2 * kGeluTabHalf;     // uint16 entries
+
+__device__ __forceinline__ void gelu_table_fill(uint16_t* tab, int t, int nt) {
+  for (int i = t; i < kGeluTabSize; i += nt) {
+    const uint32_t s = i >= kGeluTabHalf ? 1u : 0u;
+    const uint32_t b = (s << 15) + (kGeluTabE0 << 7) + (uint32_t)i - s * kGeluTabHalf;
+    tab[i] = (uint16_t)bf16x2_rne(gelu_tanh(__uint_as_float(b << 16)), 0.0f);
+  }
+}
+
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+
+// gelu of the two bf16 values in w (bits 0-15 and 16-31) from the table; sets bits of miss when
+// either lies outside it (its result is then meaningless)
+__device__ __forceinline__ uint32_t gelu2_tab(uint32_t w, const uint16_t* tab, uint32_t& miss) {
+  const u16x2_t mag = __builtin_bit_cast(u16x2_t, w & 0x7FFF7FFFu);
+  const u16x2_t d = mag - (u16x2_t){kGeluTabE0 << 7, kGeluTabE0 << 7};   // wraps below the table
+  const u16x2_t c = __builtin_elementwise_min(d, (u16x2_t){kGeluTabHalf - 1, kGeluTabHalf - 1});
+  const uint32_t c32 = __builtin_bit_cast(uint32_t, c);
+  miss |= c32 ^ __builtin_bit_cast(uint32_t, d);
+  const uint32_t idx = ((w >> 15) & 0x10001u) * kGeluTabHalf + c32;      // sign picks the half
+  return (uint32_t)tab[idx & 0xFFFFu] | ((uint32_t)tab[idx >> 16] << 16);
+}
+
+// gelu of 8 bf16 values, rounded to bf16, by the arithmetic (what the table holds)
+__device__ __forceinline__ uint4 gelu8_bf16_arith(const uint4& v) {
+  return make_uint4(bf16x2_rne(gelu_tanh(bf16_lo(v.x)), gelu_tanh(bf16_hi(v.x))),
+                    bf16x2_rne(gelu_tanh(bf16_lo(v.y)), gelu_tanh(bf16_hi(v.y))),
+                    bf16x2_rne(gelu_tanh(bf16_lo(v.z)), gelu_tanh(bf16_hi(v.z))),
+                    bf16x2_rne(gelu_tanh(bf16_lo(v.w)), gelu_tanh(bf16_hi(v.w))));
+}
+
+// gelu (bf16 in, bf16 out) of NSEG segments of 8 values: all by table first, then one branch,
+// rarely taken, that recomputes the segments holding a value outside the table. Keeping the
+// common path free of branches lets the LDS latencies of all segments overlap.
+template <int NSEG>
+__device__ __forceinline__ void gelu_segments_tab(const uint4 (&in)[NSEG], uint4 (&out)[NSEG],
+                                                  const uint16_t* tab) {
+  uint32_t missbits = 0;
 #pragma unroll
-  for (int i = 0; i < 8; i += 2) {
-    const uint32_t p = bf16x2_rne(gelu_tanh(f[i]), gelu_tanh(f[i + 1]));
-    f[i] = bf16_lo(p);
-    f[i + 1] = bf16_hi(p);
+  for (int i = 0; i < NSEG; ++i) {
+    uint32_t m = 0;
+    out[i].x = gelu2_tab(in[i].x, tab, m);
+    out[i].y = gelu2_tab(in[i].y, tab, m);
+    out[i].z = gelu2_tab(in[i].z, tab, m);
+    out[i].w = gelu2_tab(in[i].w, tab, m);
+    missbits |= (m != 0 ? 1u : 0u) << i;
+  }
+  if (missbits) {
+#pragma unroll
+    for (int i = 0; i < NSEG; ++i)
+      if ((missbits >> i) & 1u) out[i] = gelu8_bf16_arith(in[i]);
   }
 }
 

@@ -221,12 +221,51 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], const floa
 // segment (8 values, half a 16-value block, the other half in the neighbouring lane), encodes it
 // and writes 4 bytes; the scale bytes gather in a 1 KB image of the wave's two 512-byte scale
 // tiles, stored whole at the end. rtab[c] = fl32(g / e4m3(c)) for the 127 scale codes.
+// One 64-row half of the GELU + NVFP4 wave epilogue, from its bf16 image in `lds`. ROWS_IN: all
+// 64 rows lie below M (no per-row checks, so that the loop has no branches and the LDS latencies
+// of its iterations overlap).
+template <bool ROWS_IN>
+__device__ __forceinline__ void gelu_nvfp4_half(const uint8_t* lds, int half, int64_t m0w,
+                                                int64_t n0w, int64_t M, int64_t half_n,
+                                                uint8_t* packed, float g, const float* rtab,
+                                                const uint16_t* gtab, uint8_t* sfimg, int lane) {
+  const int c16 = lane & 15;
+  uint4 seg[16], gv[16];
+#pragma unroll
+  for (int it = 0; it < 16; ++it) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(lds + (it * 4 + (lane >> 4)) * kEpiRowBytes + c16 * 16);
+    seg[it] = make_uint4(v.x, v.y, v.z, v.w);
+  }
+  gelu_segments_tab(seg, gv, gtab);
+#pragma unroll
+  for (int it = 0; it < 16; ++it) {
+    const int rr = half * 64 + it * 4 + (lane >> 4);  // row inside the wave's 128 rows
+    const int64_t gm = m0w + rr;
+    float f[8];
+    unpack8(gv[it], f);
+    const float a = pair_max(absmax8(f));
+    const uint32_t S = (ROWS_IN || gm < M) ? e4m3_encode_pos(g * (a * kSixth)) : 0u;
+    const float r = rtab[S];
+    uint32_t o = 0;
+    o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, f[0] * r, f[1] * r, 1.0f, 0);
+    o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, f[2] * r, f[3] * r, 1.0f, 1);
+    o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, f[4] * r, f[5] * r, 1.0f, 2);
+    o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, f[6] * r, f[7] * r, 1.0f, 3);
+    if (ROWS_IN || gm < M)
+      __builtin_nontemporal_store(o, reinterpret_cast<uint32_t*>(packed + gm * half_n + n0w / 2 + c16 * 4));
+    // both lanes of a block hold its scale code: both store it, to the same byte
+    const int cb = c16 >> 1;  // scale column inside the wave's 8
+    sfimg[(cb >> 2) * 512 + (rr & 31) * 16 + (rr >> 5) * 4 + (cb & 3)] = (uint8_t)S;
+  }
+}
+
 __device__ __forceinline__ void store_wave_tile_gelu_nvfp4(const f32x16 (&acc)[4][4],
                                                            const float (&alpha)[4], int64_t m0w,
                                                            int64_t n0w, int64_t M, int64_t N,
                                                            uint8_t* packed, uint8_t* sf, float g,
-                                                           const float* rtab, uint8_t* lds,
-                                                           uint8_t* sfimg, int lane, int li, int h) {
+                                                           const float* rtab, const uint16_t* gtab,
+                                                           uint8_t* lds, uint8_t* sfimg, int lane,
+                                                           int li, int h) {
   if (n0w >= N) return;
   const float bq[4][4][4] = {};
   const int64_t half_n = N / 2;
@@ -244,38 +283,11 @@ __device__ __forceinline__ void store_wave_tile_gelu_nvfp4(const f32x16 (&acc)[4
               make_uint2(p01, p23);
         }
     }
-    // the same wave reads back what it wrote: LDS executes one wave's operations in order. All
-    // 16 segments are read first so that the GELU chains of all of them can interleave (one wave
-    // per SIMD has no other wave to hide their latency).
-    const int c16 = lane & 15;
-    u32x4 seg[16];
-#pragma unroll
-    for (int it = 0; it < 16; ++it)
-      seg[it] = *reinterpret_cast<const u32x4*>(lds + (it * 4 + (lane >> 4)) * kEpiRowBytes + c16 * 16);
-#pragma unroll
-    for (int it = 0; it < 16; ++it) {
-      const int row = it * 4 + (lane >> 4);
-      const u32x4 v = seg[it];
-      float f[8];
-      unpack8(make_uint4(v.x, v.y, v.z, v.w), f);
-      gelu8_bf16(f);
-      const float a = pair_max(absmax8(f));
-      const int rr = half * 64 + row;  // row inside the wave's 128 rows
-      const int64_t gm = m0w + rr;
-      const uint32_t S = gm < M ? e4m3_encode_pos(g * (a * kSixth)) : 0u;
-      const float r = rtab[S];
-      uint32_t o = 0;
-      o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, f[0] * r, f[1] * r, 1.0f, 0);
-      o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, f[2] * r, f[3] * r, 1.0f, 1);
-      o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, f[4] * r, f[5] * r, 1.0f, 2);
-      o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, f[6] * r, f[7] * r, 1.0f, 3);
-      if (gm < M)
-        __builtin_nontemporal_store(o, reinterpret_cast<uint32_t*>(packed + gm * half_n + n0w / 2 + c16 * 4));
-      if ((c16 & 1) == 0) {
-        const int cb = c16 >> 1;  // scale column inside the wave's 8
-        sfimg[(cb >> 2) * 512 + (rr & 31) * 16 + (rr >> 5) * 4 + (cb & 3)] = (uint8_t)S;
-      }
-    }
+    // the same wave reads back what it wrote: LDS executes one wave's operations in order
+    if (m0w + half * 64 + 64 <= M)
+      gelu_nvfp4_half<true>(lds, half, m0w, n0w, M, half_n, packed, g, rtab, gtab, sfimg, lane);
+    else
+      gelu_nvfp4_half<false>(lds, half, m0w, n0w, M, half_n, packed, g, rtab, gtab, sfimg, lane);
   }
   // the wave's two 512-byte scale tiles: row tile m0w / 128, column groups n0w / 64 and + 1
   if (m0w < M) {
@@ -287,19 +299,22 @@ __device__ __forceinline__ void store_wave_tile_gelu_nvfp4(const f32x16 (&acc)[4
 }
 
 // Workgroup epilogue for the GELU + NVFP4 output. The images overlay the stage memory `lds`
-// (at least 4 * (kEpiWaveBytes + 1024) bytes); rtab is the workgroup's scale-reciprocal table.
+// (at least 4 * (kEpiWaveBytes + 1024) bytes); rtab (128 floats) and gtab (kGeluTabSize) are the
+// workgroup's scale-reciprocal and GELU tables, filled here.
 __device__ __forceinline__ void store_tile_gelu_nvfp4(const f32x16 (&acc)[4][4],
                                                       const float (&alpha)[4], int64_t m0,
                                                       int64_t n0, int wm, int wn, int64_t M,
                                                       int64_t N, uint8_t* packed, uint8_t* sf,
-                                                      const float* gsf, float* rtab, uint8_t* lds,
-                                                      int t, int wave, int lane, int li, int h) {
+                                                      const float* gsf, float* rtab, uint16_t* gtab,
+                                                      uint8_t* lds, int t, int wave, int lane,
+                                                      int li, int h) {
   const float g = *gsf;
   if (t < 128) rtab[t] = (t == 0 || t > 0x7E) ? 0.0f : g / e4m3_decode_pos((uint32_t)t);
-  __syncthreads();   // rtab; every wave is done reading the stage buffers the images overlay
+  gelu_table_fill(gtab, t, 256);
+  __syncthreads();   // the tables; every wave is done reading the stage buffers the images overlay
   store_wave_tile_gelu_nvfp4(acc, alpha, m0 + wm * 128, n0 + wn * 128, M, N, packed, sf, g, rtab,
-                             lds + wave * kEpiWaveBytes, lds + 4 * kEpiWaveBytes + wave * 1024, lane,
-                             li, h);
+                             gtab, lds + wave * kEpiWaveBytes, lds + 4 * kEpiWaveBytes + wave * 1024,
+                             lane, li, h);
 }
 
 }  // namespace bsp

@@ -263,6 +263,7 @@ __global__ __launch_bounds__(256, 1) void mm_fp4_kernel(
     uint8_t* __restrict__ sf_out, const float* __restrict__ out_gsf) {
   __shared__ Stage st[NSTAGE];
   __shared__ float rtab[BIAS == kGeluNvfp4 ? 128 : 1];
+  __shared__ uint16_t gtab[BIAS == kGeluNvfp4 ? kGeluTabSize : 1];
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -405,9 +406,9 @@ __global__ __launch_bounds__(256, 1) void mm_fp4_kernel(
   static_assert(sizeof(st) >= 4 * (kEpiWaveBytes + 1024), "epilogue images overlay the stage buffers");
   if constexpr (BIAS == kGeluNvfp4) {
     store_tile_gelu_nvfp4(acc, alpha, m0, n0, wm, wn, M, N, static_cast<uint8_t*>(out), sf_out,
-                          out_gsf, rtab, reinterpret_cast<uint8_t*>(st), t, wave, lane, li, h);
+                          out_gsf, rtab, gtab, reinterpret_cast<uint8_t*>(st), t, wave, lane, li, h);
   } else {
-    (void)rtab; (void)sf_out; (void)out_gsf;
+    (void)rtab; (void)gtab; (void)sf_out; (void)out_gsf;
     store_tile<OUT_F32, BIAS>(acc, alpha, m0, n0, wm, wn, M, N, out, ldc, vec_store,
                               reinterpret_cast<uint8_t*>(st), wave, lane, li, h, bias);
   }

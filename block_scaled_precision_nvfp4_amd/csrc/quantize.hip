@@ -1,6 +1,6 @@
 // HBM-bound kernels of the NVFP4 / MXFP8 linear layer on gfx950:
-//   a1 weight global scale (amax reduction + scalar finish), a2 NVFP4 quantize, a3 alpha,
-//   a6 MXFP8 quantize, and the bf16 GELU between the FFN projections.
+//   the weight global scale (amax reduction + scalar finish), NVFP4 quantize, alpha,
+//   MXFP8 quantize, and the bf16 GELU between the FFN projections.
 //
 // Pages (by title, section): FastVideo nvfp4_qat_config.py (convert_model_to_fp4, apply),
 // FastVideo nvfp4_config.py (module docstring, _nvfp4_quantize and its shape kernel,
@@ -135,6 +135,7 @@ __global__ __launch_bounds__(256) void nvfp4_quantize_kernel(const uint16_t* __r
                                                              int64_t rows8) {
   __shared__ uint4 sf_tile[128];  // 2 KB = 4 scale tiles of 512 B
   __shared__ float rtab[128];     // fl32(g / e4m3(c)) for code c (0 for c == 0)
+  __shared__ uint16_t gtab[GELU ? kGeluTabSize : 1];
   uint8_t* sfb = reinterpret_cast<uint8_t*>(sf_tile);
   const int t = threadIdx.x;
   const int64_t row0 = (int64_t)blockIdx.y * 128;
@@ -156,7 +157,8 @@ __global__ __launch_bounds__(256) void nvfp4_quantize_kernel(const uint16_t* __r
     for (int s = 0; s < 16; ++s)
       v[s] = (kin && row0 + s * 8 + rsub < M) ? load8<VEC>(xp + s * xstep) : make_uint4(0u, 0u, 0u, 0u);
   }
-  __syncthreads();  // rtab
+  if (GELU) gelu_table_fill(gtab, t, 256);   // while the loads are in flight
+  __syncthreads();  // rtab, gtab
 
   const int64_t half_k = K / 2;
   uint8_t* pp = packed + (row0 + rsub) * half_k + kk / 2;
@@ -164,8 +166,13 @@ __global__ __launch_bounds__(256) void nvfp4_quantize_kernel(const uint16_t* __r
 #pragma unroll
   for (int s = 0; s < 16; ++s) {
     float f[8];
-    unpack8(v[s], f);
-    if (GELU) gelu8_bf16(f);  // gelu(0) = 0 keeps the padding zero
+    if (GELU) {  // gelu(0) = 0 keeps the padding zero
+      uint4 gv[1];
+      gelu_segments_tab<1>({v[s]}, gv, gtab);
+      unpack8(gv[0], f);
+    } else {
+      unpack8(v[s], f);
+    }
     const float a = pair_max(absmax8(f));
     const float sc = g * (a * kSixth);
     const uint32_t S = e4m3_encode_pos(sc);

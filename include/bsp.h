@@ -72,8 +72,8 @@ int bsp_nvfp4_global_sf(const void* w_bf16, int64_t rows, int64_t K, int64_t ld,
 int bsp_nvfp4_quantize(const void* x_bf16, int64_t M, int64_t K, int64_t ld, const float* gsf_dev,
                        uint8_t* packed, uint8_t* sf, void* stream);
 
-/* Load-time weight prequantization: a1 then a2 on W [N, K] ([FV-QAT] convert_model_to_fp4,
- * [FV-NV] convert_model_to_nvfp4). Outputs as for the two calls above (gsf_dev, inv_gsf_dev and
+/* Load-time weight prequantization: the global scale, then the NVFP4 quantize, of W [N, K]
+ * ([FV-QAT] convert_model_to_fp4, [FV-NV] convert_model_to_nvfp4). Outputs as for the two calls above (gsf_dev, inv_gsf_dev and
  * amax_dev are all required device fp32 slots; the quantize step reads *gsf_dev on the device, so
  * nothing is synchronised). The caller may free W once the stream has passed this call. */
 int bsp_nvfp4_prequantize_weight(const void* w_bf16, int64_t N, int64_t K, int64_t ld,

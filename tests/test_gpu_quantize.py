@@ -1,7 +1,7 @@
 """GPU parity of the HBM-bound kernels against the oracle: bit-exact bytes and scalars.
 
-a1 global scale, a2 NVFP4 quantize (packed nibbles + 128x4 scale bytes, padding included),
-a3 alpha, a6 MXFP8 quantize, and the GELU between the FFN projections (within one bf16 ulp).
+the global scale, NVFP4 quantize (packed nibbles + 128x4 scale bytes, padding included),
+alpha, MXFP8 quantize, and the GELU between the FFN projections (within one bf16 ulp).
 """
 import numpy as np
 import pytest

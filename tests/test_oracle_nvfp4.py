@@ -17,7 +17,7 @@ def bits(vals):
     return W.f32_to_bf16_bits(np.asarray(vals, dtype=np.float32))
 
 
-# ---------------------------------------------------------------------------------- a2 blocks
+# ------------------------------------------------------------------------------------- blocks
 def test_hand_worked_blocks():
     for line in golden_lines("nvfp4_blocks.txt"):
         head, s_hex, packed_hex = (p.split() for p in line.split("|"))
@@ -287,7 +287,7 @@ def test_k_must_be_multiple_of_16():
         N.quantize(np.zeros((2, 24), dtype=np.uint16), f32(1.0))
 
 
-# ------------------------------------------------------------------- f3 per-token activation scales
+# ---------------------------------------------------------------------- per-token activation scales
 def test_per_token_is_scale_invariant_row_by_row():
     """Rows that are power-of-two multiples of one row quantize to identical codes and scale bytes,
     and their per-row encode scales differ by exactly that power of two: the scale is per row (a
@@ -365,7 +365,7 @@ def test_per_token_linear_approximates_the_bf16_product():
     assert np.linalg.norm(c - full) / np.linalg.norm(full) < 0.15
 
 
-# ------------------------------------------------------------- f4 layout_8x4 and the 4over6 scale
+# ---------------------------------------------------------------- layout_8x4 and the 4over6 scale
 def test_sf_offsets_8x4_golden():
     for line in golden_lines("sf_offsets_8x4.txt"):
         r, c, off = (int(v) for v in line.split())
