@@ -451,18 +451,17 @@ __global__ __launch_bounds__(256) void mxfp4_quantize_kernel(const uint16_t* __r
 // =============================================================================================
 // GELU (tanh form), bf16 in/out
 // =============================================================================================
-__global__ __launch_bounds__(256) void gelu_kernel(const uint16_t* __restrict__ x,
-                                                   uint16_t* __restrict__ y, int64_t n) {
+// Grid-stride over 8-value segments, GELU by the workgroup's LDS table (gelu_segments_tab).
+__global__ __launch_bounds__(256) void gelu_kernel(const uint16_t* x, uint16_t* y, int64_t n) {
+  __shared__ uint16_t gtab[kGeluTabSize];
+  gelu_table_fill(gtab, threadIdx.x, 256);
+  __syncthreads();
   const int64_t n8 = n / 8;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8;
        i += (int64_t)gridDim.x * blockDim.x) {
-    uint4 v = load16_nt(reinterpret_cast<const uint4*>(x) + i);
-    uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      w[j] = bf16x2_rne(gelu_tanh(bf16_lo(w[j])), gelu_tanh(bf16_hi(w[j])));
-    }
-    __builtin_nontemporal_store((nt_u32x4){w[0], w[1], w[2], w[3]}, reinterpret_cast<nt_u32x4*>(y) + i);
+    uint4 v[1] = {load16_nt(reinterpret_cast<const uint4*>(x) + i)}, w[1];
+    gelu_segments_tab(v, w, gtab);
+    __builtin_nontemporal_store((nt_u32x4){w[0].x, w[0].y, w[0].z, w[0].w}, reinterpret_cast<nt_u32x4*>(y) + i);
   }
   // tail (n % 8 elements)
   int64_t i = n8 * 8 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
