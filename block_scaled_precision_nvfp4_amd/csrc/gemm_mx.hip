@@ -482,7 +482,7 @@ static int mx_checks(const char* fn, const uint8_t* a, const uint8_t* a_sf, cons
 extern "C" int bsp_mm_mxfp8(const uint8_t* a, const uint8_t* a_sf, const uint8_t* b,
                             const uint8_t* b_sf, int64_t M, int64_t N, int64_t K, void* out,
                             int64_t ldc, int out_dtype, void* stream) {
-  int e = mx_checks("bsp_mm_mxfp8", a, a_sf, b, b_sf, M, N, K, out, ldc, out_dtype, 128, 2);
+  int e = mx_checks("bsp_mm_mxfp8", a, a_sf, b, b_sf, M, N, K, out, ldc, out_dtype, 128, 4);
   if (e) return e > 0 ? BSP_OK : e;
   return mx::launch<0>(a, a_sf, b, b_sf, nullptr, M, N, K, out, ldc, out_dtype, (hipStream_t)stream,
                        "bsp_mm_mxfp8");
@@ -500,7 +500,7 @@ extern "C" int bsp_mm_mxfp4(const uint8_t* a, const uint8_t* a_sf, const uint8_t
 extern "C" int bsp_mm_mxfp8_bias(const uint8_t* a, const uint8_t* a_sf, const uint8_t* b,
                                  const uint8_t* b_sf, const float* bias_f32, int64_t M, int64_t N,
                                  int64_t K, void* out, int64_t ldc, int out_dtype, void* stream) {
-  int e = mx_checks("bsp_mm_mxfp8_bias", a, a_sf, b, b_sf, M, N, K, out, ldc, out_dtype, 128, 2,
+  int e = mx_checks("bsp_mm_mxfp8_bias", a, a_sf, b, b_sf, M, N, K, out, ldc, out_dtype, 128, 4,
                     bias_f32, 4);
   if (e) return e > 0 ? BSP_OK : e;
   return mx::launch<0, kBiasF32Before>(a, a_sf, b, b_sf, nullptr, M, N, K, out, ldc, out_dtype,

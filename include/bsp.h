@@ -110,7 +110,9 @@ int bsp_mxfp8_quantize(const void* x_bf16, int64_t M, int64_t K, int64_t ld, uin
  * fp32 accumulation, bf16 or fp32 output ([VLO] NPUMxfp8LinearMethod._quant_matmul: per-row e8m0
  * scales of both operands, group [1, 1, 32], output in the activation dtype).
  * a: [M, K] e4m3, a_sf [M, K/32]; b: [N, K] e4m3 (K-major weight), b_sf [N, K/32]; out [M, N]
- * row stride ldc. Requires K % 128 == 0. */
+ * row stride ldc. Requires K % 128 == 0; operands 16-byte and scales 4-byte aligned (else
+ * BSP_EINVAL). With K % 512 == 0 and both scale matrices 16-byte aligned the kernel fetches the
+ * scales in 512-K row blocks (faster, same results). */
 int bsp_mm_mxfp8(const uint8_t* a, const uint8_t* a_sf, const uint8_t* b, const uint8_t* b_sf,
                  int64_t M, int64_t N, int64_t K, void* out, int64_t ldc, int out_dtype,
                  void* stream);

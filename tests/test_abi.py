@@ -167,3 +167,10 @@ def test_gelu_nvfp4_epilogue_entry_point_errors():
     assert _st("bsp_mm_fp4_gelu_nvfp4", *args, 8, 256, 96, P, P, None)[0] == -2          # K % 64
     assert _st("bsp_mm_fp4_gelu_nvfp4", None, None, None, None, None, None, 0, 256, 128, None, None,
                None)[0] == 0
+
+
+def test_mxfp8_gemm_scale_alignment():
+    """The MXFP8 GEMMs read scale dwords: scale matrices must be 4-byte aligned."""
+    st, msg = _st("bsp_mm_mxfp8", P, ctypes.c_void_p(18), P, P, 8, 8, 128, P, 8, 0, None)
+    assert st == -1 and "4-byte" in msg
+    assert _st("bsp_mm_mxfp8_bias", P, P, P, ctypes.c_void_p(22), P, 8, 8, 128, P, 8, 0, None)[0] == -1
