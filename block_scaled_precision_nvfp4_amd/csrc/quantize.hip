@@ -20,25 +20,55 @@ __device__ __forceinline__ uint32_t mag_nan_to_num(uint32_t b16) {
   return m > 0x7F80u ? 0u : (m == 0x7F80u ? 0x7F7Fu : m);
 }
 
+// The quantizers read each input byte once and write each output byte once: their global loads and
+// stores are nontemporal (they do not displace other data in the caches; measured 20-30 % faster
+// when the caches hold another kernel's dirty output).
+typedef uint32_t nt_u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load16_nt(const void* p) {
+  const nt_u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4*>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+__device__ __forceinline__ void store4_nt(void* p, uint32_t v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p));
+}
+
 __global__ void amax_init_kernel(float* amax) { *reinterpret_cast<uint32_t*>(amax) = 0u; }
 
-template <bool VEC>
+__device__ __forceinline__ uint32_t mag_max8(uint32_t m, const uint4& v) {
+  const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    m = max(m, mag_nan_to_num(q[j] & 0xFFFFu));
+    m = max(m, mag_nan_to_num(q[j] >> 16));
+  }
+  return m;
+}
+
+// MODE 0: contiguous rows (ld == K, K % 8 == 0, 16-byte aligned): the matrix is one run of
+//   16-byte chunks, four loads in flight per thread per step, no index division;
+// MODE 1: strided rows with K % 8 == 0, ld % 8 == 0, 16-byte aligned: workgroups stride over rows,
+//   threads over a row's chunks;
+// MODE 2: anything else, element by element.
+template <int MODE>
 __global__ __launch_bounds__(256) void amax_reduce_kernel(const uint16_t* __restrict__ w, int64_t rows,
                                                           int64_t K, int64_t ld, float* amax) {
   uint32_t m = 0;
-  if (VEC) {  // K % 8 == 0, ld % 8 == 0, 16-byte aligned base
+  if (MODE == 0) {
+    const uint4* c = reinterpret_cast<const uint4*>(w);
+    const int64_t total = rows * (K / 8);
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    // plain (not nontemporal) loads: the quantize that follows at load time reads W again
+    for (; i + 3 * stride < total; i += 4 * stride) {
+      const uint4 v0 = c[i], v1 = c[i + stride], v2 = c[i + 2 * stride], v3 = c[i + 3 * stride];
+      m = mag_max8(mag_max8(mag_max8(mag_max8(m, v0), v1), v2), v3);
+    }
+    for (; i < total; i += stride) m = mag_max8(m, c[i]);
+  } else if (MODE == 1) {
     const int64_t cpr = K / 8;
-    const int64_t total = rows * cpr;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-         i += (int64_t)gridDim.x * blockDim.x) {
-      int64_t r = i / cpr, c = i - r * cpr;
-      uint4 v = *reinterpret_cast<const uint4*>(w + r * ld + c * 8);
-      uint32_t q[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        m = max(m, mag_nan_to_num(q[j] & 0xFFFFu));
-        m = max(m, mag_nan_to_num(q[j] >> 16));
-      }
+    for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+      const uint4* c = reinterpret_cast<const uint4*>(w + r * ld);
+      for (int64_t j = threadIdx.x; j < cpr; j += blockDim.x) m = mag_max8(m, c[j]);
     }
   } else {
     const int64_t total = rows * K;
@@ -103,18 +133,6 @@ __global__ void alpha_kernel(const float* xg, const float* wg, float* alpha) {
 // saturating at +-6, sign of zero kept -- checked against the software encoder on every fp32
 // input class (ties, denormals, huge values) on gfx950; BSP_QUANT_SW_CVT=1 selects that software
 // encoder instead.
-// The quantizers read each input byte once and write each output byte once: their global loads and
-// stores are nontemporal (they do not displace other data in the caches; measured 20-30 % faster
-// when the caches hold another kernel's dirty output).
-typedef uint32_t nt_u32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint4 load16_nt(const void* p) {
-  const nt_u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4*>(p));
-  return make_uint4(t.x, t.y, t.z, t.w);
-}
-__device__ __forceinline__ void store4_nt(void* p, uint32_t v) {
-  __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p));
-}
-
 template <bool VEC>
 __device__ __forceinline__ uint4 load8(const uint16_t* p) {
   if (VEC) return load16_nt(p);
@@ -485,15 +503,21 @@ int launch_global_sf(const void* w, int64_t rows, int64_t K, int64_t ld, float* 
   if (rows > 0 && K > 0) {
     const uint16_t* wp = static_cast<const uint16_t*>(w);
     const bool vec = (K % 8 == 0) && (ld % 8 == 0) && aligned16(w);
-    int64_t work = vec ? rows * (K / 8) : rows * K;
-    int64_t blocks = ceil_div(work, 256);
-    if (blocks > 4096) blocks = 4096;
-    if (vec)
-      hipLaunchKernelGGL(amax_reduce_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, wp, rows,
+    if (vec && (ld == K || rows == 1)) {
+      int64_t blocks = ceil_div(rows * (K / 8), 256 * 4);
+      if (blocks > 2048) blocks = 2048;
+      hipLaunchKernelGGL(amax_reduce_kernel<0>, dim3((unsigned)blocks), dim3(256), 0, s, wp, rows,
+                         K, K, amax);
+    } else if (vec) {
+      const int64_t blocks = rows < 4096 ? rows : 4096;
+      hipLaunchKernelGGL(amax_reduce_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, s, wp, rows,
                          K, ld, amax);
-    else
-      hipLaunchKernelGGL(amax_reduce_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, wp, rows,
+    } else {
+      int64_t blocks = ceil_div(rows * K, 256);
+      if (blocks > 4096) blocks = 4096;
+      hipLaunchKernelGGL(amax_reduce_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, s, wp, rows,
                          K, ld, amax);
+    }
   }
   if (four_over_six)
     hipLaunchKernelGGL(gsf_finish_4over6_kernel, dim3(1), dim3(1), 0, s, amax, gsf, inv);

@@ -178,6 +178,24 @@ def test_global_sf_bit_exact():
         assert got[0] == rg and got[1] == ri and got[2] == ra
 
 
+def test_global_sf_strided_and_tail_positions():
+    """The amax reduction's three paths (contiguous rows, strided rows, unaligned element by
+    element), with the largest magnitude planted at the first, a middle and the last element."""
+    rng = np.random.default_rng(21)
+    for rows, k, ld in [(300, 512, 512), (300, 512, 520), (37, 1000, 1000), (5, 96, 101), (1, 4096, 4096)]:
+        for pos in ("first", "middle", "last"):
+            big = W.small_case(rows, ld, int(rng.integers(1 << 30)), std=0.5)
+            r, c = {"first": (0, 0), "middle": (rows // 2, k // 3), "last": (rows - 1, k - 1)}[pos]
+            big[r, c] = 0xC2F6                                   # -123.0, the largest magnitude
+            big[:, k:] = 0x7F7F                                  # outside the view: must be ignored
+            wb = np.ascontiguousarray(big[:, :k])
+            w = dev_bf16(big)[:, :k]
+            gsf, inv, amax = bsp.bsp_nvfp4_global_sf(w)
+            rg, ri, ra = N.global_sf(wb)
+            assert ra == np.float32(123.0), (rows, k, ld, pos)
+            assert (gsf.item(), inv.item(), amax.item()) == (rg, ri, ra), (rows, k, ld, pos)
+
+
 def test_prequantize_weight_matches_separate_calls_and_oracle():
     for cfg in (1, 2):
         wb = tensor_bits(cfg, "W")
