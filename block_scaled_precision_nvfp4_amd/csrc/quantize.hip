@@ -59,9 +59,12 @@ __global__ __launch_bounds__(256) void amax_reduce_kernel(const uint16_t* __rest
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     // plain (not nontemporal) loads: the quantize that follows at load time reads W again
-    for (; i + 3 * stride < total; i += 4 * stride) {
-      const uint4 v0 = c[i], v1 = c[i + stride], v2 = c[i + 2 * stride], v3 = c[i + 3 * stride];
-      m = mag_max8(mag_max8(mag_max8(mag_max8(m, v0), v1), v2), v3);
+    for (; i + 7 * stride < total; i += 8 * stride) {
+      uint4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = c[i + u * stride];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) m = mag_max8(m, v[u]);
     }
     for (; i < total; i += stride) m = mag_max8(m, c[i]);
   } else if (MODE == 1) {
@@ -504,8 +507,8 @@ int launch_global_sf(const void* w, int64_t rows, int64_t K, int64_t ld, float* 
     const uint16_t* wp = static_cast<const uint16_t*>(w);
     const bool vec = (K % 8 == 0) && (ld % 8 == 0) && aligned16(w);
     if (vec && (ld == K || rows == 1)) {
-      int64_t blocks = ceil_div(rows * (K / 8), 256 * 4);
-      if (blocks > 2048) blocks = 2048;
+      int64_t blocks = ceil_div(rows * (K / 8), 256 * 8);
+      if (blocks > 1024) blocks = 1024;
       hipLaunchKernelGGL(amax_reduce_kernel<0>, dim3((unsigned)blocks), dim3(256), 0, s, wp, rows,
                          K, K, amax);
     } else if (vec) {
