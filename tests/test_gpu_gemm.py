@@ -68,6 +68,33 @@ def test_mm_fp4_random_operands_all_elements(m, n, k):
     assert np.linalg.norm(c32 - ref) <= 1e-5 * np.linalg.norm(ref)
 
 
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp8", "mxfp4"])
+def test_long_k_accumulation(fmt):
+    """K = 2^18 (2048 NVFP4 stages, 4096 MXFP8 stages, 512 MXFP8 scale blocks) with ragged M and N:
+    the long K loop, its 32-bit per-tile load offsets and the fp32 accumulation against the
+    oracle on every element."""
+    from oracle import mxfp4 as X4
+    m, n, k = 130, 70, 1 << 18
+    say("long K", fmt, m, n, k)
+    rng = np.random.default_rng(2718)
+    if fmt == "nvfp4":
+        pa, sa = _rand_nvfp4_operand(rng, m, k)
+        pb, sb = _rand_nvfp4_operand(rng, n, k)
+        ref = N.mm_fp4(pa, sa, pb, sb, f32(0.5), m, n, k)
+        c = bsp.bsp_mm_fp4(dev_u8(pa), dev_u8(sa), dev_u8(pb), dev_u8(sb), scalar(0.5), out_dtype=torch.float32)
+    elif fmt == "mxfp8":
+        qa, sa = _rand_mx_operand(rng, m, k)
+        qb, sb = _rand_mx_operand(rng, n, k)
+        ref = X.mm_mxfp8(qa, sa, qb, sb, m, n, k)
+        c = bsp.bsp_mm_mxfp8(dev_u8(qa), dev_u8(sa), dev_u8(qb), dev_u8(sb), out_dtype=torch.float32)
+    else:
+        pa, sa = _rand_mxfp4_operand(rng, m, k)
+        pb, sb = _rand_mxfp4_operand(rng, n, k)
+        ref = X4.mm_mxfp4(pa, sa, pb, sb, f32(1.0), m, n, k)
+        c = bsp.bsp_mm_mxfp4(dev_u8(pa), dev_u8(sa), dev_u8(pb), dev_u8(sb), None, torch.float32)
+    assert_gemm_f32(c.cpu().numpy().astype(np.float64), ref, f"long K {fmt}")
+
+
 def test_empty_inputs_are_no_ops():
     """M = 0 (no tokens) through every entry point: no launch, empty outputs, no error."""
     x = torch.empty((0, 512), dtype=torch.bfloat16, device="cuda")
