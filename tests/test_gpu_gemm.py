@@ -48,7 +48,7 @@ def _rand_nvfp4_operand(rng, rows, k):
 
 
 @pytest.mark.parametrize("m,n,k", [(1, 64, 64), (77, 200, 192), (256, 256, 512), (300, 384, 128),
-                                   (513, 130, 256), (64, 1000, 64)])
+                                   (513, 130, 256), (64, 1000, 64), (5, 1, 128), (1, 1, 64)])
 def test_mm_fp4_random_operands_all_elements(m, n, k):
     say("mm_fp4 random", m, n, k)
     rng = np.random.default_rng(m * 7 + n * 3 + k)
@@ -324,7 +324,7 @@ def _rand_mx_operand(rng, rows, k):
 
 
 @pytest.mark.parametrize("m,n,k", [(1, 64, 128), (77, 200, 256), (256, 256, 512), (300, 130, 384),
-                                   (130, 300, 1536), (257, 129, 2048)])
+                                   (130, 300, 1536), (257, 129, 2048), (3, 1, 512), (1, 1, 128)])
 def test_mm_mxfp8_random_operands_all_elements(m, n, k):
     say("mm_mxfp8 random", m, n, k)
     rng = np.random.default_rng(m + n + k)
@@ -398,7 +398,7 @@ def _rand_mxfp4_operand(rng, rows, k):
 
 
 @pytest.mark.parametrize("m,n,k", [(1, 64, 128), (77, 200, 256), (256, 256, 512), (300, 130, 384),
-                                   (513, 384, 640)])
+                                   (513, 384, 640), (3, 1, 256), (1, 1, 128)])
 def test_mm_mxfp4_random_operands_all_elements(m, n, k):
     from oracle import mxfp4 as X4
     say("mm_mxfp4 random", m, n, k)
