@@ -87,9 +87,9 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(the FFN shards by tokens or by output features with no exchange; see DESIGN.md). "
-              "Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (the FFN would shard "
+              "by tokens or by output features with no exchange). Run with --gpus 1.",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
