@@ -18,6 +18,8 @@ from what the pages state the operations compute:
   along K sharing one e8m0 scale, per the OCP MX spec) and the online
   BF16 -> MXFP8 weight conversion.
 * The bias each page's linear method adds after the GEMM (``linear``).
+* The norm whose fused quantize may hand mm_fp4 a ``pre_quantized`` triple
+  (FastVideo nvfp4_config.py, ``NVFP4QuantizeMethod.apply``): RMSNorm (``norm``).
 
 Floating-point steps are carried out in IEEE fp32 with numpy float32 arithmetic
 (every operation rounded to nearest even, no fused multiply-add), because the
@@ -30,4 +32,4 @@ values fixed by the format definitions and hand-worked examples
 (``tests/golden/``), closed forms, invariants and brute force; none is
 "parity unpinned" except where a function docstring says so.
 """
-from . import activations, formats, linear, mxfp4, mxfp8, nvfp4  # noqa: F401
+from . import activations, formats, linear, mxfp4, mxfp8, norm, nvfp4  # noqa: F401
