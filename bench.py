@@ -184,17 +184,20 @@ def main():
     kms = {n: acc[n] / args.steps for n in names}
     ms_per_step = wall * 1e3 / args.steps
 
-    # Kernel durations without the event records between a step's launches: the quantize of X
-    # back to back over two copies of X in turn (0.86 GB between reuses of a buffer, so no pass is
-    # served from the 256 MB Infinity Cache), and the unfused GELU and plain quantize of H
-    # (0.9 GB inputs) on their own. The step's own quantize time stays as quantize_x_in_step.
+    # Kernel durations without the event records between a step's launches: the quantize of X and
+    # the RMSNorm + quantize prologue back to back over two copies of X in turn (0.86 GB between
+    # reuses of a buffer, so no pass is served from the 256 MB Infinity Cache), and the unfused
+    # GELU and plain quantize of H (0.9 GB inputs) on their own. The step's own quantize time stays as quantize_x_in_step.
     h = bsp.bsp_gelu_tanh_bf16(y)
     x2 = x.clone()
     reps = max(4, 2 * (args.steps // 4))
     kms["quantize_x_in_step"] = kms["quantize_x"]
     xs = (x, x2)
     qx_calls = [lambda i=i: bsp.bsp_nvfp4_quantize(xs[i % 2], one, px, sx) for i in range(2)]
+    nq_calls = [lambda i=i: bsp.bsp_nvfp4_quantize_rmsnorm(xs[i % 2], one, None, 1e-6, px, sx)
+                for i in range(2)]
     for name, fns in (("quantize_x", qx_calls),
+                      ("rmsnorm_quantize_x", nq_calls),
                       ("gelu", [lambda: bsp.bsp_gelu_tanh_bf16(y, out=h)]),
                       ("quantize_h", [lambda: bsp.bsp_nvfp4_quantize(h, one, ph, sh)])):
         for f in fns:
@@ -216,6 +219,8 @@ def main():
 
     kernels = {
         "quantize_x": {"ms": kms["quantize_x"], "GB/s": qbytes(M, K1) / kms["quantize_x"] / 1e6},
+        "rmsnorm_quantize_x": {"ms": kms["rmsnorm_quantize_x"],
+                               "GB/s": qbytes(M, K1) / kms["rmsnorm_quantize_x"] / 1e6},
         "quantize_x_in_step": {"ms": kms["quantize_x_in_step"],
                                "GB/s": qbytes(M, K1) / kms["quantize_x_in_step"] / 1e6},
         "gelu_quantize_h": {"ms": kms["gelu_quantize_h"],

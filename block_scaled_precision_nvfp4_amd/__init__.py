@@ -51,6 +51,8 @@ SIGNATURES = {
     "bsp_mm_fp4_gelu_nvfp4": ([_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _p, _p], _int),
     "bsp_mm_mxfp8_bias": ([_p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _int, _p], _int),
     "bsp_mm_mxfp4_bias": ([_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _int, _p], _int),
+    "bsp_rmsnorm_bf16": ([_p, _i64, _i64, _i64, _p, ctypes.c_float, _p, _i64, _p], _int),
+    "bsp_nvfp4_quantize_rmsnorm": ([_p, _i64, _i64, _i64, _p, ctypes.c_float, _p, _p, _p, _p], _int),
 }
 
 
@@ -522,6 +524,54 @@ def bsp_gelu_tanh_bf16(x: torch.Tensor, out: Optional[torch.Tensor] = None) -> t
     _need(out, "out", torch.bfloat16, x.device)
     _call("bsp_gelu_tanh_bf16", x.data_ptr(), out.data_ptr(), x.numel(), _stream(x.device))
     return out
+
+
+def _rmsnorm_args(x: torch.Tensor, weight: Optional[torch.Tensor]):
+    x = _as_bf16_2d(x, "x")
+    if weight is not None:
+        _need(weight, "weight", torch.bfloat16, x.device)
+        if weight.numel() != x.shape[1] or not weight.is_contiguous():
+            raise ValueError("weight must be a contiguous bf16 vector of K elements")
+    return x
+
+
+def bsp_rmsnorm_bf16(x: torch.Tensor, weight: Optional[torch.Tensor] = None, eps: float = 1e-6,
+                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """RMSNorm of each row of x over K (optional bf16 gain), bf16 out [M, K]."""
+    x = _rmsnorm_args(x, weight)
+    m, k = x.shape
+    if out is None:
+        out = torch.empty((m, k), dtype=torch.bfloat16, device=x.device)
+    _need(out, "out", torch.bfloat16, x.device)
+    if out.dim() != 2 or out.shape[0] != m or out.shape[1] != k or out.stride(1) != 1:
+        raise ValueError("out must be bf16 [M, K] with unit column stride")
+    _call("bsp_rmsnorm_bf16", x.data_ptr(), m, k, x.stride(0), _ptr(weight), float(eps),
+          out.data_ptr(), out.stride(0), _stream(x.device))
+    return out
+
+
+def bsp_nvfp4_quantize_rmsnorm(x: torch.Tensor, gsf: torch.Tensor,
+                               weight: Optional[torch.Tensor] = None, eps: float = 1e-6,
+                               packed: Optional[torch.Tensor] = None,
+                               sf: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """NVFP4 quantize of bsp_rmsnorm_bf16(x, weight, eps) in one pass; outputs as bsp_nvfp4_quantize."""
+    x = _rmsnorm_args(x, weight)
+    _need(gsf, "gsf", torch.float32, x.device)
+    m, k = x.shape
+    mp, kp = -(-m // 128) * 128, -(-(k // 16) // 4) * 4
+    if packed is None:
+        packed = torch.empty((m, k // 2), dtype=torch.uint8, device=x.device)
+    if sf is None:
+        sf = torch.empty((mp, kp), dtype=torch.uint8, device=x.device)
+    _need(packed, "packed", torch.uint8, x.device)
+    _need(sf, "sf", torch.uint8, x.device)
+    if packed.numel() < m * (k // 2) or not packed.is_contiguous():
+        raise ValueError("packed must be contiguous with M*K/2 bytes")
+    if sf.numel() < mp * kp or not sf.is_contiguous():
+        raise ValueError("sf must be contiguous with ceil(M/128)*128 x ceil(K/64)*4 bytes")
+    _call("bsp_nvfp4_quantize_rmsnorm", x.data_ptr(), m, k, x.stride(0), _ptr(weight), float(eps),
+          gsf.data_ptr(), packed.data_ptr(), sf.data_ptr(), _stream(x.device))
+    return packed, sf
 
 
 __all__ = [n for n in SIGNATURES if n not in ("bsp_last_error",)] + [

@@ -333,6 +333,136 @@ __global__ __launch_bounds__(256) void nvfp4_quantize_token_kernel(
 }
 
 // =============================================================================================
+// RMSNorm, alone (bf16 out) or followed by the NVFP4 quantize of its bf16 output
+// =============================================================================================
+// The norm whose fused quantize hands mm_fp4 a pre-quantized activation (FastVideo
+// nvfp4_config.py, NVFP4QuantizeMethod.apply: FlashInfer's fused norm + quantize producers; the
+// page does not name the norm, RMSNorm is the norm of the LTX-2 blocks it quantizes):
+//   y = bf16( fl32( fl32(x * r) * w ) ),  r = fl32( 1 / sqrt(ss / K + eps) ),
+// w the optional bf16 gain (no multiply without one). ss, the sum of the row's squares, and r are
+// evaluated in fp64 (a bf16 square is exact there and the sums of up to 2^24 of them stay within
+// about 2^-29 relative), so r is the fp32 rounding of the exact value up to a few fp64 ulps; the
+// two products and the bf16 rounding are fp32. Each lane adds its own squares in element order,
+// then a butterfly over the wave. Row placement is
+// the per-token kernel's: one wave per row, rows q, q+32, q+64, q+96 of a 128-row tile per
+// workgroup, the row held in registers between the two phases when it fits one segment. QUANT
+// then encodes y exactly as nvfp4_quantize_kernel does (element scales tabulated once per
+// workgroup from the device global scale); otherwise y is stored. The same arithmetic in both
+// forms, so the fused bytes equal the NVFP4 quantize of the standalone output. Padding rows
+// (M..Mp-1) run with r = 0, which writes their 0x00 scales.
+template <int C, bool VEC, bool QUANT>
+__global__ __launch_bounds__(256) void rmsnorm_token_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ld,
+    const uint16_t* __restrict__ wgain, float eps, const float* __restrict__ gsf,
+    uint16_t* __restrict__ out, int64_t ldo, uint8_t* __restrict__ packed,
+    uint8_t* __restrict__ sf, int64_t Kp) {
+  __shared__ float rtab[QUANT ? 128 : 1];
+  __shared__ uint32_t srow[QUANT ? 4 : 1][QUANT ? kTokMaxCols / 4 : 1];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t tile = blockIdx.x >> 5, q = blockIdx.x & 31;
+  const int64_t row = tile * 128 + q + 32 * wave;
+  const bool live = row < M;
+  const int64_t seg_elems = 64 * 8 * C;
+  const int64_t kpad = QUANT ? Kp * 16 : K;        // elements incl. the padding scale columns
+  const int nseg = (int)((kpad + seg_elems - 1) / seg_elems);
+  const uint16_t* xr = x + (live ? row : 0) * ld;
+  float g = 1.0f;
+  if (QUANT) {
+    g = *gsf;
+    if (threadIdx.x < 128) {
+      const int c = threadIdx.x;
+      rtab[c] = (c == 0 || c > 0x7E) ? 0.0f : g / e4m3_decode_pos((uint32_t)c);
+    }
+  }
+
+  uint4 v[C];
+  double ss = 0.0;
+  for (int sg = 0; sg < nseg; ++sg) {
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      const int64_t e = sg * seg_elems + (int64_t)(j * 64 + lane) * 8;
+      v[j] = (live && e < K) ? load8<VEC>(xr + e) : make_uint4(0u, 0u, 0u, 0u);
+      float f[8];
+      unpack8(v[j], f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const double d = (double)f[i];
+        ss = __builtin_fma(d, d, ss);  // d * d is exact in fp64, so this is the rounded sum
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+  const float r = live ? (float)(1.0 / sqrt(ss / (double)K + (double)eps)) : 0.0f;
+  if (QUANT) __syncthreads();  // rtab
+
+  const int64_t half_k = K / 2;
+  uint8_t* prow = QUANT ? packed + (live ? row : 0) * half_k : nullptr;
+  uint16_t* orow = QUANT ? nullptr : out + (live ? row : 0) * ldo;
+  uint8_t* sb = reinterpret_cast<uint8_t*>(srow[QUANT ? wave : 0]);
+  for (int sg = 0; sg < nseg; ++sg) {
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      const int64_t e = sg * seg_elems + (int64_t)(j * 64 + lane) * 8;
+      const bool in = live && e < K;
+      if (nseg > 1) v[j] = in ? load8<VEC>(xr + e) : make_uint4(0u, 0u, 0u, 0u);
+      float f[8];
+      unpack8(v[j], f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) f[i] = f[i] * r;
+      if (wgain) {
+        float w[8];
+        unpack8(e < K ? load8<VEC>(wgain + e) : make_uint4(0u, 0u, 0u, 0u), w);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = f[i] * w[i];
+      }
+      const uint4 y = make_uint4(bf16x2_rne(f[0], f[1]), bf16x2_rne(f[2], f[3]),
+                                 bf16x2_rne(f[4], f[5]), bf16x2_rne(f[6], f[7]));
+      if (!QUANT) {
+        if (in) {
+          if (VEC) {
+            __builtin_nontemporal_store((nt_u32x4){y.x, y.y, y.z, y.w},
+                                        reinterpret_cast<nt_u32x4*>(orow + e));
+          } else {
+            const uint32_t yw[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              orow[e + 2 * i] = (uint16_t)(yw[i] & 0xFFFFu);
+              orow[e + 2 * i + 1] = (uint16_t)(yw[i] >> 16);
+            }
+          }
+        }
+        continue;
+      }
+      unpack8(y, f);
+      const float a = pair_max(absmax8(f));
+      const uint32_t S = e4m3_encode_pos(g * (a * kSixth));
+      const float rs = rtab[S];
+      uint32_t o = 0;
+      o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, f[0] * rs, f[1] * rs, 1.0f, 0);
+      o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, f[2] * rs, f[3] * rs, 1.0f, 1);
+      o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, f[4] * rs, f[5] * rs, 1.0f, 2);
+      o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, f[6] * rs, f[7] * rs, 1.0f, 3);
+      if (in) store4_nt(prow + e / 2, o);
+      const int64_t col = e / 16;
+      if ((lane & 1) == 0 && col < Kp) sb[col % kTokMaxCols] = (uint8_t)S;
+    }
+    if (QUANT) {
+      __syncthreads();
+      const int64_t c0 = sg * seg_elems / 16;
+      const int64_t c1 = c0 + seg_elems / 16 < Kp ? c0 + seg_elems / 16 : Kp;
+      const int64_t groups = Kp / 4;
+      for (int64_t cg = c0 / 4 + threadIdx.x; cg < c1 / 4; cg += 256) {
+        const int i = (int)(cg % (kTokMaxCols / 4));
+        *reinterpret_cast<uint4*>(sf + (tile * groups + cg) * 512 + q * 16) =
+            make_uint4(srow[0][i], srow[1][i], srow[2][i], srow[3][i]);
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// =============================================================================================
 // MXFP8 quantize
 // =============================================================================================
 // One workgroup covers 64 rows x 256 K (8 steps of 8 rows x 32 lanes x 8 elements). A 32-element
@@ -611,6 +741,85 @@ int launch_nvfp4_quantize_per_token(const void* x, int64_t M, int64_t K, int64_t
   else
     launch_token_c<32>(xp, M, K, ld, packed, sf, gsf_rows, Kp, vec, s);
   return check_launch("bsp_nvfp4_quantize_per_token");
+}
+
+template <int C, bool QUANT>
+static void launch_rmsnorm_c(const uint16_t* xp, int64_t M, int64_t K, int64_t ld,
+                             const uint16_t* wg, float eps, const float* gsf, uint16_t* out,
+                             int64_t ldo, uint8_t* packed, uint8_t* sf, int64_t Kp, bool vec,
+                             hipStream_t s) {
+  dim3 grid((unsigned)(ceil_div(M, 128) * 128 / 4));  // one wave per row of whole 128-row tiles
+  if (vec)
+    hipLaunchKernelGGL((rmsnorm_token_kernel<C, true, QUANT>), grid, dim3(256), 0, s, xp, M, K, ld,
+                       wg, eps, gsf, out, ldo, packed, sf, Kp);
+  else
+    hipLaunchKernelGGL((rmsnorm_token_kernel<C, false, QUANT>), grid, dim3(256), 0, s, xp, M, K, ld,
+                       wg, eps, gsf, out, ldo, packed, sf, Kp);
+}
+
+// QUANT: the fused NVFP4 quantize; else the standalone RMSNorm into out. The register segment is
+// the smallest that holds the (padded) row, as for the per-token quantize.
+template <bool QUANT>
+static void launch_rmsnorm_t(const uint16_t* xp, int64_t M, int64_t K, int64_t ld, const uint16_t* wg,
+                             float eps, const float* gsf, uint16_t* out, int64_t ldo,
+                             uint8_t* packed, uint8_t* sf, int64_t Kp, bool vec, hipStream_t s) {
+  const int64_t kpad = QUANT ? Kp * 16 : K;
+  if (kpad <= 64 * 8 * 4)
+    launch_rmsnorm_c<4, QUANT>(xp, M, K, ld, wg, eps, gsf, out, ldo, packed, sf, Kp, vec, s);
+  else if (kpad <= 64 * 8 * 8)
+    launch_rmsnorm_c<8, QUANT>(xp, M, K, ld, wg, eps, gsf, out, ldo, packed, sf, Kp, vec, s);
+  else if (kpad <= 64 * 8 * 10)
+    launch_rmsnorm_c<10, QUANT>(xp, M, K, ld, wg, eps, gsf, out, ldo, packed, sf, Kp, vec, s);
+  else if (kpad <= 64 * 8 * 16)
+    launch_rmsnorm_c<16, QUANT>(xp, M, K, ld, wg, eps, gsf, out, ldo, packed, sf, Kp, vec, s);
+  else
+    launch_rmsnorm_c<32, QUANT>(xp, M, K, ld, wg, eps, gsf, out, ldo, packed, sf, Kp, vec, s);
+}
+
+// quant: the fused NVFP4 quantize (gsf, packed, sf); else the standalone RMSNorm into out
+static int rmsnorm_entry(const char* fn, bool quant, const void* x, int64_t M, int64_t K, int64_t ld,
+                         const void* weight, float eps, const float* gsf, void* out, int64_t ldo,
+                         uint8_t* packed, uint8_t* sf, void* stream) {
+  BSP_REQUIRE(M >= 0 && K > 0, BSP_EINVAL, "%s: bad size M=%lld K=%lld", fn, (long long)M, (long long)K);
+  BSP_REQUIRE(eps > 0.0f && eps <= 3.4e38f, BSP_EINVAL, "%s: eps must be positive and finite", fn);
+  BSP_REQUIRE(K % 16 == 0, BSP_ESHAPE, "%s: K (%lld) must be a multiple of 16", fn, (long long)K);
+  BSP_REQUIRE(M <= 1 || ld >= K, BSP_ESHAPE, "%s: ld (%lld) < K (%lld)", fn, (long long)ld, (long long)K);
+  BSP_REQUIRE(quant || M <= 1 || ldo >= K, BSP_ESHAPE, "%s: ldo (%lld) < K (%lld)", fn,
+              (long long)ldo, (long long)K);
+  if (M == 0) return BSP_OK;
+  BSP_REQUIRE(x && (quant ? (gsf && packed && sf) : out != nullptr), BSP_EINVAL, "%s: null pointer", fn);
+  BSP_REQUIRE(!quant || ((reinterpret_cast<uintptr_t>(packed) & 3u) == 0 &&
+                         (reinterpret_cast<uintptr_t>(sf) & 15u) == 0),
+              BSP_EINVAL, "%s: packed must be 4-byte and sf 16-byte aligned", fn);
+  BSP_REQUIRE(ceil_div(M, 128) * 32 < (1ll << 31), BSP_ESHAPE, "%s: M too large", fn);
+  if (int e = check_device()) return e;
+  const uint16_t* xp = static_cast<const uint16_t*>(x);
+  const uint16_t* wg = static_cast<const uint16_t*>(weight);
+  // 16-byte loads and stores need 16-byte aligned rows of x, of the gain and (standalone) of out
+  const bool vec = (ld % 8 == 0) && aligned16(x) && (!wg || aligned16(wg)) &&
+                   (quant || ((ldo % 8 == 0) && aligned16(out)));
+  const int64_t Kp = ceil_div(K / 16, 4) * 4;
+  if (quant)
+    launch_rmsnorm_t<true>(xp, M, K, ld, wg, eps, gsf, nullptr, 0, packed, sf, Kp, vec,
+                           (hipStream_t)stream);
+  else
+    launch_rmsnorm_t<false>(xp, M, K, ld, wg, eps, nullptr, static_cast<uint16_t*>(out), ldo,
+                            nullptr, nullptr, Kp, vec, (hipStream_t)stream);
+  return check_launch(fn);
+}
+
+extern "C" int bsp_rmsnorm_bf16(const void* x, int64_t M, int64_t K, int64_t ld,
+                                const void* weight_bf16, float eps, void* out, int64_t ldo,
+                                void* stream) {
+  return rmsnorm_entry("bsp_rmsnorm_bf16", false, x, M, K, ld, weight_bf16, eps, nullptr, out, ldo,
+                       nullptr, nullptr, stream);
+}
+
+extern "C" int bsp_nvfp4_quantize_rmsnorm(const void* x, int64_t M, int64_t K, int64_t ld,
+                                          const void* weight_bf16, float eps, const float* gsf,
+                                          uint8_t* packed, uint8_t* sf, void* stream) {
+  return rmsnorm_entry("bsp_nvfp4_quantize_rmsnorm", true, x, M, K, ld, weight_bf16, eps, gsf,
+                       nullptr, 0, packed, sf, stream);
 }
 
 static int nvfp4_quantize_entry(const char* fn, const void* x, int64_t M, int64_t K, int64_t ld,

@@ -201,6 +201,27 @@ int bsp_mm_fp4_per_token(const uint8_t* a_packed, const uint8_t* a_sf, const uin
 int bsp_nvfp4_quantize_gelu(const void* y_bf16, int64_t M, int64_t K, int64_t ld, const float* gsf_dev,
                             uint8_t* packed, uint8_t* sf, void* stream);
 
+/* Producer-fused quantize of a norm's output. [FV-NV] NVFP4QuantizeMethod.apply: the activation
+ * may arrive as a pre-quantized (packed, scales, global scale) triple from a fused norm + quantize
+ * producer. The page does not name the norm; the one taken is RMSNorm over K (the norm of the
+ * LTX-2 blocks that page quantizes):
+ *   y[m, k] = bf16( fl32( fl32(x[m, k] * r_m) * w[k] ) ),  r_m = fl32( 1 / sqrt(ss_m / K + eps) ),
+ * ss_m = sum of x[m, :]^2 (no gain multiply when weight_bf16 is NULL). ss_m and r_m are evaluated
+ * in fp64 and r_m rounded once to fp32; the products and the bf16 rounding are IEEE fp32,
+ * nearest even. y is then within 3 fp32 roundings of the exact RMSNorm.
+ * bsp_rmsnorm_bf16 writes y: device bf16 [M, K], row stride ldo (>= K).
+ * bsp_nvfp4_quantize_rmsnorm writes bsp_nvfp4_quantize(y, gsf) without storing y: its bytes equal
+ * those of the NVFP4 quantize of bsp_rmsnorm_bf16's output. Packed, sf and gsf as in
+ * bsp_nvfp4_quantize (padded rows' scales 0x00).
+ * x: device bf16 [M, K], row stride ld; weight_bf16: NULL or device bf16 [K]; eps: positive and
+ * finite (else BSP_EINVAL); K % 16 == 0 (else BSP_ESHAPE); M == 0 returns BSP_OK. Inputs must be
+ * finite. Rows of up to 64*8*32 elements (padded to 64) are read from HBM once, longer rows twice. */
+int bsp_rmsnorm_bf16(const void* x_bf16, int64_t M, int64_t K, int64_t ld, const void* weight_bf16,
+                     float eps, void* out_bf16, int64_t ldo, void* stream);
+int bsp_nvfp4_quantize_rmsnorm(const void* x_bf16, int64_t M, int64_t K, int64_t ld,
+                               const void* weight_bf16, float eps, const float* gsf_dev,
+                               uint8_t* packed, uint8_t* sf, void* stream);
+
 /* The same producer fusion one step earlier, in fc_in's epilogue: the NVFP4 encoding of
  * gelu_tanh(alpha * A . B^T), byte for byte what bsp_nvfp4_quantize_gelu(bsp_mm_fp4(...), out_gsf)
  * writes, without the bf16 product ever reaching memory (it exists only as each GEMM tile's LDS

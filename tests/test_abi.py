@@ -174,3 +174,28 @@ def test_mxfp8_gemm_scale_alignment():
     st, msg = _st("bsp_mm_mxfp8", P, ctypes.c_void_p(18), P, P, 8, 8, 128, P, 8, 0, None)
     assert st == -1 and "4-byte" in msg
     assert _st("bsp_mm_mxfp8_bias", P, P, P, ctypes.c_void_p(22), P, 8, 8, 128, P, 8, 0, None)[0] == -1
+
+
+def test_rmsnorm_entry_point_errors():
+    """bsp_rmsnorm_bf16 / bsp_nvfp4_quantize_rmsnorm: eps must be positive and finite, K % 16 == 0,
+    ld (and ldo) >= K, null pointers rejected, M == 0 is a no-op; nothing is launched on error."""
+    P = ctypes.c_void_p(256)
+    f = ctypes.c_float
+    assert _st("bsp_rmsnorm_bf16", P, 4, 32, 32, None, f(0.0), P, 32, None)[0] == -1
+    assert _st("bsp_rmsnorm_bf16", P, 4, 32, 32, None, f(-1e-6), P, 32, None)[0] == -1
+    assert _st("bsp_rmsnorm_bf16", P, 4, 32, 32, None, f(float("inf")), P, 32, None)[0] == -1
+    assert _st("bsp_rmsnorm_bf16", P, 4, 32, 32, None, f(float("nan")), P, 32, None)[0] == -1
+    st, msg = _st("bsp_rmsnorm_bf16", P, 4, 24, 24, None, f(1e-6), P, 24, None)
+    assert st == -2 and "multiple of 16" in msg
+    assert _st("bsp_rmsnorm_bf16", P, 4, 32, 16, None, f(1e-6), P, 32, None)[0] == -2
+    assert _st("bsp_rmsnorm_bf16", P, 4, 32, 32, None, f(1e-6), P, 16, None)[0] == -2
+    assert _st("bsp_rmsnorm_bf16", P, 4, 32, 32, None, f(1e-6), None, 32, None)[0] == -1
+    assert _st("bsp_rmsnorm_bf16", None, 0, 32, 32, None, f(1e-6), None, 32, None)[0] == 0
+    q = "bsp_nvfp4_quantize_rmsnorm"
+    assert _st(q, P, 4, 24, 24, None, f(1e-6), P, P, P, None)[0] == -2
+    assert _st(q, P, 4, 32, 32, None, f(0.0), P, P, P, None)[0] == -1
+    assert _st(q, P, 4, 32, 32, None, f(1e-6), None, P, P, None)[0] == -1
+    assert _st(q, P, 4, 32, 32, None, f(1e-6), P, P, None, None)[0] == -1
+    assert _st(q, P, 4, 32, 32, None, f(1e-6), P, ctypes.c_void_p(258), P, None)[0] == -1
+    assert _st(q, P, 4, 32, 32, None, f(1e-6), P, P, ctypes.c_void_p(264), None)[0] == -1
+    assert _st(q, None, 0, 32, 32, None, f(1e-6), None, None, None, None)[0] == 0
