@@ -199,3 +199,17 @@ def test_rmsnorm_entry_point_errors():
     assert _st(q, P, 4, 32, 32, None, f(1e-6), P, ctypes.c_void_p(258), P, None)[0] == -1
     assert _st(q, P, 4, 32, 32, None, f(1e-6), P, P, ctypes.c_void_p(264), None)[0] == -1
     assert _st(q, None, 0, 32, 32, None, f(1e-6), None, None, None, None)[0] == 0
+
+
+def test_size_limits_rejected_on_the_host():
+    """One past each documented maximum returns BSP_ESHAPE before any launch (the maxima themselves
+    run on the GPU in tests/test_gpu_limits.py)."""
+    P = ctypes.c_void_p(256)
+    m_over = 65535 * 128 + 1
+    for fn in ("bsp_nvfp4_quantize", "bsp_nvfp4_quantize_gelu", "bsp_nvfp4_quantize_8x4"):
+        st, msg = _st(fn, P, m_over, 32, 32, P, P, P, None)
+        assert st == -2 and "too large" in msg, (fn, st, msg)
+    assert _st("bsp_mxfp4_quantize", P, m_over, 32, 32, P, P, None)[0] == -2
+    assert _st("bsp_mxfp8_quantize", P, 65535 * 64 + 1, 32, 32, P, P, None)[0] == -2
+    st, msg = _st("bsp_mm_fp4", P, P, P, P, P, 4, 4, (1 << 24) + 64, P, 4, 0, None)
+    assert st == -2 and "at most" in msg

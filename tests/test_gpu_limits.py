@@ -1,0 +1,141 @@
+"""Maximum sizes each entry point accepts, on the GPU, against the oracle.
+
+Quantizers at their largest row count (the grid's tile-row limit: ceil(M/128) < 65536, MXFP8
+ceil(M/64) < 65536) with sampled rows, the first and last rows and every padding scale byte
+checked; the GEMMs at K = 2^24 (mm_fp4's limit: per-tile 32-bit load offsets) on every element;
+a GEMM with 8.4 million rows (int64 row offsets, 32768 tiles) on sampled rows. One size past each
+limit is rejected on the host (tests/test_abi.py).
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_precision_nvfp4_amd as bsp
+import workloads as W
+from oracle import mxfp4 as X4
+from oracle import mxfp8 as X
+from oracle import nvfp4 as N
+from tests.gpu_util import (assert_gemm_f32, dev_bf16, dev_u8, host_u8, say, scalar)
+
+pytestmark = pytest.mark.gpu
+
+M_MAX_128 = 65535 * 128      # 8388480 rows: grid.y (128-row tiles) below 65536
+M_MAX_64 = 65535 * 64        # 4194240 rows: MXFP8 quantize's 64-row tiles
+
+
+def _rows(m, seed):
+    return np.unique(np.concatenate([np.random.default_rng(seed).integers(0, m, 40),
+                                     [0, 1, 127, 128, m // 2, m - 129, m - 2, m - 1]]))
+
+
+def _tall_bits(m, k, seed):
+    """Seeded bf16 rows (the workload recipe) built in chunks so the host copy stays small."""
+    out = np.empty((m, k), dtype=np.uint16)
+    step = 1 << 20
+    for r0 in range(0, m, step):
+        r1 = min(m, r0 + step)
+        out[r0:r1] = W.small_case(r1 - r0, k, seed=seed + r0 // step, std=2.0, outlier_frac=0.05)
+    return out
+
+
+def test_nvfp4_quantizers_at_max_rows():
+    m, k = M_MAX_128, 32
+    say("max rows nvfp4", m, k)
+    xb = _tall_bits(m, k, 71)
+    x = dev_bf16(xb)
+    rows = _rows(m, 3)
+    ri = torch.from_numpy(rows).cuda()
+    rp, cp = N.sf_padded_shape(m, k)
+    g = np.float32(0.37)
+    p, sf = bsp.bsp_nvfp4_quantize(x, scalar(g))
+    ref_p, ref_s = N.quantize(xb[rows], g, layout="linear")
+    lin = N.unswizzle_128x4(host_u8(sf).ravel(), rp, cp)
+    assert np.array_equal(host_u8(p[ri]), ref_p)
+    assert np.array_equal(lin[rows, : k // 16], ref_s) and not lin[:, k // 16:].any()
+    del p, sf
+    p, sf, gr = bsp.bsp_nvfp4_quantize_per_token(x)
+    ref_p, ref_s, ref_g = N.quantize_per_token(xb[rows], layout="linear")
+    lin = N.unswizzle_128x4(host_u8(sf).ravel(), rp, cp)
+    assert np.array_equal(gr[ri].cpu().numpy(), ref_g)
+    assert np.array_equal(host_u8(p[ri]), ref_p) and np.array_equal(lin[rows, : k // 16], ref_s)
+    del p, sf, gr
+    p, sf = bsp.bsp_mxfp4_quantize(x)
+    ref_p, ref_s = X4.quantize(xb[rows], layout="linear")
+    rp4, cp4 = X4.sf_padded_shape(m, k)
+    lin = N.unswizzle_128x4(host_u8(sf).ravel(), rp4, cp4)
+    assert np.array_equal(host_u8(p[ri]), ref_p) and np.array_equal(lin[rows, : k // 32], ref_s)
+
+
+def test_mxfp8_quantize_at_max_rows():
+    m, k = M_MAX_64, 64
+    say("max rows mxfp8", m, k)
+    xb = _tall_bits(m, k, 83)
+    q, s = bsp.bsp_mxfp8_quantize(dev_bf16(xb))
+    rows = _rows(m, 4)
+    ri = torch.from_numpy(rows).cuda()
+    rq, rs = X.quantize(xb[rows])
+    assert np.array_equal(host_u8(q[ri]), rq) and np.array_equal(host_u8(s[ri]), rs)
+
+
+def _nvfp4_operand(rng, rows, k):
+    packed = rng.integers(0, 256, size=(rows, k // 2), dtype=np.uint8)
+    rp, cp = N.sf_padded_shape(rows, k)
+    sfb = np.zeros(rp * cp, dtype=np.uint8)
+    r, c = np.meshgrid(np.arange(rows), np.arange(k // 16), indexing="ij")
+    sfb[N.sf_offset(r, c, cp)] = rng.integers(0x28, 0x48, size=(rows, k // 16), dtype=np.uint8)
+    return packed, sfb
+
+
+def _mxfp4_operand(rng, rows, k):
+    packed = rng.integers(0, 256, size=(rows, k // 2), dtype=np.uint8)
+    rp, cp = X4.sf_padded_shape(rows, k)
+    sfb = np.zeros(rp * cp, dtype=np.uint8)
+    r, c = np.meshgrid(np.arange(rows), np.arange(k // 32), indexing="ij")
+    sfb[N.sf_offset(r, c, cp)] = rng.integers(120, 134, size=(rows, k // 32), dtype=np.uint8)
+    return packed, sfb
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp8", "mxfp4"])
+def test_gemm_at_k_2_24(fmt):
+    """K = 2^24 (131072 NVFP4 stages per tile) with ragged M, N: every element against the oracle."""
+    m, n, k = 3, 5, 1 << 24
+    say("K = 2^24", fmt, m, n, k)
+    rng = np.random.default_rng(24)
+    if fmt == "nvfp4":
+        pa, sa = _nvfp4_operand(rng, m, k)
+        pb, sb = _nvfp4_operand(rng, n, k)
+        c = bsp.bsp_mm_fp4(dev_u8(pa), dev_u8(sa), dev_u8(pb), dev_u8(sb), scalar(0.25),
+                           out_dtype=torch.float32)
+        ref = N.mm_fp4(pa, sa, pb, sb, np.float32(0.25), m, n, k)
+    elif fmt == "mxfp8":
+        qa = rng.integers(0, 256, size=(m, k), dtype=np.uint8)
+        qb = rng.integers(0, 256, size=(n, k), dtype=np.uint8)
+        qa[(qa & 0x7F) == 0x7F] = 0x3F
+        qb[(qb & 0x7F) == 0x7F] = 0x3F
+        sa = rng.integers(120, 134, size=(m, k // 32), dtype=np.uint8)
+        sb = rng.integers(120, 134, size=(n, k // 32), dtype=np.uint8)
+        c = bsp.bsp_mm_mxfp8(dev_u8(qa), dev_u8(sa), dev_u8(qb), dev_u8(sb), out_dtype=torch.float32)
+        ref = X.mm_mxfp8(qa, sa, qb, sb, m, n, k)
+    else:
+        pa, sa = _mxfp4_operand(rng, m, k)
+        pb, sb = _mxfp4_operand(rng, n, k)
+        c = bsp.bsp_mm_mxfp4(dev_u8(pa), dev_u8(sa), dev_u8(pb), dev_u8(sb), None, torch.float32)
+        ref = X4.mm_mxfp4(pa, sa, pb, sb, np.float32(1.0), m, n, k)
+    assert_gemm_f32(c.cpu().numpy().astype(np.float64), ref, f"K=2^24 {fmt}")
+
+
+def test_mm_fp4_tall_max_rows():
+    """M = 8388480 (32768 row tiles, rows addressed past 2^31 bytes of C), N = 136 (ragged), K = 64:
+    sampled rows of C on every column against the oracle, in bf16."""
+    m, n, k = M_MAX_128, 136, 64
+    say("tall mm_fp4", m, n, k)
+    rng = np.random.default_rng(99)
+    pa, sa = _nvfp4_operand(rng, m, k)
+    pb, sb = _nvfp4_operand(rng, n, k)
+    c = bsp.bsp_mm_fp4(dev_u8(pa), dev_u8(sa), dev_u8(pb), dev_u8(sb), scalar(1.0))
+    rows = _rows(m, 5)
+    got = c[torch.from_numpy(rows).cuda()].float().cpu().numpy().astype(np.float64)
+    ref = N.dequant_rows(pa, sa, rows, m, k) @ N.dequant_rows(pb, sb, np.arange(n), n, k).T
+    err = np.abs(got - ref)
+    assert np.all(err <= 8e-3 * np.max(np.abs(ref))), float(err.max())
+    assert np.linalg.norm(got - ref) <= 3e-3 * np.linalg.norm(ref)
