@@ -350,7 +350,7 @@ __global__ __launch_bounds__(256) void nvfp4_quantize_token_kernel(
 // workgroup from the device global scale); otherwise y is stored. The same arithmetic in both
 // forms, so the fused bytes equal the NVFP4 quantize of the standalone output. Padding rows
 // (M..Mp-1) run with r = 0, which writes their 0x00 scales.
-template <int C, bool VEC, bool QUANT>
+template <int C, bool VEC, bool QUANT, bool GAIN>
 __global__ __launch_bounds__(256) void rmsnorm_token_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ld,
     const uint16_t* __restrict__ wgain, float eps, const float* __restrict__ gsf,
@@ -410,7 +410,7 @@ __global__ __launch_bounds__(256) void rmsnorm_token_kernel(
       unpack8(v[j], f);
 #pragma unroll
       for (int i = 0; i < 8; ++i) f[i] = f[i] * r;
-      if (wgain) {
+      if (GAIN) {
         float w[8];
         unpack8(e < K ? load8<VEC>(wgain + e) : make_uint4(0u, 0u, 0u, 0u), w);
 #pragma unroll
@@ -749,12 +749,18 @@ static void launch_rmsnorm_c(const uint16_t* xp, int64_t M, int64_t K, int64_t l
                              int64_t ldo, uint8_t* packed, uint8_t* sf, int64_t Kp, bool vec,
                              hipStream_t s) {
   dim3 grid((unsigned)(ceil_div(M, 128) * 128 / 4));  // one wave per row of whole 128-row tiles
-  if (vec)
-    hipLaunchKernelGGL((rmsnorm_token_kernel<C, true, QUANT>), grid, dim3(256), 0, s, xp, M, K, ld,
-                       wg, eps, gsf, out, ldo, packed, sf, Kp);
+  if (vec && wg)
+    hipLaunchKernelGGL((rmsnorm_token_kernel<C, true, QUANT, true>), grid, dim3(256), 0, s, xp, M, K,
+                       ld, wg, eps, gsf, out, ldo, packed, sf, Kp);
+  else if (vec)
+    hipLaunchKernelGGL((rmsnorm_token_kernel<C, true, QUANT, false>), grid, dim3(256), 0, s, xp, M, K,
+                       ld, wg, eps, gsf, out, ldo, packed, sf, Kp);
+  else if (wg)
+    hipLaunchKernelGGL((rmsnorm_token_kernel<C, false, QUANT, true>), grid, dim3(256), 0, s, xp, M, K,
+                       ld, wg, eps, gsf, out, ldo, packed, sf, Kp);
   else
-    hipLaunchKernelGGL((rmsnorm_token_kernel<C, false, QUANT>), grid, dim3(256), 0, s, xp, M, K, ld,
-                       wg, eps, gsf, out, ldo, packed, sf, Kp);
+    hipLaunchKernelGGL((rmsnorm_token_kernel<C, false, QUANT, false>), grid, dim3(256), 0, s, xp, M, K,
+                       ld, wg, eps, gsf, out, ldo, packed, sf, Kp);
 }
 
 // QUANT: the fused NVFP4 quantize; else the standalone RMSNorm into out. The register segment is
