@@ -1,11 +1,14 @@
 // HBM-bound kernels of the NVFP4 / MXFP8 linear layer on gfx950:
-//   the weight global scale (amax reduction + scalar finish), NVFP4 quantize, alpha,
-//   MXFP8 quantize, and the bf16 GELU between the FFN projections.
+//   the weight global scale (amax reduction + scalar finish), NVFP4 quantize (per tensor, per
+//   token, layout_8x4, fused with GELU or with RMSNorm), alpha, MXFP8 and MXFP4 quantize, the bf16
+//   GELU between the FFN projections and the standalone RMSNorm.
 //
 // Pages (by title, section): FastVideo nvfp4_qat_config.py (convert_model_to_fp4, apply),
 // FastVideo nvfp4_config.py (module docstring, _nvfp4_quantize and its shape kernel,
 // convert_model_to_nvfp4), SGLang nvfp4_online.py (_quantize_weight_nvfp4),
 // vLLM-Omni mxfp8_config.py (DiffusionMXFP8Config, NPUMxfp8LinearMethod).
+#include <cfloat>
+
 #include "common.hpp"
 
 namespace bsp {
@@ -787,7 +790,7 @@ static int rmsnorm_entry(const char* fn, bool quant, const void* x, int64_t M, i
                          const void* weight, float eps, const float* gsf, void* out, int64_t ldo,
                          uint8_t* packed, uint8_t* sf, void* stream) {
   BSP_REQUIRE(M >= 0 && K > 0, BSP_EINVAL, "%s: bad size M=%lld K=%lld", fn, (long long)M, (long long)K);
-  BSP_REQUIRE(eps > 0.0f && eps <= 3.4e38f, BSP_EINVAL, "%s: eps must be positive and finite", fn);
+  BSP_REQUIRE(eps > 0.0f && eps <= FLT_MAX, BSP_EINVAL, "%s: eps must be positive and finite", fn);
   BSP_REQUIRE(K % 16 == 0, BSP_ESHAPE, "%s: K (%lld) must be a multiple of 16", fn, (long long)K);
   BSP_REQUIRE(M <= 1 || ld >= K, BSP_ESHAPE, "%s: ld (%lld) < K (%lld)", fn, (long long)ld, (long long)K);
   BSP_REQUIRE(quant || M <= 1 || ldo >= K, BSP_ESHAPE, "%s: ldo (%lld) < K (%lld)", fn,

@@ -184,6 +184,7 @@ def test_rmsnorm_entry_point_errors():
     assert _st("bsp_rmsnorm_bf16", P, 4, 32, 32, None, f(0.0), P, 32, None)[0] == -1
     assert _st("bsp_rmsnorm_bf16", P, 4, 32, 32, None, f(-1e-6), P, 32, None)[0] == -1
     assert _st("bsp_rmsnorm_bf16", P, 4, 32, 32, None, f(float("inf")), P, 32, None)[0] == -1
+    assert _st("bsp_rmsnorm_bf16", None, 0, 32, 32, None, f(3.4028234e38), None, 32, None)[0] == 0
     assert _st("bsp_rmsnorm_bf16", P, 4, 32, 32, None, f(float("nan")), P, 32, None)[0] == -1
     st, msg = _st("bsp_rmsnorm_bf16", P, 4, 24, 24, None, f(1e-6), P, 24, None)
     assert st == -2 and "multiple of 16" in msg
