@@ -178,11 +178,17 @@ def main():
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    per_step = {n: [] for n in names}
     for e in evs:
         for j, n in enumerate(names):
-            acc[n] += e[j].elapsed_time(e[j + 1])
+            t = e[j].elapsed_time(e[j + 1])
+            acc[n] += t
+            per_step[n].append(t)
+    per_step["step"] = [e[0].elapsed_time(e[-1]) for e in evs]
     kms = {n: acc[n] / args.steps for n in names}
     ms_per_step = wall * 1e3 / args.steps
+    spread = {n: {"median": round(float(np.median(v)), 4), "p10": round(float(np.percentile(v, 10)), 4),
+                  "p90": round(float(np.percentile(v, 90)), 4)} for n, v in per_step.items()}
 
     # Kernel durations without the event records between a step's launches: the quantize of X and
     # the RMSNorm + quantize prologue back to back over two copies of X in turn (0.86 GB between
@@ -267,6 +273,7 @@ def main():
         "quantize_frac_hbm": round(min(kernels["quantize_x"]["frac_hbm"],
                                        kernels["quantize_h"]["frac_hbm"]), 4),
         "load_time_ms": {"prequantize_w1_w2": round(load_ms, 3)},
+        "event_ms_spread": spread,
     }
 
     # ---- per-token activation scales at the fc_in shape: quantize X per row + mm_fp4 with row alphas
