@@ -63,9 +63,11 @@ def gemm_metrics(c: np.ndarray, ref: np.ndarray) -> dict:
     ref = np.asarray(ref, dtype=np.float64)
     nref = np.linalg.norm(ref)
     mref = np.max(np.abs(ref))
+    b = bf16_of(ref)
     return {
         "rel_fro": float(np.linalg.norm(c - ref) / nref) if nref else float(np.linalg.norm(c)),
-        "rel_fro_vs_bf16_ref": float(np.linalg.norm(c - bf16_of(ref)) / nref) if nref else 0.0,
+        "rel_fro_vs_bf16_ref": float(np.linalg.norm(c - b) / nref) if nref else 0.0,
+        "rel_fro_of_bf16_ref": float(np.linalg.norm(b - ref) / nref) if nref else 0.0,
         "max_rel": float(np.max(np.abs(c - ref)) / mref) if mref else float(np.max(np.abs(c))),
     }
 
@@ -77,9 +79,16 @@ def assert_gemm_f32(c: np.ndarray, ref: np.ndarray, what: str = ""):
 
 
 def assert_gemm_bf16(c: np.ndarray, ref: np.ndarray, what: str = ""):
+    """bf16 output against the fp64 reference: its relative Frobenius error exceeds that of the
+    reference's own nearest-even bf16 rounding by at most REL_FRO (a bf16 cast alone is about
+    1.7e-3 from the fp64 product), and every element is within MAX_REL * max|ref|. Measuring the
+    excess over the perfectly rounded result rather than the distance to it allows the one-ulp
+    flips at exact bf16 ties: MX operands are small integers times powers of two, so a product can
+    sit exactly on a tie in fp32 and round to even while the exact sum, nudged by terms below fp32's
+    reach, rounds the other way."""
     m = gemm_metrics(c, ref)
     say(what, "bf16 out", m)
-    assert m["rel_fro_vs_bf16_ref"] <= REL_FRO, (what, m)
+    assert m["rel_fro"] <= m["rel_fro_of_bf16_ref"] + REL_FRO, (what, m)
     assert m["max_rel"] <= MAX_REL, (what, m)
 
 

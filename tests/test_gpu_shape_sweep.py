@@ -1,0 +1,102 @@
+"""Seeded sweep over random shapes (ragged M and N, several K, strided rows) for every GEMM and
+quantizer entry point, against the oracle on every element or byte.
+
+The fixed-shape tests pin known edge cases; this sweep adds breadth: tile remainders in both M and
+N at once, K that ends on a half stage, and row strides above K, drawn from one seed so a failure
+names a reproducible case.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_precision_nvfp4_amd as bsp
+import workloads as W
+from oracle import mxfp4 as X4
+from oracle import mxfp8 as X
+from oracle import nvfp4 as N
+from tests.gpu_util import (assert_gemm_bf16, assert_gemm_f32, dev_bf16, dev_u8, host_u8, say,
+                            scalar)
+
+pytestmark = pytest.mark.gpu
+
+_RNG = np.random.default_rng(20261203)
+GEMM_CASES = [(int(_RNG.integers(1, 700)), int(_RNG.integers(1, 700)), int(_RNG.integers(1, 9)) * 128)
+              for _ in range(10)]
+QUANT_CASES = [(int(_RNG.integers(1, 600)), int(_RNG.integers(1, 40)) * 32, int(_RNG.integers(0, 3)) * 8)
+               for _ in range(10)]
+
+
+def _nvfp4_operand(rng, rows, k):
+    packed = rng.integers(0, 256, size=(rows, k // 2), dtype=np.uint8)
+    rp, cp = N.sf_padded_shape(rows, k)
+    lin = np.zeros((rp, cp), dtype=np.uint8)
+    lin[:rows, : k // 16] = rng.integers(0, 0x7F, size=(rows, k // 16))
+    return packed, N.swizzle_128x4(lin)
+
+
+def _mxfp4_operand(rng, rows, k):
+    packed = rng.integers(0, 256, size=(rows, k // 2), dtype=np.uint8)
+    rp, cp = X4.sf_padded_shape(rows, k)
+    lin = np.zeros((rp, cp), dtype=np.uint8)
+    lin[:rows, : k // 32] = rng.integers(110, 140, size=(rows, k // 32))
+    return packed, N.swizzle_128x4(lin)
+
+
+def _mx8_operand(rng, rows, k):
+    q = rng.integers(0, 256, size=(rows, k), dtype=np.uint8)
+    q[(q & 0x7F) == 0x7F] = 0x3F
+    return q, rng.integers(110, 140, size=(rows, k // 32), dtype=np.uint8)
+
+
+@pytest.mark.parametrize("m,n,k", GEMM_CASES)
+def test_gemm_sweep(m, n, k):
+    """mm_fp4 (K and K - 64, the half-stage tail), mm_mxfp8 and mm_mxfp4 on every element."""
+    say("gemm sweep", m, n, k)
+    rng = np.random.default_rng(m * 1009 + n * 31 + k)
+    for kk in (k, k - 64) if k > 64 else (k,):
+        pa, sa = _nvfp4_operand(rng, m, kk)
+        pb, sb = _nvfp4_operand(rng, n, kk)
+        ref = N.mm_fp4(pa, sa, pb, sb, np.float32(0.75), m, n, kk)
+        args = (dev_u8(pa), dev_u8(sa), dev_u8(pb), dev_u8(sb), scalar(0.75))
+        assert_gemm_f32(bsp.bsp_mm_fp4(*args, out_dtype=torch.float32).cpu().numpy().astype(np.float64),
+                        ref, f"mm_fp4 {m}x{n}x{kk}")
+        assert_gemm_bf16(bsp.bsp_mm_fp4(*args).float().cpu().numpy().astype(np.float64), ref,
+                         f"mm_fp4 bf16 {m}x{n}x{kk}")
+    qa, s8a = _mx8_operand(rng, m, k)
+    qb, s8b = _mx8_operand(rng, n, k)
+    ref = X.mm_mxfp8(qa, s8a, qb, s8b, m, n, k)
+    c = bsp.bsp_mm_mxfp8(dev_u8(qa), dev_u8(s8a), dev_u8(qb), dev_u8(s8b))
+    assert_gemm_bf16(c.float().cpu().numpy().astype(np.float64), ref, f"mm_mxfp8 {m}x{n}x{k}")
+    pa, sa = _mxfp4_operand(rng, m, k)
+    pb, sb = _mxfp4_operand(rng, n, k)
+    ref = X4.mm_mxfp4(pa, sa, pb, sb, np.float32(1.0), m, n, k)
+    c = bsp.bsp_mm_mxfp4(dev_u8(pa), dev_u8(sa), dev_u8(pb), dev_u8(sb), None)
+    assert_gemm_bf16(c.float().cpu().numpy().astype(np.float64), ref, f"mm_mxfp4 {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("m,k,pad", QUANT_CASES)
+def test_quantize_sweep(m, k, pad):
+    """NVFP4 (tensor scale, per token, layout_8x4), MXFP8 and MXFP4 quantizers on rows of stride
+    K + pad: every packed, element and scale byte, padding included."""
+    say("quantize sweep", m, k, pad)
+    xb = W.small_case(m, k, seed=m * 17 + k + pad, std=1.5, outlier_frac=0.03)
+    big = np.zeros((m, k + pad), dtype=np.uint16)
+    big[:, :k] = xb
+    x = dev_bf16(big)[:, :k]
+    g = N.global_sf(xb)[0]
+    p, sf = bsp.bsp_nvfp4_quantize(x, scalar(g))
+    rp, rs = N.quantize(xb, g)
+    assert np.array_equal(host_u8(p), rp) and np.array_equal(host_u8(sf).ravel(), rs)
+    p, sf, gr = bsp.bsp_nvfp4_quantize_per_token(x)
+    rp, rs, rg = N.quantize_per_token(xb)
+    assert np.array_equal(gr.cpu().numpy(), rg)
+    assert np.array_equal(host_u8(p), rp) and np.array_equal(host_u8(sf).ravel(), rs)
+    p, sf = bsp.bsp_nvfp4_quantize_8x4(x, scalar(g))
+    rp, rs = N.quantize(xb, g, layout="8x4")
+    assert np.array_equal(host_u8(p), rp) and np.array_equal(host_u8(sf).ravel(), rs)
+    q, s = bsp.bsp_mxfp8_quantize(x)
+    rq, rs = X.quantize(xb)
+    assert np.array_equal(host_u8(q), rq) and np.array_equal(host_u8(s), rs)
+    p, sf = bsp.bsp_mxfp4_quantize(x)
+    rp, rs = X4.quantize(xb)
+    assert np.array_equal(host_u8(p), rp) and np.array_equal(host_u8(sf).ravel(), rs)
