@@ -100,3 +100,56 @@ def test_quantize_sweep(m, k, pad):
     p, sf = bsp.bsp_mxfp4_quantize(x)
     rp, rs = X4.quantize(xb)
     assert np.array_equal(host_u8(p), rp) and np.array_equal(host_u8(sf).ravel(), rs)
+
+
+VARIANT_CASES = GEMM_CASES[:6]
+
+
+@pytest.mark.parametrize("m,n,k", VARIANT_CASES)
+def test_gemm_variant_sweep(m, n, k):
+    """The GEMM entry points with per-token alphas, layout_8x4 activation scales and fused bias on
+    the sweep's shapes, every element against the oracle."""
+    from oracle import linear as L
+    say("gemm variant sweep", m, n, k)
+    rng = np.random.default_rng(m * 7 + n * 13 + k)
+    pa, sa = _nvfp4_operand(rng, m, k)
+    pb, sb = _nvfp4_operand(rng, n, k)
+    args = (dev_u8(pa), dev_u8(sa), dev_u8(pb), dev_u8(sb))
+    xg = (10.0 ** rng.uniform(-2, 3, size=m)).astype(np.float32)
+    wg = np.float32(321.5)
+    ref = N.mm_fp4_rowscale(pa, sa, pb, sb, xg, wg, m, n, k)
+    c = bsp.bsp_mm_fp4_per_token(*args, torch.from_numpy(xg).cuda(), scalar(wg))
+    assert_gemm_bf16(c.float().cpu().numpy().astype(np.float64), ref, f"per-token {m}x{n}x{k}")
+    sa8 = N.swizzle_8x4(N.unswizzle_128x4(sa, *N.sf_padded_shape(m, k))[:N.sf_padded_shape_8x4(m, k)[0]])
+    ref = N.mm_fp4(pa, sa8, pb, sb, np.float32(0.5), m, n, k, a_layout="8x4")
+    c = bsp.bsp_mm_fp4_8x4(dev_u8(pa), dev_u8(sa8), dev_u8(pb), dev_u8(sb), scalar(0.5), out_dtype=torch.float32)
+    assert_gemm_f32(c.cpu().numpy().astype(np.float64), ref, f"8x4 {m}x{n}x{k}")
+    # bias: the NVFP4 / MXFP4 outputs are the bf16 product plus the bf16 bias (the pages' bf16 add,
+    # compared bit for bit with torch's add on the device); the MXFP8 one is the fp32 product plus the
+    # fp32 bias, rounded once, against the oracle's exact product plus bias
+    bbits = W.f32_to_bf16_bits(rng.normal(0.0, float(np.std(ref)) + 1e-30, size=n).astype(np.float32))
+    bias = dev_bf16(bbits)
+    c0 = bsp.bsp_mm_fp4(*args, scalar(0.5))
+    assert_gemm_bf16(c0.float().cpu().numpy().astype(np.float64), N.mm_fp4(pa, sa, pb, sb, np.float32(0.5), m, n, k),
+                     f"mm_fp4 {m}x{n}x{k}")
+    c = bsp.bsp_mm_fp4_bias(*args, scalar(0.5), bias)
+    assert torch.equal(c.view(torch.int16), (c0.float() + bias.float()).bfloat16().view(torch.int16))
+    qa, s8a = _mx8_operand(rng, m, k)
+    qb, s8b = _mx8_operand(rng, n, k)
+    ref = X.mm_mxfp8(qa, s8a, qb, s8b, m, n, k)
+    bf = rng.normal(0.0, float(np.std(ref)) + 1e-30, size=n).astype(np.float32)
+    a8 = (dev_u8(qa), dev_u8(s8a), dev_u8(qb), dev_u8(s8b))
+    c32 = bsp.bsp_mm_mxfp8(*a8, out_dtype=torch.float32)
+    cb32 = bsp.bsp_mm_mxfp8_bias(*a8, torch.from_numpy(bf).cuda(), out_dtype=torch.float32)
+    assert np.array_equal(cb32.cpu().numpy(), (c32.cpu().numpy() + bf).astype(np.float32))
+    c = bsp.bsp_mm_mxfp8_bias(*a8, torch.from_numpy(bf).cuda())
+    assert torch.equal(c, cb32.bfloat16())
+    assert_gemm_bf16(c.float().cpu().numpy().astype(np.float64), L.gemm_plus_bias(ref, bf), f"mxfp8 bias {m}x{n}x{k}")
+    pa4, sa4 = _mxfp4_operand(rng, m, k)
+    pb4, sb4 = _mxfp4_operand(rng, n, k)
+    a4 = (dev_u8(pa4), dev_u8(sa4), dev_u8(pb4), dev_u8(sb4))
+    c0 = bsp.bsp_mm_mxfp4(*a4, scalar(0.25))
+    assert_gemm_bf16(c0.float().cpu().numpy().astype(np.float64),
+                     X4.mm_mxfp4(pa4, sa4, pb4, sb4, np.float32(0.25), m, n, k), f"mm_mxfp4 {m}x{n}x{k}")
+    c = bsp.bsp_mm_mxfp4_bias(*a4, bias, scalar(0.25))
+    assert torch.equal(c.view(torch.int16), (c0.float() + bias.float()).bfloat16().view(torch.int16))
