@@ -36,6 +36,15 @@ int main(void) {
   CHECK(bsp_mm_mxfp8((const uint8_t*)p, (const uint8_t*)p, (const uint8_t*)p, (const uint8_t*)p, 8, 8, 64,
                      p, 8, BSP_OUT_BF16, NULL) == BSP_ESHAPE);
   CHECK(bsp_nvfp4_alpha(NULL, (const float*)p, (float*)p, NULL) == BSP_EINVAL);
+  /* the norm + quantize prologue: eps must be positive and finite, K a multiple of 16 */
+  CHECK(bsp_rmsnorm_bf16(p, 4, 32, 32, NULL, 0.0f, p, 32, NULL) == BSP_EINVAL);
+  CHECK(bsp_rmsnorm_bf16(p, 4, 24, 24, NULL, 1e-6f, p, 24, NULL) == BSP_ESHAPE);
+  CHECK(bsp_nvfp4_quantize_rmsnorm(p, 4, 32, 32, NULL, 1e-6f, (const float*)p, NULL, (uint8_t*)p, NULL) ==
+        BSP_EINVAL);
+  CHECK(bsp_nvfp4_quantize_rmsnorm(NULL, 0, 32, 32, NULL, 1e-6f, NULL, NULL, NULL, NULL) == BSP_OK);
+  /* one row-tile past the quantizer's grid limit */
+  CHECK(bsp_nvfp4_quantize(p, 65535LL * 128 + 1, 32, 32, (const float*)p, (uint8_t*)p, (uint8_t*)p, NULL) ==
+        BSP_ESHAPE);
   printf("c consumer ok\n");
   return 0;
 }
