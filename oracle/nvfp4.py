@@ -66,6 +66,8 @@ def global_sf(w_bits: np.ndarray):
 
     gsf = fl32(2688 / amax), or 1.0 when amax == 0; inv_gsf = fl32(1 / gsf) is
     the fp32 weight alpha the FastVideo nvfp4_config.py page stores at load.
+    One division, as both FastVideo pages write it; SGLang nvfp4_online.py takes the
+    reciprocal of the decode scale fl32(amax / 2688) instead, one ulp off for some amax.
     """
     amax = tensor_amax(w_bits)
     gsf = F32(1.0) if amax == F32(0.0) else F32(GSF_NUMERATOR / amax)
@@ -90,7 +92,11 @@ def global_sf_4over6(w_bits: np.ndarray):
 # alpha
 # ----------------------------------------------------------------------------------------
 def alpha(x_gsf, w_gsf) -> np.float32:
-    """alpha = fl32(1 / fl32(x_gsf * w_gsf)) (fp32 throughout, reading U10)."""
+    """alpha = fl32(1 / fl32(x_gsf * w_gsf)) (fp32 throughout, reading U10).
+
+    FastVideo nvfp4_qat_config.py, ``apply``, writes this order. FastVideo nvfp4_config.py,
+    ``NVFP4QuantizeMethod.apply``, divides the stored fp32 fl32(1/w_gsf) by x_gsf instead; the two
+    agree bit for bit when x_gsf is 1 and may differ by one ulp otherwise."""
     return F32(F32(1.0) / F32(F32(x_gsf) * F32(w_gsf)))
 
 

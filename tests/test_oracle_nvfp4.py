@@ -46,6 +46,16 @@ def test_global_sf_cases():
         assert inv == f32(1.0) / f32(gsf)
 
 
+def test_global_sf_split_between_pages_is_pinned():
+    # amax 3: FastVideo's one division gives 896 exactly (golden); SGLang's decode scale
+    # fl32(3/2688) and its reciprocal give 0x445FFFFF (hand-worked in global_sf_cases.txt)
+    w = np.array([[3.0, -1.0]], dtype=np.float32)
+    g, _, a = N.global_sf(bits(w))
+    two_step = f32(f32(1.0) / f32(f32(3.0) / f32(2688.0)))
+    assert two_step.view(np.uint32) == 0x445FFFFF
+    assert g == f32(896.0) and g != two_step
+
+
 def test_global_sf_nan_inf():
     w = np.array([[1.0, np.nan, -3.0, 2.0]], dtype=np.float32)
     g, _, a = N.global_sf(bits(w))
@@ -69,6 +79,17 @@ def test_global_scale_block_gets_448():
 def test_alpha():
     assert N.alpha(1.0, 43008.0) == f32(1.0) / f32(43008.0)
     assert N.alpha(2.0, 3.0) == f32(1.0) / f32(6.0)
+    # hand-worked cases where the FastVideo nvfp4_qat_config.py form 1/(x*w) and the FastVideo
+    # nvfp4_config.py form (1/w)/x round differently (golden file); the oracle takes the first
+    for line in golden_lines("alpha_cases.txt"):
+        x, w, bits_hex = line.split()
+        want = np.array([int(bits_hex, 16)], dtype=np.uint32).view(np.float32)[0]
+        assert N.alpha(float(x), float(w)) == want, line
+    # the golden set discriminates: the other page's form misses at least one case
+    other = [f32(f32(f32(1.0) / f32(float(w))) / f32(float(x))) for x, w, _ in
+             (l.split() for l in golden_lines("alpha_cases.txt"))]
+    assert any(o != N.alpha(float(x), float(w)) for o, (x, w, _) in
+               zip(other, (l.split() for l in golden_lines("alpha_cases.txt"))))
     # static x_gsf = 1 makes alpha the stored fp32 1/w_gsf bit for bit
     for g in (2688.0, 123456.78, 0.37):
         assert N.alpha(1.0, g) == f32(1.0) / f32(g)
