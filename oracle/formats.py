@@ -114,3 +114,26 @@ def e8m0_decode(codes: np.ndarray) -> np.ndarray:
     c = np.asarray(codes, dtype=np.int64)
     out = np.ldexp(1.0, c - 127)
     return np.where(c == 255, np.nan, out)
+
+
+# ----------------------------------------------------------------------------------------
+# non-finite inputs
+# ----------------------------------------------------------------------------------------
+BF16_MAX_BITS = 0x7F7F   # largest finite bf16, 1.9921875 * 2^127
+
+
+def bf16_nan_to_num(bits: np.ndarray) -> np.ndarray:
+    """nan_to_num on bf16 bit patterns: NaN -> +0, +inf -> +largest finite, -inf -> -largest finite.
+
+    The substitution the FastVideo pages (``convert_model_to_fp4``, ``convert_model_to_nvfp4``) and
+    the SGLang page (``_quantize_weight_nvfp4``) apply before taking a weight's amax; the quantizers
+    here encode the substituted values (reading U9), so a block is encoded from the same values
+    its global scale was taken from.
+    """
+    b = np.asarray(bits, dtype=np.uint16)
+    mag = b & np.uint16(0x7FFF)
+    out = b.copy()
+    out[mag > 0x7F80] = 0
+    inf = mag == 0x7F80
+    out[inf] = (b[inf] & np.uint16(0x8000)) | np.uint16(BF16_MAX_BITS)
+    return out

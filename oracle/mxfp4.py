@@ -19,7 +19,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .formats import e2m1_decode, e2m1_encode, e8m0_decode
+from .formats import bf16_nan_to_num, e2m1_decode, e2m1_encode, e8m0_decode
 from .nvfp4 import pack_nibbles, sf_offset, swizzle_128x4, unpack_nibbles
 
 F32 = np.float32
@@ -54,7 +54,7 @@ def quantize_blocks(xf: np.ndarray):
 
 def quantize(x_bits: np.ndarray, layout: str = "128x4"):
     """bf16 X [M, K] (K % 32 == 0) -> (packed [M, K/2], scales: flat 128x4 bytes or [M, K/32])."""
-    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    x_bits = bf16_nan_to_num(x_bits)   # NaN -> 0, +-inf -> +-largest finite bf16 (reading U9)
     m, k = x_bits.shape
     if k % GROUP:
         raise ValueError("K must be a multiple of 32")

@@ -22,7 +22,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .formats import e4m3_decode, e4m3_encode, e8m0_decode
+from .formats import bf16_nan_to_num, e4m3_decode, e4m3_encode, e8m0_decode
 
 F32 = np.float32
 GROUP = 32
@@ -54,7 +54,7 @@ def quantize_blocks(xf: np.ndarray):
 
 def quantize(x_bits: np.ndarray):
     """bf16 X [M, K] (K % 32 == 0) -> (e4m3 [M, K] uint8, e8m0 [M, K/32] uint8), row-major."""
-    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    x_bits = bf16_nan_to_num(x_bits)   # NaN -> 0, +-inf -> +-largest finite bf16 (reading U9)
     m, k = x_bits.shape
     if k % GROUP:
         raise ValueError("K must be a multiple of 32")

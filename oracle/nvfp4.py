@@ -24,14 +24,14 @@ Readings where the pages are silent (U-numbers as listed in the design notes):
 U1 fp32 op order in the quantizer (below); U2 e4m3 scale RNE + saturate to 448;
 U3 e2m1 RNE + saturate to 6; U4 sign of zero kept; U5 even k in the low nibble;
 U6 the 128x4 byte offset (``sf_offset``); U7 padded scale bytes are 0x00;
-U8 gsf = 1 when amax == 0; U10 alpha from the fp32 gsf; U11 2688/amax is one
-IEEE fp32 division.
+U8 gsf = 1 when amax == 0; U9 NaN / +-inf are quantized as nan_to_num gives them;
+U10 alpha from the fp32 gsf; U11 2688/amax is one IEEE fp32 division.
 """
 from __future__ import annotations
 
 import numpy as np
 
-from .formats import e2m1_decode, e2m1_encode, e4m3_decode, e4m3_encode
+from .formats import bf16_nan_to_num, e2m1_decode, e2m1_encode, e4m3_decode, e4m3_encode
 
 F32 = np.float32
 BLOCK = 16                       # elements per e4m3 scale along K
@@ -222,8 +222,9 @@ def quantize(x_bits: np.ndarray, gsf, layout: str = "128x4"):
     Rp*Cp bytes (layout "128x4"), the flat 8x4-layout buffer (layout "8x4", rows padded to 8),
     or the [M, K/16] row-major bytes (layout "linear").
     Padded scale rows/columns hold 0x00, the scale of an all-zero padded block.
+    NaN and +-inf are encoded as 0 and +-largest finite bf16 (reading U9).
     """
-    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    x_bits = bf16_nan_to_num(x_bits)
     m, k = x_bits.shape
     if k % BLOCK:
         raise ValueError("K must be a multiple of 16")
@@ -254,8 +255,9 @@ def row_global_sf(x_bits: np.ndarray) -> np.ndarray:
 
 def quantize_per_token(x_bits: np.ndarray, layout: str = "128x4"):
     """NVFP4 quantize with one encode scale per row; returns (packed, sf, gsf_rows [M] fp32).
-    Row m is quantized exactly as ``quantize`` would with gsf = gsf_rows[m]."""
-    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    Row m is quantized exactly as ``quantize`` would with gsf = gsf_rows[m] (non-finite values
+    substituted as there, reading U9)."""
+    x_bits = bf16_nan_to_num(x_bits)
     m, k = x_bits.shape
     if k % BLOCK:
         raise ValueError("K must be a multiple of 16")
