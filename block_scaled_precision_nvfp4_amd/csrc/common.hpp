@@ -165,6 +165,45 @@ __device__ __forceinline__ void gelu_table_fill(uint16_t* tab, int t, int nt) {
 
 typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 
+// ---------------------------------------------------------------------------------------------
+// device: the values a quantizer encodes. Non-finite inputs are encoded as nan_to_num gives them
+// (NaN -> +0, +-inf -> +-largest finite bf16), the substitution the pages apply before a weight's
+// amax, so a block's scale and its elements come from the same finite values.
+// ---------------------------------------------------------------------------------------------
+// Largest magnitude among 8 bf16 values, as bf16 bits: magnitude bit patterns of non-negative
+// bf16 values order like the values, so this is an integer max (packed 16-bit maxes). At least
+// 0x7F80 exactly when one of the values is an infinity or a NaN.
+__device__ __forceinline__ uint32_t mag_bits8(const uint4& v) {
+  const u16x2_t a = __builtin_bit_cast(u16x2_t, v.x & 0x7FFF7FFFu);
+  const u16x2_t b = __builtin_bit_cast(u16x2_t, v.y & 0x7FFF7FFFu);
+  const u16x2_t c = __builtin_bit_cast(u16x2_t, v.z & 0x7FFF7FFFu);
+  const u16x2_t d = __builtin_bit_cast(u16x2_t, v.w & 0x7FFF7FFFu);
+  const u16x2_t m = __builtin_elementwise_max(__builtin_elementwise_max(a, b),
+                                              __builtin_elementwise_max(c, d));
+  return max((uint32_t)m[0], (uint32_t)m[1]);
+}
+
+__device__ __forceinline__ uint32_t bf16_nan_to_num(uint32_t h) {
+  const uint32_t m = h & 0x7FFFu;
+  return m > 0x7F80u ? 0u : (m == 0x7F80u ? (h & 0x8000u) | 0x7F7Fu : h);
+}
+
+__device__ __forceinline__ uint32_t bf16x2_nan_to_num(uint32_t w) {
+  return bf16_nan_to_num(w & 0xFFFFu) | (bf16_nan_to_num(w >> 16) << 16);
+}
+
+// The largest magnitude of the 8 bf16 values in v as an fp32 (exact), after replacing v by its
+// nan_to_num when one of the values is not finite (rare: one compare on the common path).
+__device__ __forceinline__ float finite_absmax8(uint4& v) {
+  uint32_t mb = mag_bits8(v);
+  if (mb >= 0x7F80u) {
+    v = make_uint4(bf16x2_nan_to_num(v.x), bf16x2_nan_to_num(v.y), bf16x2_nan_to_num(v.z),
+                   bf16x2_nan_to_num(v.w));
+    mb = mag_bits8(v);
+  }
+  return __uint_as_float(mb << 16);
+}
+
 // gelu of the two bf16 values in w (bits 0-15 and 16-31) from the table; sets bits of miss when
 // either lies outside it (its result is then meaningless)
 __device__ __forceinline__ uint32_t gelu2_tab(uint32_t w, const uint16_t* tab, uint32_t& miss) {

@@ -67,27 +67,36 @@ __device__ __forceinline__ void load_bias(float (&bq)[4][4][4], int64_t n0w, int
       }
 }
 
+// ACC16: the accumulators hold 2^-16 times the products (mm_fp4's f16 operands each carry 2^-8).
+// The 2^16 goes onto the accumulator, alpha * (acc * 2^16): acc * 2^16 is exact and far below
+// fp32's range (|acc| <= 2^31 for K <= 2^24), so the one rounding is that of the exact
+// alpha * sum, for every finite alpha (2^16 folded into alpha instead would overflow above 2^112).
+template <bool ACC16>
+__device__ __forceinline__ float acc_value(float a) {
+  return ACC16 ? a * 65536.0f : a;
+}
+
 // The four fp32 results of piece (m, n, b), bias of kind kBiasF32Before (or any kind for fp32
 // output) included.
-template <bool OUT_F32, int BIAS>
+template <bool OUT_F32, int BIAS, bool ACC16>
 __device__ __forceinline__ void piece_f32(const f32x16 (&acc)[4][4], const float (&alpha)[4],
                                           const float (&bq)[4][4][4], int m, int n, int b,
                                           float (&v)[4]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    v[i] = alpha[m] * acc[n][m][4 * b + i];
+    v[i] = alpha[m] * acc_value<ACC16>(acc[n][m][4 * b + i]);
     if (BIAS != kBiasNone && (OUT_F32 || BIAS == kBiasF32Before)) v[i] += bq[n][b][i];
   }
 }
 
 // The four bf16 results of piece (m, n, b) as two packed pairs (nearest even; a kBiasBf16After
 // bias is added to the rounded product and the sum rounded again).
-template <int BIAS>
+template <int BIAS, bool ACC16>
 __device__ __forceinline__ void piece_bf16(const f32x16 (&acc)[4][4], const float (&alpha)[4],
                                            const float (&bq)[4][4][4], int m, int n, int b,
                                            uint32_t& p01, uint32_t& p23) {
   float v[4];
-  piece_f32<false, BIAS>(acc, alpha, bq, m, n, b, v);
+  piece_f32<false, BIAS, ACC16>(acc, alpha, bq, m, n, b, v);
   p01 = bf16x2_rne(v[0], v[1]);
   p23 = bf16x2_rne(v[2], v[3]);
   if (BIAS == kBiasBf16After) {
@@ -101,7 +110,7 @@ __device__ __forceinline__ void piece_bf16(const f32x16 (&acc)[4][4], const floa
 }
 
 // Direct epilogue: each lane stores its 8-byte (bf16) or 16-byte (fp32) pieces, with bounds checks.
-template <bool OUT_F32, int BIAS = kBiasNone>
+template <bool OUT_F32, int BIAS, bool ACC16>
 __device__ __forceinline__ void store_wave_tile(const f32x16 (&acc)[4][4], const float (&alpha)[4],
                                                 int64_t m0w, int64_t n0w, int64_t M, int64_t N,
                                                 void* out, int64_t ldc, bool vec_store, int li, int h,
@@ -119,7 +128,7 @@ __device__ __forceinline__ void store_wave_tile(const f32x16 (&acc)[4][4], const
         const int64_t gn = n0w + n * 32 + 8 * b + 4 * h;
         if (OUT_F32) {
           float v[4];
-          piece_f32<true, BIAS>(acc, alpha, bq, m, n, b, v);
+          piece_f32<true, BIAS, ACC16>(acc, alpha, bq, m, n, b, v);
           float* o = static_cast<float*>(out) + gm * ldc + gn;
           if (vec_store && gn + 3 < N) {
             *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
@@ -131,7 +140,7 @@ __device__ __forceinline__ void store_wave_tile(const f32x16 (&acc)[4][4], const
           }
         } else {
           uint32_t p01, p23;
-          piece_bf16<BIAS>(acc, alpha, bq, m, n, b, p01, p23);
+          piece_bf16<BIAS, ACC16>(acc, alpha, bq, m, n, b, p01, p23);
           uint16_t* o = static_cast<uint16_t*>(out) + gm * ldc + gn;
           if (vec_store && gn + 3 < N) {
             *reinterpret_cast<uint2*>(o) = make_uint2(p01, p23);
@@ -156,7 +165,7 @@ __device__ __forceinline__ void store_wave_tile(const f32x16 (&acc)[4][4], const
 constexpr int kEpiRowBytes = 272;
 constexpr int kEpiWaveBytes = 64 * kEpiRowBytes;
 
-template <int BIAS = kBiasNone>
+template <int BIAS, bool ACC16>
 __device__ __forceinline__ void store_wave_tile_staged(const f32x16 (&acc)[4][4],
                                                        const float (&alpha)[4], int64_t m0w,
                                                        int64_t n0w, int64_t N, void* out,
@@ -173,7 +182,7 @@ __device__ __forceinline__ void store_wave_tile_staged(const f32x16 (&acc)[4][4]
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           uint32_t p01, p23;
-          piece_bf16<BIAS>(acc, alpha, bq, 2 * half + mm, n, b, p01, p23);
+          piece_bf16<BIAS, ACC16>(acc, alpha, bq, 2 * half + mm, n, b, p01, p23);
           *reinterpret_cast<uint2*>(lds + (mm * 32 + li) * kEpiRowBytes + (n * 32 + 8 * b + 4 * h) * 2) =
               make_uint2(p01, p23);
         }
@@ -193,7 +202,7 @@ __device__ __forceinline__ void store_wave_tile_staged(const f32x16 (&acc)[4][4]
 // workgroup's stage memory, at least 4 * kEpiWaveBytes bytes, which no wave reads or loads into
 // any more (every global -> LDS load has completed). The choice of path is uniform across the
 // workgroup, so the barrier is reached by all waves or none.
-template <bool OUT_F32, int BIAS = kBiasNone>
+template <bool OUT_F32, int BIAS, bool ACC16>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], const float (&alpha)[4],
                                            int64_t m0, int64_t n0, int wm, int wn, int64_t M,
                                            int64_t N, void* out, int64_t ldc, bool vec_store,
@@ -203,10 +212,10 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], const floa
                      (reinterpret_cast<uintptr_t>(out) & 15) == 0;
   if (whole) {
     __syncthreads();   // every wave is done reading the stage buffers the images overlay
-    store_wave_tile_staged<BIAS>(acc, alpha, m0 + wm * 128, n0 + wn * 128, N, out, ldc,
+    store_wave_tile_staged<BIAS, ACC16>(acc, alpha, m0 + wm * 128, n0 + wn * 128, N, out, ldc,
                                  lds + wave * kEpiWaveBytes, lane, li, h, bias);
   } else {
-    store_wave_tile<OUT_F32, BIAS>(acc, alpha, m0 + wm * 128, n0 + wn * 128, M, N, out, ldc,
+    store_wave_tile<OUT_F32, BIAS, ACC16>(acc, alpha, m0 + wm * 128, n0 + wn * 128, M, N, out, ldc,
                                    vec_store, li, h, bias);
   }
 }
@@ -241,9 +250,9 @@ __device__ __forceinline__ void gelu_nvfp4_half(const uint8_t* lds, int half, in
   for (int it = 0; it < 16; ++it) {
     const int rr = half * 64 + it * 4 + (lane >> 4);  // row inside the wave's 128 rows
     const int64_t gm = m0w + rr;
+    const float a = pair_max(finite_absmax8(gv[it]));
     float f[8];
     unpack8(gv[it], f);
-    const float a = pair_max(absmax8(f));
     const uint32_t S = (ROWS_IN || gm < M) ? e4m3_encode_pos(g * (a * kSixth)) : 0u;
     const float r = rtab[S];
     uint32_t o = 0;
@@ -278,7 +287,7 @@ __device__ __forceinline__ void store_wave_tile_gelu_nvfp4(const f32x16 (&acc)[4
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           uint32_t p01, p23;
-          piece_bf16<kBiasNone>(acc, alpha, bq, 2 * half + mm, n, b, p01, p23);
+          piece_bf16<kBiasNone, true>(acc, alpha, bq, 2 * half + mm, n, b, p01, p23);
           *reinterpret_cast<uint2*>(lds + (mm * 32 + li) * kEpiRowBytes + (n * 32 + 8 * b + 4 * h) * 2) =
               make_uint2(p01, p23);
         }

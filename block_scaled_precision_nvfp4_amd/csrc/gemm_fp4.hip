@@ -61,7 +61,7 @@ __device__ __forceinline__ int chunk_slot(int row, int c) {
 // f16 holding (e4m3 scale byte) * 2^-8, built from the bits alone: an e4m3 code c (non-negative)
 // shifted left by 7 is an f16 with exponent field e and mantissa m, i.e. 2^(e-15) (1 + m/8) for
 // e >= 1 and the f16 denormal m * 2^-17 for e == 0, which is the e4m3 value times 2^-8 in both
-// cases. The 2^-8 of each operand is undone in the epilogue (alpha * 2^16).
+// cases. The 2^-8 of each operand is undone in the epilogue (alpha * (acc * 2^16)).
 // A row's scale dword holds the bytes of four K blocks; two shifts and masks place bytes 0 and 2
 // (shift left 7) or bytes 1 and 3 (shift right 1) at bit 7 of the low and high f16 halves, and the
 // packed multiply broadcasts the half it needs. `mask` is 0x3F803F80 (sign bits dropped), or 0 to
@@ -389,17 +389,18 @@ __global__ __launch_bounds__(256, 1) void mm_fp4_kernel(
   }
   wait_vmcnt<0>();
 
-  // operands carried 2^-8 each (scale_pair): the products are 2^-16 of the true ones
+  // operands carried 2^-8 each (scale_pair): the accumulators hold 2^-16 of the true sums, which
+  // the epilogue undoes on the accumulator (ACC16)
   float alpha[4];
   if (ROWSCALE) {
     const float wg = *w_gsf_ptr;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int64_t gm = m0 + wm * 128 + m * 32 + li;
-      alpha[m] = gm < M ? (1.0f / (alpha_ptr[gm] * wg)) * 65536.0f : 0.0f;
+      alpha[m] = gm < M ? 1.0f / (alpha_ptr[gm] * wg) : 0.0f;
     }
   } else {
-    const float a = *alpha_ptr * 65536.0f;
+    const float a = *alpha_ptr;
 #pragma unroll
     for (int m = 0; m < 4; ++m) alpha[m] = a;
   }
@@ -409,7 +410,7 @@ __global__ __launch_bounds__(256, 1) void mm_fp4_kernel(
                           out_gsf, rtab, gtab, reinterpret_cast<uint8_t*>(st), t, wave, lane, li, h);
   } else {
     (void)rtab; (void)gtab; (void)sf_out; (void)out_gsf;
-    store_tile<OUT_F32, BIAS>(acc, alpha, m0, n0, wm, wn, M, N, out, ldc, vec_store,
+    store_tile<OUT_F32, BIAS, true>(acc, alpha, m0, n0, wm, wn, M, N, out, ldc, vec_store,
                               reinterpret_cast<uint8_t*>(st), wave, lane, li, h, bias);
   }
 }

@@ -420,7 +420,7 @@ __global__ __launch_bounds__(256, 1) void mm_mx_kernel(
   const float a = alpha_ptr ? *alpha_ptr : 1.0f;
   const float alpha[4] = {a, a, a, a};
   static_assert(sizeof(st) >= 4 * kEpiWaveBytes, "epilogue images overlay the stage buffers");
-  store_tile<OUT_F32, BIAS>(acc, alpha, m0, n0, wm, wn, M, N, out, ldc, vec_store,
+  store_tile<OUT_F32, BIAS, false>(acc, alpha, m0, n0, wm, wn, M, N, out, ldc, vec_store,
                             reinterpret_cast<uint8_t*>(st), wave, lane, li, h, bias);
 }
 

@@ -189,15 +189,11 @@ __global__ __launch_bounds__(256) void nvfp4_quantize_kernel(const uint16_t* __r
   const int64_t pstep = 8 * half_k;
 #pragma unroll
   for (int s = 0; s < 16; ++s) {
+    uint4 xv[1] = {v[s]};
+    if (GELU) gelu_segments_tab<1>({v[s]}, xv, gtab);  // gelu(0) = 0 keeps the padding zero
+    const float a = pair_max(finite_absmax8(xv[0]));
     float f[8];
-    if (GELU) {  // gelu(0) = 0 keeps the padding zero
-      uint4 gv[1];
-      gelu_segments_tab<1>({v[s]}, gv, gtab);
-      unpack8(gv[0], f);
-    } else {
-      unpack8(v[s], f);
-    }
-    const float a = pair_max(absmax8(f));
+    unpack8(xv[0], f);
     const float sc = g * (a * kSixth);
     const uint32_t S = e4m3_encode_pos(sc);
     const float r = rtab[S];
@@ -282,9 +278,7 @@ __global__ __launch_bounds__(256) void nvfp4_quantize_token_kernel(
     for (int j = 0; j < C; ++j) {
       const int64_t e = sg * seg_elems + (int64_t)(j * 64 + lane) * 8;
       v[j] = (live && e < K) ? load8<VEC>(xr + e) : make_uint4(0u, 0u, 0u, 0u);
-      float f[8];
-      unpack8(v[j], f);
-      amax = fmaxf(amax, absmax8(f));
+      amax = fmaxf(amax, finite_absmax8(v[j]));
     }
   }
 #pragma unroll
@@ -306,9 +300,9 @@ __global__ __launch_bounds__(256) void nvfp4_quantize_token_kernel(
     for (int j = 0; j < C; ++j) {
       const int64_t e = sg * seg_elems + (int64_t)(j * 64 + lane) * 8;
       if (nseg > 1) v[j] = (live && e < K) ? load8<VEC>(xr + e) : make_uint4(0u, 0u, 0u, 0u);
+      const float a = pair_max(finite_absmax8(v[j]));
       float f[8];
       unpack8(v[j], f);
-      const float a = pair_max(absmax8(f));
       const uint32_t S = e4m3_encode_pos(g * (a * kSixth));
       const float r = rtab[wave][S];
       uint32_t out = 0;
@@ -437,8 +431,9 @@ __global__ __launch_bounds__(256) void rmsnorm_token_kernel(
         }
         continue;
       }
-      unpack8(y, f);
-      const float a = pair_max(absmax8(f));
+      uint4 yq = y;
+      const float a = pair_max(finite_absmax8(yq));
+      unpack8(yq, f);
       const uint32_t S = e4m3_encode_pos(g * (a * kSixth));
       const float rs = rtab[S];
       uint32_t o = 0;
@@ -502,9 +497,9 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const uint16_t* __r
   uint8_t* sp = sf + (row0 + rsub) * ng + kk / 32;
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
+    const float a = quad_max(finite_absmax8(v[s]));
     float f[8];
     unpack8(v[s], f);
-    const float a = quad_max(absmax8(f));
     const uint32_t ef = __float_as_uint(a) >> 23;            // biased exponent (a >= 0, finite)
     const uint32_t byte = ef > 8u ? ef - 8u : 0u;            // Es + 127
     const float inv = __uint_as_float((254u - byte) << 23);  // 2^-Es = 2^(127 - byte), exact
@@ -568,9 +563,9 @@ __global__ __launch_bounds__(256) void mxfp4_quantize_kernel(const uint16_t* __r
   const int64_t pstep = 8 * half_k;
 #pragma unroll
   for (int s = 0; s < 16; ++s) {
+    const float a = quad_max(finite_absmax8(v[s]));
     float f[8];
     unpack8(v[s], f);
-    const float a = quad_max(absmax8(f));
     const uint32_t ef = __float_as_uint(a) >> 23;
     const uint32_t byte = ef > 2u ? ef - 2u : 0u;            // Es + 127
     const float inv = __uint_as_float((254u - byte) << 23);  // 2^-Es, exact

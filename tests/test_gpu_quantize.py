@@ -362,3 +362,41 @@ def test_mxfp4_quantize_bit_exact(m, k):
     p, s = bsp.bsp_mxfp4_quantize(dev_bf16(xs))
     rp, rs = X4.quantize(xs)
     assert np.array_equal(host_u8(p), rp) and np.array_equal(host_u8(s).ravel(), rs)
+
+
+# ---------------------------------------------------------------------------------------------
+# non-finite inputs: every quantizer encodes nan_to_num of its input (NaN -> +0, +-inf -> +-largest
+# finite bf16), bit-exact against the oracle
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("gsf", [1.0, 0.37, 2688.0 / 5.0])
+def test_nvfp4_quantize_nonfinite(gsf):
+    say("nvfp4_quantize nonfinite", gsf)
+    xb = W.nonfinite_block(seed=23, rows=200, cols=512)
+    packed, sf = _quant_gpu(xb, f32(gsf))
+    rp, ap = N.quantize(xb, f32(gsf))
+    assert np.array_equal(packed, rp) and np.array_equal(sf, ap)
+    p8, s8 = bsp.bsp_nvfp4_quantize_8x4(dev_bf16(xb), scalar(f32(gsf)))
+    rp8, rs8 = N.quantize(xb, f32(gsf), layout="8x4")
+    assert np.array_equal(host_u8(p8), rp8) and np.array_equal(host_u8(s8).ravel(), rs8)
+
+
+@pytest.mark.parametrize("k", [512, 16400])   # one-pass register path and two-pass path
+def test_nvfp4_quantize_per_token_nonfinite(k):
+    say("nvfp4_quantize_per_token nonfinite", k)
+    xb = W.nonfinite_block(seed=29, rows=70, cols=k)
+    p, sf, g = bsp.bsp_nvfp4_quantize_per_token(dev_bf16(xb))
+    rp, rs, rg = N.quantize_per_token(xb)
+    assert np.array_equal(g.cpu().numpy(), rg)
+    assert np.array_equal(host_u8(p), rp) and np.array_equal(host_u8(sf).ravel(), rs)
+
+
+def test_mx_quantize_nonfinite():
+    from oracle import mxfp4 as X4
+    say("mx quantize nonfinite")
+    xb = W.nonfinite_block(seed=31, rows=130, cols=512)
+    q, sf = bsp.bsp_mxfp8_quantize(dev_bf16(xb))
+    rq, rs = X.quantize(xb)
+    assert np.array_equal(host_u8(q), rq) and np.array_equal(host_u8(sf), rs)
+    p, s = bsp.bsp_mxfp4_quantize(dev_bf16(xb))
+    rp, rs4 = X4.quantize(xb)
+    assert np.array_equal(host_u8(p), rp) and np.array_equal(host_u8(s).ravel(), rs4)

@@ -185,6 +185,26 @@ def special_values_block(seed: int, rows: int, cols: int) -> np.ndarray:
     return f32_to_bf16_bits(v)
 
 
+def nonfinite_block(seed: int, rows: int, cols: int) -> np.ndarray:
+    """bf16 bits: ``special_values_block`` with infinities and NaNs written in.
+
+    About 1 % of the elements become +inf, -inf, a quiet NaN (0x7FC0 / 0xFFC0) or a signalling NaN
+    pattern (0x7F81 / 0xFF81); row 0 is all NaN, row 1 holds one +inf, row 2 one -inf among zeros.
+    """
+    b = special_values_block(seed, rows, cols)
+    rng = np.random.Generator(np.random.PCG64(seed + 1))
+    hit = rng.random((rows, cols)) < 0.01
+    pats = np.array([0x7F80, 0xFF80, 0x7FC0, 0xFFC0, 0x7F81, 0xFF81], dtype=np.uint16)
+    b[hit] = pats[rng.integers(0, pats.size, size=int(hit.sum()))]
+    if rows > 2:
+        b[0] = 0x7FC0
+        b[1] = 0
+        b[1, cols // 3] = 0x7F80
+        b[2] = 0
+        b[2, cols - 1] = 0xFF80
+    return b
+
+
 def config(idx: int) -> Config:
     return CONFIGS[idx]
 
