@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=8192,
                     help="tokens of the FFN the CPU oracle runs for cpu_baseline")
     ap.add_argument("--no-mxfp8", action="store_true")
+    ap.add_argument("--no-shapes", action="store_true", help="skip the other configurations' shapes")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the measured-ceiling probes")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device-to-device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -191,16 +193,18 @@ def main():
                   "p90": round(float(np.percentile(v, 90)), 4)} for n, v in per_step.items()}
 
     # Kernel durations without the event records between a step's launches: the quantize of X and
-    # the RMSNorm + quantize prologue back to back over two copies of X in turn (0.86 GB between
-    # reuses of a buffer, so no pass is served from the 256 MB Infinity Cache), and the unfused
-    # GELU and plain quantize of H (0.9 GB inputs) on their own. The step's own quantize time stays as quantize_x_in_step.
+    # the RMSNorm + quantize prologue back to back over two copies of X and of the outputs in turn
+    # (1.1 GB between reuses of a buffer, so no pass is served from the 256 MB Infinity Cache), and
+    # the unfused GELU and plain quantize of H (0.9 GB inputs) on their own. The step's own quantize
+    # time stays as quantize_x_in_step.
     h = bsp.bsp_gelu_tanh_bf16(y)
     x2 = x.clone()
+    px2, sx2 = torch.empty_like(px), torch.empty_like(sx)
     reps = max(4, 2 * (args.steps // 4))
     kms["quantize_x_in_step"] = kms["quantize_x"]
-    xs = (x, x2)
-    qx_calls = [lambda i=i: bsp.bsp_nvfp4_quantize(xs[i % 2], one, px, sx) for i in range(2)]
-    nq_calls = [lambda i=i: bsp.bsp_nvfp4_quantize_rmsnorm(xs[i % 2], one, None, 1e-6, px, sx)
+    xs, pxs, sxs = (x, x2), (px, px2), (sx, sx2)
+    qx_calls = [lambda i=i: bsp.bsp_nvfp4_quantize(xs[i], one, pxs[i], sxs[i]) for i in range(2)]
+    nq_calls = [lambda i=i: bsp.bsp_nvfp4_quantize_rmsnorm(xs[i], one, None, 1e-6, pxs[i], sxs[i])
                 for i in range(2)]
     for name, fns in (("quantize_x", qx_calls),
                       ("rmsnorm_quantize_x", nq_calls),
@@ -215,7 +219,7 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         kms[name] = e0.elapsed_time(e1) / reps
-    del h, x2
+    del h, x2, px2, sx2
 
     gemm_flops = 2.0 * M * N1 * K1 + 2.0 * M * N2 * N1
     value = gemm_flops / (ms_per_step * 1e-3) / 1e12
@@ -408,6 +412,33 @@ def main():
         "quantize_h_over_copy": round(kernels["quantize_h"]["GB/s"] / copy_gbs, 4)}
     log(json.dumps(result["torch_hbm_rates"]))
 
+    # ---- the other configurations' layer shapes (Wan-1.3B attention and FFN, Wan-14B to_q)
+    if not args.no_shapes:
+        result["shapes"] = measure_shapes(args.steps)
+        log(json.dumps(result["shapes"]))
+
+    # ---- measured-achievable ceilings on this GPU (MFMA-only loops, streaming kernels), and each
+    # headline kernel's fraction of them
+    if not args.no_ceilings:
+        mp = measure_ceilings()
+        result["measured_peak"] = mp
+        f16 = mp["mfma_f16_nvfp4_operands_TFLOPS"]
+        result["roofline"]["frac_of_measured_f16_mfma_loop"] = round(dom_tf / f16, 4)
+        kernels_frac = {
+            "mm_fp4_fc_in_of_f16_mfma_loop": kernels["mm_fp4_fc_in"]["TFLOPS"] / f16,
+            "mm_fp4_fc_out_of_f16_mfma_loop": kernels["mm_fp4_fc_out"]["TFLOPS"] / f16,
+            "quantize_x_of_stream_4to1": kernels["quantize_x"]["GB/s"] / mp["hbm_read4_write1_GBs"],
+            "quantize_x_in_step_of_stream_4to1": kernels["quantize_x_in_step"]["GB/s"] / mp["hbm_read4_write1_GBs"],
+            "gelu_quantize_h_of_stream_4to1": kernels["gelu_quantize_h"]["GB/s"] / mp["hbm_read4_write1_GBs"],
+            "quantize_h_of_stream_4to1": kernels["quantize_h"]["GB/s"] / mp["hbm_read4_write1_GBs"],
+        }
+        if "mxfp8" in result:
+            kernels_frac["mm_mxfp8_of_fp8_mfma_loop"] = result["mxfp8"]["TFLOPS"] / mp["mfma_fp8_scaled_TFLOPS"]
+        if "mxfp4" in result:
+            kernels_frac["mm_mxfp4_of_fp4_mfma_loop"] = result["mxfp4"]["TFLOPS"] / mp["mfma_fp4_scaled_TFLOPS"]
+        result["frac_of_measured_peak"] = {k_: round(v, 4) for k_, v in kernels_frac.items()}
+        log(json.dumps(result["measured_peak"]), json.dumps(result["frac_of_measured_peak"]))
+
     # ---- CPU oracle on a bounded sample of the same workload
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_rows)
@@ -415,6 +446,132 @@ def main():
         log(f"cpu baseline: {r['value']:.4f} {r['unit']} on {r['cores']} threads")
 
     print(json.dumps(result), flush=True)
+
+
+def _event_ms(fns, reps: int) -> float:
+    """Mean event time per call of fns (called in turn, each once untimed first) on torch's stream."""
+    import torch
+    for f in fns:
+        f()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        fns[i % len(fns)]()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def measure_shapes(steps: int) -> dict:
+    """The layer shapes of the Wan-1.3B attention projection (32760x1536x1536), the Wan-1.3B FFN
+    (fc_in 32760x8960x1536, GELU fused into the quantize of H, fc_out 32760x1536x8960) and the
+    Wan-14B to_q projection (32760x5120x5120): each GEMM and activation quantize timed on its own
+    on the configuration's seeded inputs, weights prequantized first. Quantizes cycle over enough
+    input and output copies that no buffer is reused within 768 MB of traffic."""
+    import numpy as np
+    import torch
+
+    import block_scaled_precision_nvfp4_amd as bsp
+    import workloads as W
+    dev = torch.device("cuda:0")
+    one = torch.ones(1, dtype=torch.float32, device=dev)
+    reps = max(6, steps)
+
+    def up(bits):
+        return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def qtime(x, gelu=False):
+        m, k = x.shape
+        per = 2 * m * k + m * k // 2
+        n = max(2, -(-(768 << 20) // per))
+        xs = [x] + [x.clone() for _ in range(n - 1)]
+        outs = [(torch.empty((m, k // 2), dtype=torch.uint8, device=dev),
+                 torch.empty(nvfp4_sf_shape(m, k), dtype=torch.uint8, device=dev)) for _ in range(n)]
+        fn = bsp.bsp_nvfp4_quantize_gelu if gelu else bsp.bsp_nvfp4_quantize
+        ms = _event_ms([lambda i=i: fn(xs[i], one, *outs[i]) for i in range(n)], max(reps, 2 * n))
+        gbs = (2 * m * k + m * k // 2 + nvfp4_sf_shape(m, k)[0] * k // 16) / ms / 1e6
+        return {"ms": round(ms, 4), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+
+    def gtime(px, sx, pw, sw, alpha, out):
+        m, n, k = px.shape[0], pw.shape[0], px.shape[1] * 2
+        ms = _event_ms([lambda: bsp.bsp_mm_fp4(px, sx, pw, sw, alpha, out=out)], reps)
+        tf = 2.0 * m * n * k / ms / 1e9
+        return {"ms": round(ms, 4), "TFLOPS": round(tf, 2), "frac_fp4_peak": round(tf / PEAK_FP4_TFLOPS, 4),
+                "frac_f16_mfma_peak": round(tf / PEAK_F16_TFLOPS, 4)}
+
+    res = {}
+    # Wan-1.3B attention projection
+    c2 = W.config(2)
+    x = up(W.generate(c2.tensor("X")))
+    pw, sw, g, _, _ = bsp.bsp_nvfp4_prequantize_weight(up(W.generate(c2.tensor("W"))))
+    res["wan1.3b_attn_quantize_x_32760x1536"] = qtime(x)
+    px, sx = bsp.bsp_nvfp4_quantize(x, one)
+    out = torch.empty((x.shape[0], pw.shape[0]), dtype=torch.bfloat16, device=dev)
+    res["wan1.3b_attn_mm_fp4_32760x1536x1536"] = gtime(px, sx, pw, sw, bsp.bsp_nvfp4_alpha(one, g), out)
+    # Wan-1.3B FFN
+    c3 = W.config(3)
+    x = up(W.generate(c3.tensor("X")))
+    pw1, sw1, g1, _, _ = bsp.bsp_nvfp4_prequantize_weight(up(W.generate(c3.tensor("W"))))
+    pw2, sw2, g2, _, _ = bsp.bsp_nvfp4_prequantize_weight(up(W.generate(c3.tensor("W2"))))
+    res["wan1.3b_ffn_quantize_x_32760x1536"] = qtime(x)
+    px, sx = bsp.bsp_nvfp4_quantize(x, one)
+    y = torch.empty((x.shape[0], pw1.shape[0]), dtype=torch.bfloat16, device=dev)
+    res["wan1.3b_ffn_mm_fp4_fc_in_32760x8960x1536"] = gtime(px, sx, pw1, sw1, bsp.bsp_nvfp4_alpha(one, g1), y)
+    res["wan1.3b_ffn_gelu_quantize_h_32760x8960"] = qtime(y, gelu=True)
+    ph, sh = bsp.bsp_nvfp4_quantize_gelu(y, one)
+    out = torch.empty((x.shape[0], pw2.shape[0]), dtype=torch.bfloat16, device=dev)
+    res["wan1.3b_ffn_mm_fp4_fc_out_32760x1536x8960"] = gtime(ph, sh, pw2, sw2, bsp.bsp_nvfp4_alpha(one, g2), out)
+    del y, ph, sh, out
+    # Wan-14B to_q
+    c4 = W.config(4)
+    x = up(W.generate(c4.tensor("X")))
+    pw, sw, g, _, _ = bsp.bsp_nvfp4_prequantize_weight(up(W.generate(c4.tensor("W3"))))
+    px, sx = bsp.bsp_nvfp4_quantize(x, one)
+    out = torch.empty((x.shape[0], pw.shape[0]), dtype=torch.bfloat16, device=dev)
+    res["wan14b_to_q_mm_fp4_32760x5120x5120"] = gtime(px, sx, pw, sw, bsp.bsp_nvfp4_alpha(one, g), out)
+    return res
+
+
+def measure_ceilings() -> dict:
+    """What this GPU sustains, measured with libbsp_probe: MFMA-only loops of each GEMM's matrix
+    instruction on operands like its own (4 waves per SIMD, no memory traffic), and nontemporal
+    streaming kernels over 2 GiB (read only, copy, and read:write 4:1 like the NVFP4 quantizers)."""
+    import ctypes
+
+    import torch
+    here = os.path.join(ROOT, "block_scaled_precision_nvfp4_amd", "libbsp_probe.so")
+    lib = ctypes.CDLL(here)
+    lib.bsp_probe_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.bsp_probe_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                     ctypes.c_int, ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    st = torch.cuda.current_stream(dev).cuda_stream
+    wgs = 1024
+    sink = torch.empty(wgs * 256, dtype=torch.float32, device=dev)
+    res = {}
+    for fmt, name, iters, flops in ((0, "mfma_f16_nvfp4_operands_TFLOPS", 20000, 32768.0),
+                                    (1, "mfma_fp8_scaled_TFLOPS", 10000, 131072.0),
+                                    (2, "mfma_fp4_scaled_TFLOPS", 20000, 131072.0)):
+        def run(fmt=fmt, iters=iters):
+            if lib.bsp_probe_mfma_loop(fmt, wgs, iters, ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(st)) != 0:
+                raise RuntimeError("bsp_probe_mfma_loop failed")
+        ms = _event_ms([run], 3)
+        res[name] = round(wgs * 4 * iters * 4 * flops / ms / 1e9, 1)
+    nb = 1 << 31
+    src = torch.ones(nb // 4, dtype=torch.int32, device=dev)
+    dst = torch.empty(nb // 4, dtype=torch.int32, device=dev)
+    for wd, name, nread, nwrite in ((0, "hbm_read_GBs", nb, 0), (1, "hbm_copy_GBs", nb // 2, nb // 2),
+                                   (4, "hbm_read4_write1_GBs", nb, nb // 4)):
+        def run(wd=wd, nread=nread):
+            if lib.bsp_probe_stream(wd, ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                                    nread // 16, 2048, ctypes.c_void_p(st)) != 0:
+                raise RuntimeError("bsp_probe_stream failed")
+        ms = _event_ms([run], 5)
+        res[name] = round((nread + nwrite) / ms / 1e6, 1)
+    del src, dst
+    res["note"] = ("MFMA-only loops: 1024 workgroups x 4 waves, four independent accumulator chains per "
+                   "wave; streams: 2 GiB read, nontemporal, 2048 workgroups")
+    return res
 
 
 def cpu_baseline(rows: int) -> dict:
@@ -440,21 +597,52 @@ def cpu_baseline(rows: int) -> dict:
     pw1, sw1 = N.quantize(w1, g1)
     pw2, sw2 = N.quantize(w2, g2)
     t_load = time.perf_counter() - t0
+    ops = {}
+    t_all = time.perf_counter()
     t0 = time.perf_counter()
     px, sx = N.quantize(xb, np.float32(1.0))
+    ops["quantize_x_s"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
     y = N.mm_fp4(px, sx, pw1, sw1, N.alpha(1.0, g1), rows, n1, k1)
+    ops["mm_fp4_fc_in_s"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
     yb = A.f64_to_bf16_bits(y)
     hb = A.gelu_tanh_bf16_bits(yb)
+    ops["bf16_round_and_gelu_s"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
     ph, sh = N.quantize(hb, np.float32(1.0))
+    ops["quantize_h_s"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
     _ = N.mm_fp4(ph, sh, pw2, sw2, N.alpha(1.0, g2), rows, n2, n1)
-    dt = time.perf_counter() - t0
+    ops["mm_fp4_fc_out_s"] = time.perf_counter() - t0
+    dt = time.perf_counter() - t_all
     flops = 2.0 * rows * n1 * k1 + 2.0 * rows * n2 * n1
+    qbytes_x = 2 * rows * k1 + rows * k1 // 2 + nvfp4_sf_shape(rows, k1)[0] * k1 // 16
+    qbytes_h = 2 * rows * n1 + rows * n1 // 2 + nvfp4_sf_shape(rows, n1)[0] * n1 // 16
+    rates = {"mm_fp4_fc_in_TFLOPS": 2.0 * rows * n1 * k1 / ops["mm_fp4_fc_in_s"] / 1e12,
+             "mm_fp4_fc_out_TFLOPS": 2.0 * rows * n2 * n1 / ops["mm_fp4_fc_out_s"] / 1e12,
+             "quantize_x_GBs": qbytes_x / ops["quantize_x_s"] / 1e9,
+             "quantize_h_GBs": qbytes_h / ops["quantize_h_s"] / 1e9}
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOPS", "cores": int(blas_threads),
             "kind": "oracle", "seconds": round(dt, 2), "weight_prequant_seconds": round(t_load, 2),
+            "per_op_seconds": {k: round(v, 3) for k, v in ops.items()},
+            "per_op_rates": {k: round(v, 6) for k, v in rates.items()},
+            "cpu_model": cpu_model, "blas_threads": int(blas_threads),
+            "quantize_threads": 1,
             "host_cpus": os.cpu_count(),
             "sample": f"first {rows} of 32760 tokens through the same NVFP4 FFN (quantize X, fc_in, "
                       f"GELU, quantize H, fc_out) with the numpy oracle (fp64 GEMM of dequantized "
-                      f"operands); weight prequantization excluded"}
+                      f"operands on the BLAS threads; the quantizes are single-threaded numpy); "
+                      f"weight prequantization excluded"}
 
 
 if __name__ == "__main__":

@@ -1,4 +1,5 @@
-"""Compile libbsp.so (the HIP kernels + C ABI) in-tree for gfx950 with hipcc.
+"""Compile libbsp.so (the HIP kernels + C ABI) and libbsp_probe.so (the benchmark's ceiling
+probes) in-tree for gfx950 with hipcc.
 
 Usage: python -m block_scaled_precision_nvfp4_amd._build  (or __graft_entry__.build()).
 Always recompiles; objects go to csrc/_build/, the library next to this file.
@@ -16,6 +17,9 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(CSRC, "_build")
 LIB = os.path.join(HERE, "libbsp.so")
 SOURCES = ["api.hip", "quantize.hip", "gemm_fp4.hip", "gemm_mx.hip"]
+# measurement probes (MFMA-only loops, streaming kernels): a separate library only the benchmark loads
+PROBE_SOURCES = ["probe.hip"]
+PROBE_LIB = os.path.join(HERE, "libbsp_probe.so")
 HEADERS = ["common.hpp", "gemm_common.hpp"]
 
 # IEEE fp32 everywhere: no contraction into FMA, correctly rounded division, no fast-math; packed
@@ -46,18 +50,24 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJ, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str, verbose: bool) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print("built", LIB, flush=True)
+        print("built", lib, flush=True)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(OBJ, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(5, len(srcs))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+    _link(objs[: len(SOURCES)], LIB, verbose)
+    _link(objs[len(SOURCES):], PROBE_LIB, verbose)
     return LIB
 
 

@@ -14,8 +14,8 @@ import workloads as W
 from oracle import mxfp4 as X4
 from oracle import mxfp8 as X
 from oracle import nvfp4 as N
-from tests.gpu_util import (assert_gemm_bf16, assert_gemm_f32, dev_bf16, dev_u8, host_u8, say,
-                            scalar)
+from tests.gpu_util import (REL_FRO_FP4_F32, assert_gemm_f32, check_gemm_outputs, dev_bf16, dev_u8,
+                            host_u8, say, scalar)
 
 pytestmark = pytest.mark.gpu
 
@@ -58,20 +58,20 @@ def test_gemm_sweep(m, n, k):
         pb, sb = _nvfp4_operand(rng, n, kk)
         ref = N.mm_fp4(pa, sa, pb, sb, np.float32(0.75), m, n, kk)
         args = (dev_u8(pa), dev_u8(sa), dev_u8(pb), dev_u8(sb), scalar(0.75))
-        assert_gemm_f32(bsp.bsp_mm_fp4(*args, out_dtype=torch.float32).cpu().numpy().astype(np.float64),
-                        ref, f"mm_fp4 {m}x{n}x{kk}")
-        assert_gemm_bf16(bsp.bsp_mm_fp4(*args).float().cpu().numpy().astype(np.float64), ref,
-                         f"mm_fp4 bf16 {m}x{n}x{kk}")
+        check_gemm_outputs(bsp.bsp_mm_fp4(*args), bsp.bsp_mm_fp4(*args, out_dtype=torch.float32), ref,
+                           f"mm_fp4 {m}x{n}x{kk}", f32_tol=REL_FRO_FP4_F32)
     qa, s8a = _mx8_operand(rng, m, k)
     qb, s8b = _mx8_operand(rng, n, k)
     ref = X.mm_mxfp8(qa, s8a, qb, s8b, m, n, k)
-    c = bsp.bsp_mm_mxfp8(dev_u8(qa), dev_u8(s8a), dev_u8(qb), dev_u8(s8b))
-    assert_gemm_bf16(c.float().cpu().numpy().astype(np.float64), ref, f"mm_mxfp8 {m}x{n}x{k}")
+    a8 = (dev_u8(qa), dev_u8(s8a), dev_u8(qb), dev_u8(s8b))
+    check_gemm_outputs(bsp.bsp_mm_mxfp8(*a8), bsp.bsp_mm_mxfp8(*a8, out_dtype=torch.float32), ref,
+                       f"mm_mxfp8 {m}x{n}x{k}")
     pa, sa = _mxfp4_operand(rng, m, k)
     pb, sb = _mxfp4_operand(rng, n, k)
     ref = X4.mm_mxfp4(pa, sa, pb, sb, np.float32(1.0), m, n, k)
-    c = bsp.bsp_mm_mxfp4(dev_u8(pa), dev_u8(sa), dev_u8(pb), dev_u8(sb), None)
-    assert_gemm_bf16(c.float().cpu().numpy().astype(np.float64), ref, f"mm_mxfp4 {m}x{n}x{k}")
+    a4 = (dev_u8(pa), dev_u8(sa), dev_u8(pb), dev_u8(sb), None)
+    check_gemm_outputs(bsp.bsp_mm_mxfp4(*a4), bsp.bsp_mm_mxfp4(*a4, out_dtype=torch.float32), ref,
+                       f"mm_mxfp4 {m}x{n}x{k}")
 
 
 @pytest.mark.parametrize("m,k,pad", QUANT_CASES)
@@ -118,8 +118,9 @@ def test_gemm_variant_sweep(m, n, k):
     xg = (10.0 ** rng.uniform(-2, 3, size=m)).astype(np.float32)
     wg = np.float32(321.5)
     ref = N.mm_fp4_rowscale(pa, sa, pb, sb, xg, wg, m, n, k)
-    c = bsp.bsp_mm_fp4_per_token(*args, torch.from_numpy(xg).cuda(), scalar(wg))
-    assert_gemm_bf16(c.float().cpu().numpy().astype(np.float64), ref, f"per-token {m}x{n}x{k}")
+    pt = (*args, torch.from_numpy(xg).cuda(), scalar(wg))
+    check_gemm_outputs(bsp.bsp_mm_fp4_per_token(*pt), bsp.bsp_mm_fp4_per_token(*pt, out_dtype=torch.float32),
+                       ref, f"per-token {m}x{n}x{k}", f32_tol=REL_FRO_FP4_F32)
     sa8 = N.swizzle_8x4(N.unswizzle_128x4(sa, *N.sf_padded_shape(m, k))[:N.sf_padded_shape_8x4(m, k)[0]])
     ref = N.mm_fp4(pa, sa8, pb, sb, np.float32(0.5), m, n, k, a_layout="8x4")
     c = bsp.bsp_mm_fp4_8x4(dev_u8(pa), dev_u8(sa8), dev_u8(pb), dev_u8(sb), scalar(0.5), out_dtype=torch.float32)
@@ -130,8 +131,9 @@ def test_gemm_variant_sweep(m, n, k):
     bbits = W.f32_to_bf16_bits(rng.normal(0.0, float(np.std(ref)) + 1e-30, size=n).astype(np.float32))
     bias = dev_bf16(bbits)
     c0 = bsp.bsp_mm_fp4(*args, scalar(0.5))
-    assert_gemm_bf16(c0.float().cpu().numpy().astype(np.float64), N.mm_fp4(pa, sa, pb, sb, np.float32(0.5), m, n, k),
-                     f"mm_fp4 {m}x{n}x{k}")
+    check_gemm_outputs(c0, bsp.bsp_mm_fp4(*args, scalar(0.5), out_dtype=torch.float32),
+                       N.mm_fp4(pa, sa, pb, sb, np.float32(0.5), m, n, k), f"mm_fp4 {m}x{n}x{k}",
+                       f32_tol=REL_FRO_FP4_F32)
     c = bsp.bsp_mm_fp4_bias(*args, scalar(0.5), bias)
     assert torch.equal(c.view(torch.int16), (c0.float() + bias.float()).bfloat16().view(torch.int16))
     qa, s8a = _mx8_operand(rng, m, k)
@@ -144,12 +146,12 @@ def test_gemm_variant_sweep(m, n, k):
     assert np.array_equal(cb32.cpu().numpy(), (c32.cpu().numpy() + bf).astype(np.float32))
     c = bsp.bsp_mm_mxfp8_bias(*a8, torch.from_numpy(bf).cuda())
     assert torch.equal(c, cb32.bfloat16())
-    assert_gemm_bf16(c.float().cpu().numpy().astype(np.float64), L.gemm_plus_bias(ref, bf), f"mxfp8 bias {m}x{n}x{k}")
+    check_gemm_outputs(c, cb32, L.gemm_plus_bias(ref, bf), f"mxfp8 bias {m}x{n}x{k}")
     pa4, sa4 = _mxfp4_operand(rng, m, k)
     pb4, sb4 = _mxfp4_operand(rng, n, k)
     a4 = (dev_u8(pa4), dev_u8(sa4), dev_u8(pb4), dev_u8(sb4))
     c0 = bsp.bsp_mm_mxfp4(*a4, scalar(0.25))
-    assert_gemm_bf16(c0.float().cpu().numpy().astype(np.float64),
-                     X4.mm_mxfp4(pa4, sa4, pb4, sb4, np.float32(0.25), m, n, k), f"mm_mxfp4 {m}x{n}x{k}")
+    check_gemm_outputs(c0, bsp.bsp_mm_mxfp4(*a4, scalar(0.25), out_dtype=torch.float32),
+                       X4.mm_mxfp4(pa4, sa4, pb4, sb4, np.float32(0.25), m, n, k), f"mm_mxfp4 {m}x{n}x{k}")
     c = bsp.bsp_mm_mxfp4_bias(*a4, bias, scalar(0.25))
     assert torch.equal(c.view(torch.int16), (c0.float() + bias.float()).bfloat16().view(torch.int16))
