@@ -446,11 +446,13 @@ static void launch_mm_fp4_t(const uint8_t* a, const uint8_t* sa, const uint8_t* 
 
 using namespace bsp;
 
-// bias_align: 0 for the entry points without a bias, else the bias element size (its alignment)
+// bias_align: 0 for the entry points without a bias, else the bias element size (its alignment);
+// a_sf_align: 16 for 128x4 activation scales (16-byte loads), 4 for layout_8x4 (dword loads)
 static int mm_fp4_checks(const char* fn, const uint8_t* a_packed, const uint8_t* a_sf,
                          const uint8_t* b_packed, const uint8_t* b_sf, const float* alpha_dev,
                          int64_t M, int64_t N, int64_t K, void* out, int64_t ldc, int out_dtype,
-                         const void* bias = nullptr, unsigned bias_align = 0) {
+                         const void* bias = nullptr, unsigned bias_align = 0,
+                         unsigned a_sf_align = 16) {
   BSP_REQUIRE(M >= 0 && N >= 0 && K > 0, BSP_EINVAL, "%s: bad size M=%lld N=%lld K=%lld", fn,
               (long long)M, (long long)N, (long long)K);
   BSP_REQUIRE(out_dtype == BSP_OUT_BF16 || out_dtype == BSP_OUT_F32, BSP_EDTYPE,
@@ -463,8 +465,10 @@ static int mm_fp4_checks(const char* fn, const uint8_t* a_packed, const uint8_t*
   if (M == 0 || N == 0) return 1;
   BSP_REQUIRE(a_packed && a_sf && b_packed && b_sf && alpha_dev && out, BSP_EINVAL, "%s: null pointer", fn);
   BSP_REQUIRE(((reinterpret_cast<uintptr_t>(a_packed) | reinterpret_cast<uintptr_t>(b_packed) |
-                reinterpret_cast<uintptr_t>(a_sf) | reinterpret_cast<uintptr_t>(b_sf)) & 15u) == 0,
-              BSP_EINVAL, "%s: operand and scale buffers must be 16-byte aligned", fn);
+                reinterpret_cast<uintptr_t>(b_sf)) & 15u) == 0 &&
+                  (reinterpret_cast<uintptr_t>(a_sf) & (a_sf_align - 1)) == 0,
+              BSP_EINVAL, "%s: operands and weight scales must be 16-byte, activation scales %u-byte aligned",
+              fn, a_sf_align);
   BSP_REQUIRE(ceil_div(M, 256) * ceil_div(N, 256) < (1ll << 31), BSP_ESHAPE, "%s: too many tiles", fn);
   BSP_REQUIRE(bias_align == 0 || (bias && (reinterpret_cast<uintptr_t>(bias) & (bias_align - 1)) == 0),
               BSP_EINVAL, "%s: bias must be a non-null device pointer aligned to its element size", fn);
@@ -521,9 +525,8 @@ extern "C" int bsp_mm_fp4_8x4(const uint8_t* a_packed, const uint8_t* a_sf, cons
                               const uint8_t* b_sf, const float* alpha_dev, int64_t M, int64_t N,
                               int64_t K, void* out, int64_t ldc, int out_dtype, void* stream) {
   int e = mm_fp4_checks("bsp_mm_fp4_8x4", a_packed, a_sf, b_packed, b_sf, alpha_dev, M, N, K, out, ldc,
-                        out_dtype);
+                        out_dtype, nullptr, 0, 4);
   if (e) return e > 0 ? BSP_OK : e;
-  BSP_REQUIRE((reinterpret_cast<uintptr_t>(a_sf) & 3u) == 0, BSP_EINVAL, "bsp_mm_fp4_8x4: a_sf alignment");
   launch_mm_fp4_t<false, true>(a_packed, a_sf, b_packed, b_sf, alpha_dev, nullptr, M, N, K, out, ldc,
                                out_dtype, (hipStream_t)stream);
   return check_launch("bsp_mm_fp4_8x4");

@@ -834,8 +834,10 @@ static int nvfp4_quantize_entry(const char* fn, const void* x, int64_t M, int64_
   BSP_REQUIRE(M <= 1 || ld >= K, BSP_ESHAPE, "%s: ld (%lld) < K (%lld)", fn, (long long)ld, (long long)K);
   if (M == 0) return BSP_OK;
   BSP_REQUIRE(x && gsf && packed && sf, BSP_EINVAL, "%s: null pointer", fn);
-  BSP_REQUIRE((reinterpret_cast<uintptr_t>(packed) & 3u) == 0 && (reinterpret_cast<uintptr_t>(sf) & 15u) == 0,
-              BSP_EINVAL, "%s: packed must be 4-byte and sf 16-byte aligned", fn);
+  // 128x4 scales leave as 16-byte stores, 8x4 scales as dword stores
+  const uintptr_t sf_mask = layout8 ? 3u : 15u;
+  BSP_REQUIRE((reinterpret_cast<uintptr_t>(packed) & 3u) == 0 && (reinterpret_cast<uintptr_t>(sf) & sf_mask) == 0,
+              BSP_EINVAL, "%s: packed must be 4-byte and sf %d-byte aligned", fn, layout8 ? 4 : 16);
   BSP_REQUIRE(ceil_div(M, 128) < 65536, BSP_ESHAPE, "%s: M too large", fn);
   if (int e = check_device()) return e;
   return launch_nvfp4_quantize(x, M, K, ld, gsf, packed, sf, (hipStream_t)stream, gelu, layout8);

@@ -59,7 +59,11 @@ int bsp_nvfp4_sf_bytes(int64_t rows, int64_t K, int64_t* bytes);
 int bsp_nvfp4_global_sf(const void* w_bf16, int64_t rows, int64_t K, int64_t ld,
                         float* gsf_dev, float* inv_gsf_dev, float* amax_dev, void* stream);
 
-/* NVFP4 quantize. [FV-NV] _nvfp4_quantize / module docstring: e2m1 values, one e4m3 scale
+/* Every quantizer below encodes nan_to_num of its input: a NaN as +0, +-inf as +-largest finite
+ * bf16 (the substitution [FV-QAT], [FV-NV] and [SGL] apply before a weight's amax), so scales and
+ * elements always come from finite values.
+ *
+ * NVFP4 quantize. [FV-NV] _nvfp4_quantize / module docstring: e2m1 values, one e4m3 scale
  * per 16 consecutive K elements under the fp32 global scale *gsf_dev, scales in layout_128x4.
  * Per block: a = max|x|; s = fl32(g*fl32(a*fl32(1/6))); S = e4m3(s) (nearest-even, saturate 448);
  * r = S==0 ? 0 : fl32(g/S); q = e2m1(fl32(x*r)) (nearest-even, saturate 6, sign kept).
@@ -68,6 +72,8 @@ int bsp_nvfp4_global_sf(const void* w_bf16, int64_t rows, int64_t K, int64_t ld,
  * sf: device uint8, bsp_nvfp4_sf_bytes(M, K) bytes, 128x4 layout: byte (r, c) at
  *     ((r/128)*(Kp/4) + c/4)*512 + (r%32)*16 + ((r/32)%4)*4 + c%4 with Kp = ceil(K/64)*4;
  *     rows M..Mp-1 and columns K/16..Kp-1 are written as 0x00 (zero padding, no copy of x).
+ * Alignment: packed 4-byte, sf 16-byte (else BSP_EINVAL); x any (16-byte aligned rows with
+ * ld % 8 == 0 take 16-byte loads). K % 16 != 0 or ld < K: BSP_ESHAPE. NULL pointers: BSP_EINVAL.
  * M == 0 is a no-op returning BSP_OK. */
 int bsp_nvfp4_quantize(const void* x_bf16, int64_t M, int64_t K, int64_t ld, const float* gsf_dev,
                        uint8_t* packed, uint8_t* sf, void* stream);
@@ -75,13 +81,16 @@ int bsp_nvfp4_quantize(const void* x_bf16, int64_t M, int64_t K, int64_t ld, con
 /* Load-time weight prequantization: the global scale, then the NVFP4 quantize, of W [N, K]
  * ([FV-QAT] convert_model_to_fp4, [FV-NV] convert_model_to_nvfp4). Outputs as for the two calls above (gsf_dev, inv_gsf_dev and
  * amax_dev are all required device fp32 slots; the quantize step reads *gsf_dev on the device, so
- * nothing is synchronised). The caller may free W once the stream has passed this call. */
+ * nothing is synchronised). packed 4-byte and sf 16-byte aligned (else BSP_EINVAL). The caller may
+ * free W once the stream has passed this call. */
 int bsp_nvfp4_prequantize_weight(const void* w_bf16, int64_t N, int64_t K, int64_t ld,
                                  uint8_t* packed, uint8_t* sf, float* gsf_dev, float* inv_gsf_dev,
                                  float* amax_dev, void* stream);
 
-/* alpha = fl32(1 / fl32(x_gsf * w_gsf)) on the device ([FV-QAT] NVFP4QATQuantizeMethod.apply;
- * with the static x_gsf = 1.0 this equals [FV-NV]'s stored 1/w_gsf). */
+/* alpha = fl32(1 / fl32(x_gsf * w_gsf)) on the device ([FV-QAT] NVFP4QATQuantizeMethod.apply's
+ * order; [FV-NV] NVFP4QuantizeMethod.apply divides its stored fl32(1/w_gsf) by x_gsf instead, which
+ * is the same bits when x_gsf = 1.0, the static activation scale, and may differ by one ulp
+ * otherwise). NULL pointers: BSP_EINVAL. */
 int bsp_nvfp4_alpha(const float* x_gsf_dev, const float* w_gsf_dev, float* alpha_dev, void* stream);
 
 /* mm_fp4: C[m, n] = alpha * sum_k e2m1(A[m,k])*e4m3(SA[m,k/16]) * e2m1(B[n,k])*e4m3(SB[n,k/16]),
@@ -91,7 +100,9 @@ int bsp_nvfp4_alpha(const float* x_gsf_dev, const float* w_gsf_dev, float* alpha
  * a_packed: device uint8 [M, K/2]; a_sf: 128x4 scales for M rows (bsp_nvfp4_sf_bytes(M, K));
  * b_packed: device uint8 [N, K/2]; b_sf: 128x4 scales for N rows; out: device [M, N] with row
  * stride ldc elements (bf16 or fp32 per out_dtype). Requires K % 64 == 0 and K <= 2^24 (else
- * BSP_ESHAPE); M, N arbitrary >= 0. */
+ * BSP_ESHAPE); M, N arbitrary >= 0. a_packed, a_sf, b_packed and b_sf 16-byte aligned, no NULL
+ * pointer (else BSP_EINVAL); out_dtype other than BSP_OUT_BF16 / BSP_OUT_F32: BSP_EDTYPE. Every
+ * finite alpha is applied exactly as fl32(alpha * sum) up to the fp32 accumulation. */
 int bsp_mm_fp4(const uint8_t* a_packed, const uint8_t* a_sf, const uint8_t* b_packed,
                const uint8_t* b_sf, const float* alpha_dev, int64_t M, int64_t N, int64_t K,
                void* out, int64_t ldc, int out_dtype, void* stream);
@@ -102,7 +113,8 @@ int bsp_mm_fp4(const uint8_t* a_packed, const uint8_t* a_sf, const uint8_t* b_pa
  * x: device bf16 [M, K], row stride ld, K % 32 == 0. q: device uint8 [M, K] row-major.
  * sf: device uint8 [M, K/32] row-major (the per-row (rows, ceil(K/32)) uint8 scale shape of
  * [VLO] NPUMxfp8LinearMethod.create_weights). Also used once at load for weights ([VLO]
- * NPUMxfp8OnlineLinearMethod.process_weights_after_loading). */
+ * NPUMxfp8OnlineLinearMethod.process_weights_after_loading). q 8-byte aligned (else BSP_EINVAL);
+ * K % 32 != 0 or ld < K: BSP_ESHAPE. */
 int bsp_mxfp8_quantize(const void* x_bf16, int64_t M, int64_t K, int64_t ld, uint8_t* q,
                        uint8_t* sf, void* stream);
 
@@ -126,13 +138,15 @@ int bsp_mm_mxfp8(const uint8_t* a, const uint8_t* a_sf, const uint8_t* b, const 
 int bsp_mxfp4_sf_bytes(int64_t rows, int64_t K, int64_t* bytes);
 
 /* x: device bf16 [M, K] (row stride ld), K % 32 == 0 -> packed uint8 [M, K/2] (even k in the low
- * nibble), sf (bsp_mxfp4_sf_bytes(M, K) bytes). M == 0 is a no-op. */
+ * nibble), sf (bsp_mxfp4_sf_bytes(M, K) bytes). packed 4-byte and sf 16-byte aligned (else
+ * BSP_EINVAL). M == 0 is a no-op. */
 int bsp_mxfp4_quantize(const void* x_bf16, int64_t M, int64_t K, int64_t ld, uint8_t* packed,
                        uint8_t* sf, void* stream);
 
 /* C[m, n] = alpha * sum_k e2m1(A)*2^(SA-127) * e2m1(B)*2^(SB-127), fp32 accumulation on gfx950's
  * block-scaled FP4 MFMA; alpha_dev may be NULL (alpha = 1). a: [M, K/2], b: [N, K/2] (K-major
- * weight), scales as above, out [M, N] row stride ldc (bf16 or fp32). Requires K % 128 == 0. */
+ * weight), scales as above, out [M, N] row stride ldc (bf16 or fp32). Requires K % 128 == 0
+ * (else BSP_ESHAPE); operands and scales 16-byte aligned (else BSP_EINVAL). */
 int bsp_mm_mxfp4(const uint8_t* a_packed, const uint8_t* a_sf, const uint8_t* b_packed,
                  const uint8_t* b_sf, const float* alpha_dev, int64_t M, int64_t N, int64_t K,
                  void* out, int64_t ldc, int out_dtype, void* stream);
@@ -155,12 +169,14 @@ int bsp_nvfp4_sf_bytes_8x4(int64_t rows, int64_t K, int64_t* bytes);
  * row tile is 8 (rows padded to a multiple of 8 instead of 128). Layout: 32-byte tiles of 8 rows x
  * 4 scale columns ordered row-tile-major, byte (r, c) at ((r/8)*(Kp/4) + c/4)*32 + (r%8)*4 + c%4
  * (Kp = ceil(K/64)*4); padded rows M..ceil(M/8)*8-1 and columns K/16..Kp-1 are 0x00.
- * sf: bsp_nvfp4_sf_bytes_8x4(M, K) bytes, 4-byte aligned. Everything else as bsp_nvfp4_quantize. */
+ * sf: bsp_nvfp4_sf_bytes_8x4(M, K) bytes, 4-byte aligned (else BSP_EINVAL). Everything else as
+ * bsp_nvfp4_quantize. */
 int bsp_nvfp4_quantize_8x4(const void* x_bf16, int64_t M, int64_t K, int64_t ld, const float* gsf_dev,
                            uint8_t* packed, uint8_t* sf, void* stream);
 
 /* bsp_mm_fp4 with the activation (A) scales in layout_8x4 (as written by bsp_nvfp4_quantize_8x4)
- * and the weight (B) scales in 128x4. [FV-NV] _mm_fp4: use_8x4_sf_layout. */
+ * and the weight (B) scales in 128x4. [FV-NV] _mm_fp4: use_8x4_sf_layout. a_sf 4-byte aligned;
+ * the other buffers as bsp_mm_fp4 (else BSP_EINVAL). */
 int bsp_mm_fp4_8x4(const uint8_t* a_packed, const uint8_t* a_sf, const uint8_t* b_packed,
                    const uint8_t* b_sf, const float* alpha_dev, int64_t M, int64_t N, int64_t K,
                    void* out, int64_t ldc, int out_dtype, void* stream);
@@ -178,7 +194,8 @@ int bsp_nvfp4_global_sf_4over6(const void* w_bf16, int64_t rows, int64_t K, int6
  * its own fp32 scale at run time. Row m: amax_m = max|x[m, :]|, gsf_rows[m] = fl32(2688/amax_m)
  * (1.0 for an all-zero row: the tensor rule of bsp_nvfp4_global_sf applied to the row), and the row
  * is quantized exactly as bsp_nvfp4_quantize would with gsf = gsf_rows[m]. Outputs as
- * bsp_nvfp4_quantize plus gsf_rows: device fp32 [M] (written). Inputs must be finite. Rows of up to
+ * bsp_nvfp4_quantize plus gsf_rows: device fp32 [M] (written); packed 4-byte and sf 16-byte aligned
+ * (else BSP_EINVAL). A row's amax is taken after nan_to_num, like the tensor amax. Rows of up to
  * 64*8*32 elements (padded to 64) are read once; longer rows are read twice. */
 int bsp_nvfp4_quantize_per_token(const void* x_bf16, int64_t M, int64_t K, int64_t ld,
                                  uint8_t* packed, uint8_t* sf, float* gsf_rows_dev, void* stream);
@@ -214,8 +231,10 @@ int bsp_nvfp4_quantize_gelu(const void* y_bf16, int64_t M, int64_t K, int64_t ld
  * those of the NVFP4 quantize of bsp_rmsnorm_bf16's output. Packed, sf and gsf as in
  * bsp_nvfp4_quantize (padded rows' scales 0x00).
  * x: device bf16 [M, K], row stride ld; weight_bf16: NULL or device bf16 [K]; eps: positive and
- * finite (else BSP_EINVAL); K % 16 == 0 (else BSP_ESHAPE); M == 0 returns BSP_OK. Inputs must be
- * finite. Rows of up to 64*8*32 elements (padded to 64) are read from HBM once, longer rows twice. */
+ * finite (else BSP_EINVAL); K % 16 == 0 (else BSP_ESHAPE); M == 0 returns BSP_OK; packed 4-byte
+ * and sf 16-byte aligned (else BSP_EINVAL). A non-finite value in a row of x makes r_m 0 or NaN,
+ * so that row's y is zero or NaN, which the quantize encodes as zero codes. Rows of up to 64*8*32
+ * elements (padded to 64) are read from HBM once, longer rows twice. */
 int bsp_rmsnorm_bf16(const void* x_bf16, int64_t M, int64_t K, int64_t ld, const void* weight_bf16,
                      float eps, void* out_bf16, int64_t ldo, void* stream);
 int bsp_nvfp4_quantize_rmsnorm(const void* x_bf16, int64_t M, int64_t K, int64_t ld,

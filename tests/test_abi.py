@@ -214,3 +214,41 @@ def test_size_limits_rejected_on_the_host():
     assert _st("bsp_mxfp8_quantize", P, 65535 * 64 + 1, 32, 32, P, P, None)[0] == -2
     st, msg = _st("bsp_mm_fp4", P, P, P, P, P, 4, 4, (1 << 24) + 64, P, 4, 0, None)
     assert st == -2 and "at most" in msg
+
+
+def test_probe_library_exports_its_header():
+    """libbsp_probe.so (the benchmark's ceiling probes) exports what include/bsp_probe.h declares."""
+    hdr = open(os.path.join(ROOT, "include", "bsp_probe.h")).read()
+    names = sorted(set(re.findall(r"^\s*int\s+(bsp_probe_\w+)\s*\(", hdr, re.M)))
+    assert names == ["bsp_probe_mfma_loop", "bsp_probe_stream"], names
+    lib = ctypes.CDLL(os.path.join(ROOT, "block_scaled_precision_nvfp4_amd", "libbsp_probe.so"))
+    for n in names:
+        assert hasattr(lib, n), n
+    # argument checks return -1 before anything touches a GPU
+    lib.bsp_probe_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.bsp_probe_mfma_loop(3, 1, 1, P, None) == -1
+    assert lib.bsp_probe_mfma_loop(0, 0, 1, P, None) == -1
+    lib.bsp_probe_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                     ctypes.c_int, ctypes.c_void_p]
+    assert lib.bsp_probe_stream(2, P, P, 1, 1, None) == -1
+    assert lib.bsp_probe_stream(0, ctypes.c_void_p(8), P, 1, 1, None) == -1
+
+
+def test_alignment_rules_match_the_header():
+    """layout_8x4 scale buffers need 4-byte alignment (dword stores and loads), 128x4 ones 16-byte:
+    a 4-byte aligned 8x4 buffer passes validation (the call then fails only for want of a gfx950
+    device here), a 2-byte aligned one is rejected; the same 4-byte address is rejected for 128x4."""
+    a4 = ctypes.c_void_p(0x1004)
+    a2 = ctypes.c_void_p(0x1002)
+    st, msg = _st("bsp_nvfp4_quantize_8x4", P, 8, 64, 64, P, P, a4, None)
+    assert st != -1, msg
+    st, msg = _st("bsp_nvfp4_quantize_8x4", P, 8, 64, 64, P, P, a2, None)
+    assert st == -1 and "4-byte aligned" in msg
+    st, msg = _st("bsp_nvfp4_quantize", P, 8, 64, 64, P, P, a4, None)
+    assert st == -1 and "16-byte aligned" in msg
+    st, msg = _st("bsp_mm_fp4_8x4", P, a4, P, P, P, 8, 8, 128, P, 8, 0, None)
+    assert st != -1, msg
+    st, msg = _st("bsp_mm_fp4", P, a4, P, P, P, 8, 8, 128, P, 8, 0, None)
+    assert st == -1 and "16-byte" in msg
+    st, msg = _st("bsp_mxfp8_quantize", P, 4, 64, 64, a4, P, None)
+    assert st == -1 and "8-byte" in msg
