@@ -192,17 +192,28 @@ __device__ __forceinline__ uint32_t bf16x2_nan_to_num(uint32_t w) {
   return bf16_nan_to_num(w & 0xFFFFu) | (bf16_nan_to_num(w >> 16) << 16);
 }
 
-// The largest magnitude of the 8 bf16 values in v as an fp32 (exact), after replacing v by its
-// nan_to_num when one of the values is not finite (rare: one compare on the common path).
-__device__ __forceinline__ float finite_absmax8(uint4& v) {
-  uint32_t mb = mag_bits8(v);
-  if (mb >= 0x7F80u) {
-    v = make_uint4(bf16x2_nan_to_num(v.x), bf16x2_nan_to_num(v.y), bf16x2_nan_to_num(v.z),
-                   bf16x2_nan_to_num(v.w));
-    mb = mag_bits8(v);
-  }
-  return __uint_as_float(mb << 16);
+__device__ __forceinline__ uint4 nan_to_num8(const uint4& v) {
+  return make_uint4(bf16x2_nan_to_num(v.x), bf16x2_nan_to_num(v.y), bf16x2_nan_to_num(v.z),
+                    bf16x2_nan_to_num(v.w));
 }
+
+// Replaces N segments of 8 bf16 values by their nan_to_num when any of them holds an infinity or a
+// NaN: one running integer max over all segments and one branch, rarely taken, so that the loads
+// before and the encoding after stay branch-free (the encoder takes each segment's magnitude bits
+// again, which costs a few integer instructions and no registers held across the loop).
+template <int N>
+__device__ __forceinline__ void nan_to_num_segments(uint4 (&v)[N]) {
+  uint32_t mx = 0;
+#pragma unroll
+  for (int i = 0; i < N; ++i) mx = max(mx, mag_bits8(v[i]));
+  if (mx >= 0x7F80u) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = nan_to_num8(v[i]);
+  }
+}
+
+// The fp32 value (exact) of magnitude bits from mag_bits8
+__device__ __forceinline__ float mag_value(uint32_t mb) { return __uint_as_float(mb << 16); }
 
 // gelu of the two bf16 values in w (bits 0-15 and 16-31) from the table; sets bits of miss when
 // either lies outside it (its result is then meaningless)
@@ -226,8 +237,11 @@ __device__ __forceinline__ uint4 gelu8_bf16_arith(const uint4& v) {
 
 // gelu (bf16 in, bf16 out) of NSEG segments of 8 values: all by table first, then one branch,
 // rarely taken, that recomputes the segments holding a value outside the table. Keeping the
-// common path free of branches lets the LDS latencies of all segments overlap.
-template <int NSEG>
+// common path free of branches lets the LDS latencies of all segments overlap. FINITE: the
+// recomputed segments also get nan_to_num (for an encoder's input: the table holds only finite
+// values, and gelu of a finite bf16 is finite, so only inputs outside the table can give an
+// infinity or a NaN).
+template <int NSEG, bool FINITE = false>
 __device__ __forceinline__ void gelu_segments_tab(const uint4 (&in)[NSEG], uint4 (&out)[NSEG],
                                                   const uint16_t* tab) {
   uint32_t missbits = 0;
@@ -243,7 +257,8 @@ __device__ __forceinline__ void gelu_segments_tab(const uint4 (&in)[NSEG], uint4
   if (missbits) {
 #pragma unroll
     for (int i = 0; i < NSEG; ++i)
-      if ((missbits >> i) & 1u) out[i] = gelu8_bf16_arith(in[i]);
+      if ((missbits >> i) & 1u)
+        out[i] = FINITE ? nan_to_num8(gelu8_bf16_arith(in[i])) : gelu8_bf16_arith(in[i]);
   }
 }
 
@@ -254,12 +269,6 @@ __device__ __forceinline__ void unpack8(const uint4& v, float (&f)[8]) {
   f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
 }
 
-__device__ __forceinline__ float absmax8(const float (&f)[8]) {
-  float a = fmaxf(__builtin_fabsf(f[0]), __builtin_fabsf(f[1]));
-#pragma unroll
-  for (int i = 2; i < 8; ++i) a = fmaxf(a, __builtin_fabsf(f[i]));
-  return a;
-}
 
 
 }  // namespace bsp

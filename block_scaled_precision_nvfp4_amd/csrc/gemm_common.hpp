@@ -245,12 +245,12 @@ __device__ __forceinline__ void gelu_nvfp4_half(const uint8_t* lds, int half, in
     const u32x4 v = *reinterpret_cast<const u32x4*>(lds + (it * 4 + (lane >> 4)) * kEpiRowBytes + c16 * 16);
     seg[it] = make_uint4(v.x, v.y, v.z, v.w);
   }
-  gelu_segments_tab(seg, gv, gtab);
+  gelu_segments_tab<16, true>(seg, gv, gtab);
 #pragma unroll
   for (int it = 0; it < 16; ++it) {
     const int rr = half * 64 + it * 4 + (lane >> 4);  // row inside the wave's 128 rows
     const int64_t gm = m0w + rr;
-    const float a = pair_max(finite_absmax8(gv[it]));
+    const float a = pair_max(mag_value(mag_bits8(gv[it])));
     float f[8];
     unpack8(gv[it], f);
     const uint32_t S = (ROWS_IN || gm < M) ? e4m3_encode_pos(g * (a * kSixth)) : 0u;

@@ -183,6 +183,7 @@ __global__ __launch_bounds__(256) void nvfp4_quantize_kernel(const uint16_t* __r
   }
   if (GELU) gelu_table_fill(gtab, t, 256);   // while the loads are in flight
   __syncthreads();  // rtab, gtab
+  if (!GELU) nan_to_num_segments(v);   // the GELU path substitutes in its table-miss branch
 
   const int64_t half_k = K / 2;
   uint8_t* pp = packed + (row0 + rsub) * half_k + kk / 2;
@@ -190,8 +191,8 @@ __global__ __launch_bounds__(256) void nvfp4_quantize_kernel(const uint16_t* __r
 #pragma unroll
   for (int s = 0; s < 16; ++s) {
     uint4 xv[1] = {v[s]};
-    if (GELU) gelu_segments_tab<1>({v[s]}, xv, gtab);  // gelu(0) = 0 keeps the padding zero
-    const float a = pair_max(finite_absmax8(xv[0]));
+    if (GELU) gelu_segments_tab<1, true>({v[s]}, xv, gtab);  // gelu(0) = 0 keeps the padding zero
+    const float a = pair_max(mag_value(mag_bits8(xv[0])));
     float f[8];
     unpack8(xv[0], f);
     const float sc = g * (a * kSixth);
@@ -272,17 +273,35 @@ __global__ __launch_bounds__(256) void nvfp4_quantize_token_kernel(
   const uint16_t* xr = x + (live ? row : 0) * ld;
 
   uint4 v[C];
-  float amax = 0.0f;
+  uint32_t mrow = 0;   // the row's largest magnitude, as bf16 bits (mag_bits8)
   for (int sg = 0; sg < nseg; ++sg) {
 #pragma unroll
     for (int j = 0; j < C; ++j) {
       const int64_t e = sg * seg_elems + (int64_t)(j * 64 + lane) * 8;
       v[j] = (live && e < K) ? load8<VEC>(xr + e) : make_uint4(0u, 0u, 0u, 0u);
-      amax = fmaxf(amax, finite_absmax8(v[j]));
+      mrow = max(mrow, mag_bits8(v[j]));
     }
   }
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  for (int off = 32; off > 0; off >>= 1) mrow = max(mrow, (uint32_t)__shfl_xor((int)mrow, off));
+  // a row holding an inf or a NaN (wave-uniform, rare): its amax after nan_to_num, with the
+  // registers of a one-segment row replaced in place
+  const bool nonfinite = mrow >= 0x7F80u;
+  if (nonfinite) {
+    mrow = 0;
+    for (int sg = 0; sg < nseg; ++sg) {
+#pragma unroll
+      for (int j = 0; j < C; ++j) {
+        const int64_t e = sg * seg_elems + (int64_t)(j * 64 + lane) * 8;
+        if (nseg > 1) v[j] = (live && e < K) ? load8<VEC>(xr + e) : make_uint4(0u, 0u, 0u, 0u);
+        v[j] = nan_to_num8(v[j]);
+        mrow = max(mrow, mag_bits8(v[j]));
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mrow = max(mrow, (uint32_t)__shfl_xor((int)mrow, off));
+  }
+  const float amax = mag_value(mrow);
   const float g = (amax == 0.0f) ? 1.0f : 2688.0f / amax;  // 448 * 6 / amax, one IEEE division
   if (live && lane == 0) gsf_rows[row] = g;
 #pragma unroll
@@ -299,8 +318,11 @@ __global__ __launch_bounds__(256) void nvfp4_quantize_token_kernel(
 #pragma unroll
     for (int j = 0; j < C; ++j) {
       const int64_t e = sg * seg_elems + (int64_t)(j * 64 + lane) * 8;
-      if (nseg > 1) v[j] = (live && e < K) ? load8<VEC>(xr + e) : make_uint4(0u, 0u, 0u, 0u);
-      const float a = pair_max(finite_absmax8(v[j]));
+      if (nseg > 1) {
+        v[j] = (live && e < K) ? load8<VEC>(xr + e) : make_uint4(0u, 0u, 0u, 0u);
+        if (nonfinite) v[j] = nan_to_num8(v[j]);
+      }
+      const float a = pair_max(mag_value(mag_bits8(v[j])));
       float f[8];
       unpack8(v[j], f);
       const uint32_t S = e4m3_encode_pos(g * (a * kSixth));
@@ -391,6 +413,9 @@ __global__ __launch_bounds__(256) void rmsnorm_token_kernel(
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
   const float r = live ? (float)(1.0 / sqrt(ss / (double)K + (double)eps)) : 0.0f;
+  // y can only be infinite or NaN when the row is (ss, a sum of squares, is then infinite or NaN)
+  // or when a gain multiplies it: only then does the encoder need its input substituted
+  const bool maybe_nonfinite = GAIN || !(ss <= DBL_MAX);
   if (QUANT) __syncthreads();  // rtab
 
   const int64_t half_k = K / 2;
@@ -413,8 +438,8 @@ __global__ __launch_bounds__(256) void rmsnorm_token_kernel(
 #pragma unroll
         for (int i = 0; i < 8; ++i) f[i] = f[i] * w[i];
       }
-      const uint4 y = make_uint4(bf16x2_rne(f[0], f[1]), bf16x2_rne(f[2], f[3]),
-                                 bf16x2_rne(f[4], f[5]), bf16x2_rne(f[6], f[7]));
+      uint4 y = make_uint4(bf16x2_rne(f[0], f[1]), bf16x2_rne(f[2], f[3]),
+                           bf16x2_rne(f[4], f[5]), bf16x2_rne(f[6], f[7]));
       if (!QUANT) {
         if (in) {
           if (VEC) {
@@ -431,9 +456,9 @@ __global__ __launch_bounds__(256) void rmsnorm_token_kernel(
         }
         continue;
       }
-      uint4 yq = y;
-      const float a = pair_max(finite_absmax8(yq));
-      unpack8(yq, f);
+      if (maybe_nonfinite) y = nan_to_num8(y);   // wave-uniform
+      const float a = pair_max(mag_value(mag_bits8(y)));
+      unpack8(y, f);
       const uint32_t S = e4m3_encode_pos(g * (a * kSixth));
       const float rs = rtab[S];
       uint32_t o = 0;
@@ -492,12 +517,13 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const uint16_t* __r
     for (int s = 0; s < 8; ++s)
       v[s] = (kin && row0 + s * 8 + rsub < M) ? load8<VEC>(xp + s * xstep) : make_uint4(0u, 0u, 0u, 0u);
   }
+  nan_to_num_segments(v);
   const int64_t ng = K / 32;
   uint8_t* qp = q + (row0 + rsub) * K + kk;
   uint8_t* sp = sf + (row0 + rsub) * ng + kk / 32;
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
-    const float a = quad_max(finite_absmax8(v[s]));
+    const float a = quad_max(mag_value(mag_bits8(v[s])));
     float f[8];
     unpack8(v[s], f);
     const uint32_t ef = __float_as_uint(a) >> 23;            // biased exponent (a >= 0, finite)
@@ -558,12 +584,13 @@ __global__ __launch_bounds__(256) void mxfp4_quantize_kernel(const uint16_t* __r
     for (int s = 0; s < 16; ++s)
       v[s] = (kin && row0 + s * 8 + rsub < M) ? load8<VEC>(xp + s * xstep) : make_uint4(0u, 0u, 0u, 0u);
   }
+  nan_to_num_segments(v);
   const int64_t half_k = K / 2;
   uint8_t* pp = packed + (row0 + rsub) * half_k + kk / 2;
   const int64_t pstep = 8 * half_k;
 #pragma unroll
   for (int s = 0; s < 16; ++s) {
-    const float a = quad_max(finite_absmax8(v[s]));
+    const float a = quad_max(mag_value(mag_bits8(v[s])));
     float f[8];
     unpack8(v[s], f);
     const uint32_t ef = __float_as_uint(a) >> 23;

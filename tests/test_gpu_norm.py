@@ -168,3 +168,25 @@ def test_rmsnorm_tiny_and_huge_rows(k):
     check_norm(host_bits(bsp.bsp_rmsnorm_bf16(x, None, eps)), xb, None, eps, f"tiny/huge {k}")
     p, sf = bsp.bsp_nvfp4_quantize_rmsnorm(x, scalar(1.0), None, eps)
     check_fused(p, sf, xb, None, eps, 1.0, f"quantize tiny/huge {k}")
+
+
+def test_quantize_rmsnorm_nonfinite_rows():
+    """Rows holding an inf or a NaN: their RMS is infinite or NaN, so y is +-0 or NaN there, which
+    the quantize encodes as nan_to_num gives it (zero codes, signed zeros kept); the other rows as
+    usual. Bit-exact against the oracle chain on every byte: each finite row is +-2^e for one e per
+    row, so its y is +-1 / sqrt(1 + eps 2^-2e), within 3e-5 of +-1 and far from a bf16 rounding
+    boundary (no rounding-ambiguous values)."""
+    say("quantize_rmsnorm nonfinite rows")
+    m, k = 140, 512
+    rng = np.random.default_rng(71)
+    e = rng.integers(-2, 4, (m, 1))
+    xb = W.f32_to_bf16_bits(np.ldexp(np.where(rng.integers(0, 2, (m, k)) == 1, -1.0, 1.0),
+                                     np.broadcast_to(e, (m, k))).astype(np.float32))
+    xb[3, 17] = 0x7F80           # +inf
+    xb[4, 100] = 0xFF80          # -inf
+    xb[5, 9] = 0x7FC0            # NaN
+    xb[6] = 0x7F81               # a row of NaN patterns
+    p, sf = bsp.bsp_nvfp4_quantize_rmsnorm(dev_bf16(xb), scalar(1.0), None, 1e-6)
+    rp, rs = N.quantize(R.rms_norm_bf16_bits(xb, None, 1e-6), np.float32(1.0))
+    assert np.array_equal(host_u8(p), rp)
+    assert np.array_equal(host_u8(sf).ravel(), rs)
