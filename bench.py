@@ -570,7 +570,7 @@ def measure_ceilings() -> dict:
         res[name] = round((nread + nwrite) / ms / 1e6, 1)
     del src, dst
     res["note"] = ("MFMA-only loops: 1024 workgroups x 4 waves, four independent accumulator chains per "
-                   "wave; streams: 2 GiB read, nontemporal, 2048 workgroups")
+                   "wave; streams: 2 GiB read, nontemporal, 16 loads in flight per thread, 2048 workgroups")
     return res
 
 

@@ -88,21 +88,24 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(float* out, int iters, u
 
 typedef uint32_t nt_u32x4 __attribute__((ext_vector_type(4)));
 
-// Streaming over n16 16-byte chunks, four loads in flight per thread, nontemporal as the
-// quantizers' loads and stores are. WRITE_DIV 0: read only (one word per thread written at the
-// end); 1: copy; 4: a quarter of the bytes read are written (about the NVFP4 quantize's 2 : 0.56).
+// Streaming over n16 16-byte chunks with sixteen loads in flight per thread (as many as the
+// quantizers keep), nontemporal as their loads and stores are. WRITE_DIV 0: read only (one word per
+// thread written at the end); 1: copy; 4: a quarter of the bytes read are written (about the NVFP4
+// quantize's 2 : 0.56).
+constexpr int kInFlight = 16;
 template <int WRITE_DIV>
 __global__ __launch_bounds__(256) void stream_kernel(const u32x4* __restrict__ src,
                                                      uint32_t* __restrict__ dst, int64_t n16) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   uint32_t x = 0;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    nt_u32x4 v[4];
+  for (; i + (kInFlight - 1) * stride < n16; i += kInFlight * stride) {
+    nt_u32x4 v[kInFlight];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4*>(src) + i + u * stride);
+    for (int u = 0; u < kInFlight; ++u)
+      v[u] = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4*>(src) + i + u * stride);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kInFlight; ++u) {
       if (WRITE_DIV == 1) {
         __builtin_nontemporal_store(v[u], reinterpret_cast<nt_u32x4*>(dst) + i + u * stride);
       } else if (WRITE_DIV == 4) {

@@ -21,7 +21,7 @@ extern "C" {
 int bsp_probe_mfma_loop(int fmt, int workgroups, int iters, float* out, void* stream);
 
 /* Streaming over n16 16-byte chunks of src (16-byte aligned device memory) with nontemporal loads
- * and stores, four loads in flight per thread, grid-stride over `workgroups` x 256 threads:
+ * and stores, sixteen loads in flight per thread, grid-stride over `workgroups` x 256 threads:
  *   write_div 0: read only; dst receives one uint32 per thread (workgroups * 256 * 4 bytes);
  *   write_div 1: copy, dst holds n16 * 16 bytes;
  *   write_div 4: one uint32 written per chunk read (read:write 4:1, near the NVFP4 quantize's
