@@ -14,6 +14,18 @@ Reading (as for MXFP8, with the e2m1 element):
   q_i  = e2m1(fl32(x_i * 2^-Es)), nearest even, saturating at +-6.
 Scales use the same 128x4 layout as NVFP4's (one byte per 32 K elements instead of 16), the
 layout ``mm_fp4`` takes for both kinds of operands.
+
+Fragment layout (``layout="frag"``). The FastVideo quantize op carries a ``do_shuffle`` switch for
+operands pre-arranged for the matrix unit, always off there and never defined on the pages: the
+arrangement is the library's. This one follows gfx950's block-scaled MFMA
+(v_mfma_scale_f32_32x32x64_f8f6f4), whose lane i + 32 h reads, for a 32-row tile and a 64-element
+K step, row i's 32-element block h of that step (16 bytes of e2m1) and that block's e8m0 scale.
+Operand [R, K], K % 256 == 0, rows padded with zeros to Rp = 32 * ceil(R / 32):
+  packed byte (r, j) (elements 2j, 2j+1 of row r) ->
+      ((r // 32) * (K // 64) + j // 32) * 1024 + ((j // 16) % 2 * 32 + r % 32) * 16 + j % 16;
+  scale (r, b) (block b = k // 32 of row r) ->
+      ((r // 32) * (K // 256) + b // 8) * 256 + (b % 2 * 32 + r % 32) * 4 + (b // 2) % 4.
+Only the byte order differs from the linear layout: same codes, same scales.
 """
 from __future__ import annotations
 
@@ -53,7 +65,8 @@ def quantize_blocks(xf: np.ndarray):
 
 
 def quantize(x_bits: np.ndarray, layout: str = "128x4"):
-    """bf16 X [M, K] (K % 32 == 0) -> (packed [M, K/2], scales: flat 128x4 bytes or [M, K/32])."""
+    """bf16 X [M, K] (K % 32 == 0) -> (packed [M, K/2], scales: flat 128x4 bytes or [M, K/32]);
+    layout "frag" (K % 256 == 0): both flat in the fragment layout."""
     x_bits = bf16_nan_to_num(x_bits)   # NaN -> 0, +-inf -> +-largest finite bf16 (reading U9)
     m, k = x_bits.shape
     if k % GROUP:
@@ -63,10 +76,75 @@ def quantize(x_bits: np.ndarray, layout: str = "128x4"):
     packed = pack_nibbles(codes.reshape(m, k))
     if layout == "linear":
         return packed, s
+    if layout == "frag":
+        return to_frag(packed, s, k)
     rp, cp = sf_padded_shape(m, k)
     lin = np.zeros((rp, cp), dtype=np.uint8)
     lin[:m, :ng] = s
     return packed, swizzle_128x4(lin)
+
+
+def frag_rows(rows: int) -> int:
+    return (rows + 31) // 32 * 32
+
+
+def frag_packed_offset(r, j, k: int):
+    """Byte offset in the fragment layout of packed byte j (elements 2j, 2j+1) of row r."""
+    r = np.asarray(r, dtype=np.int64)
+    j = np.asarray(j, dtype=np.int64)
+    row_tile, lane_row = r // 32, r % 32
+    k_step, half, byte = j // 32, (j // 16) % 2, j % 16
+    return (row_tile * (k // 64) + k_step) * 1024 + (half * 32 + lane_row) * 16 + byte
+
+
+def frag_sf_offset(r, b, k: int):
+    """Byte offset in the fragment layout of the scale of block b (K elements 32b..32b+31) of row r."""
+    r = np.asarray(r, dtype=np.int64)
+    b = np.asarray(b, dtype=np.int64)
+    row_tile, lane_row = r // 32, r % 32
+    group, step_in_group, half = b // 8, (b // 2) % 4, b % 2
+    return (row_tile * (k // 256) + group) * 256 + (half * 32 + lane_row) * 4 + step_in_group
+
+
+def to_frag(packed: np.ndarray, scales: np.ndarray, k: int):
+    """(packed [R, K/2], linear scales [R, K/32]) -> flat fragment-layout (packed, scales), zero rows
+    to the next multiple of 32."""
+    if k % 256:
+        raise ValueError("the fragment layout needs K % 256 == 0")
+    rows = packed.shape[0]
+    rp = frag_rows(rows)
+    fp = np.zeros(rp * k // 2, dtype=np.uint8)
+    fs = np.zeros(rp * k // 32, dtype=np.uint8)
+    r, j = np.meshgrid(np.arange(rows), np.arange(k // 2), indexing="ij")
+    fp[frag_packed_offset(r, j, k)] = packed
+    r, b = np.meshgrid(np.arange(rows), np.arange(k // 32), indexing="ij")
+    fs[frag_sf_offset(r, b, k)] = scales
+    return fp, fs
+
+
+def from_frag(fp: np.ndarray, fs: np.ndarray, rows: int, k: int):
+    """Flat fragment-layout (packed, scales) -> (packed [rows, K/2], linear scales [rows, K/32])."""
+    fp = np.asarray(fp, dtype=np.uint8).ravel()
+    fs = np.asarray(fs, dtype=np.uint8).ravel()
+    r, j = np.meshgrid(np.arange(rows), np.arange(k // 2), indexing="ij")
+    packed = fp[frag_packed_offset(r, j, k)]
+    r, b = np.meshgrid(np.arange(rows), np.arange(k // 32), indexing="ij")
+    return packed, fs[frag_sf_offset(r, b, k)]
+
+
+def dequant_linear(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """packed [R, K/2] with linear e8m0 scales [R, K/32] -> fp64 values [R, K]."""
+    rows, k = packed.shape[0], packed.shape[1] * 2
+    codes = unpack_nibbles(np.asarray(packed)).astype(np.int64)
+    vals = e2m1_decode(codes).reshape(rows, k // GROUP, GROUP) * e8m0_decode(scales)[..., None]
+    return vals.reshape(rows, k)
+
+
+def mm_mxfp4_frag(a_fp, a_fs, b_fp, b_fs, alpha_val, m: int, n: int, k: int) -> np.ndarray:
+    """C[m, n] = alpha * sum_k A[m, k] B[n, k] in fp64 for fragment-layout operands."""
+    A = dequant_linear(*from_frag(a_fp, a_fs, m, k))
+    B = dequant_linear(*from_frag(b_fp, b_fs, n, k))
+    return np.float64(F32(alpha_val)) * (A @ B.T)
 
 
 def dequant_rows(packed, sf_flat, rows, n_rows_total: int, k: int) -> np.ndarray:

@@ -77,3 +77,62 @@ def test_mm_mxfp4_brute_force_and_torch():
     assert np.allclose(float(al) * (A @ B.T).numpy(), ref, rtol=1e-12)
     r, c = np.array([2, 0]), np.array([4, 1])
     assert np.allclose(X4.mm_mxfp4_entries(pa, sa, pb, sb, al, m, n, k, r, c), ref[r, c], rtol=1e-12)
+
+
+# ------------------------------------------------------------------------ fragment layout
+def test_frag_offsets_hand_worked():
+    n = 0
+    for line in golden_lines("frag_offsets_mxfp4.txt"):
+        kind, r, c, k, off = line.split()[:5]
+        fn = X4.frag_packed_offset if kind == "p" else X4.frag_sf_offset
+        assert int(fn(int(r), int(c), int(k))) == int(off), line
+        n += 1
+    assert n == 15
+
+
+def test_frag_offsets_are_a_permutation():
+    for rows, k in [(33, 256), (64, 512), (5, 768)]:
+        rp = X4.frag_rows(rows)
+        r, j = np.meshgrid(np.arange(rp), np.arange(k // 2), indexing="ij")
+        off = X4.frag_packed_offset(r, j, k).ravel()
+        assert np.array_equal(np.sort(off), np.arange(rp * k // 2))
+        r, b = np.meshgrid(np.arange(rp), np.arange(k // 32), indexing="ij")
+        off = X4.frag_sf_offset(r, b, k).ravel()
+        assert np.array_equal(np.sort(off), np.arange(rp * k // 32))
+
+
+def test_frag_layout_matches_mfma_lane_placement():
+    """Independent construction by axis permutation: a fragment is [lane half h][row i][16 bytes]
+    of one 32-row tile and 64-K step; a scale group is [h][i][step j of the group]."""
+    rng = np.random.default_rng(8)
+    rows, k = 70, 768
+    packed = rng.integers(0, 256, size=(rows, k // 2)).astype(np.uint8)
+    scales = rng.integers(0, 256, size=(rows, k // 32)).astype(np.uint8)
+    fp, fs = X4.to_frag(packed, scales, k)
+    rp = X4.frag_rows(rows)
+    pp = np.zeros((rp, k // 2), dtype=np.uint8)
+    pp[:rows] = packed
+    ps = np.zeros((rp, k // 32), dtype=np.uint8)
+    ps[:rows] = scales
+    # packed [tile, i, step, h, byte] -> [tile, step, h, i, byte]
+    want_p = pp.reshape(rp // 32, 32, k // 64, 2, 16).transpose(0, 2, 3, 1, 4).ravel()
+    # scales [tile, i, group, j, h] (block = 8 group + 2 j + h) -> [tile, group, h, i, j]
+    want_s = ps.reshape(rp // 32, 32, k // 256, 4, 2).transpose(0, 2, 4, 1, 3).ravel()
+    assert np.array_equal(fp, want_p) and np.array_equal(fs, want_s)
+    back_p, back_s = X4.from_frag(fp, fs, rows, k)
+    assert np.array_equal(back_p, packed) and np.array_equal(back_s, scales)
+
+
+def test_frag_quantize_and_gemm_agree_with_the_linear_layouts():
+    xa = W.small_case(45, 512, 11, outlier_frac=0.02)
+    xb = W.small_case(37, 512, 12, outlier_frac=0.02)
+    fa, fsa = X4.quantize(xa, layout="frag")
+    pa, sa = X4.quantize(xa, layout="linear")
+    assert np.array_equal(X4.from_frag(fa, fsa, 45, 512)[0], pa)
+    assert np.array_equal(X4.from_frag(fa, fsa, 45, 512)[1], sa)
+    assert fa.size == 64 * 256 and not fa[X4.frag_packed_offset(np.arange(45, 64)[:, None], np.arange(256)[None, :], 512)].any()
+    fb, fsb = X4.quantize(xb, layout="frag")
+    got = X4.mm_mxfp4_frag(fa, fsa, fb, fsb, np.float32(0.75), 45, 37, 512)
+    a1, s1 = X4.quantize(xa)
+    b1, t1 = X4.quantize(xb)
+    assert np.array_equal(got, X4.mm_mxfp4(a1, s1, b1, t1, np.float32(0.75), 45, 37, 512))
