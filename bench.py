@@ -315,6 +315,7 @@ def main():
         qw, sw = bsp.bsp_mxfp8_quantize(w5)       # online BF16 -> MXFP8 weight conversion
         m1.record(stream)
         pw4, sw4 = bsp.bsp_mxfp4_quantize(w5)     # and to MXFP4 for the mm_fp4 MX variant
+        pw4f, sw4f = bsp.bsp_mxfp4_quantize_frag(w5)   # (MFMA fragment layout)
         qx = torch.empty((M, K1), dtype=torch.uint8, device=dev)
         sxm = torch.empty((M, K1 // 32), dtype=torch.uint8, device=dev)
         out5 = torch.empty((M, N1), dtype=torch.bfloat16, device=dev)
@@ -381,6 +382,40 @@ def main():
             "quantize_ms": round(q4, 4), "quantize_GBs": round(qb4 / q4 / 1e6, 1),
             "quantize_frac_hbm": round(qb4 / q4 / 1e6 / PEAK_HBM_GBS, 4)}
         log(json.dumps(result["mxfp4"]))
+        del px4, sx4
+
+        # ---- the same MXFP4 layer with both operands in the MFMA fragment layout
+        px4f, sx4f = bsp.bsp_mxfp4_quantize_frag(x5)
+
+        def step4f(e=None):
+            if e:
+                e[0].record(stream)
+            bsp.bsp_mxfp4_quantize_frag(x5, px4f, sx4f)
+            if e:
+                e[1].record(stream)
+            bsp.bsp_mm_mxfp4_frag(px4f, sx4f, pw4f, sw4f, M, N1, out=out5)
+            if e:
+                e[2].record(stream)
+
+        for _ in range(args.warmup):
+            step4f()
+        torch.cuda.synchronize()
+        e4f = [[ev() for _ in range(3)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            step4f(e4f[i])
+        torch.cuda.synchronize()
+        q4f = sum(e[0].elapsed_time(e[1]) for e in e4f) / args.steps
+        g4f = sum(e[1].elapsed_time(e[2]) for e in e4f) / args.steps
+        tf4f = 2.0 * M * N1 * K1 / g4f / 1e9
+        qb4f = 2 * M * K1 + (-(-M // 32) * 32) * (K1 // 2 + K1 // 32)
+        result["mxfp4_frag"] = {
+            "mm_mxfp4_frag_ms": round(g4f, 4), "TFLOPS": round(tf4f, 2),
+            "frac_fp4_peak": round(tf4f / PEAK_FP4_TFLOPS, 4),
+            "quantize_frag_ms": round(q4f, 4), "quantize_GBs": round(qb4f / q4f / 1e6, 1),
+            "quantize_frac_hbm": round(qb4f / q4f / 1e6 / PEAK_HBM_GBS, 4),
+            "step_ms": round(q4f + g4f, 4), "step_ms_linear_layout": round(q4 + g4, 4)}
+        log(json.dumps(result["mxfp4_frag"]))
+        del px4f, sx4f, pw4f, sw4f
 
     # ---- PyTorch's own memory-bound kernels on the same GPU, for context beside the published
     # 8 TB/s: a 2 GiB device-to-device copy (read:write 1:1) and a 2 GiB fp32 sum (read only), timed
@@ -436,6 +471,9 @@ def main():
             kernels_frac["mm_mxfp8_of_fp8_mfma_loop"] = result["mxfp8"]["TFLOPS"] / mp["mfma_fp8_scaled_TFLOPS"]
         if "mxfp4" in result:
             kernels_frac["mm_mxfp4_of_fp4_mfma_loop"] = result["mxfp4"]["TFLOPS"] / mp["mfma_fp4_scaled_TFLOPS"]
+        if "mxfp4_frag" in result:
+            kernels_frac["mm_mxfp4_frag_of_fp4_mfma_loop"] = (result["mxfp4_frag"]["TFLOPS"]
+                                                              / mp["mfma_fp4_scaled_TFLOPS"])
         result["frac_of_measured_peak"] = {k_: round(v, 4) for k_, v in kernels_frac.items()}
         log(json.dumps(result["measured_peak"]), json.dumps(result["frac_of_measured_peak"]))
 

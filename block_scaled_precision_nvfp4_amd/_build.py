@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(CSRC, "_build")
 LIB = os.path.join(HERE, "libbsp.so")
-SOURCES = ["api.hip", "quantize.hip", "gemm_fp4.hip", "gemm_mx.hip"]
+SOURCES = ["api.hip", "quantize.hip", "gemm_fp4.hip", "gemm_mx.hip", "gemm_mx_frag.hip"]
 # measurement probes (MFMA-only loops, streaming kernels): a separate library only the benchmark loads
 PROBE_SOURCES = ["probe.hip"]
 PROBE_LIB = os.path.join(HERE, "libbsp_probe.so")

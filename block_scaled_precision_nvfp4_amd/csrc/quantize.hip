@@ -560,12 +560,20 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const uint16_t* __r
 // Es + 127 with Es = clamp(floor(log2 amax) - 2, -127, 127) (0x00 for amax == 0); elements
 // e2m1(x * 2^-Es) (exact scaling, nearest even, saturating at 6). The 8 scale columns of a
 // workgroup are two 128x4 column groups, staged in LDS and stored as whole 512-byte tiles.
-template <bool HWCVT, bool VEC>
+//
+// FRAG: both outputs in the MFMA fragment layout instead (K % 256 == 0; the layout is described at
+// bsp_mxfp4_quantize_frag). The workgroup's 128 rows x 256 K are 4 row tiles x 4 K steps, sixteen
+// 1 KB fragments and four 256-byte scale groups: all staged in LDS and stored as four contiguous
+// 4 KB runs and four 256-byte runs. A thread's 4 output bytes for row rr and block cb are 16-byte
+// chunk p = (rr/32)*256 + cb*32 + rr%32 of the staging area (cb = 2 * K step + lane half), placed
+// at chunk p ^ 2cb: the eight blocks of a row otherwise sit 512 bytes apart, all in one LDS bank.
+template <bool HWCVT, bool VEC, bool FRAG = false>
 __global__ __launch_bounds__(256) void mxfp4_quantize_kernel(const uint16_t* __restrict__ x,
                                                              int64_t M, int64_t K, int64_t ld,
                                                              uint8_t* __restrict__ packed,
                                                              uint8_t* __restrict__ sf, int64_t Kp) {
-  __shared__ uint4 sf_tile[64];  // 1 KB = 2 scale tiles of 512 B
+  __shared__ uint4 sf_tile[64];  // 1 KB = 2 scale tiles of 512 B (FRAG: 4 scale groups of 256 B)
+  __shared__ uint4 frag_tile[FRAG ? 1024 : 1];  // FRAG: the workgroup's 16 KB of packed fragments
   uint8_t* sfb = reinterpret_cast<uint8_t*>(sf_tile);
   const int t = threadIdx.x;
   const int64_t row0 = (int64_t)blockIdx.y * 128;
@@ -607,13 +615,36 @@ __global__ __launch_bounds__(256) void mxfp4_quantize_kernel(const uint16_t* __r
       for (int i = 0; i < 8; ++i) out |= e2m1_encode(f[i] * inv) << (4 * i);
     }
     const int rr = s * 8 + rsub;
-    if (full || (kin && row0 + rr < M)) store4_nt(pp + s * pstep, out);
-    if ((t & 3) == 0) {
-      const int cb = (t & 31) >> 2;  // scale column inside the 8-column tile
-      sfb[(cb >> 2) * 512 + (rr & 31) * 16 + (rr >> 5) * 4 + (cb & 3)] = (uint8_t)byte;
+    const int cb = (t & 31) >> 2;  // the lane quad's 32-element block inside the workgroup's 256 K
+    if constexpr (FRAG) {
+      const int p = (rr >> 5) * 256 + cb * 32 + (rr & 31);
+      reinterpret_cast<uint32_t*>(frag_tile)[(p ^ (cb << 1)) * 4 + (t & 3)] = out;
+      if ((t & 3) == 0) sfb[(rr >> 5) * 256 + ((cb & 1) * 32 + (rr & 31)) * 4 + (cb >> 1)] = (uint8_t)byte;
+    } else {
+      if (full || (kin && row0 + rr < M)) store4_nt(pp + s * pstep, out);
+      if ((t & 3) == 0)  // cb: scale column inside the 8-column tile
+        sfb[(cb >> 2) * 512 + (rr & 31) * 16 + (rr >> 5) * 4 + (cb & 3)] = (uint8_t)byte;
     }
   }
   __syncthreads();
+  if constexpr (FRAG) {
+    // row tiles past ceil(M / 32) are not part of the buffers; padded rows inside the last one
+    // were encoded from zeros (code 0, scale 0x00)
+    const int64_t row_tiles = (M + 31) / 32, rt0 = (int64_t)blockIdx.y * 4;
+    const int64_t ks_steps = K / 64, k_groups = K / 256;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int p = it * 256 + t;
+      if (rt0 + it < row_tiles) {
+        const uint4 v = frag_tile[p ^ (((p >> 5) & 7) << 1)];
+        __builtin_nontemporal_store((nt_u32x4){v.x, v.y, v.z, v.w},
+                                    reinterpret_cast<nt_u32x4*>(packed + ((rt0 + it) * ks_steps + blockIdx.x * 4) * 1024) + (p & 255));
+      }
+    }
+    if (t < 64 && rt0 + (t >> 4) < row_tiles)
+      reinterpret_cast<uint4*>(sf + ((rt0 + (t >> 4)) * k_groups + blockIdx.x) * 256)[t & 15] = sf_tile[t];
+    return;
+  }
   const int64_t groups = Kp / 4;
   const int64_t g0 = (int64_t)blockIdx.x * 2;
   const int64_t ng = groups - g0 < 2 ? groups - g0 : 2;
@@ -986,6 +1017,45 @@ extern "C" int bsp_mxfp4_sf_bytes(int64_t rows, int64_t K, int64_t* bytes) {
   BSP_REQUIRE(rows >= 0 && K >= 0, BSP_EINVAL, "bsp_mxfp4_sf_bytes: negative size");
   *bytes = ceil_div(rows, 128) * 128 * ceil_div(K, 128) * 4;
   return BSP_OK;
+}
+
+extern "C" int bsp_mxfp4_frag_bytes(int64_t rows, int64_t K, int64_t* packed_bytes, int64_t* sf_bytes) {
+  BSP_REQUIRE(packed_bytes && sf_bytes, BSP_EINVAL, "bsp_mxfp4_frag_bytes: null output pointer");
+  BSP_REQUIRE(rows >= 0 && K >= 0, BSP_EINVAL, "bsp_mxfp4_frag_bytes: negative size");
+  BSP_REQUIRE(K % 256 == 0, BSP_ESHAPE, "bsp_mxfp4_frag_bytes: K (%lld) must be a multiple of 256",
+              (long long)K);
+  *packed_bytes = ceil_div(rows, 32) * 32 * (K / 2);
+  *sf_bytes = ceil_div(rows, 32) * 32 * (K / 32);
+  return BSP_OK;
+}
+
+extern "C" int bsp_mxfp4_quantize_frag(const void* x, int64_t M, int64_t K, int64_t ld, uint8_t* packed,
+                                       uint8_t* sf, void* stream) {
+  const char* fn = "bsp_mxfp4_quantize_frag";
+  BSP_REQUIRE(M >= 0 && K > 0, BSP_EINVAL, "%s: bad size M=%lld K=%lld", fn, (long long)M, (long long)K);
+  BSP_REQUIRE(K % 256 == 0, BSP_ESHAPE, "%s: K (%lld) must be a multiple of 256", fn, (long long)K);
+  BSP_REQUIRE(M <= 1 || ld >= K, BSP_ESHAPE, "%s: ld (%lld) < K (%lld)", fn, (long long)ld, (long long)K);
+  if (M == 0) return BSP_OK;
+  BSP_REQUIRE(x && packed && sf, BSP_EINVAL, "%s: null pointer", fn);
+  BSP_REQUIRE(((reinterpret_cast<uintptr_t>(packed) | reinterpret_cast<uintptr_t>(sf)) & 15u) == 0,
+              BSP_EINVAL, "%s: packed and sf must be 16-byte aligned", fn);
+  BSP_REQUIRE(ceil_div(M, 128) < 65536, BSP_ESHAPE, "%s: M too large", fn);
+  if (int e = check_device()) return e;
+  dim3 grid((unsigned)(K / 256), (unsigned)ceil_div(M, 128));
+  const uint16_t* xp = static_cast<const uint16_t*>(x);
+  const bool vec = (ld % 8 == 0) && aligned16(x);
+  const bool hw = hw_cvt_enabled();
+  const int64_t Kp = K / 32;
+  hipStream_t s = (hipStream_t)stream;
+  if (hw && vec)
+    hipLaunchKernelGGL((mxfp4_quantize_kernel<true, true, true>), grid, dim3(256), 0, s, xp, M, K, ld, packed, sf, Kp);
+  else if (hw)
+    hipLaunchKernelGGL((mxfp4_quantize_kernel<true, false, true>), grid, dim3(256), 0, s, xp, M, K, ld, packed, sf, Kp);
+  else if (vec)
+    hipLaunchKernelGGL((mxfp4_quantize_kernel<false, true, true>), grid, dim3(256), 0, s, xp, M, K, ld, packed, sf, Kp);
+  else
+    hipLaunchKernelGGL((mxfp4_quantize_kernel<false, false, true>), grid, dim3(256), 0, s, xp, M, K, ld, packed, sf, Kp);
+  return check_launch(fn);
 }
 
 extern "C" int bsp_mxfp4_quantize(const void* x, int64_t M, int64_t K, int64_t ld, uint8_t* packed,

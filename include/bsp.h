@@ -278,6 +278,38 @@ int bsp_mm_mxfp4_bias(const uint8_t* a_packed, const uint8_t* a_sf, const uint8_
                       const uint8_t* b_sf, const float* alpha_dev, const void* bias_bf16, int64_t M,
                       int64_t N, int64_t K, void* out, int64_t ldc, int out_dtype, void* stream);
 
+/* MXFP4 in the MFMA fragment layout. [FV-NV] _nvfp4_quantize passes a do_shuffle switch to its
+ * quantizer: operands pre-arranged for the matrix unit, the arrangement being the library's (the
+ * pages always pass False). This is that arrangement for gfx950's block-scaled MFMA
+ * (v_mfma_scale_f32_32x32x64_f8f6f4): each 64-lane operand fragment is one contiguous 1 KB, so the
+ * GEMM loads it straight into registers without staging through LDS. Same element and scale values
+ * as bsp_mxfp4_quantize (OCP MX rule above); only the byte order differs. Operand [R, K],
+ * K % 256 == 0, Rp = ceil(R/32)*32 rows (rows R..Rp-1 zero: codes 0, scales 0x00):
+ *  packed (Rp*K/2 bytes): byte j = 16 l + c of the 1 KB fragment at (rt*(K/64) + ks)*1024, lane
+ *    l = i + 32 h, holds elements 2c, 2c+1 (low nibble first) of the 32-element block 2 ks + h of
+ *    row 32 rt + i, i.e. elements 64 ks + 32 h + 2c, +1;
+ *  scales (Rp*K/32 bytes): byte 4 l + jj of the 256-byte group at (rt*(K/256) + kg)*256 is the
+ *    e8m0 scale of row 32 rt + i (l = i + 32 h), block 8 kg + 2 jj + h.
+ * Sizes: bsp_mxfp4_frag_bytes (BSP_ESHAPE unless K % 256 == 0). */
+int bsp_mxfp4_frag_bytes(int64_t rows, int64_t K, int64_t* packed_bytes, int64_t* sf_bytes);
+
+/* bsp_mxfp4_quantize writing the fragment layout. x: device bf16 [M, K] (row stride ld),
+ * K % 256 == 0 (else BSP_ESHAPE) -> packed and sf as above (bsp_mxfp4_frag_bytes(M, K) bytes each),
+ * both 16-byte aligned (else BSP_EINVAL); every byte of both, padding rows included, is written.
+ * M == 0 is a no-op. */
+int bsp_mxfp4_quantize_frag(const void* x_bf16, int64_t M, int64_t K, int64_t ld, uint8_t* packed,
+                            uint8_t* sf, void* stream);
+
+/* bsp_mm_mxfp4 on fragment-layout operands: C = alpha * A . B^T (+ bias), alpha_dev may be NULL
+ * (alpha = 1), bias_bf16 a device bf16 [N] or NULL (added as in bsp_mm_mxfp4_bias). a: A [M, K] and
+ * b: B [N, K] (K-major weight) in the fragment layout, each with its scales; out [M, N] row stride
+ * ldc, bf16 or fp32. For the same operand values the output is bit-identical to bsp_mm_mxfp4's (and
+ * bsp_mm_mxfp4_bias's). Requires K % 256 == 0 (else BSP_ESHAPE); fragments 16-byte and scales
+ * 4-byte aligned, bias 2-byte aligned (else BSP_EINVAL). */
+int bsp_mm_mxfp4_frag(const uint8_t* a_packed, const uint8_t* a_sf, const uint8_t* b_packed,
+                      const uint8_t* b_sf, const float* alpha_dev, const void* bias_bf16, int64_t M,
+                      int64_t N, int64_t K, void* out, int64_t ldc, int out_dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -252,3 +252,37 @@ def test_alignment_rules_match_the_header():
     assert st == -1 and "16-byte" in msg
     st, msg = _st("bsp_mxfp8_quantize", P, 4, 64, 64, a4, P, None)
     assert st == -1 and "8-byte" in msg
+
+
+def test_mxfp4_frag_entry_points():
+    """Fragment-layout MXFP4: sizes, and every argument rule rejected on the host before a launch."""
+    pb, sb = ctypes.c_int64(0), ctypes.c_int64(0)
+    assert bsp.lib().bsp_mxfp4_frag_bytes(33, 512, ctypes.byref(pb), ctypes.byref(sb)) == 0
+    assert (pb.value, sb.value) == (64 * 256, 64 * 16)
+    assert bsp.lib().bsp_mxfp4_frag_bytes(0, 256, ctypes.byref(pb), ctypes.byref(sb)) == 0
+    assert (pb.value, sb.value) == (0, 0)
+    assert bsp.lib().bsp_mxfp4_frag_bytes(4, 384, ctypes.byref(pb), ctypes.byref(sb)) == -2
+    assert bsp.lib().bsp_mxfp4_frag_bytes(4, 256, None, ctypes.byref(sb)) == -1
+    assert bsp.bsp_mxfp4_frag_bytes(300, 1280) == (320 * 640, 320 * 40)
+    q = "bsp_mxfp4_quantize_frag"
+    st, msg = _st(q, P, 4, 384, 384, P, P, None)
+    assert st == -2 and "multiple of 256" in msg
+    assert _st(q, P, 4, 256, 128, P, P, None)[0] == -2             # ld < K
+    assert _st(q, None, 4, 256, 256, P, P, None)[0] == -1
+    assert _st(q, P, 4, 256, 256, ctypes.c_void_p(20), P, None)[0] == -1   # packed not 16-aligned
+    assert _st(q, P, 4, 256, 256, P, ctypes.c_void_p(24), None)[0] == -1   # sf not 16-aligned
+    assert _st(q, P, 65535 * 128 + 1, 256, 256, P, P, None)[0] == -2
+    assert _st(q, None, 0, 256, 256, None, None, None)[0] == 0     # M == 0: no-op
+    g = "bsp_mm_mxfp4_frag"
+    st, msg = _st(g, P, P, P, P, None, None, 4, 4, 384, P, 4, 0, None)
+    assert st == -2 and "multiple of 256" in msg
+    assert _st(g, P, P, P, P, None, None, 4, 4, 256, P, 4, 2, None)[0] == -3   # bad out dtype
+    assert _st(g, P, P, P, P, None, None, 4, 8, 256, P, 4, 0, None)[0] == -2   # ldc < N
+    assert _st(g, ctypes.c_void_p(24), P, P, P, None, None, 4, 4, 256, P, 4, 0, None)[0] == -1
+    assert _st(g, P, ctypes.c_void_p(18), P, P, None, None, 4, 4, 256, P, 4, 0, None)[0] == -1
+    assert _st(g, P, P, P, P, None, ctypes.c_void_p(17), 4, 4, 256, P, 4, 0, None)[0] == -1
+    assert _st(g, P, None, P, P, None, None, 4, 4, 256, P, 4, 0, None)[0] == -1
+    assert _st(g, None, None, None, None, None, None, 0, 4, 256, None, 4, 0, None)[0] == 0
+    # the aligned call passes validation and fails only for want of a gfx950 device here
+    st = _st(g, P, ctypes.c_void_p(20), P, P, None, ctypes.c_void_p(18), 4, 4, 256, P, 4, 0, None)[0]
+    assert st not in (-1, -2, -3), st
