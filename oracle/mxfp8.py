@@ -17,6 +17,16 @@ Reading U12 (the OCP MX scale rule; the page only cites the spec):
   byte = Es + 127, and byte 0x00 when amax == 0;
   q_i = e4m3(fl32(x_i * 2^-Es)), round to nearest even, saturate to +-448
   (values in (448, 512) therefore clamp to 448, as the floor rule implies).
+
+Fragment layout (``quantize_frag``): the operand arrangement for the matrix unit (reading U29, as
+for MXFP4 in ``oracle.mxfp4``), here for the e4m3 operand of gfx950's
+v_mfma_scale_f32_32x32x64_f8f6f4. For a 32-row tile and a 64-element K step, lane i + 32 h of the
+instruction holds 32 bytes of row i: its bytes 0-15 are elements 16h..16h+15 of the step's first
+32-element block and bytes 16-31 the same half of the second block; its e8m0 scale is that of
+block h of the step. Operand [R, K], K % 256 == 0, rows padded with zeros to Rp = 32 ceil(R/32):
+  element (r, k) -> ((r // 32) * (K // 64) + k // 64) * 2048 + (k // 32) % 2 * 1024
+                    + ((k // 16) % 2 * 32 + r % 32) * 16 + k % 16;
+  scale (r, b)   -> as the MXFP4 fragment layout's scale offset.
 """
 from __future__ import annotations
 
@@ -89,3 +99,54 @@ def mm_mxfp8_entries(a_q, a_sf, b_q, b_sf, rows, cols) -> np.ndarray:
     A = dequant_rows(a_q, a_sf, ur)
     B = dequant_rows(b_q, b_sf, uc)
     return np.einsum("ik,ik->i", A[ri], B[ci])
+
+
+def frag_offset(r, k_idx, k: int):
+    """Byte offset in the fragment layout of element k_idx of row r."""
+    r = np.asarray(r, dtype=np.int64)
+    k_idx = np.asarray(k_idx, dtype=np.int64)
+    row_tile, lane_row = r // 32, r % 32
+    k_step, block, half, byte = k_idx // 64, (k_idx // 32) % 2, (k_idx // 16) % 2, k_idx % 16
+    return ((row_tile * (k // 64) + k_step) * 2048 + block * 1024
+            + (half * 32 + lane_row) * 16 + byte)
+
+
+def to_frag(q: np.ndarray, scales: np.ndarray, k: int):
+    """(e4m3 [R, K], e8m0 [R, K/32]) -> flat fragment-layout (elements, scales), zero rows to the
+    next multiple of 32."""
+    from .mxfp4 import frag_rows, frag_sf_offset
+    if k % 256:
+        raise ValueError("the fragment layout needs K % 256 == 0")
+    rows = q.shape[0]
+    rp = frag_rows(rows)
+    fq = np.zeros(rp * k, dtype=np.uint8)
+    fs = np.zeros(rp * k // 32, dtype=np.uint8)
+    r, c = np.meshgrid(np.arange(rows), np.arange(k), indexing="ij")
+    fq[frag_offset(r, c, k)] = q
+    r, b = np.meshgrid(np.arange(rows), np.arange(k // 32), indexing="ij")
+    fs[frag_sf_offset(r, b, k)] = scales
+    return fq, fs
+
+
+def from_frag(fq: np.ndarray, fs: np.ndarray, rows: int, k: int):
+    """Flat fragment-layout (elements, scales) -> (e4m3 [rows, K], e8m0 [rows, K/32])."""
+    from .mxfp4 import frag_sf_offset
+    fq = np.asarray(fq, dtype=np.uint8).ravel()
+    fs = np.asarray(fs, dtype=np.uint8).ravel()
+    r, c = np.meshgrid(np.arange(rows), np.arange(k), indexing="ij")
+    q = fq[frag_offset(r, c, k)]
+    r, b = np.meshgrid(np.arange(rows), np.arange(k // 32), indexing="ij")
+    return q, fs[frag_sf_offset(r, b, k)]
+
+
+def quantize_frag(x_bits: np.ndarray):
+    """bf16 X [M, K] (K % 256 == 0) -> flat fragment-layout (elements, scales)."""
+    q, s = quantize(x_bits)
+    return to_frag(q, s, x_bits.shape[1])
+
+
+def mm_mxfp8_frag(a_fq, a_fs, b_fq, b_fs, m: int, n: int, k: int) -> np.ndarray:
+    """C[m, n] = sum_k A[m, k] B[n, k] in fp64 for fragment-layout operands."""
+    aq, asf = from_frag(a_fq, a_fs, m, k)
+    bq, bsf = from_frag(b_fq, b_fs, n, k)
+    return mm_mxfp8(aq, asf, bq, bsf, m, n, k)

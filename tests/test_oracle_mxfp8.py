@@ -78,3 +78,50 @@ def test_mm_mxfp8_brute_force_and_torch():
 def test_zero_group():
     q, s = X.quantize(np.zeros((1, 64), dtype=np.uint16))
     assert np.all(q == 0) and np.all(s == 0)
+
+
+# ------------------------------------------------------------------------ fragment layout
+def test_frag_offsets_hand_worked():
+    from tests.conftest import golden_lines
+    n = 0
+    for line in golden_lines("frag_offsets_mxfp8.txt"):
+        r, c, k, off = (int(v) for v in line.split()[:4])
+        assert int(X.frag_offset(r, c, k)) == off, line
+        n += 1
+    assert n == 11
+
+
+def test_frag_layout_is_a_permutation_and_matches_the_lane_placement():
+    """Offsets form a permutation; an independent construction by axis permutation: a fragment is
+    [block b][lane half h][row i][16 bytes] of one 32-row tile and 64-K step."""
+    from oracle import mxfp4 as X4
+    for rows, k in [(33, 256), (70, 768)]:
+        rp = X4.frag_rows(rows)
+        r, c = np.meshgrid(np.arange(rp), np.arange(k), indexing="ij")
+        assert np.array_equal(np.sort(X.frag_offset(r, c, k).ravel()), np.arange(rp * k))
+        rng = np.random.default_rng(rows)
+        q = rng.integers(0, 256, size=(rows, k)).astype(np.uint8)
+        s = rng.integers(0, 256, size=(rows, k // 32)).astype(np.uint8)
+        fq, fs = X.to_frag(q, s, k)
+        qp = np.zeros((rp, k), dtype=np.uint8)
+        qp[:rows] = q
+        # [tile, i, step, block, h, byte] -> [tile, step, block, h, i, byte]
+        want = qp.reshape(rp // 32, 32, k // 64, 2, 2, 16).transpose(0, 2, 3, 4, 1, 5).ravel()
+        assert np.array_equal(fq, want)
+        sp = np.zeros((rp, k // 32), dtype=np.uint8)
+        sp[:rows] = s
+        assert np.array_equal(fs, X4.to_frag(np.zeros((rows, k // 2), np.uint8), s, k)[1])
+        assert np.array_equal(fs, sp.reshape(rp // 32, 32, k // 256, 4, 2).transpose(0, 2, 4, 1, 3).ravel())
+        bq, bs = X.from_frag(fq, fs, rows, k)
+        assert np.array_equal(bq, q) and np.array_equal(bs, s)
+
+
+def test_frag_quantize_and_gemm_agree_with_the_row_major_layout():
+    xa = W.small_case(45, 512, 21, outlier_frac=0.02)
+    xb = W.small_case(37, 512, 22, outlier_frac=0.02)
+    fa, fsa = X.quantize_frag(xa)
+    fb, fsb = X.quantize_frag(xb)
+    qa, sa = X.quantize(xa)
+    qb, sb = X.quantize(xb)
+    assert np.array_equal(X.from_frag(fa, fsa, 45, 512)[0], qa)
+    assert np.array_equal(X.mm_mxfp8_frag(fa, fsa, fb, fsb, 45, 37, 512), X.mm_mxfp8(qa, sa, qb, sb, 45, 37, 512))
