@@ -316,6 +316,7 @@ def main():
         m1.record(stream)
         pw4, sw4 = bsp.bsp_mxfp4_quantize(w5)     # and to MXFP4 for the mm_fp4 MX variant
         pw4f, sw4f = bsp.bsp_mxfp4_quantize_frag(w5)   # (MFMA fragment layout)
+        qwf, swf = bsp.bsp_mxfp8_quantize_frag(w5)
         qx = torch.empty((M, K1), dtype=torch.uint8, device=dev)
         sxm = torch.empty((M, K1 // 32), dtype=torch.uint8, device=dev)
         out5 = torch.empty((M, N1), dtype=torch.bfloat16, device=dev)
@@ -350,6 +351,39 @@ def main():
             "weight_conversion_ms": round(m0.elapsed_time(m1), 4)}
         log(json.dumps(result["mxfp8"]))
         del qx, sxm
+
+        # ---- the same MXFP8 layer with both operands in the MFMA fragment layout
+        qxf, sxf = bsp.bsp_mxfp8_quantize_frag(x5)
+
+        def step8f(e=None):
+            if e:
+                e[0].record(stream)
+            bsp.bsp_mxfp8_quantize_frag(x5, qxf, sxf)
+            if e:
+                e[1].record(stream)
+            bsp.bsp_mm_mxfp8_frag(qxf, sxf, qwf, swf, M, N1, out=out5)
+            if e:
+                e[2].record(stream)
+
+        for _ in range(args.warmup):
+            step8f()
+        torch.cuda.synchronize()
+        e8f = [[ev() for _ in range(3)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            step8f(e8f[i])
+        torch.cuda.synchronize()
+        q8f = sum(e[0].elapsed_time(e[1]) for e in e8f) / args.steps
+        g8f = sum(e[1].elapsed_time(e[2]) for e in e8f) / args.steps
+        tf8f = 2.0 * M * N1 * K1 / g8f / 1e9
+        qb8f = 2 * M * K1 + (-(-M // 32) * 32) * (K1 + K1 // 32)
+        result["mxfp8_frag"] = {
+            "mm_mxfp8_frag_ms": round(g8f, 4), "TFLOPS": round(tf8f, 2),
+            "frac_fp8_peak": round(tf8f / PEAK_FP8_TFLOPS, 4),
+            "quantize_frag_ms": round(q8f, 4), "quantize_GBs": round(qb8f / q8f / 1e6, 1),
+            "quantize_frac_hbm": round(qb8f / q8f / 1e6 / PEAK_HBM_GBS, 4),
+            "step_ms": round(q8f + g8f, 4), "step_ms_row_major_layout": round(q8 + g8, 4)}
+        log(json.dumps(result["mxfp8_frag"]))
+        del qxf, sxf, qwf, swf
 
         # ---- MXFP4 (mm_fp4 with MX scales, the format gfx950's FP4 MFMA takes natively)
         px4 = torch.empty((M, K1 // 2), dtype=torch.uint8, device=dev)
@@ -471,6 +505,9 @@ def main():
             kernels_frac["mm_mxfp8_of_fp8_mfma_loop"] = result["mxfp8"]["TFLOPS"] / mp["mfma_fp8_scaled_TFLOPS"]
         if "mxfp4" in result:
             kernels_frac["mm_mxfp4_of_fp4_mfma_loop"] = result["mxfp4"]["TFLOPS"] / mp["mfma_fp4_scaled_TFLOPS"]
+        if "mxfp8_frag" in result:
+            kernels_frac["mm_mxfp8_frag_of_fp8_mfma_loop"] = (result["mxfp8_frag"]["TFLOPS"]
+                                                              / mp["mfma_fp8_scaled_TFLOPS"])
         if "mxfp4_frag" in result:
             kernels_frac["mm_mxfp4_frag_of_fp4_mfma_loop"] = (result["mxfp4_frag"]["TFLOPS"]
                                                               / mp["mfma_fp4_scaled_TFLOPS"])

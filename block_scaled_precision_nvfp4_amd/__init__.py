@@ -56,6 +56,9 @@ SIGNATURES = {
     "bsp_mxfp4_frag_bytes": ([_i64, _i64, ctypes.POINTER(_i64), ctypes.POINTER(_i64)], _int),
     "bsp_mxfp4_quantize_frag": ([_p, _i64, _i64, _i64, _p, _p, _p], _int),
     "bsp_mm_mxfp4_frag": ([_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _int, _p], _int),
+    "bsp_mxfp8_frag_bytes": ([_i64, _i64, ctypes.POINTER(_i64), ctypes.POINTER(_i64)], _int),
+    "bsp_mxfp8_quantize_frag": ([_p, _i64, _i64, _i64, _p, _p, _p], _int),
+    "bsp_mm_mxfp8_frag": ([_p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _int, _p], _int),
 }
 
 
@@ -589,6 +592,73 @@ def bsp_mm_mxfp4_frag(a: torch.Tensor, a_sf: torch.Tensor, b: torch.Tensor, b_sf
         _bias_vector(bias, n, torch.bfloat16, dev)
     _call("bsp_mm_mxfp4_frag", a.data_ptr(), a_sf.data_ptr(), b.data_ptr(), b_sf.data_ptr(),
           _ptr(alpha), _ptr(bias), m, n, k, out.data_ptr(), out.stride(0), code, _stream(dev))
+    return out
+
+
+# ----------------------------------------------------------------- MXFP8, MFMA fragment layout
+def bsp_mxfp8_frag_bytes(rows: int, k: int) -> Tuple[int, int]:
+    """(element bytes, scale bytes) of a [rows, K] operand in the fragment layout (K % 256 == 0)."""
+    qb, sb = ctypes.c_int64(0), ctypes.c_int64(0)
+    _call("bsp_mxfp8_frag_bytes", rows, k, ctypes.byref(qb), ctypes.byref(sb))
+    return qb.value, sb.value
+
+
+def bsp_mxfp8_quantize_frag(x: torch.Tensor, q: Optional[torch.Tensor] = None,
+                            sf: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """MXFP8 of x [M, K] in the fragment layout: (q uint8 [ceil(M/32), K/64, 2048] -- one 2 KB MFMA
+    fragment per 32-row tile and 64-K step --, sf uint8 [ceil(M/32), K/256, 256])."""
+    x = _as_bf16_2d(x, "x")
+    m, k = x.shape
+    qbytes, sbytes = bsp_mxfp8_frag_bytes(m, k)
+    rt = -(-m // 32)
+    if q is None:
+        q = torch.empty((rt, k // 64, 2048), dtype=torch.uint8, device=x.device)
+    if sf is None:
+        sf = torch.empty((rt, k // 256, 256), dtype=torch.uint8, device=x.device)
+    _need(q, "q", torch.uint8, x.device)
+    _need(sf, "sf", torch.uint8, x.device)
+    if q.numel() < qbytes or not q.is_contiguous():
+        raise ValueError("q must be contiguous with bsp_mxfp8_frag_bytes(M, K)[0] bytes")
+    if sf.numel() < sbytes or not sf.is_contiguous():
+        raise ValueError("sf must be contiguous with bsp_mxfp8_frag_bytes(M, K)[1] bytes")
+    _call("bsp_mxfp8_quantize_frag", x.data_ptr(), m, k, x.stride(0), q.data_ptr(), sf.data_ptr(),
+          _stream(x.device))
+    return q, sf
+
+
+def bsp_mm_mxfp8_frag(a: torch.Tensor, a_sf: torch.Tensor, b: torch.Tensor, b_sf: torch.Tensor,
+                      m: int, n: int, bias: Optional[torch.Tensor] = None,
+                      out_dtype: torch.dtype = torch.bfloat16,
+                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C [m, n] = A . B^T (+ fp32 bias) for fragment-layout operands A [m, K] and B [n, K] (as
+    written by bsp_mxfp8_quantize_frag); bit-identical to bsp_mm_mxfp8 on the same values."""
+    _need(a, "a", torch.uint8)
+    dev = a.device
+    for t, nm in ((a_sf, "a_sf"), (b, "b"), (b_sf, "b_sf")):
+        _need(t, nm, torch.uint8, dev)
+    if a.dim() != 3 or b.dim() != 3 or a.shape[1:] != b.shape[1:] or a.shape[2] != 2048:
+        raise ValueError(f"a {tuple(a.shape)} and b {tuple(b.shape)} must be fragment tensors "
+                         "[ceil(rows/32), K/64, 2048] with the same K")
+    k = a.shape[1] * 64
+    if not (-(-m // 32) == a.shape[0] and -(-n // 32) == b.shape[0]):
+        raise ValueError(f"m={m}, n={n} do not match the fragment tensors' row tiles "
+                         f"({a.shape[0]}, {b.shape[0]})")
+    if not all(t.is_contiguous() for t in (a, a_sf, b, b_sf)):
+        raise ValueError("operands and scales must be contiguous")
+    if a_sf.numel() < bsp_mxfp8_frag_bytes(m, k)[1] or b_sf.numel() < bsp_mxfp8_frag_bytes(n, k)[1]:
+        raise ValueError("scale buffers are smaller than bsp_mxfp8_frag_bytes")
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"out_dtype must be bf16 or fp32, got {out_dtype}")
+    code = BSP_OUT_BF16 if out_dtype == torch.bfloat16 else BSP_OUT_F32
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=dev)
+    _need(out, "out", out_dtype, dev)
+    if out.dim() != 2 or out.shape[0] != m or out.shape[1] != n or out.stride(1) != 1:
+        raise ValueError(f"out must be [{m}, {n}] with unit column stride")
+    if bias is not None:
+        _bias_vector(bias, n, torch.float32, dev)
+    _call("bsp_mm_mxfp8_frag", a.data_ptr(), a_sf.data_ptr(), b.data_ptr(), b_sf.data_ptr(),
+          _ptr(bias), m, n, k, out.data_ptr(), out.stride(0), code, _stream(dev))
     return out
 
 

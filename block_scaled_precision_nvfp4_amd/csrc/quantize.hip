@@ -495,11 +495,21 @@ __global__ __launch_bounds__(256) void rmsnorm_token_kernel(
 // rounds to nearest even with the sign of zero kept (its only difference from the software
 // encoder on gfx950 is that it does not saturate, hence the clamp); BSP_QUANT_SW_CVT=1 selects
 // the software encoder.
-template <bool HWCVT, bool VEC>
+//
+// FRAG: both outputs in the MFMA fragment layout (K % 256 == 0; described at
+// bsp_mxfp8_quantize_frag). The workgroup's 64 rows x 256 K are 2 row tiles x 4 K steps, eight 2 KB
+// fragments and two 256-byte scale groups, staged in LDS and stored as two contiguous 8 KB runs
+// and two 256-byte runs. A thread's 8 output bytes for row rr and K offset 8 (t % 32) within the
+// 256 are half (t & 1) of 16-byte chunk p = (rr/32)*512 + g*32 + rr%32 of the staging area, with
+// g = (t % 32) / 2 = 4 * K step + 2 * block + lane half; it is placed at chunk p ^ 2g, as the
+// sixteen g of a row otherwise sit 512 bytes apart, in one set of LDS banks.
+template <bool HWCVT, bool VEC, bool FRAG = false>
 __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const uint16_t* __restrict__ x,
                                                              int64_t M, int64_t K, int64_t ld,
                                                              uint8_t* __restrict__ q,
                                                              uint8_t* __restrict__ sf) {
+  __shared__ uint4 frag_tile[FRAG ? 1024 : 1];  // FRAG: the workgroup's 16 KB of fragments
+  __shared__ uint4 sf_stage[FRAG ? 32 : 1];     // FRAG: its two 256-byte scale groups
   const int t = threadIdx.x;
   const int64_t row0 = (int64_t)blockIdx.y * 64;
   const int64_t kk = (int64_t)blockIdx.x * 256 + (t & 31) * 8;
@@ -544,11 +554,40 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const uint16_t* __r
 #pragma unroll
       for (int i = 0; i < 4; ++i) hi |= e4m3_encode(f[4 + i] * inv) << (8 * i);
     }
-    if (full || (kin && row0 + s * 8 + rsub < M)) {
+    if constexpr (FRAG) {
+      const int rr = s * 8 + rsub, g = (t & 31) >> 1;
+      const int p = (rr >> 5) * 512 + g * 32 + (rr & 31);
+      uint32_t* d = reinterpret_cast<uint32_t*>(frag_tile) + (p ^ (g << 1)) * 4 + (t & 1) * 2;
+      d[0] = lo;
+      d[1] = hi;
+      if ((t & 3) == 0) {  // block cb = (t % 32) / 4 of the 256 K: K step cb / 2, lane half cb % 2
+        const int cb = (t & 31) >> 2;
+        reinterpret_cast<uint8_t*>(sf_stage)[(rr >> 5) * 256 + ((cb & 1) * 32 + (rr & 31)) * 4 + (cb >> 1)] =
+            (uint8_t)byte;
+      }
+    } else if (full || (kin && row0 + s * 8 + rsub < M)) {
       typedef uint32_t u32x2_nt __attribute__((ext_vector_type(2)));
       __builtin_nontemporal_store((u32x2_nt){lo, hi}, reinterpret_cast<u32x2_nt*>(qp + s * 8 * K));
       if ((t & 3) == 0) sp[s * 8 * ng] = (uint8_t)byte;
     }
+  }
+  if constexpr (FRAG) {
+    __syncthreads();
+    // row tiles past ceil(M / 32) are not part of the buffers; padded rows inside the last one
+    // were encoded from zeros (code 0, scale 0x00)
+    const int64_t row_tiles = (M + 31) / 32, rt0 = (int64_t)blockIdx.y * 2;
+    const int64_t ks_steps = K / 64, k_groups = K / 256;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int p = it * 256 + t;
+      if (rt0 + (p >> 9) < row_tiles) {
+        const uint4 v = frag_tile[p ^ (((p >> 5) & 15) << 1)];
+        __builtin_nontemporal_store((nt_u32x4){v.x, v.y, v.z, v.w},
+                                    reinterpret_cast<nt_u32x4*>(q + ((rt0 + (p >> 9)) * ks_steps + blockIdx.x * 4) * 2048) + (p & 511));
+      }
+    }
+    if (t < 32 && rt0 + (t >> 4) < row_tiles)
+      reinterpret_cast<uint4*>(sf + ((rt0 + (t >> 4)) * k_groups + blockIdx.x) * 256)[t & 15] = sf_stage[t];
   }
 }
 
@@ -997,6 +1036,44 @@ extern "C" int bsp_mxfp8_quantize(const void* x, int64_t M, int64_t K, int64_t l
   else
     hipLaunchKernelGGL((mxfp8_quantize_kernel<false, false>), grid, dim3(256), 0, s, xp, M, K, ld, q, sf);
   return check_launch("bsp_mxfp8_quantize");
+}
+
+extern "C" int bsp_mxfp8_frag_bytes(int64_t rows, int64_t K, int64_t* q_bytes, int64_t* sf_bytes) {
+  BSP_REQUIRE(q_bytes && sf_bytes, BSP_EINVAL, "bsp_mxfp8_frag_bytes: null output pointer");
+  BSP_REQUIRE(rows >= 0 && K >= 0, BSP_EINVAL, "bsp_mxfp8_frag_bytes: negative size");
+  BSP_REQUIRE(K % 256 == 0, BSP_ESHAPE, "bsp_mxfp8_frag_bytes: K (%lld) must be a multiple of 256",
+              (long long)K);
+  *q_bytes = ceil_div(rows, 32) * 32 * K;
+  *sf_bytes = ceil_div(rows, 32) * 32 * (K / 32);
+  return BSP_OK;
+}
+
+extern "C" int bsp_mxfp8_quantize_frag(const void* x, int64_t M, int64_t K, int64_t ld, uint8_t* q,
+                                       uint8_t* sf, void* stream) {
+  const char* fn = "bsp_mxfp8_quantize_frag";
+  BSP_REQUIRE(M >= 0 && K > 0, BSP_EINVAL, "%s: bad size M=%lld K=%lld", fn, (long long)M, (long long)K);
+  BSP_REQUIRE(K % 256 == 0, BSP_ESHAPE, "%s: K (%lld) must be a multiple of 256", fn, (long long)K);
+  BSP_REQUIRE(M <= 1 || ld >= K, BSP_ESHAPE, "%s: ld (%lld) < K (%lld)", fn, (long long)ld, (long long)K);
+  if (M == 0) return BSP_OK;
+  BSP_REQUIRE(x && q && sf, BSP_EINVAL, "%s: null pointer", fn);
+  BSP_REQUIRE(((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(sf)) & 15u) == 0,
+              BSP_EINVAL, "%s: q and sf must be 16-byte aligned", fn);
+  BSP_REQUIRE(ceil_div(M, 64) < 65536, BSP_ESHAPE, "%s: M too large", fn);
+  if (int e = check_device()) return e;
+  dim3 grid((unsigned)(K / 256), (unsigned)ceil_div(M, 64));
+  const uint16_t* xp = static_cast<const uint16_t*>(x);
+  const bool vec = (ld % 8 == 0) && aligned16(x);
+  const bool hw = hw_cvt_enabled();
+  hipStream_t s = (hipStream_t)stream;
+  if (hw && vec)
+    hipLaunchKernelGGL((mxfp8_quantize_kernel<true, true, true>), grid, dim3(256), 0, s, xp, M, K, ld, q, sf);
+  else if (hw)
+    hipLaunchKernelGGL((mxfp8_quantize_kernel<true, false, true>), grid, dim3(256), 0, s, xp, M, K, ld, q, sf);
+  else if (vec)
+    hipLaunchKernelGGL((mxfp8_quantize_kernel<false, true, true>), grid, dim3(256), 0, s, xp, M, K, ld, q, sf);
+  else
+    hipLaunchKernelGGL((mxfp8_quantize_kernel<false, false, true>), grid, dim3(256), 0, s, xp, M, K, ld, q, sf);
+  return check_launch(fn);
 }
 
 extern "C" int bsp_gelu_tanh_bf16(const void* x, void* y, int64_t n, void* stream) {

@@ -310,6 +310,33 @@ int bsp_mm_mxfp4_frag(const uint8_t* a_packed, const uint8_t* a_sf, const uint8_
                       const uint8_t* b_sf, const float* alpha_dev, const void* bias_bf16, int64_t M,
                       int64_t N, int64_t K, void* out, int64_t ldc, int out_dtype, void* stream);
 
+/* MXFP8 in the MFMA fragment layout: the arrangement above for e4m3 operands. Operand [R, K],
+ * K % 256 == 0, Rp = ceil(R/32)*32 rows (rows R..Rp-1 zero):
+ *  q (Rp*K bytes): the 2 KB fragment of row tile rt and K step ks at (rt*(K/64) + ks)*2048 is two
+ *    1 KB halves b = 0, 1 (the step's two 32-element blocks); byte 16 l + c of half b, lane
+ *    l = i + 32 h, is element 64 ks + 32 b + 16 h + c of row 32 rt + i (so a lane's bytes 0-15 and
+ *    16-31 of the 32x32x64 MFMA operand are one 16-byte read from each half);
+ *  scales (Rp*K/32 bytes): exactly as the MXFP4 fragment layout.
+ * Same element and scale values as bsp_mxfp8_quantize; sizes: bsp_mxfp8_frag_bytes (BSP_ESHAPE
+ * unless K % 256 == 0). */
+int bsp_mxfp8_frag_bytes(int64_t rows, int64_t K, int64_t* q_bytes, int64_t* sf_bytes);
+
+/* bsp_mxfp8_quantize writing the fragment layout. x: device bf16 [M, K] (row stride ld),
+ * K % 256 == 0 (else BSP_ESHAPE) -> q and sf as above (bsp_mxfp8_frag_bytes(M, K) bytes each), both
+ * 16-byte aligned (else BSP_EINVAL); every byte of both, padding rows included, is written.
+ * M == 0 is a no-op. */
+int bsp_mxfp8_quantize_frag(const void* x_bf16, int64_t M, int64_t K, int64_t ld, uint8_t* q,
+                            uint8_t* sf, void* stream);
+
+/* bsp_mm_mxfp8 on fragment-layout operands (+ optional fp32 bias [N] added before the one rounding,
+ * as bsp_mm_mxfp8_bias; NULL for none). a: A [M, K], b: B [N, K] (K-major weight), each with its
+ * scales; out [M, N] row stride ldc, bf16 or fp32. For the same operand values the output is
+ * bit-identical to bsp_mm_mxfp8's (and bsp_mm_mxfp8_bias's). Requires K % 256 == 0 (else
+ * BSP_ESHAPE); fragments 16-byte, scales and bias 4-byte aligned (else BSP_EINVAL). */
+int bsp_mm_mxfp8_frag(const uint8_t* a, const uint8_t* a_sf, const uint8_t* b, const uint8_t* b_sf,
+                      const float* bias_f32, int64_t M, int64_t N, int64_t K, void* out,
+                      int64_t ldc, int out_dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -286,3 +286,30 @@ def test_mxfp4_frag_entry_points():
     # the aligned call passes validation and fails only for want of a gfx950 device here
     st = _st(g, P, ctypes.c_void_p(20), P, P, None, ctypes.c_void_p(18), 4, 4, 256, P, 4, 0, None)[0]
     assert st not in (-1, -2, -3), st
+
+
+def test_mxfp8_frag_entry_points():
+    qb, sb = ctypes.c_int64(0), ctypes.c_int64(0)
+    assert bsp.lib().bsp_mxfp8_frag_bytes(33, 512, ctypes.byref(qb), ctypes.byref(sb)) == 0
+    assert (qb.value, sb.value) == (64 * 512, 64 * 16)
+    assert bsp.lib().bsp_mxfp8_frag_bytes(4, 128, ctypes.byref(qb), ctypes.byref(sb)) == -2
+    assert bsp.bsp_mxfp8_frag_bytes(300, 1280) == (320 * 1280, 320 * 40)
+    q = "bsp_mxfp8_quantize_frag"
+    st, msg = _st(q, P, 4, 384, 384, P, P, None)
+    assert st == -2 and "multiple of 256" in msg
+    assert _st(q, P, 4, 256, 128, P, P, None)[0] == -2
+    assert _st(q, P, 4, 256, 256, ctypes.c_void_p(24), P, None)[0] == -1
+    assert _st(q, P, 4, 256, 256, P, ctypes.c_void_p(20), None)[0] == -1
+    assert _st(q, P, 65535 * 64 + 1, 256, 256, P, P, None)[0] == -2
+    assert _st(q, None, 0, 256, 256, None, None, None)[0] == 0
+    g = "bsp_mm_mxfp8_frag"
+    st, msg = _st(g, P, P, P, P, None, 4, 4, 640, P, 4, 0, None)
+    assert st == -2 and "multiple of 256" in msg
+    assert _st(g, P, P, P, P, None, 4, 4, 256, P, 4, 3, None)[0] == -3
+    assert _st(g, P, P, P, P, None, 4, 8, 256, P, 4, 0, None)[0] == -2
+    assert _st(g, ctypes.c_void_p(24), P, P, P, None, 4, 4, 256, P, 4, 0, None)[0] == -1
+    assert _st(g, P, ctypes.c_void_p(18), P, P, None, 4, 4, 256, P, 4, 0, None)[0] == -1
+    assert _st(g, P, P, P, P, ctypes.c_void_p(18), 4, 4, 256, P, 4, 0, None)[0] == -1   # bias
+    assert _st(g, None, None, None, None, None, 4, 0, 256, None, 4, 0, None)[0] == 0
+    st = _st(g, P, ctypes.c_void_p(20), P, P, ctypes.c_void_p(20), 4, 4, 256, P, 4, 0, None)[0]
+    assert st not in (-1, -2, -3), st

@@ -1,10 +1,12 @@
-"""GPU parity of the MXFP4 fragment-layout path (bsp_mxfp4_quantize_frag, bsp_mm_mxfp4_frag).
+"""GPU parity of the MX fragment-layout paths (bsp_mxfp4_quantize_frag / bsp_mm_mxfp4_frag and
+bsp_mxfp8_quantize_frag / bsp_mm_mxfp8_frag).
 
-The quantizer must write exactly the oracle's bytes (codes, scales and zero padding rows) in the
-fragment layout; the GEMM must meet the same bar as mm_mxfp4 against the oracle's fp64 product of
-the same operand bytes, and, for the same operand values, equal mm_mxfp4's output bit for bit (same
-MFMA, same K order), with and without bias. Small and ragged shapes compare every element; the
-Wan-14B fc_in shape (32760 x 13824 x 5120) runs at full size and compares sampled entries.
+The quantizers must write exactly the oracle's bytes (codes, scales and zero padding rows) in the
+fragment layout; each GEMM must meet the same bar as its linear-layout counterpart (mm_mxfp4,
+mm_mxfp8) against the oracle's fp64 product of the same operand bytes, and, for the same operand
+values, equal that counterpart's output bit for bit (same MFMA, same K order), with and without
+bias. Small and ragged shapes compare every element; the Wan-14B fc_in shape
+(32760 x 13824 x 5120) runs at full size and compares sampled entries.
 """
 import numpy as np
 import pytest
@@ -14,6 +16,7 @@ import block_scaled_precision_nvfp4_amd as bsp
 import workloads as W
 from oracle import linear as L
 from oracle import mxfp4 as X4
+from oracle import mxfp8 as X
 from oracle import nvfp4 as N
 from tests.gpu_util import (assert_gemm_bf16, check_gemm_outputs, dev_bf16, dev_u8, host_u8,
                             sample_entries, say, scalar, tensor_bits)
@@ -160,3 +163,126 @@ def test_mm_mxfp4_frag_full_size():
     lx, lsx = bsp.bsp_mxfp4_quantize(dev_bf16(xb))
     lw, lsw = bsp.bsp_mxfp4_quantize(dev_bf16(wb))
     assert torch.equal(c.view(torch.int16), bsp.bsp_mm_mxfp4(lx, lsx, lw, lsw).view(torch.int16))
+
+
+# ------------------------------------------------------------------------------------------ MXFP8
+
+def _quant8_frag_filled(xb: np.ndarray):
+    m, k = xb.shape
+    rt = X4.frag_rows(m) // 32
+    q = torch.full((rt, k // 64, 2048), 0xA5, dtype=torch.uint8, device="cuda")
+    s = torch.full((rt, k // 256, 256), 0xA5, dtype=torch.uint8, device="cuda")
+    bsp.bsp_mxfp8_quantize_frag(dev_bf16(xb), q, s)
+    return host_u8(q).ravel(), host_u8(s).ravel()
+
+
+@pytest.mark.parametrize("m,k", [(1, 256), (33, 512), (64, 256), (130, 768), (300, 1280),
+                                 (257, 2048)])
+def test_mxfp8_quantize_frag_bit_exact(m, k):
+    say("mxfp8_quantize_frag", m, k)
+    for xb in (W.small_case(m, k, seed=5 * m + k, outlier_frac=0.02),
+               W.special_values_block(seed=m + 3, rows=m, cols=k),
+               W.nonfinite_block(seed=m + 4, rows=m, cols=k)):
+        fq, fs = _quant8_frag_filled(xb)
+        rq, rs = X.quantize_frag(xb)
+        assert np.array_equal(fq, rq) and np.array_equal(fs, rs)
+
+
+def test_mxfp8_quantize_frag_strided_input():
+    xb = W.small_case(70, 1024, seed=6, outlier_frac=0.02)
+    q, s = bsp.bsp_mxfp8_quantize_frag(dev_bf16(xb)[:, :512])
+    rq, rs = X.quantize_frag(np.ascontiguousarray(xb[:, :512]))
+    assert np.array_equal(host_u8(q).ravel(), rq) and np.array_equal(host_u8(s).ravel(), rs)
+
+
+def test_mxfp8_quantize_frag_full_size():
+    """Wan-14B fc_in activation 32760 x 5120: whole row tiles against the oracle of those rows;
+    every byte against the row-major quantizer's output rearranged on the device."""
+    xb = tensor_bits(5, "X")
+    m, k = xb.shape
+    q, s = bsp.bsp_mxfp8_quantize_frag(dev_bf16(xb))
+    rt = X4.frag_rows(m) // 32
+    for t in (0, 311, rt - 1):
+        rq, rs = X.quantize_frag(xb[32 * t: min(32 * t + 32, m)])
+        assert np.array_equal(host_u8(q[t]).ravel(), rq), t
+        assert np.array_equal(host_u8(s[t]).ravel(), rs), t
+    ql, sl = bsp.bsp_mxfp8_quantize(dev_bf16(xb))
+    mp = rt * 32
+    qp = torch.zeros((mp, k), dtype=torch.uint8, device="cuda")
+    qp[:m] = ql
+    sp = torch.zeros((mp, k // 32), dtype=torch.uint8, device="cuda")
+    sp[:m] = sl
+    want_q = qp.view(rt, 32, k // 64, 2, 2, 16).permute(0, 2, 3, 4, 1, 5).contiguous().view(-1)
+    want_s = sp.view(rt, 32, k // 256, 4, 2).permute(0, 2, 4, 1, 3).contiguous().view(-1)
+    assert torch.equal(q.view(-1), want_q) and torch.equal(s.view(-1), want_s)
+
+
+def _rand_operand8(rng, rows, k):
+    """Random e4m3 bytes (no NaN codes) and scales: (fragment flat pair, row-major pair)."""
+    q = rng.integers(0, 256, size=(rows, k)).astype(np.uint8)
+    q[(q & 0x7F) == 0x7F] = 0x3F
+    s = rng.integers(110, 140, size=(rows, k // 32)).astype(np.uint8)
+    return X.to_frag(q, s, k), (q, s)
+
+
+def _frag8_dev(fq, fs, rows, k):
+    rt = X4.frag_rows(rows) // 32
+    return dev_u8(fq.reshape(rt, k // 64, 2048)), dev_u8(fs.reshape(rt, k // 256, 256))
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 64, 256), (77, 200, 256), (256, 256, 512), (300, 130, 768),
+                                   (513, 384, 1280), (3, 1, 256), (260, 520, 3328)])
+def test_mm_mxfp8_frag_random_operands_all_elements(m, n, k):
+    say("mm_mxfp8_frag random", m, n, k)
+    rng = np.random.default_rng(m * 11 + n + k)
+    (fa, fsa), (qa, sa) = _rand_operand8(rng, m, k)
+    (fb, fsb), (qb, sb) = _rand_operand8(rng, n, k)
+    ref = X.mm_mxfp8_frag(fa, fsa, fb, fsb, m, n, k)
+    a, a_s = _frag8_dev(fa, fsa, m, k)
+    b, b_s = _frag8_dev(fb, fsb, n, k)
+    t32 = bsp.bsp_mm_mxfp8_frag(a, a_s, b, b_s, m, n, out_dtype=torch.float32)
+    t16 = bsp.bsp_mm_mxfp8_frag(a, a_s, b, b_s, m, n)
+    check_gemm_outputs(t16, t32, ref, f"mxfp8 frag {m}x{n}x{k}")
+    std = (dev_u8(qa), dev_u8(sa), dev_u8(qb), dev_u8(sb))
+    assert torch.equal(t32, bsp.bsp_mm_mxfp8(*std, out_dtype=torch.float32))
+    assert torch.equal(t16.view(torch.int16), bsp.bsp_mm_mxfp8(*std).view(torch.int16))
+
+
+@pytest.mark.parametrize("m,n,k", [(77, 200, 256), (256, 256, 512)])
+def test_mm_mxfp8_frag_bias(m, n, k):
+    say("mm_mxfp8_frag bias", m, n, k)
+    rng = np.random.default_rng(m + 5 * n + k)
+    (fa, fsa), (qa, sa) = _rand_operand8(rng, m, k)
+    (fb, fsb), (qb, sb) = _rand_operand8(rng, n, k)
+    ref = X.mm_mxfp8_frag(fa, fsa, fb, fsb, m, n, k)
+    bf = rng.normal(0.0, float(np.std(ref)) + 1e-30, size=n).astype(np.float32)
+    bias = torch.from_numpy(bf).cuda()
+    a, a_s = _frag8_dev(fa, fsa, m, k)
+    b, b_s = _frag8_dev(fb, fsb, n, k)
+    tb32 = bsp.bsp_mm_mxfp8_frag(a, a_s, b, b_s, m, n, bias, out_dtype=torch.float32)
+    tb16 = bsp.bsp_mm_mxfp8_frag(a, a_s, b, b_s, m, n, bias)
+    std = (dev_u8(qa), dev_u8(sa), dev_u8(qb), dev_u8(sb))
+    assert torch.equal(tb32, bsp.bsp_mm_mxfp8_bias(*std, bias, out_dtype=torch.float32))
+    assert torch.equal(tb16.view(torch.int16), bsp.bsp_mm_mxfp8_bias(*std, bias).view(torch.int16))
+    check_gemm_outputs(tb16, tb32, L.gemm_plus_bias(ref, bf), f"mxfp8 frag bias {m}x{n}x{k}")
+
+
+def test_mm_mxfp8_frag_full_size():
+    """Wan-14B fc_in, 32760 x 13824 x 5120, operands from bsp_mxfp8_quantize_frag: sampled entries
+    against the oracle, and the whole output equal to mm_mxfp8's on the row-major operands."""
+    xb, wb = tensor_bits(5, "X"), tensor_bits(5, "W")
+    m, n, k = xb.shape[0], wb.shape[0], xb.shape[1]
+    qx, sx = bsp.bsp_mxfp8_quantize_frag(dev_bf16(xb))
+    qw, sw = bsp.bsp_mxfp8_quantize_frag(dev_bf16(wb))
+    c = bsp.bsp_mm_mxfp8_frag(qx, sx, qw, sw, m, n)
+    c32 = bsp.bsp_mm_mxfp8_frag(qx, sx, qw, sw, m, n, out_dtype=torch.float32)
+    rows, cols = sample_entries(m, n, 3000, 47)
+    ur, ri = np.unique(rows, return_inverse=True)
+    uc, ci = np.unique(cols, return_inverse=True)
+    rq, rs = X.quantize(xb[ur])
+    rqw, rsw = X.quantize(wb[uc])
+    ref = X.mm_mxfp8_entries(rq, rs, rqw, rsw, ri, ci)
+    check_gemm_outputs(c, c32, ref, "fc_in mxfp8 frag", rows, cols)
+    lx, lsx = bsp.bsp_mxfp8_quantize(dev_bf16(xb))
+    lw, lsw = bsp.bsp_mxfp8_quantize(dev_bf16(wb))
+    assert torch.equal(c.view(torch.int16), bsp.bsp_mm_mxfp8(lx, lsx, lw, lsw).view(torch.int16))
