@@ -145,22 +145,25 @@ __device__ __forceinline__ float gelu_tanh(float x) {
 }
 
 // GELU of bf16 values by table. A bf16 input has 2^16 values, so gelu rounded to bf16 is a
-// function of 16 bits; a workgroup tabulates it in LDS (with gelu_tanh itself, so the table holds
-// exactly what the arithmetic gives) for |x| in [2^-12, 2^6) -- 18 binades x 128 mantissas x 2
-// signs, 9 KB -- which holds nearly all activations of a linear layer. Lookups replace a dozen
-// VALU instructions and two quarter-rate transcendentals per value with about six instructions
-// and an LDS read; values outside the table (zeros, tiny or huge magnitudes, inf, NaN) take
-// gelu_tanh itself.
+// function of 16 bits. The table (gelu_table.inc, written by gen_gelu_table.py in exact arithmetic)
+// holds the correctly rounded bf16 of gelu(x) for |x| in [2^-12, 2^6) -- 18 binades x 128 mantissas
+// x 2 signs, 9 KB -- which holds nearly all activations of a linear layer; a workgroup copies it into
+// LDS with a few 16-byte loads. Lookups replace a dozen VALU instructions and two quarter-rate
+// transcendentals per value with about six instructions and an LDS read; values outside the table
+// (zeros, tiny or huge magnitudes, inf, NaN) take gelu_tanh above, whose bf16 rounding is within
+// one ulp of the correctly rounded value.
 constexpr int kGeluTabE0 = 115;                    // bf16 exponent field of 2^-12
 constexpr int kGeluTabHalf = 18 * 128;             // entries per sign
 constexpr int kGeluTabSize = 2 * kGeluTabHalf;     // uint16 entries
 
-__device__ __forceinline__ void gelu_table_fill(uint16_t* tab, int t, int nt) {
-  for (int i = t; i < kGeluTabSize; i += nt) {
-    const uint32_t s = i >= kGeluTabHalf ? 1u : 0u;
-    const uint32_t b = (s << 15) + (kGeluTabE0 << 7) + (uint32_t)i - s * kGeluTabHalf;
-    tab[i] = (uint16_t)bf16x2_rne(gelu_tanh(__uint_as_float(b << 16)), 0.0f);
-  }
+#include "gelu_table.inc"
+
+// tab: LDS, kGeluTabSize entries, 16-byte aligned; threads t = 0 .. nt-1 of the workgroup copy it
+// (the caller synchronises before the first lookup)
+__device__ __forceinline__ void gelu_table_load(uint16_t* tab, int t, int nt) {
+  const uint4* src = reinterpret_cast<const uint4*>(kGeluTable);
+  uint4* dst = reinterpret_cast<uint4*>(tab);
+  for (int i = t; i < kGeluTabSize / 8; i += nt) dst[i] = src[i];
 }
 
 typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
@@ -227,7 +230,7 @@ __device__ __forceinline__ uint32_t gelu2_tab(uint32_t w, const uint16_t* tab, u
   return (uint32_t)tab[idx & 0xFFFFu] | ((uint32_t)tab[idx >> 16] << 16);
 }
 
-// gelu of 8 bf16 values, rounded to bf16, by the arithmetic (what the table holds)
+// gelu of 8 bf16 values, rounded to bf16, by the arithmetic (for inputs outside the table)
 __device__ __forceinline__ uint4 gelu8_bf16_arith(const uint4& v) {
   return make_uint4(bf16x2_rne(gelu_tanh(bf16_lo(v.x)), gelu_tanh(bf16_hi(v.x))),
                     bf16x2_rne(gelu_tanh(bf16_lo(v.y)), gelu_tanh(bf16_hi(v.y))),
@@ -236,7 +239,7 @@ __device__ __forceinline__ uint4 gelu8_bf16_arith(const uint4& v) {
 }
 
 // gelu (bf16 in, bf16 out) of NSEG segments of 8 values: all by table first, then one branch,
-// rarely taken, that recomputes the segments holding a value outside the table. Keeping the
+// rarely taken, that computes the segments holding a value outside the table arithmetically. Keeping the
 // common path free of branches lets the LDS latencies of all segments overlap. FINITE: the
 // recomputed segments also get nan_to_num (for an encoder's input: the table holds only finite
 // values, and gelu of a finite bf16 is finite, so only inputs outside the table can give an

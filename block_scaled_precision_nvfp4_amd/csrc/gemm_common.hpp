@@ -319,7 +319,7 @@ __device__ __forceinline__ void store_tile_gelu_nvfp4(const f32x16 (&acc)[4][4],
                                                       int li, int h) {
   const float g = *gsf;
   if (t < 128) rtab[t] = (t == 0 || t > 0x7E) ? 0.0f : g / e4m3_decode_pos((uint32_t)t);
-  gelu_table_fill(gtab, t, 256);
+  gelu_table_load(gtab, t, 256);
   __syncthreads();   // the tables; every wave is done reading the stage buffers the images overlay
   store_wave_tile_gelu_nvfp4(acc, alpha, m0 + wm * 128, n0 + wn * 128, M, N, packed, sf, g, rtab,
                              gtab, lds + wave * kEpiWaveBytes, lds + 4 * kEpiWaveBytes + wave * 1024,

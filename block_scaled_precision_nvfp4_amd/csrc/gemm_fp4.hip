@@ -263,7 +263,7 @@ __global__ __launch_bounds__(256, 1) void mm_fp4_kernel(
     uint8_t* __restrict__ sf_out, const float* __restrict__ out_gsf) {
   __shared__ Stage st[NSTAGE];
   __shared__ float rtab[BIAS == kGeluNvfp4 ? 128 : 1];
-  __shared__ uint16_t gtab[BIAS == kGeluNvfp4 ? kGeluTabSize : 1];
+  __shared__ __attribute__((aligned(16))) uint16_t gtab[BIAS == kGeluNvfp4 ? kGeluTabSize : 8];
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int wm = wave >> 1, wn = wave & 1;

@@ -159,7 +159,7 @@ __global__ __launch_bounds__(256) void nvfp4_quantize_kernel(const uint16_t* __r
                                                              int64_t rows8) {
   __shared__ uint4 sf_tile[128];  // 2 KB = 4 scale tiles of 512 B
   __shared__ float rtab[128];     // fl32(g / e4m3(c)) for code c (0 for c == 0)
-  __shared__ uint16_t gtab[GELU ? kGeluTabSize : 1];
+  __shared__ __attribute__((aligned(16))) uint16_t gtab[GELU ? kGeluTabSize : 8];
   uint8_t* sfb = reinterpret_cast<uint8_t*>(sf_tile);
   const int t = threadIdx.x;
   const int64_t row0 = (int64_t)blockIdx.y * 128;
@@ -181,7 +181,7 @@ __global__ __launch_bounds__(256) void nvfp4_quantize_kernel(const uint16_t* __r
     for (int s = 0; s < 16; ++s)
       v[s] = (kin && row0 + s * 8 + rsub < M) ? load8<VEC>(xp + s * xstep) : make_uint4(0u, 0u, 0u, 0u);
   }
-  if (GELU) gelu_table_fill(gtab, t, 256);   // while the loads are in flight
+  if (GELU) gelu_table_load(gtab, t, 256);   // while the loads are in flight
   __syncthreads();  // rtab, gtab
   if (!GELU) nan_to_num_segments(v);   // the GELU path substitutes in its table-miss branch
 
@@ -699,8 +699,8 @@ __global__ __launch_bounds__(256) void mxfp4_quantize_kernel(const uint16_t* __r
 // =============================================================================================
 // Grid-stride over 8-value segments, GELU by the workgroup's LDS table (gelu_segments_tab).
 __global__ __launch_bounds__(256) void gelu_kernel(const uint16_t* x, uint16_t* y, int64_t n) {
-  __shared__ uint16_t gtab[kGeluTabSize];
-  gelu_table_fill(gtab, threadIdx.x, 256);
+  __shared__ __attribute__((aligned(16))) uint16_t gtab[kGeluTabSize];
+  gelu_table_load(gtab, threadIdx.x, 256);
   __syncthreads();
   const int64_t n8 = n / 8;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8;

@@ -153,8 +153,10 @@ int bsp_mm_mxfp4(const uint8_t* a_packed, const uint8_t* a_sf, const uint8_t* b_
 
 /* GELU (tanh form) on bf16, out of place or in place: y = bf16(gelu(x)) with
  * gelu(x) = 0.5*x*(1 + tanh(z)), z = sqrt(2/pi)*(x + 0.044715*x^3), evaluated in fp32 through the
- * logistic form with t = exp(-2|z|) (no cancellation, no overflow); within one bf16 ulp of exact
- * (the fp32 evaluation uses the hardware exp2 and reciprocal, a few fp32 ulps).
+ * logistic form with t = exp(-2|z|) (no cancellation, no overflow). For |x| in [2^-12, 2^6) the
+ * result is the correctly rounded bf16 of gelu(x) (a lookup table computed in exact arithmetic);
+ * other inputs take the fp32 evaluation (hardware exp2 and reciprocal, a few fp32 ulps), within
+ * one bf16 ulp of exact.
  * It is the activation between fc_in and fc_out of the Wan FFN, both of which are in the NVFP4
  * layer set of [FV-QAT] (DEFAULT_FP4_LAYERS: ffn.fc_in, ffn.fc_out).
  * x, y: device bf16 [n], contiguous, 16-byte aligned. */

@@ -181,13 +181,25 @@ def oracle_linear_entries(xb: np.ndarray, wb: np.ndarray, rows: np.ndarray, cols
     return N.mm_fp4_entries(px, sx, pw, sw, N.alpha(x_gsf, rg), len(ur), len(uc), xb.shape[1], ri, ci)
 
 
+# The kernels' GELU table covers the bf16 inputs with |x| in [2^-12, 2^6) (magnitude bits in
+# [115 << 7, 133 << 7)) and holds the correctly rounded bf16 of gelu there; other inputs take an fp32
+# evaluation accurate to a few fp32 ulps.
+GELU_TABLE_MAG = (115 << 7, 133 << 7)
+
+
+def gelu_in_table(y_bits: np.ndarray) -> np.ndarray:
+    mag = np.asarray(y_bits, dtype=np.uint16) & 0x7FFF
+    return (mag >= GELU_TABLE_MAG[0]) & (mag < GELU_TABLE_MAG[1])
+
+
 def gelu_rounding_ambiguous(y_bits: np.ndarray, eps: float = 2.0 ** -20) -> np.ndarray:
-    """bf16 inputs whose fp64 GELU lies within eps (relative; about 8 fp32 ulps) of a bf16 rounding
-    boundary, so that a GELU accurate to a few fp32 ulps may round it either way (about one input
-    in 2^11)."""
+    """bf16 inputs outside the GELU table whose fp64 GELU lies within eps (relative; about 8 fp32
+    ulps) of a bf16 rounding boundary, so that the fp32 evaluation may round it either way. Inputs
+    in the table are correctly rounded, never ambiguous."""
     y = (np.asarray(y_bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
     g = A.gelu_tanh(y.astype(np.float64))
-    return A.f64_to_bf16_bits(g * (1 - eps)) != A.f64_to_bf16_bits(g * (1 + eps))
+    near = A.f64_to_bf16_bits(g * (1 - eps)) != A.f64_to_bf16_bits(g * (1 + eps))
+    return near & ~gelu_in_table(y_bits)
 
 
 def e2m1_rank(codes: np.ndarray) -> np.ndarray:
@@ -224,10 +236,10 @@ def assert_nvfp4_of_gelu(got_packed: np.ndarray, got_sf_lin: np.ndarray, y_bits:
                          what: str = "", max_ambiguous: float = 0.03):
     """The GPU's NVFP4 encoding of gelu(y) (packed [M, K/2], scales unswizzled to [M, K/16])
     against the oracle's own chain on the same bf16 y: fp64 GELU rounded once to bf16, then the
-    NVFP4 quantize. The GPU's GELU (hardware exp2 and reciprocal) is within a few fp32 ulps, so
-    every 16-element block without a rounding-ambiguous value must be bit-exact (the others within
-    one step, assert_nvfp4_blocks). For smooth data about 16 / 2^11 of the blocks are ambiguous;
-    inputs built from rounding ties and tiny values may set max_ambiguous higher."""
+    NVFP4 quantize. The GPU's GELU is correctly rounded inside its table and within a few fp32 ulps
+    outside it, so every 16-element block without a rounding-ambiguous value (gelu_rounding_ambiguous)
+    must be bit-exact (the others within one step, assert_nvfp4_blocks). Smooth data has almost no
+    ambiguous blocks; inputs built from rounding ties and tiny values may set max_ambiguous higher."""
     y_bits = np.asarray(y_bits, dtype=np.uint16)
     m, k = y_bits.shape
     rp, rs = N.quantize(A.gelu_tanh_bf16_bits(y_bits), np.float32(gsf), layout="linear")
