@@ -280,6 +280,39 @@ def main():
         "event_ms_spread": spread,
     }
 
+    # ---- the same FFN step with fc_in's epilogue emitting the NVFP4 of gelu(C) directly
+    # (bsp_mm_fp4_gelu_nvfp4: no bf16 H in memory, no separate GELU + quantize launch)
+    def step_epi(events=None):
+        if events:
+            events[0].record(stream)
+        bsp.bsp_nvfp4_quantize(x, one, px, sx)
+        if events:
+            events[1].record(stream)
+        bsp.bsp_mm_fp4_gelu_nvfp4(px, sx, pw1, sw1, a1, one, ph, sh)
+        if events:
+            events[2].record(stream)
+        bsp.bsp_mm_fp4(ph, sh, pw2, sw2, a2, out=out)
+        if events:
+            events[3].record(stream)
+
+    for _ in range(args.warmup):
+        step_epi()
+    torch.cuda.synchronize()
+    eve = [[ev() for _ in range(4)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step_epi(eve[i])
+    torch.cuda.synchronize()
+    wall_e = time.perf_counter() - t0
+    fcin_epi = sum(e[1].elapsed_time(e[2]) for e in eve) / args.steps
+    result["ffn_step_gelu_nvfp4_epilogue"] = {
+        "ms_per_step": round(wall_e * 1e3 / args.steps, 4),
+        "TFLOPS": round(gemm_flops / (wall_e / args.steps) / 1e12, 2),
+        "mm_fp4_gelu_nvfp4_fc_in_ms": round(fcin_epi, 4),
+        "two_kernel_fc_in_plus_gelu_quantize_ms": round(kms["mm_fp4_fc_in"] + kms["gelu_quantize_h"], 4),
+        "two_kernel_ms_per_step": round(ms_per_step, 4)}
+    log(json.dumps(result["ffn_step_gelu_nvfp4_epilogue"]))
+
     # ---- per-token activation scales at the fc_in shape: quantize X per row + mm_fp4 with row alphas
     gx = torch.empty((M,), dtype=torch.float32, device=dev)
     for _ in range(max(1, args.warmup)):
