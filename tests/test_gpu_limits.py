@@ -3,8 +3,8 @@
 Quantizers at their largest row count (the grid's tile-row limit: ceil(M/128) < 65536, MXFP8
 ceil(M/64) < 65536) with sampled rows, the first and last rows and every padding scale byte
 checked; the GEMMs at K = 2^24 (mm_fp4's limit: per-tile 32-bit load offsets) on every element;
-a GEMM with 8.4 million rows (int64 row offsets, 32768 tiles) on sampled rows. One size past each
-limit is rejected on the host (tests/test_abi.py).
+GEMMs with 8.4 million rows (int64 row offsets, 32768 tiles) on sampled rows, for mm_fp4 and for the
+fragment-layout MX GEMMs. One size past each limit is rejected on the host (tests/test_abi.py).
 """
 import numpy as np
 import pytest
@@ -136,6 +136,87 @@ def test_mm_fp4_tall_max_rows():
     rows = _rows(m, 5)
     got = c[torch.from_numpy(rows).cuda()].float().cpu().numpy().astype(np.float64)
     ref = N.dequant_rows(pa, sa, rows, m, k) @ N.dequant_rows(pb, sb, np.arange(n), n, k).T
+    err = np.abs(got - ref)
+    assert np.all(err <= 8e-3 * np.max(np.abs(ref))), float(err.max())
+    assert np.linalg.norm(got - ref) <= 3e-3 * np.linalg.norm(ref)
+
+
+# --------------------------------------------------------------- MX GEMMs, fragment layout
+def _frag_operand(rng, rows, k, fmt):
+    """Random fragment-layout bytes (no NaN codes, scales 2^-17 .. 2^12), padding rows included."""
+    rp = -(-rows // 32) * 32
+    nbytes = rp * k // 2 if fmt == "mxfp4" else rp * k
+    q = rng.integers(0, 256, size=nbytes, dtype=np.uint8)
+    if fmt == "mxfp8":
+        q[(q & 0x7F) == 0x7F] = 0x3F
+    s = rng.integers(110, 140, size=rp * k // 32, dtype=np.uint8)
+    return q, s
+
+
+def _frag_dev(q, s, rows, k, fmt):
+    rt = -(-rows // 32)
+    frag = 1024 if fmt == "mxfp4" else 2048
+    return dev_u8(q.reshape(rt, k // 64, frag)), dev_u8(s.reshape(rt, k // 256, 256))
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8"])
+def test_frag_gemm_at_k_2_24(fmt):
+    """Fragment-layout GEMMs at K = 2^24 (262144 K steps per tile) with ragged M, N: every element
+    against the oracle."""
+    m, n, k = 3, 5, 1 << 24
+    say("frag K = 2^24", fmt, m, n, k)
+    rng = np.random.default_rng(124)
+    qa, sa = _frag_operand(rng, m, k, fmt)
+    qb, sb = _frag_operand(rng, n, k, fmt)
+    a, a_s = _frag_dev(qa, sa, m, k, fmt)
+    b, b_s = _frag_dev(qb, sb, n, k, fmt)
+    if fmt == "mxfp4":
+        c = bsp.bsp_mm_mxfp4_frag(a, a_s, b, b_s, m, n, scalar(0.5), out_dtype=torch.float32)
+        ref = X4.mm_mxfp4_frag(qa, sa, qb, sb, np.float32(0.5), m, n, k)
+    else:
+        c = bsp.bsp_mm_mxfp8_frag(a, a_s, b, b_s, m, n, out_dtype=torch.float32)
+        ref = X.mm_mxfp8_frag(qa, sa, qb, sb, m, n, k)
+    assert_gemm_f32(c.cpu().numpy().astype(np.float64), ref, f"frag K=2^24 {fmt}")
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8"])
+def test_frag_gemm_tall_max_rows(fmt):
+    """M = 8388480 (262140 row tiles; operand and C offsets past 2^31 bytes), N = 136, K = 256:
+    sampled rows of C, gathered from the fragment layout on the device, against the oracle."""
+    m, n, k = M_MAX_128, 136, 256
+    say("tall frag", fmt, m, n, k)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    rt = -(-m // 32)
+    frag = 1024 if fmt == "mxfp4" else 2048
+    a = torch.randint(0, 256, (rt, k // 64, frag), dtype=torch.uint8, device="cuda", generator=g)
+    if fmt == "mxfp8":
+        a[(a & 0x7F) == 0x7F] = 0x3F
+    a_s = torch.randint(115, 135, (rt, k // 256, 256), dtype=torch.uint8, device="cuda", generator=g)
+    rng = np.random.default_rng(8)
+    qb, sb = _frag_operand(rng, n, k, fmt)
+    b, b_s = _frag_dev(qb, sb, n, k, fmt)
+    if fmt == "mxfp4":
+        c = bsp.bsp_mm_mxfp4_frag(a, a_s, b, b_s, m, n)
+    else:
+        c = bsp.bsp_mm_mxfp8_frag(a, a_s, b, b_s, m, n)
+    rows = _rows(m, 9)
+    # the sampled rows' bytes, read through the layout's own offsets
+    if fmt == "mxfp4":
+        off = X4.frag_packed_offset(rows[:, None], np.arange(k // 2)[None, :], k)
+    else:
+        off = X.frag_offset(rows[:, None], np.arange(k)[None, :], k)
+    soff = X4.frag_sf_offset(rows[:, None], np.arange(k // 32)[None, :], k)
+    ra = a.view(-1)[torch.from_numpy(off.ravel()).cuda()].cpu().numpy().reshape(off.shape)
+    rs = a_s.view(-1)[torch.from_numpy(soff.ravel()).cuda()].cpu().numpy().reshape(soff.shape)
+    if fmt == "mxfp4":
+        A = X4.dequant_linear(ra, rs)
+        B = X4.dequant_linear(*X4.from_frag(qb, sb, n, k))
+    else:
+        A = X.dequant_rows(ra, rs, np.arange(len(rows)))
+        B = X.dequant_rows(*X.from_frag(qb, sb, n, k), np.arange(n))
+    ref = A @ B.T
+    got = c[torch.from_numpy(rows).cuda()].float().cpu().numpy().astype(np.float64)
     err = np.abs(got - ref)
     assert np.all(err <= 8e-3 * np.max(np.abs(ref))), float(err.max())
     assert np.linalg.norm(got - ref) <= 3e-3 * np.linalg.norm(ref)
