@@ -77,6 +77,41 @@ def test_mxfp8_quantize_at_max_rows():
     assert np.array_equal(host_u8(q[ri]), rq) and np.array_equal(host_u8(s[ri]), rs)
 
 
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8"])
+def test_frag_quantizers_at_max_rows(fmt):
+    """The fragment-layout quantizers at their largest row count minus a ragged few (seeded device
+    input, K = 256): sampled rows and every padding row of the last row tile, read through the
+    layout's offsets, against the oracle."""
+    m = (M_MAX_128 if fmt == "mxfp4" else M_MAX_64) - 7
+    k = 256
+    say("max rows frag quantize", fmt, m, k)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(31)
+    x = (torch.randn((m, k), device="cuda", generator=g) * 2.0).bfloat16()
+    if fmt == "mxfp4":
+        q, s = bsp.bsp_mxfp4_quantize_frag(x)
+    else:
+        q, s = bsp.bsp_mxfp8_quantize_frag(x)
+    rows = _rows(m, 6)
+    xb = x[torch.from_numpy(rows).cuda()].view(torch.int16).cpu().numpy().view(np.uint16)
+    rp = -(-m // 32) * 32
+    pad = np.arange(m, rp)
+    if fmt == "mxfp4":
+        ref_q, ref_s = X4.quantize(xb, layout="linear")
+        off = lambda r: X4.frag_packed_offset(r[:, None], np.arange(k // 2)[None, :], k)  # noqa: E731
+    else:
+        ref_q, ref_s = X.quantize(xb)
+        off = lambda r: X.frag_offset(r[:, None], np.arange(k)[None, :], k)  # noqa: E731
+    soff = lambda r: X4.frag_sf_offset(r[:, None], np.arange(k // 32)[None, :], k)  # noqa: E731
+
+    def gather(t, o):
+        return t.view(-1)[torch.from_numpy(o.ravel()).cuda()].cpu().numpy().reshape(o.shape)
+
+    assert np.array_equal(gather(q, off(rows)), ref_q)
+    assert np.array_equal(gather(s, soff(rows)), ref_s)
+    assert pad.size == 7 and not gather(q, off(pad)).any() and not gather(s, soff(pad)).any()
+
+
 def _nvfp4_operand(rng, rows, k):
     packed = rng.integers(0, 256, size=(rows, k // 2), dtype=np.uint8)
     rp, cp = N.sf_padded_shape(rows, k)
