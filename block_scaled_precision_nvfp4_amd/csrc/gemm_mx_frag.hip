@@ -341,6 +341,9 @@ extern "C" int bsp_mm_mxfp4_frag(const uint8_t* a, const uint8_t* a_sf, const ui
   BSP_REQUIRE(out_dtype == BSP_OUT_BF16 || out_dtype == BSP_OUT_F32, BSP_EDTYPE,
               "%s: out_dtype must be BSP_OUT_BF16 (0) or BSP_OUT_F32 (1), got %d", fn, out_dtype);
   BSP_REQUIRE(K % 256 == 0, BSP_ESHAPE, "%s: K (%lld) must be a multiple of 256", fn, (long long)K);
+  // a row tile's fragments are one buffer resource whose size (32 K bytes at most) is a signed
+  // 32-bit field
+  BSP_REQUIRE(K <= (1ll << 24), BSP_ESHAPE, "%s: K (%lld) must be at most 2^24", fn, (long long)K);
   BSP_REQUIRE(M <= 1 || ldc >= N, BSP_ESHAPE, "%s: ldc (%lld) < N (%lld)", fn, (long long)ldc, (long long)N);
   if (M == 0 || N == 0) return BSP_OK;
   BSP_REQUIRE(a && a_sf && b && b_sf && out, BSP_EINVAL, "%s: null pointer", fn);
@@ -367,6 +370,9 @@ extern "C" int bsp_mm_mxfp8_frag(const uint8_t* a, const uint8_t* a_sf, const ui
   BSP_REQUIRE(out_dtype == BSP_OUT_BF16 || out_dtype == BSP_OUT_F32, BSP_EDTYPE,
               "%s: out_dtype must be BSP_OUT_BF16 (0) or BSP_OUT_F32 (1), got %d", fn, out_dtype);
   BSP_REQUIRE(K % 256 == 0, BSP_ESHAPE, "%s: K (%lld) must be a multiple of 256", fn, (long long)K);
+  // a row tile's fragments are one buffer resource whose size (32 K bytes at most) is a signed
+  // 32-bit field
+  BSP_REQUIRE(K <= (1ll << 24), BSP_ESHAPE, "%s: K (%lld) must be at most 2^24", fn, (long long)K);
   BSP_REQUIRE(M <= 1 || ldc >= N, BSP_ESHAPE, "%s: ldc (%lld) < N (%lld)", fn, (long long)ldc, (long long)N);
   if (M == 0 || N == 0) return BSP_OK;
   BSP_REQUIRE(a && a_sf && b && b_sf && out, BSP_EINVAL, "%s: null pointer", fn);

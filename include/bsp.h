@@ -306,8 +306,8 @@ int bsp_mxfp4_quantize_frag(const void* x_bf16, int64_t M, int64_t K, int64_t ld
  * (alpha = 1), bias_bf16 a device bf16 [N] or NULL (added as in bsp_mm_mxfp4_bias). a: A [M, K] and
  * b: B [N, K] (K-major weight) in the fragment layout, each with its scales; out [M, N] row stride
  * ldc, bf16 or fp32. For the same operand values the output is bit-identical to bsp_mm_mxfp4's (and
- * bsp_mm_mxfp4_bias's). Requires K % 256 == 0 (else BSP_ESHAPE); fragments 16-byte and scales
- * 4-byte aligned, bias 2-byte aligned (else BSP_EINVAL). */
+ * bsp_mm_mxfp4_bias's). Requires K % 256 == 0 and K <= 2^24 (else BSP_ESHAPE); fragments 16-byte
+ * and scales 4-byte aligned, bias 2-byte aligned (else BSP_EINVAL). */
 int bsp_mm_mxfp4_frag(const uint8_t* a_packed, const uint8_t* a_sf, const uint8_t* b_packed,
                       const uint8_t* b_sf, const float* alpha_dev, const void* bias_bf16, int64_t M,
                       int64_t N, int64_t K, void* out, int64_t ldc, int out_dtype, void* stream);
@@ -333,8 +333,9 @@ int bsp_mxfp8_quantize_frag(const void* x_bf16, int64_t M, int64_t K, int64_t ld
 /* bsp_mm_mxfp8 on fragment-layout operands (+ optional fp32 bias [N] added before the one rounding,
  * as bsp_mm_mxfp8_bias; NULL for none). a: A [M, K], b: B [N, K] (K-major weight), each with its
  * scales; out [M, N] row stride ldc, bf16 or fp32. For the same operand values the output is
- * bit-identical to bsp_mm_mxfp8's (and bsp_mm_mxfp8_bias's). Requires K % 256 == 0 (else
- * BSP_ESHAPE); fragments 16-byte, scales and bias 4-byte aligned (else BSP_EINVAL). */
+ * bit-identical to bsp_mm_mxfp8's (and bsp_mm_mxfp8_bias's). Requires K % 256 == 0 and
+ * K <= 2^24 (else BSP_ESHAPE); fragments 16-byte, scales and bias 4-byte aligned (else
+ * BSP_EINVAL). */
 int bsp_mm_mxfp8_frag(const uint8_t* a, const uint8_t* a_sf, const uint8_t* b, const uint8_t* b_sf,
                       const float* bias_f32, int64_t M, int64_t N, int64_t K, void* out,
                       int64_t ldc, int out_dtype, void* stream);

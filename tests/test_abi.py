@@ -286,6 +286,8 @@ def test_mxfp4_frag_entry_points():
     # the aligned call passes validation and fails only for want of a gfx950 device here
     st = _st(g, P, ctypes.c_void_p(20), P, P, None, ctypes.c_void_p(18), 4, 4, 256, P, 4, 0, None)[0]
     assert st not in (-1, -2, -3), st
+    st, msg = _st(g, P, P, P, P, None, None, 4, 4, (1 << 24) + 256, P, 4, 0, None)
+    assert st == -2 and "at most" in msg
 
 
 def test_mxfp8_frag_entry_points():
@@ -313,3 +315,5 @@ def test_mxfp8_frag_entry_points():
     assert _st(g, None, None, None, None, None, 4, 0, 256, None, 4, 0, None)[0] == 0
     st = _st(g, P, ctypes.c_void_p(20), P, P, ctypes.c_void_p(20), 4, 4, 256, P, 4, 0, None)[0]
     assert st not in (-1, -2, -3), st
+    st, msg = _st(g, P, P, P, P, None, 4, 4, (1 << 24) + 256, P, 4, 0, None)
+    assert st == -2 and "at most" in msg
