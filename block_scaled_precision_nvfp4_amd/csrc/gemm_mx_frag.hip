@@ -19,10 +19,12 @@
 //          selected by op_sel for K step 4 kg + j.
 // Rows past R (to the next multiple of 32) are zero.
 //
+// (MXFP8's fragments are 2 KB, described at its kernel below; its scales are laid out as MXFP4's.)
+//
 // Every wave loads the fragments of its four A and four B row tiles straight into registers, each
-// a fully coalesced 1 KB read, three K steps ahead into a ring of four register buffers; no LDS and
-// no workgroup barrier in the K loop (the two waves that share a row tile read it from the caches
-// independently). Against the LDS-staged kernel this drops the LDS writes and reads and the
+// a fully coalesced 1 KB read, three K steps ahead into a ring of four register buffers (MXFP8: two
+// steps ahead into a ring of three); no LDS and no workgroup barrier in the K loop (the two waves
+// that share a row tile read it from the caches independently). Against the LDS-staged kernel this drops the LDS writes and reads and the
 // per-stage barriers, at twice the L2 reads. Tiling and epilogue as the LDS-staged MX kernel:
 // 256x256 C tile per 256-thread workgroup, 128x128 per wave, XCD-aware tile order, whole tiles
 // leave through LDS as whole rows.
@@ -48,6 +50,8 @@ __device__ __forceinline__ void pin_step(f32x16 (&acc)[4][4]) {
 // Operand and scale reads are raw buffer loads: one resource (base, size) per row tile held in
 // scalar registers, the K step's byte offset in a scalar register and the lane's offset in one
 // vector register, instead of a 64-bit vector address per load.
+// The resource's last word, 0x00020000, is the plain raw-buffer format of this GPU family (32-bit
+// data format, no swizzle); the stride is 0, so the byte offsets are used as given.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 __device__ __forceinline__ rsrc_t make_rsrc(const uint8_t* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, (int)bytes, 0x00020000);
