@@ -657,14 +657,15 @@ def measure_ceilings() -> dict:
     wgs = 1024
     sink = torch.empty(wgs * 256, dtype=torch.float32, device=dev)
     res = {}
-    for fmt, name, iters, flops in ((0, "mfma_f16_nvfp4_operands_TFLOPS", 20000, 32768.0),
-                                    (1, "mfma_fp8_scaled_TFLOPS", 10000, 131072.0),
-                                    (2, "mfma_fp4_scaled_TFLOPS", 20000, 131072.0)):
+    for fmt, name, iters, flops in ((0, "mfma_f16_nvfp4_operands_TFLOPS", 10000, 32768.0),
+                                    (1, "mfma_fp8_scaled_TFLOPS", 5000, 131072.0),
+                                    (2, "mfma_fp4_scaled_TFLOPS", 10000, 131072.0),
+                                    (3, "mfma_fp8_scaled_16x16x128_TFLOPS", 10000, 65536.0)):
         def run(fmt=fmt, iters=iters):
             if lib.bsp_probe_mfma_loop(fmt, wgs, iters, ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(st)) != 0:
                 raise RuntimeError("bsp_probe_mfma_loop failed")
         ms = _event_ms([run], 3)
-        res[name] = round(wgs * 4 * iters * 4 * flops / ms / 1e9, 1)
+        res[name] = round(wgs * 4 * iters * 8 * flops / ms / 1e9, 1)
     nb = 1 << 31
     src = torch.ones(nb // 4, dtype=torch.int32, device=dev)
     dst = torch.empty(nb // 4, dtype=torch.int32, device=dev)
@@ -677,8 +678,9 @@ def measure_ceilings() -> dict:
         ms = _event_ms([run], 5)
         res[name] = round((nread + nwrite) / ms / 1e6, 1)
     del src, dst
-    res["note"] = ("MFMA-only loops: 1024 workgroups x 4 waves, four independent accumulator chains per "
-                   "wave; streams: 2 GiB read, nontemporal, 16 loads in flight per thread, 2048 workgroups")
+    res["note"] = ("MFMA-only loops: 1024 workgroups x 4 waves, eight independent accumulator chains per "
+                   "wave (one wave per SIMD, as in the GEMMs); streams: 2 GiB read, nontemporal, 16 loads "
+                   "in flight per thread, 2048 workgroups")
     return res
 
 

@@ -32,6 +32,21 @@ int check_device() {
   return BSP_OK;
 }
 
+int device_cu_count() {
+  static std::mutex mu;
+  static std::vector<int> cus;  // per device: 0 unknown
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)cus.size() <= dev) cus.resize(dev + 1, 0);
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 }  // namespace bsp
 
 extern "C" const char* bsp_last_error(void) { return bsp::last_error_slot().c_str(); }

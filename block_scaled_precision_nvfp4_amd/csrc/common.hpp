@@ -34,6 +34,8 @@ inline int ok() { return BSP_OK; }
 
 // Verifies that the current device is gfx950 (cached per device).
 int check_device();
+// Compute units of the current device (cached per device; 256 on MI355X); 0 if unknown.
+int device_cu_count();
 
 inline int check_launch(const char* what) {
   hipError_t e = hipGetLastError();

@@ -33,6 +33,25 @@ __device__ __forceinline__ void tile_coords(int bid, int ntm, int ntn, int& tm, 
   tn = in / gm;
 }
 
+// Raw buffer loads for operands read straight into registers: one resource (base, size) per row
+// tile held in scalar registers, the K step's byte offset in a scalar register and the lane's
+// offset in one vector register, instead of a 64-bit vector address per load. The resource's last
+// word, 0x00020000, is the plain raw-buffer format of this GPU family (32-bit data format, no
+// swizzle); the stride is 0, so the byte offsets are used as given.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const uint8_t* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 ld16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+}
+__device__ __forceinline__ uint32_t ld4(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
+}
+__device__ __forceinline__ uint32_t ld2(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0);
+}
+
 // Bias of the linear layer, added in the epilogue:
 //  kBiasNone;
 //  kBiasBf16After: a bf16 [N] vector added to the bf16-rounded product, the sum rounded to bf16
@@ -218,6 +237,56 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], const floa
     store_wave_tile<OUT_F32, BIAS, ACC16>(acc, alpha, m0 + wm * 128, n0 + wn * 128, M, N, out, ldc,
                                    vec_store, li, h, bias);
   }
+}
+
+// Deferred epilogue of the persistent kernels. A wave's finished bf16 128x128 tile that lies wholly
+// inside C (rows 16-byte aligned) is written as a row-major image into the wave's own LDS area
+// (kImgWaveBytes; rows kImgRowBytes apart, as in the staged epilogue) and leaves later as
+// kImgStores row-segment stores, each four whole 256-byte rows, issued one at a time between the
+// MFMAs of the next tile's first K steps. The stores of all the workgroups then do not leave in
+// one burst at the end of each round of tiles, and a K step's loads queue behind at most one of
+// them (vector memory completes loads and stores in issue order). Only the wave that wrote an
+// image reads it, so no workgroup barrier is needed: LDS executes one wave's operations in order.
+constexpr int kImgRowBytes = kEpiRowBytes;
+
+// x, hidden from the optimizer: values computed from it are computed where it is used.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+constexpr int kImgWaveBytes = 128 * kImgRowBytes;
+constexpr int kImgStores = 32;
+
+template <int BIAS, bool ACC16>
+__device__ __forceinline__ void img_write(const f32x16 (&acc)[4][4], const float (&alpha)[4],
+                                          int64_t n0w, int64_t N, uint8_t* img, int li, int h,
+                                          const void* bias = nullptr) {
+  float bq[4][4][4];
+  load_bias<BIAS>(bq, n0w, N, h, bias);
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        uint32_t p01, p23;
+        piece_bf16<BIAS, ACC16>(acc, alpha, bq, m, n, b, p01, p23);
+        *reinterpret_cast<uint2*>(img + (m * 32 + li) * kImgRowBytes + (n * 32 + 8 * b + 4 * h) * 2) =
+            make_uint2(p01, p23);
+      }
+}
+
+// Row-segment load s (0 .. kImgStores-1) of a wave's image: rows 4s .. 4s+3, 16 bytes per lane.
+__device__ __forceinline__ u32x4 img_load(const uint8_t* img, int s, int lane) {
+  return *reinterpret_cast<const u32x4*>(img + (4 * s + (lane >> 4)) * kImgRowBytes + (lane & 15) * 16);
+}
+// ... and its store to C, `base` pointing at the wave tile's first element. The pointer is
+// marked global: a store through a generic pointer might write LDS, and the compiler would then
+// drain every outstanding load before the next LDS read.
+typedef __attribute__((address_space(1))) u32x4 global_u32x4;
+__device__ __forceinline__ void img_put(const u32x4& v, int s, uint16_t* base, int64_t ldc, int lane) {
+  uint16_t* o = base + (int64_t)(4 * s + (lane >> 4)) * ldc + (lane & 15) * 8;
+  __builtin_nontemporal_store(v, (global_u32x4*)(o));
 }
 
 // GELU + NVFP4 epilogue: instead of C, the NVFP4 encoding of gelu(C) (the input of the next

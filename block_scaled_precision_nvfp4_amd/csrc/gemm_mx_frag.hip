@@ -28,6 +28,8 @@
 // per-stage barriers, at twice the L2 reads. Tiling and epilogue as the LDS-staged MX kernel:
 // 256x256 C tile per 256-thread workgroup, 128x128 per wave, XCD-aware tile order, whole tiles
 // leave through LDS as whole rows.
+#include <stdlib.h>
+
 #include "gemm_common.hpp"
 
 namespace bsp {
@@ -47,34 +49,23 @@ __device__ __forceinline__ void pin_step(f32x16 (&acc)[4][4]) {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Operand and scale reads are raw buffer loads: one resource (base, size) per row tile held in
-// scalar registers, the K step's byte offset in a scalar register and the lane's offset in one
-// vector register, instead of a 64-bit vector address per load.
-// The resource's last word, 0x00020000, is the plain raw-buffer format of this GPU family (32-bit
-// data format, no swizzle); the stride is 0, so the byte offsets are used as given.
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-__device__ __forceinline__ rsrc_t make_rsrc(const uint8_t* base, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ u32x4 ld16(rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
-}
-__device__ __forceinline__ uint32_t ld4(rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
-}
-
 __device__ __forceinline__ i32x8 fp4_op(const u32x4& x) {
   return i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};  // e2m1: four registers are read
 }
 
 // One K step (J = ks % 4) of a wave: its 16 MFMAs on ring buffer J, the loads of step kl (three
 // ahead) into buffer (J + 3) % 4, whose step was consumed by the previous call, spread between them.
-template <int J>
+// ST: deferred store s of the previous tile's image rides along (its LDS read before the MFMAs,
+// its global store after the step's loads).
+template <int J, bool ST>
 __device__ __forceinline__ void frag_step(f32x16 (&acc)[4][4], u32x4 (&xa)[4][4], u32x4 (&xb)[4][4],
                                           const uint32_t (&csa)[4], const uint32_t (&csb)[4],
                                           const rsrc_t (&fa)[4], const rsrc_t (&fb)[4], uint32_t kl,
-                                          uint32_t loff) {
+                                          uint32_t loff, const uint8_t* img, int s, uint16_t* pbase,
+                                          int64_t ldc, int lane) {
   constexpr int NB = (J + 3) & 3;
+  u32x4 dv;
+  if (ST) dv = img_load(img, s, lane);
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
     const int n = q >> 1, m = 2 * (q & 1);
@@ -87,91 +78,156 @@ __device__ __forceinline__ void frag_step(f32x16 (&acc)[4][4], u32x4 (&xa)[4][4]
       xb[NB][q] = ld16(fb[q], loff, kl * 1024);
     }
   }
+  if (ST) {
+    img_put(dv, s, pbase, ldc, lane);
+    // the LDS read first, the store half a step later, so its wait on the read costs nothing
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+    __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);   // the step's eight loads
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);   // eight MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x040, 1, 0);   // the store
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);   // eight MFMAs
+  }
   pin_step(acc);  // keeps the loads of this step here, three steps before use
 }
 
-template <bool OUT_F32, int BIAS>
+// The four K steps of scale group kg, with SPG (0, 2 or 4) deferred stores, segments s0, s0 + 1, ..
+// (SPG 2: on steps 0 and 2).
+template <int SPG>
+__device__ __forceinline__ void frag_group(f32x16 (&acc)[4][4], u32x4 (&xa)[4][4], u32x4 (&xb)[4][4],
+                                           uint32_t (&csa)[4], uint32_t (&csb)[4],
+                                           const rsrc_t (&fa)[4], const rsrc_t (&fb)[4],
+                                           const rsrc_t (&qa)[4], const rsrc_t (&qb)[4], int64_t kg,
+                                           int64_t KS, int64_t KG, uint32_t loff, uint32_t soff,
+                                           const uint8_t* img, int s0, uint16_t* pbase, int64_t ldc,
+                                           int lane) {
+  uint32_t nsa[4], nsb[4];
+  {  // the next group's scale dwords (the last group reloads itself)
+    const uint32_t kn = (uint32_t)(kg + 1 < KG ? kg + 1 : KG - 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      nsa[i] = ld4(qa[i], soff, kn * 256);
+      nsb[i] = ld4(qb[i], soff, kn * 256);
+    }
+  }
+  const int64_t ks = kg * 4;   // loads run three steps ahead; past the end the last step reloads
+  frag_step<0, (SPG > 0)>(acc, xa, xb, csa, csb, fa, fb, (uint32_t)(ks + 3 < KS ? ks + 3 : KS - 1),
+                          loff, img, s0, pbase, ldc, lane);
+  frag_step<1, (SPG == 4)>(acc, xa, xb, csa, csb, fa, fb, (uint32_t)(ks + 4 < KS ? ks + 4 : KS - 1),
+                           loff, img, s0 + 1, pbase, ldc, lane);
+  frag_step<2, (SPG > 0)>(acc, xa, xb, csa, csb, fa, fb, (uint32_t)(ks + 5 < KS ? ks + 5 : KS - 1),
+                          loff, img, s0 + SPG / 2, pbase, ldc, lane);
+  frag_step<3, (SPG == 4)>(acc, xa, xb, csa, csb, fa, fb, (uint32_t)(ks + 6 < KS ? ks + 6 : KS - 1),
+                           loff, img, s0 + 3, pbase, ldc, lane);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    csa[i] = nsa[i];
+    csb[i] = nsb[i];
+  }
+}
+
+// The wave's remaining deferred stores, segments s .. kImgStores-1, back to back.
+__device__ __forceinline__ void img_flush(const uint8_t* img, int s, uint16_t* pbase, int64_t ldc,
+                                          int lane) {
+  for (; s < kImgStores; ++s) img_put(img_load(img, s, lane), s, pbase, ldc, lane);
+}
+
+// Persistent: workgroup w takes tiles w, w + gridDim.x, ... of the XCD-aware order (the grid is a
+// multiple of the XCD count, so every tile of a workgroup maps to the XCD it runs on). A wave's
+// whole bf16 tile waits in its LDS image and leaves during the next tile's first K groups, SPG
+// (2 or 4) stores per group; what a short K loop leaves is stored after it. Ragged tiles and fp32
+// output are stored directly.
+template <bool OUT_F32, int BIAS, int SPG>
 __global__ __launch_bounds__(256, 1) void mm_mxfp4_frag_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ SB, const float* __restrict__ alpha_ptr, int64_t M, int64_t N,
     int64_t K, void* __restrict__ out, int64_t ldc, int ntm, int ntn, bool vec_store,
     const void* __restrict__ bias) {
-  __shared__ __attribute__((aligned(16))) uint8_t epi[4 * kEpiWaveBytes];
+  constexpr bool kImg = !OUT_F32;
+  __shared__ __attribute__((aligned(16))) uint8_t img_all[kImg ? 4 * kImgWaveBytes : 16];
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int li = lane & 31, h = lane >> 5;
-  int tm, tn;
-  tile_coords(blockIdx.x, ntm, ntn, tm, tn);
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  uint8_t* img = img_all + (kImg ? wave * kImgWaveBytes : 0);
   const int64_t KS = K >> 6, KG = KS >> 2;
+  const int64_t kg_st = KG < kImgStores / SPG ? KG : kImgStores / SPG;  // groups that carry stores
   const int64_t ra_last = ((M + 31) >> 5) - 1, rb_last = ((N + 31) >> 5) - 1;
-
-  // wave-uniform bases of the wave's four A and four B row tiles (rows past the operand clamp to
-  // its last tile: read, never stored)
-  rsrc_t fa[4], fb[4], qa[4], qb[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int64_t ra = (m0 >> 5) + wm * 4 + i;
-    ra = ra < ra_last ? ra : ra_last;
-    int64_t rb = (n0 >> 5) + wn * 4 + i;
-    rb = rb < rb_last ? rb : rb_last;
-    fa[i] = make_rsrc(A + ra * KS * 1024, KS * 1024);
-    fb[i] = make_rsrc(B + rb * KS * 1024, KS * 1024);
-    qa[i] = make_rsrc(SA + ra * KG * 256, KG * 256);
-    qb[i] = make_rsrc(SB + rb * KG * 256, KG * 256);
-  }
-  const uint32_t loff = lane * 16, soff = lane * 4;
-
-  f32x16 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
-
-  u32x4 xa[4][4], xb[4][4];          // [ring buffer][row tile]
-  uint32_t csa[4], csb[4], nsa[4], nsb[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    csa[i] = ld4(qa[i], soff, 0);
-    csb[i] = ld4(qb[i], soff, 0);
-  }
-#pragma unroll
-  for (int b = 0; b < 3; ++b) {
-    const uint32_t ks = b < KS ? b : KS - 1;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      xa[b][i] = ld16(fa[i], loff, ks * 1024);
-      xb[b][i] = ld16(fb[i], loff, ks * 1024);
-    }
-  }
-
-  for (int64_t kg = 0; kg < KG; ++kg) {
-    {  // the next group's scale dwords (the last group reloads itself)
-      const int64_t kn = kg + 1 < KG ? kg + 1 : KG - 1;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        nsa[i] = ld4(qa[i], soff, (uint32_t)kn * 256);
-        nsb[i] = ld4(qb[i], soff, (uint32_t)kn * 256);
-      }
-    }
-    const int64_t ks = kg * 4;   // loads run three steps ahead; past the end the last step reloads
-    frag_step<0>(acc, xa, xb, csa, csb, fa, fb, (uint32_t)(ks + 3 < KS ? ks + 3 : KS - 1), loff);
-    frag_step<1>(acc, xa, xb, csa, csb, fa, fb, (uint32_t)(ks + 4 < KS ? ks + 4 : KS - 1), loff);
-    frag_step<2>(acc, xa, xb, csa, csb, fa, fb, (uint32_t)(ks + 5 < KS ? ks + 5 : KS - 1), loff);
-    frag_step<3>(acc, xa, xb, csa, csb, fa, fb, (uint32_t)(ks + 6 < KS ? ks + 6 : KS - 1), loff);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      csa[i] = nsa[i];
-      csb[i] = nsb[i];
-    }
-  }
-
+  const int total = ntm * ntn;
+  const bool can_img = kImg && ldc % 8 == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0;
   const float a = alpha_ptr ? *alpha_ptr : 1.0f;
   const float alpha[4] = {a, a, a, a};
-  store_tile<OUT_F32, BIAS, false>(acc, alpha, m0, n0, wm, wn, M, N, out, ldc, vec_store, epi, wave,
-                                   lane, li, h, bias);
+  uint16_t* pbase = nullptr;   // destination of the image waiting in LDS, null if none
+
+  for (int v = blockIdx.x; v < total; v += gridDim.x) {
+    int tm, tn;
+    tile_coords(v, ntm, ntn, tm, tn);
+    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+    // Lane-derived offsets are recomputed for each tile: hoisted out of the tile loop they would
+    // stay live across the K loop and push its registers into memory.
+    const int lk = opaque(lane);
+    const uint32_t loff = lk * 16, soff = lk * 4;
+
+    // wave-uniform bases of the wave's four A and four B row tiles (rows past the operand clamp
+    // to its last tile: read, never stored)
+    rsrc_t fa[4], fb[4], qa[4], qb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int64_t ra = (m0 >> 5) + wm * 4 + i;
+      ra = ra < ra_last ? ra : ra_last;
+      int64_t rb = (n0 >> 5) + wn * 4 + i;
+      rb = rb < rb_last ? rb : rb_last;
+      fa[i] = make_rsrc(A + ra * KS * 1024, KS * 1024);
+      fb[i] = make_rsrc(B + rb * KS * 1024, KS * 1024);
+      qa[i] = make_rsrc(SA + ra * KG * 256, KG * 256);
+      qb[i] = make_rsrc(SB + rb * KG * 256, KG * 256);
+    }
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+
+    u32x4 xa[4][4], xb[4][4];          // [ring buffer][row tile]
+    uint32_t csa[4], csb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      csa[i] = ld4(qa[i], soff, 0);
+      csb[i] = ld4(qb[i], soff, 0);
+    }
+#pragma unroll
+    for (int b = 0; b < 3; ++b) {
+      const uint32_t ks = b < KS ? b : KS - 1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xa[b][i] = ld16(fa[i], loff, ks * 1024);
+        xb[b][i] = ld16(fb[i], loff, ks * 1024);
+      }
+    }
+
+    int64_t kg = 0;
+    if (kImg && pbase) {
+      for (; kg < kg_st; ++kg)
+        frag_group<SPG>(acc, xa, xb, csa, csb, fa, fb, qa, qb, kg, KS, KG, loff, soff, img,
+                        (int)kg * SPG, pbase, ldc, lk);
+      img_flush(img, (int)kg_st * SPG, pbase, ldc, lk);
+      pbase = nullptr;
+    }
+    for (; kg < KG; ++kg)
+      frag_group<0>(acc, xa, xb, csa, csb, fa, fb, qa, qb, kg, KS, KG, loff, soff, img, 0, pbase,
+                    ldc, lk);
+
+    const int le = opaque(lane);   // the epilogue's lane offsets, computed after the K loop
+    const int64_t m0w = m0 + wm * 128, n0w = n0 + wn * 128;
+    if (can_img && m0 + BM <= M && n0 + BN <= N) {
+      img_write<BIAS, false>(acc, alpha, n0w, N, img, le & 31, le >> 5, bias);
+      pbase = static_cast<uint16_t*>(out) + m0w * ldc + n0w;
+    } else {
+      store_wave_tile<OUT_F32, BIAS, false>(acc, alpha, m0w, n0w, M, N, out, ldc, vec_store, le & 31,
+                                            le >> 5, bias);
+    }
+  }
+  if (kImg && pbase) img_flush(img, 0, pbase, ldc, lane);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -313,20 +369,42 @@ int launch8(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t
   return check_launch(name);
 }
 
+// Workgroups of the launch. Up to K = 5120 a persistent grid: one workgroup per compute unit (a
+// workgroup fills a CU's registers), rounded down to a multiple of the XCD count, each storing a
+// tile during the next one's K loop (measured at M = 32760, N = 13824: 4-12 % faster for K <=
+// 2048, even at 5120). Above it one tile per workgroup, which measured 2-4 % faster at K = 8192 and
+// 13824. BSP_PERSISTENT_GRID=n sets the count (tests use small grids so that each workgroup runs
+// many tiles).
+inline int64_t mx_frag_grid(int64_t tiles, int64_t K) {
+  int64_t g = tiles;
+  if (K <= 5120) {
+    g = device_cu_count();
+    g = g >= kXcds ? g / kXcds * kXcds : 256;
+  }
+  if (const char* e = getenv("BSP_PERSISTENT_GRID")) {
+    const long long n = atoll(e);
+    if (n > 0) g = n;
+  }
+  return tiles < g ? tiles : g;
+}
+
 template <int BIAS = kBiasNone>
 int launch(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb, const float* alpha,
            int64_t M, int64_t N, int64_t K, void* out, int64_t ldc, int out_dtype, hipStream_t s,
            const char* name, const void* bias = nullptr) {
   const int64_t ntm = ceil_div(M, BM), ntn = ceil_div(N, BN);
-  const int64_t tiles = ntm * ntn;
+  const int64_t grid = mx_frag_grid(ntm * ntn, K);
   const size_t esz = out_dtype == BSP_OUT_F32 ? 4 : 2;
   const bool vec = (ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(out) & (4 * esz - 1)) == 0);
   if (out_dtype == BSP_OUT_F32)
-    hipLaunchKernelGGL((mm_mxfp4_frag_kernel<true, BIAS>), dim3((unsigned)tiles), dim3(256), 0, s, a, sa,
-                       b, sb, alpha, M, N, K, out, ldc, (int)ntm, (int)ntn, vec, bias);
+    hipLaunchKernelGGL((mm_mxfp4_frag_kernel<true, BIAS, 2>), dim3((unsigned)grid), dim3(256), 0, s, a,
+                       sa, b, sb, alpha, M, N, K, out, ldc, (int)ntm, (int)ntn, vec, bias);
+  else if (K / 256 >= kImgStores / 2)   // 16 or more scale groups: two deferred stores per group
+    hipLaunchKernelGGL((mm_mxfp4_frag_kernel<false, BIAS, 2>), dim3((unsigned)grid), dim3(256), 0, s, a,
+                       sa, b, sb, alpha, M, N, K, out, ldc, (int)ntm, (int)ntn, vec, bias);
   else
-    hipLaunchKernelGGL((mm_mxfp4_frag_kernel<false, BIAS>), dim3((unsigned)tiles), dim3(256), 0, s, a, sa,
-                       b, sb, alpha, M, N, K, out, ldc, (int)ntm, (int)ntn, vec, bias);
+    hipLaunchKernelGGL((mm_mxfp4_frag_kernel<false, BIAS, 4>), dim3((unsigned)grid), dim3(256), 0, s, a,
+                       sa, b, sb, alpha, M, N, K, out, ldc, (int)ntm, (int)ntn, vec, bias);
   return check_launch(name);
 }
 

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "../../include/bsp_probe.h"
 
 namespace {
@@ -31,13 +33,21 @@ __device__ __forceinline__ _Float16 nvfp4_like_f16(uint32_t h) {
 
 // FMT 0: v_mfma_f32_32x32x16_f16 on NVFP4-like fp16 operands (mm_fp4's instruction);
 // FMT 1: v_mfma_scale_f32_32x32x64_f8f6f4 with e4m3 operands (mm_mxfp8's);
-// FMT 2: the same with e2m1 operands (mm_mxfp4's). Four independent accumulator chains per wave.
+// FMT 2: the same with e2m1 operands (mm_mxfp4's);
+// FMT 3: v_mfma_scale_f32_16x16x128_f8f6f4 with e4m3 operands (the fp8 shape this chip runs fastest).
+// kChains independent accumulator chains per wave: with four, the 32-cycle instructions (FMT 0
+// and 2) kept the matrix core only about 77 % busy; with eight it stays busy at one wave per SIMD,
+// as in the GEMMs.
+constexpr int kChains = 8;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 template <int FMT>
 __global__ __launch_bounds__(256) void mfma_loop_kernel(float* out, int iters, uint32_t seed) {
   const uint32_t base = mix(seed ^ (blockIdx.x * 256u + threadIdx.x));
-  f32x16 acc[4];
+  typedef typename std::conditional<FMT == 3, f32x4, f32x16>::type acc_t;
+  constexpr int kAccN = FMT == 3 ? 4 : 16;
+  acc_t acc[kChains];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) acc[c] = f32x16{};
+  for (int c = 0; c < kChains; ++c) acc[c] = acc_t{};
   if constexpr (FMT == 0) {
     f16x8 a[2], b[2];
 #pragma unroll
@@ -49,8 +59,8 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(float* out, int iters, u
       }
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[c & 1], b[c >> 1], acc[c], 0, 0, 0);
+      for (int c = 0; c < kChains; ++c)
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[c & 1], b[(c >> 1) & 1], acc[c], 0, 0, 0);
     }
   } else {
     i32x8 a[2], b[2];
@@ -59,7 +69,7 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(float* out, int iters, u
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         uint32_t x = mix(base + 16u * i + e), y = mix(base + 977u + 16u * i + e);
-        if (FMT == 1) {  // no e4m3 NaN bytes (0x7F / 0xFF): flip their lowest bit
+        if (FMT != 2) {  // no e4m3 NaN bytes (0x7F / 0xFF): flip their lowest bit
 #pragma unroll
           for (int j = 0; j < 32; j += 8) {
             if (((x >> j) & 0x7Fu) == 0x7Fu) x ^= 1u << j;
@@ -69,20 +79,25 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(float* out, int iters, u
         a[i][e] = (int)x;
         b[i][e] = (int)y;
       }
-    constexpr int code = FMT == 1 ? 0 : 4;
+    constexpr int code = FMT == 2 ? 4 : 0;
     const int sa = 0x7F7F7F7F, sb = 0x7E7E7E7E;  // e8m0 scales 1 and 1/2
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[c & 1], b[c >> 1], acc[c], code, code,
-                                                                 0, sa, 0, sb);
+      for (int c = 0; c < kChains; ++c) {
+        if constexpr (FMT == 3)
+          acc[c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[c & 1], b[(c >> 1) & 1], acc[c],
+                                                                    code, code, 0, sa, 0, sb);
+        else
+          acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[c & 1], b[(c >> 1) & 1], acc[c],
+                                                                   code, code, 0, sa, 0, sb);
+      }
     }
   }
   float s = 0.0f;
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
+  for (int c = 0; c < kChains; ++c)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) s += acc[c][e];
+    for (int e = 0; e < kAccN; ++e) s += acc[c][e];
   out[blockIdx.x * 256 + threadIdx.x] = s;
 }
 
@@ -127,12 +142,13 @@ __global__ __launch_bounds__(256) void stream_kernel(const u32x4* __restrict__ s
 }  // namespace
 
 extern "C" int bsp_probe_mfma_loop(int fmt, int workgroups, int iters, float* out, void* stream) {
-  if (fmt < 0 || fmt > 2 || workgroups <= 0 || iters <= 0 || !out) return -1;
+  if (fmt < 0 || fmt > 3 || workgroups <= 0 || iters <= 0 || !out) return -1;
   const dim3 g(workgroups), b(256);
   hipStream_t s = (hipStream_t)stream;
   if (fmt == 0) hipLaunchKernelGGL(mfma_loop_kernel<0>, g, b, 0, s, out, iters, 12345u);
   else if (fmt == 1) hipLaunchKernelGGL(mfma_loop_kernel<1>, g, b, 0, s, out, iters, 12345u);
-  else hipLaunchKernelGGL(mfma_loop_kernel<2>, g, b, 0, s, out, iters, 12345u);
+  else if (fmt == 2) hipLaunchKernelGGL(mfma_loop_kernel<2>, g, b, 0, s, out, iters, 12345u);
+  else hipLaunchKernelGGL(mfma_loop_kernel<3>, g, b, 0, s, out, iters, 12345u);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 

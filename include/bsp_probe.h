@@ -11,12 +11,14 @@
 extern "C" {
 #endif
 
-/* MFMA-only loop: `workgroups` workgroups of 256 threads, each wave issuing `iters` x 4 independent
- * matrix instructions on register operands, with no memory traffic but the final store:
+/* MFMA-only loop: `workgroups` workgroups of 256 threads, each wave issuing `iters` x 8 independent
+ * matrix instructions (eight accumulator chains) on register operands, with no memory traffic but
+ * the final store:
  *   fmt 0: v_mfma_f32_32x32x16_f16 (32768 flops each) on fp16 values of the form e2m1 x e4m3 x 2^-8,
  *          the operands mm_fp4 multiplies;
  *   fmt 1: v_mfma_scale_f32_32x32x64_f8f6f4 with e4m3 operands (131072 flops), mm_mxfp8's;
- *   fmt 2: the same with e2m1 operands, mm_mxfp4's.
+ *   fmt 2: the same with e2m1 operands, mm_mxfp4's;
+ *   fmt 3: v_mfma_scale_f32_16x16x128_f8f6f4 with e4m3 operands (65536 flops).
  * out: device fp32 [workgroups * 256], one value per thread (keeps the loop from being removed). */
 int bsp_probe_mfma_loop(int fmt, int workgroups, int iters, float* out, void* stream);
 

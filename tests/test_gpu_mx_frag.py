@@ -144,6 +144,37 @@ def test_mm_mxfp4_frag_bias(m, n, k):
     assert torch.equal(tb32, t32 + bias.float())
 
 
+@pytest.mark.parametrize("m,n,k,grids", [(1100, 1300, 1024, (1, 4, 7)),     # 4 deferred stores per K group
+                                         (530, 777, 4096, (3, 8)),          # 2 per group, all inside the K loop
+                                         (600, 520, 6144, (2, 5))])         # above the persistent K limit
+def test_mm_mxfp4_frag_persistent_grids(m, n, k, grids, monkeypatch):
+    """Small grids, so that each workgroup runs many tiles (whole and ragged) and stores each whole
+    tile during the next one's K loop: every element against the oracle, and bit for bit equal to
+    mm_mxfp4 on the linear-layout operands, with bf16 and fp32 output and with bias."""
+    rng = np.random.default_rng(m + n + k)
+    (fa, fsa), (pa, sa) = _rand_operand(rng, m, k)
+    (fb, fsb), (pb, sb) = _rand_operand(rng, n, k)
+    al = f32(0.75)
+    ref = X4.mm_mxfp4_frag(fa, fsa, fb, fsb, al, m, n, k)
+    a, a_s = _frag_dev(fa, fsa, m, k)
+    b, b_s = _frag_dev(fb, fsb, n, k)
+    std = (dev_u8(pa), dev_u8(sa), dev_u8(pb), dev_u8(sb))
+    bias = dev_bf16(W.f32_to_bf16_bits((rng.standard_normal(n) * float(np.std(ref))).astype(np.float32)))
+    want16 = bsp.bsp_mm_mxfp4(*std, scalar(al))
+    want32 = bsp.bsp_mm_mxfp4(*std, scalar(al), out_dtype=torch.float32)
+    wantb = bsp.bsp_mm_mxfp4_bias(*std, bias, scalar(al))
+    for g in grids:
+        say("mm_mxfp4_frag persistent", m, n, k, "grid", g)
+        monkeypatch.setenv("BSP_PERSISTENT_GRID", str(g))
+        t16 = bsp.bsp_mm_mxfp4_frag(a, a_s, b, b_s, m, n, scalar(al))
+        t32 = bsp.bsp_mm_mxfp4_frag(a, a_s, b, b_s, m, n, scalar(al), out_dtype=torch.float32)
+        tb = bsp.bsp_mm_mxfp4_frag(a, a_s, b, b_s, m, n, scalar(al), bias)
+        check_gemm_outputs(t16, t32, ref, f"mxfp4 frag {m}x{n}x{k} grid {g}")
+        assert torch.equal(t16.view(torch.int16), want16.view(torch.int16)), g
+        assert torch.equal(t32, want32), g
+        assert torch.equal(tb.view(torch.int16), wantb.view(torch.int16)), g
+
+
 def test_mm_mxfp4_frag_full_size():
     """Wan-14B fc_in, 32760 x 13824 x 5120, operands from bsp_mxfp4_quantize_frag: sampled entries
     against the oracle, and the whole output equal to mm_mxfp4's on the linear-layout operands."""
