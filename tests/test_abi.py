@@ -226,7 +226,7 @@ def test_probe_library_exports_its_header():
         assert hasattr(lib, n), n
     # argument checks return -1 before anything touches a GPU
     lib.bsp_probe_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
-    assert lib.bsp_probe_mfma_loop(3, 1, 1, P, None) == -1
+    assert lib.bsp_probe_mfma_loop(4, 1, 1, P, None) == -1
     assert lib.bsp_probe_mfma_loop(0, 0, 1, P, None) == -1
     lib.bsp_probe_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                      ctypes.c_int, ctypes.c_void_p]

@@ -125,6 +125,16 @@ def test_rmsnorm_strided_unaligned_and_zero_rows():
     check_fused(p, sf, xb, wb, 1e-6, 1.0, "quantize_rmsnorm unaligned")
 
 
+def test_quantize_rmsnorm_packed_not_16_byte_aligned():
+    """A packed output 4-byte but not 16-byte aligned at K % 32 == 0: each lane's four bytes are
+    stored instead of 16-byte row pieces; the bytes meet the same bar against the oracle chain."""
+    m, k = 130, 512
+    xb = W.small_case(m, k, seed=23, outlier_frac=0.02)
+    p = torch.zeros(m * (k // 2) + 4, dtype=torch.uint8, device="cuda")[4:].view(m, k // 2)
+    _, sf = bsp.bsp_nvfp4_quantize_rmsnorm(dev_bf16(xb), scalar(1.0), None, 1e-6, packed=p)
+    check_fused(p, sf, xb, None, 1e-6, 1.0, "rmsnorm quantize, packed at a 4-byte offset")
+
+
 def test_rmsnorm_empty_input():
     x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
     assert bsp.bsp_rmsnorm_bf16(x).shape == (0, 64)

@@ -102,6 +102,30 @@ def test_nvfp4_quantize_per_token_bit_exact(m, k):
     assert np.array_equal(host_u8(sf).ravel(), rs)
 
 
+def _u8_at(shape, offset):
+    """A contiguous uint8 device tensor whose data starts `offset` bytes into its allocation (the
+    allocation itself is 256-byte aligned)."""
+    n = int(np.prod(shape))
+    return torch.zeros(n + offset, dtype=torch.uint8, device="cuda")[offset:].view(*shape)
+
+
+def test_quantizers_packed_output_not_16_byte_aligned():
+    """Packed outputs 4-byte but not 16-byte aligned, at K % 32 == 0: the per-tensor, per-token and
+    RMSNorm quantizers write each lane's four bytes instead of their 16-byte row pieces, and the
+    bytes are the oracle's."""
+    m, k = 130, 512
+    xb = W.small_case(m, k, seed=21, outlier_frac=0.02)
+    rp, rs = N.quantize(xb, f32(0.5))
+    p = _u8_at((m, k // 2), 4)
+    _, s = bsp.bsp_nvfp4_quantize(dev_bf16(xb), scalar(0.5), packed=p)
+    assert np.array_equal(host_u8(p), rp) and np.array_equal(host_u8(s).ravel(), rs)
+    tp, ts, tg = N.quantize_per_token(xb)
+    p = _u8_at((m, k // 2), 4)
+    _, s, g = bsp.bsp_nvfp4_quantize_per_token(dev_bf16(xb), packed=p)
+    assert np.array_equal(g.cpu().numpy(), tg)
+    assert np.array_equal(host_u8(p), tp) and np.array_equal(host_u8(s).ravel(), ts)
+
+
 def test_nvfp4_quantize_per_token_strided_and_special():
     xb = W.special_values_block(seed=17, rows=140, cols=512)
     big = np.zeros((140, 520), dtype=np.uint16)
