@@ -554,13 +554,14 @@ __global__ __launch_bounds__(256) void rmsnorm_token_kernel(
 // 256 are half (t & 1) of 16-byte chunk p = (rr/32)*512 + g*32 + rr%32 of the staging area, with
 // g = (t % 32) / 2 = 4 * K step + 2 * block + lane half; it is placed at chunk p ^ 2g, as the
 // sixteen g of a row otherwise sit 512 bytes apart, in one set of LDS banks.
-template <bool HWCVT, bool VEC, bool FRAG = false>
+template <bool HWCVT, bool VEC, bool FRAG = false, bool WIDE = false>
 __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const uint16_t* __restrict__ x,
                                                              int64_t M, int64_t K, int64_t ld,
                                                              uint8_t* __restrict__ q,
                                                              uint8_t* __restrict__ sf) {
-  __shared__ uint4 frag_tile[FRAG ? 1024 : 1];  // FRAG: the workgroup's 16 KB of fragments
-  __shared__ uint4 sf_stage[FRAG ? 32 : 1];     // FRAG: its two 256-byte scale groups
+  // FRAG: the workgroup's 16 KB of fragments; WIDE: its 64 rows x 256 bytes of codes
+  __shared__ uint4 frag_tile[FRAG || WIDE ? 1024 : 1];
+  __shared__ uint4 sf_stage[FRAG || WIDE ? 32 : 1];  // FRAG: two 256-byte scale groups; WIDE: 64 x 8
   const int t = threadIdx.x;
   const int64_t row0 = (int64_t)blockIdx.y * 64;
   const int64_t kk = (int64_t)blockIdx.x * 256 + (t & 31) * 8;
@@ -616,10 +617,36 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const uint16_t* __r
         reinterpret_cast<uint8_t*>(sf_stage)[(rr >> 5) * 256 + ((cb & 1) * 32 + (rr & 31)) * 4 + (cb >> 1)] =
             (uint8_t)byte;
       }
+    } else if (WIDE && full) {
+      // row rr's 256 code bytes at rr * 256 of the image; its 8 scale bytes at rr * 8
+      const int rr = s * 8 + rsub;
+      reinterpret_cast<uint2*>(frag_tile)[rr * 32 + (t & 31)] = make_uint2(lo, hi);
+      if ((t & 3) == 0) reinterpret_cast<uint8_t*>(sf_stage)[rr * 8 + ((t & 31) >> 2)] = (uint8_t)byte;
     } else if (full || (kin && row0 + s * 8 + rsub < M)) {
       typedef uint32_t u32x2_nt __attribute__((ext_vector_type(2)));
       __builtin_nontemporal_store((u32x2_nt){lo, hi}, reinterpret_cast<u32x2_nt*>(qp + s * 8 * K));
       if ((t & 3) == 0) sp[s * 8 * ng] = (uint8_t)byte;
+    }
+  }
+  if (WIDE && full) {   // uniform: interior tiles leave as 16-byte pieces, 4 rows per instruction
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int p = it * 256 + t, rr = p >> 4, part = p & 15;
+      const uint4 w = frag_tile[p];
+      __builtin_nontemporal_store((nt_u32x4){w.x, w.y, w.z, w.w},
+                                  reinterpret_cast<nt_u32x4*>(q + (row0 + rr) * K + blockIdx.x * 256 + part * 16));
+    }
+    // each row's 8 scale bytes of this K range: one 8-byte store when the row offsets allow it
+    if (t < 64) {
+      const int64_t off = (row0 + t) * ng + (int64_t)blockIdx.x * 8;
+      const uint2 w = reinterpret_cast<const uint2*>(sf_stage)[t];
+      if (((reinterpret_cast<uintptr_t>(sf) + off) & 7) == 0) {
+        *reinterpret_cast<uint2*>(sf + off) = w;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sf[off + i] = (uint8_t)((i < 4 ? w.x : w.y) >> (8 * (i & 3)));
+      }
     }
   }
   if constexpr (FRAG) {
@@ -657,13 +684,14 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const uint16_t* __r
 // 4 KB runs and four 256-byte runs. A thread's 4 output bytes for row rr and block cb are 16-byte
 // chunk p = (rr/32)*256 + cb*32 + rr%32 of the staging area (cb = 2 * K step + lane half), placed
 // at chunk p ^ 2cb: the eight blocks of a row otherwise sit 512 bytes apart, all in one LDS bank.
-template <bool HWCVT, bool VEC, bool FRAG = false>
+template <bool HWCVT, bool VEC, bool FRAG = false, bool WIDE = false>
 __global__ __launch_bounds__(256) void mxfp4_quantize_kernel(const uint16_t* __restrict__ x,
                                                              int64_t M, int64_t K, int64_t ld,
                                                              uint8_t* __restrict__ packed,
                                                              uint8_t* __restrict__ sf, int64_t Kp) {
   __shared__ uint4 sf_tile[64];  // 1 KB = 2 scale tiles of 512 B (FRAG: 4 scale groups of 256 B)
-  __shared__ uint4 frag_tile[FRAG ? 1024 : 1];  // FRAG: the workgroup's 16 KB of packed fragments
+  // FRAG: the workgroup's 16 KB of packed fragments; WIDE: its 128 rows x 128 packed bytes
+  __shared__ uint4 frag_tile[FRAG || WIDE ? 1024 : 1];
   uint8_t* sfb = reinterpret_cast<uint8_t*>(sf_tile);
   const int t = threadIdx.x;
   const int64_t row0 = (int64_t)blockIdx.y * 128;
@@ -711,7 +739,8 @@ __global__ __launch_bounds__(256) void mxfp4_quantize_kernel(const uint16_t* __r
       reinterpret_cast<uint32_t*>(frag_tile)[(p ^ (cb << 1)) * 4 + (t & 3)] = out;
       if ((t & 3) == 0) sfb[(rr >> 5) * 256 + ((cb & 1) * 32 + (rr & 31)) * 4 + (cb >> 1)] = (uint8_t)byte;
     } else {
-      if (full || (kin && row0 + rr < M)) store4_nt(pp + s * pstep, out);
+      if (WIDE && full) reinterpret_cast<uint32_t*>(frag_tile)[rr * 32 + (t & 31)] = out;
+      else if (full || (kin && row0 + rr < M)) store4_nt(pp + s * pstep, out);
       if ((t & 3) == 0)  // cb: scale column inside the 8-column tile
         sfb[(cb >> 2) * 512 + (rr & 31) * 16 + (rr >> 5) * 4 + (cb & 3)] = (uint8_t)byte;
     }
@@ -734,6 +763,16 @@ __global__ __launch_bounds__(256) void mxfp4_quantize_kernel(const uint16_t* __r
     if (t < 64 && rt0 + (t >> 4) < row_tiles)
       reinterpret_cast<uint4*>(sf + ((rt0 + (t >> 4)) * k_groups + blockIdx.x) * 256)[t & 15] = sf_tile[t];
     return;
+  }
+  if (WIDE && full) {   // uniform: interior tiles leave as 16-byte pieces, 8 rows per instruction
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int p = it * 256 + t, rr = p >> 3, part = p & 7;
+      const uint4 w = frag_tile[p];
+      __builtin_nontemporal_store(
+          (nt_u32x4){w.x, w.y, w.z, w.w},
+          reinterpret_cast<nt_u32x4*>(packed + (row0 + rr) * half_k + (int64_t)blockIdx.x * 128 + part * 16));
+    }
   }
   const int64_t groups = Kp / 4;
   const int64_t g0 = (int64_t)blockIdx.x * 2;
@@ -1109,7 +1148,16 @@ extern "C" int bsp_mxfp8_quantize(const void* x, int64_t M, int64_t K, int64_t l
   const bool vec = (ld % 8 == 0) && aligned16(x);
   const bool hw = hw_cvt_enabled();
   hipStream_t s = (hipStream_t)stream;
-  if (hw && vec)
+  // interior tiles of a 16-byte aligned q leave through LDS as 16-byte pieces (rows start 16-byte
+  // aligned: K % 32 == 0); the software-encoder path (a test switch) keeps the direct stores
+  const bool wide = aligned16(q);
+  if (hw && vec && wide)
+    hipLaunchKernelGGL((mxfp8_quantize_kernel<true, true, false, true>), grid, dim3(256), 0, s, xp, M, K,
+                       ld, q, sf);
+  else if (hw && wide)
+    hipLaunchKernelGGL((mxfp8_quantize_kernel<true, false, false, true>), grid, dim3(256), 0, s, xp, M, K,
+                       ld, q, sf);
+  else if (hw && vec)
     hipLaunchKernelGGL((mxfp8_quantize_kernel<true, true>), grid, dim3(256), 0, s, xp, M, K, ld, q, sf);
   else if (hw)
     hipLaunchKernelGGL((mxfp8_quantize_kernel<true, false>), grid, dim3(256), 0, s, xp, M, K, ld, q, sf);
@@ -1238,7 +1286,16 @@ extern "C" int bsp_mxfp4_quantize(const void* x, int64_t M, int64_t K, int64_t l
   const bool vec = (ld % 8 == 0) && aligned16(x);
   const bool hw = hw_cvt_enabled();
   hipStream_t s = (hipStream_t)stream;
-  if (hw && vec)
+  // interior tiles of a 16-byte aligned packed matrix leave through LDS as 16-byte pieces (rows
+  // start 16-byte aligned: K % 32 == 0); the software-encoder path (a test switch) stores directly
+  const bool wide = aligned16(packed);
+  if (hw && vec && wide)
+    hipLaunchKernelGGL((mxfp4_quantize_kernel<true, true, false, true>), grid, dim3(256), 0, s, xp, M, K,
+                       ld, packed, sf, Kp);
+  else if (hw && wide)
+    hipLaunchKernelGGL((mxfp4_quantize_kernel<true, false, false, true>), grid, dim3(256), 0, s, xp, M, K,
+                       ld, packed, sf, Kp);
+  else if (hw && vec)
     hipLaunchKernelGGL((mxfp4_quantize_kernel<true, true>), grid, dim3(256), 0, s, xp, M, K, ld, packed, sf, Kp);
   else if (hw)
     hipLaunchKernelGGL((mxfp4_quantize_kernel<true, false>), grid, dim3(256), 0, s, xp, M, K, ld, packed, sf, Kp);
