@@ -206,8 +206,14 @@ def main():
     qx_calls = [lambda i=i: bsp.bsp_nvfp4_quantize(xs[i], one, pxs[i], sxs[i]) for i in range(2)]
     nq_calls = [lambda i=i: bsp.bsp_nvfp4_quantize_rmsnorm(xs[i], one, None, 1e-6, pxs[i], sxs[i])
                 for i in range(2)]
+    # the GELU-fused quantize of H back to back over two copies of the fc_in output (in the step it
+    # follows fc_in, whose 0.9 GB output is still being written back)
+    y2 = y.clone()
+    ys, phs, shs = (y, y2), (ph, torch.empty_like(ph)), (sh, torch.empty_like(sh))
+    gq_calls = [lambda i=i: bsp.bsp_nvfp4_quantize_gelu(ys[i], one, phs[i], shs[i]) for i in range(2)]
     for name, fns in (("quantize_x", qx_calls),
                       ("rmsnorm_quantize_x", nq_calls),
+                      ("gelu_quantize_h_back_to_back", gq_calls),
                       ("gelu", [lambda: bsp.bsp_gelu_tanh_bf16(y, out=h)]),
                       ("quantize_h", [lambda: bsp.bsp_nvfp4_quantize(h, one, ph, sh)])):
         for f in fns:
@@ -219,7 +225,7 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         kms[name] = e0.elapsed_time(e1) / reps
-    del h, x2, px2, sx2
+    del h, x2, px2, sx2, y2, ys, phs, shs
 
     gemm_flops = 2.0 * M * N1 * K1 + 2.0 * M * N2 * N1
     value = gemm_flops / (ms_per_step * 1e-3) / 1e12
@@ -235,6 +241,8 @@ def main():
                                "GB/s": qbytes(M, K1) / kms["quantize_x_in_step"] / 1e6},
         "gelu_quantize_h": {"ms": kms["gelu_quantize_h"],
                             "GB/s": qbytes(M, N1) / kms["gelu_quantize_h"] / 1e6},
+        "gelu_quantize_h_back_to_back": {"ms": kms["gelu_quantize_h_back_to_back"],
+                                         "GB/s": qbytes(M, N1) / kms["gelu_quantize_h_back_to_back"] / 1e6},
         "quantize_h": {"ms": kms["quantize_h"], "GB/s": qbytes(M, N1) / kms["quantize_h"] / 1e6},
         "gelu": {"ms": kms["gelu"], "GB/s": 4.0 * M * N1 / kms["gelu"] / 1e6},
         "mm_fp4_fc_in": {"ms": kms["mm_fp4_fc_in"],
@@ -329,10 +337,19 @@ def main():
     torch.cuda.synchronize()
     qpt = sum(e[0].elapsed_time(e[1]) for e in ept) / args.steps
     gpt = sum(e[1].elapsed_time(e[2]) for e in ept) / args.steps
+    # the per-token quantize back to back over two copies of X and of its outputs (in the loop above
+    # each call follows a GEMM whose 0.9 GB output is still being written back)
+    x2 = x.clone()
+    outs2 = [(px, sx, gx), (torch.empty_like(px), torch.empty_like(sx), torch.empty_like(gx))]
+    qpt_b2b = _event_ms([lambda i=i: bsp.bsp_nvfp4_quantize_per_token((x, x2)[i], *outs2[i])
+                         for i in range(2)], max(4, 2 * (args.steps // 4)))
+    del x2, outs2
     result["per_token"] = {
         "quantize_per_token_x_ms": round(qpt, 4),
         "quantize_per_token_GBs": round(qbytes(M, K1) / qpt / 1e6, 1),
         "quantize_per_token_frac_hbm": round(qbytes(M, K1) / qpt / 1e6 / PEAK_HBM_GBS, 4),
+        "quantize_per_token_x_back_to_back_ms": round(qpt_b2b, 4),
+        "quantize_per_token_back_to_back_frac_hbm": round(qbytes(M, K1) / qpt_b2b / 1e6 / PEAK_HBM_GBS, 4),
         "mm_fp4_per_token_fc_in_ms": round(gpt, 4),
         "mm_fp4_per_token_TFLOPS": round(2.0 * M * N1 * K1 / gpt / 1e9, 2)}
     log(json.dumps(result["per_token"]))
@@ -376,11 +393,19 @@ def main():
         g8 = sum(e[1].elapsed_time(e[2]) for e in e8) / args.steps
         tf8 = 2.0 * M * N1 * K1 / g8 / 1e9
         qb8 = 2 * M * K1 + M * K1 + M * K1 // 32
+        # the quantize back to back over two copies of X and of its outputs (as for the NVFP4 one)
+        x52 = x5.clone()
+        o52 = [(qx, sxm), (torch.empty_like(qx), torch.empty_like(sxm))]
+        q8_b2b = _event_ms([lambda i=i: bsp.bsp_mxfp8_quantize((x5, x52)[i], *o52[i]) for i in range(2)],
+                           max(4, 2 * (args.steps // 4)))
+        del o52
         result["mxfp8"] = {
             "mm_mxfp8_ms": round(g8, 4), "TFLOPS": round(tf8, 2),
             "frac_fp8_peak": round(tf8 / PEAK_FP8_TFLOPS, 4),
             "quantize_ms": round(q8, 4), "quantize_GBs": round(qb8 / q8 / 1e6, 1),
             "quantize_frac_hbm": round(qb8 / q8 / 1e6 / PEAK_HBM_GBS, 4),
+            "quantize_back_to_back_ms": round(q8_b2b, 4),
+            "quantize_back_to_back_frac_hbm": round(qb8 / q8_b2b / 1e6 / PEAK_HBM_GBS, 4),
             "weight_conversion_ms": round(m0.elapsed_time(m1), 4)}
         log(json.dumps(result["mxfp8"]))
         del qx, sxm
@@ -443,11 +468,17 @@ def main():
         g4 = sum(e[1].elapsed_time(e[2]) for e in e4) / args.steps
         tf4 = 2.0 * M * N1 * K1 / g4 / 1e9
         qb4 = 2 * M * K1 + M * K1 // 2 + (-(-M // 128) * 128) * K1 // 32
+        o42 = [(px4, sx4), (torch.empty_like(px4), torch.empty_like(sx4))]
+        q4_b2b = _event_ms([lambda i=i: bsp.bsp_mxfp4_quantize((x5, x52)[i], *o42[i]) for i in range(2)],
+                           max(4, 2 * (args.steps // 4)))
+        del o42
         result["mxfp4"] = {
             "mm_mxfp4_ms": round(g4, 4), "TFLOPS": round(tf4, 2),
             "frac_fp4_peak": round(tf4 / PEAK_FP4_TFLOPS, 4),
             "quantize_ms": round(q4, 4), "quantize_GBs": round(qb4 / q4 / 1e6, 1),
-            "quantize_frac_hbm": round(qb4 / q4 / 1e6 / PEAK_HBM_GBS, 4)}
+            "quantize_frac_hbm": round(qb4 / q4 / 1e6 / PEAK_HBM_GBS, 4),
+            "quantize_back_to_back_ms": round(q4_b2b, 4),
+            "quantize_back_to_back_frac_hbm": round(qb4 / q4_b2b / 1e6 / PEAK_HBM_GBS, 4)}
         log(json.dumps(result["mxfp4"]))
         del px4, sx4
 
@@ -482,7 +513,7 @@ def main():
             "quantize_frac_hbm": round(qb4f / q4f / 1e6 / PEAK_HBM_GBS, 4),
             "step_ms": round(q4f + g4f, 4), "step_ms_linear_layout": round(q4 + g4, 4)}
         log(json.dumps(result["mxfp4_frag"]))
-        del px4f, sx4f, pw4f, sw4f
+        del px4f, sx4f, pw4f, sw4f, x52
 
     # ---- PyTorch's own memory-bound kernels on the same GPU, for context beside the published
     # 8 TB/s: a 2 GiB device-to-device copy (read:write 1:1) and a 2 GiB fp32 sum (read only), timed
