@@ -26,6 +26,16 @@ U3 e2m1 RNE + saturate to 6; U4 sign of zero kept; U5 even k in the low nibble;
 U6 the 128x4 byte offset (``sf_offset``); U7 padded scale bytes are 0x00;
 U8 gsf = 1 when amax == 0; U9 NaN / +-inf are quantized as nan_to_num gives them;
 U10 alpha from the fp32 gsf; U11 2688/amax is one IEEE fp32 division.
+
+Fragment layout of the packed values (``frag_*``, ``quantize(..., packed_layout="frag")``). The
+FastVideo nvfp4_config.py ``_nvfp4_quantize`` carries a ``do_shuffle`` switch for operands
+pre-arranged for the matrix unit; it is off there and its arrangement is left to the library. This
+one lets a wave read a 32-row by 64-element K step of an operand as one contiguous 1 KB: lane
+i + 32 h reads the 16 bytes (32 elements) of row i at K offsets 32 h .. 32 h + 31 of the step.
+Operand [R, K], K % 64 == 0, rows zero-padded to Rp = 32 * ceil(R / 32):
+  packed byte (r, j) (elements 2j, 2j+1 of row r) ->
+      ((r // 32) * (K // 64) + j // 32) * 1024 + ((j // 16) % 2 * 32 + r % 32) * 16 + j % 16.
+The scales keep the 128x4 layout; only the order of the packed bytes differs.
 """
 from __future__ import annotations
 
@@ -215,7 +225,7 @@ def unpack_nibbles(packed: np.ndarray) -> np.ndarray:
     return out
 
 
-def quantize(x_bits: np.ndarray, gsf, layout: str = "128x4"):
+def quantize(x_bits: np.ndarray, gsf, layout: str = "128x4", packed_layout: str = "rows"):
     """NVFP4-quantize bf16 X [M, K] (K % 16 == 0) under fp32 global scale ``gsf``.
 
     Returns (packed [M, K/2] uint8, sf) where sf is the flat 128x4-layout buffer of
@@ -223,6 +233,7 @@ def quantize(x_bits: np.ndarray, gsf, layout: str = "128x4"):
     or the [M, K/16] row-major bytes (layout "linear").
     Padded scale rows/columns hold 0x00, the scale of an all-zero padded block.
     NaN and +-inf are encoded as 0 and +-largest finite bf16 (reading U9).
+    packed_layout "frag" (K % 64 == 0) returns the packed bytes flat in the fragment layout.
     """
     x_bits = bf16_nan_to_num(x_bits)
     m, k = x_bits.shape
@@ -232,6 +243,10 @@ def quantize(x_bits: np.ndarray, gsf, layout: str = "128x4"):
     xf = bf16_to_f32(x_bits).reshape(m, nb, BLOCK)
     codes, S = quantize_blocks(xf, gsf)
     packed = pack_nibbles(codes.reshape(m, k))
+    if packed_layout == "frag":
+        packed = to_frag_packed(packed, k)
+    elif packed_layout != "rows":
+        raise ValueError(f"unknown packed layout {packed_layout!r}")
     if layout == "linear":
         return packed, S
     shape_fn, _, swz = _layout_fns(layout)
@@ -281,6 +296,44 @@ def quantize_rows(x_bits: np.ndarray, gsf):
 # ----------------------------------------------------------------------------------------
 # dequant and the GEMM
 # ----------------------------------------------------------------------------------------
+def frag_rows(rows: int) -> int:
+    """Rows of a fragment-layout operand: R padded to a multiple of 32."""
+    return (rows + 31) // 32 * 32
+
+
+def frag_packed_offset(r, j, k: int):
+    """Byte offset in the fragment layout of packed byte j (elements 2j, 2j+1) of row r."""
+    r = np.asarray(r, dtype=np.int64)
+    j = np.asarray(j, dtype=np.int64)
+    fragment = (r // 32) * (k // 64) + j // 32      # 32-row tile, then 64-element K step
+    lane = (j // 16) % 2 * 32 + r % 32              # lane half = which 32 elements of the step
+    return fragment * 1024 + lane * 16 + j % 16
+
+
+def to_frag_packed(packed: np.ndarray, k: int) -> np.ndarray:
+    """packed [R, K/2] -> flat fragment-layout bytes (Rp * K/2), zero rows R..Rp-1."""
+    if k % 64:
+        raise ValueError("the fragment layout needs K % 64 == 0")
+    rows = packed.shape[0]
+    out = np.zeros(frag_rows(rows) * k // 2, dtype=np.uint8)
+    r, j = np.meshgrid(np.arange(rows), np.arange(k // 2), indexing="ij")
+    out[frag_packed_offset(r, j, k)] = packed
+    return out
+
+
+def from_frag_packed(fp: np.ndarray, rows, k: int) -> np.ndarray:
+    """Flat fragment-layout bytes -> packed [R, K/2] for rows 0..rows-1 (an int) or the listed rows."""
+    sel = np.arange(rows) if np.isscalar(rows) else np.asarray(rows, dtype=np.int64)
+    r, j = np.meshgrid(sel, np.arange(k // 2), indexing="ij")
+    return np.asarray(fp, dtype=np.uint8).ravel()[frag_packed_offset(r, j, k)]
+
+
+def mm_fp4_frag(a_fp, a_sf, b_fp, b_sf, alpha_val, m: int, n: int, k: int) -> np.ndarray:
+    """mm_fp4 for operands whose packed bytes are in the fragment layout (scales in 128x4)."""
+    return mm_fp4(from_frag_packed(a_fp, m, k), a_sf, from_frag_packed(b_fp, n, k), b_sf, alpha_val,
+                  m, n, k)
+
+
 def dequant_rows(packed: np.ndarray, sf_flat: np.ndarray, rows, n_rows_total: int, k: int,
                  gsf=None, layout: str = "128x4") -> np.ndarray:
     """fp64 values e2m1(q) * e4m3(S) (/ gsf if given) of the selected rows."""

@@ -449,3 +449,72 @@ def test_global_sf_4over6_golden_and_256_block():
         blk = np.argwhere(np.max(np.abs(xf), axis=-1) == amax)[0]
         assert sf[blk[0], blk[1]] == 0x78
         assert sf.max() <= 0x78
+
+
+# ------------------------------------------------------------------------ fragment layout
+def test_frag_offsets_hand_worked():
+    n = 0
+    for line in golden_lines("frag_offsets_nvfp4.txt"):
+        r, j, k, off = (int(v) for v in line.split()[:4])
+        assert int(N.frag_packed_offset(r, j, k)) == off, line
+        n += 1
+    assert n == 10
+
+
+def test_frag_offsets_are_a_permutation_for_any_k_multiple_of_64():
+    for rows, k in [(33, 64), (5, 192), (64, 512), (40, 320)]:
+        rp = N.frag_rows(rows)
+        r, j = np.meshgrid(np.arange(rp), np.arange(k // 2), indexing="ij")
+        off = N.frag_packed_offset(r, j, k).ravel()
+        assert np.array_equal(np.sort(off), np.arange(rp * k // 2))
+    with pytest.raises(ValueError):
+        N.to_frag_packed(np.zeros((4, 40), np.uint8), 80)
+
+
+def test_frag_layout_matches_the_lane_placement():
+    """Independent construction by axis permutation: [tile, row i, step, half h, byte] of the padded
+    row-major bytes becomes [tile, step, h, i, byte]; the round trip restores every row."""
+    rng = np.random.default_rng(21)
+    for rows, k in [(70, 192), (32, 64), (45, 768)]:
+        packed = rng.integers(0, 256, size=(rows, k // 2)).astype(np.uint8)
+        fp = N.to_frag_packed(packed, k)
+        rp = N.frag_rows(rows)
+        pp = np.zeros((rp, k // 2), dtype=np.uint8)
+        pp[:rows] = packed
+        want = pp.reshape(rp // 32, 32, k // 64, 2, 16).transpose(0, 2, 3, 1, 4).ravel()
+        assert np.array_equal(fp, want)
+        assert np.array_equal(N.from_frag_packed(fp, rows, k), packed)
+        sel = np.array([rows - 1, 0, rows // 2])
+        assert np.array_equal(N.from_frag_packed(fp, sel, k), packed[sel])
+
+
+def test_frag_packed_arrangement_is_the_mxfp4_fragment_arrangement():
+    """The MXFP4 oracle's packed fragment offsets (written separately) agree where both apply."""
+    from oracle import mxfp4 as X4
+    for rows, k in [(64, 256), (33, 768)]:
+        r, j = np.meshgrid(np.arange(N.frag_rows(rows)), np.arange(k // 2), indexing="ij")
+        assert np.array_equal(N.frag_packed_offset(r, j, k), X4.frag_packed_offset(r, j, k))
+
+
+def test_frag_quantize_and_gemm_agree_with_the_row_major_layout():
+    m, n, k = 45, 37, 320
+    xa = W.small_case(m, k, 31, outlier_frac=0.02)
+    xb = W.small_case(n, k, 32, std=0.02)
+    gb = N.global_sf(xb)[0]
+    fa, sfa = N.quantize(xa, f32(1.0), packed_layout="frag")
+    pa, sa = N.quantize(xa, f32(1.0))
+    assert np.array_equal(sfa, sa)
+    assert fa.size == 64 * k // 2
+    assert np.array_equal(N.from_frag_packed(fa, m, k), pa)
+    pad = N.frag_packed_offset(np.arange(m, 64)[:, None], np.arange(k // 2)[None, :], k)
+    assert not fa[pad].any()
+    fb, sfb = N.quantize(xb, gb, packed_layout="frag")
+    pb, sb = N.quantize(xb, gb)
+    al = N.alpha(f32(1.0), gb)
+    got = N.mm_fp4_frag(fa, sfa, fb, sfb, al, m, n, k)
+    assert np.array_equal(got, N.mm_fp4(pa, sa, pb, sb, al, m, n, k))
+    # and the product is the brute-force fp64 sum of the dequantized values
+    A = N.dequant_rows(pa, sa, np.arange(m), m, k)
+    B = N.dequant_rows(pb, sb, np.arange(n), n, k)
+    brute = np.array([[sum(A[i, t] * B[c, t] for t in range(k)) for c in range(n)] for i in range(m)])
+    np.testing.assert_allclose(got, np.float64(al) * brute, rtol=1e-12, atol=1e-12)
