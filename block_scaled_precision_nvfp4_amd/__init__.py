@@ -53,6 +53,10 @@ SIGNATURES = {
     "bsp_mm_mxfp4_bias": ([_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _int, _p], _int),
     "bsp_rmsnorm_bf16": ([_p, _i64, _i64, _i64, _p, ctypes.c_float, _p, _i64, _p], _int),
     "bsp_nvfp4_quantize_rmsnorm": ([_p, _i64, _i64, _i64, _p, ctypes.c_float, _p, _p, _p, _p], _int),
+    "bsp_nvfp4_frag_bytes": ([_i64, _i64, ctypes.POINTER(_i64)], _int),
+    "bsp_nvfp4_quantize_frag": ([_p, _i64, _i64, _i64, _p, _p, _p, _p], _int),
+    "bsp_nvfp4_quantize_gelu_frag": ([_p, _i64, _i64, _i64, _p, _p, _p, _p], _int),
+    "bsp_mm_fp4_frag": ([_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _int, _p], _int),
     "bsp_mxfp4_frag_bytes": ([_i64, _i64, ctypes.POINTER(_i64), ctypes.POINTER(_i64)], _int),
     "bsp_mxfp4_quantize_frag": ([_p, _i64, _i64, _i64, _p, _p, _p], _int),
     "bsp_mm_mxfp4_frag": ([_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _int, _p], _int),
@@ -518,6 +522,87 @@ def bsp_mm_mxfp4_bias(a: torch.Tensor, a_sf: torch.Tensor, b: torch.Tensor, b_sf
     _call("bsp_mm_mxfp4_bias", a.data_ptr(), a_sf.data_ptr(), b.data_ptr(), b_sf.data_ptr(),
           _ptr(alpha), bias.data_ptr(), m, n, k, out.data_ptr(), out.stride(0), code,
           _stream(a.device))
+    return out
+
+
+# ---------------------------------------------------------------- NVFP4, MFMA fragment layout
+def bsp_nvfp4_frag_bytes(rows: int, k: int) -> int:
+    """Packed bytes of a [rows, K] operand with its values in the fragment layout (K % 64 == 0)."""
+    pb = ctypes.c_int64(0)
+    _call("bsp_nvfp4_frag_bytes", rows, k, ctypes.byref(pb))
+    return pb.value
+
+
+def bsp_nvfp4_quantize_frag(x: torch.Tensor, gsf: torch.Tensor,
+                            packed: Optional[torch.Tensor] = None,
+                            sf: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """NVFP4 of x [M, K] with the packed values in the fragment layout: (packed uint8
+    [ceil(M/32), K/64, 1024] -- one 1 KB fragment per 32-row tile and 64-K step --, sf in the 128x4
+    layout as bsp_nvfp4_quantize's)."""
+    return _nvfp4_quantize_frag("bsp_nvfp4_quantize_frag", x, gsf, packed, sf)
+
+
+def bsp_nvfp4_quantize_gelu_frag(y: torch.Tensor, gsf: torch.Tensor,
+                                 packed: Optional[torch.Tensor] = None,
+                                 sf: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """bsp_nvfp4_quantize_gelu with the packed values in the fragment layout."""
+    return _nvfp4_quantize_frag("bsp_nvfp4_quantize_gelu_frag", y, gsf, packed, sf)
+
+
+def _nvfp4_quantize_frag(fn, x, gsf, packed, sf):
+    x = _as_bf16_2d(x, "x")
+    _need(gsf, "gsf", torch.float32, x.device)
+    m, k = x.shape
+    pb = bsp_nvfp4_frag_bytes(m, k)
+    if packed is None:
+        packed = torch.empty((-(-m // 32), k // 64, 1024), dtype=torch.uint8, device=x.device)
+    if sf is None:
+        sf = torch.empty((-(-m // 128) * 128, -(-(k // 16) // 4) * 4), dtype=torch.uint8, device=x.device)
+    _need(packed, "packed", torch.uint8, x.device)
+    _need(sf, "sf", torch.uint8, x.device)
+    if packed.numel() < pb or not packed.is_contiguous():
+        raise ValueError("packed must be contiguous with bsp_nvfp4_frag_bytes(M, K) bytes")
+    if sf.numel() < bsp_nvfp4_sf_bytes(m, k) or not sf.is_contiguous():
+        raise ValueError("sf must be contiguous with bsp_nvfp4_sf_bytes(M, K) bytes")
+    _call(fn, x.data_ptr(), m, k, x.stride(0), gsf.data_ptr(), packed.data_ptr(), sf.data_ptr(),
+          _stream(x.device))
+    return packed, sf
+
+
+def bsp_mm_fp4_frag(a: torch.Tensor, a_sf: torch.Tensor, b: torch.Tensor, b_sf: torch.Tensor,
+                    m: int, n: int, alpha: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                    out_dtype: torch.dtype = torch.bfloat16,
+                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C [m, n] = alpha * A . B^T (+ bias) for operands A [m, K] and B [n, K] whose packed values are
+    in the fragment layout (as written by bsp_nvfp4_quantize_frag), scales in 128x4."""
+    _need(a, "a", torch.uint8)
+    dev = a.device
+    for t, nm in ((a_sf, "a_sf"), (b, "b"), (b_sf, "b_sf")):
+        _need(t, nm, torch.uint8, dev)
+    _need(alpha, "alpha", torch.float32, dev)
+    if a.dim() != 3 or b.dim() != 3 or a.shape[1:] != b.shape[1:] or a.shape[2] != 1024:
+        raise ValueError(f"a {tuple(a.shape)} and b {tuple(b.shape)} must be fragment tensors "
+                         "[ceil(rows/32), K/64, 1024] with the same K")
+    k = a.shape[1] * 64
+    if not (-(-m // 32) == a.shape[0] and -(-n // 32) == b.shape[0]):
+        raise ValueError(f"m={m}, n={n} do not match the fragment tensors' row tiles "
+                         f"({a.shape[0]}, {b.shape[0]})")
+    if not all(t.is_contiguous() for t in (a, a_sf, b, b_sf)):
+        raise ValueError("operands and scales must be contiguous")
+    if a_sf.numel() < bsp_nvfp4_sf_bytes(m, k) or b_sf.numel() < bsp_nvfp4_sf_bytes(n, k):
+        raise ValueError("scale buffers are smaller than bsp_nvfp4_sf_bytes")
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"out_dtype must be bf16 or fp32, got {out_dtype}")
+    code = BSP_OUT_BF16 if out_dtype == torch.bfloat16 else BSP_OUT_F32
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=dev)
+    _need(out, "out", out_dtype, dev)
+    if out.dim() != 2 or out.shape[0] != m or out.shape[1] != n or out.stride(1) != 1:
+        raise ValueError(f"out must be [{m}, {n}] with unit column stride")
+    if bias is not None:
+        _bias_vector(bias, n, torch.bfloat16, dev)
+    _call("bsp_mm_fp4_frag", a.data_ptr(), a_sf.data_ptr(), b.data_ptr(), b_sf.data_ptr(),
+          alpha.data_ptr(), _ptr(bias), m, n, k, out.data_ptr(), out.stride(0), code, _stream(dev))
     return out
 
 

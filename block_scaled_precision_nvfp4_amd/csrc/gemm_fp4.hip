@@ -415,6 +415,202 @@ __global__ __launch_bounds__(256, 1) void mm_fp4_kernel(
   }
 }
 
+
+// ---------------------------------------------------------------------------------------------
+// Fragment-layout operands (bsp_mm_fp4_frag). The packed bytes of a 32-row tile and a 64-element K
+// step are one contiguous 1 KB fragment in which the 16 bytes of lane i + 32 h are row i's
+// elements 32 h .. 32 h + 31 of the step; the scales stay in the 128x4 layout. A wave reads its
+// operands straight into registers, with no LDS staging and no barrier: per step and row tile one
+// fully coalesced 1 KB load, and per row a 2-byte load of the two scales of the lane's 32 elements
+// (blocks 4 s + 2 h and + 1; a row's dword of a 128x4 column group holds the four blocks of one
+// step). Sub-step j (0..3) of a step uses the lane's elements 8 j .. 8 j + 7, so one MFMA pairs
+// K 64 s + 8 j + (0..7) from lanes h = 0 with 64 s + 32 + 8 j + (0..7) from lanes h = 1 -- the same
+// placement for both operands -- and each lane's eight elements lie in one 16-block, whose scale
+// is byte j / 2 of its pair. Three steps of operands live in a register ring, loaded two steps
+// ahead (a step is 64 MFMAs per wave); the dequantization is interleaved with the MFMAs as in the
+// LDS-staged loop above. Against row-major operands read the same way (32 bytes of each of 32 rows
+// per load) this avoids the partial use of every 128-byte line per step.
+
+// One 64-K step of a wave's operands.
+struct StepFrags {
+  u32x4 pa[4], pb[4];     // the lane's 16 bytes in each of the wave's A and B row tiles
+  uint32_t sa[4], sb[4];  // the two scale bytes of those 32 elements (zero-extended)
+};
+
+// Where a wave's operands come from for the whole K loop.
+struct FragPlan {
+  rsrc_t fa[4], fb[4];  // per 32-row tile: its fragments over all K
+  rsrc_t qa, qb;        // the wave's 128-row scale tile over all K
+  uint32_t vo;          // lane offset inside a fragment: (i + 32 h) * 16
+  uint32_t vs;          // lane offset inside a scale tile: i * 16 + 2 h (row tile r adds 4 r)
+};
+
+// m0w, n0w: the wave's first A and B rows (multiples of 128). Tiles past an operand re-read its
+// last tile: computed, never stored.
+__device__ __forceinline__ FragPlan make_frag_plan(const uint8_t* A, const uint8_t* SA,
+                                                   const uint8_t* B, const uint8_t* SB, int64_t M,
+                                                   int64_t N, int64_t K, int64_t m0w, int64_t n0w,
+                                                   int li, int h) {
+  FragPlan p;
+  const int64_t ks = K / 64;  // fragments per row tile = 128x4 column groups
+  const int64_t mt32 = (M + 31) / 32, nt32 = (N + 31) / 32;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t ta = m0w / 32 + i < mt32 ? m0w / 32 + i : mt32 - 1;
+    const int64_t tb = n0w / 32 + i < nt32 ? n0w / 32 + i : nt32 - 1;
+    p.fa[i] = make_rsrc(A + ta * ks * 1024, ks * 1024);
+    p.fb[i] = make_rsrc(B + tb * ks * 1024, ks * 1024);
+  }
+  // scale dword of row r, column group g: (tile * groups + g) * 512 + (r % 32) * 16 + (r / 32 % 4) * 4
+  const int64_t mt = (M + 127) / 128, nt = (N + 127) / 128;
+  const int64_t ta = m0w / 128 < mt ? m0w / 128 : mt - 1;
+  const int64_t tb = n0w / 128 < nt ? n0w / 128 : nt - 1;
+  p.qa = make_rsrc(SA + ta * ks * 512, ks * 512);
+  p.qb = make_rsrc(SB + tb * ks * 512, ks * 512);
+  p.vo = (uint32_t)((li + 32 * h) * 16);
+  p.vs = (uint32_t)(li * 16 + 2 * h);
+  return p;
+}
+
+// Load u (0..15) of step s: 0-3 A fragments, 4-7 B, 8-11 A scale pairs, 12-15 B.
+__device__ __forceinline__ void load_one(StepFrags& f, const FragPlan& p, uint32_t s, int u) {
+  const int i = u & 3;
+  if (u < 4) f.pa[i] = ld16(p.fa[i], p.vo, s * 1024);
+  else if (u < 8) f.pb[i] = ld16(p.fb[i], p.vo, s * 1024);
+  else if (u < 12) f.sa[i] = ld2(p.qa, p.vs + 4 * i, s * 512);
+  else f.sb[i] = ld2(p.qb, p.vs + 4 * i, s * 512);
+}
+
+__device__ __forceinline__ void load_step(StepFrags& f, const FragPlan& p, uint32_t s) {
+#pragma unroll
+  for (int u = 0; u < 16; ++u) load_one(f, p, s, u);
+}
+
+// converts of fragment q (0-3: A row tiles, 4-7: B) of sub-step j
+__device__ __forceinline__ Raw step_cvt(const StepFrags& f, int q, int j) {
+  const uint32_t w = q < 4 ? comp(f.pa[q], j) : comp(f.pb[q - 4], j);
+  Raw r;
+  r.s = scale_pair(q < 4 ? f.sa[q] : f.sb[q - 4], j >> 1, kScaleMask);
+  r.p[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
+  r.p[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
+  r.p[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
+  r.p[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
+  return r;
+}
+
+// The dequantization pipeline between MFMA groups: xa/xb [sub-step parity][row tile] hold the f16
+// operands; fragment 7 of the next sub-step and the last converted fragment wait as Raw.
+struct DeqState {
+  f16x8 xa[2][4], xb[2][4];
+  Raw r7, rprev;
+};
+
+// Keeps each step's MFMAs in place (the builtins carry no ordering, and a step's MFMAs drifting
+// into the next would keep ring buffers live across it).
+__device__ __forceinline__ void pin_acc(f32x16 (&acc)[4][4]) {
+#pragma unroll
+  for (int n = 0; n < 4; ++n)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) asm volatile("" : "+a"(acc[n][m]));
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// One 64-K step on ring buffer BUF: its 4 sub-steps of 16 MFMAs, each interleaved with the
+// dequantization of the next sub-step (the next step's first from buffer (BUF + 1) % 3), and the
+// 16 loads of step `sl` into buffer (BUF + 2) % 3, one every other MFMA group (a burst of them
+// would stall issue).
+template <int BUF>
+__device__ __forceinline__ void frag_step(f32x16 (&acc)[4][4], StepFrags (&F)[3], DeqState& d,
+                                          const FragPlan& p, uint32_t sl) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int cb = j & 1, nb = cb ^ 1;
+    const StepFrags& nf = F[j < 3 ? BUF : (BUF + 1) % 3];
+    const int nj = (j + 1) & 3;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      __builtin_amdgcn_sched_barrier(0);
+      if ((q & 1) == 0) {
+        load_one(F[(BUF + 2) % 3], p, sl, 4 * j + (q >> 1));
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+      const int n = q >> 1, m = 2 * (q & 1);
+      acc[n][m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(d.xb[cb][n], d.xa[cb][m], acc[n][m], 0, 0, 0);
+      acc[n][m + 1] =
+          __builtin_amdgcn_mfma_f32_32x32x16_f16(d.xb[cb][n], d.xa[cb][m + 1], acc[n][m + 1], 0, 0, 0);
+      const Raw rq = step_cvt(nf, q, nj);
+      if (q == 0) {
+        d.xb[cb][3] = raw_mul(d.r7);  // needed by groups 6-7 of this sub-step
+      } else {
+        const f16x8 v = raw_mul(d.rprev);
+        if (q - 1 < 4) d.xa[nb][q - 1] = v; else d.xb[nb][q - 5] = v;
+      }
+      if (q == 7) d.r7 = rq; else d.rprev = rq;
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+    }
+  }
+  pin_acc(acc);
+}
+
+// BIAS: kBiasNone or kBiasBf16After (as bsp_mm_fp4_bias).
+template <bool OUT_F32, int BIAS>
+__global__ __launch_bounds__(256, 1) void mm_fp4_frag_kernel(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint8_t* __restrict__ B,
+    const uint8_t* __restrict__ SB, const float* __restrict__ alpha_ptr, int64_t M, int64_t N,
+    int64_t K, void* __restrict__ out, int64_t ldc, int ntm, int ntn, bool vec_store,
+    const void* __restrict__ bias) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kEpiWaveBytes];  // epilogue images only
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int li = lane & 31, h = lane >> 5;
+
+  int tm, tn;
+  tile_coords(blockIdx.x, ntm, ntn, tm, tn);
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int64_t KS = K / 64;
+  const FragPlan p = make_frag_plan(A, SA, B, SB, M, N, K, m0 + wm * 128, n0 + wn * 128, li, h);
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+
+  StepFrags F[3];
+  load_step(F[0], p, 0);
+  load_step(F[1], p, KS > 1 ? 1 : 0);
+  DeqState d;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    d.xa[0][i] = raw_mul(step_cvt(F[0], i, 0));
+    if (i < 3) d.xb[0][i] = raw_mul(step_cvt(F[0], 4 + i, 0));
+  }
+  d.r7 = step_cvt(F[0], 7, 0);
+  d.rprev = d.r7;
+
+  // steps run in groups of three (the ring period); loads past the end repeat the last step
+  int64_t s = 0;
+  for (; s + 3 <= KS; s += 3) {
+    frag_step<0>(acc, F, d, p, (uint32_t)(s + 2 < KS ? s + 2 : KS - 1));
+    frag_step<1>(acc, F, d, p, (uint32_t)(s + 3 < KS ? s + 3 : KS - 1));
+    frag_step<2>(acc, F, d, p, (uint32_t)(s + 4 < KS ? s + 4 : KS - 1));
+  }
+  if (s < KS) frag_step<0>(acc, F, d, p, (uint32_t)(KS - 1));
+  if (s + 1 < KS) frag_step<1>(acc, F, d, p, (uint32_t)(KS - 1));
+  wait_vmcnt<0>();
+
+  // operands carried 2^-8 each (scale_pair): the accumulators hold 2^-16 of the true sums, which
+  // the epilogue undoes on the accumulator (ACC16)
+  const float a = *alpha_ptr;
+  const float alpha[4] = {a, a, a, a};
+  store_tile<OUT_F32, BIAS, true>(acc, alpha, m0, n0, wm, wn, M, N, out, ldc, vec_store, lds, wave,
+                                  lane, li, h, bias);
+}
+
 }  // namespace fp4
 
 template <bool ROWSCALE, bool SFA8, int BIAS = kBiasNone>
@@ -440,6 +636,23 @@ static void launch_mm_fp4_t(const uint8_t* a, const uint8_t* sa, const uint8_t* 
     hipLaunchKernelGGL((fp4::mm_fp4_kernel<false, ROWSCALE, SFA8, BIAS>), dim3((unsigned)tiles), dim3(256),
                        0, s, a, sa, b, sb, alpha, w_gsf, M, N, K, out, ldc, (int)ntm, (int)ntn, vec,
                        rows8, bias, sf_out, out_gsf);
+}
+
+template <int BIAS>
+static void launch_mm_fp4_frag_t(const uint8_t* a, const uint8_t* sa, const uint8_t* b,
+                                 const uint8_t* sb, const float* alpha, int64_t M, int64_t N,
+                                 int64_t K, void* out, int64_t ldc, int out_dtype, hipStream_t s,
+                                 const void* bias) {
+  const int64_t ntm = ceil_div(M, fp4::BM), ntn = ceil_div(N, fp4::BN);
+  const int64_t tiles = ntm * ntn;
+  const size_t esz = out_dtype == BSP_OUT_F32 ? 4 : 2;
+  const bool vec = (ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(out) & (4 * esz - 1)) == 0);
+  if (out_dtype == BSP_OUT_F32)
+    hipLaunchKernelGGL((fp4::mm_fp4_frag_kernel<true, BIAS>), dim3((unsigned)tiles), dim3(256), 0, s, a,
+                       sa, b, sb, alpha, M, N, K, out, ldc, (int)ntm, (int)ntn, vec, bias);
+  else
+    hipLaunchKernelGGL((fp4::mm_fp4_frag_kernel<false, BIAS>), dim3((unsigned)tiles), dim3(256), 0, s, a,
+                       sa, b, sb, alpha, M, N, K, out, ldc, (int)ntm, (int)ntn, vec, bias);
 }
 
 }  // namespace bsp
@@ -544,4 +757,20 @@ extern "C" int bsp_mm_fp4_per_token(const uint8_t* a_packed, const uint8_t* a_sf
   launch_mm_fp4_t<true, false>(a_packed, a_sf, b_packed, b_sf, x_gsf_rows, w_gsf_dev, M, N, K, out,
                                ldc, out_dtype, (hipStream_t)stream);
   return check_launch("bsp_mm_fp4_per_token");
+}
+
+extern "C" int bsp_mm_fp4_frag(const uint8_t* a_packed, const uint8_t* a_sf, const uint8_t* b_packed,
+                               const uint8_t* b_sf, const float* alpha_dev, const void* bias_bf16,
+                               int64_t M, int64_t N, int64_t K, void* out, int64_t ldc, int out_dtype,
+                               void* stream) {
+  int e = mm_fp4_checks("bsp_mm_fp4_frag", a_packed, a_sf, b_packed, b_sf, alpha_dev, M, N, K, out, ldc,
+                        out_dtype, bias_bf16, bias_bf16 ? 2 : 0);
+  if (e) return e > 0 ? BSP_OK : e;
+  if (bias_bf16)
+    launch_mm_fp4_frag_t<kBiasBf16After>(a_packed, a_sf, b_packed, b_sf, alpha_dev, M, N, K, out, ldc,
+                                         out_dtype, (hipStream_t)stream, bias_bf16);
+  else
+    launch_mm_fp4_frag_t<kBiasNone>(a_packed, a_sf, b_packed, b_sf, alpha_dev, M, N, K, out, ldc,
+                                    out_dtype, (hipStream_t)stream, nullptr);
+  return check_launch("bsp_mm_fp4_frag");
 }

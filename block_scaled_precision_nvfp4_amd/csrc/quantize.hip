@@ -139,6 +139,14 @@ __global__ void alpha_kernel(const float* xg, const float* wg, float* alpha) {
 // saturating at +-6, sign of zero kept -- checked against the software encoder on every fp32
 // input class (ties, denormals, huge values) on gfx950; BSP_QUANT_SW_CVT=1 selects that software
 // encoder instead.
+//
+// FRAG: the packed values in the fragment layout (K % 64 == 0; described at
+// bsp_nvfp4_quantize_frag), the scales still in 128x4. The workgroup's 128 rows x 256 K are 4 row
+// tiles x 4 K steps, sixteen 1 KB fragments staged in LDS and stored as four contiguous 4 KB runs
+// (steps past K are not stored). A thread's 4 bytes for row rr lie in 16-byte chunk
+// p = (rr/32)*256 + cb*32 + rr%32 of the staging area (cb = (t % 32) / 4 = 2 * K step + lane half),
+// placed at chunk p ^ 2cb: the eight 32-element blocks of a row otherwise sit 512 bytes apart, all
+// in one LDS bank.
 template <bool VEC>
 __device__ __forceinline__ uint4 load8(const uint16_t* p) {
   if (VEC) return load16_nt(p);
@@ -150,7 +158,7 @@ __device__ __forceinline__ uint4 load8(const uint16_t* p) {
   return v;
 }
 
-template <bool HWCVT, bool VEC, bool GELU, bool WIDE>
+template <bool HWCVT, bool VEC, bool GELU, bool WIDE, bool FRAG = false>
 __global__ __launch_bounds__(256) void nvfp4_quantize_kernel(const uint16_t* __restrict__ x,
                                                              int64_t M, int64_t K, int64_t ld,
                                                              const float* __restrict__ gsf,
@@ -158,8 +166,9 @@ __global__ __launch_bounds__(256) void nvfp4_quantize_kernel(const uint16_t* __r
                                                              uint8_t* __restrict__ sf, int64_t Kp,
                                                              int64_t rows8) {
   __shared__ uint4 sf_tile[128];  // 2 KB = 4 scale tiles of 512 B
-  // WIDE: the tile's packed bytes (128 rows x 128 B), stored as 16-byte pieces
-  __shared__ __attribute__((aligned(16))) uint32_t pimg[WIDE ? 128 * 32 : 1];
+  // WIDE: the tile's packed bytes (128 rows x 128 B), stored as 16-byte pieces; FRAG: its 16
+  // fragments
+  __shared__ __attribute__((aligned(16))) uint32_t pimg[WIDE || FRAG ? 128 * 32 : 1];
   __shared__ float rtab[128];     // fl32(g / e4m3(c)) for code c (0 for c == 0)
   __shared__ __attribute__((aligned(16))) uint16_t gtab[GELU ? kGeluTabSize : 8];
   uint8_t* sfb = reinterpret_cast<uint8_t*>(sf_tile);
@@ -212,7 +221,11 @@ __global__ __launch_bounds__(256) void nvfp4_quantize_kernel(const uint16_t* __r
       for (int i = 0; i < 8; ++i) out |= e2m1_encode(f[i] * r) << (4 * i);
     }
     const int rr = s * 8 + rsub;  // row inside the 128-row tile
-    if (wide) pimg[rr * 32 + (t & 31)] = out;
+    if (FRAG) {
+      const int cb = (t & 31) >> 2;
+      const int p = (rr >> 5) * 256 + cb * 32 + (rr & 31);
+      pimg[(p ^ (cb << 1)) * 4 + (t & 3)] = out;
+    } else if (wide) pimg[rr * 32 + (t & 31)] = out;
     else if (full || (kin && row0 + rr < M)) store4_nt(pp + s * pstep, out);
     if ((t & 1) == 0) {
       const int cb = (t & 31) >> 1;  // scale column inside the 16-column tile
@@ -220,7 +233,22 @@ __global__ __launch_bounds__(256) void nvfp4_quantize_kernel(const uint16_t* __r
     }
   }
   __syncthreads();
-  if (wide) {   // each row's 128 bytes as eight 16-byte pieces
+  if (FRAG) {
+    // row tiles past ceil(M / 32) are not part of the buffer; padded rows inside the last one were
+    // encoded from zeros
+    const int64_t row_tiles = (M + 31) / 32, rt0 = (int64_t)blockIdx.y * 4;
+    const int64_t ks = K / 64, ks0 = (int64_t)blockIdx.x * 4;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int p = it * 256 + t;   // chunk (p & 255) of row tile it: K step (p >> 6) & 3, lane p & 63
+      if (rt0 + it < row_tiles && ks0 + ((p >> 6) & 3) < ks) {
+        const uint4 w = reinterpret_cast<const uint4*>(pimg)[p ^ (((p >> 5) & 7) << 1)];
+        __builtin_nontemporal_store(
+            (nt_u32x4){w.x, w.y, w.z, w.w},
+            reinterpret_cast<nt_u32x4*>(packed + ((rt0 + it) * ks + ks0) * 1024) + (p & 255));
+      }
+    }
+  } else if (wide) {   // each row's 128 bytes as eight 16-byte pieces
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int p = t + 256 * i, rr = p >> 3, part = p & 7;
@@ -851,7 +879,23 @@ int launch_global_sf(const void* w, int64_t rows, int64_t K, int64_t ld, float* 
 template <bool GELU>
 static void launch_nvfp4_quantize_t(dim3 grid, const uint16_t* xp, int64_t M, int64_t K, int64_t ld,
                                     const float* gsf, uint8_t* packed, uint8_t* sf, int64_t Kp,
-                                    int64_t rows8, bool hw, bool vec, bool wide, hipStream_t s) {
+                                    int64_t rows8, bool hw, bool vec, bool wide, bool frag,
+                                    hipStream_t s) {
+  if (frag) {
+    if (hw && vec)
+      hipLaunchKernelGGL((nvfp4_quantize_kernel<true, true, GELU, false, true>), grid, dim3(256), 0, s, xp,
+                         M, K, ld, gsf, packed, sf, Kp, rows8);
+    else if (hw)
+      hipLaunchKernelGGL((nvfp4_quantize_kernel<true, false, GELU, false, true>), grid, dim3(256), 0, s, xp,
+                         M, K, ld, gsf, packed, sf, Kp, rows8);
+    else if (vec)
+      hipLaunchKernelGGL((nvfp4_quantize_kernel<false, true, GELU, false, true>), grid, dim3(256), 0, s, xp,
+                         M, K, ld, gsf, packed, sf, Kp, rows8);
+    else
+      hipLaunchKernelGGL((nvfp4_quantize_kernel<false, false, GELU, false, true>), grid, dim3(256), 0, s,
+                         xp, M, K, ld, gsf, packed, sf, Kp, rows8);
+    return;
+  }
   wide = wide && !GELU;
   if (hw && vec && wide)
     hipLaunchKernelGGL((nvfp4_quantize_kernel<true, true, GELU, true>), grid, dim3(256), 0, s, xp, M, K,
@@ -873,9 +917,11 @@ static void launch_nvfp4_quantize_t(dim3 grid, const uint16_t* xp, int64_t M, in
                        K, ld, gsf, packed, sf, Kp, rows8);
 }
 
-// layout8: scales in layout_8x4 (rows padded to 8) instead of 128x4
+// layout8: scales in layout_8x4 (rows padded to 8) instead of 128x4; frag: packed values in the
+// fragment layout (K % 64 == 0, scales in 128x4)
 int launch_nvfp4_quantize(const void* x, int64_t M, int64_t K, int64_t ld, const float* gsf,
-                          uint8_t* packed, uint8_t* sf, hipStream_t s, bool gelu, bool layout8) {
+                          uint8_t* packed, uint8_t* sf, hipStream_t s, bool gelu, bool layout8,
+                          bool frag) {
   const int64_t Mp = ceil_div(M, 128) * 128;
   const int64_t Kp = ceil_div(K / 16, 4) * 4;
   dim3 grid((unsigned)ceil_div(Kp, 16), (unsigned)(Mp / 128));
@@ -885,9 +931,10 @@ int launch_nvfp4_quantize(const void* x, int64_t M, int64_t K, int64_t ld, const
   const int64_t rows8 = layout8 ? ceil_div(M, 8) * 8 : 0;
   const bool wide = K % 32 == 0 && aligned16(packed);
   if (gelu)
-    launch_nvfp4_quantize_t<true>(grid, xp, M, K, ld, gsf, packed, sf, Kp, rows8, hw, vec, wide, s);
+    launch_nvfp4_quantize_t<true>(grid, xp, M, K, ld, gsf, packed, sf, Kp, rows8, hw, vec, wide, frag, s);
   else
-    launch_nvfp4_quantize_t<false>(grid, xp, M, K, ld, gsf, packed, sf, Kp, rows8, hw, vec, wide, s);
+    launch_nvfp4_quantize_t<false>(grid, xp, M, K, ld, gsf, packed, sf, Kp, rows8, hw, vec, wide, frag, s);
+  if (frag) return check_launch(gelu ? "bsp_nvfp4_quantize_gelu_frag" : "bsp_nvfp4_quantize_frag");
   return check_launch(gelu ? "bsp_nvfp4_quantize_gelu"
                            : (layout8 ? "bsp_nvfp4_quantize_8x4" : "bsp_nvfp4_quantize"));
 }
@@ -1046,9 +1093,10 @@ extern "C" int bsp_nvfp4_quantize_rmsnorm(const void* x, int64_t M, int64_t K, i
 
 static int nvfp4_quantize_entry(const char* fn, const void* x, int64_t M, int64_t K, int64_t ld,
                                 const float* gsf, uint8_t* packed, uint8_t* sf, void* stream, bool gelu,
-                                bool layout8 = false) {
+                                bool layout8 = false, bool frag = false) {
   BSP_REQUIRE(M >= 0 && K > 0, BSP_EINVAL, "%s: bad size M=%lld K=%lld", fn, (long long)M, (long long)K);
   BSP_REQUIRE(K % 16 == 0, BSP_ESHAPE, "%s: K (%lld) must be a multiple of 16", fn, (long long)K);
+  BSP_REQUIRE(!frag || K % 64 == 0, BSP_ESHAPE, "%s: K (%lld) must be a multiple of 64", fn, (long long)K);
   BSP_REQUIRE(M <= 1 || ld >= K, BSP_ESHAPE, "%s: ld (%lld) < K (%lld)", fn, (long long)ld, (long long)K);
   if (M == 0) return BSP_OK;
   BSP_REQUIRE(x && gsf && packed && sf, BSP_EINVAL, "%s: null pointer", fn);
@@ -1056,9 +1104,32 @@ static int nvfp4_quantize_entry(const char* fn, const void* x, int64_t M, int64_
   const uintptr_t sf_mask = layout8 ? 3u : 15u;
   BSP_REQUIRE((reinterpret_cast<uintptr_t>(packed) & 3u) == 0 && (reinterpret_cast<uintptr_t>(sf) & sf_mask) == 0,
               BSP_EINVAL, "%s: packed must be 4-byte and sf %d-byte aligned", fn, layout8 ? 4 : 16);
+  BSP_REQUIRE(!frag || aligned16(packed), BSP_EINVAL, "%s: packed must be 16-byte aligned", fn);
   BSP_REQUIRE(ceil_div(M, 128) < 65536, BSP_ESHAPE, "%s: M too large", fn);
   if (int e = check_device()) return e;
-  return launch_nvfp4_quantize(x, M, K, ld, gsf, packed, sf, (hipStream_t)stream, gelu, layout8);
+  return launch_nvfp4_quantize(x, M, K, ld, gsf, packed, sf, (hipStream_t)stream, gelu, layout8, frag);
+}
+
+extern "C" int bsp_nvfp4_frag_bytes(int64_t rows, int64_t K, int64_t* packed_bytes) {
+  BSP_REQUIRE(packed_bytes, BSP_EINVAL, "bsp_nvfp4_frag_bytes: null output pointer");
+  BSP_REQUIRE(rows >= 0 && K >= 0, BSP_EINVAL, "bsp_nvfp4_frag_bytes: negative size");
+  BSP_REQUIRE(K % 64 == 0, BSP_ESHAPE, "bsp_nvfp4_frag_bytes: K (%lld) must be a multiple of 64",
+              (long long)K);
+  *packed_bytes = ceil_div(rows, 32) * 32 * (K / 2);
+  return BSP_OK;
+}
+
+extern "C" int bsp_nvfp4_quantize_frag(const void* x, int64_t M, int64_t K, int64_t ld, const float* gsf,
+                                       uint8_t* packed, uint8_t* sf, void* stream) {
+  return nvfp4_quantize_entry("bsp_nvfp4_quantize_frag", x, M, K, ld, gsf, packed, sf, stream, false,
+                              false, true);
+}
+
+extern "C" int bsp_nvfp4_quantize_gelu_frag(const void* y, int64_t M, int64_t K, int64_t ld,
+                                            const float* gsf, uint8_t* packed, uint8_t* sf,
+                                            void* stream) {
+  return nvfp4_quantize_entry("bsp_nvfp4_quantize_gelu_frag", y, M, K, ld, gsf, packed, sf, stream, true,
+                              false, true);
 }
 
 extern "C" int bsp_nvfp4_quantize(const void* x, int64_t M, int64_t K, int64_t ld, const float* gsf,

@@ -280,6 +280,39 @@ int bsp_mm_mxfp4_bias(const uint8_t* a_packed, const uint8_t* a_sf, const uint8_
                       const uint8_t* b_sf, const float* alpha_dev, const void* bias_bf16, int64_t M,
                       int64_t N, int64_t K, void* out, int64_t ldc, int out_dtype, void* stream);
 
+/* NVFP4 with the packed values in a fragment layout. [FV-NV] _nvfp4_quantize passes a do_shuffle
+ * switch to its quantizer: operands pre-arranged for the matrix unit, the arrangement being the
+ * library's (the pages always pass False). Here a 32-row tile's 64-element K step is one
+ * contiguous 1 KB that a wave reads with one load, lane l = i + 32 h taking row i's elements
+ * 32 h .. 32 h + 31 of the step. Same codes and scale bytes as bsp_nvfp4_quantize; only the order
+ * of the packed bytes differs, and the scales stay in the 128x4 layout (bsp_nvfp4_sf_bytes).
+ * Operand [R, K], K % 64 == 0, Rp = ceil(R/32)*32 rows (rows R..Rp-1 zero):
+ *  packed (Rp*K/2 bytes): byte 16 l + c of the fragment at (rt*(K/64) + ks)*1024 holds elements
+ *    64 ks + 32 h + 2c, +1 (low nibble first) of row 32 rt + i.
+ * bsp_nvfp4_frag_bytes: the packed size (BSP_ESHAPE unless K % 64 == 0; NULL: BSP_EINVAL). */
+int bsp_nvfp4_frag_bytes(int64_t rows, int64_t K, int64_t* packed_bytes);
+
+/* bsp_nvfp4_quantize (and bsp_nvfp4_quantize_gelu) writing the packed values in the fragment
+ * layout. x: device bf16 [M, K] (row stride ld), K % 64 == 0 (else BSP_ESHAPE); packed
+ * (bsp_nvfp4_frag_bytes(M, K) bytes) and sf (128x4, bsp_nvfp4_sf_bytes(M, K) bytes) 16-byte
+ * aligned (else BSP_EINVAL); every byte of both, padding included, is written. Other arguments and
+ * errors as bsp_nvfp4_quantize. Weights take bsp_nvfp4_global_sf, then bsp_nvfp4_quantize_frag. */
+int bsp_nvfp4_quantize_frag(const void* x_bf16, int64_t M, int64_t K, int64_t ld, const float* gsf_dev,
+                            uint8_t* packed, uint8_t* sf, void* stream);
+int bsp_nvfp4_quantize_gelu_frag(const void* y_bf16, int64_t M, int64_t K, int64_t ld,
+                                 const float* gsf_dev, uint8_t* packed, uint8_t* sf, void* stream);
+
+/* bsp_mm_fp4 on fragment-layout packed operands (scales in 128x4): C = alpha * A . B^T, plus the
+ * bias as in bsp_mm_fp4_bias when bias_bf16 (device bf16 [N], 2-byte aligned) is not NULL.
+ * a_packed: A [M, K] and b_packed: B [N, K] (K-major weight) in the fragment layout; out [M, N]
+ * row stride ldc, bf16 or fp32. The same products as bsp_mm_fp4, summed in another order inside
+ * each 64-element step (the output may differ from bsp_mm_fp4's by fp32 rounding). Requires
+ * K % 64 == 0 and K <= 2^24 (else BSP_ESHAPE); operands and scales 16-byte aligned, no NULL
+ * operand, scale or alpha pointer (else BSP_EINVAL); out_dtype as bsp_mm_fp4. */
+int bsp_mm_fp4_frag(const uint8_t* a_packed, const uint8_t* a_sf, const uint8_t* b_packed,
+                    const uint8_t* b_sf, const float* alpha_dev, const void* bias_bf16, int64_t M,
+                    int64_t N, int64_t K, void* out, int64_t ldc, int out_dtype, void* stream);
+
 /* MXFP4 in the MFMA fragment layout. [FV-NV] _nvfp4_quantize passes a do_shuffle switch to its
  * quantizer: operands pre-arranged for the matrix unit, the arrangement being the library's (the
  * pages always pass False). This is that arrangement for gfx950's block-scaled MFMA

@@ -317,3 +317,40 @@ def test_mxfp8_frag_entry_points():
     assert st not in (-1, -2, -3), st
     st, msg = _st(g, P, P, P, P, None, 4, 4, (1 << 24) + 256, P, 4, 0, None)
     assert st == -2 and "at most" in msg
+
+
+def test_nvfp4_frag_entry_points():
+    """Fragment-layout NVFP4: sizes, and every argument rule rejected on the host before a launch."""
+    pb = ctypes.c_int64(0)
+    assert bsp.lib().bsp_nvfp4_frag_bytes(33, 192, ctypes.byref(pb)) == 0 and pb.value == 64 * 96
+    assert bsp.lib().bsp_nvfp4_frag_bytes(0, 64, ctypes.byref(pb)) == 0 and pb.value == 0
+    assert bsp.lib().bsp_nvfp4_frag_bytes(4, 96, ctypes.byref(pb)) == -2
+    assert bsp.lib().bsp_nvfp4_frag_bytes(4, 64, None) == -1
+    assert bsp.bsp_nvfp4_frag_bytes(32760, 5120) == 32768 * 2560
+    for q in ("bsp_nvfp4_quantize_frag", "bsp_nvfp4_quantize_gelu_frag"):
+        st, msg = _st(q, P, 4, 96, 96, P, P, P, None)
+        assert st == -2 and "multiple of 64" in msg, q
+        assert _st(q, P, 4, 24, 24, P, P, P, None)[0] == -2             # not even a multiple of 16
+        assert _st(q, P, 4, 128, 64, P, P, P, None)[0] == -2            # ld < K
+        assert _st(q, None, 4, 128, 128, P, P, P, None)[0] == -1
+        assert _st(q, P, 4, 128, 128, None, P, P, None)[0] == -1        # gsf
+        assert _st(q, P, 4, 128, 128, P, ctypes.c_void_p(20), P, None)[0] == -1   # packed 4- not 16-aligned
+        assert _st(q, P, 4, 128, 128, P, P, ctypes.c_void_p(24), None)[0] == -1   # sf not 16-aligned
+        assert _st(q, P, 65535 * 128 + 1, 128, 128, P, P, P, None)[0] == -2
+        assert _st(q, None, 0, 128, 128, None, None, None, None)[0] == 0      # M == 0: no-op
+    g = "bsp_mm_fp4_frag"
+    st, msg = _st(g, P, P, P, P, P, None, 4, 4, 96, P, 4, 0, None)
+    assert st == -2 and "multiple of 64" in msg
+    assert _st(g, P, P, P, P, P, None, 4, 4, 64, P, 4, 2, None)[0] == -3   # bad out dtype
+    assert _st(g, P, P, P, P, P, None, 4, 8, 64, P, 4, 0, None)[0] == -2   # ldc < N
+    assert _st(g, ctypes.c_void_p(24), P, P, P, P, None, 4, 4, 64, P, 4, 0, None)[0] == -1
+    assert _st(g, P, ctypes.c_void_p(20), P, P, P, None, 4, 4, 64, P, 4, 0, None)[0] == -1
+    assert _st(g, P, P, P, ctypes.c_void_p(20), P, None, 4, 4, 64, P, 4, 0, None)[0] == -1
+    assert _st(g, P, P, P, P, None, None, 4, 4, 64, P, 4, 0, None)[0] == -1   # alpha
+    assert _st(g, P, P, P, P, P, ctypes.c_void_p(17), 4, 4, 64, P, 4, 0, None)[0] == -1   # bias
+    assert _st(g, None, None, None, None, None, None, 0, 4, 64, None, 4, 0, None)[0] == 0
+    # the aligned call passes validation and fails only for want of a gfx950 device here
+    st = _st(g, P, P, P, P, P, ctypes.c_void_p(18), 4, 4, 64, P, 4, 0, None)[0]
+    assert st not in (-1, -2, -3), st
+    st, msg = _st(g, P, P, P, P, P, None, 4, 4, (1 << 24) + 64, P, 4, 0, None)
+    assert st == -2 and "at most" in msg

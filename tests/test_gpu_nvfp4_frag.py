@@ -1,0 +1,177 @@
+"""GPU parity of the NVFP4 fragment-layout path (bsp_nvfp4_quantize_frag,
+bsp_nvfp4_quantize_gelu_frag, bsp_mm_fp4_frag).
+
+The quantizers must write exactly the oracle's bytes: the packed values in the fragment layout
+(zero padding rows included) and the scales in the 128x4 layout. The GELU-fused one meets the bar of
+bsp_nvfp4_quantize_gelu against the oracle's GELU-then-quantize chain. The GEMM meets mm_fp4's bar
+against the oracle's fp64 product of the same operand bytes (it sums the same exact products in
+another order, so it is not compared bit for bit with bsp_mm_fp4). Small and ragged shapes compare
+every element; the Wan-14B fc_in shape (32760 x 13824 x 5120) runs at full size and compares
+sampled entries.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_precision_nvfp4_amd as bsp
+import workloads as W
+from oracle import activations as A
+from oracle import linear as L
+from oracle import nvfp4 as N
+from tests.gpu_util import (REL_FRO_FP4_F32, assert_gemm_bf16, assert_nvfp4_of_gelu,
+                            check_gemm_outputs, dev_bf16, dev_u8, gather, host_u8,
+                            oracle_linear_entries, sample_entries, say, scalar, tensor_bits)
+
+pytestmark = pytest.mark.gpu
+f32 = np.float32
+
+
+def _filled(fn, xb: np.ndarray, gsf):
+    """fn into buffers pre-filled with 0xA5, so a byte left unwritten shows: flat (packed, sf)."""
+    m, k = xb.shape
+    p = torch.full((N.frag_rows(m) // 32, k // 64, 1024), 0xA5, dtype=torch.uint8, device="cuda")
+    rp, cp = N.sf_padded_shape(m, k)
+    s = torch.full((rp, cp), 0xA5, dtype=torch.uint8, device="cuda")
+    fn(dev_bf16(xb), scalar(gsf), p, s)
+    return host_u8(p).ravel(), host_u8(s).ravel()
+
+
+@pytest.mark.parametrize("m,k", [(1, 64), (33, 192), (128, 256), (130, 320), (45, 64), (300, 1536),
+                                 (257, 2048)])
+@pytest.mark.parametrize("gsf_kind", ["static", "weight"])
+def test_nvfp4_quantize_frag_bit_exact(m, k, gsf_kind):
+    say("nvfp4_quantize_frag", m, k, gsf_kind)
+    for xb in (W.small_case(m, k, seed=5 * m + k, outlier_frac=0.02),
+               W.special_values_block(seed=m + 3, rows=m, cols=k),
+               W.nonfinite_block(seed=m + 4, rows=m, cols=k)):
+        g = f32(1.0) if gsf_kind == "static" else N.global_sf(xb)[0]
+        fp, fs = _filled(bsp.bsp_nvfp4_quantize_frag, xb, g)
+        rp, rs = N.quantize(xb, g, packed_layout="frag")
+        assert np.array_equal(fp, rp) and np.array_equal(fs, rs)
+
+
+def test_nvfp4_quantize_frag_strided_input():
+    """A row stride larger than K (a column slice of a wider matrix)."""
+    xb = W.small_case(70, 1024, seed=9, outlier_frac=0.02)
+    p, s = bsp.bsp_nvfp4_quantize_frag(dev_bf16(xb)[:, :704], scalar(0.5))
+    rp, rs = N.quantize(np.ascontiguousarray(xb[:, :704]), f32(0.5), packed_layout="frag")
+    assert np.array_equal(host_u8(p).ravel(), rp) and np.array_equal(host_u8(s).ravel(), rs)
+
+
+@pytest.mark.parametrize("m,k", [(1, 64), (77, 192), (129, 320), (300, 1536)])
+@pytest.mark.parametrize("gsf", [1.0, 0.37])
+def test_nvfp4_quantize_gelu_frag_matches_oracle_chain(m, k, gsf):
+    """Against the oracle's GELU-then-quantize of the same bf16 y (bit-exact in every block with no
+    rounding-ambiguous GELU value); padding rows zero; and the same codes and scales as
+    bsp_nvfp4_quantize_gelu, in the fragment order."""
+    say("nvfp4_quantize_gelu_frag", m, k, gsf)
+    yb = W.small_case(m, k, seed=3 * m + k + 1, std=2.5, outlier_frac=0.02)
+    fp, fs = _filled(bsp.bsp_nvfp4_quantize_gelu_frag, yb, gsf)
+    rp_, cp_ = N.sf_padded_shape(m, k)
+    lin = N.unswizzle_128x4(fs, rp_, cp_)
+    assert_nvfp4_of_gelu(N.from_frag_packed(fp, m, k), lin, yb, gsf, f"quantize_gelu_frag {m}x{k}")
+    assert not lin[m:].any()
+    pad = N.frag_packed_offset(np.arange(m, N.frag_rows(m))[:, None], np.arange(k // 2)[None, :], k)
+    assert not fp[pad].any()
+    p2, s2 = bsp.bsp_nvfp4_quantize_gelu(dev_bf16(yb), scalar(gsf))
+    assert np.array_equal(N.from_frag_packed(fp, m, k), host_u8(p2))
+    assert np.array_equal(fs, host_u8(s2).ravel())
+
+
+def _rand_operand(rng, rows, k):
+    """Random codes and 128x4 scales (subnormal scales included): (fragment-layout packed, packed
+    [rows, K/2], flat 128x4 scales)."""
+    packed = rng.integers(0, 256, size=(rows, k // 2)).astype(np.uint8)
+    rp, cp = N.sf_padded_shape(rows, k)
+    lin = np.zeros((rp, cp), dtype=np.uint8)
+    lin[:rows, : k // 16] = rng.integers(0, 0x7F, size=(rows, k // 16))
+    return N.to_frag_packed(packed, k), packed, N.swizzle_128x4(lin)
+
+
+def _dev_frag(fp: np.ndarray, rows: int, k: int) -> torch.Tensor:
+    return dev_u8(fp.reshape(N.frag_rows(rows) // 32, k // 64, 1024))
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 64, 64), (77, 200, 192), (256, 256, 512), (300, 130, 320),
+                                   (513, 384, 1280), (3, 1, 64), (1, 1, 128), (260, 520, 2304)])
+def test_mm_fp4_frag_random_operands_all_elements(m, n, k):
+    say("mm_fp4_frag random", m, n, k)
+    rng = np.random.default_rng(m * 5 + n * 3 + k)
+    fa, _, sa = _rand_operand(rng, m, k)
+    fb, _, sb = _rand_operand(rng, n, k)
+    al = f32(rng.uniform(0.01, 2.0))
+    ref = N.mm_fp4_frag(fa, sa, fb, sb, al, m, n, k)
+    a, b = _dev_frag(fa, m, k), _dev_frag(fb, n, k)
+    t32 = bsp.bsp_mm_fp4_frag(a, dev_u8(sa), b, dev_u8(sb), m, n, scalar(al), out_dtype=torch.float32)
+    t16 = bsp.bsp_mm_fp4_frag(a, dev_u8(sa), b, dev_u8(sb), m, n, scalar(al))
+    check_gemm_outputs(t16, t32, ref, f"fp4 frag {m}x{n}x{k}", f32_tol=REL_FRO_FP4_F32)
+
+
+@pytest.mark.parametrize("m,n,k", [(77, 200, 192), (256, 256, 512), (300, 130, 64)])
+def test_mm_fp4_frag_bias(m, n, k):
+    """With a bias: the bf16 output equals the no-bias output plus the bias (torch's bf16 add, the
+    pages' out + bias) bit for bit, and the fp32 output the fp32 product plus the bias."""
+    say("mm_fp4_frag bias", m, n, k)
+    rng = np.random.default_rng(m + 7 * n + k)
+    fa, _, sa = _rand_operand(rng, m, k)
+    fb, _, sb = _rand_operand(rng, n, k)
+    al = f32(0.75)
+    ref = N.mm_fp4_frag(fa, sa, fb, sb, al, m, n, k)
+    v = (rng.standard_normal(n) * (float(np.std(ref)) + 1e-30)).astype(np.float32)
+    v[::7] = 0.0
+    bbits = W.f32_to_bf16_bits(v)
+    bias = dev_bf16(bbits)
+    args = (_dev_frag(fa, m, k), dev_u8(sa), _dev_frag(fb, n, k), dev_u8(sb), m, n, scalar(al))
+    t16 = bsp.bsp_mm_fp4_frag(*args)
+    tb16 = bsp.bsp_mm_fp4_frag(*args, bias)
+    assert torch.equal(tb16.view(torch.int16), (t16.float() + bias.float()).bfloat16().view(torch.int16))
+    t32 = bsp.bsp_mm_fp4_frag(*args, out_dtype=torch.float32)
+    want = W.bf16_bits_to_f32(L.add_bias_bf16(A.f64_to_bf16_bits(ref), bbits)).astype(np.float64)
+    assert_gemm_bf16(tb16.float().cpu().numpy().astype(np.float64), want, t32.cpu().numpy(),
+                     f"fp4 frag bias {m}x{n}x{k}")
+    tb32 = bsp.bsp_mm_fp4_frag(*args, bias, out_dtype=torch.float32)
+    assert torch.equal(tb32, t32 + bias.float())
+
+
+def test_nvfp4_frag_full_size_fc_in():
+    """Wan-14B fc_in, 32760 x 13824 x 5120, in the bench's launch configuration: X quantized with
+    the static global scale, W prequantized (global scale, then the fragment quantizer). Whole row
+    tiles of both packed buffers (first, middle, ragged last) against the oracle, every byte against
+    the row-major quantizer's rearranged on the device, and sampled GEMM entries against the
+    oracle's linear layer."""
+    xb, wb = tensor_bits(4, "X"), tensor_bits(4, "W")
+    m, n, k = xb.shape[0], wb.shape[0], xb.shape[1]
+    one = scalar(1.0)
+    xd, wd = dev_bf16(xb), dev_bf16(wb)
+    px, sx = bsp.bsp_nvfp4_quantize_frag(xd, one)
+    gw = bsp.bsp_nvfp4_global_sf(wd)[0]
+    pw, sw = bsp.bsp_nvfp4_quantize_frag(wd, gw)
+    rg = N.global_sf(wb)[0]
+    assert gw.item() == rg
+    for buf, src, g in ((px, xb, f32(1.0)), (pw, wb, rg)):
+        rt = buf.shape[0]
+        for t in (0, rt // 3, rt - 1):
+            rows = src[32 * t: min(32 * t + 32, src.shape[0])]
+            rp, _ = N.quantize(rows, g, packed_layout="frag")
+            assert np.array_equal(host_u8(buf[t]).ravel(), rp), t
+    for buf, sbuf, d, g in ((px, sx, xd, one), (pw, sw, wd, gw)):
+        rows = d.shape[0]
+        pl, sl = bsp.bsp_nvfp4_quantize(d, g)
+        rt = buf.shape[0]
+        plin = torch.zeros((rt * 32, k // 2), dtype=torch.uint8, device="cuda")
+        plin[:rows] = pl
+        want = plin.view(rt, 32, k // 64, 2, 16).permute(0, 2, 3, 1, 4).contiguous().view(-1)
+        assert torch.equal(buf.view(-1), want) and torch.equal(sbuf, sl)
+        del pl, sl, plin, want
+    alpha = bsp.bsp_nvfp4_alpha(one, gw)
+    c = bsp.bsp_mm_fp4_frag(px, sx, pw, sw, m, n, alpha)
+    c32 = bsp.bsp_mm_fp4_frag(px, sx, pw, sw, m, n, alpha, out_dtype=torch.float32)
+    rows, cols = sample_entries(m, n, 3000, 47)
+    ref = oracle_linear_entries(xb, wb, rows, cols)
+    check_gemm_outputs(c, c32, ref, "fc_in fp4 frag", rows, cols, f32_tol=REL_FRO_FP4_F32)
+    # the same products as bsp_mm_fp4 on the row-major operands, summed in another order
+    lx, lsx = bsp.bsp_nvfp4_quantize(xd, one)
+    lw, lsw = bsp.bsp_nvfp4_quantize(wd, gw)
+    d = (bsp.bsp_mm_fp4(lx, lsx, lw, lsw, alpha, out_dtype=torch.float32) - c32).abs().max().item()
+    say("max |frag - row-major| fp32:", d, "max |c|:", c32.abs().max().item())
+    assert d <= 1e-5 * c32.abs().max().item()
