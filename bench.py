@@ -4,6 +4,8 @@
 Workload: the Wan-14B-shaped FFN on one GPU, M = 32760 tokens, hidden 5120, FFN 13824:
     quantize X[32760,5120] -> mm_fp4 fc_in (W1 13824x5120) -> GELU -> quantize H[32760,13824]
     -> mm_fp4 fc_out (W2 5120x13824) -> bf16 out[32760,5120]
+The headline step keeps the packed NVFP4 values in the MFMA fragment layout (scales in 128x4); the
+same step on row-major packed values is timed beside it ("ffn_step_row_major").
 Weights are prequantized once at load (timed separately). Inputs are seeded synthetic bf16
 tensors (workloads/, config 4: X ~ N(0,1) with 1% outlier channels x20, W ~ N(0, 0.01^2)),
 resident in HBM before timing. One step = one pass of that FFN. The MXFP8 W8A8 path at the same
@@ -129,93 +131,114 @@ def main():
     stream = torch.cuda.current_stream(dev)
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
-    # ---- load time: weight global scale + prequantization
-    l0, l1 = ev(), ev()
+    # ---- load time: weight global scale + prequantization, in the pages' row-major layout and with
+    # the packed values in the fragment layout (the same codes and 128x4 scales)
+    l0, l1, l2 = ev(), ev(), ev()
+    # untimed first calls (module and kernel loading), then the timed load of both weights
+    _wq = bsp.bsp_nvfp4_prequantize_weight(w1)
+    _wq = bsp.bsp_nvfp4_quantize_frag(w1, _wq[2])
+    torch.cuda.synchronize()
+    del _wq
     l0.record(stream)
     pw1, sw1, g1, _, _ = bsp.bsp_nvfp4_prequantize_weight(w1)
     pw2, sw2, g2, _, _ = bsp.bsp_nvfp4_prequantize_weight(w2)
     l1.record(stream)
+    g1f = bsp.bsp_nvfp4_global_sf(w1)[0]
+    pw1f, sw1f = bsp.bsp_nvfp4_quantize_frag(w1, g1f)
+    g2f = bsp.bsp_nvfp4_global_sf(w2)[0]
+    pw2f, sw2f = bsp.bsp_nvfp4_quantize_frag(w2, g2f)
+    l2.record(stream)
     one = torch.ones(1, dtype=torch.float32, device=dev)
     a1 = bsp.bsp_nvfp4_alpha(one, g1)
     a2 = bsp.bsp_nvfp4_alpha(one, g2)
     torch.cuda.synchronize()
-    load_ms = l0.elapsed_time(l1)
+    load_ms, load_frag_ms = l0.elapsed_time(l1), l1.elapsed_time(l2)
+    assert g1f.item() == g1.item() and g2f.item() == g2.item()
     del w1, w2
 
-    # ---- step buffers
+    # ---- step buffers (row-major packed values, and the fragment layout [ceil(rows/32), K/64, 1 KB])
     px = torch.empty((M, K1 // 2), dtype=torch.uint8, device=dev)
     sx = torch.empty(nvfp4_sf_shape(M, K1), dtype=torch.uint8, device=dev)
     y = torch.empty((M, N1), dtype=torch.bfloat16, device=dev)
     ph = torch.empty((M, N1 // 2), dtype=torch.uint8, device=dev)
     sh = torch.empty(nvfp4_sf_shape(M, N1), dtype=torch.uint8, device=dev)
     out = torch.empty((M, N2), dtype=torch.bfloat16, device=dev)
+    pxf = torch.empty((-(-M // 32), K1 // 64, 1024), dtype=torch.uint8, device=dev)
+    phf = torch.empty((-(-M // 32), N1 // 64, 1024), dtype=torch.uint8, device=dev)
 
-    # one step: quantize X -> fc_in -> GELU fused into the NVFP4 quantize of H -> fc_out
+    # one step: quantize X -> fc_in -> GELU fused into the NVFP4 quantize of H -> fc_out. The
+    # headline step keeps the packed values in the fragment layout (each wave loads a 1 KB operand
+    # fragment with one coalesced read); the same step on row-major packed values is timed beside it.
     names = ["quantize_x", "mm_fp4_fc_in", "gelu_quantize_h", "mm_fp4_fc_out"]
-    acc = {n: 0.0 for n in names}
+    frag_calls = [lambda: bsp.bsp_nvfp4_quantize_frag(x, one, pxf, sx),
+                  lambda: bsp.bsp_mm_fp4_frag(pxf, sx, pw1f, sw1f, M, N1, a1, out=y),
+                  lambda: bsp.bsp_nvfp4_quantize_gelu_frag(y, one, phf, sh),
+                  lambda: bsp.bsp_mm_fp4_frag(phf, sh, pw2f, sw2f, M, N2, a2, out=out)]
+    linear_calls = [lambda: bsp.bsp_nvfp4_quantize(x, one, px, sx),
+                    lambda: bsp.bsp_mm_fp4(px, sx, pw1, sw1, a1, out=y),
+                    lambda: bsp.bsp_nvfp4_quantize_gelu(y, one, ph, sh),
+                    lambda: bsp.bsp_mm_fp4(ph, sh, pw2, sw2, a2, out=out)]
 
-    def step(events=None):
-        if events:
-            events[0].record(stream)
-        bsp.bsp_nvfp4_quantize(x, one, px, sx)
-        if events:
-            events[1].record(stream)
-        bsp.bsp_mm_fp4(px, sx, pw1, sw1, a1, out=y)
-        if events:
-            events[2].record(stream)
-        bsp.bsp_nvfp4_quantize_gelu(y, one, ph, sh)
-        if events:
-            events[3].record(stream)
-        bsp.bsp_mm_fp4(ph, sh, pw2, sw2, a2, out=out)
-        if events:
-            events[4].record(stream)
+    def timed_steps(calls):
+        """W untimed steps, then K timed ones bracketed by synchronizations; HIP events on the
+        kernels' stream around every launch. Returns (wall ms per step, mean ms per kernel, spread)."""
+        def step(events=None):
+            for j, c in enumerate(calls):
+                if events:
+                    events[j].record(stream)
+                c()
+            if events:
+                events[-1].record(stream)
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        evs = [[ev() for _ in range(len(calls) + 1)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(evs[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        per = {n: [e[j].elapsed_time(e[j + 1]) for e in evs] for j, n in enumerate(names)}
+        per["step"] = [e[0].elapsed_time(e[-1]) for e in evs]
+        mean = {n: sum(per[n]) / args.steps for n in names}
+        spread = {n: {"median": round(float(np.median(v)), 4), "p10": round(float(np.percentile(v, 10)), 4),
+                      "p90": round(float(np.percentile(v, 90)), 4)} for n, v in per.items()}
+        return wall * 1e3 / args.steps, mean, spread
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [[ev() for _ in range(len(names) + 1)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per_step = {n: [] for n in names}
-    for e in evs:
-        for j, n in enumerate(names):
-            t = e[j].elapsed_time(e[j + 1])
-            acc[n] += t
-            per_step[n].append(t)
-    per_step["step"] = [e[0].elapsed_time(e[-1]) for e in evs]
-    kms = {n: acc[n] / args.steps for n in names}
-    ms_per_step = wall * 1e3 / args.steps
-    spread = {n: {"median": round(float(np.median(v)), 4), "p10": round(float(np.percentile(v, 10)), 4),
-                  "p90": round(float(np.percentile(v, 90)), 4)} for n, v in per_step.items()}
+    ms_per_step, kms, spread = timed_steps(frag_calls)
+    ms_lin, kms_lin, spread_lin = timed_steps(linear_calls)
 
-    # Kernel durations without the event records between a step's launches: the quantize of X and
-    # the RMSNorm + quantize prologue back to back over two copies of X and of the outputs in turn
-    # (1.1 GB between reuses of a buffer, so no pass is served from the 256 MB Infinity Cache), and
-    # the unfused GELU and plain quantize of H (0.9 GB inputs) on their own. The step's own quantize
-    # time stays as quantize_x_in_step.
+    # Kernel durations without the event records between a step's launches: the quantize of X (both
+    # layouts) and the RMSNorm + quantize prologue back to back over two copies of X and of the
+    # outputs in turn (1.1 GB between reuses of a buffer, so no pass is served from the 256 MB
+    # Infinity Cache), the GELU-fused quantize of H the same way, and the unfused GELU and plain
+    # quantize of H (0.9 GB inputs) on their own. The step's own quantize times stay as *_in_step.
     h = bsp.bsp_gelu_tanh_bf16(y)
     x2 = x.clone()
-    px2, sx2 = torch.empty_like(px), torch.empty_like(sx)
+    px2, sx2, pxf2 = torch.empty_like(px), torch.empty_like(sx), torch.empty_like(pxf)
     reps = max(4, 2 * (args.steps // 4))
     kms["quantize_x_in_step"] = kms["quantize_x"]
-    xs, pxs, sxs = (x, x2), (px, px2), (sx, sx2)
-    qx_calls = [lambda i=i: bsp.bsp_nvfp4_quantize(xs[i], one, pxs[i], sxs[i]) for i in range(2)]
+    kms["gelu_quantize_h_in_step"] = kms["gelu_quantize_h"]
+    xs, pxs, sxs, pxfs = (x, x2), (px, px2), (sx, sx2), (pxf, pxf2)
+    qx_calls = [lambda i=i: bsp.bsp_nvfp4_quantize_frag(xs[i], one, pxfs[i], sxs[i]) for i in range(2)]
+    ql_calls = [lambda i=i: bsp.bsp_nvfp4_quantize(xs[i], one, pxs[i], sxs[i]) for i in range(2)]
     nq_calls = [lambda i=i: bsp.bsp_nvfp4_quantize_rmsnorm(xs[i], one, None, 1e-6, pxs[i], sxs[i])
                 for i in range(2)]
     # the GELU-fused quantize of H back to back over two copies of the fc_in output (in the step it
     # follows fc_in, whose 0.9 GB output is still being written back)
     y2 = y.clone()
-    ys, phs, shs = (y, y2), (ph, torch.empty_like(ph)), (sh, torch.empty_like(sh))
-    gq_calls = [lambda i=i: bsp.bsp_nvfp4_quantize_gelu(ys[i], one, phs[i], shs[i]) for i in range(2)]
+    ys, phfs, shs = (y, y2), (phf, torch.empty_like(phf)), (sh, torch.empty_like(sh))
+    phs = (ph, torch.empty_like(ph))
+    gq_calls = [lambda i=i: bsp.bsp_nvfp4_quantize_gelu_frag(ys[i], one, phfs[i], shs[i]) for i in range(2)]
+    gl_calls = [lambda i=i: bsp.bsp_nvfp4_quantize_gelu(ys[i], one, phs[i], shs[i]) for i in range(2)]
     for name, fns in (("quantize_x", qx_calls),
+                      ("quantize_x_row_major", ql_calls),
                       ("rmsnorm_quantize_x", nq_calls),
-                      ("gelu_quantize_h_back_to_back", gq_calls),
+                      ("gelu_quantize_h", gq_calls),
+                      ("gelu_quantize_h_row_major", gl_calls),
                       ("gelu", [lambda: bsp.bsp_gelu_tanh_bf16(y, out=h)]),
-                      ("quantize_h", [lambda: bsp.bsp_nvfp4_quantize(h, one, ph, sh)])):
+                      ("quantize_h", [lambda: bsp.bsp_nvfp4_quantize_frag(h, one, phf, sh)])):
         for f in fns:
             f()
         e0, e1 = ev(), ev()
@@ -225,7 +248,7 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         kms[name] = e0.elapsed_time(e1) / reps
-    del h, x2, px2, sx2, y2, ys, phs, shs
+    del h, x2, px2, sx2, pxf2, y2, ys, phs, phfs, shs
 
     gemm_flops = 2.0 * M * N1 * K1 + 2.0 * M * N2 * N1
     value = gemm_flops / (ms_per_step * 1e-3) / 1e12
@@ -233,22 +256,26 @@ def main():
     def qbytes(m, k):
         return 2 * m * k + m * k // 2 + nvfp4_sf_shape(m, k)[0] * k // 16
 
+    def qrate(ms, m, k):
+        return {"ms": ms, "GB/s": qbytes(m, k) / ms / 1e6}
+
+    def grate(ms, m, n, k):
+        return {"ms": ms, "TFLOPS": 2.0 * m * n * k / ms / 1e9}
+
     kernels = {
-        "quantize_x": {"ms": kms["quantize_x"], "GB/s": qbytes(M, K1) / kms["quantize_x"] / 1e6},
-        "rmsnorm_quantize_x": {"ms": kms["rmsnorm_quantize_x"],
-                               "GB/s": qbytes(M, K1) / kms["rmsnorm_quantize_x"] / 1e6},
-        "quantize_x_in_step": {"ms": kms["quantize_x_in_step"],
-                               "GB/s": qbytes(M, K1) / kms["quantize_x_in_step"] / 1e6},
-        "gelu_quantize_h": {"ms": kms["gelu_quantize_h"],
-                            "GB/s": qbytes(M, N1) / kms["gelu_quantize_h"] / 1e6},
-        "gelu_quantize_h_back_to_back": {"ms": kms["gelu_quantize_h_back_to_back"],
-                                         "GB/s": qbytes(M, N1) / kms["gelu_quantize_h_back_to_back"] / 1e6},
-        "quantize_h": {"ms": kms["quantize_h"], "GB/s": qbytes(M, N1) / kms["quantize_h"] / 1e6},
+        "quantize_x": qrate(kms["quantize_x"], M, K1),
+        "quantize_x_in_step": qrate(kms["quantize_x_in_step"], M, K1),
+        "quantize_x_row_major": qrate(kms["quantize_x_row_major"], M, K1),
+        "rmsnorm_quantize_x": qrate(kms["rmsnorm_quantize_x"], M, K1),
+        "gelu_quantize_h": qrate(kms["gelu_quantize_h"], M, N1),
+        "gelu_quantize_h_in_step": qrate(kms["gelu_quantize_h_in_step"], M, N1),
+        "gelu_quantize_h_row_major": qrate(kms["gelu_quantize_h_row_major"], M, N1),
+        "quantize_h": qrate(kms["quantize_h"], M, N1),
         "gelu": {"ms": kms["gelu"], "GB/s": 4.0 * M * N1 / kms["gelu"] / 1e6},
-        "mm_fp4_fc_in": {"ms": kms["mm_fp4_fc_in"],
-                         "TFLOPS": 2.0 * M * N1 * K1 / kms["mm_fp4_fc_in"] / 1e9},
-        "mm_fp4_fc_out": {"ms": kms["mm_fp4_fc_out"],
-                          "TFLOPS": 2.0 * M * N2 * N1 / kms["mm_fp4_fc_out"] / 1e9},
+        "mm_fp4_fc_in": grate(kms["mm_fp4_fc_in"], M, N1, K1),
+        "mm_fp4_fc_out": grate(kms["mm_fp4_fc_out"], M, N2, N1),
+        "mm_fp4_fc_in_row_major": grate(kms_lin["mm_fp4_fc_in"], M, N1, K1),
+        "mm_fp4_fc_out_row_major": grate(kms_lin["mm_fp4_fc_out"], M, N2, N1),
     }
     for k_, v in kernels.items():
         if "GB/s" in v:
@@ -274,6 +301,8 @@ def main():
         "config": {"workload": "Wan-14B FFN on one GPU: X[32760,5120] -> fc_in 13824x5120 -> GELU "
                                "(fused into the NVFP4 quantize of H) -> fc_out 5120x13824, NVFP4 W4A4, "
                                "bf16 out",
+                   "layout": "packed values in the MFMA fragment layout (1 KB per 32-row tile and "
+                             "64-K step), scales in 128x4; the row-major step is ffn_step_row_major",
                    "format": "nvfp4 (e2m1 + e4m3 per 16, fp32 global scale); the GEMMs multiply "
                              "exact fp16 dequantized operands with fp32 accumulation, the quantizers "
                              "compute in fp32",
@@ -284,9 +313,15 @@ def main():
         "quantize_GBs": round(min(kernels["quantize_x"]["GB/s"], kernels["quantize_h"]["GB/s"]), 1),
         "quantize_frac_hbm": round(min(kernels["quantize_x"]["frac_hbm"],
                                        kernels["quantize_h"]["frac_hbm"]), 4),
-        "load_time_ms": {"prequantize_w1_w2": round(load_ms, 3)},
+        "load_time_ms": {"prequantize_w1_w2": round(load_ms, 3),
+                         "prequantize_w1_w2_fragment_layout": round(load_frag_ms, 3)},
         "event_ms_spread": spread,
+        "ffn_step_row_major": {
+            "ms_per_step": round(ms_lin, 4), "TFLOPS": round(gemm_flops / (ms_lin * 1e-3) / 1e12, 2),
+            "kernel_ms": {n: round(v, 4) for n, v in kms_lin.items()},
+            "event_ms_spread": spread_lin},
     }
+    log(json.dumps(result["ffn_step_row_major"]))
 
     # ---- the same FFN step with fc_in's epilogue emitting the NVFP4 of gelu(C) directly
     # (bsp_mm_fp4_gelu_nvfp4: no bf16 H in memory, no separate GELU + quantize launch)
@@ -317,8 +352,8 @@ def main():
         "ms_per_step": round(wall_e * 1e3 / args.steps, 4),
         "TFLOPS": round(gemm_flops / (wall_e / args.steps) / 1e12, 2),
         "mm_fp4_gelu_nvfp4_fc_in_ms": round(fcin_epi, 4),
-        "two_kernel_fc_in_plus_gelu_quantize_ms": round(kms["mm_fp4_fc_in"] + kms["gelu_quantize_h"], 4),
-        "two_kernel_ms_per_step": round(ms_per_step, 4)}
+        "row_major_fc_in_plus_gelu_quantize_ms": round(kms_lin["mm_fp4_fc_in"] + kms_lin["gelu_quantize_h"], 4),
+        "row_major_two_kernel_ms_per_step": round(ms_lin, 4)}
     log(json.dumps(result["ffn_step_gelu_nvfp4_epilogue"]))
 
     # ---- per-token activation scales at the fc_in shape: quantize X per row + mm_fp4 with row alphas
@@ -560,6 +595,7 @@ def main():
         kernels_frac = {
             "mm_fp4_fc_in_of_f16_mfma_loop": kernels["mm_fp4_fc_in"]["TFLOPS"] / f16,
             "mm_fp4_fc_out_of_f16_mfma_loop": kernels["mm_fp4_fc_out"]["TFLOPS"] / f16,
+            "mm_fp4_fc_in_row_major_of_f16_mfma_loop": kernels["mm_fp4_fc_in_row_major"]["TFLOPS"] / f16,
             "quantize_x_of_stream_4to1": kernels["quantize_x"]["GB/s"] / mp["hbm_read4_write1_GBs"],
             "quantize_x_in_step_of_stream_4to1": kernels["quantize_x_in_step"]["GB/s"] / mp["hbm_read4_write1_GBs"],
             "gelu_quantize_h_of_stream_4to1": kernels["gelu_quantize_h"]["GB/s"] / mp["hbm_read4_write1_GBs"],
@@ -638,36 +674,58 @@ def measure_shapes(steps: int) -> dict:
         return {"ms": round(ms, 4), "TFLOPS": round(tf, 2), "frac_fp4_peak": round(tf / PEAK_FP4_TFLOPS, 4),
                 "frac_f16_mfma_peak": round(tf / PEAK_F16_TFLOPS, 4)}
 
+    def gtime_frag(xq, wq, m, n, alpha, out):
+        (pxf, sx), (pwf, sw) = xq, wq
+        ms = _event_ms([lambda: bsp.bsp_mm_fp4_frag(pxf, sx, pwf, sw, m, n, alpha, out=out)], reps)
+        tf = 2.0 * m * n * pxf.shape[1] * 64 / ms / 1e9
+        return {"ms": round(ms, 4), "TFLOPS": round(tf, 2), "frac_fp4_peak": round(tf / PEAK_FP4_TFLOPS, 4),
+                "frac_f16_mfma_peak": round(tf / PEAK_F16_TFLOPS, 4)}
+
+    def weights(bits):
+        w = up(bits)
+        pw, sw, g, _, _ = bsp.bsp_nvfp4_prequantize_weight(w)
+        return (pw, sw), bsp.bsp_nvfp4_quantize_frag(w, g), bsp.bsp_nvfp4_alpha(one, g)
+
     res = {}
     # Wan-1.3B attention projection
     c2 = W.config(2)
     x = up(W.generate(c2.tensor("X")))
-    pw, sw, g, _, _ = bsp.bsp_nvfp4_prequantize_weight(up(W.generate(c2.tensor("W"))))
+    (pw, sw), wf, al = weights(W.generate(c2.tensor("W")))
+    m = x.shape[0]
     res["wan1.3b_attn_quantize_x_32760x1536"] = qtime(x)
     px, sx = bsp.bsp_nvfp4_quantize(x, one)
-    out = torch.empty((x.shape[0], pw.shape[0]), dtype=torch.bfloat16, device=dev)
-    res["wan1.3b_attn_mm_fp4_32760x1536x1536"] = gtime(px, sx, pw, sw, bsp.bsp_nvfp4_alpha(one, g), out)
+    out = torch.empty((m, pw.shape[0]), dtype=torch.bfloat16, device=dev)
+    res["wan1.3b_attn_mm_fp4_32760x1536x1536"] = gtime(px, sx, pw, sw, al, out)
+    res["wan1.3b_attn_mm_fp4_frag_32760x1536x1536"] = gtime_frag(
+        bsp.bsp_nvfp4_quantize_frag(x, one), wf, m, pw.shape[0], al, out)
     # Wan-1.3B FFN
     c3 = W.config(3)
     x = up(W.generate(c3.tensor("X")))
-    pw1, sw1, g1, _, _ = bsp.bsp_nvfp4_prequantize_weight(up(W.generate(c3.tensor("W"))))
-    pw2, sw2, g2, _, _ = bsp.bsp_nvfp4_prequantize_weight(up(W.generate(c3.tensor("W2"))))
+    (pw1, sw1), w1f, al1 = weights(W.generate(c3.tensor("W")))
+    (pw2, sw2), w2f, al2 = weights(W.generate(c3.tensor("W2")))
+    n1, n2 = pw1.shape[0], pw2.shape[0]
     res["wan1.3b_ffn_quantize_x_32760x1536"] = qtime(x)
     px, sx = bsp.bsp_nvfp4_quantize(x, one)
-    y = torch.empty((x.shape[0], pw1.shape[0]), dtype=torch.bfloat16, device=dev)
-    res["wan1.3b_ffn_mm_fp4_fc_in_32760x8960x1536"] = gtime(px, sx, pw1, sw1, bsp.bsp_nvfp4_alpha(one, g1), y)
+    y = torch.empty((m, n1), dtype=torch.bfloat16, device=dev)
+    res["wan1.3b_ffn_mm_fp4_fc_in_32760x8960x1536"] = gtime(px, sx, pw1, sw1, al1, y)
+    res["wan1.3b_ffn_mm_fp4_frag_fc_in_32760x8960x1536"] = gtime_frag(
+        bsp.bsp_nvfp4_quantize_frag(x, one), w1f, m, n1, al1, y)
     res["wan1.3b_ffn_gelu_quantize_h_32760x8960"] = qtime(y, gelu=True)
     ph, sh = bsp.bsp_nvfp4_quantize_gelu(y, one)
-    out = torch.empty((x.shape[0], pw2.shape[0]), dtype=torch.bfloat16, device=dev)
-    res["wan1.3b_ffn_mm_fp4_fc_out_32760x1536x8960"] = gtime(ph, sh, pw2, sw2, bsp.bsp_nvfp4_alpha(one, g2), out)
+    out = torch.empty((m, n2), dtype=torch.bfloat16, device=dev)
+    res["wan1.3b_ffn_mm_fp4_fc_out_32760x1536x8960"] = gtime(ph, sh, pw2, sw2, al2, out)
+    res["wan1.3b_ffn_mm_fp4_frag_fc_out_32760x1536x8960"] = gtime_frag(
+        bsp.bsp_nvfp4_quantize_gelu_frag(y, one), w2f, m, n2, al2, out)
     del y, ph, sh, out
     # Wan-14B to_q
     c4 = W.config(4)
     x = up(W.generate(c4.tensor("X")))
-    pw, sw, g, _, _ = bsp.bsp_nvfp4_prequantize_weight(up(W.generate(c4.tensor("W3"))))
+    (pw, sw), wf, al = weights(W.generate(c4.tensor("W3")))
     px, sx = bsp.bsp_nvfp4_quantize(x, one)
-    out = torch.empty((x.shape[0], pw.shape[0]), dtype=torch.bfloat16, device=dev)
-    res["wan14b_to_q_mm_fp4_32760x5120x5120"] = gtime(px, sx, pw, sw, bsp.bsp_nvfp4_alpha(one, g), out)
+    out = torch.empty((m, pw.shape[0]), dtype=torch.bfloat16, device=dev)
+    res["wan14b_to_q_mm_fp4_32760x5120x5120"] = gtime(px, sx, pw, sw, al, out)
+    res["wan14b_to_q_mm_fp4_frag_32760x5120x5120"] = gtime_frag(
+        bsp.bsp_nvfp4_quantize_frag(x, one), wf, m, pw.shape[0], al, out)
     return res
 
 

@@ -163,25 +163,49 @@ def test_mm_fp4_full_size_linear(cfg):
     _linear_full_size(xb, tensor_bits(cfg, wname), f"cfg{cfg} {wname}", seed=cfg)
 
 
-@pytest.mark.parametrize("cfg", [3, 4])
-def test_ffn_chain_full_size(cfg):
+def _frag_to_row_major(frag: torch.Tensor, rows: int, k: int) -> torch.Tensor:
+    """Packed bytes in the fragment layout ([rt, K/64, 1024], lane i + 32 h holding row i's bytes
+    16 h .. 16 h + 15 of the step) rearranged on the device into row-major [rows, K/2]."""
+    rt = frag.shape[0]
+    return frag.view(rt, k // 64, 2, 32, 16).permute(0, 3, 1, 2, 4).reshape(rt * 32, k // 2)[:rows]
+
+
+@pytest.mark.parametrize("cfg,layout", [(3, "linear"), (4, "linear"), (3, "frag"), (4, "frag")])
+def test_ffn_chain_full_size(cfg, layout):
     """The FFN step at full size, X -> quantize -> fc_in -> GELU fused into the quantize of H ->
     fc_out, against the oracle's own chain from the same bf16 X, W, W2 on sampled token rows
     (whole rows: fc_out needs all of H's row): fc_in's bf16 and fp32 outputs, H's quantized bytes
-    and fc_out's bf16 and fp32 outputs."""
+    and fc_out's bf16 and fp32 outputs. layout "frag" runs the same chain with every packed operand
+    in the fragment layout (bsp_nvfp4_quantize_frag / _gelu_frag, bsp_mm_fp4_frag), as the bench's
+    headline step does."""
     xb, w1b, w2b = tensor_bits(cfg, "X"), tensor_bits(cfg, "W"), tensor_bits(cfg, "W2")
     m, k1, n1, n2 = xb.shape[0], xb.shape[1], w1b.shape[0], w2b.shape[0]
-    say("ffn chain cfg", cfg, xb.shape, w1b.shape, w2b.shape)
+    say("ffn chain cfg", cfg, layout, xb.shape, w1b.shape, w2b.shape)
     one = scalar(1.0)
-    px, sx = bsp.bsp_nvfp4_quantize(dev_bf16(xb), one)
-    pw1, sw1, g1, _, _ = bsp.bsp_nvfp4_prequantize_weight(dev_bf16(w1b))
-    pw2, sw2, g2, _, _ = bsp.bsp_nvfp4_prequantize_weight(dev_bf16(w2b))
-    a1, a2 = bsp.bsp_nvfp4_alpha(one, g1), bsp.bsp_nvfp4_alpha(one, g2)
-    y = bsp.bsp_mm_fp4(px, sx, pw1, sw1, a1)
-    y32 = bsp.bsp_mm_fp4(px, sx, pw1, sw1, a1, out_dtype=torch.float32)
-    ph, sh = bsp.bsp_nvfp4_quantize_gelu(y, one)
-    out = bsp.bsp_mm_fp4(ph, sh, pw2, sw2, a2)
-    out32 = bsp.bsp_mm_fp4(ph, sh, pw2, sw2, a2, out_dtype=torch.float32)
+    if layout == "linear":
+        px, sx = bsp.bsp_nvfp4_quantize(dev_bf16(xb), one)
+        pw1, sw1, g1, _, _ = bsp.bsp_nvfp4_prequantize_weight(dev_bf16(w1b))
+        pw2, sw2, g2, _, _ = bsp.bsp_nvfp4_prequantize_weight(dev_bf16(w2b))
+        a1, a2 = bsp.bsp_nvfp4_alpha(one, g1), bsp.bsp_nvfp4_alpha(one, g2)
+        y = bsp.bsp_mm_fp4(px, sx, pw1, sw1, a1)
+        y32 = bsp.bsp_mm_fp4(px, sx, pw1, sw1, a1, out_dtype=torch.float32)
+        ph, sh = bsp.bsp_nvfp4_quantize_gelu(y, one)
+        out = bsp.bsp_mm_fp4(ph, sh, pw2, sw2, a2)
+        out32 = bsp.bsp_mm_fp4(ph, sh, pw2, sw2, a2, out_dtype=torch.float32)
+    else:
+        px, sx = bsp.bsp_nvfp4_quantize_frag(dev_bf16(xb), one)
+        w1d, w2d = dev_bf16(w1b), dev_bf16(w2b)
+        g1, g2 = bsp.bsp_nvfp4_global_sf(w1d)[0], bsp.bsp_nvfp4_global_sf(w2d)[0]
+        pw1, sw1 = bsp.bsp_nvfp4_quantize_frag(w1d, g1)
+        pw2, sw2 = bsp.bsp_nvfp4_quantize_frag(w2d, g2)
+        del w1d, w2d
+        a1, a2 = bsp.bsp_nvfp4_alpha(one, g1), bsp.bsp_nvfp4_alpha(one, g2)
+        y = bsp.bsp_mm_fp4_frag(px, sx, pw1, sw1, m, n1, a1)
+        y32 = bsp.bsp_mm_fp4_frag(px, sx, pw1, sw1, m, n1, a1, out_dtype=torch.float32)
+        phf, sh = bsp.bsp_nvfp4_quantize_gelu_frag(y, one)
+        out = bsp.bsp_mm_fp4_frag(phf, sh, pw2, sw2, m, n2, a2)
+        out32 = bsp.bsp_mm_fp4_frag(phf, sh, pw2, sw2, m, n2, a2, out_dtype=torch.float32)
+        ph = _frag_to_row_major(phf, m, n1)
     torch.cuda.synchronize()
 
     rows = np.unique(np.concatenate([np.random.default_rng(cfg).integers(0, m, 12), [0, m - 1]]))
@@ -195,7 +219,7 @@ def test_ffn_chain_full_size(cfg):
     y_ref = N.mm_fp4(rpx, rsx, rpw1, rsw1, N.alpha(1.0, rg1), r, n1, k1)       # [r, n1] exact
     ri = torch.from_numpy(rows).cuda()
     # fc_in on whole sampled rows, both outputs
-    check_gemm_outputs(y[ri], y32[ri], y_ref, f"cfg{cfg} fc_in", f32_tol=REL_FRO_FP4_F32)
+    check_gemm_outputs(y[ri], y32[ri], y_ref, f"cfg{cfg} {layout} fc_in", f32_tol=REL_FRO_FP4_F32)
     yb_ref = A.f64_to_bf16_bits(y_ref)
     hb_ref = A.gelu_tanh_bf16_bits(yb_ref)
     # H: every 16-element block must equal the oracle chain's bytes unless one of its values is
@@ -210,8 +234,8 @@ def test_ffn_chain_full_size(cfg):
     rp_, cp_ = N.sf_padded_shape(m, n1)
     sh_lin = N.unswizzle_128x4(host_u8(sh).ravel(), rp_, cp_)
     rphl, rshl = N.quantize(hb_ref, f32(1.0), layout="linear")
-    frac = assert_nvfp4_blocks(host_u8(ph[ri]), sh_lin[rows], rphl, rshl, ~amb, f"cfg{cfg} H")
-    say(f"cfg{cfg} H blocks differing from the oracle chain:", frac)
+    frac = assert_nvfp4_blocks(host_u8(ph[ri]), sh_lin[rows], rphl, rshl, ~amb, f"cfg{cfg} {layout} H")
+    say(f"cfg{cfg} {layout} H blocks differing from the oracle chain:", frac)
     assert amb.mean() < 0.05 and frac <= amb.mean()
     del y, y32
     cols = np.arange(0, n2, max(1, n2 // 512))
@@ -219,7 +243,8 @@ def test_ffn_chain_full_size(cfg):
     rpw2, rsw2 = N.quantize(w2b[cols], rg2)
     ref = N.mm_fp4(rph, rsh, rpw2, rsw2, N.alpha(1.0, rg2), r, len(cols), n1)
     rr, cc = np.repeat(rows, len(cols)), np.tile(cols, r)
-    check_gemm_outputs(out, out32, ref.ravel(), f"cfg{cfg} fc_out", rr, cc, f32_tol=REL_FRO_FP4_F32)
+    check_gemm_outputs(out, out32, ref.ravel(), f"cfg{cfg} {layout} fc_out", rr, cc,
+                       f32_tol=REL_FRO_FP4_F32)
 
 
 def test_mm_fp4_huge_alpha():
