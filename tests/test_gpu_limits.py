@@ -4,7 +4,7 @@ Quantizers at their largest row count (the grid's tile-row limit: ceil(M/128) < 
 ceil(M/64) < 65536) with sampled rows, the first and last rows and every padding scale byte
 checked; the GEMMs at K = 2^24 (mm_fp4's limit: per-tile 32-bit load offsets) on every element;
 GEMMs with 8.4 million rows (int64 row offsets, 32768 tiles) on sampled rows, for mm_fp4 and for the
-fragment-layout MX GEMMs. One size past each limit is rejected on the host (tests/test_abi.py).
+fragment-layout NVFP4 and MX GEMMs (and the fragment-layout NVFP4 GEMM at K = 2^24). One size past each limit is rejected on the host (tests/test_abi.py).
 """
 import numpy as np
 import pytest
@@ -77,32 +77,49 @@ def test_mxfp8_quantize_at_max_rows():
     assert np.array_equal(host_u8(q[ri]), rq) and np.array_equal(host_u8(s[ri]), rs)
 
 
-@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8"])
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8", "nvfp4", "nvfp4_gelu"])
 def test_frag_quantizers_at_max_rows(fmt):
     """The fragment-layout quantizers at their largest row count minus a ragged few (seeded device
     input, K = 256): sampled rows and every padding row of the last row tile, read through the
-    layout's offsets, against the oracle."""
-    m = (M_MAX_128 if fmt == "mxfp4" else M_MAX_64) - 7
+    layout's offsets, against the oracle (the GELU-fused NVFP4 one on the GPU's own GELU of the
+    same rows, the bar of its parity tests)."""
+    m = (M_MAX_64 if fmt == "mxfp8" else M_MAX_128) - 7
     k = 256
     say("max rows frag quantize", fmt, m, k)
     g = torch.Generator(device="cuda")
     g.manual_seed(31)
     x = (torch.randn((m, k), device="cuda", generator=g) * 2.0).bfloat16()
+    gs = np.float32(0.37)
     if fmt == "mxfp4":
         q, s = bsp.bsp_mxfp4_quantize_frag(x)
-    else:
+    elif fmt == "mxfp8":
         q, s = bsp.bsp_mxfp8_quantize_frag(x)
+    elif fmt == "nvfp4":
+        q, s = bsp.bsp_nvfp4_quantize_frag(x, scalar(gs))
+    else:
+        q, s = bsp.bsp_nvfp4_quantize_gelu_frag(x, scalar(gs))
     rows = _rows(m, 6)
-    xb = x[torch.from_numpy(rows).cuda()].view(torch.int16).cpu().numpy().view(np.uint16)
+    xr = x[torch.from_numpy(rows).cuda()]
+    if fmt == "nvfp4_gelu":
+        xr = bsp.bsp_gelu_tanh_bf16(xr)
+    xb = xr.view(torch.int16).cpu().numpy().view(np.uint16)
     rp = -(-m // 32) * 32
     pad = np.arange(m, rp)
     if fmt == "mxfp4":
         ref_q, ref_s = X4.quantize(xb, layout="linear")
         off = lambda r: X4.frag_packed_offset(r[:, None], np.arange(k // 2)[None, :], k)  # noqa: E731
-    else:
+    elif fmt == "mxfp8":
         ref_q, ref_s = X.quantize(xb)
         off = lambda r: X.frag_offset(r[:, None], np.arange(k)[None, :], k)  # noqa: E731
-    soff = lambda r: X4.frag_sf_offset(r[:, None], np.arange(k // 32)[None, :], k)  # noqa: E731
+    else:
+        ref_q, ref_s = N.quantize(xb, gs, layout="linear")
+        off = lambda r: N.frag_packed_offset(r[:, None], np.arange(k // 2)[None, :], k)  # noqa: E731
+    if fmt.startswith("nvfp4"):
+        cp = N.sf_padded_shape(m, k)[1]
+        soff = lambda r: N.sf_offset(r[:, None], np.arange(k // 16)[None, :], cp)  # noqa: E731
+        assert N.sf_padded_shape(m, k)[0] == rp     # the 128-row scale padding is the same 7 rows
+    else:
+        soff = lambda r: X4.frag_sf_offset(r[:, None], np.arange(k // 32)[None, :], k)  # noqa: E731
 
     def gather(t, o):
         return t.view(-1)[torch.from_numpy(o.ravel()).cuda()].cpu().numpy().reshape(o.shape)
@@ -171,6 +188,56 @@ def test_mm_fp4_tall_max_rows():
     rows = _rows(m, 5)
     got = c[torch.from_numpy(rows).cuda()].float().cpu().numpy().astype(np.float64)
     ref = N.dequant_rows(pa, sa, rows, m, k) @ N.dequant_rows(pb, sb, np.arange(n), n, k).T
+    err = np.abs(got - ref)
+    assert np.all(err <= 8e-3 * np.max(np.abs(ref))), float(err.max())
+    assert np.linalg.norm(got - ref) <= 3e-3 * np.linalg.norm(ref)
+
+
+# --------------------------------------------------------------- NVFP4 GEMM, fragment layout
+def test_mm_fp4_frag_at_k_2_24():
+    """bsp_mm_fp4_frag at K = 2^24 (262144 K steps per tile; scale loads 2^27 bytes into a row
+    tile) with ragged M, N: every element of the fp32 output against the oracle."""
+    m, n, k = 3, 5, 1 << 24
+    say("frag K = 2^24 nvfp4", m, n, k)
+    rng = np.random.default_rng(224)
+    pa, sa = _nvfp4_operand(rng, m, k)
+    pb, sb = _nvfp4_operand(rng, n, k)
+    fa, fb = N.to_frag_packed(pa, k), N.to_frag_packed(pb, k)
+    del pa, pb
+    a = dev_u8(fa.reshape(-1, k // 64, 1024))
+    b = dev_u8(fb.reshape(-1, k // 64, 1024))
+    c = bsp.bsp_mm_fp4_frag(a, dev_u8(sa), b, dev_u8(sb), m, n, scalar(0.25), out_dtype=torch.float32)
+    ref = N.mm_fp4_frag(fa, sa, fb, sb, np.float32(0.25), m, n, k)
+    assert_gemm_f32(c.cpu().numpy().astype(np.float64), ref, "frag K=2^24 nvfp4")
+
+
+def test_mm_fp4_frag_tall_max_rows():
+    """bsp_mm_fp4_frag with M = 8388480 (262140 row tiles, 32768 tile rows; C offsets past 2^31
+    bytes), N = 136 (ragged), K = 256, device-random A: sampled rows of C, their operand bytes
+    gathered through the layout's offsets, against the oracle, in bf16."""
+    m, n, k = M_MAX_128, 136, 256
+    say("tall frag nvfp4", m, n, k)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(17)
+    a = torch.randint(0, 256, (m // 32, k // 64, 1024), dtype=torch.uint8, device="cuda", generator=g)
+    rp, cp = N.sf_padded_shape(m, k)
+    a_s = torch.randint(0x28, 0x48, (rp, cp), dtype=torch.uint8, device="cuda", generator=g)
+    rng = np.random.default_rng(18)
+    pb, sb = _nvfp4_operand(rng, n, k)
+    c = bsp.bsp_mm_fp4_frag(a, a_s, dev_u8(N.to_frag_packed(pb, k).reshape(-1, k // 64, 1024)),
+                            dev_u8(sb), m, n, scalar(1.0))
+    rows = _rows(m, 19)
+    off = N.frag_packed_offset(rows[:, None], np.arange(k // 2)[None, :], k)
+    soff = N.sf_offset(rows[:, None], np.arange(k // 16)[None, :], cp)
+    pr = a.view(-1)[torch.from_numpy(off.ravel()).cuda()].cpu().numpy().reshape(off.shape)
+    sr = a_s.view(-1)[torch.from_numpy(soff.ravel()).cuda()].cpu().numpy().reshape(soff.shape)
+    # the sampled rows as a small operand of their own (row i of it is row rows[i] of A)
+    sl = np.zeros(N.sf_padded_shape(len(rows), k), dtype=np.uint8)
+    sl[: len(rows), : k // 16] = sr
+    A = N.dequant_rows(pr, N.swizzle_128x4(sl), np.arange(len(rows)), len(rows), k)
+    B = N.dequant_rows(pb, sb, np.arange(n), n, k)
+    ref = A @ B.T
+    got = c[torch.from_numpy(rows).cuda()].float().cpu().numpy().astype(np.float64)
     err = np.abs(got - ref)
     assert np.all(err <= 8e-3 * np.max(np.abs(ref))), float(err.max())
     assert np.linalg.norm(got - ref) <= 3e-3 * np.linalg.norm(ref)
