@@ -155,3 +155,63 @@ def test_gemm_variant_sweep(m, n, k):
                        X4.mm_mxfp4(pa4, sa4, pb4, sb4, np.float32(0.25), m, n, k), f"mm_mxfp4 {m}x{n}x{k}")
     c = bsp.bsp_mm_mxfp4_bias(*a4, bias, scalar(0.25))
     assert torch.equal(c.view(torch.int16), (c0.float() + bias.float()).bfloat16().view(torch.int16))
+
+
+@pytest.mark.parametrize("m,n,k", GEMM_CASES)
+def test_frag_gemm_sweep(m, n, k):
+    """The fragment-layout GEMMs on the sweep's shapes: mm_fp4_frag at K and K - 64, and the MX ones
+    at K rounded down to a multiple of 256 (at least 256), every element against the oracle."""
+    say("frag gemm sweep", m, n, k)
+    rng = np.random.default_rng(m * 2003 + n * 17 + k)
+    for kk in (k, k - 64) if k > 64 else (k,):
+        pa, sa = _nvfp4_operand(rng, m, kk)
+        pb, sb = _nvfp4_operand(rng, n, kk)
+        fa, fb = N.to_frag_packed(pa, kk), N.to_frag_packed(pb, kk)
+        ref = N.mm_fp4_frag(fa, sa, fb, sb, np.float32(0.75), m, n, kk)
+        args = (dev_u8(fa.reshape(-1, kk // 64, 1024)), dev_u8(sa), dev_u8(fb.reshape(-1, kk // 64, 1024)),
+                dev_u8(sb), m, n, scalar(0.75))
+        check_gemm_outputs(bsp.bsp_mm_fp4_frag(*args), bsp.bsp_mm_fp4_frag(*args, out_dtype=torch.float32),
+                           ref, f"mm_fp4_frag {m}x{n}x{kk}", f32_tol=REL_FRO_FP4_F32)
+    k4 = max(256, k // 256 * 256)
+    pa, pb = (rng.integers(0, 256, size=(r, k4 // 2), dtype=np.uint8) for r in (m, n))
+    la, lb = (rng.integers(110, 140, size=(r, k4 // 32), dtype=np.uint8) for r in (m, n))
+    (fa, fsa), (fb, fsb) = X4.to_frag(pa, la, k4), X4.to_frag(pb, lb, k4)
+    ref = X4.mm_mxfp4_frag(fa, fsa, fb, fsb, np.float32(1.0), m, n, k4)
+    a4 = (dev_u8(fa.reshape(-1, k4 // 64, 1024)), dev_u8(fsa.reshape(-1, k4 // 256, 256)),
+          dev_u8(fb.reshape(-1, k4 // 64, 1024)), dev_u8(fsb.reshape(-1, k4 // 256, 256)), m, n)
+    check_gemm_outputs(bsp.bsp_mm_mxfp4_frag(*a4), bsp.bsp_mm_mxfp4_frag(*a4, out_dtype=torch.float32), ref,
+                       f"mm_mxfp4_frag {m}x{n}x{k4}")
+    qa, s8a = _mx8_operand(rng, m, k4)
+    qb, s8b = _mx8_operand(rng, n, k4)
+    (ga, gsa), (gb, gsb) = X.to_frag(qa, s8a, k4), X.to_frag(qb, s8b, k4)
+    ref = X.mm_mxfp8_frag(ga, gsa, gb, gsb, m, n, k4)
+    a8 = (dev_u8(ga.reshape(-1, k4 // 64, 2048)), dev_u8(gsa.reshape(-1, k4 // 256, 256)),
+          dev_u8(gb.reshape(-1, k4 // 64, 2048)), dev_u8(gsb.reshape(-1, k4 // 256, 256)), m, n)
+    check_gemm_outputs(bsp.bsp_mm_mxfp8_frag(*a8), bsp.bsp_mm_mxfp8_frag(*a8, out_dtype=torch.float32), ref,
+                       f"mm_mxfp8_frag {m}x{n}x{k4}")
+
+
+@pytest.mark.parametrize("m,k,pad", QUANT_CASES)
+def test_frag_quantize_sweep(m, k, pad):
+    """The fragment-layout quantizers on rows of stride K + pad (K rounded up to a multiple of 64 for
+    NVFP4 and 256 for MX): every packed byte, padding rows included, and every scale byte against
+    the oracle's own fragment layout."""
+    k64, k256 = -(-k // 64) * 64, -(-k // 256) * 256
+    say("frag quantize sweep", m, k64, k256, pad)
+    for kk in sorted({k64, k256}):
+        xb = W.small_case(m, kk, seed=m * 19 + kk + pad, std=1.5, outlier_frac=0.03)
+        big = np.zeros((m, kk + pad), dtype=np.uint16)
+        big[:, :kk] = xb
+        x = dev_bf16(big)[:, :kk]
+        if kk == k64:
+            g = N.global_sf(xb)[0]
+            p, sf = bsp.bsp_nvfp4_quantize_frag(x, scalar(g))
+            rp, rs = N.quantize(xb, g, packed_layout="frag")
+            assert np.array_equal(host_u8(p).ravel(), rp) and np.array_equal(host_u8(sf).ravel(), rs)
+        if kk == k256:
+            p, sf = bsp.bsp_mxfp4_quantize_frag(x)
+            rp, rs = X4.to_frag(*X4.quantize(xb, layout="linear"), kk)
+            assert np.array_equal(host_u8(p).ravel(), rp) and np.array_equal(host_u8(sf).ravel(), rs)
+            q, s = bsp.bsp_mxfp8_quantize_frag(x)
+            rq, rs = X.quantize_frag(xb)
+            assert np.array_equal(host_u8(q).ravel(), rq) and np.array_equal(host_u8(s).ravel(), rs)
