@@ -45,6 +45,23 @@ int main(void) {
   /* one row-tile past the quantizer's grid limit */
   CHECK(bsp_nvfp4_quantize(p, 65535LL * 128 + 1, 32, 32, (const float*)p, (uint8_t*)p, (uint8_t*)p, NULL) ==
         BSP_ESHAPE);
+  /* the fragment layouts: sizes, and K rules checked before a launch */
+  int64_t sfb = -1;
+  CHECK(bsp_nvfp4_frag_bytes(33, 192, &bytes) == BSP_OK && bytes == 64LL * 96);
+  CHECK(bsp_nvfp4_frag_bytes(4, 96, &bytes) == BSP_ESHAPE);
+  CHECK(bsp_mxfp4_frag_bytes(33, 512, &bytes, &sfb) == BSP_OK && bytes == 64LL * 256 && sfb == 64LL * 16);
+  CHECK(bsp_mxfp8_frag_bytes(33, 512, &bytes, &sfb) == BSP_OK && bytes == 64LL * 512 && sfb == 64LL * 16);
+  CHECK(bsp_nvfp4_quantize_frag(p, 4, 96, 96, (const float*)p, (uint8_t*)p, (uint8_t*)p, NULL) == BSP_ESHAPE);
+  CHECK(bsp_mm_fp4_frag((const uint8_t*)p, (const uint8_t*)p, (const uint8_t*)p, (const uint8_t*)p,
+                        (const float*)p, NULL, 8, 8, 96, p, 8, BSP_OUT_BF16, NULL) == BSP_ESHAPE);
+  CHECK(bsp_mm_fp4_frag((const uint8_t*)p, (const uint8_t*)p, (const uint8_t*)p, (const uint8_t*)p,
+                        (const float*)p, NULL, 8, 8, (1LL << 24) + 64, p, 8, BSP_OUT_BF16, NULL) == BSP_ESHAPE);
+  CHECK(bsp_mm_mxfp4_frag((const uint8_t*)p, (const uint8_t*)p, (const uint8_t*)p, (const uint8_t*)p, NULL,
+                          NULL, 8, 8, 384, p, 8, BSP_OUT_BF16, NULL) == BSP_ESHAPE);
+  CHECK(bsp_mm_mxfp8_frag((const uint8_t*)p, (const uint8_t*)p, (const uint8_t*)p, (const uint8_t*)p, NULL,
+                          8, 8, 384, p, 8, BSP_OUT_BF16, NULL) == BSP_ESHAPE);
+  CHECK(bsp_mm_fp4_frag(NULL, NULL, NULL, NULL, NULL, NULL, 0, 8, 64, NULL, 8, BSP_OUT_BF16, NULL) ==
+        BSP_OK);  /* M == 0: no-op */
   printf("c consumer ok\n");
   return 0;
 }
