@@ -32,6 +32,7 @@ SIGNATURES = {
     "bsp_nvfp4_global_sf": ([_p, _i64, _i64, _i64, _p, _p, _p, _p], _int),
     "bsp_nvfp4_quantize": ([_p, _i64, _i64, _i64, _p, _p, _p, _p], _int),
     "bsp_nvfp4_prequantize_weight": ([_p, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p], _int),
+    "bsp_nvfp4_prequantize_weight_frag": ([_p, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p], _int),
     "bsp_nvfp4_alpha": ([_p, _p, _p, _p], _int),
     "bsp_mm_fp4": ([_p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _int, _p], _int),
     "bsp_mxfp8_quantize": ([_p, _i64, _i64, _i64, _p, _p, _p], _int),
@@ -567,6 +568,20 @@ def _nvfp4_quantize_frag(fn, x, gsf, packed, sf):
     _call(fn, x.data_ptr(), m, k, x.stride(0), gsf.data_ptr(), packed.data_ptr(), sf.data_ptr(),
           _stream(x.device))
     return packed, sf
+
+
+def bsp_nvfp4_prequantize_weight_frag(w: torch.Tensor):
+    """Load-time, fragment layout: (packed [ceil(N/32), K/64, 1024], sf (128x4), gsf, inv_gsf, amax)
+    for bf16 weight w [N, K], K % 64 == 0."""
+    w = _as_bf16_2d(w, "w")
+    n, k = w.shape
+    packed = torch.empty((-(-n // 32), k // 64, 1024), dtype=torch.uint8, device=w.device)
+    sf = torch.empty((-(-n // 128) * 128, -(-(k // 16) // 4) * 4), dtype=torch.uint8, device=w.device)
+    sc = torch.empty(3, dtype=torch.float32, device=w.device)
+    gsf, inv, amax = sc[0:1], sc[1:2], sc[2:3]
+    _call("bsp_nvfp4_prequantize_weight_frag", w.data_ptr(), n, k, w.stride(0), packed.data_ptr(),
+          sf.data_ptr(), gsf.data_ptr(), inv.data_ptr(), amax.data_ptr(), _stream(w.device))
+    return packed, sf, gsf, inv, amax
 
 
 def bsp_mm_fp4_frag(a: torch.Tensor, a_sf: torch.Tensor, b: torch.Tensor, b_sf: torch.Tensor,

@@ -1193,6 +1193,23 @@ extern "C" int bsp_nvfp4_prequantize_weight(const void* w, int64_t N, int64_t K,
   return bsp_nvfp4_quantize(w, N, K, ld, gsf, packed, sf, stream);
 }
 
+extern "C" int bsp_nvfp4_prequantize_weight_frag(const void* w, int64_t N, int64_t K, int64_t ld,
+                                                 uint8_t* packed, uint8_t* sf, float* gsf,
+                                                 float* inv_gsf, float* amax, void* stream) {
+  const char* fn = "bsp_nvfp4_prequantize_weight_frag";
+  BSP_REQUIRE(N > 0 && K > 0, BSP_EINVAL, "%s: bad size", fn);
+  BSP_REQUIRE(K % 64 == 0, BSP_ESHAPE, "%s: K (%lld) must be a multiple of 64", fn, (long long)K);
+  BSP_REQUIRE(w && packed && sf && gsf && inv_gsf && amax, BSP_EINVAL, "%s: null pointer", fn);
+  // everything the quantize step checks, before the global-scale step launches anything
+  BSP_REQUIRE(N <= 1 || ld >= K, BSP_ESHAPE, "%s: ld (%lld) < K (%lld)", fn, (long long)ld, (long long)K);
+  BSP_REQUIRE(((reinterpret_cast<uintptr_t>(packed) | reinterpret_cast<uintptr_t>(sf)) & 15u) == 0,
+              BSP_EINVAL, "%s: packed and sf must be 16-byte aligned", fn);
+  BSP_REQUIRE(ceil_div(N, 128) < 65536, BSP_ESHAPE, "%s: N too large", fn);
+  int e = bsp_nvfp4_global_sf(w, N, K, ld, gsf, inv_gsf, amax, stream);
+  if (e) return e;
+  return bsp_nvfp4_quantize_frag(w, N, K, ld, gsf, packed, sf, stream);
+}
+
 extern "C" int bsp_nvfp4_alpha(const float* xg, const float* wg, float* alpha, void* stream) {
   BSP_REQUIRE(xg && wg && alpha, BSP_EINVAL, "bsp_nvfp4_alpha: null pointer");
   if (int e = check_device()) return e;

@@ -302,6 +302,17 @@ int bsp_nvfp4_quantize_frag(const void* x_bf16, int64_t M, int64_t K, int64_t ld
 int bsp_nvfp4_quantize_gelu_frag(const void* y_bf16, int64_t M, int64_t K, int64_t ld,
                                  const float* gsf_dev, uint8_t* packed, uint8_t* sf, void* stream);
 
+/* Load-time weight prequantization with the packed values in the fragment layout: the global scale
+ * (bsp_nvfp4_global_sf), then bsp_nvfp4_quantize_frag, of W [N, K] ([FV-QAT] convert_model_to_fp4,
+ * [FV-NV] convert_model_to_nvfp4, with the do_shuffle arrangement above). K % 64 == 0 (else
+ * BSP_ESHAPE); packed (bsp_nvfp4_frag_bytes(N, K) bytes) and sf (bsp_nvfp4_sf_bytes(N, K) bytes)
+ * 16-byte aligned, no NULL pointer (else BSP_EINVAL); gsf_dev, inv_gsf_dev and amax_dev as for
+ * bsp_nvfp4_prequantize_weight. Nothing is synchronised; the caller may free W once the stream has
+ * passed this call. */
+int bsp_nvfp4_prequantize_weight_frag(const void* w_bf16, int64_t N, int64_t K, int64_t ld,
+                                      uint8_t* packed, uint8_t* sf, float* gsf_dev,
+                                      float* inv_gsf_dev, float* amax_dev, void* stream);
+
 /* bsp_mm_fp4 on fragment-layout packed operands (scales in 128x4): C = alpha * A . B^T, plus the
  * bias as in bsp_mm_fp4_bias when bias_bf16 (device bf16 [N], 2-byte aligned) is not NULL.
  * a_packed: A [M, K] and b_packed: B [N, K] (K-major weight) in the fragment layout; out [M, N]

@@ -354,3 +354,13 @@ def test_nvfp4_frag_entry_points():
     assert st not in (-1, -2, -3), st
     st, msg = _st(g, P, P, P, P, P, None, 4, 4, (1 << 24) + 64, P, 4, 0, None)
     assert st == -2 and "at most" in msg
+    w = "bsp_nvfp4_prequantize_weight_frag"
+    st, msg = _st(w, P, 4, 96, 96, P, P, P, P, P, None)
+    assert st == -2 and "multiple of 64" in msg
+    assert _st(w, P, 4, 128, 64, P, P, P, P, P, None)[0] == -2               # ld < K
+    assert _st(w, P, 0, 128, 128, P, P, P, P, P, None)[0] == -1              # no rows
+    assert _st(w, None, 4, 128, 128, P, P, P, P, P, None)[0] == -1
+    assert _st(w, P, 4, 128, 128, P, P, P, None, P, None)[0] == -1           # inv_gsf
+    assert _st(w, P, 4, 128, 128, ctypes.c_void_p(20), P, P, P, P, None)[0] == -1   # packed alignment
+    assert _st(w, P, 4, 128, 128, P, ctypes.c_void_p(24), P, P, P, None)[0] == -1   # sf alignment
+    assert _st(w, P, 65535 * 128 + 1, 128, 128, P, P, P, P, P, None)[0] == -2

@@ -194,11 +194,8 @@ def test_ffn_chain_full_size(cfg, layout):
         out32 = bsp.bsp_mm_fp4(ph, sh, pw2, sw2, a2, out_dtype=torch.float32)
     else:
         px, sx = bsp.bsp_nvfp4_quantize_frag(dev_bf16(xb), one)
-        w1d, w2d = dev_bf16(w1b), dev_bf16(w2b)
-        g1, g2 = bsp.bsp_nvfp4_global_sf(w1d)[0], bsp.bsp_nvfp4_global_sf(w2d)[0]
-        pw1, sw1 = bsp.bsp_nvfp4_quantize_frag(w1d, g1)
-        pw2, sw2 = bsp.bsp_nvfp4_quantize_frag(w2d, g2)
-        del w1d, w2d
+        pw1, sw1, g1, _, _ = bsp.bsp_nvfp4_prequantize_weight_frag(dev_bf16(w1b))
+        pw2, sw2, g2, _, _ = bsp.bsp_nvfp4_prequantize_weight_frag(dev_bf16(w2b))
         a1, a2 = bsp.bsp_nvfp4_alpha(one, g1), bsp.bsp_nvfp4_alpha(one, g2)
         y = bsp.bsp_mm_fp4_frag(px, sx, pw1, sw1, m, n1, a1)
         y32 = bsp.bsp_mm_fp4_frag(px, sx, pw1, sw1, m, n1, a1, out_dtype=torch.float32)

@@ -175,3 +175,34 @@ def test_nvfp4_frag_full_size_fc_in():
     d = (bsp.bsp_mm_fp4(lx, lsx, lw, lsw, alpha, out_dtype=torch.float32) - c32).abs().max().item()
     say("max |frag - row-major| fp32:", d, "max |c|:", c32.abs().max().item())
     assert d <= 1e-5 * c32.abs().max().item()
+
+
+@pytest.mark.parametrize("n,k,pad", [(1, 64, 0), (77, 192, 8), (256, 512, 0), (300, 1280, 16)])
+def test_prequantize_weight_frag_matches_oracle(n, k, pad):
+    """Load-time prequantization in the fragment layout: the weight global scale, inv_gsf and amax,
+    and every packed (padding rows included) and scale byte against the oracle."""
+    say("prequantize_weight_frag", n, k, pad)
+    wb = W.small_case(n, k, seed=n + 3 * k + pad, std=0.02, outlier_frac=0.01)
+    big = np.zeros((n, k + pad), dtype=np.uint16)
+    big[:, :k] = wb
+    p, s, g, inv, amax = bsp.bsp_nvfp4_prequantize_weight_frag(dev_bf16(big)[:, :k])
+    rg, rinv, ramax = N.global_sf(wb)
+    assert g.item() == rg and inv.item() == rinv and amax.item() == ramax
+    rp, rs = N.quantize(wb, rg, packed_layout="frag")
+    assert np.array_equal(host_u8(p).ravel(), rp) and np.array_equal(host_u8(s).ravel(), rs)
+
+
+def test_prequantize_weight_frag_full_size():
+    """Wan-14B W1 [13824, 5120]: every byte equals bsp_nvfp4_global_sf + bsp_nvfp4_quantize_frag on
+    the device, and whole row tiles (first, middle, last) equal the oracle's."""
+    wb = tensor_bits(4, "W")
+    wd = dev_bf16(wb)
+    p, s, g, _, _ = bsp.bsp_nvfp4_prequantize_weight_frag(wd)
+    g2 = bsp.bsp_nvfp4_global_sf(wd)[0]
+    p2, s2 = bsp.bsp_nvfp4_quantize_frag(wd, g2)
+    assert g.item() == g2.item() == N.global_sf(wb)[0]
+    assert torch.equal(p, p2) and torch.equal(s, s2)
+    rg = N.global_sf(wb)[0]
+    for t in (0, p.shape[0] // 2, p.shape[0] - 1):
+        rp, _ = N.quantize(wb[32 * t: 32 * t + 32], rg, packed_layout="frag")
+        assert np.array_equal(host_u8(p[t]).ravel(), rp), t
