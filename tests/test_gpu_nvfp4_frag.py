@@ -206,3 +206,32 @@ def test_prequantize_weight_frag_full_size():
     for t in (0, p.shape[0] // 2, p.shape[0] - 1):
         rp, _ = N.quantize(wb[32 * t: 32 * t + 32], rg, packed_layout="frag")
         assert np.array_equal(host_u8(p[t]).ravel(), rp), t
+
+
+@pytest.mark.parametrize("cfg", [2, 4])
+def test_mm_fp4_frag_full_size_linear(cfg):
+    """The other layers the bench times in the fragment layout at full size: the Wan-1.3B attention
+    projection (32760 x 1536 x 1536) and the Wan-14B to_q (32760 x 5120 x 5120). Weight prequantized
+    in the fragment layout, activation quantized with the static scale; sampled rows of the packed
+    activation through the layout's offsets and sampled GEMM entries against the oracle's linear
+    layer on the same bf16 X and W."""
+    xb = tensor_bits(cfg, "X")
+    wb = tensor_bits(cfg, "W" if cfg == 2 else "W3")
+    m, k, n = xb.shape[0], xb.shape[1], wb.shape[0]
+    say("full-size frag linear cfg", cfg, m, n, k)
+    one = scalar(1.0)
+    pw, sw, gw, _, _ = bsp.bsp_nvfp4_prequantize_weight_frag(dev_bf16(wb))
+    px, sx = bsp.bsp_nvfp4_quantize_frag(dev_bf16(xb), one)
+    alpha = bsp.bsp_nvfp4_alpha(one, gw)
+    c = bsp.bsp_mm_fp4_frag(px, sx, pw, sw, m, n, alpha)
+    c32 = bsp.bsp_mm_fp4_frag(px, sx, pw, sw, m, n, alpha, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert gw.item() == N.global_sf(wb)[0]
+    rows, cols = sample_entries(m, n, 3000, 100 + cfg)
+    ur = np.unique(rows)
+    rp, _ = N.quantize(xb[ur], f32(1.0), layout="linear")
+    off = N.frag_packed_offset(ur[:, None], np.arange(k // 2)[None, :], k)
+    got = px.view(-1)[torch.from_numpy(off.ravel()).cuda()].cpu().numpy().reshape(off.shape)
+    assert np.array_equal(got, rp), "activation bytes differ"
+    check_gemm_outputs(c, c32, oracle_linear_entries(xb, wb, rows, cols), f"cfg{cfg} frag linear", rows,
+                       cols, f32_tol=REL_FRO_FP4_F32)
