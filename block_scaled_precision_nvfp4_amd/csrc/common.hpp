@@ -53,6 +53,15 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // ---------------------------------------------------------------------------------------------
 // device: bf16 and the 8-bit / 4-bit scalar codecs
 // ---------------------------------------------------------------------------------------------
+// The hardware hands a launch's workgroups to the 8 XCDs round-robin by linear id, and each XCD has
+// its own L2. xcd_blocked maps linear id b of n to an order in which consecutive ids run on one
+// XCD (a bijection on [0, n)), so that workgroups that write neighbouring bytes of one memory sector
+// do so through the same L2, which merges them, instead of each XCD writing back a partial sector.
+__device__ __forceinline__ int64_t xcd_blocked(int64_t b, int64_t n) {
+  const int64_t per = n / 8, r = n % 8, xcd = b % 8, local = b / 8;
+  return (xcd < r ? xcd * (per + 1) : r * (per + 1) + (xcd - r) * per) + local;
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 

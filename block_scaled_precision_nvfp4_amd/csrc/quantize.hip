@@ -329,7 +329,9 @@ __global__ __launch_bounds__(256) void nvfp4_quantize_token_kernel(
   __shared__ uint32_t srow[4][kTokMaxCols / 4];
   __shared__ __attribute__((aligned(16))) uint32_t pimg[WIDE ? 4 : 1][WIDE ? C * 64 : 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t tile = blockIdx.x >> 5, q = blockIdx.x & 31;
+  // workgroups q and q + 1 of a tile write neighbouring 16-byte runs of each scale tile: one XCD
+  const int64_t wg = xcd_blocked(blockIdx.x, gridDim.x);
+  const int64_t tile = wg >> 5, q = wg & 31;
   const int64_t row = tile * 128 + q + 32 * wave;
   const bool live = row < M;
   const int64_t seg_elems = 64 * 8 * C;
@@ -449,7 +451,9 @@ __global__ __launch_bounds__(256) void rmsnorm_token_kernel(
   __shared__ uint32_t srow[QUANT ? 4 : 1][QUANT ? kTokMaxCols / 4 : 1];
   __shared__ __attribute__((aligned(16))) uint32_t pimg[QUANT && WIDE ? 4 : 1][QUANT && WIDE ? C * 64 : 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t tile = blockIdx.x >> 5, q = blockIdx.x & 31;
+  // workgroups q and q + 1 of a tile write neighbouring 16-byte runs of each scale tile: one XCD
+  const int64_t wg = xcd_blocked(blockIdx.x, gridDim.x);
+  const int64_t tile = wg >> 5, q = wg & 31;
   const int64_t row = tile * 128 + q + 32 * wave;
   const bool live = row < M;
   const int64_t seg_elems = 64 * 8 * C;
@@ -591,11 +595,12 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const uint16_t* __r
   __shared__ uint4 frag_tile[FRAG || WIDE ? 1024 : 1];
   __shared__ uint4 sf_stage[FRAG || WIDE ? 32 : 1];  // FRAG: two 256-byte scale groups; WIDE: 64 x 8
   const int t = threadIdx.x;
-  const int64_t row0 = (int64_t)blockIdx.y * 64;
-  const int64_t kk = (int64_t)blockIdx.x * 256 + (t & 31) * 8;
+  const int64_t bx = blockIdx.x, by = blockIdx.y;
+  const int64_t row0 = by * 64;
+  const int64_t kk = bx * 256 + (t & 31) * 8;
   const int rsub = t >> 5;
   const bool kin = kk < K;  // K % 32 == 0: a quad is entirely in or out
-  const bool full = row0 + 64 <= M && (int64_t)blockIdx.x * 256 + 256 <= K;
+  const bool full = row0 + 64 <= M && bx * 256 + 256 <= K;
   const uint16_t* xp = x + (row0 + rsub) * ld + kk;
   const int64_t xstep = 8 * ld;
   uint4 v[8];
@@ -663,11 +668,11 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const uint16_t* __r
       const int p = it * 256 + t, rr = p >> 4, part = p & 15;
       const uint4 w = frag_tile[p];
       __builtin_nontemporal_store((nt_u32x4){w.x, w.y, w.z, w.w},
-                                  reinterpret_cast<nt_u32x4*>(q + (row0 + rr) * K + blockIdx.x * 256 + part * 16));
+                                  reinterpret_cast<nt_u32x4*>(q + (row0 + rr) * K + bx * 256 + part * 16));
     }
     // each row's 8 scale bytes of this K range: one 8-byte store when the row offsets allow it
     if (t < 64) {
-      const int64_t off = (row0 + t) * ng + (int64_t)blockIdx.x * 8;
+      const int64_t off = (row0 + t) * ng + bx * 8;
       const uint2 w = reinterpret_cast<const uint2*>(sf_stage)[t];
       if (((reinterpret_cast<uintptr_t>(sf) + off) & 7) == 0) {
         *reinterpret_cast<uint2*>(sf + off) = w;
@@ -681,7 +686,7 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const uint16_t* __r
     __syncthreads();
     // row tiles past ceil(M / 32) are not part of the buffers; padded rows inside the last one
     // were encoded from zeros (code 0, scale 0x00)
-    const int64_t row_tiles = (M + 31) / 32, rt0 = (int64_t)blockIdx.y * 2;
+    const int64_t row_tiles = (M + 31) / 32, rt0 = by * 2;
     const int64_t ks_steps = K / 64, k_groups = K / 256;
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
@@ -689,11 +694,11 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const uint16_t* __r
       if (rt0 + (p >> 9) < row_tiles) {
         const uint4 v = frag_tile[p ^ (((p >> 5) & 15) << 1)];
         __builtin_nontemporal_store((nt_u32x4){v.x, v.y, v.z, v.w},
-                                    reinterpret_cast<nt_u32x4*>(q + ((rt0 + (p >> 9)) * ks_steps + blockIdx.x * 4) * 2048) + (p & 511));
+                                    reinterpret_cast<nt_u32x4*>(q + ((rt0 + (p >> 9)) * ks_steps + bx * 4) * 2048) + (p & 511));
       }
     }
     if (t < 32 && rt0 + (t >> 4) < row_tiles)
-      reinterpret_cast<uint4*>(sf + ((rt0 + (t >> 4)) * k_groups + blockIdx.x) * 256)[t & 15] = sf_stage[t];
+      reinterpret_cast<uint4*>(sf + ((rt0 + (t >> 4)) * k_groups + bx) * 256)[t & 15] = sf_stage[t];
   }
 }
 
