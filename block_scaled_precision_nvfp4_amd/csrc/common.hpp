@@ -62,6 +62,14 @@ __device__ __forceinline__ int64_t xcd_blocked(int64_t b, int64_t n) {
   return (xcd < r ? xcd * (per + 1) : r * (per + 1) + (xcd - r) * per) + local;
 }
 
+// A milder regrouping: within each complete block of 32 ids, ids 4x .. 4x + 3 (in the returned
+// order) are the four the hardware gives XCD x, so runs of four consecutive ids share one L2 while
+// the XCDs still work side by side (a bijection on [0, n); an incomplete last block is unchanged).
+__device__ __forceinline__ int64_t xcd_quads(int64_t b, int64_t n) {
+  const int64_t blk = b >> 5, w = b & 31;
+  return (blk * 32 + 32 <= n) ? blk * 32 + (w & 7) * 4 + (w >> 3) : b;
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 

@@ -595,7 +595,11 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const uint16_t* __r
   __shared__ uint4 frag_tile[FRAG || WIDE ? 1024 : 1];
   __shared__ uint4 sf_stage[FRAG || WIDE ? 32 : 1];  // FRAG: two 256-byte scale groups; WIDE: 64 x 8
   const int t = threadIdx.x;
-  const int64_t bx = blockIdx.x, by = blockIdx.y;
+  // row-major scales: the 8 scale bytes a workgroup writes per row are a quarter of a 32-byte sector,
+  // whose other quarters come from the next three K tiles; those four run on one XCD (one L2)
+  const int64_t lin = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+  const int64_t wg = FRAG ? lin : xcd_quads(lin, (int64_t)gridDim.x * gridDim.y);
+  const int64_t bx = wg % gridDim.x, by = wg / gridDim.x;
   const int64_t row0 = by * 64;
   const int64_t kk = bx * 256 + (t & 31) * 8;
   const int rsub = t >> 5;
