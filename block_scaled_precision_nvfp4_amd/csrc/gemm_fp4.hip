@@ -486,11 +486,20 @@ __device__ __forceinline__ void load_step(StepFrags& f, const FragPlan& p, uint3
   for (int u = 0; u < 16; ++u) load_one(f, p, s, u);
 }
 
-// converts of fragment q (0-3: A row tiles, 4-7: B) of sub-step j
-__device__ __forceinline__ Raw step_cvt(const StepFrags& f, int q, int j) {
+// Converts of fragment q (0-3: A row tiles, 4-7: B) of sub-step j. The first use of a step's
+// scales (j == 0) turns the lane's two e4m3 bytes into the f16 pair of their values in place, with
+// the hardware fp8 -> f16 conversion (exact for every e4m3 code, subnormals included; scale 1);
+// sub-steps 0-1 take the low half, 2-3 the high half. Unlike the LDS-staged loop's bit-built
+// scales these carry no 2^-8: every product e2m1 * e4m3 is at most 2688 and at least 2^-10 in
+// magnitude when nonzero, with at most 6 significant bits: exact in f16.
+__device__ __forceinline__ Raw step_cvt(StepFrags& f, int q, int j) {
   const uint32_t w = q < 4 ? comp(f.pa[q], j) : comp(f.pb[q - 4], j);
+  uint32_t& sw = q < 4 ? f.sa[q] : f.sb[q - 4];
+  if (j == 0)
+    sw = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, false));
+  const f16x2 t = __builtin_bit_cast(f16x2, sw);
   Raw r;
-  r.s = scale_pair(q < 4 ? f.sa[q] : f.sb[q - 4], j >> 1, kScaleMask);
+  r.s = (j >> 1) ? __builtin_shufflevector(t, t, 1, 1) : __builtin_shufflevector(t, t, 0, 0);
   r.p[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
   r.p[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
   r.p[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
@@ -525,7 +534,7 @@ __device__ __forceinline__ void frag_step(f32x16 (&acc)[4][4], StepFrags (&F)[3]
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int cb = j & 1, nb = cb ^ 1;
-    const StepFrags& nf = F[j < 3 ? BUF : (BUF + 1) % 3];
+    StepFrags& nf = F[j < 3 ? BUF : (BUF + 1) % 3];
     const int nj = (j + 1) & 3;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
@@ -603,12 +612,11 @@ __global__ __launch_bounds__(256, 1) void mm_fp4_frag_kernel(
   if (s + 1 < KS) frag_step<1>(acc, F, d, p, (uint32_t)(KS - 1));
   wait_vmcnt<0>();
 
-  // operands carried 2^-8 each (scale_pair): the accumulators hold 2^-16 of the true sums, which
-  // the epilogue undoes on the accumulator (ACC16)
+  // the operands carry their true values (step_cvt), so the accumulators hold the sums themselves
   const float a = *alpha_ptr;
   const float alpha[4] = {a, a, a, a};
-  store_tile<OUT_F32, BIAS, true>(acc, alpha, m0, n0, wm, wn, M, N, out, ldc, vec_store, lds, wave,
-                                  lane, li, h, bias);
+  store_tile<OUT_F32, BIAS, false>(acc, alpha, m0, n0, wm, wn, M, N, out, ldc, vec_store, lds, wave,
+                                   lane, li, h, bias);
 }
 
 }  // namespace fp4

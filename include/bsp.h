@@ -102,7 +102,9 @@ int bsp_nvfp4_alpha(const float* x_gsf_dev, const float* w_gsf_dev, float* alpha
  * stride ldc elements (bf16 or fp32 per out_dtype). Requires K % 64 == 0 and K <= 2^24 (else
  * BSP_ESHAPE); M, N arbitrary >= 0. a_packed, a_sf, b_packed and b_sf 16-byte aligned, no NULL
  * pointer (else BSP_EINVAL); out_dtype other than BSP_OUT_BF16 / BSP_OUT_F32: BSP_EDTYPE. Every
- * finite alpha is applied exactly as fl32(alpha * sum) up to the fp32 accumulation. */
+ * finite alpha is applied exactly as fl32(alpha * sum) up to the fp32 accumulation. Scale bytes
+ * are read as non-negative e4m3: the sign bit is ignored and the NaN code 0x7F reads as 480 (every
+ * quantizer here writes 0x00 .. 0x7E). */
 int bsp_mm_fp4(const uint8_t* a_packed, const uint8_t* a_sf, const uint8_t* b_packed,
                const uint8_t* b_sf, const float* alpha_dev, int64_t M, int64_t N, int64_t K,
                void* out, int64_t ldc, int out_dtype, void* stream);
@@ -317,7 +319,8 @@ int bsp_nvfp4_prequantize_weight_frag(const void* w_bf16, int64_t N, int64_t K, 
  * bias as in bsp_mm_fp4_bias when bias_bf16 (device bf16 [N], 2-byte aligned) is not NULL.
  * a_packed: A [M, K] and b_packed: B [N, K] (K-major weight) in the fragment layout; out [M, N]
  * row stride ldc, bf16 or fp32. The same products as bsp_mm_fp4, summed in another order inside
- * each 64-element step (the output may differ from bsp_mm_fp4's by fp32 rounding). Requires
+ * each 64-element step (the output may differ from bsp_mm_fp4's by fp32 rounding). Every scale
+ * byte is decoded as e4m3 in full (a set sign bit negates, 0x7F and 0xFF give NaN). Requires
  * K % 64 == 0 and K <= 2^24 (else BSP_ESHAPE); operands and scales 16-byte aligned, no NULL
  * operand, scale or alpha pointer (else BSP_EINVAL); out_dtype as bsp_mm_fp4. */
 int bsp_mm_fp4_frag(const uint8_t* a_packed, const uint8_t* a_sf, const uint8_t* b_packed,

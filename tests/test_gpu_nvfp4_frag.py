@@ -107,6 +107,47 @@ def test_mm_fp4_frag_random_operands_all_elements(m, n, k):
     check_gemm_outputs(t16, t32, ref, f"fp4 frag {m}x{n}x{k}", f32_tol=REL_FRO_FP4_F32)
 
 
+def _scale_code_operands(code_range: int):
+    """A [256, 64]: every e2m1 code in every row, the scale of row r's block b the code
+    (4 r + b) % code_range; B [64, 64]: e2m1 1.0 at k == n and +0 elsewhere, unit scales (0x38).
+    Each output C[m, n] is then the single product e2m1(A[m, n]) * e4m3(SA[m, n / 16]), exact in
+    fp32, or NaN where row m has a NaN scale (NaN times a zero element)."""
+    m, n, k = 256, 64, 64
+    codes = (np.arange(m)[:, None] * 7 + np.arange(k)[None, :]) % 16
+    rp, cp = N.sf_padded_shape(m, k)
+    lin = ((4 * np.arange(rp)[:, None] + np.arange(cp)[None, :]) % code_range).astype(np.uint8)
+    pa, sa = N.pack_nibbles(codes), N.swizzle_128x4(lin)
+    pb = N.pack_nibbles(np.where(np.eye(n, k, dtype=bool), 0x2, 0))
+    rpb, cpb = N.sf_padded_shape(n, k)
+    sb = N.swizzle_128x4(np.full((rpb, cpb), 0x38, dtype=np.uint8))
+    return m, n, k, pa, sa, pb, sb
+
+
+def test_mm_fp4_frag_every_scale_code_exact():
+    """Every one of the 256 e4m3 scale bytes (sign, subnormals, zero and the NaN codes included)
+    enters the fragment-layout GEMM with the value the oracle decodes: fp32 outputs equal the
+    oracle's product exactly, NaN where it is NaN."""
+    say("mm_fp4_frag every scale code")
+    m, n, k, pa, sa, pb, sb = _scale_code_operands(256)
+    ref = N.mm_fp4(pa, sa, pb, sb, f32(1.0), m, n, k).astype(np.float32)
+    assert np.isnan(ref).any() and (ref < 0).any()
+    fa, fb = N.to_frag_packed(pa, k), N.to_frag_packed(pb, k)
+    t32 = bsp.bsp_mm_fp4_frag(_dev_frag(fa, m, k), dev_u8(sa), _dev_frag(fb, n, k), dev_u8(sb), m, n,
+                              scalar(f32(1.0)), out_dtype=torch.float32)
+    assert np.array_equal(t32.cpu().numpy(), ref, equal_nan=True)
+
+
+def test_mm_fp4_every_nonnegative_scale_code_exact():
+    """The row-major GEMM on every scale byte a quantizer can write (0x00 .. 0x7E: zero,
+    subnormals and normals up to 448): fp32 outputs equal the oracle's product exactly."""
+    say("mm_fp4 every non-negative scale code")
+    m, n, k, pa, sa, pb, sb = _scale_code_operands(0x7F)
+    ref = N.mm_fp4(pa, sa, pb, sb, f32(1.0), m, n, k).astype(np.float32)
+    t32 = bsp.bsp_mm_fp4(dev_u8(pa), dev_u8(sa), dev_u8(pb), dev_u8(sb), scalar(f32(1.0)),
+                         out_dtype=torch.float32)
+    assert np.array_equal(t32.cpu().numpy(), ref)
+
+
 @pytest.mark.parametrize("m,n,k", [(77, 200, 192), (256, 256, 512), (300, 130, 64)])
 def test_mm_fp4_frag_bias(m, n, k):
     """With a bias: the bf16 output equals the no-bias output plus the bias (torch's bf16 add, the
